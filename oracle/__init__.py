@@ -1,0 +1,1 @@
+"""Plain CPU oracle: test infrastructure only (tests, smoke check, CPU baseline)."""
