@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse decode step on one MI355X.
+
+A step is one ls_decode_step call: one layer of the decode step for every
+request of the batch (coarse scoring, candidate selection, refinement and
+top-k, hot-buffer resolve and miss gather, split attention and combine).
+Inputs are synthetic and already resident in HBM when timing starts.
+
+Prints one JSON line with:
+  value       layer-steps/s (whole-step throughput, steps timed back to back)
+  roofline    the dominant kernel (coarse scoring) against the 8 TB/s HBM peak:
+              algorithmic bytes per launch / its average duration, measured
+              with HIP events recorded by the library on the launch stream
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-decode layer-steps/s at 128K (B=32) + % of HBM roofline"
+HBM_PEAK_GBS = 8000.0
+STAGES = ["coarse_score", "candidate_select", "refine_topk_resolve", "miss_gather",
+          "attention", "combine"]
+
+
+def algorithmic_bytes(wl, n_miss_total: int) -> dict:
+    """Bytes the step must move at minimum, by part (see the design notes)."""
+    B, L, H, D = wl.batch, wl.ctx, wl.idx_heads, wl.idx_dim
+    row = wl.qk_dim * 2
+    parts = {
+        "coarse_keys": B * L * D // 2,
+        "refine_keys": B * wl.n_cand * D,
+        "slot_table": B * wl.topk * 4 if wl.hot_slots else 0,
+        "miss_read": n_miss_total * row,
+        "miss_write": n_miss_total * row,
+        "kv_rows": B * wl.topk * row,
+        "attn_q": B * wl.q_heads * wl.qk_dim * 2,
+        "out_lse": B * wl.q_heads * (wl.v_dim * 2 + 4),
+        "idx_q_w": B * H * (D + 1),
+    }
+    parts["total"] = sum(parts.values())
+    return parts
+
+
+def file_sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_src):
+    """Counter-measured HBM bytes of the coarse kernel, if taken on the current
+    kernel source (profiles/coarse_traffic.json, written from rocprofv3 --pmc)."""
+    p = os.path.join(ROOT, "profiles", "coarse_traffic.json")
+    if not os.path.exists(p):
+        return None
+    t = json.load(open(p))
+    if t.get("kernel_sha") != file_sha(kernel_src):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def build_inputs(ls, synth, wl, dev, replicas):
+    import torch
+    inp = synth.indexer_inputs(wl, dev)
+    keys = inp["keys"]
+    kc = ls.pack_coarse(keys)
+    q_attn = synth.attention_query(wl, dev)
+    pool = synth.kv_pool(wl, dev, pin=wl.pool_on_host, gen_device=dev)
+    ctx_len = torch.full((wl.batch,), wl.ctx, dtype=torch.int32, device=dev)
+    # the hot buffer is laid out from this workload's own selection, computed
+    # once here (setup, untimed) so that exactly the stated share misses
+    cand = ls.index_coarse(inp["q"], inp["w"], kc, ctx_len, wl.n_cand)
+    sel, _ = ls.refine_topk(inp["q"], inp["w"], keys, cand, ctx_len, wl.topk)
+    pos2slot, hot, n_miss = synth.hot_fill(wl, sel, pool, dev)
+    reps = []
+    for r in range(replicas):
+        reps.append(dict(
+            q_idx=inp["q"], w_idx=inp["w"], ctx_len=ctx_len,
+            k8=keys if r == 0 else keys.clone(), kc=kc if r == 0 else kc.clone(),
+            q_attn=q_attn if r == 0 else q_attn.clone(),
+            pos2slot=pos2slot if r == 0 else pos2slot.clone(),
+            hot_kv=hot if r == 0 else hot.clone(), pool_kv=pool))
+    torch.cuda.synchronize()
+    return reps, n_miss, inp, q_attn, pool, pos2slot, hot
+
+
+def cpu_baseline(wl, inp, q_attn, pool, pos2slot, hot, n_sample):
+    """The oracle, as it stands, on n_sample requests of the same step."""
+    import numpy as np
+    import torch
+    from oracle import oracle as orc
+
+    def bits(t):
+        return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    t_total = 0.0
+    for b in range(n_sample):
+        q, w = inp["q"][b].cpu().numpy(), inp["w"][b].cpu().numpy()
+        keys = inp["keys"][b].cpu().numpy()
+        qa = bits(q_attn[b])
+        p2s = pos2slot[b].cpu().numpy()
+        hb = bits(hot[b]).copy()
+        pb = bits(pool[b])
+        t0 = time.perf_counter()
+        orc.decode_request(q, w, keys, wl.ctx, wl.n_cand, wl.topk, qa, wl.scale,
+                           pos2slot=p2s, hot_bits=hb, pool_bits=pb, v_dim=wl.v_dim,
+                           row_stride=wl.qk_dim)
+        t_total += time.perf_counter() - t0
+    per_request = t_total / n_sample
+    return {
+        "value": 1.0 / (per_request * wl.batch),
+        "unit": "layer-steps/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "%d of %d requests of %s, whole step per request (coarse scores, "
+                  "candidates, refine, top-k, hot resolve + gather, attention), "
+                  "single-threaded C; %.2f s per request, scaled to the %d-request batch"
+                  % (n_sample, wl.batch, wl.name, per_request, wl.batch),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode-128k-b32")
+    ap.add_argument("--replicas", type=int, default=2)
+    ap.add_argument("--cpu-sample", type=int, default=4,
+                    help="requests the CPU oracle baseline runs (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import top_sparse_attention_ls_amd as ls
+    from top_sparse_attention_ls_amd import synth
+
+    ls.load()
+    wl = synth.WORKLOADS[args.workload]
+    if wl.n_query:
+        print("prefill workloads are measured by their own entry point", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("[bench] building inputs for %s" % wl.name, file=sys.stderr, flush=True)
+    reps, n_miss, inp, q_attn, pool, pos2slot, hot = build_inputs(ls, synth, wl, dev,
+                                                                  args.replicas)
+    step = ls.DecodeStep(batch=wl.batch, max_ctx=wl.ctx, idx_heads=wl.idx_heads,
+                         idx_dim=wl.idx_dim, n_cand=wl.n_cand, topk=wl.topk,
+                         q_heads=wl.q_heads, qk_dim=wl.qk_dim, v_dim=wl.v_dim, scale=wl.scale,
+                         hot_slots=wl.hot_slots, pool_on_host=wl.pool_on_host, device=dev)
+
+    def run(i, events=None):
+        r = reps[i % len(reps)]
+        step.run(q_idx=r["q_idx"], w_idx=r["w_idx"], kc=r["kc"], k8=r["k8"],
+                 ctx_len=r["ctx_len"], q_attn=r["q_attn"], pos2slot=r["pos2slot"],
+                 hot_kv=r["hot_kv"], pool_kv=r["pool_kv"], events=events)
+
+    print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    miss_now = step.n_miss.cpu().tolist()
+    assert miss_now == n_miss, "hot buffer miss counts drifted: %s" % miss_now
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ls.STEP_EVENTS)]
+           for _ in range(K)]
+    for row in evs:            # create the underlying events before use
+        for e in row:
+            e.record()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    print("[bench] timing %d steps" % K, file=sys.stderr, flush=True)
+    t_start.record()
+    for i in range(K):
+        run(i, evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / K
+    stage_ms = [0.0] * (ls.STEP_EVENTS - 1)
+    for row in evs:
+        for s in range(ls.STEP_EVENTS - 1):
+            stage_ms[s] += row[s].elapsed_time(row[s + 1]) / K
+
+    ab = algorithmic_bytes(wl, sum(n_miss))
+    steps_per_s = 1000.0 / ms_per_step
+    coarse_ms = stage_ms[0]
+    coarse_bytes = wl.batch * wl.ctx * wl.idx_dim // 2 + wl.batch * wl.idx_heads * (wl.idx_dim + 1)
+    achieved = coarse_bytes / (coarse_ms * 1e-3) / 1e9
+    kernel_src = os.path.join(ROOT, "top_sparse_attention_ls_amd", "csrc", "k_index.hip")
+    result = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 2),
+        "unit": "layer-steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "batch": wl.batch, "ctx": wl.ctx, "idx_heads": wl.idx_heads,
+            "idx_dim": wl.idx_dim, "n_cand": wl.n_cand, "topk": wl.topk,
+            "q_heads": wl.q_heads, "latent": wl.qk_dim, "v_dim": wl.v_dim,
+            "hot_slots": wl.hot_slots, "miss_rate": wl.miss_rate,
+            "pool": "pinned-host" if wl.pool_on_host else "hbm",
+            "replicas": args.replicas, "parallelism": "single-gpu",
+        },
+        "hbm_roofline_step": {
+            "algorithmic_bytes": ab["total"],
+            "achieved_GBs": round(ab["total"] * steps_per_s / 1e9, 1),
+            "frac": round(ab["total"] * steps_per_s / 1e9 / HBM_PEAK_GBS, 4),
+        },
+        "roofline": {
+            "kernel": "coarse_score (k_coarse)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic(kernel_src),
+            "algorithmic_bytes_per_launch": coarse_bytes,
+            "avg_launch_us": round(coarse_ms * 1000, 2),
+        },
+        "stages_us": {n: round(v * 1000, 2) for n, v in zip(STAGES, stage_ms)},
+        "request_layer_steps_per_s": round(steps_per_s * wl.batch, 1),
+    }
+    if args.cpu_sample > 0:
+        print("[bench] cpu baseline on %d requests" % args.cpu_sample, file=sys.stderr,
+              flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, inp, q_attn, pool, pos2slot, hot,
+                                              min(args.cpu_sample, wl.batch))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

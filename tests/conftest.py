@@ -31,3 +31,12 @@ def ls():
     import top_sparse_attention_ls_amd as lsmod
     lsmod.load()
     return lsmod
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Name the case on stderr (flushed) before a GPU test touches the device."""
+    if request.node.get_closest_marker("gpu") is not None:
+        sys.stderr.write("\n[gpu case] %s\n" % request.node.nodeid)
+        sys.stderr.flush()
+    yield

@@ -1,0 +1,168 @@
+"""Host-side checks of the C-ABI that need no GPU: the library loads, exports
+every function include/ls.h declares, sizes workspaces, and rejects bad
+arguments before anything is enqueued (so no HIP call is made)."""
+import ctypes
+import subprocess
+
+import pytest
+
+import top_sparse_attention_ls_amd as ls
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ls.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = ls.header_symbols()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", ls.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert set(names) <= exported
+
+
+def test_header_compiles_as_c99(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "ls.h"\nint main(void){ return ls_abi_version() == 0; }\n')
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-c", "-I",
+                        ls.HEADER_PATH.rsplit("/", 1)[0], str(src), "-o", str(tmp_path / "t.o")],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_struct_layouts_match_header(tmp_path):
+    src = tmp_path / "s.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "ls.h"\n'
+                   'int main(void){ printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n",'
+                   ' sizeof(ls_idx_desc), sizeof(ls_hot_desc), sizeof(ls_attn_desc),'
+                   ' sizeof(ls_step_desc), sizeof(ls_step_io), sizeof(ls_prefill_desc),'
+                   ' offsetof(ls_attn_desc, scale), offsetof(ls_step_desc, attn)); return 0; }\n')
+    exe = tmp_path / "s"
+    subprocess.check_call(["gcc", "-std=c99", "-I", ls.HEADER_PATH.rsplit("/", 1)[0], str(src),
+                           "-o", str(exe)])
+    got = [int(x) for x in subprocess.check_output([str(exe)]).split()]
+    want = [ctypes.sizeof(ls.IdxDesc), ctypes.sizeof(ls.HotDesc), ctypes.sizeof(ls.AttnDesc),
+            ctypes.sizeof(ls.StepDesc), ctypes.sizeof(ls.StepIO), ctypes.sizeof(ls.PrefillDesc),
+            ls.AttnDesc.scale.offset, ls.StepDesc.attn.offset]
+    assert got == want
+
+
+def test_version_and_error_string(lib):
+    assert lib.ls_abi_version() == 1
+    assert isinstance(lib.ls_last_error(), bytes)
+
+
+def idx(**kw):
+    base = dict(batch=2, max_ctx=4096, n_heads=64, head_dim=128, n_cand=1024, topk=256)
+    base.update(kw)
+    return ls.IdxDesc(**base)
+
+
+def test_workspace_sizes(lib):
+    n = lib.ls_workspace_size(ls.OP_COARSE, ctypes.byref(idx()))
+    # scores + two tie arrays dominate: 3 * B * L * 4 bytes
+    assert n >= 3 * 2 * 4096 * 4
+    assert lib.ls_workspace_size(ls.OP_REFINE, ctypes.byref(idx())) >= 2 * 1024 * 8
+    bad = idx(head_dim=96)
+    assert lib.ls_workspace_size(ls.OP_COARSE, ctypes.byref(bad)) == 0
+    assert b"head_dim" in lib.ls_last_error()
+    assert lib.ls_workspace_size(99, ctypes.byref(idx())) == 0
+
+
+def test_step_workspace_grows_with_batch(lib):
+    def step(b):
+        i = idx(batch=b, max_ctx=131072, n_cand=8192, topk=2048)
+        h = ls.HotDesc(b, 131072, 2048, 4096, 576, 0)
+        a = ls.AttnDesc(b, 128, 1, 576, 512, 2048, 4096 + 2048, 576, 0, 0.07, 0)
+        return lib.ls_workspace_size(ls.OP_STEP, ctypes.byref(ls.StepDesc(i, h, a, 1)))
+    assert 0 < step(1) < step(32)
+
+
+FAKE = ctypes.c_void_p(0x100000)   # aligned, never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(batch=0), ls.LS_E_ARG, b"batch"),
+    (dict(max_ctx=0), ls.LS_E_ARG, b"max_ctx"),
+    (dict(n_cand=0), ls.LS_E_ARG, b"n_cand"),
+    (dict(topk=0), ls.LS_E_ARG, b"topk"),
+    (dict(n_heads=65), ls.LS_E_UNSUPPORTED, b"n_heads"),
+    (dict(head_dim=32), ls.LS_E_UNSUPPORTED, b"head_dim"),
+])
+def test_index_coarse_rejects_bad_shapes(lib, kw, code, needle):
+    d = idx(**kw)
+    rc = lib.ls_index_coarse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert rc == code
+    assert needle in lib.ls_last_error()
+
+
+def test_null_pointers_rejected(lib):
+    d = idx()
+    rc = lib.ls_index_coarse(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert rc == ls.LS_E_ARG and b"null" in lib.ls_last_error()
+    rc = lib.ls_refine_topk(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, FAKE, None, FAKE,
+                            1 << 30, None)
+    assert rc == ls.LS_E_ARG
+
+
+def test_misaligned_rejected(lib):
+    d = idx()
+    rc = lib.ls_index_coarse(ctypes.byref(d), FAKE, FAKE, ctypes.c_void_p(0x100001), FAKE, FAKE,
+                             FAKE, 1 << 30, None)
+    assert rc == ls.LS_E_ARG and b"aligned" in lib.ls_last_error()
+
+
+def test_workspace_too_small_rejected(lib):
+    d = idx()
+    rc = lib.ls_index_coarse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1024, None)
+    assert rc == ls.LS_E_WORKSPACE and b"too small" in lib.ls_last_error()
+    rc = lib.ls_index_coarse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, 1 << 30, None)
+    assert rc == ls.LS_E_WORKSPACE
+
+
+def test_attention_validation(lib):
+    a = ls.AttnDesc(2, 12, 5, 64, 64, 16, 100, 320, 64, 0.125, 0)   # 12 % 5 != 0
+    rc = lib.ls_sparse_attn_decode(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   1 << 30, None)
+    assert rc == ls.LS_E_ARG and b"multiple" in lib.ls_last_error()
+    a = ls.AttnDesc(2, 8, 8, 64, 64, 16, 100, 512, 64, float("nan"), 0)
+    rc = lib.ls_sparse_attn_decode(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   1 << 30, None)
+    assert rc == ls.LS_E_ARG and b"finite" in lib.ls_last_error()
+    a = ls.AttnDesc(2, 8, 8, 2048, 64, 16, 100, 512, 64, 0.1, 0)
+    rc = lib.ls_sparse_attn_decode(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   1 << 30, None)
+    assert rc == ls.LS_E_UNSUPPORTED
+
+
+def test_step_validation(lib):
+    i = idx()
+    h = ls.HotDesc(2, 4096, 256, 64, 576, 0)
+    a = ls.AttnDesc(2, 128, 1, 576, 512, 256, 64 + 256, 576, 0, 0.07, 0)
+    io = ls.StepIO()
+    rc = lib.ls_decode_step(ctypes.byref(ls.StepDesc(i, h, a, 1)), ctypes.byref(io), FAKE,
+                            1 << 30, None)
+    assert rc == ls.LS_E_ARG and b"null" in lib.ls_last_error()
+    a_bad = ls.AttnDesc(3, 128, 1, 576, 512, 256, 64 + 256, 576, 0, 0.07, 0)
+    rc = lib.ls_decode_step(ctypes.byref(ls.StepDesc(i, h, a_bad, 1)), ctypes.byref(io), FAKE,
+                            1 << 30, None)
+    assert rc == ls.LS_E_ARG and b"match" in lib.ls_last_error()
+    rc = lib.ls_decode_step(None, ctypes.byref(io), FAKE, 1 << 30, None)
+    assert rc == ls.LS_E_ARG
+
+
+def test_pack_validation(lib):
+    assert lib.ls_pack_coarse(FAKE, FAKE, 10, 6, None) == ls.LS_E_ARG
+    assert lib.ls_pack_coarse(None, FAKE, 10, 8, None) == ls.LS_E_ARG
+    assert lib.ls_pack_coarse(FAKE, FAKE, -1, 8, None) == ls.LS_E_ARG
+    assert lib.ls_pack_coarse(FAKE, FAKE, 0, 8, None) == ls.LS_OK   # nothing to do
+
+
+def test_python_binding_requires_gpu_tensors_types():
+    import torch
+    with pytest.raises(TypeError):
+        ls.pack_coarse(torch.zeros(4, 8, dtype=torch.uint8))

@@ -1,0 +1,413 @@
+"""GPU parity of every stage against the CPU oracle, at sizes the oracle
+finishes in seconds that still span several tiles and a ragged tail, plus the
+edge cases: ragged and empty requests, every token a candidate, all-equal
+scores, negative weights, padded selections, empty row lists.
+
+Integer stages (compact keys, candidates, top-k positions and scores, slot
+resolution, gathered bytes) must match bit for bit; attention within 2e-2
+(bf16 output) and 1e-4 (fp32 log-sum-exp)."""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from top_sparse_attention_ls_amd import synth
+from tests.gpu_common import (OUT_TOL, LSE_TOL, np_, bits, bf16_to_f64, oracle_cand,
+                              oracle_topk, poison_, assert_attention_close)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+TINY = synth.WORKLOADS["tiny-4k"]
+SHRUNK = dataclasses.replace(synth.WORKLOADS["decode-128k-b32"], name="shrunk-128k", batch=3,
+                             ctx=8192 + 37, n_cand=1024, topk=256, planted=82, hot_slots=512)
+
+
+def idx_inputs(wl, ctx_len=None, device="cpu"):
+    return synth.indexer_inputs(wl, device, ctx_len=ctx_len)
+
+
+# ------------------------------------------------------------------ pack --
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_pack_coarse_bit_exact(ls, D):
+    g = torch.Generator().manual_seed(D)
+    k = torch.randint(-128, 128, (777, D), generator=g, dtype=torch.int32).to(torch.int8)
+    k[0, :] = torch.arange(-128, 128, dtype=torch.int32)[:D].to(torch.int8)
+    k[1, :] = torch.arange(-128, 128, dtype=torch.int32)[-D:].to(torch.int8)
+    got = np_(ls.pack_coarse(k.to(DEV)))
+    assert np.array_equal(got, orc.pack_coarse(k.numpy()))
+
+
+# -------------------------------------------------- coarse + candidates --
+
+def run_coarse_case(ls, inp, ctx_len, C):
+    q, w, keys = inp["q"], inp["w"], inp["keys"]
+    kc = ls.pack_coarse(keys.to(DEV))
+    cl = torch.tensor(ctx_len, dtype=torch.int32, device=DEV)
+    cand = ls.index_coarse(q.to(DEV), w.to(DEV), kc, cl, C)
+    got = np_(cand)
+    for b in range(q.shape[0]):
+        exp = oracle_cand(q[b].numpy(), w[b].numpy(), keys[b].numpy(), ctx_len[b], C)
+        assert got[b].tolist() == exp.tolist(), "request %d" % b
+    return got
+
+
+def test_index_coarse_tiny(ls):
+    inp = idx_inputs(TINY)
+    got = run_coarse_case(ls, inp, [TINY.ctx], TINY.n_cand)
+    # planted tokens are strong: all of them are candidates
+    planted = set(inp["planted"][0].tolist())
+    assert planted <= set(got[0].tolist())
+
+
+def test_index_coarse_shrunk_ragged(ls):
+    ctx = [SHRUNK.ctx, 5000, 700]            # full (ragged tail), partial, fewer than C
+    inp = idx_inputs(SHRUNK, ctx_len=ctx)
+    run_coarse_case(ls, inp, ctx, SHRUNK.n_cand)
+
+
+def test_index_coarse_empty_and_tiny_requests(ls):
+    wl = dataclasses.replace(SHRUNK, batch=4, ctx=3000)
+    ctx = [0, 1, 63, 3000]
+    inp = idx_inputs(wl, ctx_len=ctx)
+    got = run_coarse_case(ls, inp, ctx, 1024)
+    assert got[0].tolist() == [-1] * 1024
+    assert got[1].tolist() == [0] + [-1] * 1023
+
+
+def test_index_coarse_all_equal_scores(ls):
+    # every key identical: every score ties, the lowest positions win
+    wl = dataclasses.replace(SHRUNK, batch=2, ctx=20000)
+    inp = idx_inputs(wl)
+    inp["keys"][:] = inp["keys"][:, :1, :]
+    got = run_coarse_case(ls, inp, [20000, 20000], 1024)
+    assert got[0].tolist() == list(range(1024))
+
+
+def test_index_coarse_few_distinct_scores(ls):
+    # keys drawn from 3 patterns: huge tie groups cross the threshold
+    wl = dataclasses.replace(SHRUNK, batch=2, ctx=12000)
+    inp = idx_inputs(wl)
+    g = torch.Generator().manual_seed(3)
+    pick = torch.randint(0, 3, (2, 12000), generator=g)
+    for b in range(2):
+        inp["keys"][b] = inp["keys"][b, :3][pick[b]]
+    run_coarse_case(ls, inp, [12000, 11111], 1000)
+
+
+def test_index_coarse_negative_weights(ls):
+    wl = dataclasses.replace(SHRUNK, batch=2, ctx=9000)
+    inp = idx_inputs(wl)
+    g = torch.Generator().manual_seed(4)
+    inp["w"] = torch.randint(-128, 128, inp["w"].shape, generator=g, dtype=torch.int32).to(torch.int8)
+    run_coarse_case(ls, inp, [9000, 8999], 777)
+
+
+@pytest.mark.parametrize("H,D", [(4, 64), (20, 64), (33, 128), (64, 64)])
+def test_index_coarse_head_shapes(ls, H, D):
+    wl = dataclasses.replace(SHRUNK, batch=2, ctx=6000, idx_heads=H, idx_dim=D)
+    inp = idx_inputs(wl)
+    run_coarse_case(ls, inp, [6000, 4321], 500)
+
+
+def test_index_coarse_every_token_a_candidate(ls):
+    wl = dataclasses.replace(SHRUNK, batch=2, ctx=3000)
+    inp = idx_inputs(wl)
+    got = run_coarse_case(ls, inp, [3000, 2000], 4096)
+    assert got[0].tolist()[:3000] == list(range(3000))
+
+
+# ------------------------------------------------------ refine + top-k --
+
+def run_refine_case(ls, inp, ctx_len, C, K):
+    q, w, keys = inp["q"], inp["w"], inp["keys"]
+    B = q.shape[0]
+    cands = np.stack([oracle_cand(q[b].numpy(), w[b].numpy(), keys[b].numpy(), ctx_len[b], C)
+                      for b in range(B)])
+    cl = torch.tensor(ctx_len, dtype=torch.int32, device=DEV)
+    tk, sc = ls.refine_topk(q.to(DEV), w.to(DEV), keys.to(DEV), torch.from_numpy(cands).to(DEV),
+                            cl, K)
+    tk, sc = np_(tk), np_(sc)
+    for b in range(B):
+        ep, es = oracle_topk(q[b].numpy(), w[b].numpy(), keys[b].numpy(), cands[b], K)
+        assert tk[b].tolist() == ep.tolist(), "request %d positions" % b
+        assert sc[b].tolist() == es.tolist(), "request %d scores" % b
+    return tk
+
+
+def test_refine_topk_tiny(ls):
+    inp = idx_inputs(TINY)
+    tk = run_refine_case(ls, inp, [TINY.ctx], TINY.n_cand, TINY.topk)
+    assert set(inp["planted"][0].tolist()) <= set(tk[0].tolist())
+
+
+def test_refine_topk_shrunk_ragged(ls):
+    ctx = [SHRUNK.ctx, 3000, 200]
+    inp = idx_inputs(SHRUNK, ctx_len=ctx)
+    run_refine_case(ls, inp, ctx, SHRUNK.n_cand, SHRUNK.topk)
+
+
+def test_refine_topk_k_above_candidates(ls):
+    wl = dataclasses.replace(SHRUNK, batch=2, ctx=5000)
+    inp = idx_inputs(wl)
+    run_refine_case(ls, inp, [5000, 100], 300, 400)
+
+
+def test_refine_topk_ties(ls):
+    wl = dataclasses.replace(SHRUNK, batch=2, ctx=6000)
+    inp = idx_inputs(wl)
+    g = torch.Generator().manual_seed(5)
+    pick = torch.randint(0, 4, (2, 6000), generator=g)
+    for b in range(2):
+        inp["keys"][b] = inp["keys"][b, :4][pick[b]]
+    run_refine_case(ls, inp, [6000, 6000], 2000, 333)
+
+
+def test_full_candidates_equal_exact_topk_gpu(ls):
+    # C = all tokens: the GPU coarse-to-fine result equals the exact top-k
+    wl = dataclasses.replace(SHRUNK, batch=2, ctx=4000)
+    inp = idx_inputs(wl)
+    q, w, keys = inp["q"], inp["w"], inp["keys"]
+    cl = torch.tensor([4000, 4000], dtype=torch.int32, device=DEV)
+    cand = ls.index_coarse(q.to(DEV), w.to(DEV), ls.pack_coarse(keys.to(DEV)), cl, 4000)
+    tk, sc = ls.refine_topk(q.to(DEV), w.to(DEV), keys.to(DEV), cand, cl, 128)
+    for b in range(2):
+        fine = orc.index_scores(q[b].numpy(), w[b].numpy(), keys[b].numpy(), False)
+        ep, es = orc.select_top(fine, np.arange(4000, dtype=np.int32), 128)
+        assert np_(tk)[b].tolist() == ep.tolist()
+        assert np_(sc)[b].tolist() == es.tolist()
+
+
+# ---------------------------------------------------------- hot buffer --
+
+def test_hot_gather_parity(ls):
+    wl = dataclasses.replace(SHRUNK, batch=3, ctx=3000, topk=200, hot_slots=256, miss_rate=0.3)
+    g = torch.Generator().manual_seed(6)
+    sel = torch.full((3, 200), -1, dtype=torch.int32)
+    counts = [200, 150, 0]
+    for b, c in enumerate(counts):
+        sel[b, :c] = torch.sort(torch.randperm(3000, generator=g)[:c]).values.to(torch.int32)
+    pool = synth.kv_pool(wl, "cpu")
+    pos2slot, hot, n_miss = synth.hot_fill(wl, sel, pool, "cpu")
+    hot_dev = hot.to(DEV)
+    rows, nm = ls.hot_gather(sel.to(DEV), pos2slot.to(DEV), hot_dev, pool.to(DEV), 256)
+    rows, nm = np_(rows), np_(nm)
+    hot_np = bits(hot).reshape(3, 456, 576).copy()
+    pool_np = bits(pool)
+    for b in range(3):
+        n_sel = counts[b]
+        e_rows, e_miss = orc.hot_resolve(np_(sel[b])[:n_sel], np_(pos2slot[b]), 256)
+        assert rows[b].tolist() == e_rows.tolist() + [-1] * (200 - n_sel)
+        assert nm[b] == len(e_miss) == n_miss[b]
+        orc.hot_gather(pool_np[b], e_miss, hot_np[b], 256)
+    assert np.array_equal(bits(hot_dev).reshape(3, 456, 576), hot_np)
+
+
+def test_hot_gather_from_pinned_host_pool(ls):
+    wl = dataclasses.replace(SHRUNK, batch=2, ctx=2000, topk=64, hot_slots=64, miss_rate=0.5)
+    g = torch.Generator().manual_seed(7)
+    sel = torch.stack([torch.sort(torch.randperm(2000, generator=g)[:64]).values
+                       for _ in range(2)]).to(torch.int32)
+    pool = synth.kv_pool(wl, "cpu", pin=True)
+    pos2slot, hot, n_miss = synth.hot_fill(wl, sel, pool, "cpu")
+    hot_dev = hot.to(DEV)
+    rows, nm = ls.hot_gather(sel.to(DEV), pos2slot.to(DEV), hot_dev, pool, 64)
+    torch.cuda.synchronize()
+    for b in range(2):
+        for i in range(64):
+            r = int(np_(rows)[b, i])
+            assert torch.equal(hot_dev[b, r].cpu(), pool[b, int(sel[b, i])])
+    assert np_(nm).tolist() == n_miss
+
+
+# ----------------------------------------------------------- attention --
+
+def mla_case(B, Hq, n_rows, K, S, seed):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, Hq, 576, generator=g).to(torch.bfloat16)
+    kv = torch.randn(B, S + K, 576, generator=g).to(torch.bfloat16)
+    rows = torch.full((B, K), -1, dtype=torch.int32)
+    for b in range(B):
+        rows[b, :n_rows[b]] = torch.randperm(S + K, generator=g)[:n_rows[b]].to(torch.int32)
+    return q, kv, rows
+
+
+def oracle_mla(q, kv, rows, scale):
+    B, Hq, _ = q.shape
+    outs, lses = [], []
+    for b in range(B):
+        o, l_ = orc.attention(bits(q[b]), bits(kv[b]).reshape(-1), bits(kv[b]).reshape(-1),
+                              np_(rows[b]), scale, 1, 512, 576, 0)
+        outs.append(o)
+        lses.append(l_)
+    return np.stack(outs), np.stack(lses)
+
+
+@pytest.mark.parametrize("Hq,n_splits", [(128, 0), (128, 1), (128, 3), (64, 0), (16, 2),
+                                         (48, 5)])
+def test_attention_mla_parity(ls, Hq, n_splits):
+    B, K, S = 3, 256, 300
+    q, kv, rows = mla_case(B, Hq, [256, 161, 1], K, S, seed=Hq + n_splits)
+    scale = 1 / math.sqrt(192)
+    kvd = kv.to(DEV)
+    out, lse = ls.sparse_attn_decode(q.to(DEV), kvd, kvd, rows.to(DEV), scale, 1, 512, S + K,
+                                     576, n_splits=n_splits)
+    e_out, e_lse = oracle_mla(q, kv, rows, scale)
+    assert_attention_close(out, lse, e_out, e_lse, "mla Hq=%d splits=%d" % (Hq, n_splits))
+
+
+def test_attention_mla_all_rows_equal_dense(ls):
+    # k >= context: sparse attention over every row equals dense attention
+    B, Hq, L = 2, 32, 200
+    g = torch.Generator().manual_seed(9)
+    q = torch.randn(B, Hq, 576, generator=g).to(torch.bfloat16)
+    kv = torch.randn(B, L, 576, generator=g).to(torch.bfloat16)
+    rows = torch.arange(L, dtype=torch.int32).repeat(B, 1)
+    kvd = kv.to(DEV)
+    out, lse = ls.sparse_attn_decode(q.to(DEV), kvd, kvd, rows.to(DEV), 0.07, 1, 512, L, 576)
+    qf, kf = q.double(), kv.double()
+    s = 0.07 * torch.einsum("bhd,bnd->bhn", qf, kf)
+    e_out = torch.einsum("bhn,bnd->bhd", torch.softmax(s, -1), kf[:, :, :512]).numpy()
+    e_lse = torch.logsumexp(s, -1).numpy()
+    assert_attention_close(out, lse, e_out, e_lse, "dense")
+
+
+def test_attention_mla_edge_rows(ls):
+    B, Hq, K, S = 3, 16, 64, 10
+    q, kv, rows = mla_case(B, Hq, [0, 1, 64], K, S, seed=11)
+    rows[1, 0] = 4
+    kvd = kv.to(DEV)
+    out, lse = ls.sparse_attn_decode(q.to(DEV), kvd, kvd, rows.to(DEV), 0.1, 1, 512, S + K, 576,
+                                     n_splits=2)
+    o = np_(out.float())
+    assert np.all(o[0] == 0) and np.all(np.isneginf(np_(lse)[0]))
+    # one row: the output is that row's V exactly, lse = its score
+    assert torch.equal(out[1].cpu(), kv[1, 4, :512].expand(Hq, 512))
+    e_out, e_lse = oracle_mla(q, kv, rows, 0.1)
+    assert_attention_close(out[1:], lse[1:], e_out[1:], e_lse[1:], "edge")
+
+
+@pytest.mark.parametrize("Hq,n_kv,D", [(8, 8, 64), (8, 2, 64), (4, 1, 128), (6, 3, 32)])
+def test_attention_mha_parity(ls, Hq, n_kv, D):
+    B, L, K = 2, 300, 128
+    g = torch.Generator().manual_seed(Hq * 7 + n_kv)
+    q = torch.randn(B, Hq, D, generator=g).to(torch.bfloat16)
+    Kc = torch.randn(B, L, n_kv, D, generator=g).to(torch.bfloat16)
+    Vc = torch.randn(B, L, n_kv, D, generator=g).to(torch.bfloat16)
+    rows = torch.full((B, K), -1, dtype=torch.int32)
+    rows[0] = torch.sort(torch.randperm(L, generator=g)[:K]).values.to(torch.int32)
+    rows[1, :50] = torch.sort(torch.randperm(L, generator=g)[:50]).values.to(torch.int32)
+    out, lse = ls.sparse_attn_decode(q.to(DEV), Kc.to(DEV), Vc.to(DEV), rows.to(DEV), 0.125, n_kv,
+                                     D, L, n_kv * D, D)
+    e_out, e_lse = [], []
+    for b in range(B):
+        o, l_ = orc.attention(bits(q[b]), bits(Kc[b]).reshape(-1), bits(Vc[b]).reshape(-1),
+                              np_(rows[b]), 0.125, n_kv, D, n_kv * D, D)
+        e_out.append(o)
+        e_lse.append(l_)
+    assert_attention_close(out, lse, np.stack(e_out), np.stack(e_lse), "mha")
+
+
+# --------------------------------------------------------- whole step --
+
+def test_decode_step_tiny_mha(ls):
+    wl = TINY
+    inp = idx_inputs(wl)
+    qa = synth.attention_query(wl, "cpu")
+    Kc, Vc = synth.kv_cache_mha(wl, "cpu")
+    step = ls.DecodeStep(batch=1, max_ctx=wl.ctx, idx_heads=wl.idx_heads, idx_dim=wl.idx_dim,
+                         n_cand=wl.n_cand, topk=wl.topk, q_heads=wl.q_heads, qk_dim=wl.qk_dim,
+                         v_dim=wl.v_dim, scale=wl.scale, kv_heads=wl.kv_heads,
+                         kv_row_stride=wl.kv_heads * wl.qk_dim, kv_head_stride=wl.qk_dim)
+    for t in (step.cand, step.topk, step.topk_score, step.out, step.lse):
+        poison_(t)
+    keys = inp["keys"].to(DEV)
+    cl = torch.tensor([wl.ctx], dtype=torch.int32, device=DEV)
+    out, lse = step.run(q_idx=inp["q"].to(DEV), w_idx=inp["w"].to(DEV), kc=ls.pack_coarse(keys),
+                        k8=keys, ctx_len=cl, q_attn=qa.to(DEV), k_cache=Kc.to(DEV),
+                        v_cache=Vc.to(DEV))
+    r = orc.decode_request(inp["q"][0].numpy(), inp["w"][0].numpy(), inp["keys"][0].numpy(),
+                           wl.ctx, wl.n_cand, wl.topk, bits(qa[0]), wl.scale,
+                           k_cache_bits=bits(Kc[0]).reshape(-1),
+                           v_cache_bits=bits(Vc[0]).reshape(-1), n_kv_heads=wl.kv_heads,
+                           v_dim=wl.v_dim, row_stride=wl.kv_heads * wl.qk_dim,
+                           head_stride=wl.qk_dim)
+    assert np_(step.cand)[0].tolist() == r["cand"].tolist()
+    assert np_(step.topk)[0].tolist() == r["topk"].tolist()
+    assert np_(step.topk_score)[0].tolist() == r["topk_score"].tolist()
+    assert_attention_close(out, lse, r["out"][None], r["lse"][None], "tiny step")
+
+
+def mla_step_case(ls, wl, ctx_len, device_pool=True):
+    B = wl.batch
+    inp = idx_inputs(wl, ctx_len=ctx_len)
+    qa = synth.attention_query(wl, "cpu")
+    pool = synth.kv_pool(wl, "cpu")
+    sel = []
+    for b in range(B):
+        cand = oracle_cand(inp["q"][b].numpy(), inp["w"][b].numpy(), inp["keys"][b].numpy(),
+                           ctx_len[b], wl.n_cand)
+        tk, _ = oracle_topk(inp["q"][b].numpy(), inp["w"][b].numpy(), inp["keys"][b].numpy(),
+                            cand, wl.topk)
+        sel.append(torch.from_numpy(tk))
+    pos2slot, hot, n_miss = synth.hot_fill(wl, torch.stack(sel), pool, "cpu")
+    step = ls.DecodeStep(batch=B, max_ctx=wl.ctx, idx_heads=wl.idx_heads, idx_dim=wl.idx_dim,
+                         n_cand=wl.n_cand, topk=wl.topk, q_heads=wl.q_heads, qk_dim=wl.qk_dim,
+                         v_dim=wl.v_dim, scale=wl.scale, hot_slots=wl.hot_slots)
+    for t in (step.cand, step.topk, step.topk_score, step.rows, step.n_miss, step.out, step.lse):
+        poison_(t)
+    keys = inp["keys"].to(DEV)
+    hot_dev = hot.to(DEV)
+    cl = torch.tensor(ctx_len, dtype=torch.int32, device=DEV)
+    out, lse = step.run(q_idx=inp["q"].to(DEV), w_idx=inp["w"].to(DEV), kc=ls.pack_coarse(keys),
+                        k8=keys, ctx_len=cl, q_attn=qa.to(DEV), pos2slot=pos2slot.to(DEV),
+                        hot_kv=hot_dev, pool_kv=pool.to(DEV))
+    torch.cuda.synchronize()
+    for b in range(B):
+        hot_b = bits(hot[b]).copy()
+        r = orc.decode_request(inp["q"][b].numpy(), inp["w"][b].numpy(), inp["keys"][b].numpy(),
+                               ctx_len[b], wl.n_cand, wl.topk, bits(qa[b]), wl.scale,
+                               pos2slot=np_(pos2slot[b]), hot_bits=hot_b, pool_bits=bits(pool[b]))
+        assert np_(step.cand)[b].tolist() == r["cand"].tolist(), b
+        assert np_(step.topk)[b].tolist() == r["topk"].tolist(), b
+        assert np_(step.topk_score)[b].tolist() == r["topk_score"].tolist(), b
+        assert np_(step.rows)[b].tolist() == r["rows"].tolist(), b
+        assert int(np_(step.n_miss)[b]) == r["n_miss"] == n_miss[b], b
+        assert np.array_equal(bits(hot_dev[b]), hot_b), b
+        assert_attention_close(out[b:b + 1], lse[b:b + 1], r["out"][None], r["lse"][None],
+                               "request %d" % b)
+    return step
+
+
+def test_decode_step_shrunk_mla(ls):
+    wl = dataclasses.replace(SHRUNK, batch=3, ctx=16384 + 5, n_cand=2048, topk=512,
+                             hot_slots=1024, planted=163)
+    mla_step_case(ls, wl, [wl.ctx, 9000, 300])
+
+
+def test_decode_step_deterministic(ls):
+    wl = dataclasses.replace(SHRUNK, batch=2, ctx=9000, n_cand=1024, topk=256, hot_slots=300)
+    inp = idx_inputs(wl)
+    qa = synth.attention_query(wl, DEV)
+    pool = synth.kv_pool(wl, DEV)
+    sel = torch.stack([torch.arange(256, dtype=torch.int32) * 30 for _ in range(2)])
+    pos2slot, hot, _ = synth.hot_fill(wl, sel, pool, DEV)
+    step = ls.DecodeStep(batch=2, max_ctx=wl.ctx, idx_heads=64, idx_dim=128, n_cand=1024,
+                         topk=256, q_heads=128, qk_dim=576, v_dim=512, scale=wl.scale,
+                         hot_slots=300)
+    keys = inp["keys"].to(DEV)
+    kc = ls.pack_coarse(keys)
+    cl = torch.tensor([9000, 9000], dtype=torch.int32, device=DEV)
+    results = []
+    for _ in range(3):
+        out, lse = step.run(q_idx=inp["q"].to(DEV), w_idx=inp["w"].to(DEV), kc=kc, k8=keys,
+                            ctx_len=cl, q_attn=qa, pos2slot=pos2slot, hot_kv=hot, pool_kv=pool)
+        results.append([t.clone() for t in (step.cand, step.topk, step.topk_score, step.rows,
+                                            step.n_miss, out.view(torch.int16), lse)])
+    for r in results[1:]:
+        for a, b_ in zip(results[0], r):
+            assert torch.equal(a, b_)

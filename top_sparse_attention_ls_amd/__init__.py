@@ -1,0 +1,303 @@
+"""Python binding of libls.so, the gfx950 sparse-decode library.
+
+Argument marshalling only: every function here turns torch tensors into
+device pointers and the current torch stream into a hipStream_t, and calls
+the C-ABI declared in include/ls.h.  All computation happens in the HIP
+kernels; there is no CPU fallback.  If the library is missing, load() raises.
+
+Stages (see include/ls.h for the exact contracts):
+  pack_coarse          compact 4-bit indexer keys (run when keys are appended)
+  index_coarse         coarse scores of every token -> n_cand candidates
+  refine_topk          exact int8 scores of the candidates -> top-k
+  hot_gather           resolve against the hot buffer, copy misses from the pool
+  sparse_attn_decode   attention over the selected rows
+  DecodeStep           the whole step, one call
+  prefill_index_topk / prefill_stream_layers   prefill-chunk indexer
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libls.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "ls.h")
+
+LS_OK, LS_E_ARG, LS_E_UNSUPPORTED, LS_E_WORKSPACE, LS_E_HIP = 0, -1, -2, -3, -4
+OP_COARSE, OP_REFINE, OP_HOT, OP_ATTN, OP_STEP, OP_PREFILL = 1, 2, 3, 4, 5, 6
+STEP_EVENTS = 7
+
+_I32, _I64, _F32, _P = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+
+
+class IdxDesc(ctypes.Structure):
+    _fields_ = [(n, _I32) for n in ("batch", "max_ctx", "n_heads", "head_dim", "n_cand", "topk")]
+
+
+class HotDesc(ctypes.Structure):
+    _fields_ = [(n, _I32) for n in ("batch", "max_ctx", "topk", "hot_slots", "row_elems",
+                                    "pool_on_host")]
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = ([(n, _I32) for n in ("batch", "n_q_heads", "n_kv_heads", "qk_dim", "v_dim",
+                                     "topk")]
+                + [(n, _I64) for n in ("kv_rows_per_req", "kv_row_stride", "kv_head_stride")]
+                + [("scale", _F32), ("n_splits", _I32)])
+
+
+class StepDesc(ctypes.Structure):
+    _fields_ = [("idx", IdxDesc), ("hot", HotDesc), ("attn", AttnDesc), ("use_hot", _I32)]
+
+
+class StepIO(ctypes.Structure):
+    _fields_ = [(n, _P) for n in (
+        "q_idx_dev", "w_idx_dev", "kc_dev", "k8_dev", "ctx_len_dev", "cand_dev", "topk_dev",
+        "topk_score_dev", "pos2slot_dev", "hot_kv_dev", "pool_kv_dev", "rows_dev", "n_miss_dev",
+        "q_attn_dev", "k_cache_dev", "v_cache_dev", "out_dev", "lse_dev", "stage_events")]
+
+
+class PrefillDesc(ctypes.Structure):
+    _fields_ = [(n, _I32) for n in ("n_query", "max_ctx", "q_pos0", "n_heads", "head_dim",
+                                    "topk")]
+
+
+_lib = None
+
+
+def load():
+    """Load libls.so (built in-tree by build()).  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libls.so not built (%s); run python -m "
+                           "top_sparse_attention_ls_amd.build" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    L.ls_abi_version.restype = _I32
+    L.ls_last_error.restype = ctypes.c_char_p
+    L.ls_last_hip_error.restype = _I32
+    L.ls_workspace_size.argtypes = [_I32, _P]
+    L.ls_workspace_size.restype = ctypes.c_size_t
+    L.ls_workspace_init.argtypes = [_P, ctypes.c_size_t, _P]
+    L.ls_pack_coarse.argtypes = [_P, _P, _I64, _I32, _P]
+    L.ls_index_coarse.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    L.ls_refine_topk.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    L.ls_hot_gather.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    L.ls_sparse_attn_decode.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    L.ls_decode_step.argtypes = [_P, _P, _P, ctypes.c_size_t, _P]
+    L.ls_prefill_index_topk.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    L.ls_prefill_stream_layers.argtypes = [_P, _I32, _P, _P, _P, _P, _P, _P, _P,
+                                           ctypes.c_size_t, _P, _P]
+    for name in ("ls_pack_coarse", "ls_index_coarse", "ls_refine_topk", "ls_hot_gather",
+                 "ls_sparse_attn_decode", "ls_decode_step", "ls_prefill_index_topk",
+                 "ls_prefill_stream_layers", "ls_workspace_init"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def header_symbols() -> list:
+    """Names of every function declared in include/ls.h."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ls_[a-z0-9_]+)\s*\(", text)))
+
+
+class LSError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("libls error %d: %s" % (code, msg))
+        self.code = code
+
+
+def _check(rc):
+    if rc != LS_OK:
+        raise LSError(rc, load().ls_last_error().decode())
+
+
+def last_error() -> str:
+    return load().ls_last_error().decode()
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+# ---------------------------------------------------------------- workspace --
+
+_ws_cache = {}
+
+
+def workspace_size(op: int, desc) -> int:
+    n = load().ls_workspace_size(op, ctypes.byref(desc))
+    if n == 0:
+        raise LSError(LS_E_ARG, last_error())
+    return n
+
+
+def workspace(op: int, desc, device) -> torch.Tensor:
+    """A cleared workspace for (op, shapes), cached per device."""
+    key = (op, bytes(desc), str(device))
+    ws = _ws_cache.get(key)
+    if ws is None:
+        n = workspace_size(op, desc)
+        ws = torch.empty(n, dtype=torch.uint8, device=device)
+        _check(load().ls_workspace_init(_p(ws), n, _stream()))
+        _ws_cache[key] = ws
+    return ws
+
+
+def new_workspace(op: int, desc, device) -> torch.Tensor:
+    n = workspace_size(op, desc)
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    _check(load().ls_workspace_init(_p(ws), n, _stream()))
+    return ws
+
+
+# ------------------------------------------------------------------- stages --
+
+def pack_coarse(k8: torch.Tensor) -> torch.Tensor:
+    """[..., D] int8 keys -> [..., D/2] uint8 compact keys."""
+    _need(k8, torch.int8, "k8")
+    d = k8.shape[-1]
+    kc = torch.empty(k8.shape[:-1] + (d // 2,), dtype=torch.uint8, device=k8.device)
+    _check(load().ls_pack_coarse(_p(k8), _p(kc), k8.numel() // d, d, _stream()))
+    return kc
+
+
+def idx_desc(q, keys_like_rows: int, n_cand: int, topk: int) -> IdxDesc:
+    B, H, D = q.shape
+    return IdxDesc(B, keys_like_rows, H, D, n_cand, topk)
+
+
+def index_coarse(q, w, kc, ctx_len, n_cand: int, topk: int = 1, ws=None) -> torch.Tensor:
+    """q [B,H,D] int8, w [B,H] int8, kc [B,L,D/2] uint8, ctx_len [B] int32."""
+    _need(q, torch.int8, "q"), _need(w, torch.int8, "w"), _need(kc, torch.uint8, "kc")
+    _need(ctx_len, torch.int32, "ctx_len")
+    d = idx_desc(q, kc.shape[1], n_cand, topk)
+    ws = workspace(OP_COARSE, d, q.device) if ws is None else ws
+    cand = torch.empty((q.shape[0], n_cand), dtype=torch.int32, device=q.device)
+    _check(load().ls_index_coarse(ctypes.byref(d), _p(q), _p(w), _p(kc), _p(ctx_len), _p(cand),
+                                  _p(ws), ws.numel(), _stream()))
+    return cand
+
+
+def refine_topk(q, w, k8, cand, ctx_len, topk: int, ws=None):
+    """Returns (topk [B,topk] int32, scores [B,topk] int64)."""
+    _need(q, torch.int8, "q"), _need(w, torch.int8, "w"), _need(k8, torch.int8, "k8")
+    _need(cand, torch.int32, "cand"), _need(ctx_len, torch.int32, "ctx_len")
+    d = idx_desc(q, k8.shape[1], cand.shape[1], topk)
+    ws = workspace(OP_REFINE, d, q.device) if ws is None else ws
+    out = torch.empty((q.shape[0], topk), dtype=torch.int32, device=q.device)
+    sc = torch.empty((q.shape[0], topk), dtype=torch.int64, device=q.device)
+    _check(load().ls_refine_topk(ctypes.byref(d), _p(q), _p(w), _p(k8), _p(cand), _p(ctx_len),
+                                 _p(out), _p(sc), _p(ws), ws.numel(), _stream()))
+    return out, sc
+
+
+def hot_gather(topk, pos2slot, hot, pool, hot_slots: int, ws=None):
+    """topk [B,K] int32, pos2slot [B,L] int32, hot [B,S+K,row] bf16 (updated in
+    place), pool [B,L,row] bf16 (device or pinned host).  Returns (rows, n_miss)."""
+    _need(topk, torch.int32, "topk"), _need(pos2slot, torch.int32, "pos2slot")
+    _need(hot, torch.bfloat16, "hot"), _need(pool, torch.bfloat16, "pool")
+    B, K = topk.shape
+    d = HotDesc(B, pool.shape[1], K, hot_slots, hot.shape[2], 0 if pool.is_cuda else 1)
+    ws = workspace(OP_HOT, d, topk.device) if ws is None else ws
+    rows = torch.empty((B, K), dtype=torch.int32, device=topk.device)
+    n_miss = torch.empty((B,), dtype=torch.int32, device=topk.device)
+    _check(load().ls_hot_gather(ctypes.byref(d), _p(topk), _p(pos2slot), _p(hot), _p(pool),
+                                _p(rows), _p(n_miss), _p(ws), ws.numel(), _stream()))
+    return rows, n_miss
+
+
+def attn_desc(q, topk: int, n_kv_heads: int, v_dim: int, kv_rows_per_req: int,
+              kv_row_stride: int, kv_head_stride: int, scale: float, n_splits: int = 0):
+    B, Hq, dqk = q.shape
+    return AttnDesc(B, Hq, n_kv_heads, dqk, v_dim, topk, kv_rows_per_req, kv_row_stride,
+                    kv_head_stride, float(scale), n_splits)
+
+
+def sparse_attn_decode(q, k_base, v_base, rows, scale: float, n_kv_heads: int, v_dim: int,
+                       kv_rows_per_req: int, kv_row_stride: int, kv_head_stride: int = 0,
+                       n_splits: int = 0, ws=None):
+    """q [B,Hq,qk_dim] bf16; rows [B,K] int32 (-1 ends a list).  K/V element
+    (b, row r, kv head g, d) sits at base[(b*kv_rows_per_req + r)*kv_row_stride
+    + g*kv_head_stride + d].  Returns (out [B,Hq,v_dim] bf16, lse [B,Hq] f32)."""
+    _need(q, torch.bfloat16, "q"), _need(rows, torch.int32, "rows")
+    d = attn_desc(q, rows.shape[1], n_kv_heads, v_dim, kv_rows_per_req, kv_row_stride,
+                  kv_head_stride, scale, n_splits)
+    ws = workspace(OP_ATTN, d, q.device) if ws is None else ws
+    B, Hq, _ = q.shape
+    out = torch.empty((B, Hq, v_dim), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check(load().ls_sparse_attn_decode(ctypes.byref(d), _p(q), _p(k_base), _p(v_base), _p(rows),
+                                        _p(out), _p(lse), _p(ws), ws.numel(), _stream()))
+    return out, lse
+
+
+class DecodeStep:
+    """One layer's decode step over a batch: fixed shapes, own workspace and
+    output buffers.  run() enqueues the whole step on the current stream."""
+
+    def __init__(self, *, batch, max_ctx, idx_heads, idx_dim, n_cand, topk, q_heads, qk_dim,
+                 v_dim, scale, hot_slots=0, kv_heads=1, kv_row_stride=None, kv_head_stride=0,
+                 pool_on_host=False, n_splits=0, device="cuda"):
+        self.use_hot = hot_slots > 0
+        idx = IdxDesc(batch, max_ctx, idx_heads, idx_dim, n_cand, topk)
+        row = qk_dim
+        if self.use_hot:
+            hot = HotDesc(batch, max_ctx, topk, hot_slots, row, 1 if pool_on_host else 0)
+            attn = AttnDesc(batch, q_heads, 1, qk_dim, v_dim, topk, hot_slots + topk, row, 0,
+                            float(scale), n_splits)
+        else:
+            hot = HotDesc(0, 0, 0, 0, 0, 0)
+            stride = kv_row_stride if kv_row_stride is not None else kv_heads * qk_dim
+            attn = AttnDesc(batch, q_heads, kv_heads, qk_dim, v_dim, topk, max_ctx, stride,
+                            kv_head_stride, float(scale), n_splits)
+        self.desc = StepDesc(idx, hot, attn, 1 if self.use_hot else 0)
+        self.device = torch.device(device)
+        self.ws = new_workspace(OP_STEP, self.desc, self.device)
+        dev = self.device
+        self.cand = torch.empty((batch, n_cand), dtype=torch.int32, device=dev)
+        self.topk = torch.empty((batch, topk), dtype=torch.int32, device=dev)
+        self.topk_score = torch.empty((batch, topk), dtype=torch.int64, device=dev)
+        self.rows = torch.empty((batch, topk), dtype=torch.int32, device=dev)
+        self.n_miss = torch.empty((batch,), dtype=torch.int32, device=dev)
+        self.out = torch.empty((batch, q_heads, v_dim), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((batch, q_heads), dtype=torch.float32, device=dev)
+
+    def run(self, *, q_idx, w_idx, kc, k8, ctx_len, q_attn, pos2slot=None, hot_kv=None,
+            pool_kv=None, k_cache=None, v_cache=None, events=None):
+        io = StepIO()
+        io.q_idx_dev, io.w_idx_dev = q_idx.data_ptr(), w_idx.data_ptr()
+        io.kc_dev, io.k8_dev, io.ctx_len_dev = kc.data_ptr(), k8.data_ptr(), ctx_len.data_ptr()
+        io.cand_dev, io.topk_dev = self.cand.data_ptr(), self.topk.data_ptr()
+        io.topk_score_dev = self.topk_score.data_ptr()
+        if self.use_hot:
+            io.pos2slot_dev, io.hot_kv_dev = pos2slot.data_ptr(), hot_kv.data_ptr()
+            io.pool_kv_dev = pool_kv.data_ptr()
+            io.rows_dev, io.n_miss_dev = self.rows.data_ptr(), self.n_miss.data_ptr()
+        else:
+            io.k_cache_dev, io.v_cache_dev = k_cache.data_ptr(), v_cache.data_ptr()
+        io.q_attn_dev = q_attn.data_ptr()
+        io.out_dev, io.lse_dev = self.out.data_ptr(), self.lse.data_ptr()
+        if events is not None:
+            arr = (ctypes.c_void_p * STEP_EVENTS)(*[e.cuda_event for e in events])
+            io.stage_events = ctypes.cast(arr, ctypes.c_void_p)
+        _check(load().ls_decode_step(ctypes.byref(self.desc), ctypes.byref(io), _p(self.ws),
+                                     self.ws.numel(), _stream()))
+        return self.out, self.lse

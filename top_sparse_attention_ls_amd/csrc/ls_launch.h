@@ -1,0 +1,87 @@
+// Internal launch interface between the C-ABI host code (ls_abi.hip) and the
+// kernel translation units.  Every launcher only enqueues on `st` and returns
+// the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ls {
+
+// Histogram of coarse scores: float-like monotone buckets of an int32 score,
+// 6 mantissa bits, both signs (see coarse_bucket in k_index.hip).
+constexpr int kCoarseBins = 3328;
+// Positions handled by one workgroup of the candidate filter.
+constexpr int kSelectChunk = 8192;
+// Tokens scored by one workgroup of the coarse kernel.
+constexpr int kCoarseTokPerWG = 2048;
+// Candidates scored by one workgroup of the refine kernel.
+constexpr int kRefinePerWG = 256;
+
+struct CoarseWS {
+  int32_t* scores;     // [B, max_ctx]
+  uint32_t* hist;      // [B, kCoarseBins]      zero between calls
+  uint32_t* bitmap;    // [B, bitmap_words]
+  int32_t* tie_s;      // [B, max_ctx]
+  int32_t* tie_p;      // [B, max_ctx]
+  uint32_t* ctr;       // [B, 2] tie count, done counter;   zero between calls
+  int bitmap_words;
+};
+
+struct RefineWS {
+  int64_t* fs;         // [B, n_cand]
+  uint32_t* ctr;       // [B] done counter;                 zero between calls
+  int32_t* miss_pos;   // [B, topk]
+};
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+
+hipError_t launch_pack_coarse(const int8_t* k8, uint8_t* kc, int64_t n_rows, int dim,
+                              hipStream_t st);
+
+hipError_t launch_coarse_scores(const int8_t* q, const int8_t* w, const uint8_t* kc,
+                                const int32_t* ctx_len, const CoarseWS& ws, int B, int H,
+                                int D, int max_ctx, hipStream_t st);
+
+hipError_t launch_topc_select(const int32_t* ctx_len, const CoarseWS& ws, int32_t* cand, int B,
+                              int max_ctx, int C, hipStream_t st);
+
+// Refine + top-k; with pos2slot != nullptr also the hot-buffer resolve
+// (rows, n_miss, miss list in ws.miss_pos).
+hipError_t launch_refine_topk(const int8_t* q, const int8_t* w, const int8_t* k8,
+                              const int32_t* cand, const RefineWS& ws, int32_t* topk,
+                              int64_t* topk_score, const int32_t* pos2slot, int32_t* rows,
+                              int32_t* n_miss, int hot_slots, int B, int H, int D, int max_ctx,
+                              int C, int K, hipStream_t st);
+
+hipError_t launch_hot_resolve(const int32_t* topk, const int32_t* pos2slot, int32_t* rows,
+                              int32_t* n_miss, int32_t* miss_pos, int hot_slots, int B,
+                              int max_ctx, int K, hipStream_t st);
+
+hipError_t launch_hot_gather(const int32_t* miss_pos, const int32_t* n_miss, const void* pool,
+                             void* hot, int hot_slots, int B, int max_ctx, int K, int row_elems,
+                             hipStream_t st);
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* rows;
+  uint16_t* out;
+  float* lse;
+  float* part_o;
+  float* part_lse;
+  int B, Hq, n_kv, qk_dim, v_dim, K;
+  int64_t rows_per_req, row_stride, head_stride;
+  float scale;
+  int n_splits;
+};
+
+// Whether the MFMA path serves these shapes (else the generic kernel).
+bool attn_uses_mfma(int Hq, int n_kv, int qk_dim, int v_dim, const void* k, const void* v);
+int attn_auto_splits(int B, int Hq, int K, bool mfma);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
+hipError_t launch_combine(const AttnArgs& a, hipStream_t st);
+
+}  // namespace ls
