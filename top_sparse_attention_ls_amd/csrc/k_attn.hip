@@ -21,38 +21,43 @@ constexpr float kLn2 = 0.6931471805599453f;
 // ---------------------------------------------------------------- MFMA path --
 //
 // Workgroup = NW waves x 16 query heads, one request, one split of the row
-// list.  Rows are staged 32 at a time in LDS twice: row-major (the A operand
-// of S^T = K Q^T, 16 rows x 32 dims per lane group read) and transposed for
-// the first v_dim dims (the A operand of O^T = V^T P^T).  Q stays in VGPRs
-// as the B operand (lane: head n = lane%16, dims 8*(lane/16) .. +8 of each
-// 32-dim step).  The S^T accumulator leaves every lane with 8 scores of its
-// own head (rows 4g..4g+3 and 16+4g..16+4g+3); converted to bf16 they are
-// exactly the B operand of the P.V product when the transposed V tile
-// stores its rows in that same order (slot 8g+e).  O^T accumulates 16 dims x
-// 16 heads per MFMA, so every lane also owns one head's outputs and the
-// softmax rescale is lane-local.
+// list.  Rows are staged 32 at a time in LDS, row-major (padded stride).
+// Q stays in VGPRs as the B operand of S^T = K Q^T (lane: head n = lane%16,
+// dims 8*(lane/16) .. +8 of each 32-dim step); the K tile gives the A
+// operand (16 rows x 8 dims per lane).  The S^T accumulator leaves every
+// lane with 8 scores of its own head, rows 4g..4g+3 and 16+4g..16+4g+3
+// (g = lane/16); converted to bf16 they are the B operand of O^T = V^T P^T
+// with that row order.  The matching A operand -- 8 rows of one V column --
+// comes straight from the row-major tile through the gfx950 LDS transpose
+// read (ds_read_b64_tr_b16): within each 16-lane group, lane j points at
+// row base + j/4, columns 4*(j%4) .. +3, and lane i receives column i of
+// those 4 rows; two such reads (row bases 4g and 16+4g) give the 8 rows.
+// O^T accumulates 16 dims x 16 heads per MFMA, so every lane owns one head's
+// outputs and the online-softmax rescale is lane-local.
 constexpr int kTileR = 32;
 
-__device__ __forceinline__ int vt_slot(int r) {
-  return r < 16 ? 8 * (r >> 2) + (r & 3) : 8 * ((r - 16) >> 2) + 4 + ((r - 16) & 3);
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4i16 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(p));
 }
 
 template <int DQK, int DV, int NW>
-__global__ __launch_bounds__(NW * 64) void k_attn_mfma(
+__global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ rows, uint16_t* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ part_o, float* __restrict__ part_lse, int Hq, int K,
     int64_t rows_per_req, int64_t row_stride, float scale_log2, int n_splits,
     int rows_per_split) {
   constexpr int NT = NW * 64;
-  constexpr int KS = DQK + 8;   // LDS row stride of the K tile (bf16 elements)
-  constexpr int VS = kTileR + 8;  // LDS row stride of the transposed V tile
+  constexpr int KS = DQK + 8;     // LDS row stride of the tile (bf16 elements)
   constexpr int QK_STEPS = DQK / 32;
   constexpr int DT = DV / 16;
-  constexpr int CH = DQK / 8;   // 16-byte chunks per row
+  constexpr int CH = DQK / 8;     // 16-byte chunks per row
+  constexpr int CPT = NT / kTileR;              // chunk lanes per row
+  constexpr int LPT = (CH + CPT - 1) / CPT;     // chunk loads per thread per tile
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kTileR * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t VT[DV * VS];
-  __shared__ uint32_t valid_mask;
 
   const int split = blockIdx.x, b = blockIdx.z;
   const int l = lane_id(), n = l & 15, g = l >> 4;
@@ -77,31 +82,41 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(
   const int i_end = min(i_begin + rows_per_split, K);
   const int32_t* rb = rows + (size_t)b * K;
   const uint16_t* kvb = kv + (size_t)b * rows_per_req * row_stride;
+  // this thread stages row lr of every tile, chunks lc, lc + CPT, ...
+  const int lr = threadIdx.x % kTileR, lc = threadIdx.x / kTileR;
 
   for (int tile0 = i_begin; tile0 < i_end; tile0 += kTileR) {
-    __syncthreads();
-    if (threadIdx.x == 0) valid_mask = 0;
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < kTileR * CH; idx += NT) {
-      const int r = idx % kTileR, c = idx / kTileR;
-      const int i = tile0 + r;
-      const int32_t rid = (i < i_end) ? rb[i] : -1;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (rid >= 0) v = *(const uint4*)(kvb + (size_t)rid * row_stride + 8 * c);
-      if (c == 0 && rid >= 0) atomicOr(&valid_mask, 1u << r);
-      *(uint4*)&Ks[r * KS + 8 * c] = v;
-      if (8 * c < DV) {
-        const int sl = vt_slot(r);
-        const uint16_t e[8] = {(uint16_t)(v.x & 0xFFFF), (uint16_t)(v.x >> 16),
-                               (uint16_t)(v.y & 0xFFFF), (uint16_t)(v.y >> 16),
-                               (uint16_t)(v.z & 0xFFFF), (uint16_t)(v.z >> 16),
-                               (uint16_t)(v.w & 0xFFFF), (uint16_t)(v.w >> 16)};
+    const int i = tile0 + lr;
+    const int32_t rid = (i < i_end) ? rb[i] : -1;
+    // every wave holds rows 0..31 in lanes 0..31: the tile's validity mask
+    const uint32_t vmask = (uint32_t)__ballot(rid >= 0);
+    const uint16_t* src = kvb + (size_t)(rid >= 0 ? rid : 0) * row_stride;
+    // two batches of chunk loads keep the staging registers small: the first
+    // is in flight across the barrier, the second right after it
+    constexpr int LA = (LPT + 1) / 2;
+    uint4 v[LA];
 #pragma unroll
-        for (int k = 0; k < 8; k++) VT[(8 * c + k) * VS + sl] = e[k];
-      }
+    for (int j = 0; j < LA; j++) {
+      const int c = lc + CPT * j;
+      v[j] = (c < CH && rid >= 0) ? *(const uint4*)(src + 8 * c) : make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();  // the previous tile is no longer read
+#pragma unroll
+    for (int j = 0; j < LA; j++) {
+      const int c = lc + CPT * j;
+      if (c < CH) *(uint4*)&Ks[lr * KS + 8 * c] = v[j];
+    }
+#pragma unroll
+    for (int j = LA; j < LPT; j++) {
+      const int c = lc + CPT * j;
+      v[j - LA] = (c < CH && rid >= 0) ? *(const uint4*)(src + 8 * c) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = LA; j < LPT; j++) {
+      const int c = lc + CPT * j;
+      if (c < CH) *(uint4*)&Ks[lr * KS + 8 * c] = v[j - LA];
     }
     __syncthreads();
-    const uint32_t vmask = valid_mask;
 
     // S^T = K Q^T for rows 0..15 and 16..31
     v4f sacc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
@@ -119,8 +134,8 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(
 #pragma unroll
     for (int e = 0; e < 8; e++) {
       const int r = (e < 4) ? 4 * g + e : 16 + 4 * g + (e - 4);
-      const float v = (e < 4) ? sacc[0][e] : sacc[1][e - 4];
-      s[e] = ((vmask >> r) & 1u) ? v * scale_log2 : -INFINITY;
+      const float sv = (e < 4) ? sacc[0][e] : sacc[1][e - 4];
+      s[e] = ((vmask >> r) & 1u) ? sv * scale_log2 : -INFINITY;
       tmax = fmaxf(tmax, s[e]);
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
@@ -142,10 +157,16 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(
     m_run = m_new;  // stays -inf until a valid row appears
     v8u16 pv = {pb[0], pb[1], pb[2], pb[3], pb[4], pb[5], pb[6], pb[7]};
     const v8bf pB = __builtin_bit_cast(v8bf, pv);
+    // transpose-read addresses: lane j of the group -> row base + j/4, cols 4*(j%4)
+    const uint16_t* tr0 = &Ks[(4 * g + (n >> 2)) * KS + 4 * (n & 3)];
+    const uint16_t* tr1 = tr0 + 16 * KS;
 #pragma unroll
     for (int dt = 0; dt < DT; dt++) {
       oacc[dt] *= alpha;
-      v8u16 a = *(const v8u16*)&VT[(16 * dt + n) * VS + 8 * g];
+      const v4i16 a0 = lds_read_tr16(tr0 + 16 * dt);
+      const v4i16 a1 = lds_read_tr16(tr1 + 16 * dt);
+      const v8u16 a = {(uint16_t)a0[0], (uint16_t)a0[1], (uint16_t)a0[2], (uint16_t)a0[3],
+                       (uint16_t)a1[0], (uint16_t)a1[1], (uint16_t)a1[2], (uint16_t)a1[3]};
       oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), pB,
                                                           oacc[dt], 0, 0, 0);
     }

@@ -1,12 +1,9 @@
 // Indexer kernels for gfx950: compact-key packing, coarse scoring on int8
-// MFMA with a fused score histogram, candidate selection, exact refinement
-// with top-k, and the hot-buffer resolve + miss gather.
+// MFMA with a fused score histogram, and the candidate selection.
 //
 // Method: LeanSparse (arXiv 2611.04671), Abstract -- coarse-to-fine indexing
-// scores compact key representations, keeps candidates, and fetches original
-// indexer keys only to refine them.  Hot buffer: XM-Sparse digest, section on
-// the hot buffer -- only selected rows missing from the HBM hot buffer are
-// fetched from the full history.
+// scores compact key representations and keeps candidates; only those are
+// refined with the original indexer keys (k_refine.hip).
 #include "ls_device.h"
 #include "ls_launch.h"
 
@@ -73,12 +70,18 @@ hipError_t launch_pack_coarse(const int8_t* k8, uint8_t* kc, int64_t n_rows, int
 // n is widened to the byte n*16 by masking (x & 0xF0F0F0F0 for the odd
 // elements, (x << 4) & 0xF0F0F0F0 for the even ones), so the MFMA returns
 // 16 * dot exactly; the query is laid out even/odd to match.  Epilogue:
-// max(.,0) >> 4, times the head weight, summed over heads in-lane and then
-// across the four 16-lane groups with a reduce-scatter that leaves one
-// token per lane.  Every lane then buckets its score into an LDS histogram
-// which is flushed to the request's global histogram at the end -- the
-// first pass of the candidate selection, fused here so the scores are not
-// read again to build it.
+// max(.,0) >> 4, times the head weight (24-bit multiply-add), summed over
+// heads in-lane and then across the four 16-lane groups with a
+// reduce-scatter that leaves one token per lane.  Every lane then buckets its
+// score into an LDS histogram that is flushed to the request's global
+// histogram at the end: the first pass of the candidate selection, fused
+// here so that nothing re-reads the scores to build it.
+//
+// Memory: each wave streams 64 tokens (4 KiB of compact keys) per step with
+// one 16-byte load per lane per 16-token tile, and prefetches the next 64
+// tokens into registers before computing the current ones.  Loads past the
+// request's end are clamped to its last token (their results are dropped),
+// so the loop has no divergent branches around memory operations.
 //
 // Exactness: |q.kc| <= 128*127*8 < 2^17, |w| <= 128, <= 16 heads per lane
 // and 4 lane groups: |sum| < 2^31.
@@ -97,27 +100,33 @@ __device__ __forceinline__ uint32_t coarse_bucket(int32_t x) {
                 : (uint32_t)kNBHalf - 1u - mag_bucket((uint32_t)(-(x + 1)));
 }
 
-// Query operand bytes for head h, lane group g, MFMA number mf (see layout
-// notes above).  D = 128: mf 0 holds d = 32g + 2j, mf 1 holds d = 32g+2j+1.
-// D = 64: byte j < 8 holds d = 16g + 2j, byte 8 + j holds d = 16g + 2j + 1.
+// Query operands for head row qh, lane group g.  D = 128: lane group g owns
+// dims [32g, 32g+32); mf 0 holds the even dims, mf 1 the odd ones (byte j =
+// dim 32g + 2j + mf).  D = 64: dims [16g, 16g+16); bytes 0..7 the even
+// dims, bytes 8..15 the odd ones.
 template <int D>
-__device__ __forceinline__ v4i coarse_q_operand(const int8_t* qh, int g, int mf) {
-  uint32_t wds[4];
+__device__ __forceinline__ void coarse_q_operands(const int8_t* qh, int g, v4i* out) {
+  if (D == 128) {
+    const v4i a = *(const v4i*)(qh + 32 * g);
+    const v4i c = *(const v4i*)(qh + 32 * g + 16);
+    const uint32_t w[8] = {(uint32_t)a[0], (uint32_t)a[1], (uint32_t)a[2], (uint32_t)a[3],
+                           (uint32_t)c[0], (uint32_t)c[1], (uint32_t)c[2], (uint32_t)c[3]};
+    uint32_t ev[4], od[4];
 #pragma unroll
-  for (int k = 0; k < 4; k++) {
-    uint32_t v = 0;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      int j = 4 * k + i;
-      int d;
-      if (D == 128) d = 32 * g + 2 * j + mf;
-      else d = (j < 8) ? 16 * g + 2 * j : 16 * g + 2 * (j - 8) + 1;
-      v |= (uint32_t)(uint8_t)qh[d] << (8 * i);
+    for (int k = 0; k < 4; k++) {
+      ev[k] = __builtin_amdgcn_perm(w[2 * k + 1], w[2 * k], 0x06040200u);
+      od[k] = __builtin_amdgcn_perm(w[2 * k + 1], w[2 * k], 0x07050301u);
     }
-    wds[k] = v;
+    out[0] = v4i{(int)ev[0], (int)ev[1], (int)ev[2], (int)ev[3]};
+    out[1] = v4i{(int)od[0], (int)od[1], (int)od[2], (int)od[3]};
+  } else {
+    const v4i a = *(const v4i*)(qh + 16 * g);
+    const uint32_t e0 = __builtin_amdgcn_perm((uint32_t)a[1], (uint32_t)a[0], 0x06040200u);
+    const uint32_t e1 = __builtin_amdgcn_perm((uint32_t)a[3], (uint32_t)a[2], 0x06040200u);
+    const uint32_t o0 = __builtin_amdgcn_perm((uint32_t)a[1], (uint32_t)a[0], 0x07050301u);
+    const uint32_t o1 = __builtin_amdgcn_perm((uint32_t)a[3], (uint32_t)a[2], 0x07050301u);
+    out[0] = v4i{(int)e0, (int)e1, (int)o0, (int)o1};
   }
-  v4i r = {(int)wds[0], (int)wds[1], (int)wds[2], (int)wds[3]};
-  return r;
 }
 
 // Reduce-scatter over the four 16-lane groups: on entry p[tt] is this lane's
@@ -136,6 +145,22 @@ __device__ __forceinline__ T reduce_scatter4(T p0, T p1, T p2, T p3, int g) {
   return (even ? k0 : k1) + r;
 }
 
+template <int D>
+__device__ __forceinline__ void coarse_load4(const uint8_t* kb, int base, int n, int t_last,
+                                             v4i (&r)[4]) {
+  constexpr int KB = D / 2;
+#pragma unroll
+  for (int tt = 0; tt < 4; tt++) {
+    const int t = min(base + 16 * tt + n, t_last);
+    if (D == 128) {
+      r[tt] = *(const v4i*)(kb + (size_t)t * KB);
+    } else {
+      const int2 v = *(const int2*)(kb + (size_t)t * KB);
+      r[tt] = v4i{v.x, v.y, 0, 0};
+    }
+  }
+}
+
 template <int D, int HT>
 __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
                                                 const int8_t* __restrict__ w,
@@ -146,6 +171,7 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
                                                 int max_ctx) {
   constexpr int KB = D / 2;       // packed bytes per token
   constexpr int NMF = D / 64;     // MFMAs (K = 64) per head tile
+  constexpr int LB = KB / 4;      // bytes per lane per token
   __shared__ uint32_t lhist[kCoarseBins];
 
   const int b = blockIdx.y;
@@ -163,10 +189,11 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
 #pragma unroll
   for (int mt = 0; mt < HT; mt++) {
     const int h = 16 * mt + n;
+    if (h < H) {
+      coarse_q_operands<D>(qb + (size_t)h * D, g, qa[mt]);
+    } else {
 #pragma unroll
-    for (int mf = 0; mf < NMF; mf++) {
-      if (h < H) qa[mt][mf] = coarse_q_operand<D>(qb + (size_t)h * D, g, mf);
-      else qa[mt][mf] = v4i{0, 0, 0, 0};
+      for (int mf = 0; mf < NMF; mf++) qa[mt][mf] = v4i{0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -176,52 +203,71 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
   }
   __syncthreads();
 
-  const uint8_t* kb = kc + (size_t)b * max_ctx * KB;
+  const uint8_t* kb = kc + (size_t)b * max_ctx * KB + g * LB;
   int32_t* sb = scores + (size_t)b * max_ctx;
-  for (int base = t_begin + wave_id() * 64; base < t_end; base += 4 * 64) {
-    v4i raw[4];
+  const int t_last = t_end - 1;
+
+  // One 64-token step: all MFMAs first (independent accumulators), then the
+  // epilogue, so MFMA latency overlaps the VALU work of earlier tiles.
+  auto process = [&](int base, const v4i (&raw)[4]) {
+    const uint32_t m = 0xF0F0F0F0u;
+    v4i acc[4][HT];
 #pragma unroll
     for (int tt = 0; tt < 4; tt++) {
-      const int t = base + 16 * tt + n;
+      const uint32_t x0 = (uint32_t)raw[tt][0], x1 = (uint32_t)raw[tt][1];
+      const uint32_t x2 = (uint32_t)raw[tt][2], x3 = (uint32_t)raw[tt][3];
+      v4i bop[NMF];
       if (D == 128) {
-        raw[tt] = (t < t_end) ? *(const v4i*)(kb + (size_t)t * KB + 16 * g) : v4i{0, 0, 0, 0};
+        bop[0] = v4i{(int)((x0 << 4) & m), (int)((x1 << 4) & m), (int)((x2 << 4) & m),
+                     (int)((x3 << 4) & m)};
+        bop[NMF - 1] = v4i{(int)(x0 & m), (int)(x1 & m), (int)(x2 & m), (int)(x3 & m)};
       } else {
-        int2 v = (t < t_end) ? *(const int2*)(kb + (size_t)t * KB + 8 * g) : make_int2(0, 0);
-        raw[tt] = v4i{v.x, v.y, 0, 0};
+        bop[0] = v4i{(int)((x0 << 4) & m), (int)((x1 << 4) & m), (int)(x0 & m), (int)(x1 & m)};
+      }
+#pragma unroll
+      for (int mt = 0; mt < HT; mt++)
+        acc[tt][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[mt][0], bop[0], v4i{0, 0, 0, 0},
+                                                            0, 0, 0);
+      if (NMF == 2) {
+#pragma unroll
+        for (int mt = 0; mt < HT; mt++)
+          acc[tt][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[mt][NMF - 1], bop[NMF - 1],
+                                                              acc[tt][mt], 0, 0, 0);
       }
     }
     int32_t part[4];
 #pragma unroll
     for (int tt = 0; tt < 4; tt++) {
-      v4i bop[NMF];
-      if (D == 128) {
-        const uint32_t m = 0xF0F0F0F0u;
-        bop[0] = v4i{(int)(((uint32_t)raw[tt][0] << 4) & m), (int)(((uint32_t)raw[tt][1] << 4) & m),
-                     (int)(((uint32_t)raw[tt][2] << 4) & m), (int)(((uint32_t)raw[tt][3] << 4) & m)};
-        bop[NMF - 1] = v4i{(int)((uint32_t)raw[tt][0] & m), (int)((uint32_t)raw[tt][1] & m),
-                           (int)((uint32_t)raw[tt][2] & m), (int)((uint32_t)raw[tt][3] & m)};
-      } else {
-        const uint32_t m = 0xF0F0F0F0u;
-        bop[0] = v4i{(int)(((uint32_t)raw[tt][0] << 4) & m), (int)(((uint32_t)raw[tt][1] << 4) & m),
-                     (int)((uint32_t)raw[tt][0] & m), (int)((uint32_t)raw[tt][1] & m)};
-      }
-      int32_t acc_sum = 0;
+      int32_t s = 0;
 #pragma unroll
-      for (int mt = 0; mt < HT; mt++) {
-        v4i acc = {0, 0, 0, 0};
+      for (int mt = 0; mt < HT; mt++)
 #pragma unroll
-        for (int mf = 0; mf < NMF; mf++)
-          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[mt][mf], bop[mf], acc, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; i++) acc_sum += wv[mt][i] * (max(acc[i], 0) >> 4);
-      }
-      part[tt] = acc_sum;
+        for (int i = 0; i < 4; i++) s += __mul24(wv[mt][i], max(acc[tt][mt][i], 0) >> 4);
+      part[tt] = s;
     }
     const int32_t score = reduce_scatter4(part[0], part[1], part[2], part[3], g);
     const int t = base + l;
     if (t < t_end) {
       sb[t] = score;
       atomicAdd(&lhist[coarse_bucket(score)], 1u);
+    }
+  };
+
+  // Ping-pong register buffers: the loads of step i+1 are in flight while
+  // step i computes.  Past the end every lane loads row t_last (one line).
+  int base = __builtin_amdgcn_readfirstlane(t_begin + wave_id() * 64);
+  if (base < t_end) {
+    v4i bufA[4], bufB[4];
+    coarse_load4<D>(kb, base, n, t_last, bufA);
+    while (true) {
+      coarse_load4<D>(kb, base + 256, n, t_last, bufB);
+      process(base, bufA);
+      base += 256;
+      if (base >= t_end) break;
+      coarse_load4<D>(kb, base + 256, n, t_last, bufA);
+      process(base, bufB);
+      base += 256;
+      if (base >= t_end) break;
     }
   }
   __syncthreads();
@@ -253,73 +299,83 @@ hipError_t launch_coarse_scores(const int8_t* q, const int8_t* w, const uint8_t*
 
 // ------------------------------------------------- candidate select (A2) ----
 //
-// Keeps the C best tokens under (score desc, position asc).  Every workgroup
-// reads the request's bucket histogram and finds the bucket beta where the
-// count from the top crosses C.  It then filters its chunk of positions:
-// tokens in buckets above beta are kept outright (a bit in the request's
-// position bitmap, written one wave ballot = 64 positions at a time); tokens
-// in bucket beta are appended to a tie list (wave ballot + mbcnt ranks, one
-// atomic per wave).  The last workgroup of the request to finish resolves
-// the tie list exactly with the block radix threshold search, sets the
-// winners' bits, and emits the kept positions in ascending order from the
-// bitmap.  It then clears the histogram and counters for the next call.
-__global__ __launch_bounds__(256) void k_topc_select(const int32_t* __restrict__ ctx_len,
+// Keeps the C best tokens under (score desc, position asc), in two kernels.
+//
+// k_topc_filter (many workgroups per request): every workgroup reads the
+// request's bucket histogram and finds the bucket beta where the count from
+// the top crosses C.  It then filters its chunk of positions: tokens in
+// buckets above beta are kept outright -- a bit in the request's position
+// bitmap, written one wave ballot (64 positions) at a time; tokens in bucket
+// beta are appended to a tie list (wave ballot + mbcnt ranks, one atomic per
+// wave).
+//
+// k_topc_emit (one 1024-thread workgroup per request): resolves the tie list
+// exactly with the block radix threshold search (in LDS when it fits), sets
+// the winners' bits, emits the kept positions in ascending order from the
+// bitmap, and clears the histogram and tie counter for the next call.
+
+// Finds beta and the count strictly above it from a request's histogram.
+// NT threads; result in *beta (-1: every valid token is kept) and *above.
+template <int NT>
+__device__ void coarse_threshold(const uint32_t* hb, int n_valid, int C, int* beta,
+                                 uint32_t* above, uint32_t* scan_sh) {
+  constexpr int kPer = (kCoarseBins + NT - 1) / NT;
+  if (threadIdx.x == 0) {
+    *beta = -1;
+    *above = 0;
+  }
+  __syncthreads();
+  if (n_valid <= C) return;
+  const int seg = NT - 1 - (int)threadIdx.x;  // thread 0 owns the top segment
+  uint32_t s = 0;
+  for (int k = 0; k < kPer; k++) {
+    const int bin = seg * kPer + k;
+    if (bin < kCoarseBins) s += hb[bin];
+  }
+  uint32_t tot;
+  const uint32_t above_seg = block_excl_scan<NT>(s, scan_sh, &tot);
+  if (above_seg < (uint32_t)C && (uint32_t)C <= above_seg + s) {
+    uint32_t run = above_seg;
+    for (int k = kPer - 1; k >= 0; k--) {
+      const int bin = seg * kPer + k;
+      const uint32_t c = bin < kCoarseBins ? hb[bin] : 0u;
+      if (run + c >= (uint32_t)C) {
+        *beta = bin;
+        *above = run;
+        break;
+      }
+      run += c;
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void k_topc_filter(const int32_t* __restrict__ ctx_len,
                                                      const int32_t* __restrict__ scores,
-                                                     uint32_t* __restrict__ hist,
+                                                     const uint32_t* __restrict__ hist,
                                                      uint32_t* __restrict__ bitmap,
                                                      int32_t* __restrict__ tie_s,
                                                      int32_t* __restrict__ tie_p,
-                                                     uint32_t* __restrict__ ctr,
-                                                     int32_t* __restrict__ cand, int max_ctx,
+                                                     uint32_t* __restrict__ ctr, int max_ctx,
                                                      int C, int bitmap_words) {
   __shared__ uint32_t scan_sh[4];
   __shared__ int sh_beta;
   __shared__ uint32_t sh_above;
-  __shared__ int sh_last;
-  __shared__ SelectShared ssh;
-
+  __shared__ uint32_t n_local, g_base;
+  __shared__ int32_t loc_s[kSelectChunk];
+  __shared__ int32_t loc_p[kSelectChunk];
   const int b = blockIdx.y;
   const int tid = threadIdx.x, l = lane_id();
   const int n_valid = clamp_ctx(ctx_len, b, max_ctx);
-  uint32_t* hb = hist + (size_t)b * kCoarseBins;
-  uint32_t* bm = bitmap + (size_t)b * bitmap_words;
-  uint32_t* tie_count = ctr + 2 * b;
-  uint32_t* done = ctr + 2 * b + 1;
-
-  // ---- threshold bucket (every workgroup, redundantly)
-  if (tid == 0) {
-    sh_beta = -1;
-    sh_above = 0;
-  }
-  __syncthreads();
-  if (n_valid > C) {
-    constexpr int kPer = kCoarseBins / 256;
-    const int seg = 255 - tid;  // thread 0 owns the top segment
-    uint32_t s = 0;
-    for (int k = 0; k < kPer; k++) s += hb[seg * kPer + k];
-    uint32_t tot;
-    uint32_t above_seg = block_excl_scan<256>(s, scan_sh, &tot);
-    if (above_seg < (uint32_t)C && (uint32_t)C <= above_seg + s) {
-      uint32_t run = above_seg;
-      for (int k = kPer - 1; k >= 0; k--) {
-        uint32_t c = hb[seg * kPer + k];
-        if (run + c >= (uint32_t)C) {
-          sh_beta = seg * kPer + k;
-          sh_above = run;
-          break;
-        }
-        run += c;
-      }
-    }
-  }
-  __syncthreads();
+  if (tid == 0) n_local = 0;
+  coarse_threshold<256>(hist + (size_t)b * kCoarseBins, n_valid, C, &sh_beta, &sh_above,
+                        scan_sh);
   const int beta = sh_beta;
-  const uint32_t above = sh_above;
-
-  // ---- filter this workgroup's chunk
+  uint32_t* bm = bitmap + (size_t)b * bitmap_words;
   const int c0 = blockIdx.x * kSelectChunk;
   const int c1 = min(c0 + kSelectChunk, bitmap_words * 32);
   const int32_t* sb = scores + (size_t)b * max_ctx;
+  // keep bits go straight to the bitmap; ties are collected in LDS first
   for (int base = c0 + wave_id() * 64; base < c1; base += 256) {
     const int t = base + l;
     const bool valid = t < n_valid;
@@ -329,62 +385,95 @@ __global__ __launch_bounds__(256) void k_topc_select(const int32_t* __restrict__
     const bool tie_f = valid && beta >= 0 && bk == beta;
     const uint64_t mk = __ballot(keep_f);
     const uint64_t mt = __ballot(tie_f);
-    if (l == 0) {
-      bm[base / 32] = (uint32_t)mk;
-      bm[base / 32 + 1] = (uint32_t)(mk >> 32);
-    }
+    if (l == 0) *(uint2*)&bm[base / 32] = make_uint2((uint32_t)mk, (uint32_t)(mk >> 32));
     if (mt) {
       uint32_t off = 0;
-      if (l == 0) off = atomicAdd(tie_count, (uint32_t)__popcll(mt));
+      if (l == 0) off = atomicAdd(&n_local, (uint32_t)__popcll(mt));
       off = __shfl(off, 0, kWave);
       if (tie_f) {
         const uint32_t idx = off + lane_rank(mt);
-        tie_s[(size_t)b * max_ctx + idx] = s;
-        tie_p[(size_t)b * max_ctx + idx] = t;
+        loc_s[idx] = s;
+        loc_p[idx] = t;
       }
     }
   }
+  __syncthreads();
+  const uint32_t nl = n_local;
+  if (nl == 0) return;
+  // one reservation per workgroup in the request's tie list
+  if (tid == 0) g_base = atomicAdd(&ctr[kCtrStride * b], nl);
+  __syncthreads();
+  const size_t gb = (size_t)b * max_ctx + g_base;
+  for (uint32_t i = tid; i < nl; i += 256) {
+    tie_s[gb + i] = loc_s[i];
+    tie_p[gb + i] = loc_p[i];
+  }
+}
 
-  // ---- the last workgroup of this request finishes the selection
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) sh_last = (atomicAdd(done, 1u) == gridDim.x - 1) ? 1 : 0;
-  __syncthreads();
-  if (!sh_last) return;
-  __threadfence();
+constexpr int kEmitThreads = 1024;
+constexpr int kTieLds = 6144;
+
+__global__ __launch_bounds__(kEmitThreads) void k_topc_emit(
+    const int32_t* __restrict__ ctx_len, uint32_t* __restrict__ hist,
+    uint32_t* __restrict__ bitmap, const int32_t* __restrict__ tie_s,
+    const int32_t* __restrict__ tie_p, uint32_t* __restrict__ ctr, int32_t* __restrict__ cand,
+    int max_ctx, int C, int bitmap_words) {
+  __shared__ uint32_t scan_sh[kEmitThreads / kWave];
+  __shared__ int sh_beta;
+  __shared__ uint32_t sh_above;
+  __shared__ SelectShared ssh;
+  __shared__ int32_t lds_s[kTieLds];
+  __shared__ int32_t lds_p[kTieLds];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n_valid = clamp_ctx(ctx_len, b, max_ctx);
+  uint32_t* hb = hist + (size_t)b * kCoarseBins;
+  uint32_t* bm = bitmap + (size_t)b * bitmap_words;
+  coarse_threshold<kEmitThreads>(hb, n_valid, C, &sh_beta, &sh_above, scan_sh);
+  const int beta = sh_beta;
 
   if (beta >= 0) {
-    const uint32_t n_tie = __hip_atomic_load(tie_count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t need = (uint32_t)C - above;  // 1 <= need <= n_tie
+    const uint32_t n_tie = ctr[kCtrStride * b];
+    const uint32_t need = (uint32_t)C - sh_above;  // 1 <= need <= n_tie
     const int32_t* ts = tie_s + (size_t)b * max_ctx;
     const int32_t* tp = tie_p + (size_t)b * max_ctx;
+    const bool in_lds = n_tie <= (uint32_t)kTieLds;
+    if (in_lds) {
+      for (int i = tid; i < (int)n_tie; i += kEmitThreads) {
+        lds_s[i] = ts[i];
+        lds_p[i] = tp[i];
+      }
+      __syncthreads();
+    }
+    const int32_t* ss = in_lds ? lds_s : ts;
+    const int32_t* pp = in_lds ? lds_p : tp;
     Threshold thr{0ull, 0u, 0};
     if (need < n_tie) {
       auto get = [&](int i, uint64_t& u, uint32_t& p) {
-        u = key_of_i32(ts[i]);
-        p = (uint32_t)tp[i];
+        u = key_of_i32(ss[i]);
+        p = (uint32_t)pp[i];
       };
-      thr = block_threshold<256>(get, (int)n_tie, need, ssh);
+      thr = block_threshold<kEmitThreads>(get, (int)n_tie, need, ssh);
     }
-    for (int i = tid; i < (int)n_tie; i += 256) {
-      const uint32_t p = (uint32_t)tp[i];
-      if (keep(thr, key_of_i32(ts[i]), p)) atomicOr(&bm[p / 32], 1u << (p % 32));
+    for (int i = tid; i < (int)n_tie; i += kEmitThreads) {
+      const uint32_t p = (uint32_t)pp[i];
+      if (keep(thr, key_of_i32(ss[i]), p)) atomicOr(&bm[p / 32], 1u << (p % 32));
     }
-    __threadfence();
     __syncthreads();
   }
 
-  // ---- emit ascending positions from the bitmap
+  // emit ascending positions: contiguous word ranges per thread, one scan
   const int nw = (n_valid + 31) / 32;
-  const int wpt = (nw + 255) / 256;
+  const int wpt = (nw + kEmitThreads - 1) / kEmitThreads;
   const int w0 = tid * wpt, w1 = min(w0 + wpt, nw);
   uint32_t cnt = 0;
-  for (int wi = w0; wi < w1; wi++) cnt += __popc(bm[wi]);
+  for (int wi = w0; wi < w1; wi++)
+    cnt += __popc(__hip_atomic_load(&bm[wi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   uint32_t total;
-  uint32_t off = block_excl_scan<256>(cnt, scan_sh, &total);
+  uint32_t off = block_excl_scan<kEmitThreads>(cnt, scan_sh, &total);
   int32_t* cb = cand + (size_t)b * C;
   for (int wi = w0; wi < w1; wi++) {
-    uint32_t bits = bm[wi];
+    uint32_t bits = __hip_atomic_load(&bm[wi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     while (bits) {
       const int k = __ffs(bits) - 1;
       if (off < (uint32_t)C) cb[off] = 32 * wi + k;
@@ -392,298 +481,22 @@ __global__ __launch_bounds__(256) void k_topc_select(const int32_t* __restrict__
       bits &= bits - 1;
     }
   }
-  for (int i = (int)total + tid; i < C; i += 256) cb[i] = -1;
+  for (int i = (int)total + tid; i < C; i += kEmitThreads) cb[i] = -1;
 
-  // ---- leave the workspace cleared for the next call
-  for (int i = tid; i < kCoarseBins; i += 256) hb[i] = 0;
-  if (tid == 0) {
-    *tie_count = 0;
-    *done = 0;
-  }
+  // leave the histogram and tie counter cleared for the next call
+  for (int i = tid; i < kCoarseBins; i += kEmitThreads) hb[i] = 0;
+  if (tid == 0) ctr[kCtrStride * b] = 0;
 }
 
 hipError_t launch_topc_select(const int32_t* ctx_len, const CoarseWS& ws, int32_t* cand, int B,
                               int max_ctx, int C, hipStream_t st) {
   dim3 grid((ws.bitmap_words * 32 + kSelectChunk - 1) / kSelectChunk, B);
-  hipLaunchKernelGGL(k_topc_select, grid, dim3(256), 0, st, ctx_len, ws.scores, ws.hist,
+  hipLaunchKernelGGL(k_topc_filter, grid, dim3(256), 0, st, ctx_len, ws.scores, ws.hist,
+                     ws.bitmap, ws.tie_s, ws.tie_p, ws.ctr, max_ctx, C, ws.bitmap_words);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_topc_emit, dim3(B), dim3(kEmitThreads), 0, st, ctx_len, ws.hist,
                      ws.bitmap, ws.tie_s, ws.tie_p, ws.ctr, cand, max_ctx, C, ws.bitmap_words);
-  return hipGetLastError();
-}
-
-// ------------------------------------------------ selected-list emission ----
-//
-// Block helper: items 0..n-1 in ascending position order, item i kept iff
-// sel(i).  Writes the kept positions (and scores) densely to topk[0..K),
-// padding with -1 / 0.  With a slot table, also resolves each kept token:
-// rows[j] = its slot if resident, else hot_slots + (its rank among the
-// misses), and records the misses' positions in miss_pos; *n_miss = count.
-template <class Sel, class Pos, class Score>
-__device__ void emit_selected(int n, const Sel& sel, const Pos& pos, const Score& score, int K,
-                              int32_t* topk, int64_t* topk_score, const int32_t* p2s,
-                              int32_t* rows, int32_t* miss_pos, int32_t* n_miss,
-                              int hot_slots, uint32_t* scan_sh) {
-  const int tid = threadIdx.x;
-  const int per = (n + 255) / 256;
-  const int i0 = tid * per, i1 = min(i0 + per, n);
-  uint32_t c_sel = 0, c_miss = 0;
-  for (int i = i0; i < i1; i++) {
-    if (sel(i)) {
-      c_sel++;
-      if (p2s && p2s[pos(i)] < 0) c_miss++;
-    }
-  }
-  uint32_t tot_sel, tot_miss;
-  uint32_t o_sel = block_excl_scan<256>(c_sel, scan_sh, &tot_sel);
-  uint32_t o_miss = block_excl_scan<256>(c_miss, scan_sh, &tot_miss);
-  for (int i = i0; i < i1; i++) {
-    if (!sel(i)) continue;
-    const int32_t p = pos(i);
-    if (o_sel < (uint32_t)K) {
-      topk[o_sel] = p;
-      if (topk_score) topk_score[o_sel] = score(i);
-      if (p2s) {
-        const int32_t slot = p2s[p];
-        if (slot >= 0) {
-          rows[o_sel] = slot;
-        } else {
-          rows[o_sel] = hot_slots + (int32_t)o_miss;
-          miss_pos[o_miss] = p;
-          o_miss++;
-        }
-      } else if (rows) {
-        rows[o_sel] = p;
-      }
-    }
-    o_sel++;
-  }
-  for (int j = (int)tot_sel + tid; j < K; j += 256) {
-    topk[j] = -1;
-    if (topk_score) topk_score[j] = 0;
-    if (rows) rows[j] = -1;
-  }
-  if (tid == 0 && n_miss) *n_miss = p2s ? (int32_t)tot_miss : 0;
-}
-
-// ------------------------------------------------ refine + top-k (A3, A4) ----
-//
-// fs[b,c] = sum_h w[b,h] * max(0, q[b,h] . k8[b, cand[b,c]]) with the original
-// int8 keys: gathered 32-byte slices per lane (D = 128) feed
-// v_mfma_i32_16x16x64_i8 directly, 16 candidates per tile.  Per-head dots
-// are exact in int32 (|dot| < 2^21); w * relu(dot) < 2^28 and groups of four
-// stay below 2^30 before widening to int64.  The last workgroup of each
-// request selects the top K of the candidates (block radix threshold over
-// (fs, position)), emits them in ascending order and, when a slot table is
-// given, resolves them against the hot buffer.
-template <int D, int HT>
-__global__ __launch_bounds__(256) void k_refine(
-    const int8_t* __restrict__ q, const int8_t* __restrict__ w, const int8_t* __restrict__ k8,
-    const int32_t* __restrict__ cand, int64_t* __restrict__ fs, uint32_t* __restrict__ done_ctr,
-    int32_t* __restrict__ topk, int64_t* __restrict__ topk_score,
-    const int32_t* __restrict__ pos2slot, int32_t* __restrict__ rows,
-    int32_t* __restrict__ n_miss, int32_t* __restrict__ miss_pos, int hot_slots, int H,
-    int max_ctx, int C, int K) {
-  constexpr int NMF = D / 64;
-  __shared__ uint32_t scan_sh[4];
-  __shared__ int sh_last;
-  __shared__ SelectShared ssh;
-
-  const int b = blockIdx.y;
-  const int tid = threadIdx.x, l = lane_id(), n = l & 15, g = l >> 4;
-  const int8_t* qb = q + (size_t)b * H * D;
-  const int32_t* cb = cand + (size_t)b * C;
-  int64_t* fb = fs + (size_t)b * C;
-
-  v4i qa[HT][NMF];
-  int32_t wv[HT][4];
-#pragma unroll
-  for (int mt = 0; mt < HT; mt++) {
-    const int h = 16 * mt + n;
-#pragma unroll
-    for (int mf = 0; mf < NMF; mf++) {
-      // D = 128: lane group g owns bytes [32g, 32g+32): mf 0 the first 16, mf 1 the rest.
-      // D = 64:  lane group g owns bytes [16g, 16g+16).
-      const int off = (D == 128) ? 32 * g + 16 * mf : 16 * g;
-      qa[mt][mf] = (h < H) ? *(const v4i*)(qb + (size_t)h * D + off) : v4i{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int hh = 16 * mt + 4 * g + i;
-      wv[mt][i] = hh < H ? (int32_t)w[(size_t)b * H + hh] : 0;
-    }
-  }
-
-  const int c_base = blockIdx.x * kRefinePerWG + wave_id() * 64;
-  const int8_t* kb = k8 + (size_t)b * max_ctx * D;
-  int64_t part[4];
-#pragma unroll
-  for (int tt = 0; tt < 4; tt++) {
-    const int c = c_base + 16 * tt + n;
-    const int32_t p = (c < C) ? cb[c] : -1;
-    v4i raw[NMF];
-#pragma unroll
-    for (int mf = 0; mf < NMF; mf++) {
-      const int off = (D == 128) ? 32 * g + 16 * mf : 16 * g;
-      raw[mf] = (p >= 0) ? *(const v4i*)(kb + (size_t)p * D + off) : v4i{0, 0, 0, 0};
-    }
-    int64_t sum = 0;
-#pragma unroll
-    for (int mt = 0; mt < HT; mt++) {
-      v4i acc = {0, 0, 0, 0};
-#pragma unroll
-      for (int mf = 0; mf < NMF; mf++)
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[mt][mf], raw[mf], acc, 0, 0, 0);
-      int32_t s4 = 0;
-#pragma unroll
-      for (int i = 0; i < 4; i++) s4 += wv[mt][i] * max(acc[i], 0);
-      sum += (int64_t)s4;
-    }
-    part[tt] = sum;
-  }
-  const int64_t score = reduce_scatter4(part[0], part[1], part[2], part[3], g);
-  {
-    const int c = c_base + l;
-    if (c < C) fb[c] = (cb[c] >= 0) ? score : 0;
-  }
-
-  // ---- last workgroup of the request: top-K of the candidates
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) sh_last = (atomicAdd(&done_ctr[b], 1u) == gridDim.x - 1) ? 1 : 0;
-  __syncthreads();
-  if (!sh_last) return;
-  __threadfence();
-
-  // valid candidates form a prefix (ascending, -1 padded)
-  uint32_t nv = 0;
-  for (int i = tid; i < C; i += 256) nv += (cb[i] >= 0) ? 1u : 0u;
-  uint32_t n_c;
-  block_excl_scan<256>(nv, scan_sh, &n_c);
-  const uint32_t need = min((uint32_t)K, n_c);
-  Threshold thr{0ull, 0u, 0};
-  const bool all = need >= n_c;
-  if (!all) {
-    auto get = [&](int i, uint64_t& u, uint32_t& p) {
-      u = key_of_i64(fb[i]);
-      p = (uint32_t)cb[i];
-    };
-    thr = block_threshold<256>(get, (int)n_c, need, ssh);
-  }
-  auto sel = [&](int i) { return all || keep(thr, key_of_i64(fb[i]), (uint32_t)cb[i]); };
-  auto pos = [&](int i) { return cb[i]; };
-  auto scr = [&](int i) { return fb[i]; };
-  emit_selected((int)n_c, sel, pos, scr, K, topk + (size_t)b * K,
-                topk_score ? topk_score + (size_t)b * K : nullptr,
-                pos2slot ? pos2slot + (size_t)b * max_ctx : nullptr,
-                rows ? rows + (size_t)b * K : nullptr,
-                miss_pos ? miss_pos + (size_t)b * K : nullptr, n_miss ? n_miss + b : nullptr,
-                hot_slots, scan_sh);
-  if (tid == 0) done_ctr[b] = 0;
-}
-
-hipError_t launch_refine_topk(const int8_t* q, const int8_t* w, const int8_t* k8,
-                              const int32_t* cand, const RefineWS& ws, int32_t* topk,
-                              int64_t* topk_score, const int32_t* pos2slot, int32_t* rows,
-                              int32_t* n_miss, int hot_slots, int B, int H, int D, int max_ctx,
-                              int C, int K, hipStream_t st) {
-  dim3 grid((C + kRefinePerWG - 1) / kRefinePerWG, B);
-  const int HT = (H + 15) / 16;
-#define LS_REFINE(DD, TT)                                                                      \
-  hipLaunchKernelGGL((k_refine<DD, TT>), grid, dim3(256), 0, st, q, w, k8, cand, ws.fs, ws.ctr, \
-                     topk, topk_score, pos2slot, rows, n_miss, ws.miss_pos, hot_slots, H,       \
-                     max_ctx, C, K)
-  if (D == 128) {
-    if (HT == 1) LS_REFINE(128, 1); else if (HT == 2) LS_REFINE(128, 2);
-    else if (HT == 3) LS_REFINE(128, 3); else LS_REFINE(128, 4);
-  } else {
-    if (HT == 1) LS_REFINE(64, 1); else if (HT == 2) LS_REFINE(64, 2);
-    else if (HT == 3) LS_REFINE(64, 3); else LS_REFINE(64, 4);
-  }
-#undef LS_REFINE
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------ hot resolve (A5) ----
-// Standalone resolve of an existing selection (one workgroup per request).
-__global__ __launch_bounds__(256) void k_hot_resolve(const int32_t* __restrict__ topk,
-                                                     const int32_t* __restrict__ pos2slot,
-                                                     int32_t* __restrict__ rows,
-                                                     int32_t* __restrict__ n_miss,
-                                                     int32_t* __restrict__ miss_pos,
-                                                     int hot_slots, int max_ctx, int K) {
-  __shared__ uint32_t scan_sh[4];
-  const int b = blockIdx.x;
-  const int32_t* tb = topk + (size_t)b * K;
-  // the selection is ascending and -1 padded: copy it through emit_selected
-  // into a scratch copy is unnecessary; write topk back in place unchanged.
-  uint32_t nv = 0;
-  for (int i = threadIdx.x; i < K; i += 256) nv += (tb[i] >= 0) ? 1u : 0u;
-  uint32_t n_sel;
-  block_excl_scan<256>(nv, scan_sh, &n_sel);
-  const int32_t* p2s = pos2slot + (size_t)b * max_ctx;
-  const int per = (K + 255) / 256;
-  const int i0 = threadIdx.x * per, i1 = min(i0 + per, (int)n_sel);
-  uint32_t c_miss = 0;
-  for (int i = i0; i < i1; i++) c_miss += (p2s[tb[i]] < 0) ? 1u : 0u;
-  uint32_t tot;
-  uint32_t o = block_excl_scan<256>(c_miss, scan_sh, &tot);
-  int32_t* rb = rows + (size_t)b * K;
-  int32_t* mb = miss_pos + (size_t)b * K;
-  for (int i = i0; i < i1; i++) {
-    const int32_t p = tb[i];
-    const int32_t slot = p2s[p];
-    if (slot >= 0) {
-      rb[i] = slot;
-    } else {
-      rb[i] = hot_slots + (int32_t)o;
-      mb[o] = p;
-      o++;
-    }
-  }
-  for (int i = (int)n_sel + threadIdx.x; i < K; i += 256) rb[i] = -1;
-  if (threadIdx.x == 0) n_miss[b] = (int32_t)tot;
-}
-
-hipError_t launch_hot_resolve(const int32_t* topk, const int32_t* pos2slot, int32_t* rows,
-                              int32_t* n_miss, int32_t* miss_pos, int hot_slots, int B,
-                              int max_ctx, int K, hipStream_t st) {
-  hipLaunchKernelGGL(k_hot_resolve, dim3(B), dim3(256), 0, st, topk, pos2slot, rows, n_miss,
-                     miss_pos, hot_slots, max_ctx, K);
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------- miss gather (A6) ---
-// hot[b, hot_slots + j] := pool[b, miss_pos[b, j]] for j < n_miss[b], in
-// 16-byte pieces spread over the workgroups of the request.  The pool may
-// be pinned host memory (reads then cross PCIe).
-constexpr int kGatherWGPerReq = 16;
-
-__global__ __launch_bounds__(256) void k_hot_gather(const int32_t* __restrict__ miss_pos,
-                                                    const int32_t* __restrict__ n_miss,
-                                                    const uint4* pool, uint4* __restrict__ hot,
-                                                    int hot_slots, int max_ctx, int K,
-                                                    int chunks) {
-  const int b = blockIdx.y;
-  const int nm = n_miss[b];
-  const int64_t total = (int64_t)nm * chunks;
-  const int64_t per = (total + gridDim.x - 1) / gridDim.x;
-  const int64_t i0 = (int64_t)blockIdx.x * per;
-  const int64_t i1 = min(i0 + per, total);
-  const int32_t* mp = miss_pos + (size_t)b * K;
-  const size_t pool_base = (size_t)b * max_ctx;
-  const size_t hot_base = (size_t)b * (hot_slots + K) + hot_slots;
-  for (int64_t i = i0 + threadIdx.x; i < i1; i += 256) {
-    const int j = (int)(i / chunks), c = (int)(i % chunks);
-    const int32_t p = mp[j];
-    hot[(hot_base + j) * chunks + c] = pool[(pool_base + p) * chunks + c];
-  }
-}
-
-hipError_t launch_hot_gather(const int32_t* miss_pos, const int32_t* n_miss, const void* pool,
-                             void* hot, int hot_slots, int B, int max_ctx, int K, int row_elems,
-                             hipStream_t st) {
-  const int chunks = row_elems * 2 / 16;
-  hipLaunchKernelGGL(k_hot_gather, dim3(kGatherWGPerReq, B), dim3(256), 0, st, miss_pos, n_miss,
-                     (const uint4*)pool, (uint4*)hot, hot_slots, max_ctx, K, chunks);
   return hipGetLastError();
 }
 

@@ -1,0 +1,314 @@
+// Refinement kernels for gfx950: exact scores of the candidates from their
+// original int8 keys, the top-k of those, the hot-buffer resolve, and the
+// gather of the misses from the full-history pool.
+//
+// Method: LeanSparse (arXiv 2611.04671), Abstract -- the original indexer
+// keys are fetched only for the candidates the coarse pass kept.  Hot
+// buffer: XM-Sparse digest, section on the hot buffer -- after the selection
+// only the selected rows missing from the HBM hot buffer are fetched.
+#include "ls_device.h"
+#include "ls_launch.h"
+
+namespace ls {
+
+// ----------------------------------------------------- refine scores (A3) ---
+//
+// fs[b,c] = sum_h w[b,h] * max(0, q[b,h] . k8[b, cand[b,c]]).  16 candidates
+// per tile feed v_mfma_i32_16x16x64_i8 directly: lane (n, g) gathers the
+// 32-byte slice [32g, 32g+32) of candidate n's 128-byte key row (D = 128) or
+// [16g, 16g+16) of its 64-byte row (D = 64); the query slice of the same
+// dims is the A operand.  Per-head dots are exact in int32 (|dot| < 2^21);
+// w * relu(dot) < 2^28 and groups of four stay below 2^30 before widening
+// to int64.  Invalid candidates (-1) score 0 and are never selected.
+template <int D, int HT>
+__global__ __launch_bounds__(256) void k_refine(const int8_t* __restrict__ q,
+                                                const int8_t* __restrict__ w,
+                                                const int8_t* __restrict__ k8,
+                                                const int32_t* __restrict__ cand,
+                                                int64_t* __restrict__ fs, int H, int max_ctx,
+                                                int C) {
+  constexpr int NMF = D / 64;
+  const int b = blockIdx.y;
+  const int l = lane_id(), n = l & 15, g = l >> 4;
+  const int8_t* qb = q + (size_t)b * H * D;
+  const int32_t* cb = cand + (size_t)b * C;
+
+  const int c_base = blockIdx.x * kRefinePerWG + wave_id() * 64;
+  const int8_t* kb = k8 + (size_t)b * max_ctx * D;
+  int32_t pos[4];
+  v4i raw[4][NMF];
+#pragma unroll
+  for (int tt = 0; tt < 4; tt++) {
+    const int c = c_base + 16 * tt + n;
+    pos[tt] = (c < C) ? cb[c] : -1;
+    const int p = pos[tt] >= 0 ? pos[tt] : 0;
+#pragma unroll
+    for (int mf = 0; mf < NMF; mf++) {
+      const int off = (D == 128) ? 32 * g + 16 * mf : 16 * g;
+      raw[tt][mf] = *(const v4i*)(kb + (size_t)p * D + off);
+    }
+  }
+
+  v4i qa[HT][NMF];
+  int32_t wv[HT][4];
+#pragma unroll
+  for (int mt = 0; mt < HT; mt++) {
+    const int h = 16 * mt + n;
+#pragma unroll
+    for (int mf = 0; mf < NMF; mf++) {
+      const int off = (D == 128) ? 32 * g + 16 * mf : 16 * g;
+      qa[mt][mf] = (h < H) ? *(const v4i*)(qb + (size_t)h * D + off) : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int hh = 16 * mt + 4 * g + i;
+      wv[mt][i] = hh < H ? (int32_t)w[(size_t)b * H + hh] : 0;
+    }
+  }
+
+  int64_t part[4];
+#pragma unroll
+  for (int tt = 0; tt < 4; tt++) {
+    v4i acc[HT];
+#pragma unroll
+    for (int mt = 0; mt < HT; mt++)
+      acc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[mt][0], raw[tt][0], v4i{0, 0, 0, 0}, 0,
+                                                      0, 0);
+    if (NMF == 2) {
+#pragma unroll
+      for (int mt = 0; mt < HT; mt++)
+        acc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[mt][NMF - 1], raw[tt][NMF - 1],
+                                                        acc[mt], 0, 0, 0);
+    }
+    int64_t sum = 0;
+#pragma unroll
+    for (int mt = 0; mt < HT; mt++) {
+      int32_t s4 = 0;
+#pragma unroll
+      for (int i = 0; i < 4; i++) s4 += wv[mt][i] * max(acc[mt][i], 0);
+      sum += (int64_t)s4;
+    }
+    part[tt] = sum;
+  }
+  // reduce-scatter over the four lane groups: lane (n, g) ends with tile g
+  const bool lo = g < 2;
+  int64_t s0 = lo ? part[2] : part[0], s1 = lo ? part[3] : part[1];
+  int64_t r0 = __shfl_xor(s0, 32, kWave), r1 = __shfl_xor(s1, 32, kWave);
+  int64_t k0 = (lo ? part[0] : part[2]) + r0, k1 = (lo ? part[1] : part[3]) + r1;
+  const bool even = (g & 1) == 0;
+  int64_t sx = even ? k1 : k0;
+  int64_t rx = __shfl_xor(sx, 16, kWave);
+  const int64_t score = (even ? k0 : k1) + rx;
+  const int c = c_base + l;
+  if (c < C) fs[(size_t)b * C + c] = (cb[c] >= 0) ? score : 0;
+}
+
+// ---------------------------------------------- top-k + resolve (A4, A5) ----
+//
+// One 1024-thread workgroup per request.  The candidates' (fine score,
+// position) pairs are staged in LDS when they fit, the block radix threshold
+// search finds the cut that keeps exactly min(K, valid) of them under
+// (score desc, position asc), and the kept ones are emitted in candidate
+// order, i.e. ascending position.  With a slot table the emission also
+// resolves each kept token against the hot buffer: rows[j] = its slot if
+// resident, else hot_slots + (its rank among the misses); the misses'
+// positions go to miss_pos in the same order.
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkLds = 8192;
+
+__global__ __launch_bounds__(kTopkThreads) void k_topk(
+    const int32_t* __restrict__ cand, const int64_t* __restrict__ fs, int32_t* __restrict__ topk,
+    int64_t* __restrict__ topk_score, const int32_t* __restrict__ pos2slot,
+    int32_t* __restrict__ rows, int32_t* __restrict__ n_miss, int32_t* __restrict__ miss_pos,
+    int hot_slots, int max_ctx, int C, int K) {
+  constexpr int NT = kTopkThreads;
+  __shared__ uint32_t scan_sh[NT / kWave];
+  __shared__ SelectShared ssh;
+  __shared__ int64_t lds_f[kTopkLds];
+  __shared__ int32_t lds_c[kTopkLds];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int32_t* cb = cand + (size_t)b * C;
+  const int64_t* fb = fs + (size_t)b * C;
+
+  // valid candidates form a prefix (ascending, -1 padded)
+  uint32_t nv = 0;
+  for (int i = tid; i < C; i += NT) nv += (cb[i] >= 0) ? 1u : 0u;
+  uint32_t n_c;
+  block_excl_scan<NT>(nv, scan_sh, &n_c);
+  const bool in_lds = n_c <= (uint32_t)kTopkLds;
+  if (in_lds) {
+    for (int i = tid; i < (int)n_c; i += NT) {
+      lds_f[i] = fb[i];
+      lds_c[i] = cb[i];
+    }
+    __syncthreads();
+  }
+  const int64_t* ff = in_lds ? lds_f : fb;
+  const int32_t* cc = in_lds ? lds_c : cb;
+
+  const uint32_t need = min((uint32_t)K, n_c);
+  const bool all = need >= n_c;
+  Threshold thr{0ull, 0u, 0};
+  if (!all) {
+    auto get = [&](int i, uint64_t& u, uint32_t& p) {
+      u = key_of_i64(ff[i]);
+      p = (uint32_t)cc[i];
+    };
+    thr = block_threshold<NT>(get, (int)n_c, need, ssh);
+  }
+
+  const int32_t* p2s = pos2slot ? pos2slot + (size_t)b * max_ctx : nullptr;
+  const int per = ((int)n_c + NT - 1) / NT;
+  const int i0 = tid * per, i1 = min(i0 + per, (int)n_c);
+  uint32_t c_sel = 0, c_miss = 0;
+  for (int i = i0; i < i1; i++) {
+    const bool s = all || keep(thr, key_of_i64(ff[i]), (uint32_t)cc[i]);
+    if (s) {
+      c_sel++;
+      if (p2s && p2s[cc[i]] < 0) c_miss++;
+    }
+  }
+  uint32_t tot_sel, tot_miss;
+  uint32_t o_sel = block_excl_scan<NT>(c_sel, scan_sh, &tot_sel);
+  uint32_t o_miss = block_excl_scan<NT>(c_miss, scan_sh, &tot_miss);
+  int32_t* tb = topk + (size_t)b * K;
+  int64_t* sb = topk_score ? topk_score + (size_t)b * K : nullptr;
+  int32_t* rb = rows ? rows + (size_t)b * K : nullptr;
+  int32_t* mb = miss_pos ? miss_pos + (size_t)b * K : nullptr;
+  for (int i = i0; i < i1; i++) {
+    const int32_t p = cc[i];
+    if (!(all || keep(thr, key_of_i64(ff[i]), (uint32_t)p))) continue;
+    if (o_sel < (uint32_t)K) {
+      tb[o_sel] = p;
+      if (sb) sb[o_sel] = ff[i];
+      if (p2s) {
+        const int32_t slot = p2s[p];
+        if (slot >= 0) {
+          rb[o_sel] = slot;
+        } else {
+          rb[o_sel] = hot_slots + (int32_t)o_miss;
+          mb[o_miss] = p;
+          o_miss++;
+        }
+      }
+    }
+    o_sel++;
+  }
+  for (int j = (int)tot_sel + tid; j < K; j += NT) {
+    tb[j] = -1;
+    if (sb) sb[j] = 0;
+    if (rb) rb[j] = -1;
+  }
+  if (tid == 0 && n_miss) n_miss[b] = p2s ? (int32_t)tot_miss : 0;
+}
+
+hipError_t launch_refine_topk(const int8_t* q, const int8_t* w, const int8_t* k8,
+                              const int32_t* cand, const RefineWS& ws, int32_t* topk,
+                              int64_t* topk_score, const int32_t* pos2slot, int32_t* rows,
+                              int32_t* n_miss, int hot_slots, int B, int H, int D, int max_ctx,
+                              int C, int K, hipStream_t st) {
+  dim3 grid((C + kRefinePerWG - 1) / kRefinePerWG, B);
+  const int HT = (H + 15) / 16;
+#define LS_REFINE(DD, TT)                                                                     \
+  hipLaunchKernelGGL((k_refine<DD, TT>), grid, dim3(256), 0, st, q, w, k8, cand, ws.fs, H, \
+                     max_ctx, C)
+  if (D == 128) {
+    if (HT == 1) LS_REFINE(128, 1); else if (HT == 2) LS_REFINE(128, 2);
+    else if (HT == 3) LS_REFINE(128, 3); else LS_REFINE(128, 4);
+  } else {
+    if (HT == 1) LS_REFINE(64, 1); else if (HT == 2) LS_REFINE(64, 2);
+    else if (HT == 3) LS_REFINE(64, 3); else LS_REFINE(64, 4);
+  }
+#undef LS_REFINE
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_topk, dim3(B), dim3(kTopkThreads), 0, st, cand, ws.fs, topk, topk_score,
+                     pos2slot, rows, n_miss, ws.miss_pos, hot_slots, max_ctx, C, K);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------ hot resolve (A5) ----
+// Standalone resolve of an existing selection (one workgroup per request):
+// the selection is ascending and -1 padded.
+__global__ __launch_bounds__(256) void k_hot_resolve(const int32_t* __restrict__ topk,
+                                                     const int32_t* __restrict__ pos2slot,
+                                                     int32_t* __restrict__ rows,
+                                                     int32_t* __restrict__ n_miss,
+                                                     int32_t* __restrict__ miss_pos,
+                                                     int hot_slots, int max_ctx, int K) {
+  __shared__ uint32_t scan_sh[4];
+  const int b = blockIdx.x;
+  const int32_t* tb = topk + (size_t)b * K;
+  uint32_t nv = 0;
+  for (int i = threadIdx.x; i < K; i += 256) nv += (tb[i] >= 0) ? 1u : 0u;
+  uint32_t n_sel;
+  block_excl_scan<256>(nv, scan_sh, &n_sel);
+  const int32_t* p2s = pos2slot + (size_t)b * max_ctx;
+  const int per = (K + 255) / 256;
+  const int i0 = threadIdx.x * per, i1 = min(i0 + per, (int)n_sel);
+  uint32_t c_miss = 0;
+  for (int i = i0; i < i1; i++) c_miss += (p2s[tb[i]] < 0) ? 1u : 0u;
+  uint32_t tot;
+  uint32_t o = block_excl_scan<256>(c_miss, scan_sh, &tot);
+  int32_t* rb = rows + (size_t)b * K;
+  int32_t* mb = miss_pos + (size_t)b * K;
+  for (int i = i0; i < i1; i++) {
+    const int32_t p = tb[i];
+    const int32_t slot = p2s[p];
+    if (slot >= 0) {
+      rb[i] = slot;
+    } else {
+      rb[i] = hot_slots + (int32_t)o;
+      mb[o] = p;
+      o++;
+    }
+  }
+  for (int i = (int)n_sel + threadIdx.x; i < K; i += 256) rb[i] = -1;
+  if (threadIdx.x == 0) n_miss[b] = (int32_t)tot;
+}
+
+hipError_t launch_hot_resolve(const int32_t* topk, const int32_t* pos2slot, int32_t* rows,
+                              int32_t* n_miss, int32_t* miss_pos, int hot_slots, int B,
+                              int max_ctx, int K, hipStream_t st) {
+  hipLaunchKernelGGL(k_hot_resolve, dim3(B), dim3(256), 0, st, topk, pos2slot, rows, n_miss,
+                     miss_pos, hot_slots, max_ctx, K);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- miss gather (A6) ---
+// hot[b, hot_slots + j] := pool[b, miss_pos[b, j]] for j < n_miss[b], in
+// 16-byte pieces spread over the workgroups of the request.  The pool may
+// be pinned host memory (reads then cross PCIe).
+constexpr int kGatherWGPerReq = 16;
+
+__global__ __launch_bounds__(256) void k_hot_gather(const int32_t* __restrict__ miss_pos,
+                                                    const int32_t* __restrict__ n_miss,
+                                                    const uint4* pool, uint4* __restrict__ hot,
+                                                    int hot_slots, int max_ctx, int K,
+                                                    int chunks) {
+  const int b = blockIdx.y;
+  const int nm = n_miss[b];
+  const int64_t total = (int64_t)nm * chunks;
+  const int64_t per = (total + gridDim.x - 1) / gridDim.x;
+  const int64_t i0 = (int64_t)blockIdx.x * per;
+  const int64_t i1 = min(i0 + per, total);
+  const int32_t* mp = miss_pos + (size_t)b * K;
+  const size_t pool_base = (size_t)b * max_ctx;
+  const size_t hot_base = (size_t)b * (hot_slots + K) + hot_slots;
+  for (int64_t i = i0 + threadIdx.x; i < i1; i += 256) {
+    const int j = (int)(i / chunks), c = (int)(i % chunks);
+    const int32_t p = mp[j];
+    hot[(hot_base + j) * chunks + c] = pool[(pool_base + p) * chunks + c];
+  }
+}
+
+hipError_t launch_hot_gather(const int32_t* miss_pos, const int32_t* n_miss, const void* pool,
+                             void* hot, int hot_slots, int B, int max_ctx, int K, int row_elems,
+                             hipStream_t st) {
+  const int chunks = row_elems * 2 / 16;
+  hipLaunchKernelGGL(k_hot_gather, dim3(kGatherWGPerReq, B), dim3(256), 0, st, miss_pos, n_miss,
+                     (const uint4*)pool, (uint4*)hot, hot_slots, max_ctx, K, chunks);
+  return hipGetLastError();
+}
+
+}  // namespace ls

@@ -106,7 +106,7 @@ void carve_coarse(Carve& c, const ls_idx_desc* d, ls::CoarseWS* ws) {
   const size_t B = d->batch, L = d->max_ctx;
   ls::CoarseWS w;
   w.hist = c.take<uint32_t>(B * ls::kCoarseBins);
-  w.ctr = c.take<uint32_t>(B * 2);
+  w.ctr = c.take<uint32_t>(B * ls::kCtrStride);
   w.scores = c.take<int32_t>(B * L);
   w.bitmap_words = bitmap_words(d->max_ctx);
   w.bitmap = c.take<uint32_t>(B * w.bitmap_words);
@@ -118,7 +118,6 @@ void carve_coarse(Carve& c, const ls_idx_desc* d, ls::CoarseWS* ws) {
 void carve_refine(Carve& c, const ls_idx_desc* d, ls::RefineWS* ws) {
   const size_t B = d->batch;
   ls::RefineWS w;
-  w.ctr = c.take<uint32_t>(B);
   w.fs = c.take<int64_t>(B * d->n_cand);
   w.miss_pos = c.take<int32_t>(B * d->topk);
   if (ws) *ws = w;

@@ -13,7 +13,9 @@ namespace ls {
 // 6 mantissa bits, both signs (see coarse_bucket in k_index.hip).
 constexpr int kCoarseBins = 3328;
 // Positions handled by one workgroup of the candidate filter.
-constexpr int kSelectChunk = 8192;
+constexpr int kSelectChunk = 4096;
+// Per-request counters sit on their own 128-byte lines (32 words apart).
+constexpr int kCtrStride = 32;
 // Tokens scored by one workgroup of the coarse kernel.
 constexpr int kCoarseTokPerWG = 2048;
 // Candidates scored by one workgroup of the refine kernel.
@@ -25,13 +27,12 @@ struct CoarseWS {
   uint32_t* bitmap;    // [B, bitmap_words]
   int32_t* tie_s;      // [B, max_ctx]
   int32_t* tie_p;      // [B, max_ctx]
-  uint32_t* ctr;       // [B, 2] tie count, done counter;   zero between calls
+  uint32_t* ctr;       // [B, kCtrStride] tie count (word 0); zero between calls
   int bitmap_words;
 };
 
 struct RefineWS {
   int64_t* fs;         // [B, n_cand]
-  uint32_t* ctr;       // [B] done counter;                 zero between calls
   int32_t* miss_pos;   // [B, topk]
 };
 
