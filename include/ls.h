@@ -115,7 +115,8 @@ typedef struct {
  * g, dim d) is at base[(b * kv_rows_per_req + r) * kv_row_stride
  * + g * kv_head_stride + d].  For a latent (MLA-style) cache pass the same
  * base for K and V: V is then the first v_dim elements of the K row.
- * n_splits: number of row splits per request (0 = chosen by the library).  */
+ * n_splits: number of row splits per request (0 = chosen by the library;
+ * the latent-layout kernel raises it so that no split exceeds 1024 rows).  */
 typedef struct {
     int32_t batch, n_q_heads, n_kv_heads, qk_dim, v_dim, topk;
     int64_t kv_rows_per_req, kv_row_stride, kv_head_stride;

@@ -291,6 +291,28 @@ def test_attention_mla_edge_rows(ls):
     assert_attention_close(out[1:], lse[1:], e_out[1:], e_lse[1:], "edge")
 
 
+def test_attention_mla_score_jump_recomputes(ls):
+    # rows after the first 32-row tile score thousands of log2 units above the
+    # first tile's maximum: the kernel must fall back to its exact-max pass
+    B, Hq, K, S = 2, 128, 256, 64
+    q, kv, rows = mla_case(B, Hq, [256, 200], K, S, seed=77)
+    g = torch.Generator().manual_seed(78)
+    kvf = kv.float()
+    for b in range(B):
+        late = rows[b, 40:60].long()
+        # only the 64 rope dims grow (scores jump ~250 log2 units); V, the
+        # first 512 dims, stays N(0, 1) so the output keeps its usual scale
+        kvf[b, late, 512:] = 40.0 * q[b, (torch.arange(20) * 5) % Hq, 512:].float() + \
+            0.1 * torch.randn(20, 64, generator=g)
+    kv = kvf.to(torch.bfloat16)
+    kvd = kv.to(DEV)
+    out, lse = ls.sparse_attn_decode(q.to(DEV), kvd, kvd, rows.to(DEV), 1 / math.sqrt(192), 1,
+                                     512, S + K, 576, n_splits=1)
+    e_out, e_lse = oracle_mla(q, kv, rows, 1 / math.sqrt(192))
+    assert np.isfinite(np_(lse)).all()
+    assert_attention_close(out, lse, e_out, e_lse, "score jump")
+
+
 @pytest.mark.parametrize("Hq,n_kv,D", [(8, 8, 64), (8, 2, 64), (4, 1, 128), (6, 3, 32)])
 def test_attention_mha_parity(ls, Hq, n_kv, D):
     B, L, K = 2, 300, 128

@@ -20,187 +20,351 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 // ---------------------------------------------------------------- MFMA path --
 //
-// Workgroup = NW waves x 16 query heads, one request, one split of the row
-// list.  Rows are staged 32 at a time in LDS, row-major (padded stride).
-// Q stays in VGPRs as the B operand of S^T = K Q^T (lane: head n = lane%16,
-// dims 8*(lane/16) .. +8 of each 32-dim step); the K tile gives the A
-// operand (16 rows x 8 dims per lane).  The S^T accumulator leaves every
-// lane with 8 scores of its own head, rows 4g..4g+3 and 16+4g..16+4g+3
-// (g = lane/16); converted to bf16 they are the B operand of O^T = V^T P^T
-// with that row order.  The matching A operand -- 8 rows of one V column --
-// comes straight from the row-major tile through the gfx950 LDS transpose
-// read (ds_read_b64_tr_b16): within each 16-lane group, lane j points at
-// row base + j/4, columns 4*(j%4) .. +3, and lane i receives column i of
-// those 4 rows; two such reads (row bases 4g and 16+4g) give the 8 rows.
-// O^T accumulates 16 dims x 16 heads per MFMA, so every lane owns one head's
-// outputs and the online-softmax rescale is lane-local.
+// Workgroup = 4 waves x 32 query heads (the 128 heads of a request), one
+// request, one split of the row list; one workgroup (one wave per SIMD) per
+// CU, which leaves every wave 512 registers: Q stays in VGPRs, the O
+// accumulator in AGPRs.  Products use v_mfma_f32_32x32x16_bf16, so every
+// LDS byte read feeds 32 heads.
+//
+// Rows are staged 32 at a time in LDS by the gfx950 global->LDS DMA load
+// (global_load_lds_dwordx4: lane L's 16 bytes land at base + 16 L) into a
+// ring of NBUF buffers: NBUF-1 tiles stream in while one computes, and no
+// VGPRs hold tile data.  Every row is read once per request and split.
+//
+// LDS tile layout: 16-byte chunk c (dims 8c .. 8c+7) of tile row r sits at
+// chunk slot c*32 + (r ^ 8*(c&1)).  DMA instruction k (1 KiB) fills slots
+// 64k .. 64k+63, i.e. chunks 2k and 2k+1 of all 32 rows; lane L loads row
+// (L&31) ^ 8*(L>>5), chunk 2k + (L>>5).  The row swizzle keeps both reads
+// below free of bank conflicts.
+//
+// 32x32 MFMA layouts (lane l, half = l/32): A holds row l%32, k = 8 half..+7;
+// B holds column l%32, k = 8 half..+7; D register r holds row
+// 8(r/4) + 4 half + r%4 of column l%32.
+//
+// S^T = K Q^T: A = tile rows (16 dims per step), B = Q^T (head l%32).  The
+// accumulator leaves lane (head n, half) with the scores of rows
+// 8j + 4 half + i; its registers 8s..8s+7, converted to bf16, are the B
+// operand of step s (rows 16s + 8e' + 4 half + i) of O^T = V^T P^T.  The
+// matching A operand -- those 8 rows of one V column -- comes from the same
+// tile through the LDS transpose read (ds_read_b64_tr_b16): within a 16-lane
+// group, lane j points at row base + j/4, columns 4(j%4) .. +3, and lane i
+// receives column i of those 4 rows; two reads (row bases 16s + 4 half and
+// +8) give the 8 rows.  O^T lands with the head in the lane, so the online
+// softmax stays lane-local (a head's 32 rows sit in lanes l and l+32).
+//
+// No accumulator rescale in the loop: each head's exponent base is the
+// maximum score of its first valid tile (the accumulator is still zero then),
+// and later tiles may exceed it by up to 2^64 -- probabilities and sums stay
+// far inside the fp32/bf16 range and the final o / l is scale-free.  If a
+// head's score ever exceeds its base by more, the workgroup recomputes its
+// split with the exact maximum seen in the first pass as the base (so every
+// probability is <= 1).  This keeps the 256-value accumulator in AGPRs, out
+// of reach of VALU code.
 constexpr int kTileR = 32;
+constexpr int kAttnWaves = 4;
+constexpr int kAttnBufs = 4;
+constexpr int kHeadsPerWave = 32;
+constexpr float kBaseSlack = 64.f;  // log2 units a score may exceed its head's base
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ v4i16 lds_read_tr16(const uint16_t* p) {
+__device__ __forceinline__ v4i16 lds_read_tr16(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) v4i16*)(p));
 }
 
-template <int DQK, int DV, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(
+// Byte offset of (row r, chunk c) in a tile buffer.
+__device__ __forceinline__ int tile_off(int r, int c) {
+  return (c * kTileR + (r ^ ((c & 1) << 3))) * 16;
+}
+
+// Largest row range one workgroup handles (its row ids are staged in LDS).
+constexpr int kMaxSplitRows = kAttnMaxSplitRows;
+
+// Workgroup barrier without the release/acquire fences of __syncthreads:
+// LDS hazards are handled by the explicit waits at each use, and the empty
+// asm statements keep the compiler from moving memory operations across it.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt immediates (gfx9 encoding): vmcnt <= N, other counters free.
+constexpr int waitcnt_vm(int nvm) { return (nvm & 15) | (7 << 4) | (15 << 8) | ((nvm >> 4) << 14); }
+constexpr int kWaitLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+
+// Wait until at most `ahead` tiles of this wave's DMA (PER_WAVE instructions
+// each) are still in flight.  Immediates must be constants, hence the switch.
+template <int PER_WAVE>
+__device__ __forceinline__ void wait_tiles_ahead(int ahead) {
+  switch (ahead) {
+    case 0: __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER_WAVE)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * PER_WAVE)); break;
+    default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * PER_WAVE)); break;
+  }
+}
+
+template <int DQK, int DV, int NBUF>
+__global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ rows, uint16_t* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ part_o, float* __restrict__ part_lse, int Hq, int K,
+    uint16_t* __restrict__ part_o, float* __restrict__ part_lse, int Hq, int K,
     int64_t rows_per_req, int64_t row_stride, float scale_log2, int n_splits,
     int rows_per_split) {
-  constexpr int NT = NW * 64;
-  constexpr int KS = DQK + 8;     // LDS row stride of the tile (bf16 elements)
-  constexpr int QK_STEPS = DQK / 32;
-  constexpr int DT = DV / 16;
-  constexpr int CH = DQK / 8;     // 16-byte chunks per row
-  constexpr int CPT = NT / kTileR;              // chunk lanes per row
-  constexpr int LPT = (CH + CPT - 1) / CPT;     // chunk loads per thread per tile
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kTileR * KS];
+  constexpr int NW = kAttnWaves;
+  constexpr int QK_STEPS = DQK / 16;
+  constexpr int DT = DV / 32;
+  constexpr int CH = DQK / 8;              // 16-byte chunks per row
+  constexpr int TILE_BYTES = CH * kTileR * 16;
+  constexpr int N_DMA = TILE_BYTES / 1024;  // 1 KiB DMA instructions per tile
+  constexpr int DMA_PER_WAVE = N_DMA / NW;
+  static_assert(CH % 2 == 0 && N_DMA % NW == 0 && NBUF <= 4, "tile layout");
+  __shared__ __attribute__((aligned(1024))) uint8_t tiles[NBUF][TILE_BYTES];
+  __shared__ int32_t rid_lds[kMaxSplitRows + kTileR];
 
   const int split = blockIdx.x, b = blockIdx.z;
-  const int l = lane_id(), n = l & 15, g = l >> 4;
-  const int h = blockIdx.y * (16 * NW) + wave_id() * 16 + n;
+  const int l = lane_id(), w = wave_id();
+  const int n = l & 31, half = l >> 5;
+  const int h = blockIdx.y * (kHeadsPerWave * NW) + w * kHeadsPerWave + n;
   const bool h_ok = h < Hq;
-
-  v8bf qB[QK_STEPS];
-  {
-    const uint16_t* qh = q + ((size_t)b * Hq + (h_ok ? h : 0)) * DQK;
-#pragma unroll
-    for (int ks = 0; ks < QK_STEPS; ks++) {
-      v8u16 v = h_ok ? *(const v8u16*)(qh + 32 * ks + 8 * g) : v8u16{0, 0, 0, 0, 0, 0, 0, 0};
-      qB[ks] = __builtin_bit_cast(v8bf, v);
-    }
-  }
-  v4f oacc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; dt++) oacc[dt] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
 
   const int i_begin = split * rows_per_split;
   const int i_end = min(i_begin + rows_per_split, K);
-  const int32_t* rb = rows + (size_t)b * K;
-  const uint16_t* kvb = kv + (size_t)b * rows_per_req * row_stride;
-  // this thread stages row lr of every tile, chunks lc, lc + CPT, ...
-  const int lr = threadIdx.x % kTileR, lc = threadIdx.x / kTileR;
+  const int n_rows = max(i_end - i_begin, 0);
+  const int n_tiles = (n_rows + kTileR - 1) / kTileR;
+  const int32_t* rb = rows + (size_t)b * K + i_begin;
+  for (int i = threadIdx.x; i < n_tiles * kTileR; i += NW * 64)
+    rid_lds[i] = i < n_rows ? rb[i] : -1;
 
-  for (int tile0 = i_begin; tile0 < i_end; tile0 += kTileR) {
-    const int i = tile0 + lr;
-    const int32_t rid = (i < i_end) ? rb[i] : -1;
-    // every wave holds rows 0..31 in lanes 0..31: the tile's validity mask
-    const uint32_t vmask = (uint32_t)__ballot(rid >= 0);
-    const uint16_t* src = kvb + (size_t)(rid >= 0 ? rid : 0) * row_stride;
-    // two batches of chunk loads keep the staging registers small: the first
-    // is in flight across the barrier, the second right after it
-    constexpr int LA = (LPT + 1) / 2;
-    uint4 v[LA];
-#pragma unroll
-    for (int j = 0; j < LA; j++) {
-      const int c = lc + CPT * j;
-      v[j] = (c < CH && rid >= 0) ? *(const uint4*)(src + 8 * c) : make_uint4(0, 0, 0, 0);
-    }
-    __syncthreads();  // the previous tile is no longer read
-#pragma unroll
-    for (int j = 0; j < LA; j++) {
-      const int c = lc + CPT * j;
-      if (c < CH) *(uint4*)&Ks[lr * KS + 8 * c] = v[j];
-    }
-#pragma unroll
-    for (int j = LA; j < LPT; j++) {
-      const int c = lc + CPT * j;
-      v[j - LA] = (c < CH && rid >= 0) ? *(const uint4*)(src + 8 * c) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = LA; j < LPT; j++) {
-      const int c = lc + CPT * j;
-      if (c < CH) *(uint4*)&Ks[lr * KS + 8 * c] = v[j - LA];
-    }
-    __syncthreads();
-
-    // S^T = K Q^T for rows 0..15 and 16..31
-    v4f sacc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+  // B operand of S^T = K Q^T: head n, dims 16 ks + 8 half .. +7
+  v8bf qB[QK_STEPS];
+  {
+    const uint16_t* qh = q + ((size_t)b * Hq + (h_ok ? h : 0)) * DQK + 8 * half;
 #pragma unroll
     for (int ks = 0; ks < QK_STEPS; ks++) {
-#pragma unroll
-      for (int rt = 0; rt < 2; rt++) {
-        v8u16 a = *(const v8u16*)&Ks[(16 * rt + n) * KS + 32 * ks + 8 * g];
-        sacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), qB[ks],
-                                                            sacc[rt], 0, 0, 0);
-      }
-    }
-    float s[8];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 8; e++) {
-      const int r = (e < 4) ? 4 * g + e : 16 + 4 * g + (e - 4);
-      const float sv = (e < 4) ? sacc[0][e] : sacc[1][e - 4];
-      s[e] = ((vmask >> r) & 1u) ? sv * scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, s[e]);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    const float m_new = fmaxf(m_run, tmax);
-    // Branch-free when no row is valid yet (m_new = -inf): alpha = 0 on a
-    // zero accumulator and every p = 0.  MFMAs stay outside divergent code.
-    const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_ref);
-    float psum = 0.f;
-    uint16_t pb[8];
-#pragma unroll
-    for (int e = 0; e < 8; e++) {
-      const float p = exp2f(s[e] - m_ref);
-      psum += p;
-      pb[e] = f32_to_bf16_rne(p);
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;  // stays -inf until a valid row appears
-    v8u16 pv = {pb[0], pb[1], pb[2], pb[3], pb[4], pb[5], pb[6], pb[7]};
-    const v8bf pB = __builtin_bit_cast(v8bf, pv);
-    // transpose-read addresses: lane j of the group -> row base + j/4, cols 4*(j%4)
-    const uint16_t* tr0 = &Ks[(4 * g + (n >> 2)) * KS + 4 * (n & 3)];
-    const uint16_t* tr1 = tr0 + 16 * KS;
-#pragma unroll
-    for (int dt = 0; dt < DT; dt++) {
-      oacc[dt] *= alpha;
-      const v4i16 a0 = lds_read_tr16(tr0 + 16 * dt);
-      const v4i16 a1 = lds_read_tr16(tr1 + 16 * dt);
-      const v8u16 a = {(uint16_t)a0[0], (uint16_t)a0[1], (uint16_t)a0[2], (uint16_t)a0[3],
-                       (uint16_t)a1[0], (uint16_t)a1[1], (uint16_t)a1[2], (uint16_t)a1[3]};
-      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), pB,
-                                                          oacc[dt], 0, 0, 0);
+      v8u16 v = h_ok ? *(const v8u16*)(qh + 16 * ks) : v8u16{0, 0, 0, 0, 0, 0, 0, 0};
+      qB[ks] = __builtin_bit_cast(v8bf, v);
     }
   }
+  __shared__ int redo;
+  if (threadIdx.x == 0) redo = 0;
+  v16f oacc[DT];
+  float m_used, l_run, m_seen = -INFINITY;
+  bool over = false;
+  // Q and the row ids have landed before the loop, so the compiler has no
+  // load of its own outstanding inside it (it would otherwise wait on every
+  // iteration, which would also drain the tile DMA in flight).
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();  // row ids staged
 
-  float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
-  l_tot += __shfl_xor(l_tot, 32, kWave);
+  const uint16_t* kvb = kv + (size_t)b * rows_per_req * row_stride;
+  // the tile row this lane loads in every DMA instruction, and its chunk parity
+  const int dma_row = (l & 31) ^ (half << 3);
+
+  // Tile DMA: wave w issues instructions k = w, w + NW, ...  The instruction
+  // is written out (M0 = LDS destination) so that the compiler does not
+  // order LDS reads of other buffers behind it; the waits on it are the
+  // explicit vmcnt waits below.  It has no VGPR destination, so nothing it
+  // writes can be reused while it is in flight.
+  auto issue_dma = [&](int t) {
+    const int32_t rid = rid_lds[t * kTileR + dma_row];
+    const uint8_t* src = (const uint8_t*)(kvb + (size_t)(rid >= 0 ? rid : 0) * row_stride) +
+                         16 * (2 * w + half);
+    const uint32_t dst =
+        (uint32_t)(uintptr_t)(lds_void*)(&tiles[t % NBUF][0]) + 1024u * w;
+#pragma unroll
+    for (int j = 0; j < DMA_PER_WAVE; j++) {
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(dst + 1024u * NW * j);
+      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                   :
+                   : "v"(src + 32 * NW * j), "s"(m0)
+                   : "memory", "m0");
+    }
+  };
+
+  // Per-lane LDS byte offsets; every read below is base + compile-time step.
+  // QK A operand: row n, chunk 2 ks + half (parity = half): 1024 B per ks.
+  const int qk_off = tile_off(n, half);
+  // transpose read: 16-lane group G = l/16 covers columns 16 (G&1) .. +15 of
+  // a 32-dim tile; lane j = l%16 -> row 16 s + 4 half + j/4 (+8), chunk
+  // 4 dt + 2 (G&1) + (j%4)/2, byte 8 (j&1): 2048 B per dt, 256 B per s.
+  const int j16 = l & 15, cb = (l >> 4) & 1, par = (j16 & 3) >> 1;
+  const int tr_off0 = (2 * cb + par) * 512 + (((4 * half + (j16 >> 2)) ^ (par << 3)) * 16) +
+                      8 * (j16 & 1);
+  const int tr_off1 = (2 * cb + par) * 512 + (((4 * half + (j16 >> 2) + 8) ^ (par << 3)) * 16) +
+                      8 * (j16 & 1);
+
+  // pass 0: base = first valid tile's max; pass 1 (only if a score overran
+  // its base by more than kBaseSlack): base = the exact max from pass 0
+  for (int pass = 0; pass < 2; pass++) {
+  if (pass == 1) {
+    if (!redo) break;
+    m_used = m_seen;
+  } else {
+    m_used = -INFINITY;
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; dt++) oacc[dt] = v16f{};
+  l_run = 0.f;
+  for (int t = 0; t < NBUF - 1 && t < n_tiles; t++) issue_dma(t);
+  for (int t = 0; t < n_tiles; t++) {
+    // refill the buffer freed at the end of the previous step
+    if (t + NBUF - 1 < n_tiles) issue_dma(t + NBUF - 1);
+    // loads complete in order: at most `ahead` later tiles still in flight
+    wait_tiles_ahead<DMA_PER_WAVE>(min(n_tiles - 1 - t, NBUF - 1));
+    wg_barrier();  // tile t is in LDS for every wave
+    const uint8_t* cur = &tiles[t % NBUF][0];
+    const uint32_t vmask =
+        (uint32_t)__ballot(l < kTileR && rid_lds[t * kTileR + (l & 31)] >= 0);
+
+    // S^T = K Q^T (32 rows x 32 heads): operand reads run 4 steps ahead of
+    // their MFMAs, and even/odd steps feed two accumulators so consecutive
+    // MFMAs never wait on each other.
+    v16f sacc0 = {}, sacc1 = {};
+    {
+      v8u16 ab[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) ab[i] = *(const v8u16*)(cur + qk_off + 1024 * i);
+#pragma unroll
+      for (int ks = 0; ks < QK_STEPS; ks++) {
+        const v8u16 a = ab[ks & 3];
+        if (ks + 4 < QK_STEPS) ab[ks & 3] = *(const v8u16*)(cur + qk_off + 1024 * (ks + 4));
+        if (ks & 1)
+          sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), qB[ks],
+                                                          sacc1, 0, 0, 0);
+        else
+          sacc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), qB[ks],
+                                                          sacc0, 0, 0, 0);
+      }
+      // scheduling contract for the loop above: 4 reads, then MFMA/read pairs
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < QK_STEPS - 4; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
+    const v16f sacc = sacc0 + sacc1;
+    // phase fences for the scheduler: keep the PV operand reads from being
+    // hoisted over QK and the softmax, where they would starve QK of VGPRs
+    __builtin_amdgcn_sched_barrier(0);
+    float sv[16];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; r++) sv[r] = sacc[r] * scale_log2;
+    if (vmask != 0xFFFFFFFFu) {  // only a split's last tile can be partial
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int row = 8 * (r >> 2) + 4 * half + (r & 3);
+        sv[r] = ((vmask >> row) & 1u) ? sv[r] : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; r++) tmax = fmaxf(tmax, sv[r]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    m_seen = fmaxf(m_seen, tmax);
+    if (m_used == -INFINITY) m_used = tmax;         // first valid tile of this head
+    else over = over || (tmax > m_used + kBaseSlack);  // never in pass 1
+    const float m_ref = (m_used == -INFINITY) ? 0.f : m_used;
+    v8bf pB[2];
+    {
+      uint16_t pb[16];
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const float p = __builtin_amdgcn_exp2f(sv[r] - m_ref);  // exp2(-inf) = 0
+        psum += p;
+        pb[r] = f32_to_bf16_rne(p);
+      }
+      l_run += psum;
+      const v8u16 p0 = {pb[0], pb[1], pb[2], pb[3], pb[4], pb[5], pb[6], pb[7]};
+      const v8u16 p1 = {pb[8], pb[9], pb[10], pb[11], pb[12], pb[13], pb[14], pb[15]};
+      pB[0] = __builtin_bit_cast(v8bf, p0);
+      pB[1] = __builtin_bit_cast(v8bf, p1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // O^T += V^T P^T, two 16-row steps per 32-dim tile; the transpose reads
+    // of tile dt+1 are issued before the MFMAs of tile dt
+    {
+      auto tr_read = [&](int dt, int ss) {
+        const v4i16 a0 = lds_read_tr16(cur + tr_off0 + 2048 * dt + 256 * ss);
+        const v4i16 a1 = lds_read_tr16(cur + tr_off1 + 2048 * dt + 256 * ss);
+        const v8u16 a = {(uint16_t)a0[0], (uint16_t)a0[1], (uint16_t)a0[2], (uint16_t)a0[3],
+                         (uint16_t)a1[0], (uint16_t)a1[1], (uint16_t)a1[2], (uint16_t)a1[3]};
+        return a;
+      };
+      v8u16 va0 = tr_read(0, 0), va1 = tr_read(0, 1);
+#pragma unroll
+      for (int dt = 0; dt < DT; dt++) {
+        const v8u16 c0 = va0, c1 = va1;
+        if (dt + 1 < DT) {
+          va0 = tr_read(dt + 1, 0);
+          va1 = tr_read(dt + 1, 1);
+        }
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, c0), pB[0],
+                                                           oacc[dt], 0, 0, 0);
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, c1), pB[1],
+                                                           oacc[dt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+      for (int i = 0; i < DT - 1; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    wg_barrier();  // every wave is done reading `cur` before it is refilled
+  }
+  if (pass == 0) {
+    if (over) redo = 1;
+    __syncthreads();
+  }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
   if (!h_ok) return;
   const bool any = l_tot > 0.f;
   const float inv = any ? 1.f / l_tot : 0.f;
-  const float lse2 = any ? m_run + log2f(l_tot) : -INFINITY;
+  const float lse2 = any ? m_used + log2f(l_tot) : -INFINITY;
+  // lane (head n, half): oacc[dt][r] = O[head][32 dt + 8 (r/4) + 4 half + r%4]
   if (n_splits == 1) {
-    uint16_t* ob = out + ((size_t)b * Hq + h) * DV;
+    uint16_t* ob = out + ((size_t)b * Hq + h) * DV + 4 * half;
 #pragma unroll
-    for (int dt = 0; dt < DT; dt++) {
-      const int d = 16 * dt + 4 * g;
-      uint2 v;
-      v.x = (uint32_t)f32_to_bf16_rne(oacc[dt][0] * inv) |
-            ((uint32_t)f32_to_bf16_rne(oacc[dt][1] * inv) << 16);
-      v.y = (uint32_t)f32_to_bf16_rne(oacc[dt][2] * inv) |
-            ((uint32_t)f32_to_bf16_rne(oacc[dt][3] * inv) << 16);
-      *(uint2*)(ob + d) = v;
-    }
-    if (g == 0) lse[(size_t)b * Hq + h] = any ? lse2 * kLn2 : -INFINITY;
+    for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) {
+        uint2 v;
+        v.x = (uint32_t)f32_to_bf16_rne(oacc[dt][4 * jj] * inv) |
+              ((uint32_t)f32_to_bf16_rne(oacc[dt][4 * jj + 1] * inv) << 16);
+        v.y = (uint32_t)f32_to_bf16_rne(oacc[dt][4 * jj + 2] * inv) |
+              ((uint32_t)f32_to_bf16_rne(oacc[dt][4 * jj + 3] * inv) << 16);
+        *(uint2*)(ob + 32 * dt + 8 * jj) = v;
+      }
+    if (half == 0) lse[(size_t)b * Hq + h] = any ? lse2 * kLn2 : -INFINITY;
   } else {
+    // per-split output, normalised by its own sum, stored as bf16 (the merge
+    // weights and the split's log-sum-exp stay fp32)
     const size_t ps = ((size_t)b * Hq + h) * n_splits + split;
-    float* po = part_o + ps * DV;
+    uint16_t* po = part_o + ps * DV + 4 * half;
 #pragma unroll
-    for (int dt = 0; dt < DT; dt++) {
-      const int d = 16 * dt + 4 * g;
-      *(float4*)(po + d) = make_float4(oacc[dt][0] * inv, oacc[dt][1] * inv,
-                                       oacc[dt][2] * inv, oacc[dt][3] * inv);
-    }
-    if (g == 0) part_lse[ps] = lse2;
+    for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) {
+        uint2 v;
+        v.x = (uint32_t)f32_to_bf16_rne(oacc[dt][4 * jj] * inv) |
+              ((uint32_t)f32_to_bf16_rne(oacc[dt][4 * jj + 1] * inv) << 16);
+        v.y = (uint32_t)f32_to_bf16_rne(oacc[dt][4 * jj + 2] * inv) |
+              ((uint32_t)f32_to_bf16_rne(oacc[dt][4 * jj + 3] * inv) << 16);
+        *(uint2*)(po + 32 * dt + 8 * jj) = v;
+      }
+    if (half == 0) part_lse[ps] = lse2;
   }
 }
 
@@ -300,7 +464,7 @@ __global__ __launch_bounds__(256) void k_attn_valu(
 
 // ------------------------------------------------------------------ combine --
 // out = sum_j o_j 2^(lse_j - L) with L = log2 sum_j 2^lse_j; lse = L ln 2.
-__global__ __launch_bounds__(128) void k_combine(const float* __restrict__ part_o,
+__global__ __launch_bounds__(128) void k_combine(const uint16_t* __restrict__ part_o,
                                                  const float* __restrict__ part_lse,
                                                  uint16_t* __restrict__ out,
                                                  float* __restrict__ lse, int DV,
@@ -318,21 +482,21 @@ __global__ __launch_bounds__(128) void k_combine(const float* __restrict__ part_
   float W = 0.f;
   for (int j = 0; j < n_splits; j++) W += exp2f(pl[j] - M);
   const float L = M + log2f(W);
-  const float* po = part_o + bh * n_splits * DV;
+  const uint16_t* po = part_o + bh * n_splits * DV;
   for (int d = threadIdx.x * 4; d < DV; d += 128 * 4) {
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
     for (int j = 0; j < n_splits; j++) {
       const float wj = exp2f(pl[j] - L);
       if (wj == 0.f) continue;
-      const float4 v = *(const float4*)(po + (size_t)j * DV + d);
-      a.x += wj * v.x;
-      a.y += wj * v.y;
-      a.z += wj * v.z;
-      a.w += wj * v.w;
+      const uint2 v = *(const uint2*)(po + (size_t)j * DV + d);
+      a0 += wj * bf16_to_f32((uint16_t)(v.x & 0xFFFF));
+      a1 += wj * bf16_to_f32((uint16_t)(v.x >> 16));
+      a2 += wj * bf16_to_f32((uint16_t)(v.y & 0xFFFF));
+      a3 += wj * bf16_to_f32((uint16_t)(v.y >> 16));
     }
     uint2 pk;
-    pk.x = (uint32_t)f32_to_bf16_rne(a.x) | ((uint32_t)f32_to_bf16_rne(a.y) << 16);
-    pk.y = (uint32_t)f32_to_bf16_rne(a.z) | ((uint32_t)f32_to_bf16_rne(a.w) << 16);
+    pk.x = (uint32_t)f32_to_bf16_rne(a0) | ((uint32_t)f32_to_bf16_rne(a1) << 16);
+    pk.y = (uint32_t)f32_to_bf16_rne(a2) | ((uint32_t)f32_to_bf16_rne(a3) << 16);
     *(uint2*)(ob + d) = pk;
   }
   if (threadIdx.x == 0) lse[bh] = L * kLn2;
@@ -346,11 +510,14 @@ bool attn_uses_mfma(int Hq, int n_kv, int qk_dim, int v_dim, const void* k, cons
 
 int attn_auto_splits(int B, int Hq, int K, bool mfma) {
   if (!mfma) return 1;
-  const int groups = (Hq + 63) / 64;
-  int s = (512 + B * groups - 1) / (B * groups);
+  // one workgroup per CU: aim for about 256 workgroups
+  const int groups = (Hq + kHeadsPerWave * kAttnWaves - 1) / (kHeadsPerWave * kAttnWaves);
+  int s = (256 + B * groups - 1) / (B * groups);
   const int max_s = (K + kTileR - 1) / kTileR;
   if (s > 16) s = 16;
   if (s > max_s) s = max_s;
+  const int min_s = (K + kMaxSplitRows - 1) / kMaxSplitRows;
+  if (s < min_s) s = min_s;
   if (s < 1) s = 1;
   return s;
 }
@@ -358,8 +525,11 @@ int attn_auto_splits(int B, int Hq, int K, bool mfma) {
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   if (attn_uses_mfma(a.Hq, a.n_kv, a.qk_dim, a.v_dim, a.k, a.v)) {
     const int rps = ((a.K + a.n_splits - 1) / a.n_splits + kTileR - 1) / kTileR * kTileR;
-    dim3 grid(a.n_splits, (a.Hq + 63) / 64, a.B);
-    hipLaunchKernelGGL((k_attn_mfma<576, 512, 4>), grid, dim3(256), 0, st, a.q, a.k, a.rows,
+    if (rps > kMaxSplitRows) return hipErrorInvalidValue;
+    const int hpw = kHeadsPerWave * kAttnWaves;
+    dim3 grid(a.n_splits, (a.Hq + hpw - 1) / hpw, a.B);
+    hipLaunchKernelGGL((k_attn_mfma<576, 512, kAttnBufs>), grid, dim3(64 * kAttnWaves), 0, st,
+                       a.q, a.k, a.rows,
                        a.out, a.lse, a.part_o, a.part_lse, a.Hq, a.K, a.rows_per_req,
                        a.row_stride, a.scale * kLog2e, a.n_splits, rps);
   } else {

@@ -128,14 +128,16 @@ int attn_splits(const ls_attn_desc* d, const void* k, const void* v) {
   if (!mfma) return 1;
   int s = d->n_splits > 0 ? d->n_splits : ls::attn_auto_splits(d->batch, d->n_q_heads, d->topk, true);
   const int max_s = (d->topk + 31) / 32;
-  return s > max_s ? max_s : s;
+  const int min_s = (d->topk + ls::kAttnMaxSplitRows - 1) / ls::kAttnMaxSplitRows;
+  if (s > max_s) s = max_s;
+  return s < min_s ? min_s : s;
 }
 
-void carve_attn(Carve& c, const ls_attn_desc* d, int splits, float** part_o, float** part_lse) {
+void carve_attn(Carve& c, const ls_attn_desc* d, int splits, uint16_t** part_o,
+                float** part_lse) {
   const size_t BH = (size_t)d->batch * d->n_q_heads;
-  // size for the largest split count the MFMA path can choose
   const size_t s = splits > 1 ? splits : 0;
-  float* po = c.take<float>(BH * s * d->v_dim);
+  uint16_t* po = c.take<uint16_t>(BH * s * d->v_dim);
   float* pl = c.take<float>(BH * s);
   if (part_o) *part_o = po;
   if (part_lse) *part_lse = pl;
@@ -150,7 +152,9 @@ int attn_ws_splits(const ls_attn_desc* d) {
   if (!latent) return 1;
   int s = d->n_splits > 0 ? d->n_splits : ls::attn_auto_splits(d->batch, d->n_q_heads, d->topk, true);
   const int max_s = (d->topk + 31) / 32;
-  return s > max_s ? max_s : s;
+  const int min_s = (d->topk + ls::kAttnMaxSplitRows - 1) / ls::kAttnMaxSplitRows;
+  if (s > max_s) s = max_s;
+  return s < min_s ? min_s : s;
 }
 
 size_t ws_size(int32_t op, const void* desc) {

@@ -250,11 +250,9 @@ __device__ Threshold block_threshold(const Get& get, int n, uint32_t need, Selec
 }
 
 // ----------------------------------------------------------------------------
-// float -> bfloat16 bits, round to nearest even (finite inputs).
+// float -> bfloat16 bits, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

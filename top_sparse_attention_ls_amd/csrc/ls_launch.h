@@ -71,13 +71,17 @@ struct AttnArgs {
   const int32_t* rows;
   uint16_t* out;
   float* lse;
-  float* part_o;
+  uint16_t* part_o;   // per-split outputs, bf16
   float* part_lse;
   int B, Hq, n_kv, qk_dim, v_dim, K;
   int64_t rows_per_req, row_stride, head_stride;
   float scale;
   int n_splits;
 };
+
+// Rows one workgroup of the latent attention kernel handles at most; the
+// split count is raised to keep every split within it.
+constexpr int kAttnMaxSplitRows = 1024;
 
 // Whether the MFMA path serves these shapes (else the generic kernel).
 bool attn_uses_mfma(int Hq, int n_kv, int qk_dim, int v_dim, const void* k, const void* v);
