@@ -16,7 +16,6 @@ Prints one JSON line with:
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -51,20 +50,30 @@ def algorithmic_bytes(wl, n_miss_total: int) -> dict:
     return parts
 
 
-def file_sha(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
-
-
-def load_traffic(kernel_src):
-    """Counter-measured HBM bytes of the coarse kernel, if taken on the current
-    kernel source (profiles/coarse_traffic.json, written from rocprofv3 --pmc)."""
-    p = os.path.join(ROOT, "profiles", "coarse_traffic.json")
+def load_traffic(workload):
+    """Counter-measured HBM bytes per launch of the coarse kernel, if they were
+    taken on the current kernel source (written by profsum from two
+    rocprofv3 --pmc runs, FETCH_SIZE and WRITE_SIZE)."""
+    from top_sparse_attention_ls_amd import profsum
+    p = os.path.join(ROOT, "profiles", "k_coarse.%s.traffic.json" % workload)
     if not os.path.exists(p):
         return None
     t = json.load(open(p))
-    if t.get("kernel_sha") != file_sha(kernel_src):
+    if t.get("kernel_sha") != profsum.coarse_kernel_sha():
         return None
     return t.get("bytes_per_launch")
+
+
+def copy_calibration(nbytes):
+    """A plain device-to-device copy of known size, run only under the
+    counter passes so that FETCH_SIZE / WRITE_SIZE can be scaled."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
 
 
 def build_inputs(ls, synth, wl, dev, replicas):
@@ -136,6 +145,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=2)
     ap.add_argument("--cpu-sample", type=int, default=4,
                     help="requests the CPU oracle baseline runs (0 = skip)")
+    ap.add_argument("--copy-calib", type=int, default=0,
+                    help="MiB of a plain device copy run after timing (counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -200,7 +211,6 @@ def main():
     coarse_ms = stage_ms[0]
     coarse_bytes = wl.batch * wl.ctx * wl.idx_dim // 2 + wl.batch * wl.idx_heads * (wl.idx_dim + 1)
     achieved = coarse_bytes / (coarse_ms * 1e-3) / 1e9
-    kernel_src = os.path.join(ROOT, "top_sparse_attention_ls_amd", "csrc", "k_index.hip")
     result = {
         "metric": METRIC,
         "value": round(steps_per_s, 2),
@@ -234,13 +244,15 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": load_traffic(kernel_src),
+            "traffic": load_traffic(wl.name),
             "algorithmic_bytes_per_launch": coarse_bytes,
             "avg_launch_us": round(coarse_ms * 1000, 2),
         },
         "stages_us": {n: round(v * 1000, 2) for n, v in zip(STAGES, stage_ms)},
         "request_layer_steps_per_s": round(steps_per_s * wl.batch, 1),
     }
+    if args.copy_calib > 0:
+        copy_calibration(args.copy_calib << 20)
     if args.cpu_sample > 0:
         print("[bench] cpu baseline on %d requests" % args.cpu_sample, file=sys.stderr,
               flush=True)

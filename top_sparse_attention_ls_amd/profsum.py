@@ -1,0 +1,143 @@
+"""Summaries of rocprofv3 output for the profiles folder.
+
+  python -m top_sparse_attention_ls_amd.profsum stats KERNEL_STATS_CSV \\
+      --out profiles/NAME.md --cmd "the rocprofv3 command"
+      per-kernel calls / average / total duration of the library's kernels
+
+  python -m top_sparse_attention_ls_amd.profsum traffic \\
+      --fetch FETCH_COUNTER_CSV --write WRITE_COUNTER_CSV --copy-mib N \\
+      --workload NAME --cmd-fetch "..." --cmd-write "..."
+      HBM bytes per launch of the coarse scoring kernel from FETCH_SIZE and
+      WRITE_SIZE (KiB per dispatch), each scaled by what the same counter
+      reads for the plain N MiB device copy that bench.py --copy-calib runs
+      last.  Writes profiles/k_coarse.NAME.traffic.json (read by bench.py,
+      keyed to the kernel's source hash) and a .md beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+# the coarse kernel and every header it includes
+COARSE_SOURCES = ["k_index.hip", "ls_bucket.h", "ls_device.h", "ls_launch.h"]
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def coarse_kernel_sha() -> str:
+    h = hashlib.sha256()
+    for f in COARSE_SOURCES:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    n = name[5:] if name.startswith("void ") else name
+    return n.split("(")[0]
+
+
+def cmd_stats(args):
+    rows = list(csv.DictReader(open(args.csv)))
+    ours = [r for r in rows if short_name(r["Name"]).startswith("ls::")]
+    ours.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = ["# %s" % args.title, "", "Command:", "", "```", args.cmd, "```", "",
+             "| kernel | calls | avg us | min us | max us | total us |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for r in ours:
+        lines.append("| `%s` | %s | %.2f | %.2f | %.2f | %.1f |" % (
+            short_name(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+            float(r["TotalDurationNs"]) / 1e3))
+    if args.note:
+        lines += ["", args.note]
+    open(args.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _counter_rows(path, counter):
+    out = []
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    out.sort()
+    return out
+
+
+def _scaled(path, counter, copy_kib, kernel):
+    rows = _counter_rows(path, counter)
+    copies = [v for _, n, v in rows if n == COPY_KERNEL][-2:]
+    if len(copies) < 2:
+        raise SystemExit("no calibration copy found in %s" % path)
+    cal = sum(copies) / len(copies)
+    if not (0.5 * copy_kib < cal < 2.0 * copy_kib):
+        raise SystemExit("%s of the copy reads %.0f KiB, expected about %.0f" %
+                         (counter, cal, copy_kib))
+    factor = copy_kib / cal
+    vals = [v for _, n, v in rows if short_name(n).startswith("ls::" + kernel)]
+    if not vals:
+        raise SystemExit("no %s dispatch in %s" % (kernel, path))
+    # the first launches of a run can see cold TLBs; use the later ones
+    steady = vals[len(vals) // 2:] if len(vals) > 2 else vals
+    avg_kib = sum(steady) / len(steady)
+    return {"counter": counter, "raw_kib_per_launch": avg_kib, "launches": len(vals),
+            "copy_raw_kib": cal, "copy_expected_kib": copy_kib, "factor": factor,
+            "bytes_per_launch": avg_kib * factor * 1024.0}
+
+
+def cmd_traffic(args):
+    copy_kib = args.copy_mib * 1024.0
+    f = _scaled(args.fetch, "FETCH_SIZE", copy_kib, "k_coarse")
+    w = _scaled(args.write, "WRITE_SIZE", copy_kib, "k_coarse")
+    total = f["bytes_per_launch"] + w["bytes_per_launch"]
+    res = {"kernel": "k_coarse", "workload": args.workload, "kernel_sha": coarse_kernel_sha(),
+           "bytes_per_launch": round(total), "fetch": f, "write": w,
+           "algorithmic_bytes_per_launch": args.algorithmic,
+           "commands": [args.cmd_fetch, args.cmd_write]}
+    base = os.path.join(ROOT, "profiles", "k_coarse.%s.traffic" % args.workload)
+    json.dump(res, open(base + ".json", "w"), indent=1)
+    lines = ["# k_coarse HBM traffic, %s" % args.workload, "",
+             "Commands (one counter per pass):", "", "```", args.cmd_fetch, args.cmd_write,
+             "```", "",
+             "| counter | raw KiB / launch | copy raw KiB | copy expected KiB | factor | "
+             "scaled bytes / launch |", "|---|---:|---:|---:|---:|---:|"]
+    for c in (f, w):
+        lines.append("| %s | %.0f | %.0f | %.0f | %.4f | %.0f |" % (
+            c["counter"], c["raw_kib_per_launch"], c["copy_raw_kib"], c["copy_expected_kib"],
+            c["factor"], c["bytes_per_launch"]))
+    lines += ["", "Total HBM bytes per launch: %.0f" % total]
+    if args.algorithmic:
+        lines.append("Algorithmic bytes per launch: %d (ratio %.3f)" %
+                     (args.algorithmic, total / args.algorithmic))
+    lines.append("Kernel source hash: %s" % res["kernel_sha"])
+    open(base + ".md", "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="action", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--out", required=True)
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--title", default="Kernel durations")
+    s.add_argument("--note", default="")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-mib", type=int, required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--algorithmic", type=int, default=0)
+    t.add_argument("--cmd-fetch", required=True)
+    t.add_argument("--cmd-write", required=True)
+    args = ap.parse_args()
+    (cmd_stats if args.action == "stats" else cmd_traffic)(args)
+
+
+if __name__ == "__main__":
+    main()
