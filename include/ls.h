@@ -103,8 +103,9 @@ typedef struct {
 
 /* Hot KV buffer of one layer.  Each request owns hot_slots resident rows
  * followed by topk scratch rows that receive the step's misses; a row is
- * row_elems bf16 values (a multiple of 8).  pool_on_host = 1 means the pool
- * is pinned host memory that the device reads over PCIe.                    */
+ * row_elems bf16 values (a multiple of 8, with topk * row_elems / 8 below
+ * 2^31).  pool_on_host = 1 means the pool is pinned host memory that the
+ * device reads over PCIe.                                                   */
 typedef struct {
     int32_t batch, max_ctx, topk, hot_slots, row_elems, pool_on_host;
 } ls_hot_desc;

@@ -7,6 +7,7 @@
 // buffer: XM-Sparse digest, section on the hot buffer -- after the selection
 // only the selected rows missing from the HBM hot buffer are fetched.
 #include "ls_device.h"
+#include "ls_select.h"
 #include "ls_launch.h"
 
 namespace ls {
@@ -105,16 +106,264 @@ __global__ __launch_bounds__(256) void k_refine(const int8_t* __restrict__ q,
 
 // ---------------------------------------------- top-k + resolve (A4, A5) ----
 //
-// One 1024-thread workgroup per request.  The candidates' (fine score,
-// position) pairs are staged in LDS when they fit, the block radix threshold
-// search finds the cut that keeps exactly min(K, valid) of them under
-// (score desc, position asc), and the kept ones are emitted in candidate
-// order, i.e. ascending position.  With a slot table the emission also
-// resolves each kept token against the hot buffer: rows[j] = its slot if
-// resident, else hot_slots + (its rank among the misses); the misses'
-// positions go to miss_pos in the same order.
+// One 1024-thread workgroup per request keeps min(K, valid) candidates under
+// (fine score desc, position asc) and emits them in candidate order, i.e.
+// ascending position.  With a slot table the emission also resolves each
+// kept token against the hot buffer: rows[j] = its slot if resident, else
+// hot_slots + (its rank among the misses); the misses' positions go to
+// miss_pos in the same order.
+//
+// k_topk_hist (C <= 16384): thread t holds candidates t, t + 1024, ... in
+// registers (coalesced loads).  Their fine scores are bucketed (float-like,
+// 6 mantissa bits, both signs) into an LDS histogram; one scan from the top
+// finds the bucket beta where the count crosses K.  Candidates above beta
+// are kept; the few in beta go to an LDS tie list that one wave resolves
+// exactly with the radix threshold search.  Output offsets come from wave
+// ballots plus one small table of per-wave counts that wave 0 scans, so the
+// kept candidates are written by consecutive lanes to consecutive slots.
+// The hot-slot lookups are issued with the loads and overlap the selection.
+//
+// k_topk (any C, also the fallback when the tie list overflows LDS): the
+// block radix threshold search over all candidates.
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkLds = 8192;
+constexpr int kFineHalf = 3776;          // magnitude buckets of a 63-bit value
+constexpr int kFineBins = 2 * kFineHalf;  // 7552
+constexpr int kFineBinsPad = 8192;        // 8 per thread
+constexpr int kTopkTieLds = 8192;
+
+__device__ __forceinline__ uint32_t fine_mag_bucket(uint64_t y) {  // y < 2^63
+  if (y < 128u) return (uint32_t)y;
+  const uint32_t e = 63u - (uint32_t)__clzll((long long)y);
+  return 128u + (e - 7u) * 64u + (uint32_t)((y >> (e - 6u)) & 63u);
+}
+
+// Scores in magnitude bucket m: [lo, hi].
+__device__ __forceinline__ void fine_mag_range(uint32_t m, uint64_t& lo, uint64_t& hi) {
+  if (m < 128u) {
+    lo = hi = m;
+    return;
+  }
+  const uint32_t e = 7u + (m - 128u) / 64u, j = (m - 128u) % 64u;
+  lo = (uint64_t)(64u + j) << (e - 6u);
+  hi = lo + ((1ull << (e - 6u)) - 1ull);
+}
+
+// Scores in bucket bk: [lo, hi] (the inverse of fine_bucket).
+__device__ __forceinline__ void fine_bucket_range(int bk, int64_t& lo, int64_t& hi) {
+  uint64_t a, b;
+  if (bk >= kFineHalf) {
+    fine_mag_range((uint32_t)(bk - kFineHalf), a, b);
+    lo = (int64_t)a;
+    hi = (int64_t)b;
+  } else {
+    fine_mag_range((uint32_t)(kFineHalf - 1 - bk), a, b);
+    lo = -(int64_t)b - 1;
+    hi = -(int64_t)a - 1;
+  }
+}
+
+// Monotone bucket of an int64 score in [0, kFineBins).
+__device__ __forceinline__ uint32_t fine_bucket(int64_t x) {
+  return x >= 0 ? (uint32_t)kFineHalf + fine_mag_bucket((uint64_t)x)
+                : (uint32_t)kFineHalf - 1u - fine_mag_bucket((uint64_t)(-(x + 1)));
+}
+
+template <int PER>
+__global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
+    const int32_t* __restrict__ cand, const int64_t* __restrict__ fs, int32_t* __restrict__ topk,
+    int64_t* __restrict__ topk_score, const int32_t* __restrict__ pos2slot,
+    int32_t* __restrict__ rows, int32_t* __restrict__ n_miss, int32_t* __restrict__ miss_pos,
+    int hot_slots, int max_ctx, int C, int K) {
+  constexpr int NT = kTopkThreads;
+  constexpr int NW = NT / kWave;
+  constexpr int BPT = kFineBinsPad / NT;  // bins per thread
+  constexpr int NTAB = PER * NW;          // per-(k, wave) count table
+  __shared__ uint32_t scan_sh[NW];
+  __shared__ SelectShared ssh;
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kFineBinsPad];
+  __shared__ int64_t tie_f[kTopkTieLds];
+  __shared__ int32_t tie_c[kTopkTieLds];
+  __shared__ uint32_t tab[NTAB];
+  __shared__ Threshold sh_thr;
+  __shared__ int sh_beta;
+  __shared__ uint32_t sh_above, n_tie, sh_tot;
+  const int b = blockIdx.x, tid = threadIdx.x, l = lane_id(), wv = wave_id();
+  const int32_t* cb = cand + (size_t)b * C;
+  const int64_t* fb = fs + (size_t)b * C;
+
+  int32_t c[PER];
+  int64_t f[PER];
+#pragma unroll
+  for (int k = 0; k < PER; k++) {
+    const int i = tid + NT * k;
+    const bool in = i < C;
+    c[k] = in ? cb[i] : -1;
+    f[k] = in ? fb[i] : 0;
+  }
+  // hot-slot lookups of every valid candidate, in flight during the selection
+  const int32_t* p2s = pos2slot ? pos2slot + (size_t)b * max_ctx : nullptr;
+  int32_t slot[PER];
+#pragma unroll
+  for (int k = 0; k < PER; k++) slot[k] = (p2s && c[k] >= 0) ? p2s[c[k]] : 0;
+#pragma unroll
+  for (int k = 0; k < BPT; k++) hist[tid * BPT + k] = 0;
+  if (tid == 0) {
+    sh_beta = -1;
+    sh_above = 0;
+    n_tie = 0;
+  }
+  __syncthreads();
+  uint32_t bk[PER];
+#pragma unroll
+  for (int k = 0; k < PER; k++) {
+    bk[k] = fine_bucket(f[k]);
+    if (c[k] >= 0) atomicAdd(&hist[bk[k]], 1u);
+  }
+  __syncthreads();
+
+  // bucket where the count from the top crosses K (thread 0: top bins)
+  const int seg = NT - 1 - tid;
+  uint32_t hc[BPT];
+  uint32_t s = 0;
+#pragma unroll
+  for (int k = 0; k < BPT; k++) {
+    hc[k] = hist[seg * BPT + k];
+    s += hc[k];
+  }
+  uint32_t n_c;
+  const uint32_t above_seg = block_excl_scan<NT>(s, scan_sh, &n_c);
+  const uint32_t need_all = min((uint32_t)K, n_c);
+  if (need_all < n_c && above_seg < need_all && need_all <= above_seg + s) {
+    uint32_t run = above_seg;
+#pragma unroll
+    for (int k = BPT - 1; k >= 0; k--) {
+      if (run < need_all && run + hc[k] >= need_all) {
+        sh_beta = seg * BPT + k;
+        sh_above = run;
+      }
+      run += hc[k];
+    }
+  }
+  __syncthreads();
+  const int beta = sh_beta;  // -1: every valid candidate is kept
+
+  bool sel[PER];
+  if (beta < 0) {
+#pragma unroll
+    for (int k = 0; k < PER; k++) sel[k] = c[k] >= 0;
+  } else {
+    const uint32_t need = need_all - sh_above;  // 1 <= need <= ties
+#pragma unroll
+    for (int k = 0; k < PER; k++) {
+      const bool tie = c[k] >= 0 && (int)bk[k] == beta;
+      const uint64_t mt = __ballot(tie);
+      if (mt) {
+        uint32_t base = 0;
+        if (l == 0) base = atomicAdd(&n_tie, (uint32_t)__popcll(mt));
+        const uint32_t i = wave_read(base, 0) + lane_rank(mt);
+        if (tie && i < (uint32_t)kTopkTieLds) {
+          tie_f[i] = f[k];
+          tie_c[i] = c[k];
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t nt = n_tie;
+    const bool overflow = nt > (uint32_t)kTopkTieLds;
+    Threshold thr{0ull, 0u, 0};
+    if (overflow) {  // every valid candidate takes part: the cut is exact on its own
+      auto get = [&](int i, uint64_t& u, uint32_t& p) {
+        u = key_of_i64(fb[i]);
+        p = (uint32_t)cb[i];
+      };
+      thr = block_threshold<NT>(get, (int)n_c, need_all, ssh);
+    } else if (need < nt) {
+      if (wv == 0) {
+        auto get = [&](int i, uint64_t& u, uint32_t& p) {
+          u = key_of_i64(tie_f[i]);
+          p = (uint32_t)tie_c[i];
+        };
+        int64_t lo, hi;
+        fine_bucket_range(beta, lo, hi);
+        const Threshold t = wave_threshold(get, (int)nt, need, ssh.hist, key_of_i64(lo),
+                                           key_of_i64(hi), pos_bits_below(max_ctx));
+        if (l == 0) sh_thr = t;
+      }
+      __syncthreads();
+      thr = sh_thr;
+    }
+#pragma unroll
+    for (int k = 0; k < PER; k++) {
+      const bool v = c[k] >= 0;
+      if (overflow)
+        sel[k] = v && keep(thr, key_of_i64(f[k]), (uint32_t)c[k]);
+      else
+        sel[k] = v && ((int)bk[k] > beta ||
+                       ((int)bk[k] == beta && keep(thr, key_of_i64(f[k]), (uint32_t)c[k])));
+    }
+  }
+
+  // ---- emission in candidate order
+  uint64_t ms[PER], mm[PER];
+#pragma unroll
+  for (int k = 0; k < PER; k++) {
+    ms[k] = __ballot(sel[k]);
+    mm[k] = __ballot(sel[k] && slot[k] < 0);
+    // kept and missed counts, packed (both stay below 2^16)
+    if (l == 0) tab[k * NW + wv] = (uint32_t)__popcll(ms[k]) | ((uint32_t)__popcll(mm[k]) << 16);
+  }
+  __syncthreads();
+  if (wv == 0) {  // exclusive scan of the table in (k, wave) order
+    constexpr int Q = NTAB >= kWave ? NTAB / kWave : 1;
+    uint32_t v[Q];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int q = 0; q < Q; q++) {
+      const int e = l * Q + q;
+      v[q] = e < NTAB ? tab[e] : 0u;
+      sum += v[q];
+    }
+    const uint32_t incl = wave_incl_scan(sum);
+    uint32_t run = incl - sum;
+#pragma unroll
+    for (int q = 0; q < Q; q++) {
+      const int e = l * Q + q;
+      if (e < NTAB) tab[e] = run;
+      run += v[q];
+    }
+    if (l == kWave - 1) sh_tot = incl;
+  }
+  __syncthreads();
+  int32_t* tb = topk + (size_t)b * K;
+  int64_t* sb = topk_score ? topk_score + (size_t)b * K : nullptr;
+  int32_t* rb = rows ? rows + (size_t)b * K : nullptr;
+  int32_t* mb = miss_pos ? miss_pos + (size_t)b * K : nullptr;
+#pragma unroll
+  for (int k = 0; k < PER; k++) {
+    if (!sel[k]) continue;
+    const uint32_t base = tab[k * NW + wv];
+    const uint32_t o = (base & 0xFFFFu) + lane_rank(ms[k]);
+    tb[o] = c[k];
+    if (sb) sb[o] = f[k];
+    if (p2s) {
+      if (slot[k] >= 0) {
+        rb[o] = slot[k];
+      } else {
+        const uint32_t om = (base >> 16) + lane_rank(mm[k]);
+        rb[o] = hot_slots + (int32_t)om;
+        mb[om] = c[k];
+      }
+    }
+  }
+  const uint32_t tot = sh_tot;
+  for (int j = (int)(tot & 0xFFFFu) + tid; j < K; j += NT) {
+    tb[j] = -1;
+    if (sb) sb[j] = 0;
+    if (rb) rb[j] = -1;
+  }
+  if (tid == 0 && n_miss) n_miss[b] = p2s ? (int32_t)(tot >> 16) : 0;
+}
 
 __global__ __launch_bounds__(kTopkThreads) void k_topk(
     const int32_t* __restrict__ cand, const int64_t* __restrict__ fs, int32_t* __restrict__ topk,
@@ -222,8 +471,18 @@ hipError_t launch_refine_topk(const int8_t* q, const int8_t* w, const int8_t* k8
 #undef LS_REFINE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_topk, dim3(B), dim3(kTopkThreads), 0, st, cand, ws.fs, topk, topk_score,
-                     pos2slot, rows, n_miss, ws.miss_pos, hot_slots, max_ctx, C, K);
+#define LS_TOPK(P)                                                                         \
+  hipLaunchKernelGGL(k_topk_hist<P>, dim3(B), dim3(kTopkThreads), 0, st, cand, ws.fs, topk,   \
+                     topk_score, pos2slot, rows, n_miss, ws.miss_pos, hot_slots, max_ctx, C, K)
+  if (C <= kTopkThreads) LS_TOPK(1);
+  else if (C <= 2 * kTopkThreads) LS_TOPK(2);
+  else if (C <= 4 * kTopkThreads) LS_TOPK(4);
+  else if (C <= 8 * kTopkThreads) LS_TOPK(8);
+  else if (C <= 16 * kTopkThreads) LS_TOPK(16);
+  else
+    hipLaunchKernelGGL(k_topk, dim3(B), dim3(kTopkThreads), 0, st, cand, ws.fs, topk, topk_score,
+                       pos2slot, rows, n_miss, ws.miss_pos, hot_slots, max_ctx, C, K);
+#undef LS_TOPK
   return hipGetLastError();
 }
 
@@ -277,9 +536,11 @@ hipError_t launch_hot_resolve(const int32_t* topk, const int32_t* pos2slot, int3
 
 // ------------------------------------------------------- miss gather (A6) ---
 // hot[b, hot_slots + j] := pool[b, miss_pos[b, j]] for j < n_miss[b], in
-// 16-byte pieces spread over the workgroups of the request.  The pool may
-// be pinned host memory (reads then cross PCIe).
-constexpr int kGatherWGPerReq = 16;
+// 16-byte pieces: each workgroup copies a contiguous share of the request's
+// pieces, every thread four pieces at a time with all loads issued before
+// the stores.  The pool may be pinned host memory (reads then cross PCIe).
+constexpr int kGatherWGPerReq = 32;
+constexpr int kGatherUnroll = 4;
 
 __global__ __launch_bounds__(256) void k_hot_gather(const int32_t* __restrict__ miss_pos,
                                                     const int32_t* __restrict__ n_miss,
@@ -287,18 +548,26 @@ __global__ __launch_bounds__(256) void k_hot_gather(const int32_t* __restrict__ 
                                                     int hot_slots, int max_ctx, int K,
                                                     int chunks) {
   const int b = blockIdx.y;
-  const int nm = n_miss[b];
-  const int64_t total = (int64_t)nm * chunks;
-  const int64_t per = (total + gridDim.x - 1) / gridDim.x;
-  const int64_t i0 = (int64_t)blockIdx.x * per;
-  const int64_t i1 = min(i0 + per, total);
+  const uint32_t total = (uint32_t)n_miss[b] * (uint32_t)chunks;
+  const uint32_t per = (total + gridDim.x - 1) / gridDim.x;
+  const uint32_t i0 = blockIdx.x * per;
+  const uint32_t i1 = min(i0 + per, total);
   const int32_t* mp = miss_pos + (size_t)b * K;
-  const size_t pool_base = (size_t)b * max_ctx;
-  const size_t hot_base = (size_t)b * (hot_slots + K) + hot_slots;
-  for (int64_t i = i0 + threadIdx.x; i < i1; i += 256) {
-    const int j = (int)(i / chunks), c = (int)(i % chunks);
-    const int32_t p = mp[j];
-    hot[(hot_base + j) * chunks + c] = pool[(pool_base + p) * chunks + c];
+  const uint4* pb = pool + (size_t)b * max_ctx * chunks;
+  uint4* hb = hot + ((size_t)b * (hot_slots + K) + hot_slots) * chunks;
+  for (uint32_t i = i0 + threadIdx.x; i < i1; i += 256 * kGatherUnroll) {
+    uint4 v[kGatherUnroll];
+    uint32_t dst[kGatherUnroll];
+#pragma unroll
+    for (int u = 0; u < kGatherUnroll; u++) {
+      const uint32_t idx = min(i + 256u * u, i1 - 1);
+      const uint32_t j = idx / (uint32_t)chunks, c = idx - j * (uint32_t)chunks;
+      v[u] = pb[(size_t)mp[j] * chunks + c];
+      dst[u] = idx;
+    }
+#pragma unroll
+    for (int u = 0; u < kGatherUnroll; u++)
+      if (i + 256u * u < i1) hb[dst[u]] = v[u];
   }
 }
 

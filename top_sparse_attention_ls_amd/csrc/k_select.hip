@@ -4,6 +4,7 @@
 // Method: LeanSparse (arXiv 2611.04671), Abstract -- the coarse pass keeps a
 // candidate set that the original indexer keys then refine.
 #include "ls_device.h"
+#include "ls_select.h"
 #include "ls_launch.h"
 #include "ls_bucket.h"
 
@@ -11,204 +12,276 @@ namespace ls {
 
 // ------------------------------------------------- candidate select (A2) ----
 //
-// Keeps the C best tokens under (score desc, position asc), in two kernels.
+// Keeps the C best tokens under (score desc, position asc), in two kernels
+// with the kernel boundary as the only cross-workgroup synchronisation.
 //
-// k_topc_filter (many workgroups per request): every workgroup reads the
-// request's bucket histogram and finds the bucket beta where the count from
-// the top crosses C.  It then filters its chunk of positions: tokens in
-// buckets above beta are kept outright -- a bit in the request's position
-// bitmap, written one wave ballot (64 positions) at a time; tokens in bucket
-// beta are appended to a tie list (wave ballot + mbcnt ranks, one atomic per
-// wave).
+// k_topc_filter (16384 positions per 512-thread workgroup): every lane first
+// issues its loads -- the request's histogram share, then all 32 of its
+// scores (one coalesced dword per lane per wave step, clamped to the row) --
+// so that the threshold search waits only for the histogram.  From the
+// histogram the workgroup finds the bucket beta where the count from the
+// top crosses C.  Tokens in buckets above beta are kept outright: one wave
+// ballot is one 64-bit word of the request's position bitmap.  Tokens in
+// bucket beta are appended to the wave's own LDS tie list (ranks from the
+// ballot, so no atomics in the loop) and the workgroup reserves room in the
+// request's global list with one atomic.  Workgroup 0 also stores beta and
+// the count above it for the emit kernel.
 //
-// k_topc_emit (one 1024-thread workgroup per request): resolves the tie list
-// exactly with the block radix threshold search (in LDS when it fits), sets
-// the winners' bits, emits the kept positions in ascending order from the
-// bitmap, and clears the histogram and tie counter for the next call.
+// k_topc_emit (one 1024-thread workgroup per request): copies the bitmap to
+// LDS, resolves the tie list exactly (one wave runs the radix threshold
+// search when the list fits in LDS, the whole workgroup otherwise), sets the
+// winners' bits with LDS atomics, and emits the kept positions in ascending
+// order, every thread owning a contiguous run of bitmap words.  It leaves
+// the histogram and the tie counter cleared for the next call.  Contexts
+// whose bitmap does not fit in LDS use the same steps on the global bitmap.
 
-// Finds beta and the count strictly above it from a request's histogram.
-// NT threads; result in *beta (-1: every valid token is kept) and *above.
-template <int NT>
-__device__ void coarse_threshold(const uint32_t* hb, int n_valid, int C, int* beta,
-                                 uint32_t* above, uint32_t* scan_sh) {
-  constexpr int kPer = (kCoarseBins + NT - 1) / NT;
-  if (threadIdx.x == 0) {
-    *beta = -1;
-    *above = 0;
-  }
-  __syncthreads();
-  if (n_valid <= C) return;
-  const int seg = NT - 1 - (int)threadIdx.x;  // thread 0 owns the top segment
-  uint32_t s = 0;
+constexpr int kFilterThreads = 512;
+constexpr int kFilterIters = 32;
+constexpr int kFilterChunk = kFilterThreads * kFilterIters;  // 16384 positions
+constexpr int kFilterWaveTies = 512;
+// ctr words of a request: tie count, beta, count above beta
+constexpr int kCtrTies = 0, kCtrBeta = 1, kCtrAbove = 2;
+
+__global__ __launch_bounds__(kFilterThreads) void k_topc_filter(
+    const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ scores,
+    const uint32_t* __restrict__ hist, uint32_t* __restrict__ bitmap,
+    int32_t* __restrict__ tie_s, int32_t* __restrict__ tie_p, uint32_t* __restrict__ ctr,
+    int max_ctx, int C, int bitmap_words) {
+  constexpr int NW = kFilterThreads / kWave;
+  constexpr int kPer = (kCoarseBins + kFilterThreads - 1) / kFilterThreads;
+  __shared__ uint32_t scan_sh[NW];
+  __shared__ int sh_beta;
+  __shared__ uint32_t sh_above;
+  __shared__ uint32_t wave_n[NW];
+  __shared__ uint32_t g_base;
+  __shared__ int32_t loc_s[NW][kFilterWaveTies];
+  __shared__ int32_t loc_p[NW][kFilterWaveTies];
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x, l = lane_id(), wv = wave_id();
+  const int c0 = blockIdx.x * kFilterChunk;
+  uint32_t* cr = ctr + (size_t)kCtrStride * b;
+
+  const int n_valid = clamp_ctx(ctx_len, b, max_ctx);
+  const uint32_t* hb = hist + (size_t)b * kCoarseBins;
+  const int seg = kFilterThreads - 1 - tid;  // thread 0 owns the top bins
+  uint32_t hc[kPer];
+#pragma unroll
   for (int k = 0; k < kPer; k++) {
     const int bin = seg * kPer + k;
-    if (bin < kCoarseBins) s += hb[bin];
+    hc[k] = bin < kCoarseBins ? hb[bin] : 0u;
   }
+  __builtin_amdgcn_sched_barrier(0);
+  const int32_t* sb = scores + (size_t)b * max_ctx;
+  int32_t sv[kFilterIters];
+#pragma unroll
+  for (int u = 0; u < kFilterIters; u++)
+    sv[u] = sb[min(c0 + (u * NW + wv) * kWave + l, max_ctx - 1)];
+
+  // threshold bucket from the histogram
+  if (tid == 0) {
+    sh_beta = -1;
+    sh_above = 0;
+  }
+  uint32_t s = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; k++) s += hc[k];
   uint32_t tot;
-  const uint32_t above_seg = block_excl_scan<NT>(s, scan_sh, &tot);
-  if (above_seg < (uint32_t)C && (uint32_t)C <= above_seg + s) {
+  const uint32_t above_seg = block_excl_scan<kFilterThreads>(s, scan_sh, &tot);
+  if (n_valid > C && above_seg < (uint32_t)C && (uint32_t)C <= above_seg + s) {
     uint32_t run = above_seg;
+#pragma unroll
     for (int k = kPer - 1; k >= 0; k--) {
-      const int bin = seg * kPer + k;
-      const uint32_t c = bin < kCoarseBins ? hb[bin] : 0u;
-      if (run + c >= (uint32_t)C) {
-        *beta = bin;
-        *above = run;
-        break;
+      if (run < (uint32_t)C && run + hc[k] >= (uint32_t)C) {
+        sh_beta = seg * kPer + k;
+        sh_above = run;
       }
-      run += c;
+      run += hc[k];
     }
   }
   __syncthreads();
-}
-
-__global__ __launch_bounds__(256) void k_topc_filter(const int32_t* __restrict__ ctx_len,
-                                                     const int32_t* __restrict__ scores,
-                                                     const uint32_t* __restrict__ hist,
-                                                     uint32_t* __restrict__ bitmap,
-                                                     int32_t* __restrict__ tie_s,
-                                                     int32_t* __restrict__ tie_p,
-                                                     uint32_t* __restrict__ ctr, int max_ctx,
-                                                     int C, int bitmap_words) {
-  __shared__ uint32_t scan_sh[4];
-  __shared__ int sh_beta;
-  __shared__ uint32_t sh_above;
-  __shared__ uint32_t n_local, g_base;
-  __shared__ int32_t loc_s[kSelectChunk];
-  __shared__ int32_t loc_p[kSelectChunk];
-  const int b = blockIdx.y;
-  const int tid = threadIdx.x, l = lane_id();
-  const int n_valid = clamp_ctx(ctx_len, b, max_ctx);
-  if (tid == 0) n_local = 0;
-  coarse_threshold<256>(hist + (size_t)b * kCoarseBins, n_valid, C, &sh_beta, &sh_above,
-                        scan_sh);
   const int beta = sh_beta;
+  if (blockIdx.x == 0 && tid == 0) {
+    cr[kCtrBeta] = (uint32_t)beta;
+    cr[kCtrAbove] = sh_above;
+  }
+
   uint32_t* bm = bitmap + (size_t)b * bitmap_words;
-  const int c0 = blockIdx.x * kSelectChunk;
-  const int c1 = min(c0 + kSelectChunk, bitmap_words * 32);
-  const int32_t* sb = scores + (size_t)b * max_ctx;
-  // keep bits go straight to the bitmap; ties are collected in LDS first
-  for (int base = c0 + wave_id() * 64; base < c1; base += 256) {
+  const size_t tb = (size_t)b * max_ctx;
+  uint32_t wn = 0;  // this wave's ties so far (wave-uniform)
+#pragma unroll
+  for (int u = 0; u < kFilterIters; u++) {
+    const int base = c0 + (u * NW + wv) * kWave;
     const int t = base + l;
     const bool valid = t < n_valid;
-    const int32_t s = valid ? sb[t] : 0;
-    const int bk = (int)coarse_bucket(s);
+    const int bk = (int)coarse_bucket(sv[u]);
     const bool keep_f = valid && (beta < 0 || bk > beta);
     const bool tie_f = valid && beta >= 0 && bk == beta;
     const uint64_t mk = __ballot(keep_f);
     const uint64_t mt = __ballot(tie_f);
-    if (l == 0) *(uint2*)&bm[base / 32] = make_uint2((uint32_t)mk, (uint32_t)(mk >> 32));
-    if (mt) {
-      uint32_t off = 0;
-      if (l == 0) off = atomicAdd(&n_local, (uint32_t)__popcll(mt));
-      off = __shfl(off, 0, kWave);
-      if (tie_f) {
-        const uint32_t idx = off + lane_rank(mt);
-        loc_s[idx] = s;
-        loc_p[idx] = t;
+    if (l == 0 && base / 32 < bitmap_words)
+      *(uint2*)&bm[base / 32] = make_uint2((uint32_t)mk, (uint32_t)(mk >> 32));
+    if (tie_f) {
+      const uint32_t idx = wn + lane_rank(mt);
+      if (idx < (uint32_t)kFilterWaveTies) {
+        loc_s[wv][idx] = sv[u];
+        loc_p[wv][idx] = t;
+      } else {  // more ties than the wave's LDS list holds: straight to the global list
+        const uint32_t g = atomicAdd(&cr[kCtrTies], 1u);
+        tie_s[tb + g] = sv[u];
+        tie_p[tb + g] = t;
       }
     }
+    wn += (uint32_t)__popcll(mt);
+  }
+  if (l == 0) wave_n[wv] = min(wn, (uint32_t)kFilterWaveTies);
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t n = 0;
+#pragma unroll
+    for (int w = 0; w < NW; w++) n += wave_n[w];
+    g_base = n ? atomicAdd(&cr[kCtrTies], n) : 0u;  // one reservation per workgroup
   }
   __syncthreads();
-  const uint32_t nl = n_local;
-  if (nl == 0) return;
-  // one reservation per workgroup in the request's tie list
-  if (tid == 0) g_base = atomicAdd(&ctr[kCtrStride * b], nl);
-  __syncthreads();
-  const size_t gb = (size_t)b * max_ctx + g_base;
-  for (uint32_t i = tid; i < nl; i += 256) {
-    tie_s[gb + i] = loc_s[i];
-    tie_p[gb + i] = loc_p[i];
+  uint32_t off = g_base;
+  for (int w = 0; w < wv; w++) off += wave_n[w];
+  const uint32_t mine = wave_n[wv];
+  for (uint32_t i = l; i < mine; i += kWave) {
+    tie_s[tb + off + i] = loc_s[wv][i];
+    tie_p[tb + off + i] = loc_p[wv][i];
   }
 }
 
 constexpr int kEmitThreads = 1024;
-constexpr int kTieLds = 6144;
+constexpr int kEmitMaxWords = 32768;  // bitmap in LDS up to 2^20 positions
+constexpr int kEmitTieLds = 3072;
 
+template <bool LDS_BM>
 __global__ __launch_bounds__(kEmitThreads) void k_topc_emit(
     const int32_t* __restrict__ ctx_len, uint32_t* __restrict__ hist,
     uint32_t* __restrict__ bitmap, const int32_t* __restrict__ tie_s,
     const int32_t* __restrict__ tie_p, uint32_t* __restrict__ ctr, int32_t* __restrict__ cand,
     int max_ctx, int C, int bitmap_words) {
-  __shared__ uint32_t scan_sh[kEmitThreads / kWave];
-  __shared__ int sh_beta;
-  __shared__ uint32_t sh_above;
+  constexpr int NT = kEmitThreads;
+  __shared__ uint32_t scan_sh[NT / kWave];
   __shared__ SelectShared ssh;
-  __shared__ int32_t lds_s[kTieLds];
-  __shared__ int32_t lds_p[kTieLds];
+  __shared__ __attribute__((aligned(16))) uint32_t bm_l[LDS_BM ? kEmitMaxWords : 4];
+  __shared__ uint2 lds_t[kEmitTieLds];  // (key, position) of the ties
+  __shared__ Threshold sh_thr;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int n_valid = clamp_ctx(ctx_len, b, max_ctx);
+  const int nw = (n_valid + 31) / 32;
+  const int nw4 = (nw + 3) / 4;
   uint32_t* hb = hist + (size_t)b * kCoarseBins;
-  uint32_t* bm = bitmap + (size_t)b * bitmap_words;
-  coarse_threshold<kEmitThreads>(hb, n_valid, C, &sh_beta, &sh_above, scan_sh);
-  const int beta = sh_beta;
+  uint32_t* bmg = bitmap + (size_t)b * bitmap_words;
+  uint32_t* cr = ctr + (size_t)kCtrStride * b;
+  uint32_t* bm = LDS_BM ? bm_l : bmg;
+  if (LDS_BM) {
+    for (int i = tid; i < nw4; i += NT) ((uint4*)bm_l)[i] = ((const uint4*)bmg)[i];
+  }
+  const uint32_t n_tie = cr[kCtrTies];
+  const int beta = n_valid > C ? (int)cr[kCtrBeta] : -1;
+  const uint32_t above = cr[kCtrAbove];
 
   if (beta >= 0) {
-    const uint32_t n_tie = ctr[kCtrStride * b];
-    const uint32_t need = (uint32_t)C - sh_above;  // 1 <= need <= n_tie
+    const uint32_t need = (uint32_t)C - above;  // 1 <= need <= n_tie
     const int32_t* ts = tie_s + (size_t)b * max_ctx;
     const int32_t* tp = tie_p + (size_t)b * max_ctx;
-    const bool in_lds = n_tie <= (uint32_t)kTieLds;
+    const bool in_lds = n_tie <= (uint32_t)kEmitTieLds;
     if (in_lds) {
-      for (int i = tid; i < (int)n_tie; i += kEmitThreads) {
-        lds_s[i] = ts[i];
-        lds_p[i] = tp[i];
-      }
-      __syncthreads();
-    }
-    const int32_t* ss = in_lds ? lds_s : ts;
-    const int32_t* pp = in_lds ? lds_p : tp;
-    Threshold thr{0ull, 0u, 0};
-    if (need < n_tie) {
-      auto get = [&](int i, uint64_t& u, uint32_t& p) {
-        u = key_of_i32(ss[i]);
-        p = (uint32_t)pp[i];
-      };
-      thr = block_threshold<kEmitThreads>(get, (int)n_tie, need, ssh);
-    }
-    for (int i = tid; i < (int)n_tie; i += kEmitThreads) {
-      const uint32_t p = (uint32_t)pp[i];
-      if (keep(thr, key_of_i32(ss[i]), p)) atomicOr(&bm[p / 32], 1u << (p % 32));
+      for (int i = tid; i < (int)n_tie; i += NT)
+        lds_t[i] = make_uint2((uint32_t)key_of_i32(ts[i]), (uint32_t)tp[i]);
     }
     __syncthreads();
-  }
-
-  // emit ascending positions: contiguous word ranges per thread, one scan
-  const int nw = (n_valid + 31) / 32;
-  const int wpt = (nw + kEmitThreads - 1) / kEmitThreads;
-  const int w0 = tid * wpt, w1 = min(w0 + wpt, nw);
-  uint32_t cnt = 0;
-  for (int wi = w0; wi < w1; wi++)
-    cnt += __popc(__hip_atomic_load(&bm[wi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  uint32_t total;
-  uint32_t off = block_excl_scan<kEmitThreads>(cnt, scan_sh, &total);
-  int32_t* cb = cand + (size_t)b * C;
-  for (int wi = w0; wi < w1; wi++) {
-    uint32_t bits = __hip_atomic_load(&bm[wi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    while (bits) {
-      const int k = __ffs(bits) - 1;
-      if (off < (uint32_t)C) cb[off] = 32 * wi + k;
-      off++;
-      bits &= bits - 1;
+    Threshold thr{0ull, 0u, 0};
+    if (need < n_tie) {
+      if (in_lds) {
+        if (wave_id() == 0) {
+          auto get = [&](int i, uint64_t& u, uint32_t& p) {
+            const uint2 e = lds_t[i];
+            u = e.x;
+            p = e.y;
+          };
+          int32_t lo, hi;
+          coarse_bucket_range(beta, lo, hi);
+          const Threshold t = wave_threshold(get, (int)n_tie, need, ssh.hist, key_of_i32(lo),
+                                             key_of_i32(hi), pos_bits_below(max_ctx));
+          if (lane_id() == 0) sh_thr = t;
+        }
+        __syncthreads();
+        thr = sh_thr;
+      } else {
+        auto get = [&](int i, uint64_t& u, uint32_t& p) {
+          u = key_of_i32(ts[i]);
+          p = (uint32_t)tp[i];
+        };
+        thr = block_threshold<NT>(get, (int)n_tie, need, ssh);
+      }
+    }
+    if (in_lds) {
+      for (int i = tid; i < (int)n_tie; i += NT) {
+        const uint2 e = lds_t[i];
+        if (keep(thr, e.x, e.y)) atomicOr(&bm[e.y / 32], 1u << (e.y % 32));
+      }
+    } else {
+      for (int i = tid; i < (int)n_tie; i += NT) {
+        const uint32_t p = (uint32_t)tp[i];
+        if (keep(thr, key_of_i32(ts[i]), p)) atomicOr(&bm[p / 32], 1u << (p % 32));
+      }
     }
   }
-  for (int i = (int)total + tid; i < C; i += kEmitThreads) cb[i] = -1;
+  __syncthreads();
+
+  // emit ascending positions: contiguous runs of 4-word groups per thread
+  const int gpt = (nw4 + NT - 1) / NT;
+  const int g0 = tid * gpt, g1 = min(g0 + gpt, nw4);
+  auto word = [&](int wi) -> uint32_t {
+    if (LDS_BM) return bm_l[wi];
+    return __hip_atomic_load(&bmg[wi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  uint32_t cnt = 0;
+  for (int gi = g0; gi < g1; gi++)
+#pragma unroll
+    for (int k = 0; k < 4; k++) cnt += __popc(word(4 * gi + k));
+  uint32_t total;
+  uint32_t off = block_excl_scan<NT>(cnt, scan_sh, &total);
+  int32_t* cb = cand + (size_t)b * C;
+  for (int gi = g0; gi < g1; gi++) {
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const int wi = 4 * gi + k;
+      uint32_t bits = word(wi);
+      while (bits) {
+        const int j = __ffs(bits) - 1;
+        if (off < (uint32_t)C) cb[off] = 32 * wi + j;
+        off++;
+        bits &= bits - 1;
+      }
+    }
+  }
+  for (int i = (int)total + tid; i < C; i += NT) cb[i] = -1;
 
   // leave the histogram and tie counter cleared for the next call
-  for (int i = tid; i < kCoarseBins; i += kEmitThreads) hb[i] = 0;
-  if (tid == 0) ctr[kCtrStride * b] = 0;
+  for (int i = tid; i < kCoarseBins; i += NT) hb[i] = 0;
+  if (tid == 0) cr[kCtrTies] = 0;
 }
 
 hipError_t launch_topc_select(const int32_t* ctx_len, const CoarseWS& ws, int32_t* cand, int B,
                               int max_ctx, int C, hipStream_t st) {
-  dim3 grid((ws.bitmap_words * 32 + kSelectChunk - 1) / kSelectChunk, B);
-  hipLaunchKernelGGL(k_topc_filter, grid, dim3(256), 0, st, ctx_len, ws.scores, ws.hist,
-                     ws.bitmap, ws.tie_s, ws.tie_p, ws.ctr, max_ctx, C, ws.bitmap_words);
+  dim3 grid((ws.bitmap_words * 32 + kFilterChunk - 1) / kFilterChunk, B);
+  hipLaunchKernelGGL(k_topc_filter, grid, dim3(kFilterThreads), 0, st, ctx_len, ws.scores,
+                     ws.hist, ws.bitmap, ws.tie_s, ws.tie_p, ws.ctr, max_ctx, C,
+                     ws.bitmap_words);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_topc_emit, dim3(B), dim3(kEmitThreads), 0, st, ctx_len, ws.hist,
-                     ws.bitmap, ws.tie_s, ws.tie_p, ws.ctr, cand, max_ctx, C, ws.bitmap_words);
+  if (ws.bitmap_words <= kEmitMaxWords)
+    hipLaunchKernelGGL(k_topc_emit<true>, dim3(B), dim3(kEmitThreads), 0, st, ctx_len, ws.hist,
+                       ws.bitmap, ws.tie_s, ws.tie_p, ws.ctr, cand, max_ctx, C,
+                       ws.bitmap_words);
+  else
+    hipLaunchKernelGGL(k_topc_emit<false>, dim3(B), dim3(kEmitThreads), 0, st, ctx_len,
+                       ws.hist, ws.bitmap, ws.tie_s, ws.tie_p, ws.ctr, cand, max_ctx, C,
+                       ws.bitmap_words);
   return hipGetLastError();
 }
 

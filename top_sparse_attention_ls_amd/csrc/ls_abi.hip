@@ -62,6 +62,8 @@ int check_hot(const ls_hot_desc* d) {
                 d->batch, d->max_ctx, d->topk, d->hot_slots);
   if (d->row_elems < 8 || d->row_elems % 8 != 0)
     return fail(LS_E_ARG, "row_elems must be a positive multiple of 8 (got %d)", d->row_elems);
+  if ((int64_t)d->topk * (d->row_elems / 8) >= (int64_t)1 << 31)
+    return fail(LS_E_ARG, "topk * row_elems / 8 must stay below 2^31");
   if (d->pool_on_host != 0 && d->pool_on_host != 1)
     return fail(LS_E_ARG, "pool_on_host must be 0 or 1");
   return LS_OK;
@@ -99,7 +101,8 @@ struct Carve {
   }
 };
 
-int bitmap_words(int max_ctx) { return (max_ctx + 63) / 64 * 2; }
+// whole 16-byte groups per request row
+int bitmap_words(int max_ctx) { return (max_ctx + 127) / 128 * 4; }
 
 // Counters and histograms first (they must read zero between calls), bulk after.
 void carve_coarse(Carve& c, const ls_idx_desc* d, ls::CoarseWS* ws) {

@@ -1,6 +1,5 @@
 // Device helpers shared by the gfx950 kernels of libls.so: wave and block
-// scans, the block-cooperative radix threshold search used by every
-// selection, MFMA operand types and bf16 conversion.
+// scans, order-preserving keys, MFMA operand types and bf16 conversion.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,13 +23,29 @@ __device__ __forceinline__ uint32_t lane_rank(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// DPP lane move within the wave; lanes without a source (or outside
+// row_mask) contribute 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_or_zero(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Inclusive prefix sum over the wave on DPP moves (row_shr 1/2/4/8 within
+// each 16-lane row, then row_bcast 15 and 31 across rows).  Every lane of
+// the wave must be active.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    uint32_t t = __shfl_up(v, o, kWave);
-    if (lane_id() >= o) v += t;
-  }
+  v += dpp_or_zero<0x111, 0xF>(v);
+  v += dpp_or_zero<0x112, 0xF>(v);
+  v += dpp_or_zero<0x114, 0xF>(v);
+  v += dpp_or_zero<0x118, 0xF>(v);
+  v += dpp_or_zero<0x142, 0xA>(v);
+  v += dpp_or_zero<0x143, 0xC>(v);
   return v;
+}
+
+// Value of lane src (wave-uniform) in every lane.
+__device__ __forceinline__ uint32_t wave_read(uint32_t v, int src) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, src);
 }
 
 // Sum over this lane and every higher lane.
@@ -44,9 +59,7 @@ __device__ __forceinline__ uint32_t wave_incl_suffix(uint32_t v) {
 }
 
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_read(wave_incl_scan(v), kWave - 1);
 }
 
 __device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
@@ -94,159 +107,6 @@ __device__ __forceinline__ uint64_t key_of_i32(int32_t x) {
 }
 __device__ __forceinline__ uint64_t key_of_i64(int64_t x) {
   return (uint64_t)x ^ 0x8000000000000000ull;
-}
-
-// Result of a threshold search: an entry (key u, position p) is kept iff
-//   mode 0:  u >= key
-//   mode 1:  u > key, or u == key and p <= pos.
-struct Threshold {
-  uint64_t key;
-  uint32_t pos;
-  int mode;
-};
-
-__device__ __forceinline__ bool keep(const Threshold& t, uint64_t u, uint32_t p) {
-  return t.mode == 0 ? (u >= t.key) : (u > t.key || (u == t.key && p <= t.pos));
-}
-
-struct SelectShared {
-  uint32_t hist[256];
-  uint64_t red[2][16];
-  uint32_t beta, before, cnt;
-};
-
-// Block reduction of (min, max) of unsigned 64-bit keys.  NT threads.
-template <int NT>
-__device__ __forceinline__ void block_minmax(uint64_t& mn, uint64_t& mx, SelectShared& sh) {
-  mn = wave_min_u64(mn);
-  mx = wave_max_u64(mx);
-  if (lane_id() == 0) {
-    sh.red[0][wave_id()] = mn;
-    sh.red[1][wave_id()] = mx;
-  }
-  __syncthreads();
-  mn = sh.red[0][0];
-  mx = sh.red[1][0];
-#pragma unroll
-  for (int i = 1; i < NT / kWave; i++) {
-    mn = sh.red[0][i] < mn ? sh.red[0][i] : mn;
-    mx = sh.red[1][i] > mx ? sh.red[1][i] : mx;
-  }
-  __syncthreads();
-}
-
-// Wave 0 finds the bin where the running count crosses `need`, counting
-// from the top bin down (from_top) or from bin 0 up.  Writes beta, the count
-// strictly before it in that direction, and the bin's own count.
-__device__ __forceinline__ void find_crossing(SelectShared& sh, uint32_t need, bool from_top) {
-  if (wave_id() != 0) return;
-  const int l = lane_id();
-  uint32_t c0 = sh.hist[4 * l], c1 = sh.hist[4 * l + 1], c2 = sh.hist[4 * l + 2],
-           c3 = sh.hist[4 * l + 3];
-  uint32_t s = c0 + c1 + c2 + c3;
-  uint32_t excl = from_top ? wave_incl_suffix(s) - s : wave_incl_scan(s) - s;
-  if (excl < need && need <= excl + s) {
-    uint32_t c[4] = {c0, c1, c2, c3};
-    uint32_t run = excl;
-    for (int k = 0; k < 4; k++) {
-      int kk = from_top ? 3 - k : k;
-      if (run + c[kk] >= need) {
-        sh.beta = 4 * l + kk;
-        sh.before = run;
-        sh.cnt = c[kk];
-        break;
-      }
-      run += c[kk];
-    }
-  }
-}
-
-// Block-cooperative threshold search over n entries (key, position), keys
-// unsigned, positions unique.  Finds the threshold that keeps exactly `need`
-// entries (1 <= need < n) under the order key descending, position
-// ascending, by narrowing 8-bit digits of the key from the first bit where
-// the entries differ, then digits of the position among entries tied at the
-// cut key.  get(i, u, p) loads entry i.  NT threads; every thread returns
-// the same threshold.
-template <int NT, class Get>
-__device__ Threshold block_threshold(const Get& get, int n, uint32_t need, SelectShared& sh) {
-  const int tid = threadIdx.x;
-  uint64_t mn = ~0ull, mx = 0;
-  for (int i = tid; i < n; i += NT) {
-    uint64_t u;
-    uint32_t p;
-    get(i, u, p);
-    mn = u < mn ? u : mn;
-    mx = u > mx ? u : mx;
-  }
-  block_minmax<NT>(mn, mx, sh);
-
-  // ---- key digits, from the top
-  int nb = (mn == mx) ? 0 : 64 - __clzll(mx ^ mn);
-  uint64_t prefix = (nb >= 64) ? 0ull : ((mx >> nb) << nb);
-  while (nb > 0) {
-    const int d = nb < 8 ? nb : 8;
-    const int shft = nb - d;
-    const uint64_t dmask = (1ull << d) - 1ull;
-    for (int i = tid; i < 256; i += NT) sh.hist[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += NT) {
-      uint64_t u;
-      uint32_t p;
-      get(i, u, p);
-      bool in = (nb >= 64) || ((u >> nb) == (prefix >> nb));
-      if (in) atomicAdd(&sh.hist[(uint32_t)((u >> shft) & dmask)], 1u);
-    }
-    __syncthreads();
-    find_crossing(sh, need, true);
-    __syncthreads();
-    const uint32_t beta = sh.beta, before = sh.before, cnt = sh.cnt;
-    __syncthreads();
-    need -= before;
-    prefix |= (uint64_t)beta << shft;
-    nb = shft;
-    if (cnt == need) return Threshold{prefix, 0u, 0};
-  }
-
-  // ---- every remaining candidate has key == prefix: smallest positions win
-  const uint64_t cut = prefix;
-  uint64_t pmn = ~0ull, pmx = 0;
-  for (int i = tid; i < n; i += NT) {
-    uint64_t u;
-    uint32_t p;
-    get(i, u, p);
-    if (u == cut) {
-      pmn = p < pmn ? p : pmn;
-      pmx = p > pmx ? p : pmx;
-    }
-  }
-  block_minmax<NT>(pmn, pmx, sh);
-  int pb = (pmn == pmx) ? 0 : 64 - __clzll(pmx ^ pmn);
-  uint64_t pprefix = (pb >= 64) ? 0ull : ((pmn >> pb) << pb);
-  while (pb > 0) {
-    const int d = pb < 8 ? pb : 8;
-    const int shft = pb - d;
-    const uint64_t dmask = (1ull << d) - 1ull;
-    for (int i = tid; i < 256; i += NT) sh.hist[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += NT) {
-      uint64_t u;
-      uint32_t p;
-      get(i, u, p);
-      if (u == cut && ((uint64_t)p >> pb) == (pprefix >> pb))
-        atomicAdd(&sh.hist[(uint32_t)(((uint64_t)p >> shft) & dmask)], 1u);
-    }
-    __syncthreads();
-    find_crossing(sh, need, false);
-    __syncthreads();
-    const uint32_t beta = sh.beta, before = sh.before, cnt = sh.cnt;
-    __syncthreads();
-    need -= before;
-    pprefix |= (uint64_t)beta << shft;
-    pb = shft;
-    if (cnt == need) return Threshold{cut, (uint32_t)(pprefix + ((1ull << shft) - 1ull)), 1};
-  }
-  return Threshold{cut, (uint32_t)pprefix, 1};
 }
 
 // ----------------------------------------------------------------------------
