@@ -18,7 +18,8 @@ namespace ls {
 // per tile feed v_mfma_i32_16x16x64_i8 directly: lane (n, g) gathers the
 // 32-byte slice [32g, 32g+32) of candidate n's 128-byte key row (D = 128) or
 // [16g, 16g+16) of its 64-byte row (D = 64); the query slice of the same
-// dims is the A operand.  Per-head dots are exact in int32 (|dot| < 2^21);
+// dims is the A operand.  With a slot table it also stores each candidate's
+// hot slot.  Per-head dots are exact in int32 (|dot| < 2^21);
 // w * relu(dot) < 2^28 and groups of four stay below 2^30 before widening
 // to int64.  Invalid candidates (-1) score 0 and are never selected.
 template <int D, int HT>
@@ -26,7 +27,9 @@ __global__ __launch_bounds__(256) void k_refine(const int8_t* __restrict__ q,
                                                 const int8_t* __restrict__ w,
                                                 const int8_t* __restrict__ k8,
                                                 const int32_t* __restrict__ cand,
-                                                int64_t* __restrict__ fs, int H, int max_ctx,
+                                                int64_t* __restrict__ fs,
+                                                const int32_t* __restrict__ pos2slot,
+                                                int32_t* __restrict__ cslot, int H, int max_ctx,
                                                 int C) {
   constexpr int NMF = D / 64;
   const int b = blockIdx.y;
@@ -101,7 +104,13 @@ __global__ __launch_bounds__(256) void k_refine(const int8_t* __restrict__ q,
   int64_t rx = __shfl_xor(sx, 16, kWave);
   const int64_t score = (even ? k0 : k1) + rx;
   const int c = c_base + l;
-  if (c < C) fs[(size_t)b * C + c] = (cb[c] >= 0) ? score : 0;
+  if (c < C) {
+    const int32_t p = cb[c];
+    fs[(size_t)b * C + c] = (p >= 0) ? score : 0;
+    // the candidate's hot slot, looked up here where the lookups spread over
+    // the whole grid, for the per-request top-k to read coalesced
+    if (pos2slot) cslot[(size_t)b * C + c] = (p >= 0) ? pos2slot[(size_t)b * max_ctx + p] : 0;
+  }
 }
 
 // ---------------------------------------------- top-k + resolve (A4, A5) ----
@@ -121,7 +130,7 @@ __global__ __launch_bounds__(256) void k_refine(const int8_t* __restrict__ q,
 // exactly with the radix threshold search.  Output offsets come from wave
 // ballots plus one small table of per-wave counts that wave 0 scans, so the
 // kept candidates are written by consecutive lanes to consecutive slots.
-// The hot-slot lookups are issued with the loads and overlap the selection.
+// The candidates' hot slots were looked up by the refine kernel.
 //
 // k_topk (any C, also the fallback when the tie list overflows LDS): the
 // block radix threshold search over all candidates.
@@ -171,7 +180,8 @@ __device__ __forceinline__ uint32_t fine_bucket(int64_t x) {
 
 template <int PER>
 __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
-    const int32_t* __restrict__ cand, const int64_t* __restrict__ fs, int32_t* __restrict__ topk,
+    const int32_t* __restrict__ cand, const int64_t* __restrict__ fs,
+    const int32_t* __restrict__ cslot, int32_t* __restrict__ topk,
     int64_t* __restrict__ topk_score, const int32_t* __restrict__ pos2slot,
     int32_t* __restrict__ rows, int32_t* __restrict__ n_miss, int32_t* __restrict__ miss_pos,
     int hot_slots, int max_ctx, int C, int K) {
@@ -201,11 +211,15 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
     c[k] = in ? cb[i] : -1;
     f[k] = in ? fb[i] : 0;
   }
-  // hot-slot lookups of every valid candidate, in flight during the selection
-  const int32_t* p2s = pos2slot ? pos2slot + (size_t)b * max_ctx : nullptr;
+  // hot slots of the candidates, looked up by the refine kernel
+  const bool resolve = pos2slot != nullptr;
+  const int32_t* csb = cslot + (size_t)b * C;
   int32_t slot[PER];
 #pragma unroll
-  for (int k = 0; k < PER; k++) slot[k] = (p2s && c[k] >= 0) ? p2s[c[k]] : 0;
+  for (int k = 0; k < PER; k++) {
+    const int i = tid + NT * k;
+    slot[k] = (resolve && i < C) ? csb[i] : 0;
+  }
 #pragma unroll
   for (int k = 0; k < BPT; k++) hist[tid * BPT + k] = 0;
   if (tid == 0) {
@@ -346,7 +360,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
     const uint32_t o = (base & 0xFFFFu) + lane_rank(ms[k]);
     tb[o] = c[k];
     if (sb) sb[o] = f[k];
-    if (p2s) {
+    if (resolve) {
       if (slot[k] >= 0) {
         rb[o] = slot[k];
       } else {
@@ -362,7 +376,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
     if (sb) sb[j] = 0;
     if (rb) rb[j] = -1;
   }
-  if (tid == 0 && n_miss) n_miss[b] = p2s ? (int32_t)(tot >> 16) : 0;
+  if (tid == 0 && n_miss) n_miss[b] = resolve ? (int32_t)(tot >> 16) : 0;
 }
 
 __global__ __launch_bounds__(kTopkThreads) void k_topk(
@@ -459,8 +473,8 @@ hipError_t launch_refine_topk(const int8_t* q, const int8_t* w, const int8_t* k8
   dim3 grid((C + kRefinePerWG - 1) / kRefinePerWG, B);
   const int HT = (H + 15) / 16;
 #define LS_REFINE(DD, TT)                                                                     \
-  hipLaunchKernelGGL((k_refine<DD, TT>), grid, dim3(256), 0, st, q, w, k8, cand, ws.fs, H, \
-                     max_ctx, C)
+  hipLaunchKernelGGL((k_refine<DD, TT>), grid, dim3(256), 0, st, q, w, k8, cand, ws.fs,     \
+                     pos2slot, ws.slot, H, max_ctx, C)
   if (D == 128) {
     if (HT == 1) LS_REFINE(128, 1); else if (HT == 2) LS_REFINE(128, 2);
     else if (HT == 3) LS_REFINE(128, 3); else LS_REFINE(128, 4);
@@ -472,8 +486,9 @@ hipError_t launch_refine_topk(const int8_t* q, const int8_t* w, const int8_t* k8
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 #define LS_TOPK(P)                                                                         \
-  hipLaunchKernelGGL(k_topk_hist<P>, dim3(B), dim3(kTopkThreads), 0, st, cand, ws.fs, topk,   \
-                     topk_score, pos2slot, rows, n_miss, ws.miss_pos, hot_slots, max_ctx, C, K)
+  hipLaunchKernelGGL(k_topk_hist<P>, dim3(B), dim3(kTopkThreads), 0, st, cand, ws.fs, ws.slot, \
+                     topk, topk_score, pos2slot, rows, n_miss, ws.miss_pos, hot_slots, max_ctx, \
+                     C, K)
   if (C <= kTopkThreads) LS_TOPK(1);
   else if (C <= 2 * kTopkThreads) LS_TOPK(2);
   else if (C <= 4 * kTopkThreads) LS_TOPK(4);

@@ -105,6 +105,11 @@ __global__ __launch_bounds__(kFilterThreads) void k_topc_filter(
     cr[kCtrAbove] = sh_above;
   }
 
+  // bucket beta holds the scores [beta_lo, beta_hi]: above it means kept,
+  // inside it means tied (no bucket: every valid token is kept)
+  int32_t beta_lo = 0, beta_hi = 0;
+  if (beta >= 0) coarse_bucket_range(beta, beta_lo, beta_hi);
+  const bool all_keep = beta < 0;
   uint32_t* bm = bitmap + (size_t)b * bitmap_words;
   const size_t tb = (size_t)b * max_ctx;
   uint32_t wn = 0;  // this wave's ties so far (wave-uniform)
@@ -113,9 +118,8 @@ __global__ __launch_bounds__(kFilterThreads) void k_topc_filter(
     const int base = c0 + (u * NW + wv) * kWave;
     const int t = base + l;
     const bool valid = t < n_valid;
-    const int bk = (int)coarse_bucket(sv[u]);
-    const bool keep_f = valid && (beta < 0 || bk > beta);
-    const bool tie_f = valid && beta >= 0 && bk == beta;
+    const bool keep_f = valid && (all_keep || sv[u] > beta_hi);
+    const bool tie_f = valid && !all_keep && sv[u] >= beta_lo && sv[u] <= beta_hi;
     const uint64_t mk = __ballot(keep_f);
     const uint64_t mt = __ballot(tie_f);
     if (l == 0 && base / 32 < bitmap_words)

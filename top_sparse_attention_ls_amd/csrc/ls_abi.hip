@@ -122,6 +122,7 @@ void carve_refine(Carve& c, const ls_idx_desc* d, ls::RefineWS* ws) {
   const size_t B = d->batch;
   ls::RefineWS w;
   w.fs = c.take<int64_t>(B * d->n_cand);
+  w.slot = c.take<int32_t>(B * d->n_cand);
   w.miss_pos = c.take<int32_t>(B * d->topk);
   if (ws) *ws = w;
 }

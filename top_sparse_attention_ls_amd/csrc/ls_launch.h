@@ -33,6 +33,7 @@ struct CoarseWS {
 
 struct RefineWS {
   int64_t* fs;         // [B, n_cand]
+  int32_t* slot;       // [B, n_cand] hot slot of each candidate (with a slot table)
   int32_t* miss_pos;   // [B, topk]
 };
 
