@@ -26,8 +26,7 @@
  *   [DSA] Related-papers list, abstract on dynamic sparse attention -- the
  *         attention reads only a top-k subset of the cached rows.
  *
- * Readings where the pages are silent (each one is listed in the design
- * notes of the repository):
+ * Readings where the pages are silent:
  *   - indexer score of token t: sum over heads h of w[h]*max(0, q[h].k[t]),
  *     one int8 key per token shared by all heads;
  *   - the compact key is the arithmetic (floor) shift k >> 4, a signed
