@@ -224,8 +224,10 @@ int ls_hot_gather(const ls_hot_desc *desc, const int32_t *topk_dev, const int32_
                   int32_t *n_miss_dev, void *ws_dev, size_t ws_bytes, ls_stream_t stream);
 
 /* Stage 4: attention of q [B,Hq,qk_dim] bf16 over the rows listed in
- * rows [B,topk] (-1 ends a request's list) of the K/V bases described in
- * desc.  out: [B,Hq,v_dim] bf16 (round to nearest even), lse: [B,Hq] fp32.
+ * rows [B,topk] of the K/V bases described in desc; -1, and any id outside
+ * [0, kv_rows_per_req), is padding and is skipped.  out: [B,Hq,v_dim] bf16
+ * (round to nearest even), lse: [B,Hq] fp32 (-inf and a zero output when a
+ * request lists no row).
  * [related-papers list, dynamic sparse attention abstract.]                 */
 int ls_sparse_attn_decode(const ls_attn_desc *desc, const void *q_dev, const void *k_base_dev,
                           const void *v_base_dev, const int32_t *rows_dev, void *out_dev,

@@ -166,3 +166,21 @@ def test_python_binding_requires_gpu_tensors_types():
     import torch
     with pytest.raises(TypeError):
         ls.pack_coarse(torch.zeros(4, 8, dtype=torch.uint8))
+
+
+def test_binding_rejects_mis_sized_tensors():
+    """The library trusts the descriptor's sizes; the binding checks every
+    tensor against them before a launch (a short hot buffer would otherwise
+    be written past its end)."""
+    import torch
+    import top_sparse_attention_ls_amd as ls
+    t = torch.zeros((2, 5, 8), dtype=torch.bfloat16)
+    ls._need(t, torch.bfloat16, "hot", (2, 5, 8))
+    with pytest.raises(ValueError):
+        ls._need(t, torch.bfloat16, "hot", (2, 6, 8))
+    with pytest.raises(TypeError):
+        ls._need(t, torch.float32, "hot", (2, 5, 8))
+    with pytest.raises(ValueError):
+        ls._need(t.transpose(1, 2), torch.bfloat16, "hot")
+    with pytest.raises(ValueError):
+        ls._need_rows(t, 81, "k_base")

@@ -1,0 +1,104 @@
+"""GPU parity at the served workloads' full sizes, in the launch configuration
+the benchmark times (one DecodeStep call over the whole batch, automatic
+split count), against the CPU oracle on sampled requests.
+
+The hot buffer is laid out from the generator's planted positions (all of
+them resident, the remaining slots random), which the HIP path never sees,
+so no oracle input comes from the GPU.  On every request, sampled or not,
+the test also checks what holds at any size: ascending, in-range, unique
+positions; selected scores equal to the oracle's exact score of those
+positions; hot-buffer rows and miss list consistent with the slot table; the
+gathered rows byte-equal to the pool rows."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from top_sparse_attention_ls_amd import synth
+from tests.gpu_common import np_, bits, assert_attention_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def run_full(ls, name, sample):
+    wl = synth.WORKLOADS[name]
+    B, L = wl.batch, wl.ctx
+    print("[fullsize] %s: building inputs" % name, flush=True)
+    inp = synth.indexer_inputs(wl, DEV)
+    qa = synth.attention_query(wl, DEV)
+    pool = synth.kv_pool(wl, DEV, pin=wl.pool_on_host, gen_device=DEV)
+    width = max(int(p.numel()) for p in inp["planted"])
+    planted = torch.full((B, width), -1, dtype=torch.int32)
+    for b, p in enumerate(inp["planted"]):
+        planted[b, :p.numel()] = p.to("cpu", torch.int32)
+    pos2slot, hot, _ = synth.hot_fill(wl, planted, pool, DEV, miss_rate=0.0, scratch=wl.topk)
+    hot0 = hot.clone()
+    keys = inp["keys"]
+    kc = ls.pack_coarse(keys)
+    ctx_len = torch.full((B,), L, dtype=torch.int32, device=DEV)
+    step = ls.DecodeStep(batch=B, max_ctx=L, idx_heads=wl.idx_heads, idx_dim=wl.idx_dim,
+                         n_cand=wl.n_cand, topk=wl.topk, q_heads=wl.q_heads, qk_dim=wl.qk_dim,
+                         v_dim=wl.v_dim, scale=wl.scale, hot_slots=wl.hot_slots,
+                         pool_on_host=wl.pool_on_host, device=DEV)
+    print("[fullsize] %s: step" % name, flush=True)
+    out, lse = step.run(q_idx=inp["q"], w_idx=inp["w"], kc=kc, k8=keys, ctx_len=ctx_len,
+                        q_attn=qa, pos2slot=pos2slot, hot_kv=hot, pool_kv=pool)
+    torch.cuda.synchronize()
+
+    cand, topk, score = np_(step.cand), np_(step.topk), np_(step.topk_score)
+    rows, n_miss = np_(step.rows), np_(step.n_miss)
+    p2s = np_(pos2slot)
+    S, K = wl.hot_slots, wl.topk
+    for b in range(B):
+        c = cand[b][cand[b] >= 0]
+        assert len(c) == min(wl.n_cand, L), (b, len(c))
+        assert (np.diff(c) > 0).all() and c[-1] < L, (b, "candidates not ascending/in range")
+        t = topk[b][topk[b] >= 0]
+        assert len(t) == min(K, len(c)), (b, len(t), "selected count")
+        assert (np.diff(t) > 0).all(), (b, "top-k not ascending", np.where(np.diff(t) <= 0)[0][:8])
+        assert np.isin(t, c).all(), (b, "top-k outside the candidates")
+        exact = orc.index_scores_at(np_(inp["q"][b]), np_(inp["w"][b]), np_(keys[b]),
+                                    t.astype(np.int32), False)
+        bad = np.where(score[b][:len(t)] != exact)[0]
+        assert len(bad) == 0, (b, "scores differ at", bad[:8], score[b][bad[:4]], exact[bad[:4]])
+        slot = p2s[b][t]
+        miss = slot < 0
+        assert n_miss[b] == miss.sum(), (b, int(n_miss[b]), int(miss.sum()), "miss count")
+        bad = np.where(rows[b][:len(t)][~miss] != slot[~miss])[0]
+        assert len(bad) == 0, (b, "hit rows differ at", bad[:8])
+        bad = np.where(rows[b][:len(t)][miss] != S + np.arange(miss.sum()))[0]
+        assert len(bad) == 0, (b, "miss rows differ at", bad[:8], rows[b][:len(t)][miss][bad[:4]])
+        got = bits(hot[b, S:S + int(miss.sum())])
+        assert np.array_equal(got, bits(pool[b].index_select(
+            0, torch.from_numpy(t[miss]).to(pool.device, torch.int64)))), b
+
+    for b in sample:
+        print("[fullsize] %s: oracle on request %d" % (name, b), flush=True)
+        hot_b = bits(hot0[b]).copy()
+        r = orc.decode_request(np_(inp["q"][b]), np_(inp["w"][b]), np_(keys[b]), L, wl.n_cand,
+                               wl.topk, bits(qa[b]), wl.scale, pos2slot=p2s[b],
+                               hot_bits=hot_b, pool_bits=bits(pool[b]))
+        bad = np.where(cand[b] != r["cand"])[0]
+        assert len(bad) == 0, (b, "candidates differ at", bad[:8], cand[b][bad[:4]], r["cand"][bad[:4]])
+        bad = np.where(topk[b] != r["topk"])[0]
+        assert len(bad) == 0, (b, "top-k differs at", bad[:8], topk[b][bad[:4]], r["topk"][bad[:4]])
+        assert score[b].tolist() == r["topk_score"].tolist(), b
+        assert rows[b].tolist() == r["rows"].tolist(), b
+        assert int(n_miss[b]) == r["n_miss"], b
+        assert np.array_equal(bits(hot[b]), hot_b), b
+        assert_attention_close(out[b:b + 1], lse[b:b + 1], r["out"][None], r["lse"][None],
+                               "%s request %d" % (name, b))
+
+
+def test_fullsize_decode_128k_b32(ls):
+    run_full(ls, "decode-128k-b32", sample=[0, 31])
+
+
+def test_fullsize_decode_16k_b192_pinned_host_pool(ls):
+    run_full(ls, "decode-16k-b192", sample=[0, 95, 191])
+
+
+@pytest.mark.timeout(300)
+def test_fullsize_decode_950k_b4(ls):
+    run_full(ls, "decode-950k-b4", sample=[3])

@@ -130,11 +130,21 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _need(t, dtype, name):
+def _need(t, dtype, name, shape=None):
+    """The library takes raw pointers and trusts the descriptor's sizes, so
+    every tensor is checked against them here, before any launch."""
     if t.dtype != dtype:
         raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s (got %s)" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _need_rows(t, min_elems, name):
+    if t.numel() < min_elems:
+        raise ValueError("%s holds %d elements, the descriptor needs %d" % (name, t.numel(),
+                                                                           min_elems))
 
 
 # ---------------------------------------------------------------- workspace --
@@ -186,8 +196,10 @@ def idx_desc(q, keys_like_rows: int, n_cand: int, topk: int) -> IdxDesc:
 
 def index_coarse(q, w, kc, ctx_len, n_cand: int, topk: int = 1, ws=None) -> torch.Tensor:
     """q [B,H,D] int8, w [B,H] int8, kc [B,L,D/2] uint8, ctx_len [B] int32."""
-    _need(q, torch.int8, "q"), _need(w, torch.int8, "w"), _need(kc, torch.uint8, "kc")
-    _need(ctx_len, torch.int32, "ctx_len")
+    _need(q, torch.int8, "q")
+    B, H, D = q.shape
+    _need(w, torch.int8, "w", (B, H)), _need(kc, torch.uint8, "kc", (B, kc.shape[1], D // 2))
+    _need(ctx_len, torch.int32, "ctx_len", (B,))
     d = idx_desc(q, kc.shape[1], n_cand, topk)
     ws = workspace(OP_COARSE, d, q.device) if ws is None else ws
     cand = torch.empty((q.shape[0], n_cand), dtype=torch.int32, device=q.device)
@@ -198,8 +210,11 @@ def index_coarse(q, w, kc, ctx_len, n_cand: int, topk: int = 1, ws=None) -> torc
 
 def refine_topk(q, w, k8, cand, ctx_len, topk: int, ws=None):
     """Returns (topk [B,topk] int32, scores [B,topk] int64)."""
-    _need(q, torch.int8, "q"), _need(w, torch.int8, "w"), _need(k8, torch.int8, "k8")
-    _need(cand, torch.int32, "cand"), _need(ctx_len, torch.int32, "ctx_len")
+    _need(q, torch.int8, "q")
+    B, H, D = q.shape
+    _need(w, torch.int8, "w", (B, H)), _need(k8, torch.int8, "k8", (B, k8.shape[1], D))
+    _need(cand, torch.int32, "cand", (B, cand.shape[1]))
+    _need(ctx_len, torch.int32, "ctx_len", (B,))
     d = idx_desc(q, k8.shape[1], cand.shape[1], topk)
     ws = workspace(OP_REFINE, d, q.device) if ws is None else ws
     out = torch.empty((q.shape[0], topk), dtype=torch.int32, device=q.device)
@@ -212,9 +227,13 @@ def refine_topk(q, w, k8, cand, ctx_len, topk: int, ws=None):
 def hot_gather(topk, pos2slot, hot, pool, hot_slots: int, ws=None):
     """topk [B,K] int32, pos2slot [B,L] int32, hot [B,S+K,row] bf16 (updated in
     place), pool [B,L,row] bf16 (device or pinned host).  Returns (rows, n_miss)."""
-    _need(topk, torch.int32, "topk"), _need(pos2slot, torch.int32, "pos2slot")
-    _need(hot, torch.bfloat16, "hot"), _need(pool, torch.bfloat16, "pool")
+    _need(topk, torch.int32, "topk")
     B, K = topk.shape
+    _need(pool, torch.bfloat16, "pool")
+    L, row = pool.shape[1], pool.shape[2]
+    _need(pool, torch.bfloat16, "pool", (B, L, row))
+    _need(pos2slot, torch.int32, "pos2slot", (B, L))
+    _need(hot, torch.bfloat16, "hot", (B, hot_slots + K, row))
     d = HotDesc(B, pool.shape[1], K, hot_slots, hot.shape[2], 0 if pool.is_cuda else 1)
     ws = workspace(OP_HOT, d, topk.device) if ws is None else ws
     rows = torch.empty((B, K), dtype=torch.int32, device=topk.device)
@@ -237,7 +256,11 @@ def sparse_attn_decode(q, k_base, v_base, rows, scale: float, n_kv_heads: int, v
     """q [B,Hq,qk_dim] bf16; rows [B,K] int32 (-1 ends a list).  K/V element
     (b, row r, kv head g, d) sits at base[(b*kv_rows_per_req + r)*kv_row_stride
     + g*kv_head_stride + d].  Returns (out [B,Hq,v_dim] bf16, lse [B,Hq] f32)."""
-    _need(q, torch.bfloat16, "q"), _need(rows, torch.int32, "rows")
+    _need(q, torch.bfloat16, "q"), _need(rows, torch.int32, "rows", (q.shape[0], rows.shape[1]))
+    _need(k_base, torch.bfloat16, "k_base"), _need(v_base, torch.bfloat16, "v_base")
+    last = (q.shape[0] * kv_rows_per_req - 1) * kv_row_stride + (n_kv_heads - 1) * kv_head_stride
+    _need_rows(k_base, last + q.shape[2], "k_base")
+    _need_rows(v_base, last + v_dim, "v_base")
     d = attn_desc(q, rows.shape[1], n_kv_heads, v_dim, kv_rows_per_req, kv_row_stride,
                   kv_head_stride, scale, n_splits)
     ws = workspace(OP_ATTN, d, q.device) if ws is None else ws
@@ -282,6 +305,26 @@ class DecodeStep:
 
     def run(self, *, q_idx, w_idx, kc, k8, ctx_len, q_attn, pos2slot=None, hot_kv=None,
             pool_kv=None, k_cache=None, v_cache=None, events=None):
+        i, a, h = self.desc.idx, self.desc.attn, self.desc.hot
+        B, L, H, D = i.batch, i.max_ctx, i.n_heads, i.head_dim
+        _need(q_idx, torch.int8, "q_idx", (B, H, D)), _need(w_idx, torch.int8, "w_idx", (B, H))
+        _need(kc, torch.uint8, "kc", (B, L, D // 2)), _need(k8, torch.int8, "k8", (B, L, D))
+        _need(ctx_len, torch.int32, "ctx_len", (B,))
+        _need(q_attn, torch.bfloat16, "q_attn", (B, a.n_q_heads, a.qk_dim))
+        if self.use_hot:
+            row = h.row_elems
+            _need(pos2slot, torch.int32, "pos2slot", (B, L))
+            _need(hot_kv, torch.bfloat16, "hot_kv", (B, h.hot_slots + i.topk, row))
+            _need(pool_kv, torch.bfloat16, "pool_kv", (B, L, row))
+            if pool_kv.is_cuda == bool(h.pool_on_host):
+                raise ValueError("pool_kv must be %s memory for this step" %
+                                 ("pinned host" if h.pool_on_host else "device"))
+        else:
+            _need(k_cache, torch.bfloat16, "k_cache"), _need(v_cache, torch.bfloat16, "v_cache")
+            last = (B * a.kv_rows_per_req - 1) * a.kv_row_stride + \
+                (a.n_kv_heads - 1) * a.kv_head_stride
+            _need_rows(k_cache, last + a.qk_dim, "k_cache")
+            _need_rows(v_cache, last + a.v_dim, "v_cache")
         io = StepIO()
         io.q_idx_dev, io.w_idx_dev = q_idx.data_ptr(), w_idx.data_ptr()
         io.kc_dev, io.k8_dev, io.ctx_len_dev = kc.data_ptr(), k8.data_ptr(), ctx_len.data_ptr()

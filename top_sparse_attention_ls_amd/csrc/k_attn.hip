@@ -138,7 +138,11 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
   const int n_tiles = (n_rows + kTileR - 1) / kTileR;
   const int32_t* rb = rows + (size_t)b * K + i_begin;
   for (int i = threadIdx.x; i < n_tiles * kTileR; i += NW * 64)
-    rid_lds[i] = i < n_rows ? rb[i] : -1;
+  {
+    // row ids outside the request's rows are padding, like -1
+    const int32_t r = i < n_rows ? rb[i] : -1;
+    rid_lds[i] = (r >= 0 && r < rows_per_req) ? r : -1;
+  }
 
   // B operand of S^T = K Q^T: head n, dims 16 ks + 8 half .. +7
   v8bf qB[QK_STEPS];
@@ -412,7 +416,8 @@ __global__ __launch_bounds__(256) void k_attn_valu(
   const int32_t* rb = rows + (size_t)b * K;
   const size_t req_off = (size_t)b * rows_per_req * row_stride + (size_t)kvh * head_stride;
   for (int i = wv; i < K; i += 4) {
-    const int32_t r = rb[i];
+    const int32_t r0 = rb[i];
+    const int32_t r = (r0 >= 0 && r0 < rows_per_req) ? r0 : -1;  // out of range = padding
     float dot = 0.f;
     if (r >= 0) {
       const uint16_t* kr = kbase + req_off + (size_t)r * row_stride;
@@ -447,7 +452,8 @@ __global__ __launch_bounds__(256) void k_attn_valu(
     if (rg < groups && m != -INFINITY) {
       for (int i = rg; i < K; i += groups) {
         const int32_t r = rb[i];
-        if (r >= 0) acc += sc[i] * bf16_to_f32(vbase[req_off + (size_t)r * row_stride + d]);
+        if (r >= 0 && r < rows_per_req)
+          acc += sc[i] * bf16_to_f32(vbase[req_off + (size_t)r * row_stride + d]);
       }
     }
     acc_sh[tid] = (rg < groups) ? acc : 0.f;

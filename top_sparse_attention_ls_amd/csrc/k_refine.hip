@@ -355,9 +355,9 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
   int32_t* mb = miss_pos ? miss_pos + (size_t)b * K : nullptr;
 #pragma unroll
   for (int k = 0; k < PER; k++) {
-    if (!sel[k]) continue;
     const uint32_t base = tab[k * NW + wv];
     const uint32_t o = (base & 0xFFFFu) + lane_rank(ms[k]);
+    if (!sel[k] || o >= (uint32_t)K) continue;  // exactly min(K, valid) are kept
     tb[o] = c[k];
     if (sb) sb[o] = f[k];
     if (resolve) {
@@ -563,7 +563,8 @@ __global__ __launch_bounds__(256) void k_hot_gather(const int32_t* __restrict__ 
                                                     int hot_slots, int max_ctx, int K,
                                                     int chunks) {
   const int b = blockIdx.y;
-  const uint32_t total = (uint32_t)n_miss[b] * (uint32_t)chunks;
+  const int nm = min(max(n_miss[b], 0), K);  // a list never holds more than K misses
+  const uint32_t total = (uint32_t)nm * (uint32_t)chunks;
   const uint32_t per = (total + gridDim.x - 1) / gridDim.x;
   const uint32_t i0 = blockIdx.x * per;
   const uint32_t i1 = min(i0 + per, total);
@@ -577,7 +578,8 @@ __global__ __launch_bounds__(256) void k_hot_gather(const int32_t* __restrict__ 
     for (int u = 0; u < kGatherUnroll; u++) {
       const uint32_t idx = min(i + 256u * u, i1 - 1);
       const uint32_t j = idx / (uint32_t)chunks, c = idx - j * (uint32_t)chunks;
-      v[u] = pb[(size_t)mp[j] * chunks + c];
+      const int32_t p = min(max(mp[j], 0), max_ctx - 1);
+      v[u] = pb[(size_t)p * chunks + c];
       dst[u] = idx;
     }
 #pragma unroll

@@ -206,19 +206,21 @@ def kv_cache_mha(wl: Workload, device, batch=None, ctx=None):
 
 
 def hot_fill(wl: Workload, selected: torch.Tensor, pool: torch.Tensor, device,
-             miss_rate=None, hot_slots=None, ctx=None):
+             miss_rate=None, hot_slots=None, ctx=None, scratch=None):
     """Lay out the hot buffer so that a fixed share of a known selection misses.
 
-    selected: [B, k] int32 selected positions per request (-1 padding), as
-    computed by the caller.  For each request, round(rate * n_sel) selected
+    selected: [B, n] int32 selected positions per request (-1 padding), as
+    computed by the caller.  scratch: rows reserved for the step's misses
+    after the slots (the step's top-k; default n).  For each request, round(rate * n_sel) selected
     tokens are left out; the others are made resident at random distinct
     slots, and the remaining slots hold random unselected tokens.  Resident
     rows are byte copies of the pool rows; the k scratch rows after the slots
     start zeroed.
-    Returns pos2slot [B, L] int32, hot [B, S + k, row] bf16, n_miss list."""
+    Returns pos2slot [B, L] int32, hot [B, S + scratch, row] bf16, n_miss list."""
     rate = wl.miss_rate if miss_rate is None else miss_rate
     S = wl.hot_slots if hot_slots is None else hot_slots
-    B, k = selected.shape
+    B, n = selected.shape
+    k = n if scratch is None else scratch
     L = pool.shape[1] if ctx is None else ctx
     row = pool.shape[2]
     sel_cpu = selected.to("cpu")
