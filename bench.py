@@ -10,7 +10,10 @@ Prints one JSON line with:
   value       layer-steps/s (whole-step throughput, steps timed back to back)
   roofline    the dominant kernel (coarse scoring) against the 8 TB/s HBM peak:
               algorithmic bytes per launch / its average duration, measured
-              with HIP events recorded by the library on the launch stream
+              with two HIP events the library records on the launch stream
+              around that kernel, on every 4th step of the timed region
+  stages_us_instrumented  per-stage times from a separate run in which every
+              stage is bracketed by events (each adds a few microseconds)
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -186,29 +189,48 @@ def main():
     assert miss_now == n_miss, "hot buffer miss counts drifted: %s" % miss_now
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ls.STEP_EVENTS)]
-           for _ in range(K)]
-    for row in evs:            # create the underlying events before use
-        for e in row:
+    # timed region: whole steps back to back; on every SAMPLE-th step the
+    # library also records two events around the coarse kernel (an event
+    # costs the stream a few microseconds, so only the measured kernel is
+    # bracketed, and only on a sample of the steps)
+    SAMPLE = 4
+    coarse_ev = {}
+    for i in range(0, K, SAMPLE):
+        coarse_ev[i] = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for pair in coarse_ev.values():  # create the underlying events before use
+        for e in pair:
             e.record()
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     print("[bench] timing %d steps" % K, file=sys.stderr, flush=True)
     t_start.record()
     for i in range(K):
-        run(i, evs[i])
+        pair = coarse_ev.get(i)
+        run(i, None if pair is None else [pair[0], pair[1]] + [None] * (ls.STEP_EVENTS - 2))
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / K
+    coarse_ms = sum(p[0].elapsed_time(p[1]) for p in coarse_ev.values()) / len(coarse_ev)
+
+    # stage breakdown from a separate instrumented run (every stage bracketed)
+    n_inst = min(K, 20)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ls.STEP_EVENTS)]
+           for _ in range(n_inst)]
+    for row in evs:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    for i in range(n_inst):
+        run(i, evs[i])
+    torch.cuda.synchronize()
     stage_ms = [0.0] * (ls.STEP_EVENTS - 1)
     for row in evs:
-        for s in range(ls.STEP_EVENTS - 1):
-            stage_ms[s] += row[s].elapsed_time(row[s + 1]) / K
+        for s_ in range(ls.STEP_EVENTS - 1):
+            stage_ms[s_] += row[s_].elapsed_time(row[s_ + 1]) / n_inst
 
     ab = algorithmic_bytes(wl, sum(n_miss))
     steps_per_s = 1000.0 / ms_per_step
-    coarse_ms = stage_ms[0]
     coarse_bytes = wl.batch * wl.ctx * wl.idx_dim // 2 + wl.batch * wl.idx_heads * (wl.idx_dim + 1)
     achieved = coarse_bytes / (coarse_ms * 1e-3) / 1e9
     result = {
@@ -248,7 +270,8 @@ def main():
             "algorithmic_bytes_per_launch": coarse_bytes,
             "avg_launch_us": round(coarse_ms * 1000, 2),
         },
-        "stages_us": {n: round(v * 1000, 2) for n, v in zip(STAGES, stage_ms)},
+        "coarse_events_sampled": len(coarse_ev),
+        "stages_us_instrumented": {n: round(v * 1000, 2) for n, v in zip(STAGES, stage_ms)},
         "request_layer_steps_per_s": round(steps_per_s * wl.batch, 1),
     }
     if args.copy_calib > 0:

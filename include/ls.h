@@ -138,7 +138,9 @@ typedef struct {
 /* Number of stage events ls_decode_step records when given an event array:
  * [0] start, [1] after coarse scoring, [2] after candidate selection,
  * [3] after refinement + top-k (+ hot resolve), [4] after the miss gather,
- * [5] after the attention kernel, [6] after the combine pass (end).        */
+ * [5] after the attention kernel, [6] after the combine pass (end).  A NULL
+ * entry is skipped (each recorded event costs the stream a few
+ * microseconds, so a caller that times one stage records only its two).   */
 #define LS_STEP_EVENTS 7
 
 /* Device pointers of one step (see the individual stages for shapes). */

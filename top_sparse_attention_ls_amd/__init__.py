@@ -338,8 +338,9 @@ class DecodeStep:
             io.k_cache_dev, io.v_cache_dev = k_cache.data_ptr(), v_cache.data_ptr()
         io.q_attn_dev = q_attn.data_ptr()
         io.out_dev, io.lse_dev = self.out.data_ptr(), self.lse.data_ptr()
-        if events is not None:
-            arr = (ctypes.c_void_p * STEP_EVENTS)(*[e.cuda_event for e in events])
+        if events is not None:  # STEP_EVENTS torch events; None entries are skipped
+            arr = (ctypes.c_void_p * STEP_EVENTS)(*[e.cuda_event if e is not None else None
+                                                    for e in events])
             io.stage_events = ctypes.cast(arr, ctypes.c_void_p)
         _check(load().ls_decode_step(ctypes.byref(self.desc), ctypes.byref(io), _p(self.ws),
                                      self.ws.numel(), _stream()))

@@ -243,7 +243,7 @@ int run_coarse(const ls_idx_desc* d, const int8_t* q, const int8_t* w, const uin
   LS_HIP(ls::launch_coarse_scores(q, w, kc, ctx_len, ws, d->batch, d->n_heads, d->head_dim,
                                   d->max_ctx, st),
          "coarse score launch");
-  if (ev) LS_HIP(hipEventRecord((hipEvent_t)ev[1], st), "event record");
+  if (ev && ev[1]) LS_HIP(hipEventRecord((hipEvent_t)ev[1], st), "event record");
   LS_HIP(ls::launch_topc_select(ctx_len, ws, cand, d->batch, d->max_ctx, d->n_cand, st),
          "candidate select launch");
   return LS_OK;
@@ -412,7 +412,7 @@ static int attn_args(const ls_attn_desc* d, const void* q, const void* k, const 
 
 static int run_attention(const ls::AttnArgs& a, hipStream_t st, ls_event_t* ev) {
   LS_HIP(ls::launch_attention(a, st), "attention launch");
-  if (ev) LS_HIP(hipEventRecord((hipEvent_t)ev[5], st), "event record");
+  if (ev && ev[5]) LS_HIP(hipEventRecord((hipEvent_t)ev[5], st), "event record");
   if (a.n_splits > 1) LS_HIP(ls::launch_combine(a, st), "combine launch");
   return LS_OK;
 }
@@ -512,10 +512,10 @@ int ls_decode_step(const ls_step_desc* desc, const ls_step_io* io, void* ws_dev,
 
   hipStream_t st = (hipStream_t)stream;
   ls_event_t* ev = io->stage_events;
-  if (ev) LS_HIP(hipEventRecord((hipEvent_t)ev[0], st), "event record");
+  if (ev && ev[0]) LS_HIP(hipEventRecord((hipEvent_t)ev[0], st), "event record");
   LS_TRY(run_coarse(id, io->q_idx_dev, io->w_idx_dev, io->kc_dev, io->ctx_len_dev, io->cand_dev,
                     cws, st, ev));
-  if (ev) LS_HIP(hipEventRecord((hipEvent_t)ev[2], st), "event record");
+  if (ev && ev[2]) LS_HIP(hipEventRecord((hipEvent_t)ev[2], st), "event record");
   LS_HIP(ls::launch_refine_topk(io->q_idx_dev, io->w_idx_dev, io->k8_dev, io->cand_dev, rws,
                                 io->topk_dev, io->topk_score_dev,
                                 desc->use_hot ? io->pos2slot_dev : nullptr,
@@ -524,15 +524,15 @@ int ls_decode_step(const ls_step_desc* desc, const ls_step_io* io, void* ws_dev,
                                 id->batch, id->n_heads, id->head_dim, id->max_ctx, id->n_cand,
                                 id->topk, st),
          "refine launch");
-  if (ev) LS_HIP(hipEventRecord((hipEvent_t)ev[3], st), "event record");
+  if (ev && ev[3]) LS_HIP(hipEventRecord((hipEvent_t)ev[3], st), "event record");
   if (desc->use_hot)
     LS_HIP(ls::launch_hot_gather(rws.miss_pos, io->n_miss_dev, pool, io->hot_kv_dev,
                                  desc->hot.hot_slots, id->batch, id->max_ctx, id->topk,
                                  desc->hot.row_elems, st),
            "miss gather launch");
-  if (ev) LS_HIP(hipEventRecord((hipEvent_t)ev[4], st), "event record");
+  if (ev && ev[4]) LS_HIP(hipEventRecord((hipEvent_t)ev[4], st), "event record");
   LS_TRY(run_attention(a, st, ev));
-  if (ev) LS_HIP(hipEventRecord((hipEvent_t)ev[6], st), "event record");
+  if (ev && ev[6]) LS_HIP(hipEventRecord((hipEvent_t)ev[6], st), "event record");
   return LS_OK;
 }
 
