@@ -1,0 +1,106 @@
+"""GPU parity of the prefill-chunk indexer against the CPU oracle: per-row
+causal top-k (bit-exact positions), across row blocks, head shapes, rows
+that see fewer keys than k, exact ties, and the layer-streamed entry point
+(bit-identical to separate calls), up to the full 4096 x 131072 chunk on
+sampled rows."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from top_sparse_attention_ls_amd import synth
+from tests.gpu_common import np_
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+PF = synth.WORKLOADS["prefill-4k-128k"]
+
+
+def check_rows(got, q, w, keys, q_pos0, topk, rows):
+    for i in rows:
+        exp, _ = orc.prefill_row(q[i], w[i], keys, q_pos0 + i, topk)
+        bad = np.where(got[i] != exp)[0]
+        assert len(bad) == 0, ("row", i, bad[:8], got[i][bad[:4]], exp[bad[:4]])
+
+
+def valid_rows(got, q_pos0, topk, L):
+    for i in range(got.shape[0]):
+        n = min(topk, min(q_pos0 + i + 1, L))
+        r = got[i]
+        assert (r[:n] >= 0).all() and (r[n:] == -1).all(), ("row", i, "padding")
+        assert (np.diff(r[:n]) > 0).all() and r[n - 1] <= q_pos0 + i, ("row", i, "order/causal")
+
+
+def run_case(ls, n_query, ctx, H, D, topk, q_pos0, layer=0, rows=None):
+    wl = dataclasses.replace(PF, idx_heads=H, idx_dim=D, topk=topk)
+    inp = synth.prefill_inputs(wl, layer, "cpu", n_query=n_query, ctx=ctx)
+    q, w, keys = inp["q"], inp["w"], inp["keys"]
+    got = np_(ls.prefill_index_topk(q.to(DEV), w.to(DEV), keys.to(DEV), q_pos0, topk))
+    valid_rows(got, q_pos0, topk, ctx)
+    check_rows(got, q.numpy(), w.numpy(), keys.numpy(), q_pos0,
+               topk, range(n_query) if rows is None else rows)
+    return got
+
+
+def test_prefill_chunk_at_the_end(ls):
+    run_case(ls, n_query=96, ctx=3000, H=64, D=128, topk=256, q_pos0=3000 - 96)
+
+
+def test_prefill_from_start_rows_see_fewer_keys_than_k(ls):
+    # q_pos0 = 0: row i sees i + 1 keys, so the first rows are padded; 600
+    # rows span two row blocks
+    run_case(ls, n_query=600, ctx=2048, H=4, D=64, topk=64, q_pos0=0)
+
+
+@pytest.mark.parametrize("H,D", [(20, 64), (33, 128), (64, 64)])
+def test_prefill_head_shapes(ls, H, D):
+    run_case(ls, n_query=40, ctx=4500, H=H, D=D, topk=100, q_pos0=4500 - 40)
+
+
+def test_prefill_all_keys_equal_takes_lowest_positions(ls):
+    q = torch.randint(-127, 128, (16, 8, 64), dtype=torch.int32).to(torch.int8)
+    w = torch.randint(1, 17, (16, 8), dtype=torch.int32).to(torch.int8)
+    keys = torch.full((5000, 64), 3, dtype=torch.int8)
+    got = np_(ls.prefill_index_topk(q.to(DEV), w.to(DEV), keys.to(DEV), 4984, 300))
+    for i in range(16):
+        exp, _ = orc.prefill_row(q[i].numpy(), w[i].numpy(), keys.numpy(), 4984 + i, 300)
+        assert got[i].tolist() == exp.tolist() == list(range(300))
+
+
+def test_prefill_stream_equals_separate_calls(ls):
+    wl = dataclasses.replace(PF, idx_heads=64, idx_dim=128, topk=128)
+    n_query, ctx, q_pos0 = 64, 2500, 2500 - 64
+    layers = [synth.prefill_inputs(wl, l, "cpu", n_query=n_query, ctx=ctx) for l in range(3)]
+    qs = [x["q"].to(DEV) for x in layers]
+    ws_ = [x["w"].to(DEV) for x in layers]
+    kh = [x["keys"].pin_memory() for x in layers]
+    outs = ls.prefill_stream_layers(qs, ws_, kh, q_pos0, 128)
+    torch.cuda.synchronize()
+    for l in range(3):
+        sep = ls.prefill_index_topk(qs[l], ws_[l], kh[l].to(DEV), q_pos0, 128)
+        assert torch.equal(outs[l], sep), l
+        check_rows(np_(outs[l]), layers[l]["q"].numpy(), layers[l]["w"].numpy(),
+                   layers[l]["keys"].numpy(), q_pos0, 128, [0, 31, 63])
+
+
+@pytest.mark.timeout(600)
+def test_prefill_fullsize_streamed_sampled_rows(ls):
+    wl = PF
+    Tq, L = wl.n_query, wl.ctx
+    q_pos0 = L - Tq
+    print("[prefill] building %d layers" % wl.layers, flush=True)
+    layers = [synth.prefill_inputs(wl, l, DEV) for l in range(wl.layers)]
+    qs = [x["q"] for x in layers]
+    ws_ = [x["w"] for x in layers]
+    kh = [x["keys"].cpu().pin_memory() for x in layers]
+    print("[prefill] streamed run", flush=True)
+    outs = ls.prefill_stream_layers(qs, ws_, kh, q_pos0, wl.topk)
+    torch.cuda.synchronize()
+    rows = [0, 1365, 2730, Tq - 1]
+    for l in range(wl.layers):
+        got = np_(outs[l])
+        valid_rows(got, q_pos0, wl.topk, L)
+        print("[prefill] oracle rows of layer %d" % l, flush=True)
+        check_rows(got, np_(qs[l]), np_(ws_[l]), kh[l].numpy(), q_pos0, wl.topk, rows)

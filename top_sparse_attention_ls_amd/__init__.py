@@ -345,3 +345,62 @@ class DecodeStep:
         _check(load().ls_decode_step(ctypes.byref(self.desc), ctypes.byref(io), _p(self.ws),
                                      self.ws.numel(), _stream()))
         return self.out, self.lse
+
+
+# ------------------------------------------------------------------ prefill --
+
+def prefill_desc(q, max_ctx: int, q_pos0: int, topk: int) -> PrefillDesc:
+    Tq, H, D = q.shape
+    return PrefillDesc(Tq, max_ctx, q_pos0, H, D, topk)
+
+
+def prefill_index_topk(q, w, keys, q_pos0: int, topk: int, ws=None) -> torch.Tensor:
+    """q [Tq,H,D] int8, w [Tq,H] int8, keys [L,D] int8 on the device.  Query i
+    sits at absolute position q_pos0 + i and sees keys 0..q_pos0+i.  Returns
+    topk [Tq, topk] int32, ascending, -1 padded."""
+    _need(q, torch.int8, "q")
+    Tq, H, D = q.shape
+    _need(w, torch.int8, "w", (Tq, H)), _need(keys, torch.int8, "keys", (keys.shape[0], D))
+    d = prefill_desc(q, keys.shape[0], q_pos0, topk)
+    ws = workspace(OP_PREFILL, d, q.device) if ws is None else ws
+    out = torch.empty((Tq, topk), dtype=torch.int32, device=q.device)
+    _check(load().ls_prefill_index_topk(ctypes.byref(d), _p(q), _p(w), _p(keys), _p(out),
+                                        _p(ws), ws.numel(), _stream()))
+    return out
+
+
+def prefill_stream_layers(qs, ws_, keys_host, q_pos0: int, topk: int, buf0=None, buf1=None,
+                          copy_stream=None, ws=None):
+    """Layers l = 0..n-1: qs[l] [Tq,H,D] int8 and ws_[l] [Tq,H] int8 on the
+    device, keys_host[l] [L,D] int8 in pinned host memory.  The histories are
+    copied through the two device buffers buf0 / buf1 on copy_stream while
+    the indexer runs on the current stream.  Returns the per-layer top-k."""
+    n = len(qs)
+    Tq, H, D = qs[0].shape
+    L = keys_host[0].shape[0]
+    for l in range(n):
+        _need(qs[l], torch.int8, "q[%d]" % l, (Tq, H, D))
+        _need(ws_[l], torch.int8, "w[%d]" % l, (Tq, H))
+        _need(keys_host[l], torch.int8, "keys[%d]" % l, (L, D))
+        if keys_host[l].is_cuda or not keys_host[l].is_pinned():
+            raise ValueError("keys[%d] must be pinned host memory" % l)
+    dev = qs[0].device
+    buf0 = torch.empty((L, D), dtype=torch.int8, device=dev) if buf0 is None else buf0
+    buf1 = torch.empty((L, D), dtype=torch.int8, device=dev) if buf1 is None else buf1
+    _need(buf0, torch.int8, "buf0", (L, D)), _need(buf1, torch.int8, "buf1", (L, D))
+    copy_stream = torch.cuda.Stream(device=dev) if copy_stream is None else copy_stream
+    # the buffers are written on the copy stream: keep the allocator from
+    # handing their memory out again before that stream is done with them
+    buf0.record_stream(copy_stream)
+    buf1.record_stream(copy_stream)
+    d = prefill_desc(qs[0], L, q_pos0, topk)
+    ws = workspace(OP_PREFILL, d, dev) if ws is None else ws
+    outs = [torch.empty((Tq, topk), dtype=torch.int32, device=dev) for _ in range(n)]
+
+    def arr(ts):
+        return (ctypes.c_void_p * n)(*[t.data_ptr() for t in ts])
+
+    _check(load().ls_prefill_stream_layers(ctypes.byref(d), n, arr(qs), arr(ws_), arr(keys_host),
+                                           _p(buf0), _p(buf1), arr(outs), _p(ws), ws.numel(),
+                                           _stream(), ctypes.c_void_p(copy_stream.cuda_stream)))
+    return outs

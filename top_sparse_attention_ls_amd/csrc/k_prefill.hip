@@ -1,3 +1,197 @@
-// Prefill-chunk indexer kernels (added with the prefill entry points).
+// Prefill-chunk indexer for gfx950: for every query row of the chunk, the
+// scores of all keys it may see (causal), then the per-row top-k.
+//
+// Method: LeanSparse (arXiv 2611.04671), Abstract -- prefill runs the
+// indexer over the layer's whole history; the history is streamed through
+// two reusable device buffers so that loading the next layer overlaps the
+// current layer's work (ls_prefill_stream_layers in ls_abi.hip).
+//
+// score[i, t] = sum_h w[i,h] * max(0, q[i,h] . k[t]) for t <= q_pos0 + i,
+// computed exactly (int64: with full int8 keys a row can exceed 2^31).
 #include "ls_device.h"
 #include "ls_launch.h"
+#include "ls_bucket.h"
+
+namespace ls {
+
+constexpr int kPrefillRowsPerWG = 2;  // query rows sharing each key tile
+
+__global__ __launch_bounds__(256) void k_prefill_ctx(int32_t* __restrict__ ctx, int rows,
+                                                      int first_pos, int max_ctx) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < rows) ctx[i] = min(max(first_pos + i + 1, 0), max_ctx);
+}
+
+// Scores of kPrefillRowsPerWG query rows against kPrefillTokPerWG keys, as
+// an int8 GEMM on v_mfma_i32_16x16x64_i8: A = one row's query (16 heads per
+// tile, held in VGPRs), B = 16 keys.  Lane (n, g) holds, for k-step mf,
+// dims 32 g + 16 mf .. +15 of head (or key) n: the same dims in A and B, so
+// every MFMA contracts 64 of the 128 dims (D = 64: dims 16 g .. +15).
+// Epilogue per key: max(., 0) times the head weight (24-bit multiply-add),
+// summed over four heads in int32 (< 2^30), then over head tiles in int64,
+// then across the four lane groups with a reduce-scatter that leaves one
+// key per lane.  Each lane buckets its row's score into that row's LDS
+// histogram (flushed once per workgroup), the first pass of the selection.
+// Keys past a row's causal limit are computed with the rest of the tile
+// but neither stored nor counted.  Key loads are clamped to the tile's last
+// key and ping-pong prefetched 64 keys ahead.
+template <int D, int HT>
+__global__ __launch_bounds__(256) void k_prefill_scores(
+    const int8_t* __restrict__ q, const int8_t* __restrict__ w, const int8_t* __restrict__ keys,
+    int64_t* __restrict__ scores, uint32_t* __restrict__ hist, int rows, int first_pos, int H,
+    int max_ctx) {
+  constexpr int QR = kPrefillRowsPerWG;
+  constexpr int NMF = D / 64;
+  __shared__ uint32_t lhist[QR][kWideBins];
+
+  const int r0 = blockIdx.y * QR;
+  int nv[QR];
+  int nv_max = 0;
+#pragma unroll
+  for (int r = 0; r < QR; r++) {
+    nv[r] = (r0 + r < rows) ? min(max(first_pos + r0 + r + 1, 0), max_ctx) : 0;
+    nv_max = max(nv_max, nv[r]);
+  }
+  const int t_begin = blockIdx.x * kPrefillTokPerWG;
+  if (t_begin >= nv_max) return;
+  const int t_end = min(t_begin + kPrefillTokPerWG, nv_max);
+
+  for (int i = threadIdx.x; i < QR * kWideBins; i += 256) (&lhist[0][0])[i] = 0;
+
+  const int l = lane_id(), n = l & 15, g = l >> 4;
+  const int off = (D == 128) ? 32 * g : 16 * g;
+  v4i qa[QR][HT][NMF];
+  int32_t wv[QR][HT][4];
+#pragma unroll
+  for (int r = 0; r < QR; r++) {
+    const int row = min(r0 + r, rows - 1);
+    const int8_t* qr = q + (size_t)row * H * D;
+#pragma unroll
+    for (int mt = 0; mt < HT; mt++) {
+      const int h = 16 * mt + n;
+#pragma unroll
+      for (int mf = 0; mf < NMF; mf++)
+        qa[r][mt][mf] = (h < H) ? *(const v4i*)(qr + (size_t)h * D + off + 16 * mf)
+                                : v4i{0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int hh = 16 * mt + 4 * g + i;
+        wv[r][mt][i] = hh < H ? (int32_t)w[(size_t)row * H + hh] : 0;
+      }
+    }
+  }
+  __syncthreads();
+
+  const int8_t* kb = keys + off;
+  const int t_last = t_end - 1;
+  auto load4 = [&](int base, v4i (&raw)[4][NMF]) {
+#pragma unroll
+    for (int tt = 0; tt < 4; tt++) {
+      const int t = min(base + 16 * tt + n, t_last);
+#pragma unroll
+      for (int mf = 0; mf < NMF; mf++) raw[tt][mf] = *(const v4i*)(kb + (size_t)t * D + 16 * mf);
+    }
+  };
+  auto process = [&](int base, const v4i (&raw)[4][NMF]) {
+    int64_t part[QR][4];
+#pragma unroll
+    for (int tt = 0; tt < 4; tt++) {
+      v4i acc[QR][HT];
+#pragma unroll
+      for (int r = 0; r < QR; r++)
+#pragma unroll
+        for (int mt = 0; mt < HT; mt++)
+          acc[r][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[r][mt][0], raw[tt][0],
+                                                             v4i{0, 0, 0, 0}, 0, 0, 0);
+      if (NMF == 2) {
+#pragma unroll
+        for (int r = 0; r < QR; r++)
+#pragma unroll
+          for (int mt = 0; mt < HT; mt++)
+            acc[r][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[r][mt][NMF - 1],
+                                                               raw[tt][NMF - 1], acc[r][mt], 0,
+                                                               0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < QR; r++) {
+        int64_t s = 0;
+#pragma unroll
+        for (int mt = 0; mt < HT; mt++) {
+          int32_t s4 = 0;
+#pragma unroll
+          for (int i = 0; i < 4; i++) s4 += __mul24(wv[r][mt][i], max(acc[r][mt][i], 0));
+          s += (int64_t)s4;
+        }
+        part[r][tt] = s;
+      }
+    }
+    const bool lo = g < 2, even = (g & 1) == 0;
+    const int t = base + l;
+#pragma unroll
+    for (int r = 0; r < QR; r++) {
+      // reduce-scatter over the four lane groups: lane (n, g) ends with tile g
+      const int64_t s0 = lo ? part[r][2] : part[r][0], s1 = lo ? part[r][3] : part[r][1];
+      const int64_t k0 = (lo ? part[r][0] : part[r][2]) + __shfl_xor(s0, 32, kWave);
+      const int64_t k1 = (lo ? part[r][1] : part[r][3]) + __shfl_xor(s1, 32, kWave);
+      const int64_t score = (even ? k0 : k1) + __shfl_xor(even ? k1 : k0, 16, kWave);
+      if (t < nv[r]) {
+        scores[(size_t)(r0 + r) * max_ctx + t] = score;
+        atomicAdd(&lhist[r][wide_bucket(score)], 1u);
+      }
+    }
+  };
+
+  int base = __builtin_amdgcn_readfirstlane(t_begin + wave_id() * 64);
+  if (base < t_end) {
+    v4i bufA[4][NMF], bufB[4][NMF];
+    load4(base, bufA);
+    while (true) {
+      load4(base + 256, bufB);
+      process(base, bufA);
+      base += 256;
+      if (base >= t_end) break;
+      load4(base + 256, bufA);
+      process(base, bufB);
+      base += 256;
+      if (base >= t_end) break;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < QR; r++) {
+    if (r0 + r >= rows) continue;
+    uint32_t* hb = hist + (size_t)(r0 + r) * kWideBins;
+    for (int i = threadIdx.x; i < kWideBins; i += 256) {
+      const uint32_t c = lhist[r][i];
+      if (c) atomicAdd(&hb[i], c);
+    }
+  }
+}
+
+hipError_t launch_prefill_block(const int8_t* q, const int8_t* w, const int8_t* keys,
+                                const WideWS& ws, int32_t* ctx, int32_t* topk_out, int rows,
+                                int first_pos, int H, int D, int max_ctx, int K, hipStream_t st) {
+  hipLaunchKernelGGL(k_prefill_ctx, dim3((rows + 255) / 256), dim3(256), 0, st, ctx, rows,
+                     first_pos, max_ctx);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 grid((max_ctx + kPrefillTokPerWG - 1) / kPrefillTokPerWG,
+            (rows + kPrefillRowsPerWG - 1) / kPrefillRowsPerWG);
+  const int HT = (H + 15) / 16;
+#define LS_PREFILL(DD, TT)                                                                  \
+  hipLaunchKernelGGL((k_prefill_scores<DD, TT>), grid, dim3(256), 0, st, q, w, keys,        \
+                     ws.scores, ws.hist, rows, first_pos, H, max_ctx)
+  if (D == 128) {
+    if (HT == 1) LS_PREFILL(128, 1); else if (HT == 2) LS_PREFILL(128, 2);
+    else if (HT == 3) LS_PREFILL(128, 3); else LS_PREFILL(128, 4);
+  } else {
+    if (HT == 1) LS_PREFILL(64, 1); else if (HT == 2) LS_PREFILL(64, 2);
+    else if (HT == 3) LS_PREFILL(64, 3); else LS_PREFILL(64, 4);
+  }
+#undef LS_PREFILL
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_wide_select(ctx, ws, topk_out, rows, max_ctx, K, st);
+}
+
+}  // namespace ls

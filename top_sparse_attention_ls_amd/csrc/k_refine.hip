@@ -9,6 +9,7 @@
 #include "ls_device.h"
 #include "ls_select.h"
 #include "ls_launch.h"
+#include "ls_bucket.h"
 
 namespace ls {
 
@@ -136,47 +137,8 @@ __global__ __launch_bounds__(256) void k_refine(const int8_t* __restrict__ q,
 // block radix threshold search over all candidates.
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkLds = 8192;
-constexpr int kFineHalf = 3776;          // magnitude buckets of a 63-bit value
-constexpr int kFineBins = 2 * kFineHalf;  // 7552
-constexpr int kFineBinsPad = 8192;        // 8 per thread
+constexpr int kFineBinsPad = 8192;  // wide buckets, padded to 8 per thread
 constexpr int kTopkTieLds = 8192;
-
-__device__ __forceinline__ uint32_t fine_mag_bucket(uint64_t y) {  // y < 2^63
-  if (y < 128u) return (uint32_t)y;
-  const uint32_t e = 63u - (uint32_t)__clzll((long long)y);
-  return 128u + (e - 7u) * 64u + (uint32_t)((y >> (e - 6u)) & 63u);
-}
-
-// Scores in magnitude bucket m: [lo, hi].
-__device__ __forceinline__ void fine_mag_range(uint32_t m, uint64_t& lo, uint64_t& hi) {
-  if (m < 128u) {
-    lo = hi = m;
-    return;
-  }
-  const uint32_t e = 7u + (m - 128u) / 64u, j = (m - 128u) % 64u;
-  lo = (uint64_t)(64u + j) << (e - 6u);
-  hi = lo + ((1ull << (e - 6u)) - 1ull);
-}
-
-// Scores in bucket bk: [lo, hi] (the inverse of fine_bucket).
-__device__ __forceinline__ void fine_bucket_range(int bk, int64_t& lo, int64_t& hi) {
-  uint64_t a, b;
-  if (bk >= kFineHalf) {
-    fine_mag_range((uint32_t)(bk - kFineHalf), a, b);
-    lo = (int64_t)a;
-    hi = (int64_t)b;
-  } else {
-    fine_mag_range((uint32_t)(kFineHalf - 1 - bk), a, b);
-    lo = -(int64_t)b - 1;
-    hi = -(int64_t)a - 1;
-  }
-}
-
-// Monotone bucket of an int64 score in [0, kFineBins).
-__device__ __forceinline__ uint32_t fine_bucket(int64_t x) {
-  return x >= 0 ? (uint32_t)kFineHalf + fine_mag_bucket((uint64_t)x)
-                : (uint32_t)kFineHalf - 1u - fine_mag_bucket((uint64_t)(-(x + 1)));
-}
 
 template <int PER>
 __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
@@ -231,7 +193,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
   uint32_t bk[PER];
 #pragma unroll
   for (int k = 0; k < PER; k++) {
-    bk[k] = fine_bucket(f[k]);
+    bk[k] = wide_bucket(f[k]);
     if (c[k] >= 0) atomicAdd(&hist[bk[k]], 1u);
   }
   __syncthreads();
@@ -299,7 +261,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
           p = (uint32_t)tie_c[i];
         };
         int64_t lo, hi;
-        fine_bucket_range(beta, lo, hi);
+        wide_bucket_range(beta, lo, hi);
         const Threshold t = wave_threshold(get, (int)nt, need, ssh.hist, key_of_i64(lo),
                                            key_of_i64(hi), pos_bits_below(max_ctx));
         if (l == 0) sh_thr = t;

@@ -1,5 +1,6 @@
-// Candidate selection for gfx950: keeps the C best coarse scores of every
-// request from the score histogram the coarse kernel built.
+// Histogram-driven selection for gfx950: keeps the C best scores of every
+// row (a decode request's coarse scores, or a prefill query's scores) from
+// the per-row bucket histogram that the scoring kernel built.
 //
 // Method: LeanSparse (arXiv 2611.04671), Abstract -- the coarse pass keeps a
 // candidate set that the original indexer keys then refine.
@@ -42,19 +43,21 @@ constexpr int kFilterWaveTies = 512;
 // ctr words of a request: tie count, beta, count above beta
 constexpr int kCtrTies = 0, kCtrBeta = 1, kCtrAbove = 2;
 
+template <class S>
 __global__ __launch_bounds__(kFilterThreads) void k_topc_filter(
-    const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ scores,
+    const int32_t* __restrict__ ctx_len, const typename S::T* __restrict__ scores,
     const uint32_t* __restrict__ hist, uint32_t* __restrict__ bitmap,
-    int32_t* __restrict__ tie_s, int32_t* __restrict__ tie_p, uint32_t* __restrict__ ctr,
+    typename S::T* __restrict__ tie_s, int32_t* __restrict__ tie_p, uint32_t* __restrict__ ctr,
     int max_ctx, int C, int bitmap_words) {
+  using T = typename S::T;
   constexpr int NW = kFilterThreads / kWave;
-  constexpr int kPer = (kCoarseBins + kFilterThreads - 1) / kFilterThreads;
+  constexpr int kPer = (S::kBins + kFilterThreads - 1) / kFilterThreads;
   __shared__ uint32_t scan_sh[NW];
   __shared__ int sh_beta;
   __shared__ uint32_t sh_above;
   __shared__ uint32_t wave_n[NW];
   __shared__ uint32_t g_base;
-  __shared__ int32_t loc_s[NW][kFilterWaveTies];
+  __shared__ T loc_s[NW][kFilterWaveTies];
   __shared__ int32_t loc_p[NW][kFilterWaveTies];
   const int b = blockIdx.y;
   const int tid = threadIdx.x, l = lane_id(), wv = wave_id();
@@ -62,17 +65,17 @@ __global__ __launch_bounds__(kFilterThreads) void k_topc_filter(
   uint32_t* cr = ctr + (size_t)kCtrStride * b;
 
   const int n_valid = clamp_ctx(ctx_len, b, max_ctx);
-  const uint32_t* hb = hist + (size_t)b * kCoarseBins;
+  const uint32_t* hb = hist + (size_t)b * S::kBins;
   const int seg = kFilterThreads - 1 - tid;  // thread 0 owns the top bins
   uint32_t hc[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; k++) {
     const int bin = seg * kPer + k;
-    hc[k] = bin < kCoarseBins ? hb[bin] : 0u;
+    hc[k] = bin < S::kBins ? hb[bin] : 0u;
   }
   __builtin_amdgcn_sched_barrier(0);
-  const int32_t* sb = scores + (size_t)b * max_ctx;
-  int32_t sv[kFilterIters];
+  const T* sb = scores + (size_t)b * max_ctx;
+  T sv[kFilterIters];
 #pragma unroll
   for (int u = 0; u < kFilterIters; u++)
     sv[u] = sb[min(c0 + (u * NW + wv) * kWave + l, max_ctx - 1)];
@@ -107,8 +110,8 @@ __global__ __launch_bounds__(kFilterThreads) void k_topc_filter(
 
   // bucket beta holds the scores [beta_lo, beta_hi]: above it means kept,
   // inside it means tied (no bucket: every valid token is kept)
-  int32_t beta_lo = 0, beta_hi = 0;
-  if (beta >= 0) coarse_bucket_range(beta, beta_lo, beta_hi);
+  T beta_lo = 0, beta_hi = 0;
+  if (beta >= 0) S::range(beta, beta_lo, beta_hi);
   const bool all_keep = beta < 0;
   uint32_t* bm = bitmap + (size_t)b * bitmap_words;
   const size_t tb = (size_t)b * max_ctx;
@@ -156,27 +159,56 @@ __global__ __launch_bounds__(kFilterThreads) void k_topc_filter(
 }
 
 constexpr int kEmitThreads = 1024;
-constexpr int kEmitMaxWords = 32768;  // bitmap in LDS up to 2^20 positions
-constexpr int kEmitTieLds = 3072;
 
-template <bool LDS_BM>
+// LDS budget of the emit kernel per score kind: the bitmap (when it fits)
+// and the tie list as (order-preserving key, position) entries.
+template <class S> struct EmitCfg;
+template <> struct EmitCfg<NarrowScore> {
+  static constexpr int kMaxWords = 32768;  // bitmap in LDS up to 2^20 positions
+  static constexpr int kTies = 3072;
+  using E = uint2;
+  static __device__ __forceinline__ E pack(int32_t s, int32_t p) {
+    return make_uint2((uint32_t)key_of_i32(s), (uint32_t)p);
+  }
+  static __device__ __forceinline__ uint64_t key(const E& e) { return e.x; }
+  static __device__ __forceinline__ uint32_t pos(const E& e) { return e.y; }
+  static __device__ __forceinline__ uint64_t key_of(int32_t s) { return key_of_i32(s); }
+};
+template <> struct EmitCfg<WideScore> {
+  static constexpr int kMaxWords = 8192;  // bitmap in LDS up to 2^18 positions
+  static constexpr int kTies = 4096;
+  using E = uint4;
+  static __device__ __forceinline__ E pack(int64_t s, int32_t p) {
+    const uint64_t k = key_of_i64(s);
+    return make_uint4((uint32_t)k, (uint32_t)(k >> 32), (uint32_t)p, 0u);
+  }
+  static __device__ __forceinline__ uint64_t key(const E& e) {
+    return (uint64_t)e.x | ((uint64_t)e.y << 32);
+  }
+  static __device__ __forceinline__ uint32_t pos(const E& e) { return e.z; }
+  static __device__ __forceinline__ uint64_t key_of(int64_t s) { return key_of_i64(s); }
+};
+
+template <class S, bool LDS_BM>
 __global__ __launch_bounds__(kEmitThreads) void k_topc_emit(
     const int32_t* __restrict__ ctx_len, uint32_t* __restrict__ hist,
-    uint32_t* __restrict__ bitmap, const int32_t* __restrict__ tie_s,
+    uint32_t* __restrict__ bitmap, const typename S::T* __restrict__ tie_s,
     const int32_t* __restrict__ tie_p, uint32_t* __restrict__ ctr, int32_t* __restrict__ cand,
     int max_ctx, int C, int bitmap_words) {
+  using T = typename S::T;
+  using Cfg = EmitCfg<S>;
   constexpr int NT = kEmitThreads;
   __shared__ uint32_t scan_sh[NT / kWave];
   __shared__ SelectShared ssh;
-  __shared__ __attribute__((aligned(16))) uint32_t bm_l[LDS_BM ? kEmitMaxWords : 4];
-  __shared__ uint2 lds_t[kEmitTieLds];  // (key, position) of the ties
+  __shared__ __attribute__((aligned(16))) uint32_t bm_l[LDS_BM ? Cfg::kMaxWords : 4];
+  __shared__ typename Cfg::E lds_t[Cfg::kTies];  // (key, position) of the ties
   __shared__ Threshold sh_thr;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int n_valid = clamp_ctx(ctx_len, b, max_ctx);
   const int nw = (n_valid + 31) / 32;
   const int nw4 = (nw + 3) / 4;
-  uint32_t* hb = hist + (size_t)b * kCoarseBins;
+  uint32_t* hb = hist + (size_t)b * S::kBins;
   uint32_t* bmg = bitmap + (size_t)b * bitmap_words;
   uint32_t* cr = ctr + (size_t)kCtrStride * b;
   uint32_t* bm = LDS_BM ? bm_l : bmg;
@@ -189,12 +221,11 @@ __global__ __launch_bounds__(kEmitThreads) void k_topc_emit(
 
   if (beta >= 0) {
     const uint32_t need = (uint32_t)C - above;  // 1 <= need <= n_tie
-    const int32_t* ts = tie_s + (size_t)b * max_ctx;
+    const T* ts = tie_s + (size_t)b * max_ctx;
     const int32_t* tp = tie_p + (size_t)b * max_ctx;
-    const bool in_lds = n_tie <= (uint32_t)kEmitTieLds;
+    const bool in_lds = n_tie <= (uint32_t)Cfg::kTies;
     if (in_lds) {
-      for (int i = tid; i < (int)n_tie; i += NT)
-        lds_t[i] = make_uint2((uint32_t)key_of_i32(ts[i]), (uint32_t)tp[i]);
+      for (int i = tid; i < (int)n_tie; i += NT) lds_t[i] = Cfg::pack(ts[i], tp[i]);
     }
     __syncthreads();
     Threshold thr{0ull, 0u, 0};
@@ -202,21 +233,21 @@ __global__ __launch_bounds__(kEmitThreads) void k_topc_emit(
       if (in_lds) {
         if (wave_id() == 0) {
           auto get = [&](int i, uint64_t& u, uint32_t& p) {
-            const uint2 e = lds_t[i];
-            u = e.x;
-            p = e.y;
+            const typename Cfg::E e = lds_t[i];
+            u = Cfg::key(e);
+            p = Cfg::pos(e);
           };
-          int32_t lo, hi;
-          coarse_bucket_range(beta, lo, hi);
-          const Threshold t = wave_threshold(get, (int)n_tie, need, ssh.hist, key_of_i32(lo),
-                                             key_of_i32(hi), pos_bits_below(max_ctx));
+          T lo, hi;
+          S::range(beta, lo, hi);
+          const Threshold t = wave_threshold(get, (int)n_tie, need, ssh.hist, Cfg::key_of(lo),
+                                             Cfg::key_of(hi), pos_bits_below(max_ctx));
           if (lane_id() == 0) sh_thr = t;
         }
         __syncthreads();
         thr = sh_thr;
       } else {
         auto get = [&](int i, uint64_t& u, uint32_t& p) {
-          u = key_of_i32(ts[i]);
+          u = Cfg::key_of(ts[i]);
           p = (uint32_t)tp[i];
         };
         thr = block_threshold<NT>(get, (int)n_tie, need, ssh);
@@ -224,13 +255,14 @@ __global__ __launch_bounds__(kEmitThreads) void k_topc_emit(
     }
     if (in_lds) {
       for (int i = tid; i < (int)n_tie; i += NT) {
-        const uint2 e = lds_t[i];
-        if (keep(thr, e.x, e.y)) atomicOr(&bm[e.y / 32], 1u << (e.y % 32));
+        const typename Cfg::E e = lds_t[i];
+        const uint32_t p = Cfg::pos(e);
+        if (keep(thr, Cfg::key(e), p)) atomicOr(&bm[p / 32], 1u << (p % 32));
       }
     } else {
       for (int i = tid; i < (int)n_tie; i += NT) {
         const uint32_t p = (uint32_t)tp[i];
-        if (keep(thr, key_of_i32(ts[i]), p)) atomicOr(&bm[p / 32], 1u << (p % 32));
+        if (keep(thr, Cfg::key_of(ts[i]), p)) atomicOr(&bm[p / 32], 1u << (p % 32));
       }
     }
   }
@@ -266,27 +298,38 @@ __global__ __launch_bounds__(kEmitThreads) void k_topc_emit(
   for (int i = (int)total + tid; i < C; i += NT) cb[i] = -1;
 
   // leave the histogram and tie counter cleared for the next call
-  for (int i = tid; i < kCoarseBins; i += NT) hb[i] = 0;
+  for (int i = tid; i < S::kBins; i += NT) hb[i] = 0;
   if (tid == 0) cr[kCtrTies] = 0;
 }
 
-hipError_t launch_topc_select(const int32_t* ctx_len, const CoarseWS& ws, int32_t* cand, int B,
-                              int max_ctx, int C, hipStream_t st) {
+template <class S>
+hipError_t launch_select(const int32_t* ctx_len, const SelectWS<typename S::T>& ws, int32_t* out,
+                         int B, int max_ctx, int C, hipStream_t st) {
   dim3 grid((ws.bitmap_words * 32 + kFilterChunk - 1) / kFilterChunk, B);
-  hipLaunchKernelGGL(k_topc_filter, grid, dim3(kFilterThreads), 0, st, ctx_len, ws.scores,
+  hipLaunchKernelGGL(k_topc_filter<S>, grid, dim3(kFilterThreads), 0, st, ctx_len, ws.scores,
                      ws.hist, ws.bitmap, ws.tie_s, ws.tie_p, ws.ctr, max_ctx, C,
                      ws.bitmap_words);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (ws.bitmap_words <= kEmitMaxWords)
-    hipLaunchKernelGGL(k_topc_emit<true>, dim3(B), dim3(kEmitThreads), 0, st, ctx_len, ws.hist,
-                       ws.bitmap, ws.tie_s, ws.tie_p, ws.ctr, cand, max_ctx, C,
+  if (ws.bitmap_words <= EmitCfg<S>::kMaxWords)
+    hipLaunchKernelGGL((k_topc_emit<S, true>), dim3(B), dim3(kEmitThreads), 0, st, ctx_len,
+                       ws.hist, ws.bitmap, ws.tie_s, ws.tie_p, ws.ctr, out, max_ctx, C,
                        ws.bitmap_words);
   else
-    hipLaunchKernelGGL(k_topc_emit<false>, dim3(B), dim3(kEmitThreads), 0, st, ctx_len,
-                       ws.hist, ws.bitmap, ws.tie_s, ws.tie_p, ws.ctr, cand, max_ctx, C,
+    hipLaunchKernelGGL((k_topc_emit<S, false>), dim3(B), dim3(kEmitThreads), 0, st, ctx_len,
+                       ws.hist, ws.bitmap, ws.tie_s, ws.tie_p, ws.ctr, out, max_ctx, C,
                        ws.bitmap_words);
   return hipGetLastError();
+}
+
+hipError_t launch_topc_select(const int32_t* ctx_len, const CoarseWS& ws, int32_t* cand, int B,
+                              int max_ctx, int C, hipStream_t st) {
+  return launch_select<NarrowScore>(ctx_len, ws, cand, B, max_ctx, C, st);
+}
+
+hipError_t launch_wide_select(const int32_t* ctx_len, const WideWS& ws, int32_t* out, int B,
+                              int max_ctx, int C, hipStream_t st) {
+  return launch_select<WideScore>(ctx_len, ws, out, B, max_ctx, C, st);
 }
 
 }  // namespace ls

@@ -5,6 +5,10 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+#include <new>
+#include <vector>
+
 #include <hip/hip_runtime.h>
 
 #include "../../include/ls.h"
@@ -69,6 +73,21 @@ int check_hot(const ls_hot_desc* d) {
   return LS_OK;
 }
 
+int check_prefill(const ls_prefill_desc* d) {
+  if (!d) return fail(LS_E_ARG, "null prefill descriptor");
+  if (d->n_query < 1) return fail(LS_E_ARG, "n_query must be >= 1 (got %d)", d->n_query);
+  if (d->max_ctx < 1 || d->max_ctx >= (1 << 28))
+    return fail(LS_E_ARG, "max_ctx must be in [1, 2^28) (got %d)", d->max_ctx);
+  if (d->q_pos0 < 0) return fail(LS_E_ARG, "q_pos0 must be >= 0 (got %d)", d->q_pos0);
+  if (d->topk < 1) return fail(LS_E_ARG, "topk must be >= 1 (got %d)", d->topk);
+  if (d->n_heads < 1) return fail(LS_E_ARG, "n_heads must be >= 1 (got %d)", d->n_heads);
+  if (d->n_heads > 64)
+    return fail(LS_E_UNSUPPORTED, "n_heads > 64 is not supported (got %d)", d->n_heads);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(LS_E_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", d->head_dim);
+  return LS_OK;
+}
+
 int check_attn(const ls_attn_desc* d) {
   if (!d) return fail(LS_E_ARG, "null attention descriptor");
   if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->topk < 1)
@@ -116,6 +135,23 @@ void carve_coarse(Carve& c, const ls_idx_desc* d, ls::CoarseWS* ws) {
   w.tie_s = c.take<int32_t>(B * L);
   w.tie_p = c.take<int32_t>(B * L);
   if (ws) *ws = w;
+}
+
+// One block of prefill rows: every row is a "request" of the int64 selection.
+void carve_prefill(Carve& c, const ls_prefill_desc* d, ls::WideWS* ws, int32_t** ctx) {
+  const size_t R = d->n_query < ls::kPrefillRowBlock ? d->n_query : ls::kPrefillRowBlock;
+  const size_t L = d->max_ctx;
+  ls::WideWS w;
+  w.hist = c.take<uint32_t>(R * ls::kWideBins);
+  w.ctr = c.take<uint32_t>(R * ls::kCtrStride);
+  w.scores = c.take<int64_t>(R * L);
+  w.bitmap_words = bitmap_words(d->max_ctx);
+  w.bitmap = c.take<uint32_t>(R * w.bitmap_words);
+  w.tie_s = c.take<int64_t>(R * L);
+  w.tie_p = c.take<int32_t>(R * L);
+  int32_t* cx = c.take<int32_t>(R);
+  if (ws) *ws = w;
+  if (ctx) *ctx = cx;
 }
 
 void carve_refine(Carve& c, const ls_idx_desc* d, ls::RefineWS* ws) {
@@ -199,6 +235,12 @@ size_t ws_size(int32_t op, const void* desc) {
       carve_coarse(c, &d->idx, nullptr);
       carve_refine(c, &d->idx, nullptr);
       carve_attn(c, &d->attn, attn_ws_splits(&d->attn), nullptr, nullptr);
+      break;
+    }
+    case LS_OP_PREFILL: {
+      const ls_prefill_desc* d = (const ls_prefill_desc*)desc;
+      if (check_prefill(d)) return 0;
+      carve_prefill(c, d, nullptr, nullptr);
       break;
     }
     default:
@@ -539,9 +581,28 @@ int ls_decode_step(const ls_step_desc* desc, const ls_step_io* io, void* ws_dev,
 int ls_prefill_index_topk(const ls_prefill_desc* desc, const int8_t* q_dev, const int8_t* w_dev,
                           const int8_t* keys_dev, int32_t* topk_dev, void* ws_dev,
                           size_t ws_bytes, ls_stream_t stream) {
-  (void)desc; (void)q_dev; (void)w_dev; (void)keys_dev; (void)topk_dev; (void)ws_dev;
-  (void)ws_bytes; (void)stream;
-  return fail(LS_E_UNSUPPORTED, "prefill indexer not built yet");
+  LS_TRY(check_prefill(desc));
+  LS_NONNULL(q_dev);
+  LS_NONNULL(w_dev);
+  LS_NONNULL(keys_dev);
+  LS_NONNULL(topk_dev);
+  LS_ALIGNED(q_dev);
+  LS_ALIGNED(keys_dev);
+  LS_TRY(check_ws(LS_OP_PREFILL, desc, ws_dev, ws_bytes));
+  Carve c;
+  c.base = (char*)ws_dev;
+  ls::WideWS ws;
+  int32_t* ctx = nullptr;
+  carve_prefill(c, desc, &ws, &ctx);
+  const int H = desc->n_heads, D = desc->head_dim, K = desc->topk;
+  for (int r0 = 0; r0 < desc->n_query; r0 += ls::kPrefillRowBlock) {
+    const int rows = std::min(ls::kPrefillRowBlock, desc->n_query - r0);
+    LS_HIP(ls::launch_prefill_block(q_dev + (size_t)r0 * H * D, w_dev + (size_t)r0 * H, keys_dev,
+                                    ws, ctx, topk_dev + (size_t)r0 * K, rows, desc->q_pos0 + r0,
+                                    H, D, desc->max_ctx, K, (hipStream_t)stream),
+           "prefill launch");
+  }
+  return LS_OK;
 }
 
 int ls_prefill_stream_layers(const ls_prefill_desc* desc, int32_t n_layers,
@@ -549,9 +610,65 @@ int ls_prefill_stream_layers(const ls_prefill_desc* desc, int32_t n_layers,
                              const int8_t* const* keys_host, int8_t* buf0_dev, int8_t* buf1_dev,
                              int32_t* const* topk_dev, void* ws_dev, size_t ws_bytes,
                              ls_stream_t stream, ls_stream_t copy_stream) {
-  (void)desc; (void)n_layers; (void)q_dev; (void)w_dev; (void)keys_host; (void)buf0_dev;
-  (void)buf1_dev; (void)topk_dev; (void)ws_dev; (void)ws_bytes; (void)stream; (void)copy_stream;
-  return fail(LS_E_UNSUPPORTED, "prefill streaming not built yet");
+  LS_TRY(check_prefill(desc));
+  if (n_layers < 1) return fail(LS_E_ARG, "n_layers must be >= 1 (got %d)", n_layers);
+  LS_NONNULL(q_dev);
+  LS_NONNULL(w_dev);
+  LS_NONNULL(keys_host);
+  LS_NONNULL(topk_dev);
+  LS_NONNULL(buf0_dev);
+  LS_NONNULL(buf1_dev);
+  LS_ALIGNED(buf0_dev);
+  LS_ALIGNED(buf1_dev);
+  if (stream == copy_stream)
+    return fail(LS_E_ARG, "the copy stream must differ from the compute stream");
+  for (int l = 0; l < n_layers; l++) {
+    if (!q_dev[l] || !w_dev[l] || !keys_host[l] || !topk_dev[l])
+      return fail(LS_E_ARG, "null pointer for layer %d", l);
+  }
+  LS_TRY(check_ws(LS_OP_PREFILL, desc, ws_dev, ws_bytes));
+  hipStream_t st = (hipStream_t)stream, cp = (hipStream_t)copy_stream;
+  const size_t bytes = (size_t)desc->max_ctx * desc->head_dim;
+  // copied[l]: layer l's keys are in its buffer; done[l]: layer l no longer
+  // reads its buffer, so layer l + 2 may overwrite it
+  std::vector<hipEvent_t> copied, done;
+  try {
+    copied.assign(n_layers, nullptr);
+    done.assign(n_layers, nullptr);
+  } catch (const std::bad_alloc&) {
+    return fail(LS_E_ARG, "cannot track %d layers", n_layers);
+  }
+  int rc = LS_OK;
+  for (int l = 0; l < n_layers && rc == LS_OK; l++) {
+    int8_t* buf = (l & 1) ? buf1_dev : buf0_dev;
+    hipError_t e = hipEventCreateWithFlags(&copied[l], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&done[l], hipEventDisableTiming);
+    if (e == hipSuccess && l >= 2) e = hipStreamWaitEvent(cp, done[l - 2], 0);
+    if (e == hipSuccess) e = hipMemcpyAsync(buf, keys_host[l], bytes, hipMemcpyHostToDevice, cp);
+    if (e == hipSuccess) e = hipEventRecord(copied[l], cp);
+    if (e == hipSuccess) e = hipStreamWaitEvent(st, copied[l], 0);
+    if (e != hipSuccess) {
+      rc = hip_fail(e, "prefill stream ordering");
+      break;
+    }
+    rc = ls_prefill_index_topk(desc, q_dev[l], w_dev[l], buf, topk_dev[l], ws_dev, ws_bytes,
+                               stream);
+    if (rc == LS_OK) {
+      e = hipEventRecord(done[l], st);
+      if (e != hipSuccess) rc = hip_fail(e, "prefill stream ordering");
+    }
+  }
+  // the copy stream ends after the compute stream's last use of the buffers
+  if (rc == LS_OK) {
+    hipError_t e = hipStreamWaitEvent(cp, done[n_layers - 1], 0);
+    if (e != hipSuccess) rc = hip_fail(e, "prefill stream ordering");
+  }
+  // events still pending are released by the runtime once they complete
+  for (int l = 0; l < n_layers; l++) {
+    if (copied[l]) (void)hipEventDestroy(copied[l]);
+    if (done[l]) (void)hipEventDestroy(done[l]);
+  }
+  return rc;
 }
 
 }  // extern "C"

@@ -12,24 +12,32 @@ namespace ls {
 // Histogram of coarse scores: float-like monotone buckets of an int32 score,
 // 6 mantissa bits, both signs (see coarse_bucket in k_index.hip).
 constexpr int kCoarseBins = 3328;
-// Positions handled by one workgroup of the candidate filter.
-constexpr int kSelectChunk = 4096;
+// The same for int64 scores (prefill rows): 7552 buckets.
+constexpr int kWideBins = 7552;
 // Per-request counters sit on their own 128-byte lines (32 words apart).
 constexpr int kCtrStride = 32;
 // Tokens scored by one workgroup of the coarse kernel.
 constexpr int kCoarseTokPerWG = 2048;
 // Candidates scored by one workgroup of the refine kernel.
 constexpr int kRefinePerWG = 256;
+// Keys scored by one workgroup of the prefill indexer, and query rows per
+// pass of it (each pass owns one score buffer of that many rows).
+constexpr int kPrefillTokPerWG = 4096;
+constexpr int kPrefillRowBlock = 512;
 
-struct CoarseWS {
-  int32_t* scores;     // [B, max_ctx]
-  uint32_t* hist;      // [B, kCoarseBins]      zero between calls
+// Workspace of a histogram-driven selection over rows of scores of type T.
+template <class T>
+struct SelectWS {
+  T* scores;           // [B, max_ctx]
+  uint32_t* hist;      // [B, bins]             zero between calls
   uint32_t* bitmap;    // [B, bitmap_words]
-  int32_t* tie_s;      // [B, max_ctx]
+  T* tie_s;            // [B, max_ctx]
   int32_t* tie_p;      // [B, max_ctx]
   uint32_t* ctr;       // [B, kCtrStride] tie count (word 0); zero between calls
   int bitmap_words;
 };
+using CoarseWS = SelectWS<int32_t>;  // coarse scores, kCoarseBins buckets
+using WideWS = SelectWS<int64_t>;    // int64 scores, 7552 buckets
 
 struct RefineWS {
   int64_t* fs;         // [B, n_cand]
@@ -47,6 +55,16 @@ hipError_t launch_coarse_scores(const int8_t* q, const int8_t* w, const uint8_t*
                                 int D, int max_ctx, hipStream_t st);
 
 hipError_t launch_topc_select(const int32_t* ctx_len, const CoarseWS& ws, int32_t* cand, int B,
+                              int max_ctx, int C, hipStream_t st);
+
+// Prefill indexer for `rows` query rows at absolute positions first_pos ..:
+// scores into ws, row lengths into ctx [rows], top-K into topk_out [rows, K].
+hipError_t launch_prefill_block(const int8_t* q, const int8_t* w, const int8_t* keys,
+                                const WideWS& ws, int32_t* ctx, int32_t* topk_out, int rows,
+                                int first_pos, int H, int D, int max_ctx, int K, hipStream_t st);
+
+// The same selection over int64 scores (prefill rows).
+hipError_t launch_wide_select(const int32_t* ctx_len, const WideWS& ws, int32_t* out, int B,
                               int max_ctx, int C, hipStream_t st);
 
 // Refine + top-k; with pos2slot != nullptr also the hot-buffer resolve
