@@ -28,9 +28,14 @@ FLAGS = [
 ]
 
 
+# Per-source additions.  The coarse scoring kernel reads every MFMA result
+# in a VALU epilogue, so its accumulators live in VGPRs (no AGPR copies).
+EXTRA = {"k_index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-c",
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-I", os.path.join(ROOT, "include"), "-c",
            os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"

@@ -68,16 +68,20 @@ hipError_t launch_pack_coarse(const int8_t* k8, uint8_t* kc, int64_t n_rows, int
 //
 // As an int8 GEMM [heads x D] x [D x tokens] on v_mfma_i32_16x16x64_i8: the
 // A operand is the int8 query (16 heads per tile, held in VGPRs for the
-// whole kernel), the B operand is 16 tokens' compact keys.  A packed nibble
-// n is widened to the byte n*16 by masking (x & 0xF0F0F0F0 for the odd
-// elements, (x << 4) & 0xF0F0F0F0 for the even ones), so the MFMA returns
-// 16 * dot exactly; the query is laid out even/odd to match.  Epilogue:
-// max(.,0) >> 4, times the head weight (24-bit multiply-add), summed over
-// heads in-lane and then across the four 16-lane groups with a
-// reduce-scatter that leaves one token per lane.  Every lane then buckets its
-// score into an LDS histogram that is flushed to the request's global
-// histogram at the end: the first pass of the candidate selection, fused
-// here so that nothing re-reads the scores to build it.
+// whole kernel), the B operand is 16 tokens' compact keys.  A stored nibble
+// b (two's complement, value v in [-8, 7]) read as b ^ 8 is the offset-binary
+// value v + 8 in [0, 15], so one xor and one mask widen it to a byte and the
+// MFMA returns dot + c_h with c_h = 8 * sum_d q[h][d]; the query is laid out
+// even/odd to match the nibble order.  Then w * max(0, dot) =
+// w * max(acc, c_h) - w * c_h: one max and one 24-bit multiply-add per head
+// and token, and the constant sum of w * c_h over the lane's heads is
+// subtracted once per token.  Sums wrap modulo 2^32, which is exact because
+// the true score fits in int32.  The head sum then finishes across the four
+// 16-lane groups with a reduce-scatter that leaves one token per lane.
+// Every lane then buckets its score into an LDS histogram that is flushed to
+// the request's global histogram at the end: the first pass of the
+// candidate selection, fused here so that nothing re-reads the scores to
+// build it.
 //
 // Memory: each wave streams 64 tokens (4 KiB of compact keys) per step with
 // one 16-byte load per lane per 16-token tile, and prefetches the next 64
@@ -85,8 +89,8 @@ hipError_t launch_pack_coarse(const int8_t* k8, uint8_t* kc, int64_t n_rows, int
 // request's end are clamped to its last token (their results are dropped),
 // so the loop has no divergent branches around memory operations.
 //
-// Exactness: |q.kc| <= 128*127*8 < 2^17, |w| <= 128, <= 16 heads per lane
-// and 4 lane groups: |sum| < 2^31.
+// Exactness: |q.kc| <= 128*128*8 = 2^17, |w| <= 128, 64 heads: |score| <
+// 2^31; every partial sum is taken modulo 2^32.
 
 // Query operands for head row qh, lane group g.  D = 128: lane group g owns
 // dims [32g, 32g+32); mf 0 holds the even dims, mf 1 the odd ones (byte j =
@@ -133,17 +137,28 @@ __device__ __forceinline__ T reduce_scatter4(T p0, T p1, T p2, T p3, int g) {
   return (even ? k0 : k1) + r;
 }
 
+// 24-bit signed multiply-add, c + a * b modulo 2^32 (one v_mad_i32_i24; the
+// compiler would otherwise split the chain into multiplies and 3-way adds).
+__device__ __forceinline__ uint32_t mad_i24(int32_t a, int32_t b, uint32_t c) {
+  uint32_t d;
+  asm("v_mad_i32_i24 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
+// The four 16-token tiles of one 64-token step: lane (n, g) loads token
+// base + 16 tt + n (clamped to t_last) at byte offset g * LB of its row.
+// Offsets stay 32-bit (a request's compact keys are < 4 GiB).
 template <int D>
 __device__ __forceinline__ void coarse_load4(const uint8_t* kb, int base, int n, int t_last,
                                              v4i (&r)[4]) {
-  constexpr int KB = D / 2;
+  constexpr uint32_t KB = D / 2;
 #pragma unroll
   for (int tt = 0; tt < 4; tt++) {
-    const int t = min(base + 16 * tt + n, t_last);
+    const uint32_t t = (uint32_t)min(base + 16 * tt + n, t_last);
     if (D == 128) {
-      r[tt] = *(const v4i*)(kb + (size_t)t * KB);
+      r[tt] = *(const v4i*)(kb + t * KB);
     } else {
-      const int2 v = *(const int2*)(kb + (size_t)t * KB);
+      const int2 v = *(const int2*)(kb + t * KB);
       r[tt] = v4i{v.x, v.y, 0, 0};
     }
   }
@@ -172,6 +187,19 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
 
   const int l = lane_id(), n = l & 15, g = l >> 4;
   const int8_t* qb = q + (size_t)b * H * D;
+  // c_h = 8 * sum_d q[h][d] of every head, through LDS
+  __shared__ int32_t hsum[64];
+  if (threadIdx.x < H) {
+    const v4i* qh = (const v4i*)(qb + (size_t)threadIdx.x * D);
+    int32_t sacc = 0;
+#pragma unroll
+    for (int j = 0; j < D / 16; j++) {
+      const v4i v = qh[j];
+#pragma unroll
+      for (int k = 0; k < 4; k++) sacc = __builtin_amdgcn_sdot4(v[k], 0x01010101, sacc, false);
+    }
+    hsum[threadIdx.x] = 8 * sacc;
+  }
   v4i qa[HT][NMF];
   int32_t wv[HT][4];
 #pragma unroll
@@ -190,15 +218,26 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
     }
   }
   __syncthreads();
+  int32_t cv[HT][4];
+  uint32_t k_lane = 0;  // sum of w * c_h over this lane's heads
+#pragma unroll
+  for (int mt = 0; mt < HT; mt++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int hh = 16 * mt + 4 * g + i;
+      cv[mt][i] = hh < H ? hsum[hh] : 0;
+      k_lane += (uint32_t)(wv[mt][i] * cv[mt][i]);
+    }
 
-  const uint8_t* kb = kc + (size_t)b * max_ctx * KB + g * LB;
+  const uint8_t* kb = kc + (size_t)b * max_ctx * KB + g * LB;  // + 32-bit token offsets
   int32_t* sb = scores + (size_t)b * max_ctx;
   const int t_last = t_end - 1;
 
   // One 64-token step: all MFMAs first (independent accumulators), then the
   // epilogue, so MFMA latency overlaps the VALU work of earlier tiles.
   auto process = [&](int base, const v4i (&raw)[4]) {
-    const uint32_t m = 0xF0F0F0F0u;
+    // low / high nibble of every byte as offset binary: (x & m) ^ 8 per byte
+    const uint32_t m = 0x0F0F0F0Fu, f = 0x08080808u;
     v4i acc[4][HT];
 #pragma unroll
     for (int tt = 0; tt < 4; tt++) {
@@ -206,11 +245,13 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
       const uint32_t x2 = (uint32_t)raw[tt][2], x3 = (uint32_t)raw[tt][3];
       v4i bop[NMF];
       if (D == 128) {
-        bop[0] = v4i{(int)((x0 << 4) & m), (int)((x1 << 4) & m), (int)((x2 << 4) & m),
-                     (int)((x3 << 4) & m)};
-        bop[NMF - 1] = v4i{(int)(x0 & m), (int)(x1 & m), (int)(x2 & m), (int)(x3 & m)};
+        bop[0] = v4i{(int)((x0 & m) ^ f), (int)((x1 & m) ^ f), (int)((x2 & m) ^ f),
+                     (int)((x3 & m) ^ f)};
+        bop[NMF - 1] = v4i{(int)(((x0 >> 4) & m) ^ f), (int)(((x1 >> 4) & m) ^ f),
+                           (int)(((x2 >> 4) & m) ^ f), (int)(((x3 >> 4) & m) ^ f)};
       } else {
-        bop[0] = v4i{(int)((x0 << 4) & m), (int)((x1 << 4) & m), (int)(x0 & m), (int)(x1 & m)};
+        bop[0] = v4i{(int)((x0 & m) ^ f), (int)((x1 & m) ^ f), (int)(((x0 >> 4) & m) ^ f),
+                     (int)(((x1 >> 4) & m) ^ f)};
       }
 #pragma unroll
       for (int mt = 0; mt < HT; mt++)
@@ -226,14 +267,15 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
     int32_t part[4];
 #pragma unroll
     for (int tt = 0; tt < 4; tt++) {
-      int32_t s = 0;
+      uint32_t s = 0u - k_lane;
 #pragma unroll
       for (int mt = 0; mt < HT; mt++)
 #pragma unroll
-        for (int i = 0; i < 4; i++) s += __mul24(wv[mt][i], max(acc[tt][mt][i], 0) >> 4);
-      part[tt] = s;
+        for (int i = 0; i < 4; i++) s = mad_i24(wv[mt][i], max(acc[tt][mt][i], cv[mt][i]), s);
+      part[tt] = (int32_t)s;
     }
-    const int32_t score = reduce_scatter4(part[0], part[1], part[2], part[3], g);
+    const int32_t score = (int32_t)reduce_scatter4((uint32_t)part[0], (uint32_t)part[1],
+                                                   (uint32_t)part[2], (uint32_t)part[3], g);
     const int t = base + l;
     if (t < t_end) {
       sb[t] = score;
@@ -242,7 +284,8 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
   };
 
   // Ping-pong register buffers: the loads of step i+1 are in flight while
-  // step i computes.  Past the end every lane loads row t_last (one line).
+  // step i computes (a third buffer measured slower).  Past the end every
+  // lane loads row t_last (one line).
   int base = __builtin_amdgcn_readfirstlane(t_begin + wave_id() * 64);
   if (base < t_end) {
     v4i bufA[4], bufB[4];
