@@ -164,6 +164,8 @@ __device__ __forceinline__ void coarse_load4(const uint8_t* kb, int base, int n,
   }
 }
 
+constexpr int kCoarseTileGroup = 2;
+
 template <int D, int HT>
 __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
                                                 const int8_t* __restrict__ w,
@@ -238,41 +240,47 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
   auto process = [&](int base, const v4i (&raw)[4]) {
     // low / high nibble of every byte as offset binary: (x & m) ^ 8 per byte
     const uint32_t m = 0x0F0F0F0Fu, f = 0x08080808u;
-    v4i acc[4][HT];
+    int32_t part[4];
+    // tiles in groups of kCoarseTileGroup: the group's MFMAs, then its
+    // epilogue (fewer live accumulators, so more waves fit per SIMD)
 #pragma unroll
-    for (int tt = 0; tt < 4; tt++) {
-      const uint32_t x0 = (uint32_t)raw[tt][0], x1 = (uint32_t)raw[tt][1];
-      const uint32_t x2 = (uint32_t)raw[tt][2], x3 = (uint32_t)raw[tt][3];
-      v4i bop[NMF];
-      if (D == 128) {
-        bop[0] = v4i{(int)((x0 & m) ^ f), (int)((x1 & m) ^ f), (int)((x2 & m) ^ f),
-                     (int)((x3 & m) ^ f)};
-        bop[NMF - 1] = v4i{(int)(((x0 >> 4) & m) ^ f), (int)(((x1 >> 4) & m) ^ f),
-                           (int)(((x2 >> 4) & m) ^ f), (int)(((x3 >> 4) & m) ^ f)};
-      } else {
-        bop[0] = v4i{(int)((x0 & m) ^ f), (int)((x1 & m) ^ f), (int)(((x0 >> 4) & m) ^ f),
-                     (int)(((x1 >> 4) & m) ^ f)};
-      }
+    for (int t0 = 0; t0 < 4; t0 += kCoarseTileGroup) {
+      v4i acc[kCoarseTileGroup][HT];
 #pragma unroll
-      for (int mt = 0; mt < HT; mt++)
-        acc[tt][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[mt][0], bop[0], v4i{0, 0, 0, 0},
-                                                            0, 0, 0);
-      if (NMF == 2) {
+      for (int u = 0; u < kCoarseTileGroup; u++) {
+        const int tt = t0 + u;
+        const uint32_t x0 = (uint32_t)raw[tt][0], x1 = (uint32_t)raw[tt][1];
+        const uint32_t x2 = (uint32_t)raw[tt][2], x3 = (uint32_t)raw[tt][3];
+        v4i bop[NMF];
+        if (D == 128) {
+          bop[0] = v4i{(int)((x0 & m) ^ f), (int)((x1 & m) ^ f), (int)((x2 & m) ^ f),
+                       (int)((x3 & m) ^ f)};
+          bop[NMF - 1] = v4i{(int)(((x0 >> 4) & m) ^ f), (int)(((x1 >> 4) & m) ^ f),
+                             (int)(((x2 >> 4) & m) ^ f), (int)(((x3 >> 4) & m) ^ f)};
+        } else {
+          bop[0] = v4i{(int)((x0 & m) ^ f), (int)((x1 & m) ^ f), (int)(((x0 >> 4) & m) ^ f),
+                       (int)(((x1 >> 4) & m) ^ f)};
+        }
 #pragma unroll
         for (int mt = 0; mt < HT; mt++)
-          acc[tt][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[mt][NMF - 1], bop[NMF - 1],
-                                                              acc[tt][mt], 0, 0, 0);
+          acc[u][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[mt][0], bop[0],
+                                                             v4i{0, 0, 0, 0}, 0, 0, 0);
+        if (NMF == 2) {
+#pragma unroll
+          for (int mt = 0; mt < HT; mt++)
+            acc[u][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[mt][NMF - 1], bop[NMF - 1],
+                                                               acc[u][mt], 0, 0, 0);
+        }
       }
-    }
-    int32_t part[4];
 #pragma unroll
-    for (int tt = 0; tt < 4; tt++) {
-      uint32_t s = 0u - k_lane;
+      for (int u = 0; u < kCoarseTileGroup; u++) {
+        uint32_t s = 0u - k_lane;
 #pragma unroll
-      for (int mt = 0; mt < HT; mt++)
+        for (int mt = 0; mt < HT; mt++)
 #pragma unroll
-        for (int i = 0; i < 4; i++) s = mad_i24(wv[mt][i], max(acc[tt][mt][i], cv[mt][i]), s);
-      part[tt] = (int32_t)s;
+          for (int i = 0; i < 4; i++) s = mad_i24(wv[mt][i], max(acc[u][mt][i], cv[mt][i]), s);
+        part[t0 + u] = (int32_t)s;
+      }
     }
     const int32_t score = (int32_t)reduce_scatter4((uint32_t)part[0], (uint32_t)part[1],
                                                    (uint32_t)part[2], (uint32_t)part[3], g);

@@ -17,7 +17,7 @@ constexpr int kWideBins = 7552;
 // Per-request counters sit on their own 128-byte lines (32 words apart).
 constexpr int kCtrStride = 32;
 // Tokens scored by one workgroup of the coarse kernel.
-constexpr int kCoarseTokPerWG = 2048;
+constexpr int kCoarseTokPerWG = 8192;
 // Candidates scored by one workgroup of the refine kernel.
 constexpr int kRefinePerWG = 256;
 // Keys scored by one workgroup of the prefill indexer, and query rows per
