@@ -68,15 +68,19 @@ __global__ __launch_bounds__(256) void k_prefill_scores(
     const int8_t* qr = q + (size_t)row * H * D;
 #pragma unroll
     for (int mt = 0; mt < HT; mt++) {
+      // unconditional loads (clamped index, result selected): a load under
+      // a divergent condition would be a branch that waits for it
       const int h = 16 * mt + n;
 #pragma unroll
-      for (int mf = 0; mf < NMF; mf++)
-        qa[r][mt][mf] = (h < H) ? *(const v4i*)(qr + (size_t)h * D + off + 16 * mf)
-                                : v4i{0, 0, 0, 0};
+      for (int mf = 0; mf < NMF; mf++) {
+        const v4i v = *(const v4i*)(qr + (size_t)min(h, H - 1) * D + off + 16 * mf);
+        qa[r][mt][mf] = (h < H) ? v : v4i{0, 0, 0, 0};
+      }
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int hh = 16 * mt + 4 * g + i;
-        wv[r][mt][i] = hh < H ? (int32_t)w[(size_t)row * H + hh] : 0;
+        const int32_t wr = (int32_t)w[(size_t)row * H + min(hh, H - 1)];
+        wv[r][mt][i] = hh < H ? wr : 0;
       }
     }
   }

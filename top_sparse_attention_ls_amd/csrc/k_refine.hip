@@ -40,19 +40,34 @@ __global__ __launch_bounds__(256) void k_refine(const int8_t* __restrict__ q,
 
   const int c_base = blockIdx.x * kRefinePerWG + wave_id() * 64;
   const int8_t* kb = k8 + (size_t)b * max_ctx * D;
+  // Every load below is unconditional (indices clamped, results selected
+  // afterwards): a load under a divergent condition becomes a branch that
+  // waits for it, which would serialise the whole prologue.
+  // The candidate this lane reports, and its hot slot: looked up now, in
+  // parallel with the key loads below.
+  const int c_out = c_base + l;
+  const int32_t p_raw = cb[min(c_out, C - 1)];
+  const int32_t p_out = (c_out < C) ? p_raw : -1;
   int32_t pos[4];
   v4i raw[4][NMF];
 #pragma unroll
   for (int tt = 0; tt < 4; tt++) {
     const int c = c_base + 16 * tt + n;
-    pos[tt] = (c < C) ? cb[c] : -1;
-    const int p = pos[tt] >= 0 ? pos[tt] : 0;
+    const int32_t pr = cb[min(c, C - 1)];
+    pos[tt] = (c < C) ? pr : -1;
+    const int p = max(pos[tt], 0);
 #pragma unroll
     for (int mf = 0; mf < NMF; mf++) {
       const int off = (D == 128) ? 32 * g + 16 * mf : 16 * g;
       raw[tt][mf] = *(const v4i*)(kb + (size_t)p * D + off);
     }
   }
+
+  // hot slot of the reported candidate (without a table, a harmless read of
+  // the candidate list stands in, so that no branch waits on the load)
+  const int32_t* p2s = pos2slot ? pos2slot + (size_t)b * max_ctx : cb;
+  const int32_t slot_raw = p2s[pos2slot ? max(p_out, 0) : 0];
+  const int32_t slot_out = (p_out >= 0) ? slot_raw : 0;
 
   v4i qa[HT][NMF];
   int32_t wv[HT][4];
@@ -62,12 +77,14 @@ __global__ __launch_bounds__(256) void k_refine(const int8_t* __restrict__ q,
 #pragma unroll
     for (int mf = 0; mf < NMF; mf++) {
       const int off = (D == 128) ? 32 * g + 16 * mf : 16 * g;
-      qa[mt][mf] = (h < H) ? *(const v4i*)(qb + (size_t)h * D + off) : v4i{0, 0, 0, 0};
+      const v4i v = *(const v4i*)(qb + (size_t)min(h, H - 1) * D + off);
+      qa[mt][mf] = (h < H) ? v : v4i{0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int hh = 16 * mt + 4 * g + i;
-      wv[mt][i] = hh < H ? (int32_t)w[(size_t)b * H + hh] : 0;
+      const int32_t wr = (int32_t)w[(size_t)b * H + min(hh, H - 1)];
+      wv[mt][i] = hh < H ? wr : 0;
     }
   }
 
@@ -104,13 +121,11 @@ __global__ __launch_bounds__(256) void k_refine(const int8_t* __restrict__ q,
   int64_t sx = even ? k1 : k0;
   int64_t rx = __shfl_xor(sx, 16, kWave);
   const int64_t score = (even ? k0 : k1) + rx;
-  const int c = c_base + l;
-  if (c < C) {
-    const int32_t p = cb[c];
-    fs[(size_t)b * C + c] = (p >= 0) ? score : 0;
+  if (c_out < C) {
+    fs[(size_t)b * C + c_out] = (p_out >= 0) ? score : 0;
     // the candidate's hot slot, looked up here where the lookups spread over
     // the whole grid, for the per-request top-k to read coalesced
-    if (pos2slot) cslot[(size_t)b * C + c] = (p >= 0) ? pos2slot[(size_t)b * max_ctx + p] : 0;
+    if (pos2slot) cslot[(size_t)b * C + c_out] = slot_out;
   }
 }
 
@@ -166,21 +181,21 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
 
   int32_t c[PER];
   int64_t f[PER];
-#pragma unroll
-  for (int k = 0; k < PER; k++) {
-    const int i = tid + NT * k;
-    const bool in = i < C;
-    c[k] = in ? cb[i] : -1;
-    f[k] = in ? fb[i] : 0;
-  }
-  // hot slots of the candidates, looked up by the refine kernel
+  // unconditional loads (clamped index, result selected afterwards)
   const bool resolve = pos2slot != nullptr;
   const int32_t* csb = cslot + (size_t)b * C;
   int32_t slot[PER];
 #pragma unroll
   for (int k = 0; k < PER; k++) {
     const int i = tid + NT * k;
-    slot[k] = (resolve && i < C) ? csb[i] : 0;
+    const int ic = min(i, C - 1);
+    const int32_t cr = cb[ic];
+    const int64_t fr = fb[ic];
+    const int32_t sr = csb[ic];  // hot slots of the candidates (refine kernel)
+    const bool in = i < C;
+    c[k] = in ? cr : -1;
+    f[k] = in ? fr : 0;
+    slot[k] = (resolve && in) ? sr : 0;
   }
 #pragma unroll
   for (int k = 0; k < BPT; k++) hist[tid * BPT + k] = 0;
@@ -535,18 +550,24 @@ __global__ __launch_bounds__(256) void k_hot_gather(const int32_t* __restrict__ 
   uint4* hb = hot + ((size_t)b * (hot_slots + K) + hot_slots) * chunks;
   for (uint32_t i = i0 + threadIdx.x; i < i1; i += 256 * kGatherUnroll) {
     uint4 v[kGatherUnroll];
-    uint32_t dst[kGatherUnroll];
+    uint32_t dst[kGatherUnroll], c[kGatherUnroll];
+    int32_t p[kGatherUnroll];
+    // all miss positions first, then all row loads, then all stores
 #pragma unroll
     for (int u = 0; u < kGatherUnroll; u++) {
       const uint32_t idx = min(i + 256u * u, i1 - 1);
-      const uint32_t j = idx / (uint32_t)chunks, c = idx - j * (uint32_t)chunks;
-      const int32_t p = min(max(mp[j], 0), max_ctx - 1);
-      v[u] = pb[(size_t)p * chunks + c];
+      const uint32_t j = idx / (uint32_t)chunks;
+      c[u] = idx - j * (uint32_t)chunks;
       dst[u] = idx;
+      p[u] = mp[j];
     }
 #pragma unroll
     for (int u = 0; u < kGatherUnroll; u++)
-      if (i + 256u * u < i1) hb[dst[u]] = v[u];
+      v[u] = pb[(size_t)min(max(p[u], 0), max_ctx - 1) * chunks + c[u]];
+    // past the range the index is clamped to the range's last piece, so a
+    // duplicate store writes that piece's own value again: no branch needed
+#pragma unroll
+    for (int u = 0; u < kGatherUnroll; u++) hb[dst[u]] = v[u];
   }
 }
 
