@@ -136,33 +136,26 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
   const int i_end = min(i_begin + rows_per_split, K);
   const int n_rows = max(i_end - i_begin, 0);
   const int n_tiles = (n_rows + kTileR - 1) / kTileR;
-  const int32_t* rb = rows + (size_t)b * K + i_begin;
-  for (int i = threadIdx.x; i < n_tiles * kTileR; i += NW * 64)
-  {
-    // row ids outside the request's rows are padding, like -1
-    const int32_t r = i < n_rows ? rb[i] : -1;
-    rid_lds[i] = (r >= 0 && r < rows_per_req) ? r : -1;
-  }
-
-  // B operand of S^T = K Q^T: head n, dims 16 ks + 8 half .. +7
-  v8bf qB[QK_STEPS];
-  {
-    const uint16_t* qh = q + ((size_t)b * Hq + (h_ok ? h : 0)) * DQK + 8 * half;
+  // Prologue, ordered so that the latencies overlap: the split's row ids
+  // (loaded unconditionally, clamped into the request's list), staged in
+  // LDS; the first tiles' DMA as soon as they are; the query meanwhile.
+  const int32_t* rq = rows + (size_t)b * K;
+  constexpr int kRidIters = (kMaxSplitRows + kTileR + NW * 64 - 1) / (NW * 64);
+  int32_t rv[kRidIters];
 #pragma unroll
-    for (int ks = 0; ks < QK_STEPS; ks++) {
-      v8u16 v = h_ok ? *(const v8u16*)(qh + 16 * ks) : v8u16{0, 0, 0, 0, 0, 0, 0, 0};
-      qB[ks] = __builtin_bit_cast(v8bf, v);
-    }
+  for (int k = 0; k < kRidIters; k++) {
+    const int i = threadIdx.x + k * NW * 64;
+    rv[k] = rq[min(i_begin + min(i, max(n_rows - 1, 0)), K - 1)];
+  }
+#pragma unroll
+  for (int k = 0; k < kRidIters; k++) {
+    const int i = threadIdx.x + k * NW * 64;
+    // row ids outside the request's rows are padding, like -1
+    const int32_t r = i < n_rows ? rv[k] : -1;
+    if (i < n_tiles * kTileR) rid_lds[i] = (r >= 0 && r < rows_per_req) ? r : -1;
   }
   __shared__ int redo;
   if (threadIdx.x == 0) redo = 0;
-  v16f oacc[DT];
-  float m_used, l_run, m_seen = -INFINITY;
-  bool over = false;
-  // Q and the row ids have landed before the loop, so the compiler has no
-  // load of its own outstanding inside it (it would otherwise wait on every
-  // iteration, which would also drain the tile DMA in flight).
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();  // row ids staged
 
   const uint16_t* kvb = kv + (size_t)b * rows_per_req * row_stride;
@@ -190,6 +183,28 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
     }
   };
 
+  for (int t = 0; t < NBUF - 1 && t < n_tiles; t++) issue_dma(t);
+
+  // B operand of S^T = K Q^T: head n, dims 16 ks + 8 half .. +7 (loaded
+  // unconditionally from a clamped head, then selected)
+  v8bf qB[QK_STEPS];
+  {
+    const uint16_t* qh = q + ((size_t)b * Hq + min(h, Hq - 1)) * DQK + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < QK_STEPS; ks++) {
+      const v8u16 v = *(const v8u16*)(qh + 16 * ks);
+      qB[ks] = __builtin_bit_cast(v8bf, h_ok ? v : v8u16{0, 0, 0, 0, 0, 0, 0, 0});
+    }
+  }
+  v16f oacc[DT];
+  float m_used, l_run, m_seen = -INFINITY;
+  bool over = false;
+  // The query has landed before the loop (with the first tiles, which are
+  // needed at once anyway), so the compiler has no load of its own
+  // outstanding inside it (it would otherwise wait on every iteration, which
+  // would also drain the tile DMA in flight).
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+
   // Per-lane LDS byte offsets; every read below is base + compile-time step.
   // QK A operand: row n, chunk 2 ks + half (parity = half): 1024 B per ks.
   const int qk_off = tile_off(n, half);
@@ -214,7 +229,8 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
 #pragma unroll
   for (int dt = 0; dt < DT; dt++) oacc[dt] = v16f{};
   l_run = 0.f;
-  for (int t = 0; t < NBUF - 1 && t < n_tiles; t++) issue_dma(t);
+  if (pass == 1)  // pass 0's first tiles were issued with the prologue
+    for (int t = 0; t < NBUF - 1 && t < n_tiles; t++) issue_dma(t);
   for (int t = 0; t < n_tiles; t++) {
     // refill the buffer freed at the end of the previous step
     if (t + NBUF - 1 < n_tiles) issue_dma(t + NBUF - 1);
@@ -333,42 +349,46 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
-  if (!h_ok) return;
   const bool any = l_tot > 0.f;
   const float inv = any ? 1.f / l_tot : 0.f;
   const float lse2 = any ? m_used + log2f(l_tot) : -INFINITY;
+  // Output rows go through LDS (the tile ring is free: the loop ended with a
+  // barrier after the last tile): each wave writes its 32 heads' rows as
+  // bf16 into its own region, then stores them whole, 16 bytes per lane, so
+  // every store instruction covers one contiguous 1 KiB row.
   // lane (head n, half): oacc[dt][r] = O[head][32 dt + 8 (r/4) + 4 half + r%4]
-  if (n_splits == 1) {
-    uint16_t* ob = out + ((size_t)b * Hq + h) * DV + 4 * half;
+  constexpr int kRowPitch = DV * 2 + 16;  // bytes; padding spreads the banks
+  static_assert(NW * kHeadsPerWave * kRowPitch <= NBUF * TILE_BYTES, "epilogue staging");
+  uint8_t* stage = &tiles[0][0] + w * (kHeadsPerWave * kRowPitch);
 #pragma unroll
-    for (int dt = 0; dt < DT; dt++)
+  for (int dt = 0; dt < DT; dt++)
 #pragma unroll
-      for (int jj = 0; jj < 4; jj++) {
-        uint2 v;
-        v.x = (uint32_t)f32_to_bf16_rne(oacc[dt][4 * jj] * inv) |
-              ((uint32_t)f32_to_bf16_rne(oacc[dt][4 * jj + 1] * inv) << 16);
-        v.y = (uint32_t)f32_to_bf16_rne(oacc[dt][4 * jj + 2] * inv) |
-              ((uint32_t)f32_to_bf16_rne(oacc[dt][4 * jj + 3] * inv) << 16);
-        *(uint2*)(ob + 32 * dt + 8 * jj) = v;
-      }
-    if (half == 0) lse[(size_t)b * Hq + h] = any ? lse2 * kLn2 : -INFINITY;
-  } else {
-    // per-split output, normalised by its own sum, stored as bf16 (the merge
-    // weights and the split's log-sum-exp stay fp32)
-    const size_t ps = ((size_t)b * Hq + h) * n_splits + split;
-    uint16_t* po = part_o + ps * DV + 4 * half;
-#pragma unroll
-    for (int dt = 0; dt < DT; dt++)
-#pragma unroll
-      for (int jj = 0; jj < 4; jj++) {
-        uint2 v;
-        v.x = (uint32_t)f32_to_bf16_rne(oacc[dt][4 * jj] * inv) |
-              ((uint32_t)f32_to_bf16_rne(oacc[dt][4 * jj + 1] * inv) << 16);
-        v.y = (uint32_t)f32_to_bf16_rne(oacc[dt][4 * jj + 2] * inv) |
-              ((uint32_t)f32_to_bf16_rne(oacc[dt][4 * jj + 3] * inv) << 16);
-        *(uint2*)(po + 32 * dt + 8 * jj) = v;
-      }
-    if (half == 0) part_lse[ps] = lse2;
+    for (int jj = 0; jj < 4; jj++) {
+      uint2 v;
+      v.x = (uint32_t)f32_to_bf16_rne(oacc[dt][4 * jj] * inv) |
+            ((uint32_t)f32_to_bf16_rne(oacc[dt][4 * jj + 1] * inv) << 16);
+      v.y = (uint32_t)f32_to_bf16_rne(oacc[dt][4 * jj + 2] * inv) |
+            ((uint32_t)f32_to_bf16_rne(oacc[dt][4 * jj + 3] * inv) << 16);
+      *(uint2*)(stage + n * kRowPitch + 2 * (32 * dt + 8 * jj + 4 * half)) = v;
+    }
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this wave's rows are staged
+  static_assert(DV * 2 == 64 * 16, "one 16-byte piece per lane per row");
+  const int h0 = blockIdx.y * (kHeadsPerWave * NW) + w * kHeadsPerWave;
+#pragma unroll 4
+  for (int hr = 0; hr < kHeadsPerWave; hr++) {
+    const int head = h0 + hr;
+    if (head >= Hq) break;  // wave-uniform
+    const uint4 piece = *(const uint4*)(stage + hr * kRowPitch + 16 * l);
+    uint16_t* dst = (n_splits == 1)
+                        ? out + ((size_t)b * Hq + head) * DV
+                        : part_o + (((size_t)b * Hq + head) * n_splits + split) * DV;
+    *(uint4*)((uint8_t*)dst + 16 * l) = piece;
+  }
+  if (h_ok && half == 0) {
+    if (n_splits == 1)
+      lse[(size_t)b * Hq + h] = any ? lse2 * kLn2 : -INFINITY;
+    else
+      part_lse[((size_t)b * Hq + h) * n_splits + split] = lse2;
   }
 }
 
