@@ -260,6 +260,21 @@ def test_attention_mla_parity(ls, Hq, n_splits):
     assert_attention_close(out, lse, e_out, e_lse, "mla Hq=%d splits=%d" % (Hq, n_splits))
 
 
+@pytest.mark.parametrize("n_splits", [9, 11, 16])
+def test_attention_mla_parity_many_splits(ls, n_splits):
+    # more splits than the combine loads at once (8), a partial last group,
+    # a request with no rows at all and one whose rows fill only the first
+    # split (the others end with no rows and lse = -inf)
+    B, K, S = 3, 512, 300
+    q, kv, rows = mla_case(B, 128, [512, 0, 20], K, S, seed=100 + n_splits)
+    scale = 1 / math.sqrt(192)
+    kvd = kv.to(DEV)
+    out, lse = ls.sparse_attn_decode(q.to(DEV), kvd, kvd, rows.to(DEV), scale, 1, 512, S + K,
+                                     576, n_splits=n_splits)
+    e_out, e_lse = oracle_mla(q, kv, rows, scale)
+    assert_attention_close(out, lse, e_out, e_lse, "mla splits=%d" % n_splits)
+
+
 def test_attention_mla_all_rows_equal_dense(ls):
     # k >= context: sparse attention over every row equals dense attention
     B, Hq, L = 2, 32, 200

@@ -126,10 +126,15 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
   __shared__ __attribute__((aligned(1024))) uint8_t tiles[NBUF][TILE_BYTES];
   __shared__ int32_t rid_lds[kMaxSplitRows + kTileR];
 
-  const int split = blockIdx.x, b = blockIdx.z;
+  // (split, head group, request), numbered so that one request's workgroups
+  // run on one XCD and share its query and row ids in that L2
+  const int lin = xcd_major(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
+                            gridDim.x * gridDim.y * gridDim.z);
+  const int split = lin % gridDim.x, hg = (lin / gridDim.x) % gridDim.y;
+  const int b = lin / (gridDim.x * gridDim.y);
   const int l = lane_id(), w = wave_id();
   const int n = l & 31, half = l >> 5;
-  const int h = blockIdx.y * (kHeadsPerWave * NW) + w * kHeadsPerWave + n;
+  const int h = hg * (kHeadsPerWave * NW) + w * kHeadsPerWave + n;
   const bool h_ok = h < Hq;
 
   const int i_begin = split * rows_per_split;
@@ -286,7 +291,11 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
     }
 #pragma unroll
     for (int r = 0; r < 16; r++) tmax = fmaxf(tmax, sv[r]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    {
+      float lo, hi;  // the head's two 16-row halves (lanes n and n + 32)
+      pair32(tmax, lo, hi);
+      tmax = fmaxf(lo, hi);
+    }
     m_seen = fmaxf(m_seen, tmax);
     if (m_used == -INFINITY) m_used = tmax;         // first valid tile of this head
     else over = over || (tmax > m_used + kBaseSlack);  // never in pass 1
@@ -348,7 +357,9 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
   }
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+  float l_lo, l_hi;
+  pair32(l_run, l_lo, l_hi);
+  const float l_tot = l_lo + l_hi;
   const bool any = l_tot > 0.f;
   const float inv = any ? 1.f / l_tot : 0.f;
   const float lse2 = any ? m_used + log2f(l_tot) : -INFINITY;
@@ -373,7 +384,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
     }
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this wave's rows are staged
   static_assert(DV * 2 == 64 * 16, "one 16-byte piece per lane per row");
-  const int h0 = blockIdx.y * (kHeadsPerWave * NW) + w * kHeadsPerWave;
+  const int h0 = hg * (kHeadsPerWave * NW) + w * kHeadsPerWave;
 #pragma unroll 4
   for (int hr = 0; hr < kHeadsPerWave; hr++) {
     const int head = h0 + hr;
@@ -490,42 +501,60 @@ __global__ __launch_bounds__(256) void k_attn_valu(
 
 // ------------------------------------------------------------------ combine --
 // out = sum_j o_j 2^(lse_j - L) with L = log2 sum_j 2^lse_j; lse = L ln 2.
-__global__ __launch_bounds__(128) void k_combine(const uint16_t* __restrict__ part_o,
+// One wave per (request, head), four per workgroup, numbered like the
+// attention grid so that a request's partials are read on the XCD that wrote
+// them.  Each lane combines 8 consecutive dims: the 16-byte pieces of eight
+// splits are loaded before any is used.  DV is a multiple of 8.
+__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ part_o,
                                                  const float* __restrict__ part_lse,
                                                  uint16_t* __restrict__ out,
-                                                 float* __restrict__ lse, int DV,
+                                                 float* __restrict__ lse, int BH, int DV,
                                                  int n_splits) {
-  const size_t bh = blockIdx.x;
-  const float* pl = part_lse + bh * n_splits;
+  const int bh = xcd_major(blockIdx.x, gridDim.x) * 4 + wave_id();
+  if (bh >= BH) return;
+  const int l = lane_id();
+  const float* pl = part_lse + (size_t)bh * n_splits;
   float M = -INFINITY;
   for (int j = 0; j < n_splits; j++) M = fmaxf(M, pl[j]);
-  uint16_t* ob = out + bh * DV;
+  uint16_t* ob = out + (size_t)bh * DV;
   if (M == -INFINITY) {
-    for (int d = threadIdx.x; d < DV; d += 128) ob[d] = 0;
-    if (threadIdx.x == 0) lse[bh] = -INFINITY;
+    for (int d = 8 * l; d < DV; d += 8 * kWave) *(uint4*)(ob + d) = uint4{0, 0, 0, 0};
+    if (l == 0) lse[bh] = -INFINITY;
     return;
   }
   float W = 0.f;
   for (int j = 0; j < n_splits; j++) W += exp2f(pl[j] - M);
   const float L = M + log2f(W);
-  const uint16_t* po = part_o + bh * n_splits * DV;
-  for (int d = threadIdx.x * 4; d < DV; d += 128 * 4) {
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    for (int j = 0; j < n_splits; j++) {
-      const float wj = exp2f(pl[j] - L);
-      if (wj == 0.f) continue;
-      const uint2 v = *(const uint2*)(po + (size_t)j * DV + d);
-      a0 += wj * bf16_to_f32((uint16_t)(v.x & 0xFFFF));
-      a1 += wj * bf16_to_f32((uint16_t)(v.x >> 16));
-      a2 += wj * bf16_to_f32((uint16_t)(v.y & 0xFFFF));
-      a3 += wj * bf16_to_f32((uint16_t)(v.y >> 16));
+  const uint16_t* po = part_o + (size_t)bh * n_splits * DV;
+  for (int d = 8 * l; d < DV; d += 8 * kWave) {
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < n_splits; j0 += 8) {
+      uint4 v[8];
+      float wj[8];
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        const int j = min(j0 + u, n_splits - 1);
+        v[u] = *(const uint4*)(po + (size_t)j * DV + d);
+        wj[u] = j0 + u < n_splits ? exp2f(pl[j] - L) : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        const uint32_t x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          a[2 * e] += wj[u] * __uint_as_float(x[e] << 16);
+          a[2 * e + 1] += wj[u] * __uint_as_float(x[e] & 0xFFFF0000u);
+        }
+      }
     }
-    uint2 pk;
-    pk.x = (uint32_t)f32_to_bf16_rne(a0) | ((uint32_t)f32_to_bf16_rne(a1) << 16);
-    pk.y = (uint32_t)f32_to_bf16_rne(a2) | ((uint32_t)f32_to_bf16_rne(a3) << 16);
-    *(uint2*)(ob + d) = pk;
+    uint4 pk;
+    pk.x = (uint32_t)f32_to_bf16_rne(a[0]) | ((uint32_t)f32_to_bf16_rne(a[1]) << 16);
+    pk.y = (uint32_t)f32_to_bf16_rne(a[2]) | ((uint32_t)f32_to_bf16_rne(a[3]) << 16);
+    pk.z = (uint32_t)f32_to_bf16_rne(a[4]) | ((uint32_t)f32_to_bf16_rne(a[5]) << 16);
+    pk.w = (uint32_t)f32_to_bf16_rne(a[6]) | ((uint32_t)f32_to_bf16_rne(a[7]) << 16);
+    *(uint4*)(ob + d) = pk;
   }
-  if (threadIdx.x == 0) lse[bh] = L * kLn2;
+  if (l == 0) lse[bh] = L * kLn2;
 }
 
 // ---------------------------------------------------------------- launchers --
@@ -567,8 +596,10 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_combine(const AttnArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_combine, dim3(a.B * a.Hq), dim3(128), 0, st, a.part_o, a.part_lse, a.out,
-                     a.lse, a.v_dim, a.n_splits);
+  if (a.v_dim % 8 != 0) return hipErrorInvalidValue;
+  const int BH = a.B * a.Hq;
+  hipLaunchKernelGGL(k_combine, dim3((BH + 3) / 4), dim3(256), 0, st, a.part_o, a.part_lse, a.out,
+                     a.lse, BH, a.v_dim, a.n_splits);
   return hipGetLastError();
 }
 

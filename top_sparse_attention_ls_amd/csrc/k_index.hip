@@ -121,22 +121,6 @@ __device__ __forceinline__ void coarse_q_operands(const int8_t* qh, int g, v4i* 
   }
 }
 
-// Reduce-scatter over the four 16-lane groups: on entry p[tt] is this lane's
-// partial for token (tile tt, n); on exit the result is the full sum for
-// tile g = lane/16, token n.
-template <class T>
-__device__ __forceinline__ T reduce_scatter4(T p0, T p1, T p2, T p3, int g) {
-  const bool lo = g < 2;
-  T s0 = lo ? p2 : p0, s1 = lo ? p3 : p1;
-  T r0 = __shfl_xor(s0, 32, kWave), r1 = __shfl_xor(s1, 32, kWave);
-  T k0 = (lo ? p0 : p2) + r0;
-  T k1 = (lo ? p1 : p3) + r1;
-  const bool even = (g & 1) == 0;
-  T s = even ? k1 : k0;
-  T r = __shfl_xor(s, 16, kWave);
-  return (even ? k0 : k1) + r;
-}
-
 // 24-bit signed multiply-add, c + a * b modulo 2^32 (one v_mad_i32_i24; the
 // compiler would otherwise split the chain into multiplies and 3-way adds).
 __device__ __forceinline__ uint32_t mad_i24(int32_t a, int32_t b, uint32_t c) {
@@ -283,7 +267,7 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
       }
     }
     const int32_t score = (int32_t)reduce_scatter4((uint32_t)part[0], (uint32_t)part[1],
-                                                   (uint32_t)part[2], (uint32_t)part[3], g);
+                                                   (uint32_t)part[2], (uint32_t)part[3]);
     const int t = base + l;
     if (t < t_end) {
       sb[t] = score;

@@ -129,15 +129,12 @@ __global__ __launch_bounds__(256) void k_prefill_scores(
         part[r][tt] = s;
       }
     }
-    const bool lo = g < 2, even = (g & 1) == 0;
     const int t = base + l;
 #pragma unroll
     for (int r = 0; r < QR; r++) {
       // reduce-scatter over the four lane groups: lane (n, g) ends with tile g
-      const int64_t s0 = lo ? part[r][2] : part[r][0], s1 = lo ? part[r][3] : part[r][1];
-      const int64_t k0 = (lo ? part[r][0] : part[r][2]) + __shfl_xor(s0, 32, kWave);
-      const int64_t k1 = (lo ? part[r][1] : part[r][3]) + __shfl_xor(s1, 32, kWave);
-      const int64_t score = (even ? k0 : k1) + __shfl_xor(even ? k1 : k0, 16, kWave);
+      const int64_t score = (int64_t)reduce_scatter4((uint64_t)part[r][0], (uint64_t)part[r][1],
+                                                     (uint64_t)part[r][2], (uint64_t)part[r][3]);
       if (t < nv[r]) {
         scores[(size_t)(r0 + r) * max_ctx + t] = score;
         atomicAdd(&lhist[r][wide_bucket(score)], 1u);

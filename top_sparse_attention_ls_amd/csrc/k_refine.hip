@@ -113,14 +113,8 @@ __global__ __launch_bounds__(256) void k_refine(const int8_t* __restrict__ q,
     part[tt] = sum;
   }
   // reduce-scatter over the four lane groups: lane (n, g) ends with tile g
-  const bool lo = g < 2;
-  int64_t s0 = lo ? part[2] : part[0], s1 = lo ? part[3] : part[1];
-  int64_t r0 = __shfl_xor(s0, 32, kWave), r1 = __shfl_xor(s1, 32, kWave);
-  int64_t k0 = (lo ? part[0] : part[2]) + r0, k1 = (lo ? part[1] : part[3]) + r1;
-  const bool even = (g & 1) == 0;
-  int64_t sx = even ? k1 : k0;
-  int64_t rx = __shfl_xor(sx, 16, kWave);
-  const int64_t score = (even ? k0 : k1) + rx;
+  const int64_t score = (int64_t)reduce_scatter4((uint64_t)part[0], (uint64_t)part[1],
+                                                 (uint64_t)part[2], (uint64_t)part[3]);
   if (c_out < C) {
     fs[(size_t)b * C + c_out] = (p_out >= 0) ? score : 0;
     // the candidate's hot slot, looked up here where the lookups spread over

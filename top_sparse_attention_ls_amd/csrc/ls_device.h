@@ -17,6 +17,15 @@ typedef unsigned short v8u16 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
 
+// Workgroups are dispatched to the eight XCDs in turn (id mod 8), and each
+// XCD has its own L2.  xcd_major renumbers a grid of n workgroups so that
+// consecutive new ids run on one XCD: workgroups that share data (the splits
+// of one request, say) then share that XCD's L2.  A bijection on [0, n).
+__device__ __forceinline__ int xcd_major(int id, int n) {
+  const int x = id & 7, j = id >> 3, per = n >> 3, rem = n & 7;
+  return x < rem ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j;
+}
+
 // Lanes below this one whose bit is set in mask (the wave's own rank).
 __device__ __forceinline__ uint32_t lane_rank(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
@@ -56,6 +65,58 @@ __device__ __forceinline__ uint32_t wave_incl_suffix(uint32_t v) {
     if (lane_id() + o < kWave) v += t;
   }
   return v;
+}
+
+// Lane swaps of gfx950 (VALU, no LDS round trip).  permlane32_swap(X, Y)
+// exchanges the upper 32 lanes of X with the lower 32 lanes of Y;
+// permlane16_swap(X, Y) exchanges the odd 16-lane rows of X with the even
+// rows of Y.  The 64-bit forms move each 32-bit word the same way.
+__device__ __forceinline__ void swap32(uint32_t& x, uint32_t& y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+  x = r[0];
+  y = r[1];
+}
+__device__ __forceinline__ void swap16(uint32_t& x, uint32_t& y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+  x = r[0];
+  y = r[1];
+}
+__device__ __forceinline__ void swap32(uint64_t& x, uint64_t& y) {
+  uint32_t xl = (uint32_t)x, xh = (uint32_t)(x >> 32), yl = (uint32_t)y, yh = (uint32_t)(y >> 32);
+  swap32(xl, yl);
+  swap32(xh, yh);
+  x = ((uint64_t)xh << 32) | xl;
+  y = ((uint64_t)yh << 32) | yl;
+}
+__device__ __forceinline__ void swap16(uint64_t& x, uint64_t& y) {
+  uint32_t xl = (uint32_t)x, xh = (uint32_t)(x >> 32), yl = (uint32_t)y, yh = (uint32_t)(y >> 32);
+  swap16(xl, yl);
+  swap16(xh, yh);
+  x = ((uint64_t)xh << 32) | xl;
+  y = ((uint64_t)yh << 32) | yl;
+}
+
+// Reduce-scatter over the four 16-lane groups g = lane/16 (sums modulo
+// 2^bits of U): on entry p_tt is this lane's partial for (tile tt, lane%16);
+// on exit the result is the full sum for tile g, lane%16.  Swapping (p0, p2)
+// leaves every lane with the partials of lanes l and l^32 for tile 0 (lanes
+// < 32) or tile 2 (lanes >= 32), and (p1, p3) likewise for tiles 1 / 3; the
+// 16-lane swap of those sums then pairs groups g and g^1.
+template <class U>
+__device__ __forceinline__ U reduce_scatter4(U p0, U p1, U p2, U p3) {
+  swap32(p0, p2);
+  swap32(p1, p3);
+  U k0 = p0 + p2, k1 = p1 + p3;
+  swap16(k0, k1);
+  return k0 + k1;
+}
+
+// x of lanes l and l^32: the pair (lower lane's, upper lane's) in every lane.
+__device__ __forceinline__ void pair32(float x, float& lo, float& hi) {
+  uint32_t a = __float_as_uint(x), b = a;
+  swap32(a, b);
+  lo = __uint_as_float(a);
+  hi = __uint_as_float(b);
 }
 
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
