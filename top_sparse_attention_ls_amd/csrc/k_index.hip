@@ -149,6 +149,7 @@ __device__ __forceinline__ void coarse_load4(const uint8_t* kb, int base, int n,
 }
 
 constexpr int kCoarseTileGroup = 2;
+constexpr int kCoarseDepth = 2;
 
 template <int D, int HT>
 __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
@@ -190,17 +191,17 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
   int32_t wv[HT][4];
 #pragma unroll
   for (int mt = 0; mt < HT; mt++) {
+    // unconditional loads from clamped heads, then selected: a load under a
+    // divergent condition is a branch that waits for it
     const int h = 16 * mt + n;
-    if (h < H) {
-      coarse_q_operands<D>(qb + (size_t)h * D, g, qa[mt]);
-    } else {
+    coarse_q_operands<D>(qb + (size_t)min(h, H - 1) * D, g, qa[mt]);
 #pragma unroll
-      for (int mf = 0; mf < NMF; mf++) qa[mt][mf] = v4i{0, 0, 0, 0};
-    }
+    for (int mf = 0; mf < NMF; mf++) qa[mt][mf] = h < H ? qa[mt][mf] : v4i{0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int hh = 16 * mt + 4 * g + i;
-      wv[mt][i] = hh < H ? (int32_t)w[(size_t)b * H + hh] : 0;
+      const int32_t wr = (int32_t)w[(size_t)b * H + min(hh, H - 1)];
+      wv[mt][i] = hh < H ? wr : 0;
     }
   }
   __syncthreads();
@@ -216,7 +217,9 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
     }
 
   const uint8_t* kb = kc + (size_t)b * max_ctx * KB + g * LB;  // + 32-bit token offsets
-  int32_t* sb = scores + (size_t)b * max_ctx;
+  // this workgroup's score range as a buffer: lanes past t_end store nothing
+  const __amdgpu_buffer_rsrc_t sres =
+      buffer_rsrc(scores + (size_t)b * max_ctx + t_begin, 4u * (uint32_t)(t_end - t_begin));
   const int t_last = t_end - 1;
 
   // One 64-token step: all MFMAs first (independent accumulators), then the
@@ -269,28 +272,37 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
     const int32_t score = (int32_t)reduce_scatter4((uint32_t)part[0], (uint32_t)part[1],
                                                    (uint32_t)part[2], (uint32_t)part[3]);
     const int t = base + l;
-    if (t < t_end) {
-      sb[t] = score;
-      atomicAdd(&lhist[coarse_bucket(score)], 1u);
-    }
+    // no branch: the buffer drops stores past t_end, and those lanes add 0
+    __builtin_amdgcn_raw_buffer_store_b32(score, sres, 4 * (t - t_begin), 0, 0);
+    atomicAdd(&lhist[coarse_bucket(score)], t < t_end ? 1u : 0u);
   };
 
-  // Ping-pong register buffers: the loads of step i+1 are in flight while
-  // step i computes (a third buffer measured slower).  Past the end every
-  // lane loads row t_last (one line).
+  // A ring of kCoarseDepth register buffers: the loads of the next
+  // kCoarseDepth - 1 steps are in flight while a step computes (two buffers
+  // measured fastest; deeper rings cost more in register moves at the loop
+  // edge than they gain).  The scheduling fences keep each
+  // step's refill ahead of its compute (the scheduler would otherwise sink
+  // it below the wait for the current buffer).  Past the end every lane
+  // loads row t_last (one line).
+  constexpr int S = 256;  // tokens per workgroup step (4 waves x 64)
   int base = __builtin_amdgcn_readfirstlane(t_begin + wave_id() * 64);
   if (base < t_end) {
-    v4i bufA[4], bufB[4];
-    coarse_load4<D>(kb, base, n, t_last, bufA);
-    while (true) {
-      coarse_load4<D>(kb, base + 256, n, t_last, bufB);
-      process(base, bufA);
-      base += 256;
-      if (base >= t_end) break;
-      coarse_load4<D>(kb, base + 256, n, t_last, bufA);
-      process(base, bufB);
-      base += 256;
-      if (base >= t_end) break;
+    v4i buf[kCoarseDepth][4];
+#pragma unroll
+    for (int k = 0; k < kCoarseDepth - 1; k++) coarse_load4<D>(kb, base + k * S, n, t_last, buf[k]);
+    bool more = true;
+    while (more) {
+#pragma unroll
+      for (int k = 0; k < kCoarseDepth; k++) {
+        if (more) {
+          coarse_load4<D>(kb, base + (kCoarseDepth - 1) * S, n, t_last,
+                          buf[(k + kCoarseDepth - 1) % kCoarseDepth]);
+          __builtin_amdgcn_sched_barrier(0);
+          process(base, buf[k]);
+          base += S;
+          more = base < t_end;
+        }
+      }
     }
   }
   __syncthreads();

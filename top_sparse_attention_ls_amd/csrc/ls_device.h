@@ -181,6 +181,13 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 }
 
 // Valid token count of request b, clamped to [0, max_ctx].
+// Raw buffer resource over [p, p + bytes) (stride 0, gfx9 dword-3 format
+// word): the hardware range check drops stores at offsets beyond `bytes` and
+// returns 0 for such loads, so edge lanes need no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+
 __device__ __forceinline__ int clamp_ctx(const int32_t* ctx_len, int b, int max_ctx) {
   int n = ctx_len[b];
   return n < 0 ? 0 : (n > max_ctx ? max_ctx : n);
