@@ -68,7 +68,6 @@ constexpr float kBaseSlack = 64.f;  // log2 units a score may exceed its head's 
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ v4i16 lds_read_tr16(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -141,9 +140,9 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
   const int i_end = min(i_begin + rows_per_split, K);
   const int n_rows = max(i_end - i_begin, 0);
   const int n_tiles = (n_rows + kTileR - 1) / kTileR;
-  // Prologue, ordered so that the latencies overlap: the split's row ids
-  // (loaded unconditionally, clamped into the request's list), staged in
-  // LDS; the first tiles' DMA as soon as they are; the query meanwhile.
+  // Prologue: the split's row ids (loaded unconditionally, clamped into the
+  // request's list) and the query in one round trip; the row ids staged in
+  // LDS; the first tiles' DMA, which the loop waits for tile by tile.
   const int32_t* rq = rows + (size_t)b * K;
   constexpr int kRidIters = (kMaxSplitRows + kTileR + NW * 64 - 1) / (NW * 64);
   int32_t rv[kRidIters];
@@ -152,6 +151,22 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
     const int i = threadIdx.x + k * NW * 64;
     rv[k] = rq[min(i_begin + min(i, max(n_rows - 1, 0)), K - 1)];
   }
+  // B operand of S^T = K Q^T: head n, dims 16 ks + 8 half .. +7 (loaded
+  // unconditionally from a clamped head, then selected)
+  v8bf qB[QK_STEPS];
+  {
+    const uint16_t* qh = q + ((size_t)b * Hq + min(h, Hq - 1)) * DQK + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < QK_STEPS; ks++) {
+      const v8u16 v = *(const v8u16*)(qh + 16 * ks);
+      qB[ks] = __builtin_bit_cast(v8bf, h_ok ? v : v8u16{0, 0, 0, 0, 0, 0, 0, 0});
+    }
+  }
+  // Row ids and query have landed before anything else is issued, so the
+  // compiler has no load of its own outstanding in the tile loop (it would
+  // otherwise wait on every iteration, which would also drain the tile DMA
+  // in flight); the loop then waits for each tile's DMA alone.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 #pragma unroll
   for (int k = 0; k < kRidIters; k++) {
     const int i = threadIdx.x + k * NW * 64;
@@ -167,48 +182,22 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
   // the tile row this lane loads in every DMA instruction, and its chunk parity
   const int dma_row = (l & 31) ^ (half << 3);
 
-  // Tile DMA: wave w issues instructions k = w, w + NW, ...  The instruction
-  // is written out (M0 = LDS destination) so that the compiler does not
-  // order LDS reads of other buffers behind it; the waits on it are the
-  // explicit vmcnt waits below.  It has no VGPR destination, so nothing it
-  // writes can be reused while it is in flight.
+  // Tile DMA: wave w issues instructions k = w, w + NW, ... (lds_dma16: the
+  // waits on it are the explicit vmcnt waits below)
   auto issue_dma = [&](int t) {
     const int32_t rid = rid_lds[t * kTileR + dma_row];
     const uint8_t* src = (const uint8_t*)(kvb + (size_t)(rid >= 0 ? rid : 0) * row_stride) +
                          16 * (2 * w + half);
-    const uint32_t dst =
-        (uint32_t)(uintptr_t)(lds_void*)(&tiles[t % NBUF][0]) + 1024u * w;
+    const uint32_t dst = lds_addr(&tiles[t % NBUF][0]) + 1024u * w;
 #pragma unroll
-    for (int j = 0; j < DMA_PER_WAVE; j++) {
-      const uint32_t m0 = __builtin_amdgcn_readfirstlane(dst + 1024u * NW * j);
-      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                   :
-                   : "v"(src + 32 * NW * j), "s"(m0)
-                   : "memory", "m0");
-    }
+    for (int j = 0; j < DMA_PER_WAVE; j++) lds_dma16(src + 32 * NW * j, dst + 1024u * NW * j);
   };
 
   for (int t = 0; t < NBUF - 1 && t < n_tiles; t++) issue_dma(t);
 
-  // B operand of S^T = K Q^T: head n, dims 16 ks + 8 half .. +7 (loaded
-  // unconditionally from a clamped head, then selected)
-  v8bf qB[QK_STEPS];
-  {
-    const uint16_t* qh = q + ((size_t)b * Hq + min(h, Hq - 1)) * DQK + 8 * half;
-#pragma unroll
-    for (int ks = 0; ks < QK_STEPS; ks++) {
-      const v8u16 v = *(const v8u16*)(qh + 16 * ks);
-      qB[ks] = __builtin_bit_cast(v8bf, h_ok ? v : v8u16{0, 0, 0, 0, 0, 0, 0, 0});
-    }
-  }
   v16f oacc[DT];
   float m_used, l_run, m_seen = -INFINITY;
   bool over = false;
-  // The query has landed before the loop (with the first tiles, which are
-  // needed at once anyway), so the compiler has no load of its own
-  // outstanding inside it (it would otherwise wait on every iteration, which
-  // would also drain the tile DMA in flight).
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
   // Per-lane LDS byte offsets; every read below is base + compile-time step.
   // QK A operand: row n, chunk 2 ks + half (parity = half): 1024 B per ks.

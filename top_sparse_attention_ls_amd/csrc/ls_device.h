@@ -181,6 +181,26 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 }
 
 // Valid token count of request b, clamped to [0, max_ctx].
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void*)p;
+}
+
+// One 1 KiB global -> LDS copy (global_load_lds_dwordx4): lane i's 16 bytes
+// at src land at LDS byte lds_base + 16 i (lds_base wave-uniform).  Written
+// out so that the compiler neither reorders LDS accesses across it nor
+// counts it: the caller waits for it with an explicit vmcnt.  It has no VGPR
+// destination, so nothing it writes can be reused while it is in flight.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(m0)
+               : "memory", "m0");
+}
+
 // Raw buffer resource over [p, p + bytes) (stride 0, gfx9 dword-3 format
 // word): the hardware range check drops stores at offsets beyond `bytes` and
 // returns 0 for such loads, so edge lanes need no branch.
