@@ -14,7 +14,8 @@ namespace ls {
 // ------------------------------------------------- candidate select (A2) ----
 //
 // Keeps the C best tokens under (score desc, position asc), in two kernels
-// with the kernel boundary as the only cross-workgroup synchronisation.
+// that meet only at the kernel boundary (the emit workgroups also count
+// their arrivals, but only so that the last one clears the tie counter).
 //
 // k_topc_filter (16384 positions per 512-thread workgroup): every lane first
 // issues its loads -- the request's histogram share, then all 32 of its
@@ -26,21 +27,19 @@ namespace ls {
 // bucket beta are appended to the wave's own LDS tie list (ranks from the
 // ballot, so no atomics in the loop) and the workgroup reserves room in the
 // request's global list with one atomic.  Workgroup 0 also stores beta and
-// the count above it for the emit kernel.
+// the count above it, and every workgroup its chunk's count of positions
+// kept outright, for the emit kernel.
 //
-// k_topc_emit (one 1024-thread workgroup per request): copies the bitmap to
-// LDS, resolves the tie list exactly (one wave runs the radix threshold
-// search when the list fits in LDS, the whole workgroup otherwise), sets the
-// winners' bits with LDS atomics, and emits the kept positions in ascending
-// order, every thread owning a contiguous run of bitmap words.  It leaves
-// the histogram and the tie counter cleared for the next call.  Contexts
-// whose bitmap does not fit in LDS use the same steps on the global bitmap.
+// k_topc_emit (one workgroup per filter chunk): resolves the tie list
+// exactly and emits its chunk's kept positions at their place in the
+// request's ascending list (details at the kernel).
 
 constexpr int kFilterThreads = 512;
 constexpr int kFilterIters = 32;
 constexpr int kFilterChunk = kFilterThreads * kFilterIters;  // 16384 positions
 constexpr int kFilterWaveTies = 512;
-// ctr words of a request: tie count, beta, count above beta
+// ctr words of a request: tie count, beta, count above beta (word 3: emit
+// workgroups done, kCtrDone below)
 constexpr int kCtrTies = 0, kCtrBeta = 1, kCtrAbove = 2;
 
 template <class S>
@@ -48,7 +47,7 @@ __global__ __launch_bounds__(kFilterThreads) void k_topc_filter(
     const int32_t* __restrict__ ctx_len, const typename S::T* __restrict__ scores,
     const uint32_t* __restrict__ hist, uint32_t* __restrict__ bitmap,
     typename S::T* __restrict__ tie_s, int32_t* __restrict__ tie_p, uint32_t* __restrict__ ctr,
-    int max_ctx, int C, int bitmap_words) {
+    uint32_t* __restrict__ chunk, int max_ctx, int C, int bitmap_words) {
   using T = typename S::T;
   constexpr int NW = kFilterThreads / kWave;
   constexpr int kPer = (S::kBins + kFilterThreads - 1) / kFilterThreads;
@@ -56,6 +55,7 @@ __global__ __launch_bounds__(kFilterThreads) void k_topc_filter(
   __shared__ int sh_beta;
   __shared__ uint32_t sh_above;
   __shared__ uint32_t wave_n[NW];
+  __shared__ uint32_t wave_k[NW];
   __shared__ uint32_t g_base;
   __shared__ T loc_s[NW][kFilterWaveTies];
   __shared__ int32_t loc_p[NW][kFilterWaveTies];
@@ -116,6 +116,7 @@ __global__ __launch_bounds__(kFilterThreads) void k_topc_filter(
   uint32_t* bm = bitmap + (size_t)b * bitmap_words;
   const size_t tb = (size_t)b * max_ctx;
   uint32_t wn = 0;  // this wave's ties so far (wave-uniform)
+  uint32_t wk = 0;  // this wave's kept positions (wave-uniform)
 #pragma unroll
   for (int u = 0; u < kFilterIters; u++) {
     const int base = c0 + (u * NW + wv) * kWave;
@@ -139,14 +140,22 @@ __global__ __launch_bounds__(kFilterThreads) void k_topc_filter(
       }
     }
     wn += (uint32_t)__popcll(mt);
+    wk += (uint32_t)__popcll(mk);
   }
-  if (l == 0) wave_n[wv] = min(wn, (uint32_t)kFilterWaveTies);
+  if (l == 0) {
+    wave_n[wv] = min(wn, (uint32_t)kFilterWaveTies);
+    wave_k[wv] = wk;
+  }
   __syncthreads();
   if (tid == 0) {
-    uint32_t n = 0;
+    uint32_t n = 0, k = 0;
 #pragma unroll
-    for (int w = 0; w < NW; w++) n += wave_n[w];
+    for (int w = 0; w < NW; w++) {
+      n += wave_n[w];
+      k += wave_k[w];
+    }
     g_base = n ? atomicAdd(&cr[kCtrTies], n) : 0u;  // one reservation per workgroup
+    chunk[(size_t)b * gridDim.x + blockIdx.x] = k;  // positions kept outright in this chunk
   }
   __syncthreads();
   uint32_t off = g_base;
@@ -158,13 +167,15 @@ __global__ __launch_bounds__(kFilterThreads) void k_topc_filter(
   }
 }
 
-constexpr int kEmitThreads = 1024;
+constexpr int kEmitThreads = 512;
+constexpr int kCtrDone = 3;  // ctr word: emit workgroups of the request done
+static_assert(kFilterChunk / 32 == kSelectChunkWords && kSelectChunkWords == kEmitThreads,
+              "one filter and one emit workgroup per chunk, one bitmap word per emit thread");
 
-// LDS budget of the emit kernel per score kind: the bitmap (when it fits)
-// and the tie list as (order-preserving key, position) entries.
+// LDS budget of the emit kernel per score kind: the tie list as
+// (order-preserving key, position) entries.
 template <class S> struct EmitCfg;
 template <> struct EmitCfg<NarrowScore> {
-  static constexpr int kMaxWords = 32768;  // bitmap in LDS up to 2^20 positions
   static constexpr int kTies = 3072;
   using E = uint2;
   static __device__ __forceinline__ E pack(int32_t s, int32_t p) {
@@ -175,7 +186,6 @@ template <> struct EmitCfg<NarrowScore> {
   static __device__ __forceinline__ uint64_t key_of(int32_t s) { return key_of_i32(s); }
 };
 template <> struct EmitCfg<WideScore> {
-  static constexpr int kMaxWords = 8192;  // bitmap in LDS up to 2^18 positions
   static constexpr int kTies = 4096;
   using E = uint4;
   static __device__ __forceinline__ E pack(int64_t s, int32_t p) {
@@ -189,46 +199,62 @@ template <> struct EmitCfg<WideScore> {
   static __device__ __forceinline__ uint64_t key_of(int64_t s) { return key_of_i64(s); }
 };
 
-template <class S, bool LDS_BM>
+// k_topc_emit: one 512-thread workgroup per (request, chunk of 16384
+// positions), so a request's emission spreads over as many workgroups as its
+// filter.  Every workgroup resolves the request's tie list itself (one wave
+// runs the radix threshold search when the list fits in LDS, the whole
+// workgroup otherwise): the list is short, and repeating the search costs
+// less than another kernel boundary.  Its output offset is the kept count of
+// the chunks before it (written by the filter) plus the winning ties before
+// it; it sets its winners' bits in its LDS copy of the chunk's 512 bitmap
+// words and emits the kept positions in ascending order, one word per
+// thread.  Chunk 0 pads the list with -1.  Each workgroup clears its share of
+// the request's histogram; the last one to finish clears the tie counter.
+template <class S>
 __global__ __launch_bounds__(kEmitThreads) void k_topc_emit(
     const int32_t* __restrict__ ctx_len, uint32_t* __restrict__ hist,
-    uint32_t* __restrict__ bitmap, const typename S::T* __restrict__ tie_s,
-    const int32_t* __restrict__ tie_p, uint32_t* __restrict__ ctr, int32_t* __restrict__ cand,
-    int max_ctx, int C, int bitmap_words) {
-  using T = typename S::T;
+    const uint32_t* __restrict__ bitmap, const typename S::T* __restrict__ tie_s,
+    const int32_t* __restrict__ tie_p, uint32_t* __restrict__ ctr,
+    const uint32_t* __restrict__ chunk, int32_t* __restrict__ cand, int max_ctx, int C,
+    int bitmap_words) {
   using Cfg = EmitCfg<S>;
   constexpr int NT = kEmitThreads;
   __shared__ uint32_t scan_sh[NT / kWave];
   __shared__ SelectShared ssh;
-  __shared__ __attribute__((aligned(16))) uint32_t bm_l[LDS_BM ? Cfg::kMaxWords : 4];
+  __shared__ uint32_t bm_l[kSelectChunkWords];
   __shared__ typename Cfg::E lds_t[Cfg::kTies];  // (key, position) of the ties
   __shared__ Threshold sh_thr;
-  const int b = blockIdx.x;
+  const int n_chunks = gridDim.x;
+  // (chunk, request), numbered so that one request's workgroups share an
+  // XCD's L2 (they all read the request's tie list)
+  const int lin = xcd_major(blockIdx.x + n_chunks * blockIdx.y, n_chunks * gridDim.y);
+  const int ck = lin % n_chunks, b = lin / n_chunks;
   const int tid = threadIdx.x;
   const int n_valid = clamp_ctx(ctx_len, b, max_ctx);
-  const int nw = (n_valid + 31) / 32;
-  const int nw4 = (nw + 3) / 4;
-  uint32_t* hb = hist + (size_t)b * S::kBins;
-  uint32_t* bmg = bitmap + (size_t)b * bitmap_words;
+  const int w0 = ck * kSelectChunkWords;  // first bitmap word of the chunk
+  const uint32_t* bmg = bitmap + (size_t)b * bitmap_words;
   uint32_t* cr = ctr + (size_t)kCtrStride * b;
-  uint32_t* bm = LDS_BM ? bm_l : bmg;
-  if (LDS_BM) {
-    for (int i = tid; i < nw4; i += NT) ((uint4*)bm_l)[i] = ((const uint4*)bmg)[i];
-  }
+
+  // unconditional loads (clamped), selected afterwards
+  const uint32_t wd = bmg[min(w0 + tid, bitmap_words - 1)];
+  bm_l[tid] = w0 + tid < bitmap_words ? wd : 0u;
+  uint32_t before = 0;  // kept outright in the chunks before this one
+  for (int i = tid; i < ck; i += NT) before += chunk[(size_t)b * n_chunks + i];
   const uint32_t n_tie = cr[kCtrTies];
   const int beta = n_valid > C ? (int)cr[kCtrBeta] : -1;
   const uint32_t above = cr[kCtrAbove];
 
+  uint32_t ties_before = 0;  // winning ties before the chunk (this thread's share)
   if (beta >= 0) {
     const uint32_t need = (uint32_t)C - above;  // 1 <= need <= n_tie
-    const T* ts = tie_s + (size_t)b * max_ctx;
+    const typename S::T* ts = tie_s + (size_t)b * max_ctx;
     const int32_t* tp = tie_p + (size_t)b * max_ctx;
     const bool in_lds = n_tie <= (uint32_t)Cfg::kTies;
     if (in_lds) {
       for (int i = tid; i < (int)n_tie; i += NT) lds_t[i] = Cfg::pack(ts[i], tp[i]);
     }
     __syncthreads();
-    Threshold thr{0ull, 0u, 0};
+    Threshold thr{0ull, 0u, 0};  // every tie wins when need == n_tie
     if (need < n_tie) {
       if (in_lds) {
         if (wave_id() == 0) {
@@ -237,7 +263,7 @@ __global__ __launch_bounds__(kEmitThreads) void k_topc_emit(
             u = Cfg::key(e);
             p = Cfg::pos(e);
           };
-          T lo, hi;
+          typename S::T lo, hi;
           S::range(beta, lo, hi);
           const Threshold t = wave_threshold(get, (int)n_tie, need, ssh.hist, Cfg::key_of(lo),
                                              Cfg::key_of(hi), pos_bits_below(max_ctx));
@@ -253,72 +279,71 @@ __global__ __launch_bounds__(kEmitThreads) void k_topc_emit(
         thr = block_threshold<NT>(get, (int)n_tie, need, ssh);
       }
     }
-    if (in_lds) {
-      for (int i = tid; i < (int)n_tie; i += NT) {
+    const uint32_t p_lo = 32u * (uint32_t)w0, p_hi = p_lo + 32u * kSelectChunkWords;
+    for (int i = tid; i < (int)n_tie; i += NT) {
+      uint64_t u;
+      uint32_t p;
+      if (in_lds) {
         const typename Cfg::E e = lds_t[i];
-        const uint32_t p = Cfg::pos(e);
-        if (keep(thr, Cfg::key(e), p)) atomicOr(&bm[p / 32], 1u << (p % 32));
+        u = Cfg::key(e);
+        p = Cfg::pos(e);
+      } else {
+        u = Cfg::key_of(ts[i]);
+        p = (uint32_t)tp[i];
       }
-    } else {
-      for (int i = tid; i < (int)n_tie; i += NT) {
-        const uint32_t p = (uint32_t)tp[i];
-        if (keep(thr, Cfg::key_of(ts[i]), p)) atomicOr(&bm[p / 32], 1u << (p % 32));
+      if (keep(thr, u, p)) {
+        if (p >= p_lo && p < p_hi) atomicOr(&bm_l[(p - p_lo) / 32], 1u << (p % 32));
+        else if (p < p_lo) ties_before++;
       }
     }
   }
   __syncthreads();
+  uint32_t base;
+  block_excl_scan<NT>(before + ties_before, scan_sh, &base);
 
-  // emit ascending positions: contiguous runs of 4-word groups per thread
-  const int gpt = (nw4 + NT - 1) / NT;
-  const int g0 = tid * gpt, g1 = min(g0 + gpt, nw4);
-  auto word = [&](int wi) -> uint32_t {
-    if (LDS_BM) return bm_l[wi];
-    return __hip_atomic_load(&bmg[wi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  };
-  uint32_t cnt = 0;
-  for (int gi = g0; gi < g1; gi++)
-#pragma unroll
-    for (int k = 0; k < 4; k++) cnt += __popc(word(4 * gi + k));
-  uint32_t total;
-  uint32_t off = block_excl_scan<NT>(cnt, scan_sh, &total);
+  // emit ascending positions: thread tid owns bitmap word w0 + tid
+  const uint32_t word = bm_l[tid];
+  uint32_t chunk_total;
+  uint32_t off = base + block_excl_scan<NT>((uint32_t)__popc(word), scan_sh, &chunk_total);
   int32_t* cb = cand + (size_t)b * C;
-  for (int gi = g0; gi < g1; gi++) {
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      const int wi = 4 * gi + k;
-      uint32_t bits = word(wi);
-      while (bits) {
-        const int j = __ffs(bits) - 1;
-        if (off < (uint32_t)C) cb[off] = 32 * wi + j;
-        off++;
-        bits &= bits - 1;
-      }
+  uint32_t bits = word;
+  while (bits) {
+    const int j = __ffs(bits) - 1;
+    if (off < (uint32_t)C) cb[off] = 32 * (w0 + tid) + j;
+    off++;
+    bits &= bits - 1;
+  }
+  // every valid token is kept when there is no threshold bucket; otherwise
+  // exactly C are
+  if (ck == 0) {
+    const int total = beta >= 0 ? C : min(n_valid, C);
+    for (int i = total + tid; i < C; i += NT) cb[i] = -1;
+  }
+
+  // leave the histogram (this chunk's share) and the tie counter cleared
+  uint32_t* hb = hist + (size_t)b * S::kBins;
+  const int per = (S::kBins + n_chunks - 1) / n_chunks;
+  for (int i = ck * per + tid; i < min((ck + 1) * per, S::kBins); i += NT) hb[i] = 0;
+  __syncthreads();  // every read of the counters and the tie list is done
+  if (tid == 0) {
+    if (atomicAdd(&cr[kCtrDone], 1u) == (uint32_t)n_chunks - 1) {
+      cr[kCtrTies] = 0;
+      cr[kCtrDone] = 0;
     }
   }
-  for (int i = (int)total + tid; i < C; i += NT) cb[i] = -1;
-
-  // leave the histogram and tie counter cleared for the next call
-  for (int i = tid; i < S::kBins; i += NT) hb[i] = 0;
-  if (tid == 0) cr[kCtrTies] = 0;
 }
 
 template <class S>
 hipError_t launch_select(const int32_t* ctx_len, const SelectWS<typename S::T>& ws, int32_t* out,
                          int B, int max_ctx, int C, hipStream_t st) {
-  dim3 grid((ws.bitmap_words * 32 + kFilterChunk - 1) / kFilterChunk, B);
+  dim3 grid(select_chunks(ws.bitmap_words), B);
   hipLaunchKernelGGL(k_topc_filter<S>, grid, dim3(kFilterThreads), 0, st, ctx_len, ws.scores,
-                     ws.hist, ws.bitmap, ws.tie_s, ws.tie_p, ws.ctr, max_ctx, C,
+                     ws.hist, ws.bitmap, ws.tie_s, ws.tie_p, ws.ctr, ws.chunk, max_ctx, C,
                      ws.bitmap_words);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (ws.bitmap_words <= EmitCfg<S>::kMaxWords)
-    hipLaunchKernelGGL((k_topc_emit<S, true>), dim3(B), dim3(kEmitThreads), 0, st, ctx_len,
-                       ws.hist, ws.bitmap, ws.tie_s, ws.tie_p, ws.ctr, out, max_ctx, C,
-                       ws.bitmap_words);
-  else
-    hipLaunchKernelGGL((k_topc_emit<S, false>), dim3(B), dim3(kEmitThreads), 0, st, ctx_len,
-                       ws.hist, ws.bitmap, ws.tie_s, ws.tie_p, ws.ctr, out, max_ctx, C,
-                       ws.bitmap_words);
+  hipLaunchKernelGGL(k_topc_emit<S>, grid, dim3(kEmitThreads), 0, st, ctx_len, ws.hist, ws.bitmap,
+                     ws.tie_s, ws.tie_p, ws.ctr, ws.chunk, out, max_ctx, C, ws.bitmap_words);
   return hipGetLastError();
 }
 

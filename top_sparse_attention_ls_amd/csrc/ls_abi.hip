@@ -132,6 +132,7 @@ void carve_coarse(Carve& c, const ls_idx_desc* d, ls::CoarseWS* ws) {
   w.scores = c.take<int32_t>(B * L);
   w.bitmap_words = bitmap_words(d->max_ctx);
   w.bitmap = c.take<uint32_t>(B * w.bitmap_words);
+  w.chunk = c.take<uint32_t>(B * ls::select_chunks(w.bitmap_words));
   w.tie_s = c.take<int32_t>(B * L);
   w.tie_p = c.take<int32_t>(B * L);
   if (ws) *ws = w;
@@ -147,6 +148,7 @@ void carve_prefill(Carve& c, const ls_prefill_desc* d, ls::WideWS* ws, int32_t**
   w.scores = c.take<int64_t>(R * L);
   w.bitmap_words = bitmap_words(d->max_ctx);
   w.bitmap = c.take<uint32_t>(R * w.bitmap_words);
+  w.chunk = c.take<uint32_t>(R * ls::select_chunks(w.bitmap_words));
   w.tie_s = c.take<int64_t>(R * L);
   w.tie_p = c.take<int32_t>(R * L);
   int32_t* cx = c.take<int32_t>(R);

@@ -34,8 +34,16 @@ struct SelectWS {
   T* tie_s;            // [B, max_ctx]
   int32_t* tie_p;      // [B, max_ctx]
   uint32_t* ctr;       // [B, kCtrStride] tie count (word 0); zero between calls
+  uint32_t* chunk;     // [B, n_chunks] kept count of each 16384-position chunk
   int bitmap_words;
 };
+// Chunks of 16384 positions (512 bitmap words) the selection works in: one
+// filter and one emit workgroup each.
+constexpr int kSelectChunkWords = 512;
+inline int select_chunks(int bitmap_words) {
+  return (bitmap_words + kSelectChunkWords - 1) / kSelectChunkWords;
+}
+
 using CoarseWS = SelectWS<int32_t>;  // coarse scores, kCoarseBins buckets
 using WideWS = SelectWS<int64_t>;    // int64 scores, 7552 buckets
 
