@@ -141,6 +141,10 @@ __global__ __launch_bounds__(256) void k_refine(const int8_t* __restrict__ q,
 // ballots plus one small table of per-wave counts that wave 0 scans, so the
 // kept candidates are written by consecutive lanes to consecutive slots.
 // The candidates' hot slots were looked up by the refine kernel.
+// A request runs PER workgroups (grid.x): every one makes the whole
+// selection (the candidates are 16 B each, read from L2), then writes only
+// its slice of 1024 candidates (k = its index) at the offsets the shared scan
+// gives.
 //
 // k_topk (any C, also the fallback when the tie list overflows LDS): the
 // block radix threshold search over all candidates.
@@ -169,7 +173,11 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
   __shared__ Threshold sh_thr;
   __shared__ int sh_beta;
   __shared__ uint32_t sh_above, n_tie, sh_tot;
-  const int b = blockIdx.x, tid = threadIdx.x, l = lane_id(), wv = wave_id();
+  // (slice, request), numbered so that a request's workgroups share an XCD's
+  // L2 (they all read the request's candidates)
+  const int lin = xcd_major(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+  const int m = lin % gridDim.x, b = lin / gridDim.x;
+  const int tid = threadIdx.x, l = lane_id(), wv = wave_id();
   const int32_t* cb = cand + (size_t)b * C;
   const int64_t* fb = fs + (size_t)b * C;
 
@@ -324,8 +332,10 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
   int64_t* sb = topk_score ? topk_score + (size_t)b * K : nullptr;
   int32_t* rb = rows ? rows + (size_t)b * K : nullptr;
   int32_t* mb = miss_pos ? miss_pos + (size_t)b * K : nullptr;
+  const uint32_t tot = sh_tot;
 #pragma unroll
   for (int k = 0; k < PER; k++) {
+    if (k != m) continue;  // this workgroup's slice (workgroup-uniform)
     const uint32_t base = tab[k * NW + wv];
     const uint32_t o = (base & 0xFFFFu) + lane_rank(ms[k]);
     if (!sel[k] || o >= (uint32_t)K) continue;  // exactly min(K, valid) are kept
@@ -341,13 +351,14 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
       }
     }
   }
-  const uint32_t tot = sh_tot;
-  for (int j = (int)(tot & 0xFFFFu) + tid; j < K; j += NT) {
-    tb[j] = -1;
-    if (sb) sb[j] = 0;
-    if (rb) rb[j] = -1;
+  if (m == 0) {
+    for (int j = (int)(tot & 0xFFFFu) + tid; j < K; j += NT) {
+      tb[j] = -1;
+      if (sb) sb[j] = 0;
+      if (rb) rb[j] = -1;
+    }
+    if (tid == 0 && n_miss) n_miss[b] = resolve ? (int32_t)(tot >> 16) : 0;
   }
-  if (tid == 0 && n_miss) n_miss[b] = resolve ? (int32_t)(tot >> 16) : 0;
 }
 
 __global__ __launch_bounds__(kTopkThreads) void k_topk(
@@ -456,10 +467,10 @@ hipError_t launch_refine_topk(const int8_t* q, const int8_t* w, const int8_t* k8
 #undef LS_REFINE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-#define LS_TOPK(P)                                                                         \
-  hipLaunchKernelGGL(k_topk_hist<P>, dim3(B), dim3(kTopkThreads), 0, st, cand, ws.fs, ws.slot, \
-                     topk, topk_score, pos2slot, rows, n_miss, ws.miss_pos, hot_slots, max_ctx, \
-                     C, K)
+#define LS_TOPK(P)                                                                           \
+  hipLaunchKernelGGL(k_topk_hist<P>, dim3(P, B), dim3(kTopkThreads), 0, st, cand, ws.fs,       \
+                     ws.slot, topk, topk_score, pos2slot, rows, n_miss, ws.miss_pos,           \
+                     hot_slots, max_ctx, C, K)
   if (C <= kTopkThreads) LS_TOPK(1);
   else if (C <= 2 * kTopkThreads) LS_TOPK(2);
   else if (C <= 4 * kTopkThreads) LS_TOPK(4);
@@ -525,6 +536,7 @@ hipError_t launch_hot_resolve(const int32_t* topk, const int32_t* pos2slot, int3
 // 16-byte pieces: each workgroup copies a contiguous share of the request's
 // pieces, every thread four pieces at a time with all loads issued before
 // the stores.  The pool may be pinned host memory (reads then cross PCIe).
+
 constexpr int kGatherWGPerReq = 32;
 constexpr int kGatherUnroll = 4;
 
