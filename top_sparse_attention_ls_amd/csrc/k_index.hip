@@ -130,19 +130,21 @@ __device__ __forceinline__ uint32_t mad_i24(int32_t a, int32_t b, uint32_t c) {
 }
 
 // The four 16-token tiles of one 64-token step: lane (n, g) loads token
-// base + 16 tt + n (clamped to t_last) at byte offset g * LB of its row.
-// Offsets stay 32-bit (a request's compact keys are < 4 GiB).
+// base + 16 tt + n at byte g * LB of its row, through a buffer resource over
+// the request's valid keys (tokens past them read as zero, and their scores
+// are dropped).  The tile's token offset is a scalar (soffset) and the lane's
+// offset a constant, so a load costs no VALU address arithmetic.
 template <int D>
-__device__ __forceinline__ void coarse_load4(const uint8_t* kb, int base, int n, int t_last,
-                                             v4i (&r)[4]) {
-  constexpr uint32_t KB = D / 2;
+__device__ __forceinline__ void coarse_load4(__amdgpu_buffer_rsrc_t kres, uint32_t lane_off,
+                                             int base, v4i (&r)[4]) {
+  constexpr int KB = D / 2;
 #pragma unroll
   for (int tt = 0; tt < 4; tt++) {
-    const uint32_t t = (uint32_t)min(base + 16 * tt + n, t_last);
+    const int so = __builtin_amdgcn_readfirstlane((base + 16 * tt) * KB);
     if (D == 128) {
-      r[tt] = *(const v4i*)(kb + t * KB);
+      r[tt] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(kres, lane_off, so, 0));
     } else {
-      const int2 v = *(const int2*)(kb + t * KB);
+      const int2 v = __builtin_bit_cast(int2, __builtin_amdgcn_raw_buffer_load_b64(kres, lane_off, so, 0));
       r[tt] = v4i{v.x, v.y, 0, 0};
     }
   }
@@ -216,11 +218,13 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
       k_lane += (uint32_t)(wv[mt][i] * cv[mt][i]);
     }
 
-  const uint8_t* kb = kc + (size_t)b * max_ctx * KB + g * LB;  // + 32-bit token offsets
+  // the request's valid compact keys (tokens past n_valid read as zero)
+  const __amdgpu_buffer_rsrc_t kres =
+      buffer_rsrc(kc + (size_t)b * max_ctx * KB, (uint32_t)n_valid * KB);
+  const uint32_t lane_off = (uint32_t)(n * KB + g * LB);
   // this workgroup's score range as a buffer: lanes past t_end store nothing
   const __amdgpu_buffer_rsrc_t sres =
       buffer_rsrc(scores + (size_t)b * max_ctx + t_begin, 4u * (uint32_t)(t_end - t_begin));
-  const int t_last = t_end - 1;
 
   // One 64-token step: all MFMAs first (independent accumulators), then the
   // epilogue, so MFMA latency overlaps the VALU work of earlier tiles.
@@ -282,20 +286,19 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
   // measured fastest; deeper rings cost more in register moves at the loop
   // edge than they gain).  The scheduling fences keep each
   // step's refill ahead of its compute (the scheduler would otherwise sink
-  // it below the wait for the current buffer).  Past the end every lane
-  // loads row t_last (one line).
+  // it below the wait for the current buffer).
   constexpr int S = 256;  // tokens per workgroup step (4 waves x 64)
   int base = __builtin_amdgcn_readfirstlane(t_begin + wave_id() * 64);
   if (base < t_end) {
     v4i buf[kCoarseDepth][4];
 #pragma unroll
-    for (int k = 0; k < kCoarseDepth - 1; k++) coarse_load4<D>(kb, base + k * S, n, t_last, buf[k]);
+    for (int k = 0; k < kCoarseDepth - 1; k++) coarse_load4<D>(kres, lane_off, base + k * S, buf[k]);
     bool more = true;
     while (more) {
 #pragma unroll
       for (int k = 0; k < kCoarseDepth; k++) {
         if (more) {
-          coarse_load4<D>(kb, base + (kCoarseDepth - 1) * S, n, t_last,
+          coarse_load4<D>(kres, lane_off, base + (kCoarseDepth - 1) * S,
                           buf[(k + kCoarseDepth - 1) % kCoarseDepth]);
           __builtin_amdgcn_sched_barrier(0);
           process(base, buf[k]);
