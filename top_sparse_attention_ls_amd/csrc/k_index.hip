@@ -151,7 +151,7 @@ __device__ __forceinline__ void coarse_load4(__amdgpu_buffer_rsrc_t kres, uint32
 }
 
 constexpr int kCoarseTileGroup = 2;
-constexpr int kCoarseDepth = 2;
+constexpr int kCoarseDepth = 2;  // deeper rings measured slower (more bytes in flight)
 
 template <int D, int HT>
 __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
@@ -282,31 +282,33 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
   };
 
   // A ring of kCoarseDepth register buffers: the loads of the next
-  // kCoarseDepth - 1 steps are in flight while a step computes (two buffers
-  // measured fastest; deeper rings cost more in register moves at the loop
-  // edge than they gain).  The scheduling fences keep each
-  // step's refill ahead of its compute (the scheduler would otherwise sink
-  // it below the wait for the current buffer).
+  // kCoarseDepth - 1 steps are in flight while a step computes.  The main
+  // loop runs whole groups of kCoarseDepth steps with a straight-line body
+  // (no exit in the middle, so the ring stays in the same registers across
+  // the loop edge and nothing drains there); the last steps then use the
+  // buffers already loaded.  The scheduling fences keep each step's refill
+  // ahead of its compute (the scheduler would otherwise sink it below the
+  // wait for the current buffer).
   constexpr int S = 256;  // tokens per workgroup step (4 waves x 64)
-  int base = __builtin_amdgcn_readfirstlane(t_begin + wave_id() * 64);
-  if (base < t_end) {
-    v4i buf[kCoarseDepth][4];
+  constexpr int R = kCoarseDepth;
+  const int base0 = __builtin_amdgcn_readfirstlane(t_begin + wave_id() * 64);
+  const int n_steps = base0 < t_end ? (t_end - base0 + S - 1) / S : 0;  // wave-uniform
+  if (n_steps > 0) {
+    v4i buf[R][4];
 #pragma unroll
-    for (int k = 0; k < kCoarseDepth - 1; k++) coarse_load4<D>(kres, lane_off, base + k * S, buf[k]);
-    bool more = true;
-    while (more) {
+    for (int k = 0; k < R - 1; k++) coarse_load4<D>(kres, lane_off, base0 + k * S, buf[k]);
+    int k0 = 0;
+    for (; k0 + R <= n_steps; k0 += R) {
 #pragma unroll
-      for (int k = 0; k < kCoarseDepth; k++) {
-        if (more) {
-          coarse_load4<D>(kres, lane_off, base + (kCoarseDepth - 1) * S,
-                          buf[(k + kCoarseDepth - 1) % kCoarseDepth]);
-          __builtin_amdgcn_sched_barrier(0);
-          process(base, buf[k]);
-          base += S;
-          more = base < t_end;
-        }
+      for (int j = 0; j < R; j++) {
+        coarse_load4<D>(kres, lane_off, base0 + (k0 + j + R - 1) * S, buf[(j + R - 1) % R]);
+        __builtin_amdgcn_sched_barrier(0);
+        process(base0 + (k0 + j) * S, buf[j]);
       }
     }
+#pragma unroll
+    for (int j = 0; j < R - 1; j++)
+      if (k0 + j < n_steps) process(base0 + (k0 + j) * S, buf[j]);
   }
   __syncthreads();
   uint32_t* hb = hist + (size_t)b * kCoarseBins;
