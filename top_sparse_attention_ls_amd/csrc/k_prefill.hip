@@ -15,6 +15,7 @@
 namespace ls {
 
 constexpr int kPrefillRowsPerWG = 2;  // query rows sharing each key tile
+constexpr int kPrefillWaves = 8;      // waves of a workgroup, all on its rows
 
 __global__ __launch_bounds__(256) void k_prefill_ctx(int32_t* __restrict__ ctx, int rows,
                                                       int first_pos, int max_ctx) {
@@ -22,7 +23,7 @@ __global__ __launch_bounds__(256) void k_prefill_ctx(int32_t* __restrict__ ctx, 
   if (i < rows) ctx[i] = min(max(first_pos + i + 1, 0), max_ctx);
 }
 
-// Scores of kPrefillRowsPerWG query rows against kPrefillTokPerWG keys, as
+// Scores of kPrefillRowsPerWG query rows against every key they may see, as
 // an int8 GEMM on v_mfma_i32_16x16x64_i8: A = one row's query (16 heads per
 // tile, held in VGPRs), B = 16 keys.  Lane (n, g) holds, for k-step mf,
 // dims 32 g + 16 mf .. +15 of head (or key) n: the same dims in A and B, so
@@ -31,12 +32,15 @@ __global__ __launch_bounds__(256) void k_prefill_ctx(int32_t* __restrict__ ctx, 
 // summed over four heads in int32 (< 2^30), then over head tiles in int64,
 // then across the four lane groups with a reduce-scatter that leaves one
 // key per lane.  Each lane buckets its row's score into that row's LDS
-// histogram (flushed once per workgroup), the first pass of the selection.
-// Keys past a row's causal limit are computed with the rest of the tile
-// but neither stored nor counted.  Key loads are clamped to the tile's last
-// key and ping-pong prefetched 64 keys ahead.
+// histogram, the first pass of the selection.  The workgroup owns its rows:
+// kPrefillWaves waves stride over the keys (64 per wave step), the query
+// operands are loaded once, and the rows' histograms are zeroed once and
+// stored whole at the end (no global atomics).  Keys past a row's causal
+// limit are computed with the rest of the tile but neither stored nor
+// counted.  Key loads are clamped to the last key and ping-pong prefetched
+// one workgroup step ahead.
 template <int D, int HT>
-__global__ __launch_bounds__(256) void k_prefill_scores(
+__global__ __launch_bounds__(64 * kPrefillWaves) void k_prefill_scores(
     const int8_t* __restrict__ q, const int8_t* __restrict__ w, const int8_t* __restrict__ keys,
     int64_t* __restrict__ scores, uint32_t* __restrict__ hist, int rows, int first_pos, int H,
     int max_ctx) {
@@ -44,7 +48,8 @@ __global__ __launch_bounds__(256) void k_prefill_scores(
   constexpr int NMF = D / 64;
   __shared__ uint32_t lhist[QR][kWideBins];
 
-  const int r0 = blockIdx.y * QR;
+  constexpr int NT = 64 * kPrefillWaves;
+  const int r0 = blockIdx.x * QR;
   int nv[QR];
   int nv_max = 0;
 #pragma unroll
@@ -52,11 +57,9 @@ __global__ __launch_bounds__(256) void k_prefill_scores(
     nv[r] = (r0 + r < rows) ? min(max(first_pos + r0 + r + 1, 0), max_ctx) : 0;
     nv_max = max(nv_max, nv[r]);
   }
-  const int t_begin = blockIdx.x * kPrefillTokPerWG;
-  if (t_begin >= nv_max) return;
-  const int t_end = min(t_begin + kPrefillTokPerWG, nv_max);
+  const int t_end = nv_max;
 
-  for (int i = threadIdx.x; i < QR * kWideBins; i += 256) (&lhist[0][0])[i] = 0;
+  for (int i = threadIdx.x; i < QR * kWideBins; i += NT) (&lhist[0][0])[i] = 0;
 
   const int l = lane_id(), n = l & 15, g = l >> 4;
   const int off = (D == 128) ? 32 * g : 16 * g;
@@ -142,30 +145,31 @@ __global__ __launch_bounds__(256) void k_prefill_scores(
     }
   };
 
-  int base = __builtin_amdgcn_readfirstlane(t_begin + wave_id() * 64);
+  constexpr int S = 64 * kPrefillWaves;  // keys per workgroup step
+  int base = __builtin_amdgcn_readfirstlane(wave_id() * 64);
   if (base < t_end) {
     v4i bufA[4][NMF], bufB[4][NMF];
     load4(base, bufA);
     while (true) {
-      load4(base + 256, bufB);
+      load4(base + S, bufB);
+      __builtin_amdgcn_sched_barrier(0);
       process(base, bufA);
-      base += 256;
+      base += S;
       if (base >= t_end) break;
-      load4(base + 256, bufA);
+      load4(base + S, bufA);
+      __builtin_amdgcn_sched_barrier(0);
       process(base, bufB);
-      base += 256;
+      base += S;
       if (base >= t_end) break;
     }
   }
   __syncthreads();
+  // the rows' histograms are complete: store them whole
 #pragma unroll
   for (int r = 0; r < QR; r++) {
     if (r0 + r >= rows) continue;
     uint32_t* hb = hist + (size_t)(r0 + r) * kWideBins;
-    for (int i = threadIdx.x; i < kWideBins; i += 256) {
-      const uint32_t c = lhist[r][i];
-      if (c) atomicAdd(&hb[i], c);
-    }
+    for (int i = threadIdx.x; i < kWideBins; i += NT) hb[i] = lhist[r][i];
   }
 }
 
@@ -176,12 +180,11 @@ hipError_t launch_prefill_block(const int8_t* q, const int8_t* w, const int8_t* 
                      first_pos, max_ctx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 grid((max_ctx + kPrefillTokPerWG - 1) / kPrefillTokPerWG,
-            (rows + kPrefillRowsPerWG - 1) / kPrefillRowsPerWG);
+  dim3 grid((rows + kPrefillRowsPerWG - 1) / kPrefillRowsPerWG);
   const int HT = (H + 15) / 16;
 #define LS_PREFILL(DD, TT)                                                                  \
-  hipLaunchKernelGGL((k_prefill_scores<DD, TT>), grid, dim3(256), 0, st, q, w, keys,        \
-                     ws.scores, ws.hist, rows, first_pos, H, max_ctx)
+  hipLaunchKernelGGL((k_prefill_scores<DD, TT>), grid, dim3(64 * kPrefillWaves), 0, st, q, w, \
+                     keys, ws.scores, ws.hist, rows, first_pos, H, max_ctx)
   if (D == 128) {
     if (HT == 1) LS_PREFILL(128, 1); else if (HT == 2) LS_PREFILL(128, 2);
     else if (HT == 3) LS_PREFILL(128, 3); else LS_PREFILL(128, 4);

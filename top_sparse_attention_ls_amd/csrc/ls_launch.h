@@ -22,7 +22,6 @@ constexpr int kCoarseTokPerWG = 8192;
 constexpr int kRefinePerWG = 256;
 // Keys scored by one workgroup of the prefill indexer, and query rows per
 // pass of it (each pass owns one score buffer of that many rows).
-constexpr int kPrefillTokPerWG = 4096;
 constexpr int kPrefillRowBlock = 512;
 
 // Workspace of a histogram-driven selection over rows of scores of type T.
