@@ -199,24 +199,26 @@ template <> struct EmitCfg<WideScore> {
   static __device__ __forceinline__ uint64_t key_of(int64_t s) { return key_of_i64(s); }
 };
 
-// k_topc_emit: one 512-thread workgroup per (request, chunk of 16384
-// positions), so a request's emission spreads over as many workgroups as its
-// filter.  Every workgroup resolves the request's tie list itself (one wave
-// runs the radix threshold search when the list fits in LDS, the whole
-// workgroup otherwise): the list is short, and repeating the search costs
-// less than another kernel boundary.  Its output offset is the kept count of
-// the chunks before it (written by the filter) plus the winning ties before
-// it; it sets its winners' bits in its LDS copy of the chunk's 512 bitmap
-// words and emits the kept positions in ascending order, one word per
-// thread.  Chunk 0 pads the list with -1.  Each workgroup clears its share of
-// the request's histogram; the last one to finish clears the tie counter.
+// k_topc_emit: one 512-thread workgroup per (request, run of cpw chunks of
+// 16384 positions).  With few requests cpw = 1, so a request's emission
+// spreads over as many workgroups as its filter; with many (prefill rows)
+// one workgroup takes all of a row's chunks.  Every workgroup resolves the
+// request's tie list itself (one wave runs the radix threshold search when
+// the list fits in LDS, the whole workgroup otherwise): the list is short,
+// and repeating the search costs less than another kernel boundary.  Its
+// output offset is the kept count of the chunks before its run (written by
+// the filter) plus the winning ties before it.  For each chunk of the run it
+// sets the winners' bits in an LDS copy of the chunk's 512 bitmap words and
+// emits the kept positions in ascending order, one word per thread.  The
+// first run pads the list with -1.  Each workgroup clears its share of the
+// request's histogram; the last one to finish clears the tie counter.
 template <class S>
 __global__ __launch_bounds__(kEmitThreads) void k_topc_emit(
     const int32_t* __restrict__ ctx_len, uint32_t* __restrict__ hist,
     const uint32_t* __restrict__ bitmap, const typename S::T* __restrict__ tie_s,
     const int32_t* __restrict__ tie_p, uint32_t* __restrict__ ctr,
     const uint32_t* __restrict__ chunk, int32_t* __restrict__ cand, int max_ctx, int C,
-    int bitmap_words) {
+    int bitmap_words, int n_chunks, int cpw) {
   using Cfg = EmitCfg<S>;
   constexpr int NT = kEmitThreads;
   __shared__ uint32_t scan_sh[NT / kWave];
@@ -224,37 +226,45 @@ __global__ __launch_bounds__(kEmitThreads) void k_topc_emit(
   __shared__ uint32_t bm_l[kSelectChunkWords];
   __shared__ typename Cfg::E lds_t[Cfg::kTies];  // (key, position) of the ties
   __shared__ Threshold sh_thr;
-  const int n_chunks = gridDim.x;
-  // (chunk, request), numbered so that one request's workgroups share an
+  const int n_runs = gridDim.x;  // workgroups per request
+  // (run, request), numbered so that one request's workgroups share an
   // XCD's L2 (they all read the request's tie list)
-  const int lin = xcd_major(blockIdx.x + n_chunks * blockIdx.y, n_chunks * gridDim.y);
-  const int ck = lin % n_chunks, b = lin / n_chunks;
+  const int lin = xcd_major(blockIdx.x + n_runs * blockIdx.y, n_runs * gridDim.y);
+  const int run = lin % n_runs, b = lin / n_runs;
+  const int ck0 = run * cpw, ck1 = min(ck0 + cpw, n_chunks);  // this workgroup's chunks
   const int tid = threadIdx.x;
   const int n_valid = clamp_ctx(ctx_len, b, max_ctx);
-  const int w0 = ck * kSelectChunkWords;  // first bitmap word of the chunk
   const uint32_t* bmg = bitmap + (size_t)b * bitmap_words;
   uint32_t* cr = ctr + (size_t)kCtrStride * b;
 
-  // unconditional loads (clamped), selected afterwards
-  const uint32_t wd = bmg[min(w0 + tid, bitmap_words - 1)];
-  bm_l[tid] = w0 + tid < bitmap_words ? wd : 0u;
-  uint32_t before = 0;  // kept outright in the chunks before this one
-  for (int i = tid; i < ck; i += NT) before += chunk[(size_t)b * n_chunks + i];
+  uint32_t before = 0;  // kept outright in the chunks before the run
+  for (int i = tid; i < ck0; i += NT) before += chunk[(size_t)b * n_chunks + i];
   const uint32_t n_tie = cr[kCtrTies];
   const int beta = n_valid > C ? (int)cr[kCtrBeta] : -1;
   const uint32_t above = cr[kCtrAbove];
 
-  uint32_t ties_before = 0;  // winning ties before the chunk (this thread's share)
+  uint32_t ties_before = 0;  // winning ties before the run (this thread's share)
+  const typename S::T* ts = tie_s + (size_t)b * max_ctx;
+  const int32_t* tp = tie_p + (size_t)b * max_ctx;
+  const bool in_lds = n_tie <= (uint32_t)Cfg::kTies;
+  // tie i as (order-preserving key, position), from LDS or the global list
+  auto tie_entry = [&](int i, uint64_t& u, uint32_t& p) {
+    if (in_lds) {
+      const typename Cfg::E e = lds_t[i];
+      u = Cfg::key(e);
+      p = Cfg::pos(e);
+    } else {
+      u = Cfg::key_of(ts[i]);
+      p = (uint32_t)tp[i];
+    }
+  };
+  Threshold thr{0ull, 0u, 0};  // every tie wins when need == n_tie
   if (beta >= 0) {
     const uint32_t need = (uint32_t)C - above;  // 1 <= need <= n_tie
-    const typename S::T* ts = tie_s + (size_t)b * max_ctx;
-    const int32_t* tp = tie_p + (size_t)b * max_ctx;
-    const bool in_lds = n_tie <= (uint32_t)Cfg::kTies;
     if (in_lds) {
       for (int i = tid; i < (int)n_tie; i += NT) lds_t[i] = Cfg::pack(ts[i], tp[i]);
     }
     __syncthreads();
-    Threshold thr{0ull, 0u, 0};  // every tie wins when need == n_tie
     if (need < n_tie) {
       if (in_lds) {
         if (wave_id() == 0) {
@@ -279,54 +289,62 @@ __global__ __launch_bounds__(kEmitThreads) void k_topc_emit(
         thr = block_threshold<NT>(get, (int)n_tie, need, ssh);
       }
     }
-    const uint32_t p_lo = 32u * (uint32_t)w0, p_hi = p_lo + 32u * kSelectChunkWords;
+    const uint32_t p_lo = 32u * (uint32_t)(ck0 * kSelectChunkWords);
     for (int i = tid; i < (int)n_tie; i += NT) {
       uint64_t u;
       uint32_t p;
-      if (in_lds) {
-        const typename Cfg::E e = lds_t[i];
-        u = Cfg::key(e);
-        p = Cfg::pos(e);
-      } else {
-        u = Cfg::key_of(ts[i]);
-        p = (uint32_t)tp[i];
-      }
-      if (keep(thr, u, p)) {
-        if (p >= p_lo && p < p_hi) atomicOr(&bm_l[(p - p_lo) / 32], 1u << (p % 32));
-        else if (p < p_lo) ties_before++;
-      }
+      tie_entry(i, u, p);
+      if (p < p_lo && keep(thr, u, p)) ties_before++;
     }
   }
-  __syncthreads();
   uint32_t base;
   block_excl_scan<NT>(before + ties_before, scan_sh, &base);
 
-  // emit ascending positions: thread tid owns bitmap word w0 + tid
-  const uint32_t word = bm_l[tid];
-  uint32_t chunk_total;
-  uint32_t off = base + block_excl_scan<NT>((uint32_t)__popc(word), scan_sh, &chunk_total);
+  // the run's chunks in order; thread tid owns bitmap word w0 + tid
   int32_t* cb = cand + (size_t)b * C;
-  uint32_t bits = word;
-  while (bits) {
-    const int j = __ffs(bits) - 1;
-    if (off < (uint32_t)C) cb[off] = 32 * (w0 + tid) + j;
-    off++;
-    bits &= bits - 1;
+  for (int ck = ck0; ck < ck1; ck++) {
+    const int w0 = ck * kSelectChunkWords;
+    // unconditional load (clamped), selected afterwards
+    const uint32_t wd = bmg[min(w0 + tid, bitmap_words - 1)];
+    bm_l[tid] = w0 + tid < bitmap_words ? wd : 0u;
+    __syncthreads();
+    if (beta >= 0) {  // the winning ties of this chunk
+      const uint32_t p_lo = 32u * (uint32_t)w0, p_hi = p_lo + 32u * kSelectChunkWords;
+      for (int i = tid; i < (int)n_tie; i += NT) {
+        uint64_t u;
+        uint32_t p;
+        tie_entry(i, u, p);
+        if (p >= p_lo && p < p_hi && keep(thr, u, p))
+          atomicOr(&bm_l[(p - p_lo) / 32], 1u << (p % 32));
+      }
+      __syncthreads();
+    }
+    const uint32_t word = bm_l[tid];
+    uint32_t chunk_total;
+    uint32_t off = base + block_excl_scan<NT>((uint32_t)__popc(word), scan_sh, &chunk_total);
+    uint32_t bits = word;
+    while (bits) {
+      const int j = __ffs(bits) - 1;
+      if (off < (uint32_t)C) cb[off] = 32 * (w0 + tid) + j;
+      off++;
+      bits &= bits - 1;
+    }
+    base += chunk_total;
   }
   // every valid token is kept when there is no threshold bucket; otherwise
   // exactly C are
-  if (ck == 0) {
+  if (run == 0) {
     const int total = beta >= 0 ? C : min(n_valid, C);
     for (int i = total + tid; i < C; i += NT) cb[i] = -1;
   }
 
-  // leave the histogram (this chunk's share) and the tie counter cleared
+  // leave the histogram (this workgroup's share) and the tie counter cleared
   uint32_t* hb = hist + (size_t)b * S::kBins;
-  const int per = (S::kBins + n_chunks - 1) / n_chunks;
-  for (int i = ck * per + tid; i < min((ck + 1) * per, S::kBins); i += NT) hb[i] = 0;
+  const int per = (S::kBins + n_runs - 1) / n_runs;
+  for (int i = run * per + tid; i < min((run + 1) * per, S::kBins); i += NT) hb[i] = 0;
   __syncthreads();  // every read of the counters and the tie list is done
   if (tid == 0) {
-    if (atomicAdd(&cr[kCtrDone], 1u) == (uint32_t)n_chunks - 1) {
+    if (atomicAdd(&cr[kCtrDone], 1u) == (uint32_t)n_runs - 1) {
       cr[kCtrTies] = 0;
       cr[kCtrDone] = 0;
     }
@@ -342,8 +360,14 @@ hipError_t launch_select(const int32_t* ctx_len, const SelectWS<typename S::T>& 
                      ws.bitmap_words);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_topc_emit<S>, grid, dim3(kEmitThreads), 0, st, ctx_len, ws.hist, ws.bitmap,
-                     ws.tie_s, ws.tie_p, ws.ctr, ws.chunk, out, max_ctx, C, ws.bitmap_words);
+  // one workgroup per chunk while that is needed to fill the GPU; with many
+  // rows, one per row
+  const int n_chunks = (int)grid.x;
+  const int cpw = B >= 256 ? n_chunks : 1;
+  const dim3 egrid((n_chunks + cpw - 1) / cpw, B);
+  hipLaunchKernelGGL(k_topc_emit<S>, egrid, dim3(kEmitThreads), 0, st, ctx_len, ws.hist,
+                     ws.bitmap, ws.tie_s, ws.tie_p, ws.ctr, ws.chunk, out, max_ctx, C,
+                     ws.bitmap_words, n_chunks, cpw);
   return hipGetLastError();
 }
 
