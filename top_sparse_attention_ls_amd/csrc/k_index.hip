@@ -130,10 +130,11 @@ __device__ __forceinline__ uint32_t mad_i24(int32_t a, int32_t b, uint32_t c) {
 }
 
 // The four 16-token tiles of one 64-token step: lane (n, g) loads token
-// base + 16 tt + n at byte g * LB of its row, through a buffer resource over
-// the request's valid keys (tokens past them read as zero, and their scores
-// are dropped).  The tile's token offset is a scalar (soffset) and the lane's
-// offset a constant, so a load costs no VALU address arithmetic.
+// base + 16 tt + n (counted from the workgroup's first token) at byte g * LB
+// of its row, through a buffer resource over the workgroup's own keys
+// (tokens past them read as zero without a memory access, and their scores
+// are dropped).  The tile's token offset is a scalar (soffset) and the
+// lane's offset a constant, so a load costs no VALU address arithmetic.
 template <int D>
 __device__ __forceinline__ void coarse_load4(__amdgpu_buffer_rsrc_t kres, uint32_t lane_off,
                                              int base, v4i (&r)[4]) {
@@ -218,9 +219,9 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
       k_lane += (uint32_t)(wv[mt][i] * cv[mt][i]);
     }
 
-  // the request's valid compact keys (tokens past n_valid read as zero)
-  const __amdgpu_buffer_rsrc_t kres =
-      buffer_rsrc(kc + (size_t)b * max_ctx * KB, (uint32_t)n_valid * KB);
+  // this workgroup's compact keys (tokens past t_end read as zero)
+  const __amdgpu_buffer_rsrc_t kres = buffer_rsrc(kc + ((size_t)b * max_ctx + t_begin) * KB,
+                                                  (uint32_t)(t_end - t_begin) * KB);
   const uint32_t lane_off = (uint32_t)(n * KB + g * LB);
   // this workgroup's score range as a buffer: lanes past t_end store nothing
   const __amdgpu_buffer_rsrc_t sres =
@@ -296,12 +297,13 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
   if (n_steps > 0) {
     v4i buf[R][4];
 #pragma unroll
-    for (int k = 0; k < R - 1; k++) coarse_load4<D>(kres, lane_off, base0 + k * S, buf[k]);
+    for (int k = 0; k < R - 1; k++) coarse_load4<D>(kres, lane_off, base0 - t_begin + k * S, buf[k]);
     int k0 = 0;
     for (; k0 + R <= n_steps; k0 += R) {
 #pragma unroll
       for (int j = 0; j < R; j++) {
-        coarse_load4<D>(kres, lane_off, base0 + (k0 + j + R - 1) * S, buf[(j + R - 1) % R]);
+        coarse_load4<D>(kres, lane_off, base0 - t_begin + (k0 + j + R - 1) * S,
+                        buf[(j + R - 1) % R]);
         __builtin_amdgcn_sched_barrier(0);
         process(base0 + (k0 + j) * S, buf[j]);
       }
