@@ -166,6 +166,10 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
   constexpr int NMF = D / 64;     // MFMAs (K = 64) per head tile
   constexpr int LB = KB / 4;      // bytes per lane per token
   __shared__ uint32_t lhist[kCoarseBins];
+  // the workgroup's scores, kept here and written out once at the end: a
+  // 4-byte store per lane and step, interleaved with the key stream, costs
+  // the key reads far more than one burst of whole 16-byte pieces
+  __shared__ __attribute__((aligned(16))) int32_t lsc[kCoarseTokPerWG];
 
   const int b = blockIdx.y;
   const int n_valid = clamp_ctx(ctx_len, b, max_ctx);
@@ -223,9 +227,6 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
   const __amdgpu_buffer_rsrc_t kres = buffer_rsrc(kc + ((size_t)b * max_ctx + t_begin) * KB,
                                                   (uint32_t)(t_end - t_begin) * KB);
   const uint32_t lane_off = (uint32_t)(n * KB + g * LB);
-  // this workgroup's score range as a buffer: lanes past t_end store nothing
-  const __amdgpu_buffer_rsrc_t sres =
-      buffer_rsrc(scores + (size_t)b * max_ctx + t_begin, 4u * (uint32_t)(t_end - t_begin));
 
   // One 64-token step: all MFMAs first (independent accumulators), then the
   // epilogue, so MFMA latency overlaps the VALU work of earlier tiles.
@@ -277,8 +278,10 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
     const int32_t score = (int32_t)reduce_scatter4((uint32_t)part[0], (uint32_t)part[1],
                                                    (uint32_t)part[2], (uint32_t)part[3]);
     const int t = base + l;
-    // no branch: the buffer drops stores past t_end, and those lanes add 0
-    __builtin_amdgcn_raw_buffer_store_b32(score, sres, 4 * (t - t_begin), 0, 0);
+    // no branch: lanes past t_end land on slots that are never written out
+    // (or on the last slot, clamped, when the range ends in mid-step, which
+    // is then past t_end too), and they add 0 to the histogram
+    lsc[min(t - t_begin, kCoarseTokPerWG - 1)] = score;
     atomicAdd(&lhist[coarse_bucket(score)], t < t_end ? 1u : 0u);
   };
 
@@ -313,6 +316,15 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
       if (k0 + j < n_steps) process(base0 + (k0 + j) * S, buf[j]);
   }
   __syncthreads();
+  {
+    // the scores: whole 16-byte pieces where the row is 16-byte aligned (it
+    // is unless max_ctx is not a multiple of 4), then the rest one by one
+    const int n_tok = t_end - t_begin;
+    int32_t* sb = scores + (size_t)b * max_ctx + t_begin;
+    const int n4 = ((uintptr_t)sb & 15) == 0 ? n_tok / 4 : 0;
+    for (int i = threadIdx.x; i < n4; i += 256) *(int4*)(sb + 4 * i) = *(const int4*)&lsc[4 * i];
+    for (int j = 4 * n4 + threadIdx.x; j < n_tok; j += 256) sb[j] = lsc[j];
+  }
   uint32_t* hb = hist + (size_t)b * kCoarseBins;
   for (int i = threadIdx.x; i < kCoarseBins; i += 256) {
     uint32_t c = lhist[i];
