@@ -14,6 +14,12 @@ Prints one JSON line with:
               around that kernel, on every 4th step of the timed region
   stages_us_instrumented  per-stage times from a separate run in which every
               stage is bracketed by events (each adds a few microseconds)
+  graph       the same steps replayed from HIP graphs (one per input replica)
+  mfma_util   int8 TOPS of the coarse scoring (live events) and bf16 TFLOP/s
+              of the attention kernel (instrumented run) against the dense
+              MFMA peaks
+  copy_GBs    a plain 1 GiB device-to-device copy, read + write bytes per
+              second (context for the HBM figures)
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -65,6 +71,55 @@ def load_traffic(workload):
     if t.get("kernel_sha") != profsum.coarse_kernel_sha():
         return None
     return t.get("bytes_per_launch")
+
+
+def copy_bandwidth(nbytes=1 << 30, reps=5):
+    """Read + write bytes per second of a plain device copy (context)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(gbs, 1)
+
+
+def graph_timing(run, n_reps, steps):
+    """The step captured in a HIP graph per input replica, replays timed back
+    to back (the step only enqueues kernels, so it can be captured)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(n_reps):
+            run(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for i in range(n_reps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run(i)
+        graphs.append(g)
+    for i in range(2 * n_reps):
+        graphs[i % n_reps].replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(steps):
+        graphs[i % n_reps].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"ms_per_step": round(ms, 5), "value": round(1000.0 / ms, 2)}
 
 
 def copy_calibration(nbytes):
@@ -306,6 +361,13 @@ def main():
         for s_ in range(ls.STEP_EVENTS - 1):
             stage_ms[s_] += row[s_].elapsed_time(row[s_ + 1]) / n_inst
 
+    # the same steps replayed from HIP graphs (reported beside the eager value)
+    try:
+        graph = graph_timing(run, len(reps), K)
+    except Exception as exc:  # reported, never hidden: the eager value stands
+        graph = {"error": repr(exc)}
+    torch.cuda.synchronize()
+
     ab = algorithmic_bytes(wl, sum(n_miss))
     steps_per_s = 1000.0 / ms_per_step
     coarse_bytes = wl.batch * wl.ctx * wl.idx_dim // 2 + wl.batch * wl.idx_heads * (wl.idx_dim + 1)
@@ -350,7 +412,18 @@ def main():
         "coarse_events_sampled": len(coarse_ev),
         "stages_us_instrumented": {n: round(v * 1000, 2) for n, v in zip(STAGES, stage_ms)},
         "request_layer_steps_per_s": round(steps_per_s * wl.batch, 1),
+        "graph": graph,
     }
+    coarse_ops = 2 * wl.batch * wl.ctx * wl.idx_heads * wl.idx_dim
+    attn_flops = 2 * wl.batch * wl.q_heads * wl.topk * (wl.qk_dim + wl.v_dim)
+    attn_ms = stage_ms[STAGES.index("attention")]
+    result["mfma_util"] = {
+        "coarse_int8_TOPS": round(coarse_ops / (coarse_ms * 1e-3) / 1e12, 1),
+        "coarse_frac_of_5000": round(coarse_ops / (coarse_ms * 1e-3) / 1e12 / 5000.0, 4),
+        "attention_bf16_TFLOPs": round(attn_flops / (attn_ms * 1e-3) / 1e12, 1),
+        "attention_frac_of_2500": round(attn_flops / (attn_ms * 1e-3) / 1e12 / 2500.0, 4),
+    }
+    result["copy_GBs"] = copy_bandwidth()
     if args.copy_calib > 0:
         copy_calibration(args.copy_calib << 20)
     if args.cpu_sample > 0:
