@@ -24,31 +24,50 @@ __global__ __launch_bounds__(256) void k_prefill_ctx(int32_t* __restrict__ ctx, 
 }
 
 // Scores of kPrefillRowsPerWG query rows against every key they may see, as
-// an int8 GEMM on v_mfma_i32_16x16x64_i8: A = one row's query (16 heads per
-// tile, held in VGPRs), B = 16 keys.  Lane (n, g) holds, for k-step mf,
-// dims 32 g + 16 mf .. +15 of head (or key) n: the same dims in A and B, so
-// every MFMA contracts 64 of the 128 dims (D = 64: dims 16 g .. +15).
-// Epilogue per key: max(., 0) times the head weight (24-bit multiply-add),
-// summed over four heads in int32 (< 2^30), then over head tiles in int64,
-// then across the four lane groups with a reduce-scatter that leaves one
-// key per lane.  Each lane buckets its row's score into that row's LDS
-// histogram, the first pass of the selection.  The workgroup owns its rows:
-// kPrefillWaves waves stride over the keys (64 per wave step), the query
-// operands are loaded once, and the rows' histograms are zeroed once and
-// stored whole at the end (no global atomics).  Keys past a row's causal
-// limit are computed with the rest of the tile but neither stored nor
-// counted.  Key loads are clamped to the last key and ping-pong prefetched
-// one workgroup step ahead.
+// an int8 GEMM on v_mfma_i32_16x16x64_i8, and the first half of their top-k
+// selection.  A = one row's query (16 heads per tile, held in VGPRs), B = 16
+// keys.  Lane (n, g) holds, for k-step mf, dims 32 g + 16 mf .. +15 of head
+// (or key) n: the same dims in A and B, so every MFMA contracts 64 of the
+// 128 dims (D = 64: dims 16 g .. +15).  Epilogue per key: max(., 0) times
+// the head weight (24-bit multiply-add), summed over four heads in int32
+// (< 2^30), then over head tiles in int64, then across the four lane groups
+// with a reduce-scatter that leaves one key per lane.
+//
+// The workgroup owns its rows: kPrefillWaves waves stride over the keys (64
+// per wave step) with the query operands loaded once, keys clamped to the
+// last one and ping-pong prefetched one workgroup step ahead.  Each score is
+// bucketed into its row's LDS histogram and only its bucket (2 bytes) is
+// stored -- not the score.  When the keys are done the histogram is
+// complete, so the workgroup does the filter's work itself, row by row:
+//   - the bucket beta where the count from the top crosses K (none when the
+//     row sees at most K keys);
+//   - one pass over the row's stored buckets: keys above beta become bitmap
+//     bits (one wave ballot per 64 keys), keys in beta are appended to the
+//     row's tie list, and every 16384-key chunk's kept count is recorded;
+//   - the exact int64 scores of the ties only, recomputed on the MFMA from
+//     the query operands still in VGPRs;
+//   - the row's counters (tie count, beta, count above beta).
+// The emit kernel of the selection then finishes the row.  Keys past a
+// row's causal limit are computed with the rest of the tile but neither
+// stored nor counted.
 template <int D, int HT>
-__global__ __launch_bounds__(64 * kPrefillWaves) void k_prefill_scores(
+__global__ __launch_bounds__(64 * kPrefillWaves) void k_prefill_select(
     const int8_t* __restrict__ q, const int8_t* __restrict__ w, const int8_t* __restrict__ keys,
-    int64_t* __restrict__ scores, uint32_t* __restrict__ hist, int rows, int first_pos, int H,
-    int max_ctx) {
+    uint16_t* __restrict__ bucket, uint32_t* __restrict__ bitmap, int64_t* __restrict__ tie_s,
+    int32_t* __restrict__ tie_p, uint32_t* __restrict__ ctr, uint32_t* __restrict__ chunk,
+    int rows, int first_pos, int H, int max_ctx, int K, int bitmap_words) {
   constexpr int QR = kPrefillRowsPerWG;
   constexpr int NMF = D / 64;
-  __shared__ uint32_t lhist[QR][kWideBins];
-
   constexpr int NT = 64 * kPrefillWaves;
+  constexpr int NW = kPrefillWaves;
+  constexpr int kPer = (kWideBins + NT - 1) / NT;  // histogram bins per thread
+  constexpr int kChunkIters = kSelectChunkWords * 32 / NT;  // classification steps per chunk
+  __shared__ uint32_t lhist[QR][kWideBins];
+  __shared__ uint32_t scan_sh[NW];
+  __shared__ uint32_t wave_k[NW];
+  __shared__ int sh_beta;
+  __shared__ uint32_t sh_above, sh_ntie;
+
   const int r0 = blockIdx.x * QR;
   int nv[QR];
   int nv_max = 0;
@@ -61,10 +80,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void k_prefill_scores(
 
   for (int i = threadIdx.x; i < QR * kWideBins; i += NT) (&lhist[0][0])[i] = 0;
 
-  const int l = lane_id(), n = l & 15, g = l >> 4;
+  const int tid = threadIdx.x, l = lane_id(), wv = wave_id(), n = l & 15, g = l >> 4;
   const int off = (D == 128) ? 32 * g : 16 * g;
   v4i qa[QR][HT][NMF];
-  int32_t wv[QR][HT][4];
+  int32_t wv4[QR][HT][4];
 #pragma unroll
   for (int r = 0; r < QR; r++) {
     const int row = min(r0 + r, rows - 1);
@@ -83,23 +102,16 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void k_prefill_scores(
       for (int i = 0; i < 4; i++) {
         const int hh = 16 * mt + 4 * g + i;
         const int32_t wr = (int32_t)w[(size_t)row * H + min(hh, H - 1)];
-        wv[r][mt][i] = hh < H ? wr : 0;
+        wv4[r][mt][i] = hh < H ? wr : 0;
       }
     }
   }
   __syncthreads();
 
   const int8_t* kb = keys + off;
-  const int t_last = t_end - 1;
-  auto load4 = [&](int base, v4i (&raw)[4][NMF]) {
-#pragma unroll
-    for (int tt = 0; tt < 4; tt++) {
-      const int t = min(base + 16 * tt + n, t_last);
-#pragma unroll
-      for (int mf = 0; mf < NMF; mf++) raw[tt][mf] = *(const v4i*)(kb + (size_t)t * D + 16 * mf);
-    }
-  };
-  auto process = [&](int base, const v4i (&raw)[4][NMF]) {
+  // scores of 64 keys (lane l: key 16 (l / 16) + l % 16 of the four tiles
+  // after the reduce-scatter) for both rows; raw[tt] holds tile tt's keys
+  auto scores64 = [&](const v4i (&raw)[4][NMF], int64_t (&sc)[QR]) {
     int64_t part[QR][4];
 #pragma unroll
     for (int tt = 0; tt < 4; tt++) {
@@ -126,50 +138,167 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void k_prefill_scores(
         for (int mt = 0; mt < HT; mt++) {
           int32_t s4 = 0;
 #pragma unroll
-          for (int i = 0; i < 4; i++) s4 += __mul24(wv[r][mt][i], max(acc[r][mt][i], 0));
+          for (int i = 0; i < 4; i++) s4 += __mul24(wv4[r][mt][i], max(acc[r][mt][i], 0));
           s += (int64_t)s4;
         }
         part[r][tt] = s;
       }
     }
+#pragma unroll
+    for (int r = 0; r < QR; r++)
+      sc[r] = (int64_t)reduce_scatter4((uint64_t)part[r][0], (uint64_t)part[r][1],
+                                       (uint64_t)part[r][2], (uint64_t)part[r][3]);
+  };
+
+  // ---- scores of every key: buckets stored, histograms in LDS
+  const int t_last = t_end - 1;
+  auto load4 = [&](int base, v4i (&raw)[4][NMF]) {
+#pragma unroll
+    for (int tt = 0; tt < 4; tt++) {
+      const int t = min(base + 16 * tt + n, t_last);
+#pragma unroll
+      for (int mf = 0; mf < NMF; mf++) raw[tt][mf] = *(const v4i*)(kb + (size_t)t * D + 16 * mf);
+    }
+  };
+  auto process = [&](int base, const v4i (&raw)[4][NMF]) {
+    int64_t sc[QR];
+    scores64(raw, sc);
     const int t = base + l;
 #pragma unroll
     for (int r = 0; r < QR; r++) {
-      // reduce-scatter over the four lane groups: lane (n, g) ends with tile g
-      const int64_t score = (int64_t)reduce_scatter4((uint64_t)part[r][0], (uint64_t)part[r][1],
-                                                     (uint64_t)part[r][2], (uint64_t)part[r][3]);
       if (t < nv[r]) {
-        scores[(size_t)(r0 + r) * max_ctx + t] = score;
-        atomicAdd(&lhist[r][wide_bucket(score)], 1u);
+        const uint32_t bk = wide_bucket(sc[r]);
+        bucket[(size_t)(r0 + r) * max_ctx + t] = (uint16_t)bk;
+        atomicAdd(&lhist[r][bk], 1u);
       }
     }
   };
-
   constexpr int S = 64 * kPrefillWaves;  // keys per workgroup step
-  int base = __builtin_amdgcn_readfirstlane(wave_id() * 64);
-  if (base < t_end) {
-    v4i bufA[4][NMF], bufB[4][NMF];
-    load4(base, bufA);
-    while (true) {
-      load4(base + S, bufB);
-      __builtin_amdgcn_sched_barrier(0);
-      process(base, bufA);
-      base += S;
-      if (base >= t_end) break;
-      load4(base + S, bufA);
-      __builtin_amdgcn_sched_barrier(0);
-      process(base, bufB);
-      base += S;
-      if (base >= t_end) break;
+  {
+    int base = __builtin_amdgcn_readfirstlane(wv * 64);
+    if (base < t_end) {
+      v4i bufA[4][NMF], bufB[4][NMF];
+      load4(base, bufA);
+      while (true) {
+        load4(base + S, bufB);
+        __builtin_amdgcn_sched_barrier(0);
+        process(base, bufA);
+        base += S;
+        if (base >= t_end) break;
+        load4(base + S, bufA);
+        __builtin_amdgcn_sched_barrier(0);
+        process(base, bufB);
+        base += S;
+        if (base >= t_end) break;
+      }
     }
   }
-  __syncthreads();
-  // the rows' histograms are complete: store them whole
+  __syncthreads();  // every bucket stored, the histograms complete
+
+  // ---- the filter, row by row (r is a compile-time index: qa[r] stays in
+  // registers)
+  const int n_chunks = select_chunks(bitmap_words);
 #pragma unroll
   for (int r = 0; r < QR; r++) {
-    if (r0 + r >= rows) continue;
-    uint32_t* hb = hist + (size_t)(r0 + r) * kWideBins;
-    for (int i = threadIdx.x; i < kWideBins; i += NT) hb[i] = lhist[r][i];
+    if (r0 + r >= rows) continue;  // workgroup-uniform
+    const int row = r0 + r, nvr = nv[r];
+    uint32_t* cr = ctr + (size_t)kCtrStride * row;
+    if (tid == 0) {
+      sh_beta = -1;
+      sh_above = 0;
+      sh_ntie = 0;
+    }
+    // beta: thread tid holds bins kPer (NT - 1 - tid) .. +kPer-1 (thread 0
+    // the top ones), an exclusive scan gives the count above each segment
+    const int seg = NT - 1 - tid;
+    uint32_t hc[kPer];
+    uint32_t s = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; k++) {
+      const int bin = seg * kPer + k;
+      hc[k] = bin < kWideBins ? lhist[r][bin] : 0u;
+      s += hc[k];
+    }
+    uint32_t tot;
+    const uint32_t above_seg = block_excl_scan<NT>(s, scan_sh, &tot);  // (barriers)
+    if (nvr > K && above_seg < (uint32_t)K && (uint32_t)K <= above_seg + s) {
+      uint32_t run = above_seg;
+#pragma unroll
+      for (int k = kPer - 1; k >= 0; k--) {
+        if (run < (uint32_t)K && run + hc[k] >= (uint32_t)K) {
+          sh_beta = seg * kPer + k;
+          sh_above = run;
+        }
+        run += hc[k];
+      }
+    }
+    __syncthreads();
+    const int beta = sh_beta;  // -1: every valid key is kept
+
+    // one pass over the row's buckets: bitmap words, tie list, chunk counts
+    const uint16_t* bb = bucket + (size_t)row * max_ctx;
+    uint32_t* bm = bitmap + (size_t)row * bitmap_words;
+    int32_t* tp = tie_p + (size_t)row * max_ctx;
+    for (int ck = 0; ck < n_chunks; ck++) {
+      uint32_t wk = 0;  // this wave's kept keys in the chunk (wave-uniform)
+      uint16_t bv[kChunkIters];
+#pragma unroll
+      for (int it = 0; it < kChunkIters; it++) {
+        const int t = (ck * kChunkIters + it) * NT + wv * 64 + l;
+        bv[it] = bb[min(t, max_ctx - 1)];  // unconditional (clamped), selected below
+      }
+#pragma unroll
+      for (int it = 0; it < kChunkIters; it++) {
+        const int base = (ck * kChunkIters + it) * NT + wv * 64;
+        const int t = base + l;
+        const bool valid = t < nvr;
+        const bool keep_f = valid && (beta < 0 || (int)bv[it] > beta);
+        const bool tie_f = valid && beta >= 0 && (int)bv[it] == beta;
+        const uint64_t mk = __ballot(keep_f);
+        const uint64_t mt = __ballot(tie_f);
+        if (l == 0 && base / 32 < bitmap_words)
+          *(uint2*)&bm[base / 32] = make_uint2((uint32_t)mk, (uint32_t)(mk >> 32));
+        if (mt) {  // wave-uniform
+          uint32_t first = 0;
+          if (l == 0) first = atomicAdd(&sh_ntie, (uint32_t)__popcll(mt));
+          const uint32_t idx = wave_read(first, 0) + lane_rank(mt);
+          if (tie_f) tp[idx] = t;  // idx < nvr <= max_ctx
+        }
+        wk += (uint32_t)__popcll(mk);
+      }
+      if (l == 0) wave_k[wv] = wk;
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t k = 0;
+#pragma unroll
+        for (int i = 0; i < NW; i++) k += wave_k[i];
+        chunk[(size_t)row * n_chunks + ck] = k;
+      }
+      __syncthreads();
+    }
+    const uint32_t n_tie = sh_ntie;  // (the last barrier above made it final)
+
+    // exact scores of the ties: 64 per wave step, gathered keys
+    int64_t* ts = tie_s + (size_t)row * max_ctx;
+    for (int jb = wv * 64; jb < (int)n_tie; jb += NT) {
+      v4i raw[4][NMF];
+#pragma unroll
+      for (int tt = 0; tt < 4; tt++) {
+        const int p = tp[min(jb + 16 * tt + n, (int)n_tie - 1)];
+#pragma unroll
+        for (int mf = 0; mf < NMF; mf++)
+          raw[tt][mf] = *(const v4i*)(kb + (size_t)p * D + 16 * mf);
+      }
+      int64_t sc[QR];
+      scores64(raw, sc);
+      if (jb + l < (int)n_tie) ts[jb + l] = sc[r];
+    }
+    if (tid == 0) {
+      cr[kCtrTies] = n_tie;
+      cr[kCtrBeta] = (uint32_t)beta;
+      cr[kCtrAbove] = sh_above;
+    }
+    __syncthreads();  // the LDS counters are reused by the next row
   }
 }
 
@@ -183,8 +312,9 @@ hipError_t launch_prefill_block(const int8_t* q, const int8_t* w, const int8_t* 
   dim3 grid((rows + kPrefillRowsPerWG - 1) / kPrefillRowsPerWG);
   const int HT = (H + 15) / 16;
 #define LS_PREFILL(DD, TT)                                                                  \
-  hipLaunchKernelGGL((k_prefill_scores<DD, TT>), grid, dim3(64 * kPrefillWaves), 0, st, q, w, \
-                     keys, ws.scores, ws.hist, rows, first_pos, H, max_ctx)
+  hipLaunchKernelGGL((k_prefill_select<DD, TT>), grid, dim3(64 * kPrefillWaves), 0, st, q, w, \
+                     keys, ws.bucket, ws.bitmap, ws.tie_s, ws.tie_p, ws.ctr, ws.chunk, rows,  \
+                     first_pos, H, max_ctx, K, ws.bitmap_words)
   if (D == 128) {
     if (HT == 1) LS_PREFILL(128, 1); else if (HT == 2) LS_PREFILL(128, 2);
     else if (HT == 3) LS_PREFILL(128, 3); else LS_PREFILL(128, 4);
@@ -195,7 +325,7 @@ hipError_t launch_prefill_block(const int8_t* q, const int8_t* w, const int8_t* 
 #undef LS_PREFILL
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_wide_select(ctx, ws, topk_out, rows, max_ctx, K, st);
+  return launch_wide_emit(ctx, ws, topk_out, rows, max_ctx, K, st);
 }
 
 }  // namespace ls

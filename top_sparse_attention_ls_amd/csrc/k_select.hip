@@ -38,9 +38,6 @@ constexpr int kFilterThreads = 512;
 constexpr int kFilterIters = 32;
 constexpr int kFilterChunk = kFilterThreads * kFilterIters;  // 16384 positions
 constexpr int kFilterWaveTies = 512;
-// ctr words of a request: tie count, beta, count above beta (word 3: emit
-// workgroups done, kCtrDone below)
-constexpr int kCtrTies = 0, kCtrBeta = 1, kCtrAbove = 2;
 
 template <class S>
 __global__ __launch_bounds__(kFilterThreads) void k_topc_filter(
@@ -168,7 +165,6 @@ __global__ __launch_bounds__(kFilterThreads) void k_topc_filter(
 }
 
 constexpr int kEmitThreads = 512;
-constexpr int kCtrDone = 3;  // ctr word: emit workgroups of the request done
 static_assert(kFilterChunk / 32 == kSelectChunkWords && kSelectChunkWords == kEmitThreads,
               "one filter and one emit workgroup per chunk, one bitmap word per emit thread");
 
@@ -352,6 +348,20 @@ __global__ __launch_bounds__(kEmitThreads) void k_topc_emit(
 }
 
 template <class S>
+hipError_t launch_emit(const int32_t* ctx_len, const SelectWS<typename S::T>& ws, int32_t* out,
+                       int B, int max_ctx, int C, hipStream_t st) {
+  // one workgroup per chunk while that is needed to fill the GPU; with many
+  // rows, one per row
+  const int n_chunks = select_chunks(ws.bitmap_words);
+  const int cpw = B >= 256 ? n_chunks : 1;
+  const dim3 egrid((n_chunks + cpw - 1) / cpw, B);
+  hipLaunchKernelGGL(k_topc_emit<S>, egrid, dim3(kEmitThreads), 0, st, ctx_len, ws.hist,
+                     ws.bitmap, ws.tie_s, ws.tie_p, ws.ctr, ws.chunk, out, max_ctx, C,
+                     ws.bitmap_words, n_chunks, cpw);
+  return hipGetLastError();
+}
+
+template <class S>
 hipError_t launch_select(const int32_t* ctx_len, const SelectWS<typename S::T>& ws, int32_t* out,
                          int B, int max_ctx, int C, hipStream_t st) {
   dim3 grid(select_chunks(ws.bitmap_words), B);
@@ -360,15 +370,7 @@ hipError_t launch_select(const int32_t* ctx_len, const SelectWS<typename S::T>& 
                      ws.bitmap_words);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // one workgroup per chunk while that is needed to fill the GPU; with many
-  // rows, one per row
-  const int n_chunks = (int)grid.x;
-  const int cpw = B >= 256 ? n_chunks : 1;
-  const dim3 egrid((n_chunks + cpw - 1) / cpw, B);
-  hipLaunchKernelGGL(k_topc_emit<S>, egrid, dim3(kEmitThreads), 0, st, ctx_len, ws.hist,
-                     ws.bitmap, ws.tie_s, ws.tie_p, ws.ctr, ws.chunk, out, max_ctx, C,
-                     ws.bitmap_words, n_chunks, cpw);
-  return hipGetLastError();
+  return launch_emit<S>(ctx_len, ws, out, B, max_ctx, C, st);
 }
 
 hipError_t launch_topc_select(const int32_t* ctx_len, const CoarseWS& ws, int32_t* cand, int B,
@@ -379,6 +381,11 @@ hipError_t launch_topc_select(const int32_t* ctx_len, const CoarseWS& ws, int32_
 hipError_t launch_wide_select(const int32_t* ctx_len, const WideWS& ws, int32_t* out, int B,
                               int max_ctx, int C, hipStream_t st) {
   return launch_select<WideScore>(ctx_len, ws, out, B, max_ctx, C, st);
+}
+
+hipError_t launch_wide_emit(const int32_t* ctx_len, const WideWS& ws, int32_t* out, int B,
+                            int max_ctx, int C, hipStream_t st) {
+  return launch_emit<WideScore>(ctx_len, ws, out, B, max_ctx, C, st);
 }
 
 }  // namespace ls

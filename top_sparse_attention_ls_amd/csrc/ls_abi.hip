@@ -133,6 +133,7 @@ void carve_coarse(Carve& c, const ls_idx_desc* d, ls::CoarseWS* ws) {
   w.bitmap_words = bitmap_words(d->max_ctx);
   w.bitmap = c.take<uint32_t>(B * w.bitmap_words);
   w.chunk = c.take<uint32_t>(B * ls::select_chunks(w.bitmap_words));
+  w.bucket = nullptr;
   w.tie_s = c.take<int32_t>(B * L);
   w.tie_p = c.take<int32_t>(B * L);
   if (ws) *ws = w;
@@ -145,7 +146,8 @@ void carve_prefill(Carve& c, const ls_prefill_desc* d, ls::WideWS* ws, int32_t**
   ls::WideWS w;
   w.hist = c.take<uint32_t>(R * ls::kWideBins);
   w.ctr = c.take<uint32_t>(R * ls::kCtrStride);
-  w.scores = c.take<int64_t>(R * L);
+  w.scores = nullptr;  // the scoring kernel keeps only each score's bucket
+  w.bucket = c.take<uint16_t>(R * L);
   w.bitmap_words = bitmap_words(d->max_ctx);
   w.bitmap = c.take<uint32_t>(R * w.bitmap_words);
   w.chunk = c.take<uint32_t>(R * ls::select_chunks(w.bitmap_words));

@@ -34,12 +34,16 @@ struct SelectWS {
   int32_t* tie_p;      // [B, max_ctx]
   uint32_t* ctr;       // [B, kCtrStride] tie count (word 0); zero between calls
   uint32_t* chunk;     // [B, n_chunks] kept count of each 16384-position chunk
+  uint16_t* bucket;    // [B, max_ctx] bucket of every score (prefill rows only)
   int bitmap_words;
 };
 // Chunks of 16384 positions (512 bitmap words) the selection works in: one
 // filter and one emit workgroup each.
 constexpr int kSelectChunkWords = 512;
-inline int select_chunks(int bitmap_words) {
+// ctr words of a request: tie count, beta, count above beta, emit workgroups
+// done (the tie count and the last word read zero between calls)
+constexpr int kCtrTies = 0, kCtrBeta = 1, kCtrAbove = 2, kCtrDone = 3;
+__host__ __device__ inline int select_chunks(int bitmap_words) {
   return (bitmap_words + kSelectChunkWords - 1) / kSelectChunkWords;
 }
 
@@ -73,6 +77,11 @@ hipError_t launch_prefill_block(const int8_t* q, const int8_t* w, const int8_t* 
 // The same selection over int64 scores (prefill rows).
 hipError_t launch_wide_select(const int32_t* ctx_len, const WideWS& ws, int32_t* out, int B,
                               int max_ctx, int C, hipStream_t st);
+
+// Its second kernel alone, for rows whose bitmap, tie list, chunk counts and
+// counters were written by the scoring kernel itself.
+hipError_t launch_wide_emit(const int32_t* ctx_len, const WideWS& ws, int32_t* out, int B,
+                            int max_ctx, int C, hipStream_t st);
 
 // Refine + top-k; with pos2slot != nullptr also the hot-buffer resolve
 // (rows, n_miss, miss list in ws.miss_pos).
