@@ -17,6 +17,16 @@ namespace ls {
 constexpr int kPrefillRowsPerWG = 2;  // query rows sharing each key tile
 constexpr int kPrefillWaves = 8;      // waves of a workgroup, all on its rows
 
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
+// operations, not for its global loads in flight (which __syncthreads()
+// would drain).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __global__ __launch_bounds__(256) void k_prefill_ctx(int32_t* __restrict__ ctx, int rows,
                                                       int first_pos, int max_ctx) {
   const int i = blockIdx.x * 256 + threadIdx.x;
@@ -66,7 +76,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void k_prefill_select(
   __shared__ uint32_t scan_sh[NW];
   __shared__ uint32_t wave_k[NW];
   __shared__ int sh_beta;
-  __shared__ uint32_t sh_above, sh_ntie;
+  __shared__ uint32_t sh_above;
+  __shared__ uint32_t sh_ntie_r[QR];
 
   const int r0 = blockIdx.x * QR;
   int nv[QR];
@@ -195,21 +206,19 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void k_prefill_select(
   }
   __syncthreads();  // every bucket stored, the histograms complete
 
-  // ---- the filter, row by row (r is a compile-time index: qa[r] stays in
-  // registers)
+  // ---- the filter.  Beta of both rows first.
   const int n_chunks = select_chunks(bitmap_words);
+  const bool counts = emit_chunks_per_run(rows, n_chunks) == 1;  // the emit reads them
+  int beta[QR];
+  uint32_t above[QR];
 #pragma unroll
   for (int r = 0; r < QR; r++) {
-    if (r0 + r >= rows) continue;  // workgroup-uniform
-    const int row = r0 + r, nvr = nv[r];
-    uint32_t* cr = ctr + (size_t)kCtrStride * row;
     if (tid == 0) {
       sh_beta = -1;
       sh_above = 0;
-      sh_ntie = 0;
     }
-    // beta: thread tid holds bins kPer (NT - 1 - tid) .. +kPer-1 (thread 0
-    // the top ones), an exclusive scan gives the count above each segment
+    // thread tid holds bins kPer (NT - 1 - tid) .. +kPer-1 (thread 0 the top
+    // ones); an exclusive scan gives the count above each segment
     const int seg = NT - 1 - tid;
     uint32_t hc[kPer];
     uint32_t s = 0;
@@ -221,7 +230,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void k_prefill_select(
     }
     uint32_t tot;
     const uint32_t above_seg = block_excl_scan<NT>(s, scan_sh, &tot);  // (barriers)
-    if (nvr > K && above_seg < (uint32_t)K && (uint32_t)K <= above_seg + s) {
+    if (nv[r] > K && above_seg < (uint32_t)K && (uint32_t)K <= above_seg + s) {
       uint32_t run = above_seg;
 #pragma unroll
       for (int k = kPer - 1; k >= 0; k--) {
@@ -233,52 +242,89 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void k_prefill_select(
       }
     }
     __syncthreads();
-    const int beta = sh_beta;  // -1: every valid key is kept
+    beta[r] = sh_beta;  // -1: every valid key is kept
+    above[r] = sh_above;
+    __syncthreads();  // sh_beta / sh_above are reused
+  }
+  if (tid < QR) sh_ntie_r[tid] = 0;
+  __syncthreads();
 
-    // one pass over the row's buckets: bitmap words, tie list, chunk counts
-    const uint16_t* bb = bucket + (size_t)row * max_ctx;
-    uint32_t* bm = bitmap + (size_t)row * bitmap_words;
-    int32_t* tp = tie_p + (size_t)row * max_ctx;
-    for (int ck = 0; ck < n_chunks; ck++) {
-      uint32_t wk = 0;  // this wave's kept keys in the chunk (wave-uniform)
-      uint16_t bv[kChunkIters];
+  // One pass over both rows' buckets, a chunk (16384 keys) at a time with the
+  // next chunk's buckets in flight: bitmap words (one ballot per 64 keys),
+  // tie lists, and -- when the emit reads them -- chunk counts (reduced
+  // through LDS behind a barrier that does not wait for the loads in flight).
+  auto load_chunk = [&](int ck, uint16_t (&bv)[QR][kChunkIters]) {
+#pragma unroll
+    for (int r = 0; r < QR; r++) {
+      const uint16_t* bb = bucket + (size_t)min(r0 + r, rows - 1) * max_ctx;
 #pragma unroll
       for (int it = 0; it < kChunkIters; it++) {
         const int t = (ck * kChunkIters + it) * NT + wv * 64 + l;
-        bv[it] = bb[min(t, max_ctx - 1)];  // unconditional (clamped), selected below
+        bv[r][it] = bb[min(t, max_ctx - 1)];  // unconditional (clamped), selected below
       }
+    }
+  };
+  auto classify = [&](int ck, const uint16_t (&bv)[QR][kChunkIters]) {
+#pragma unroll
+    for (int r = 0; r < QR; r++) {
+      if (r0 + r >= rows) continue;  // workgroup-uniform
+      const int row = r0 + r;
+      uint32_t* bm = bitmap + (size_t)row * bitmap_words;
+      int32_t* tp = tie_p + (size_t)row * max_ctx;
+      uint32_t wk = 0;  // this wave's kept keys in the chunk (wave-uniform)
 #pragma unroll
       for (int it = 0; it < kChunkIters; it++) {
         const int base = (ck * kChunkIters + it) * NT + wv * 64;
         const int t = base + l;
-        const bool valid = t < nvr;
-        const bool keep_f = valid && (beta < 0 || (int)bv[it] > beta);
-        const bool tie_f = valid && beta >= 0 && (int)bv[it] == beta;
+        const bool valid = t < nv[r];
+        const bool keep_f = valid && (beta[r] < 0 || (int)bv[r][it] > beta[r]);
+        const bool tie_f = valid && beta[r] >= 0 && (int)bv[r][it] == beta[r];
         const uint64_t mk = __ballot(keep_f);
         const uint64_t mt = __ballot(tie_f);
         if (l == 0 && base / 32 < bitmap_words)
           *(uint2*)&bm[base / 32] = make_uint2((uint32_t)mk, (uint32_t)(mk >> 32));
         if (mt) {  // wave-uniform
           uint32_t first = 0;
-          if (l == 0) first = atomicAdd(&sh_ntie, (uint32_t)__popcll(mt));
+          if (l == 0) first = atomicAdd(&sh_ntie_r[r], (uint32_t)__popcll(mt));
           const uint32_t idx = wave_read(first, 0) + lane_rank(mt);
-          if (tie_f) tp[idx] = t;  // idx < nvr <= max_ctx
+          if (tie_f) tp[idx] = t;  // idx < nv[r] <= max_ctx
         }
         wk += (uint32_t)__popcll(mk);
       }
-      if (l == 0) wave_k[wv] = wk;
-      __syncthreads();
-      if (tid == 0) {
-        uint32_t k = 0;
+      if (counts) {
+        if (l == 0) wave_k[wv] = wk;
+        lds_barrier();
+        if (tid == 0) {
+          uint32_t k = 0;
 #pragma unroll
-        for (int i = 0; i < NW; i++) k += wave_k[i];
-        chunk[(size_t)row * n_chunks + ck] = k;
+          for (int i = 0; i < NW; i++) k += wave_k[i];
+          chunk[(size_t)row * n_chunks + ck] = k;
+        }
+        lds_barrier();
       }
-      __syncthreads();
     }
-    const uint32_t n_tie = sh_ntie;  // (the last barrier above made it final)
+  };
+  {
+    uint16_t bvA[QR][kChunkIters], bvB[QR][kChunkIters];
+    load_chunk(0, bvA);
+    for (int ck = 0; ck < n_chunks; ck += 2) {
+      if (ck + 1 < n_chunks) load_chunk(ck + 1, bvB);  // workgroup-uniform
+      classify(ck, bvA);
+      if (ck + 1 >= n_chunks) break;
+      if (ck + 2 < n_chunks) load_chunk(ck + 2, bvA);
+      classify(ck + 1, bvB);
+    }
+  }
+  __syncthreads();  // tie lists and counts complete (and visible to every wave)
 
-    // exact scores of the ties: 64 per wave step, gathered keys
+  // exact scores of the ties, 64 per wave step from gathered keys; then the
+  // rows' counters
+#pragma unroll
+  for (int r = 0; r < QR; r++) {
+    if (r0 + r >= rows) continue;  // workgroup-uniform
+    const int row = r0 + r;
+    const uint32_t n_tie = sh_ntie_r[r];
+    const int32_t* tp = tie_p + (size_t)row * max_ctx;
     int64_t* ts = tie_s + (size_t)row * max_ctx;
     for (int jb = wv * 64; jb < (int)n_tie; jb += NT) {
       v4i raw[4][NMF];
@@ -294,11 +340,11 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void k_prefill_select(
       if (jb + l < (int)n_tie) ts[jb + l] = sc[r];
     }
     if (tid == 0) {
+      uint32_t* cr = ctr + (size_t)kCtrStride * row;
       cr[kCtrTies] = n_tie;
-      cr[kCtrBeta] = (uint32_t)beta;
-      cr[kCtrAbove] = sh_above;
+      cr[kCtrBeta] = (uint32_t)beta[r];
+      cr[kCtrAbove] = above[r];
     }
-    __syncthreads();  // the LDS counters are reused by the next row
   }
 }
 

@@ -350,10 +350,8 @@ __global__ __launch_bounds__(kEmitThreads) void k_topc_emit(
 template <class S>
 hipError_t launch_emit(const int32_t* ctx_len, const SelectWS<typename S::T>& ws, int32_t* out,
                        int B, int max_ctx, int C, hipStream_t st) {
-  // one workgroup per chunk while that is needed to fill the GPU; with many
-  // rows, one per row
   const int n_chunks = select_chunks(ws.bitmap_words);
-  const int cpw = B >= 256 ? n_chunks : 1;
+  const int cpw = emit_chunks_per_run(B, n_chunks);
   const dim3 egrid((n_chunks + cpw - 1) / cpw, B);
   hipLaunchKernelGGL(k_topc_emit<S>, egrid, dim3(kEmitThreads), 0, st, ctx_len, ws.hist,
                      ws.bitmap, ws.tie_s, ws.tie_p, ws.ctr, ws.chunk, out, max_ctx, C,

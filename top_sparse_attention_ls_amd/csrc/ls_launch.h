@@ -46,6 +46,11 @@ constexpr int kCtrTies = 0, kCtrBeta = 1, kCtrAbove = 2, kCtrDone = 3;
 __host__ __device__ inline int select_chunks(int bitmap_words) {
   return (bitmap_words + kSelectChunkWords - 1) / kSelectChunkWords;
 }
+// Chunks each emit workgroup takes: one while that is needed to fill the GPU,
+// all of a row's with many rows (then no chunk counts are read).
+__host__ __device__ inline int emit_chunks_per_run(int rows, int n_chunks) {
+  return rows >= 256 ? n_chunks : 1;
+}
 
 using CoarseWS = SelectWS<int32_t>;  // coarse scores, kCoarseBins buckets
 using WideWS = SelectWS<int64_t>;    // int64 scores, 7552 buckets
