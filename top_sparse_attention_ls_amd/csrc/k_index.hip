@@ -121,14 +121,6 @@ __device__ __forceinline__ void coarse_q_operands(const int8_t* qh, int g, v4i* 
   }
 }
 
-// 24-bit signed multiply-add, c + a * b modulo 2^32 (one v_mad_i32_i24; the
-// compiler would otherwise split the chain into multiplies and 3-way adds).
-__device__ __forceinline__ uint32_t mad_i24(int32_t a, int32_t b, uint32_t c) {
-  uint32_t d;
-  asm("v_mad_i32_i24 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
-  return d;
-}
-
 // The four 16-token tiles of one 64-token step: lane (n, g) loads token
 // base + 16 tt + n (counted from the workgroup's first token) at byte g * LB
 // of its row, through a buffer resource over the workgroup's own keys

@@ -39,9 +39,10 @@ __global__ __launch_bounds__(256) void k_prefill_ctx(int32_t* __restrict__ ctx, 
 // keys.  Lane (n, g) holds, for k-step mf, dims 32 g + 16 mf .. +15 of head
 // (or key) n: the same dims in A and B, so every MFMA contracts 64 of the
 // 128 dims (D = 64: dims 16 g .. +15).  Epilogue per key: max(., 0) times
-// the head weight (24-bit multiply-add), summed over four heads in int32
-// (< 2^30), then over head tiles in int64, then across the four lane groups
-// with a reduce-scatter that leaves one key per lane.
+// the head weight (24-bit multiply-add), summed over eight heads in 32 bits
+// (exact: each term is at most 2^28 in magnitude), then in int64, then
+// across the four lane groups with a reduce-scatter that leaves one key per
+// lane.
 //
 // The workgroup owns its rows: kPrefillWaves waves stride over the keys (64
 // per wave step) with the query operands loaded once, keys clamped to the
@@ -144,13 +145,17 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void k_prefill_select(
       }
 #pragma unroll
       for (int r = 0; r < QR; r++) {
+        // eight heads at a time in 32 bits (|w * relu(dot)| <= 2^28, so a sum
+        // of eight lies in [-2^31, 2^31)), then widened
         int64_t s = 0;
 #pragma unroll
-        for (int mt = 0; mt < HT; mt++) {
-          int32_t s4 = 0;
+        for (int m0 = 0; m0 < HT; m0 += 2) {
+          uint32_t s8 = 0;
 #pragma unroll
-          for (int i = 0; i < 4; i++) s4 += __mul24(wv4[r][mt][i], max(acc[r][mt][i], 0));
-          s += (int64_t)s4;
+          for (int mt = m0; mt < m0 + 2 && mt < HT; mt++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) s8 = mad_i24(wv4[r][mt][i], max(acc[r][mt][i], 0), s8);
+          s += (int64_t)(int32_t)s8;
         }
         part[r][tt] = s;
       }

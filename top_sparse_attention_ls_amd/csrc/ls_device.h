@@ -201,6 +201,14 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// 24-bit signed multiply-add, c + a * b modulo 2^32 (one v_mad_i32_i24; the
+// compiler would otherwise split the chain into multiplies and 3-way adds).
+__device__ __forceinline__ uint32_t mad_i24(int32_t a, int32_t b, uint32_t c) {
+  uint32_t d;
+  asm("v_mad_i32_i24 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
 // Raw buffer resource over [p, p + bytes) (stride 0, gfx9 dword-3 format
 // word): the hardware range check drops stores at offsets beyond `bytes` and
 // returns 0 for such loads, so edge lanes need no branch.
