@@ -11,7 +11,7 @@ Prints one JSON line with:
   roofline    the dominant kernel (coarse scoring) against the 8 TB/s HBM peak:
               algorithmic bytes per launch / its average duration, measured
               with two HIP events the library records on the launch stream
-              around that kernel, on every 4th step of the timed region
+              around that kernel, on every 8th step of the timed region
   stages_us_instrumented  per-stage times from a separate run in which every
               stage is bracketed by events (each adds a few microseconds)
   graph       the same steps replayed from HIP graphs (one per input replica)
@@ -325,7 +325,7 @@ def main():
     # library also records two events around the coarse kernel (an event
     # costs the stream a few microseconds, so only the measured kernel is
     # bracketed, and only on a sample of the steps)
-    SAMPLE = 4
+    SAMPLE = 8
     coarse_ev = {}
     for i in range(0, K, SAMPLE):
         coarse_ev[i] = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
