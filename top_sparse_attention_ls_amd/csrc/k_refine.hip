@@ -125,8 +125,9 @@ __global__ __launch_bounds__(256) void k_refine(const int8_t* __restrict__ q,
 
 // ---------------------------------------------- top-k + resolve (A4, A5) ----
 //
-// One 1024-thread workgroup per request keeps min(K, valid) candidates under
-// (fine score desc, position asc) and emits them in candidate order, i.e.
+// 1024-thread workgroups (k_topk_hist: one per 1024-candidate slice of a
+// request; k_topk: one per request) keep min(K, valid) candidates under
+// (fine score desc, position asc) and emit them in candidate order, i.e.
 // ascending position.  With a slot table the emission also resolves each
 // kept token against the hot buffer: rows[j] = its slot if resident, else
 // hot_slots + (its rank among the misses); the misses' positions go to

@@ -74,7 +74,8 @@ hipError_t launch_topc_select(const int32_t* ctx_len, const CoarseWS& ws, int32_
                               int max_ctx, int C, hipStream_t st);
 
 // Prefill indexer for `rows` query rows at absolute positions first_pos ..:
-// scores into ws, row lengths into ctx [rows], top-K into topk_out [rows, K].
+// score buckets, bitmap and tie lists into ws, row lengths into ctx [rows],
+// top-K into topk_out [rows, K].
 hipError_t launch_prefill_block(const int8_t* q, const int8_t* w, const int8_t* keys,
                                 const WideWS& ws, int32_t* ctx, int32_t* topk_out, int rows,
                                 int first_pos, int H, int D, int max_ctx, int K, hipStream_t st);
