@@ -123,42 +123,58 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void k_prefill_select(
   const int8_t* kb = keys + off;
   // scores of 64 keys (lane l: key 16 (l / 16) + l % 16 of the four tiles
   // after the reduce-scatter) for both rows; raw[tt] holds tile tt's keys
+  // The tiles are software-pipelined across the two rows: the MFMAs of
+  // (row a, tile t) are issued interleaved with the epilogue of the pair
+  // before it -- one MFMA, then a share of the other row's max /
+  // multiply-adds -- so the matrix core and the VALU work together.  Each
+  // row's accumulators are read by the epilogue before that row's next
+  // MFMAs overwrite them, so the pipeline needs no extra registers.
+  static_assert(QR == 2, "the pipeline alternates two rows");
   auto scores64 = [&](const v4i (&raw)[4][NMF], int64_t (&sc)[QR]) {
+    constexpr int NM = HT * NMF;  // MFMAs per (row, tile)
+    constexpr int NV = 4 * HT;    // epilogue values per lane per (row, tile)
+    v4i acc[QR][HT];
     int64_t part[QR][4];
-#pragma unroll
-    for (int tt = 0; tt < 4; tt++) {
-      v4i acc[QR][HT];
-#pragma unroll
-      for (int r = 0; r < QR; r++)
-#pragma unroll
-        for (int mt = 0; mt < HT; mt++)
-          acc[r][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[r][mt][0], raw[tt][0],
-                                                             v4i{0, 0, 0, 0}, 0, 0, 0);
-      if (NMF == 2) {
-#pragma unroll
-        for (int r = 0; r < QR; r++)
-#pragma unroll
-          for (int mt = 0; mt < HT; mt++)
-            acc[r][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[r][mt][NMF - 1],
-                                                               raw[tt][NMF - 1], acc[r][mt], 0,
-                                                               0, 0);
+    auto mfma_i = [&](int r, int tt, int i) {
+      const int mt = i % HT, mf = i / HT;
+      acc[r][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+          qa[r][mt][mf], raw[tt][mf], mf == 0 ? v4i{0, 0, 0, 0} : acc[r][mt], 0, 0, 0);
+    };
+    // value j of row r's epilogue: eight heads at a time in 32 bits
+    // (|w * relu(dot)| <= 2^28, so a sum of eight lies in [-2^31, 2^31)),
+    // then widened
+    auto epi_j = [&](int r, int j, uint32_t& s8, int64_t& s) {
+      const int mt = j / 4, i = j % 4;
+      s8 = mad_i24(wv4[r][mt][i], max(acc[r][mt][i], 0), s8);
+      if (j % 8 == 7 || j == NV - 1) {
+        s += (int64_t)(int32_t)s8;
+        s8 = 0;
       }
+    };
 #pragma unroll
-      for (int r = 0; r < QR; r++) {
-        // eight heads at a time in 32 bits (|w * relu(dot)| <= 2^28, so a sum
-        // of eight lies in [-2^31, 2^31)), then widened
-        int64_t s = 0;
+    for (int i = 0; i < NM; i++) mfma_i(0, 0, i);
 #pragma unroll
-        for (int m0 = 0; m0 < HT; m0 += 2) {
-          uint32_t s8 = 0;
+    for (int k = 1; k < 2 * 4; k++) {
+      const int ra = k % 2, ta = k / 2;              // MFMAs of this pair
+      const int re = (k - 1) % 2, te = (k - 1) / 2;  // epilogue of the one before
+      uint32_t s8 = 0;
+      int64_t s = 0;
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int mt = m0; mt < m0 + 2 && mt < HT; mt++)
+      for (int i = 0; i < NM; i++) {
+        mfma_i(ra, ta, i);
 #pragma unroll
-            for (int i = 0; i < 4; i++) s8 = mad_i24(wv4[r][mt][i], max(acc[r][mt][i], 0), s8);
-          s += (int64_t)(int32_t)s8;
-        }
-        part[r][tt] = s;
+        for (int j = i * NV / NM; j < (i + 1) * NV / NM; j++) epi_j(re, j, s8, s);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      part[re][te] = s;
+    }
+    {
+      uint32_t s8 = 0;
+      int64_t s = 0;
+#pragma unroll
+      for (int j = 0; j < NV; j++) epi_j(1, j, s8, s);
+      part[1][3] = s;
     }
 #pragma unroll
     for (int r = 0; r < QR; r++)
