@@ -45,8 +45,8 @@ __global__ __launch_bounds__(256) void k_prefill_ctx(int32_t* __restrict__ ctx, 
 // lane.
 //
 // The workgroup owns its rows: kPrefillWaves waves stride over the keys (64
-// per wave step) with the query operands loaded once, keys clamped to the
-// last one and ping-pong prefetched one workgroup step ahead.  Each score is
+// per wave step) with the query operands loaded once, keys ping-pong
+// prefetched one workgroup step ahead.  Each score is
 // bucketed into its row's LDS histogram and only its bucket (2 bytes) is
 // stored -- not the score.  When the keys are done the histogram is
 // complete, so the workgroup does the filter's work itself, row by row:
@@ -183,13 +183,20 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void k_prefill_select(
   };
 
   // ---- scores of every key: buckets stored, histograms in LDS
-  const int t_last = t_end - 1;
+  // keys through a buffer resource over the ones the rows may see: the
+  // tile's key offset is a scalar (soffset), the lane's a constant, and keys
+  // past the end read as zero without a memory access (their scores are
+  // dropped)
+  const __amdgpu_buffer_rsrc_t kres = buffer_rsrc(keys, (uint32_t)t_end * D);
+  const uint32_t lane_off = (uint32_t)(n * D + off);
   auto load4 = [&](int base, v4i (&raw)[4][NMF]) {
 #pragma unroll
     for (int tt = 0; tt < 4; tt++) {
-      const int t = min(base + 16 * tt + n, t_last);
+      const int so = __builtin_amdgcn_readfirstlane((base + 16 * tt) * D);
 #pragma unroll
-      for (int mf = 0; mf < NMF; mf++) raw[tt][mf] = *(const v4i*)(kb + (size_t)t * D + 16 * mf);
+      for (int mf = 0; mf < NMF; mf++)
+        raw[tt][mf] = __builtin_bit_cast(
+            v4i, __builtin_amdgcn_raw_buffer_load_b128(kres, lane_off + 16 * mf, so, 0));
     }
   };
   auto process = [&](int base, const v4i (&raw)[4][NMF]) {
