@@ -140,17 +140,45 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
   const int i_end = min(i_begin + rows_per_split, K);
   const int n_rows = max(i_end - i_begin, 0);
   const int n_tiles = (n_rows + kTileR - 1) / kTileR;
-  // Prologue: the split's row ids (loaded unconditionally, clamped into the
-  // request's list) and the query in one round trip; the row ids staged in
-  // LDS; the first tiles' DMA, which the loop waits for tile by tile.
   const int32_t* rq = rows + (size_t)b * K;
+  const uint16_t* kvb = kv + (size_t)b * rows_per_req * row_stride;
+  // the tile row this lane loads in every DMA instruction, and its chunk parity
+  const int dma_row = (l & 31) ^ (half << 3);
+  // row id at position i of the split, clamped into the request's list
+  // (loads are unconditional; positions past the split are padding)
+  auto rid_at = [&](int i) { return rq[min(i_begin + min(i, max(n_rows - 1, 0)), K - 1)]; };
+  // what a tile position holds: its row, or -1 for padding and ids out of range
+  auto rid_valid = [&](int i, int32_t r) { return (i < n_rows && r >= 0 && r < rows_per_req) ? r : -1; };
+
+  // Tile DMA of tile t, this lane's row being rid (padding loads row 0):
+  // wave w issues instructions k = w, w + NW, ...  (lds_dma16: the waits on it
+  // are the explicit vmcnt waits below)
+  auto issue_dma_row = [&](int t, int32_t rid) {
+    const uint8_t* src = (const uint8_t*)(kvb + (size_t)(rid >= 0 ? rid : 0) * row_stride) +
+                         16 * (2 * w + half);
+    const uint32_t dst = lds_addr(&tiles[t % NBUF][0]) + 1024u * w;
+#pragma unroll
+    for (int j = 0; j < DMA_PER_WAVE; j++) lds_dma16(src + 32 * NW * j, dst + 1024u * NW * j);
+  };
+  auto issue_dma = [&](int t) { issue_dma_row(t, rid_lds[t * kTileR + dma_row]); };
+
+  // Prologue in two round trips.  First each lane's own DMA rows of the
+  // first tiles, whose DMA then starts at once; then the split's row ids (to
+  // be staged in LDS) and the query, which load while that DMA is in flight.
+  {
+    int32_t r0[NBUF - 1];
+#pragma unroll
+    for (int t = 0; t < NBUF - 1; t++) r0[t] = rid_at(t * kTileR + dma_row);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+#pragma unroll
+    for (int t = 0; t < NBUF - 1; t++)
+      if (t < n_tiles) issue_dma_row(t, rid_valid(t * kTileR + dma_row, r0[t]));
+  }
+  __builtin_amdgcn_sched_barrier(0);
   constexpr int kRidIters = (kMaxSplitRows + kTileR + NW * 64 - 1) / (NW * 64);
   int32_t rv[kRidIters];
 #pragma unroll
-  for (int k = 0; k < kRidIters; k++) {
-    const int i = threadIdx.x + k * NW * 64;
-    rv[k] = rq[min(i_begin + min(i, max(n_rows - 1, 0)), K - 1)];
-  }
+  for (int k = 0; k < kRidIters; k++) rv[k] = rid_at(threadIdx.x + k * NW * 64);
   // B operand of S^T = K Q^T: head n, dims 16 ks + 8 half .. +7 (loaded
   // unconditionally from a clamped head, then selected)
   v8bf qB[QK_STEPS];
@@ -162,38 +190,19 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
       qB[ks] = __builtin_bit_cast(v8bf, h_ok ? v : v8u16{0, 0, 0, 0, 0, 0, 0, 0});
     }
   }
-  // Row ids and query have landed before anything else is issued, so the
-  // compiler has no load of its own outstanding in the tile loop (it would
-  // otherwise wait on every iteration, which would also drain the tile DMA
-  // in flight); the loop then waits for each tile's DMA alone.
+  // Everything has landed (the first tiles too) before the loop, so the
+  // compiler has no load of its own outstanding there (it would otherwise
+  // wait on every iteration, which would also drain the tile DMA in flight);
+  // the loop then waits for each tile's DMA alone.
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 #pragma unroll
   for (int k = 0; k < kRidIters; k++) {
     const int i = threadIdx.x + k * NW * 64;
-    // row ids outside the request's rows are padding, like -1
-    const int32_t r = i < n_rows ? rv[k] : -1;
-    if (i < n_tiles * kTileR) rid_lds[i] = (r >= 0 && r < rows_per_req) ? r : -1;
+    if (i < n_tiles * kTileR) rid_lds[i] = rid_valid(i, rv[k]);
   }
   __shared__ int redo;
   if (threadIdx.x == 0) redo = 0;
   __syncthreads();  // row ids staged
-
-  const uint16_t* kvb = kv + (size_t)b * rows_per_req * row_stride;
-  // the tile row this lane loads in every DMA instruction, and its chunk parity
-  const int dma_row = (l & 31) ^ (half << 3);
-
-  // Tile DMA: wave w issues instructions k = w, w + NW, ... (lds_dma16: the
-  // waits on it are the explicit vmcnt waits below)
-  auto issue_dma = [&](int t) {
-    const int32_t rid = rid_lds[t * kTileR + dma_row];
-    const uint8_t* src = (const uint8_t*)(kvb + (size_t)(rid >= 0 ? rid : 0) * row_stride) +
-                         16 * (2 * w + half);
-    const uint32_t dst = lds_addr(&tiles[t % NBUF][0]) + 1024u * w;
-#pragma unroll
-    for (int j = 0; j < DMA_PER_WAVE; j++) lds_dma16(src + 32 * NW * j, dst + 1024u * NW * j);
-  };
-
-  for (int t = 0; t < NBUF - 1 && t < n_tiles; t++) issue_dma(t);
 
   v16f oacc[DT];
   float m_used, l_run, m_seen = -INFINITY;
