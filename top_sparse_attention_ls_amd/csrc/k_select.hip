@@ -4,6 +4,8 @@
 //
 // Method: LeanSparse (arXiv 2611.04671), Abstract -- the coarse pass keeps a
 // candidate set that the original indexer keys then refine.
+#include <type_traits>
+
 #include "ls_device.h"
 #include "ls_select.h"
 #include "ls_launch.h"
@@ -17,27 +19,29 @@ namespace ls {
 // that meet only at the kernel boundary (the emit workgroups also count
 // their arrivals, but only so that the last one clears the tie counter).
 //
-// k_topc_filter (16384 positions per 512-thread workgroup): every lane first
-// issues its loads -- the request's histogram share, then all 32 of its
-// scores (one coalesced dword per lane per wave step, clamped to the row) --
-// so that the threshold search waits only for the histogram.  From the
-// histogram the workgroup finds the bucket beta where the count from the
-// top crosses C.  Tokens in buckets above beta are kept outright: one wave
-// ballot is one 64-bit word of the request's position bitmap.  Tokens in
-// bucket beta are appended to the wave's own LDS tie list (ranks from the
-// ballot, so no atomics in the loop) and the workgroup reserves room in the
-// request's global list with one atomic.  Workgroup 0 also stores beta and
-// the count above it, and every workgroup its chunk's count of positions
-// kept outright, for the emit kernel.
+// k_topc_filter (16384 positions per 1024-thread workgroup): every lane
+// first issues its loads -- the request's histogram share, then all 16 of
+// its scores (wave w covers 1024 consecutive positions, one coalesced dword
+// per lane per wave step, clamped to the row) -- so that the threshold
+// search waits only for the histogram.  From the histogram the workgroup
+// finds the bucket beta where the count from the top crosses C.  Tokens in
+// buckets above beta are kept outright: one wave ballot is one 64-bit word
+// of the request's position bitmap, parked in lane u of a register by step u
+// and stored by the wave in one piece at the end.  Tokens in bucket beta
+// are appended to the wave's own LDS tie list (ranks from the ballot, so no
+// atomics in the loop) and the workgroup reserves room in the request's
+// global list with one atomic.  Workgroup 0 also stores beta and the count
+// above it, and every workgroup its chunk's count of positions kept
+// outright, for the emit kernel.
 //
 // k_topc_emit (one workgroup per filter chunk): resolves the tie list
 // exactly and emits its chunk's kept positions at their place in the
 // request's ascending list (details at the kernel).
 
-constexpr int kFilterThreads = 512;
-constexpr int kFilterIters = 32;
+constexpr int kFilterThreads = 1024;
+constexpr int kFilterIters = 16;
 constexpr int kFilterChunk = kFilterThreads * kFilterIters;  // 16384 positions
-constexpr int kFilterWaveTies = 512;
+constexpr int kFilterWaveTies = 256;
 
 template <class S>
 __global__ __launch_bounds__(kFilterThreads) void k_topc_filter(
@@ -46,8 +50,10 @@ __global__ __launch_bounds__(kFilterThreads) void k_topc_filter(
     typename S::T* __restrict__ tie_s, int32_t* __restrict__ tie_p, uint32_t* __restrict__ ctr,
     uint32_t* __restrict__ chunk, int max_ctx, int C, int bitmap_words) {
   using T = typename S::T;
+  using U = typename std::make_unsigned<T>::type;
   constexpr int NW = kFilterThreads / kWave;
   constexpr int kPer = (S::kBins + kFilterThreads - 1) / kFilterThreads;
+  static_assert(kFilterIters <= kWave / 2, "one bitmap word pair per lane");
   __shared__ uint32_t scan_sh[NW];
   __shared__ int sh_beta;
   __shared__ uint32_t sh_above;
@@ -59,6 +65,7 @@ __global__ __launch_bounds__(kFilterThreads) void k_topc_filter(
   const int b = blockIdx.y;
   const int tid = threadIdx.x, l = lane_id(), wv = wave_id();
   const int c0 = blockIdx.x * kFilterChunk;
+  const int p0 = c0 + wv * (kFilterIters * kWave);  // this wave's first position
   uint32_t* cr = ctr + (size_t)kCtrStride * b;
 
   const int n_valid = clamp_ctx(ctx_len, b, max_ctx);
@@ -74,8 +81,7 @@ __global__ __launch_bounds__(kFilterThreads) void k_topc_filter(
   const T* sb = scores + (size_t)b * max_ctx;
   T sv[kFilterIters];
 #pragma unroll
-  for (int u = 0; u < kFilterIters; u++)
-    sv[u] = sb[min(c0 + (u * NW + wv) * kWave + l, max_ctx - 1)];
+  for (int u = 0; u < kFilterIters; u++) sv[u] = sb[min(p0 + u * kWave + l, max_ctx - 1)];
 
   // threshold bucket from the histogram
   if (tid == 0) {
@@ -106,38 +112,47 @@ __global__ __launch_bounds__(kFilterThreads) void k_topc_filter(
   }
 
   // bucket beta holds the scores [beta_lo, beta_hi]: above it means kept,
-  // inside it means tied (no bucket: every valid token is kept)
+  // inside it means tied -- one unsigned compare, (x - beta_lo) < span (no
+  // bucket: every valid token is kept and span = 0 admits no tie)
   T beta_lo = 0, beta_hi = 0;
   if (beta >= 0) S::range(beta, beta_lo, beta_hi);
   const bool all_keep = beta < 0;
-  uint32_t* bm = bitmap + (size_t)b * bitmap_words;
+  const U span = all_keep ? (U)0 : (U)((U)beta_hi - (U)beta_lo) + (U)1;
   const size_t tb = (size_t)b * max_ctx;
-  uint32_t wn = 0;  // this wave's ties so far (wave-uniform)
-  uint32_t wk = 0;  // this wave's kept positions (wave-uniform)
+  uint32_t wn = 0;     // this wave's ties so far (wave-uniform)
+  uint32_t wk = 0;     // this wave's kept positions (wave-uniform)
+  uint32_t bw_lo = 0, bw_hi = 0;  // lane u: the bitmap words of step u
 #pragma unroll
   for (int u = 0; u < kFilterIters; u++) {
-    const int base = c0 + (u * NW + wv) * kWave;
-    const int t = base + l;
+    const int t = p0 + u * kWave + l;
     const bool valid = t < n_valid;
-    const bool keep_f = valid && (all_keep || sv[u] > beta_hi);
-    const bool tie_f = valid && !all_keep && sv[u] >= beta_lo && sv[u] <= beta_hi;
+    const bool keep_f = valid & (all_keep | (sv[u] > beta_hi));
+    const bool tie_f = valid & ((U)((U)sv[u] - (U)beta_lo) < span);
     const uint64_t mk = __ballot(keep_f);
     const uint64_t mt = __ballot(tie_f);
-    if (l == 0 && base / 32 < bitmap_words)
-      *(uint2*)&bm[base / 32] = make_uint2((uint32_t)mk, (uint32_t)(mk >> 32));
-    if (tie_f) {
-      const uint32_t idx = wn + lane_rank(mt);
-      if (idx < (uint32_t)kFilterWaveTies) {
-        loc_s[wv][idx] = sv[u];
-        loc_p[wv][idx] = t;
-      } else {  // more ties than the wave's LDS list holds: straight to the global list
-        const uint32_t g = atomicAdd(&cr[kCtrTies], 1u);
-        tie_s[tb + g] = sv[u];
-        tie_p[tb + g] = t;
+    bw_lo = l == u ? (uint32_t)mk : bw_lo;
+    bw_hi = l == u ? (uint32_t)(mk >> 32) : bw_hi;
+    if (mt) {  // wave-uniform
+      if (tie_f) {
+        const uint32_t idx = wn + lane_rank(mt);
+        if (idx < (uint32_t)kFilterWaveTies) {
+          loc_s[wv][idx] = sv[u];
+          loc_p[wv][idx] = t;
+        } else {  // more ties than the wave's LDS list holds: straight to the global list
+          const uint32_t g = atomicAdd(&cr[kCtrTies], 1u);
+          tie_s[tb + g] = sv[u];
+          tie_p[tb + g] = t;
+        }
       }
+      wn += (uint32_t)__popcll(mt);
     }
-    wn += (uint32_t)__popcll(mt);
     wk += (uint32_t)__popcll(mk);
+  }
+  // the wave's 32 bitmap words (positions p0 .. p0 + 1023) in one store
+  {
+    const int w = p0 / 32 + 2 * l;
+    if (l < kFilterIters && w < bitmap_words) *(uint2*)&bitmap[(size_t)b * bitmap_words + w] =
+        make_uint2(bw_lo, bw_hi);
   }
   if (l == 0) {
     wave_n[wv] = min(wn, (uint32_t)kFilterWaveTies);
