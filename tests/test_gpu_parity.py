@@ -167,6 +167,44 @@ def test_refine_topk_ties(ls):
     run_refine_case(ls, inp, [6000, 6000], 2000, 333)
 
 
+def three_level_patterns(q, w, keys, coarse):
+    """Three key rows of strictly decreasing (coarse or fine) score."""
+    s = orc.index_scores(q, w, keys[:64].numpy(), coarse)
+    order = np.argsort(-s, kind="stable")
+    hi, mid, lo = order[0], order[len(order) // 2], order[-1]
+    assert s[hi] > s[mid] > s[lo]
+    return keys[[int(hi), int(mid), int(lo)]].clone()
+
+
+@pytest.mark.parametrize("stage", ["coarse", "fine"])
+def test_cut_inside_a_short_equal_group(ls, stage):
+    # strong tokens, then 50 tokens of one equal score with the cut inside
+    # that group (its 20 lowest positions win), then weak tokens: the exact
+    # tie search ends on a group of equal keys short enough to be ranked
+    # lane by lane
+    wl = dataclasses.replace(SHRUNK, batch=2, ctx=6000)
+    inp = idx_inputs(wl)
+    q, w, keys = inp["q"], inp["w"], inp["keys"]
+    g = torch.Generator().manual_seed(11)
+    n_strong = 980 if stage == "coarse" else 300
+    expect = []
+    for b in range(2):
+        pats = three_level_patterns(q[b].numpy(), w[b].numpy(), keys[b], stage == "coarse")
+        perm = torch.randperm(6000, generator=g)
+        lvl = torch.full((6000,), 2, dtype=torch.long)
+        lvl[perm[:n_strong]] = 0
+        lvl[perm[n_strong:n_strong + 50]] = 1
+        keys[b] = pats[lvl]
+        mid = np.sort(perm[n_strong:n_strong + 50].numpy())[:20]
+        expect.append(np.sort(np.concatenate([perm[:n_strong].numpy(), mid])).tolist())
+    if stage == "coarse":
+        got = run_coarse_case(ls, inp, [6000, 6000], n_strong + 20)
+    else:
+        got = run_refine_case(ls, inp, [6000, 6000], 6000, n_strong + 20)
+    for b in range(2):
+        assert got[b].tolist() == expect[b], "request %d" % b
+
+
 def test_full_candidates_equal_exact_topk_gpu(ls):
     # C = all tokens: the GPU coarse-to-fine result equals the exact top-k
     wl = dataclasses.replace(SHRUNK, batch=2, ctx=4000)

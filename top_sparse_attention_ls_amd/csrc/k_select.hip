@@ -248,6 +248,24 @@ __global__ __launch_bounds__(kEmitThreads) void k_topc_emit(
   const uint32_t* bmg = bitmap + (size_t)b * bitmap_words;
   uint32_t* cr = ctr + (size_t)kCtrStride * b;
 
+  // Issued together, before any of them is waited for: the first kTiePre
+  // entries of the tie list (usually all of it; loaded unconditionally,
+  // clamped to the row), the run's first bitmap word, the chunk counts
+  // before the run and the counters.
+  constexpr int kPre = 3;
+  constexpr int kTiePre = kPre * NT;
+  static_assert(kTiePre <= Cfg::kTies, "the prefetched ties fit the LDS list");
+  const typename S::T* ts = tie_s + (size_t)b * max_ctx;
+  const int32_t* tp = tie_p + (size_t)b * max_ctx;
+  typename S::T ts_pre[kPre];
+  int32_t tp_pre[kPre];
+#pragma unroll
+  for (int k = 0; k < kPre; k++) {
+    const int i = min(tid + k * NT, max_ctx - 1);
+    ts_pre[k] = ts[i];
+    tp_pre[k] = tp[i];
+  }
+  const uint32_t wd_first = bmg[min(ck0 * kSelectChunkWords + tid, bitmap_words - 1)];
   uint32_t before = 0;  // kept outright in the chunks before the run
   for (int i = tid; i < ck0; i += NT) before += chunk[(size_t)b * n_chunks + i];
   const uint32_t n_tie = cr[kCtrTies];
@@ -255,8 +273,6 @@ __global__ __launch_bounds__(kEmitThreads) void k_topc_emit(
   const uint32_t above = cr[kCtrAbove];
 
   uint32_t ties_before = 0;  // winning ties before the run (this thread's share)
-  const typename S::T* ts = tie_s + (size_t)b * max_ctx;
-  const int32_t* tp = tie_p + (size_t)b * max_ctx;
   const bool in_lds = n_tie <= (uint32_t)Cfg::kTies;
   // tie i as (order-preserving key, position), from LDS or the global list
   auto tie_entry = [&](int i, uint64_t& u, uint32_t& p) {
@@ -273,7 +289,12 @@ __global__ __launch_bounds__(kEmitThreads) void k_topc_emit(
   if (beta >= 0) {
     const uint32_t need = (uint32_t)C - above;  // 1 <= need <= n_tie
     if (in_lds) {
-      for (int i = tid; i < (int)n_tie; i += NT) lds_t[i] = Cfg::pack(ts[i], tp[i]);
+#pragma unroll
+      for (int k = 0; k < kPre; k++) {
+        const int i = tid + k * NT;
+        if (i < (int)n_tie) lds_t[i] = Cfg::pack(ts_pre[k], tp_pre[k]);
+      }
+      for (int i = kTiePre + tid; i < (int)n_tie; i += NT) lds_t[i] = Cfg::pack(ts[i], tp[i]);
     }
     __syncthreads();
     if (need < n_tie) {
@@ -315,8 +336,9 @@ __global__ __launch_bounds__(kEmitThreads) void k_topc_emit(
   int32_t* cb = cand + (size_t)b * C;
   for (int ck = ck0; ck < ck1; ck++) {
     const int w0 = ck * kSelectChunkWords;
-    // unconditional load (clamped), selected afterwards
-    const uint32_t wd = bmg[min(w0 + tid, bitmap_words - 1)];
+    // unconditional load (clamped), selected afterwards; the run's first
+    // word was loaded up front
+    const uint32_t wd = ck == ck0 ? wd_first : bmg[min(w0 + tid, bitmap_words - 1)];
     bm_l[tid] = w0 + tid < bitmap_words ? wd : 0u;
     __syncthreads();
     if (beta >= 0) {  // the winning ties of this chunk
