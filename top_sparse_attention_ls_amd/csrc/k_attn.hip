@@ -501,48 +501,89 @@ __global__ __launch_bounds__(256) void k_attn_valu(
 // out = sum_j o_j 2^(lse_j - L) with L = log2 sum_j 2^lse_j; lse = L ln 2.
 // One wave per (request, head), four per workgroup, numbered like the
 // attention grid so that a request's partials are read on the XCD that wrote
-// them.  Each lane combines 8 consecutive dims: the 16-byte pieces of eight
-// splits are loaded before any is used.  DV is a multiple of 8.
+// them.  Each lane combines 8 consecutive dims, eight splits at a time.  The
+// split LSEs are read eight at a time (L by a running max and rescaled sum),
+// and the first batch of them and of the partials -- for 512 dims and up to
+// eight splits, all of the data -- load together: one round trip per head.
+// DV is a multiple of 8.
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ part_o,
                                                  const float* __restrict__ part_lse,
                                                  uint16_t* __restrict__ out,
                                                  float* __restrict__ lse, int BH, int DV,
                                                  int n_splits) {
-  const int bh = xcd_major(blockIdx.x, gridDim.x) * 4 + wave_id();
+  const int bh = __builtin_amdgcn_readfirstlane(xcd_major(blockIdx.x, gridDim.x) * 4 + wave_id());
   if (bh >= BH) return;
   const int l = lane_id();
   const float* pl = part_lse + (size_t)bh * n_splits;
-  float M = -INFINITY;
-  for (int j = 0; j < n_splits; j++) M = fmaxf(M, pl[j]);
+  const uint16_t* po = part_o + (size_t)bh * n_splits * DV;
+  // splits j0 .. j0+7 of dims d .. d+7, and their LSEs (unconditional loads:
+  // split and dim clamped; splits past the end get LSE -inf, weight 0)
+  auto load8 = [&](int j0, int d, uint4 (&v)[8]) {
+    const int dc = min(d, DV - 8);
+#pragma unroll
+    for (int u = 0; u < 8; u++) v[u] = *(const uint4*)(po + (size_t)min(j0 + u, n_splits - 1) * DV + dc);
+  };
+  auto load_lse8 = [&](int j0, float (&x)[8]) {
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      const float y = pl[min(j0 + u, n_splits - 1)];
+      x[u] = j0 + u < n_splits ? y : -INFINITY;
+    }
+  };
+  uint4 v0[8];
+  float ls0[8];
+  load8(0, 8 * l, v0);
+  load_lse8(0, ls0);
+  __builtin_amdgcn_sched_barrier(0);
+  float M = -INFINITY, W = 0.f;  // running max and sum of 2^(lse - M)
+  auto fold = [&](const float (&x)[8]) {
+    float mb = x[0];
+#pragma unroll
+    for (int u = 1; u < 8; u++) mb = fmaxf(mb, x[u]);
+    if (mb == -INFINITY) return;
+    const float Mn = fmaxf(M, mb);
+    float s = W * exp2f(M - Mn);  // 0 while M is -inf
+#pragma unroll
+    for (int u = 0; u < 8; u++) s += exp2f(x[u] - Mn);
+    W = s;
+    M = Mn;
+  };
+  fold(ls0);
+  for (int j0 = 8; j0 < n_splits; j0 += 8) {
+    float x[8];
+    load_lse8(j0, x);
+    fold(x);
+  }
   uint16_t* ob = out + (size_t)bh * DV;
   if (M == -INFINITY) {
     for (int d = 8 * l; d < DV; d += 8 * kWave) *(uint4*)(ob + d) = uint4{0, 0, 0, 0};
     if (l == 0) lse[bh] = -INFINITY;
     return;
   }
-  float W = 0.f;
-  for (int j = 0; j < n_splits; j++) W += exp2f(pl[j] - M);
   const float L = M + log2f(W);
-  const uint16_t* po = part_o + (size_t)bh * n_splits * DV;
+  auto accum = [&](const uint4 (&v)[8], const float (&x)[8], float (&a)[8]) {
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      const float wj = exp2f(x[u] - L);  // 0 for splits past the end
+      const uint32_t y[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        a[2 * e] += wj * __uint_as_float(y[e] << 16);
+        a[2 * e + 1] += wj * __uint_as_float(y[e] & 0xFFFF0000u);
+      }
+    }
+  };
   for (int d = 8 * l; d < DV; d += 8 * kWave) {
     float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j0 = 0; j0 < n_splits; j0 += 8) {
-      uint4 v[8];
-      float wj[8];
-#pragma unroll
-      for (int u = 0; u < 8; u++) {
-        const int j = min(j0 + u, n_splits - 1);
-        v[u] = *(const uint4*)(po + (size_t)j * DV + d);
-        wj[u] = j0 + u < n_splits ? exp2f(pl[j] - L) : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; u++) {
-        const uint32_t x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          a[2 * e] += wj[u] * __uint_as_float(x[e] << 16);
-          a[2 * e + 1] += wj[u] * __uint_as_float(x[e] & 0xFFFF0000u);
-        }
+      if (d == 8 * l && j0 == 0) {
+        accum(v0, ls0, a);
+      } else {
+        uint4 v[8];
+        float x[8];
+        load8(j0, d, v);
+        load_lse8(j0, x);
+        accum(v, x, a);
       }
     }
     uint4 pk;
