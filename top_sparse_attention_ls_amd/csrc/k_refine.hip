@@ -546,36 +546,52 @@ __global__ __launch_bounds__(256) void k_hot_gather(const int32_t* __restrict__ 
                                                     const uint4* pool, uint4* __restrict__ hot,
                                                     int hot_slots, int max_ctx, int K,
                                                     int chunks) {
+  // Workgroup x copies misses x, x + G, x + 2G, ... (G workgroups per
+  // request), as 16-byte pieces numbered (slot m of its list, chunk c) in
+  // order, kGatherUnroll pieces per thread per round.  Positions and rows
+  // load speculatively -- indices clamped, so every access stays inside the
+  // lists and the pool -- at the same time as the miss count.  The stores go
+  // through a buffer resource over the n_miss rows of the list: pieces of
+  // slots past the count are dropped by the hardware, with no branch (a
+  // branch would let the compiler sink each row load into it).
   const int b = blockIdx.y;
-  const int nm = min(max(n_miss[b], 0), K);  // a list never holds more than K misses
-  const uint32_t total = (uint32_t)nm * (uint32_t)chunks;
-  const uint32_t per = (total + gridDim.x - 1) / gridDim.x;
-  const uint32_t i0 = blockIdx.x * per;
-  const uint32_t i1 = min(i0 + per, total);
+  const int G = gridDim.x;
   const int32_t* mp = miss_pos + (size_t)b * K;
   const uint4* pb = pool + (size_t)b * max_ctx * chunks;
   uint4* hb = hot + ((size_t)b * (hot_slots + K) + hot_slots) * chunks;
-  for (uint32_t i = i0 + threadIdx.x; i < i1; i += 256 * kGatherUnroll) {
+  const int nm_raw = n_miss[b];
+  // one round of kGatherUnroll pieces per thread from piece f0 on: every
+  // position, then every row, then (after the fence) the stores
+  auto round = [&](uint32_t f0, int nm) {
     uint4 v[kGatherUnroll];
-    uint32_t dst[kGatherUnroll], c[kGatherUnroll];
+    uint32_t off[kGatherUnroll], c[kGatherUnroll];
     int32_t p[kGatherUnroll];
-    // all miss positions first, then all row loads, then all stores
 #pragma unroll
     for (int u = 0; u < kGatherUnroll; u++) {
-      const uint32_t idx = min(i + 256u * u, i1 - 1);
-      const uint32_t j = idx / (uint32_t)chunks;
-      c[u] = idx - j * (uint32_t)chunks;
-      dst[u] = idx;
-      p[u] = mp[j];
+      const uint32_t f = f0 + threadIdx.x + 256u * u;
+      const uint32_t m = f / (uint32_t)chunks;
+      c[u] = f - m * (uint32_t)chunks;
+      const int jj = blockIdx.x + G * (int)m;
+      off[u] = ((uint32_t)jj * (uint32_t)chunks + c[u]) * 16u;
+      p[u] = mp[min(jj, K - 1)];
     }
 #pragma unroll
     for (int u = 0; u < kGatherUnroll; u++)
       v[u] = pb[(size_t)min(max(p[u], 0), max_ctx - 1) * chunks + c[u]];
-    // past the range the index is clamped to the range's last piece, so a
-    // duplicate store writes that piece's own value again: no branch needed
+    __builtin_amdgcn_sched_barrier(0);
+    if (nm < 0) nm = min(max(nm_raw, 0), K);  // a list never holds more than K misses
+    const __amdgpu_buffer_rsrc_t hres = buffer_rsrc(hb, (uint32_t)nm * (uint32_t)chunks * 16u);
 #pragma unroll
-    for (int u = 0; u < kGatherUnroll; u++) hb[dst[u]] = v[u];
-  }
+    for (int u = 0; u < kGatherUnroll; u++)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v[u]), hres, off[u], 0, 0);
+    return nm;
+  };
+  constexpr uint32_t kRound = 256u * kGatherUnroll;
+  const int nm = round(0u, -1);
+  // slots of this workgroup (uniform); more rounds only past the first
+  // kRound pieces
+  const uint32_t my = nm > (int)blockIdx.x ? (uint32_t)((nm - 1 - (int)blockIdx.x) / G + 1) : 0u;
+  for (uint32_t f0 = kRound; f0 < my * (uint32_t)chunks; f0 += kRound) round(f0, nm);
 }
 
 hipError_t launch_hot_gather(const int32_t* miss_pos, const int32_t* n_miss, const void* pool,
