@@ -172,6 +172,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
   __shared__ int32_t tie_c[kTopkTieLds];
   __shared__ uint32_t tab[NTAB];
   __shared__ Threshold sh_thr;
+  __shared__ ThresholdScratch thr_sc;  // the tie search's short list
   __shared__ int sh_beta;
   __shared__ uint32_t sh_above, n_tie, sh_tot;
   // (slice, request), numbered so that a request's workgroups share an XCD's
@@ -273,19 +274,14 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
       };
       thr = block_threshold<NT>(get, (int)n_c, need_all, ssh);
     } else if (need < nt) {
-      if (wv == 0) {
-        auto get = [&](int i, uint64_t& u, uint32_t& p) {
-          u = key_of_i64(tie_f[i]);
-          p = (uint32_t)tie_c[i];
-        };
-        int64_t lo, hi;
-        wide_bucket_range(beta, lo, hi);
-        const Threshold t = wave_threshold(get, (int)nt, need, ssh.hist, key_of_i64(lo),
-                                           key_of_i64(hi), pos_bits_below(max_ctx));
-        if (l == 0) sh_thr = t;
-      }
-      __syncthreads();
-      thr = sh_thr;
+      auto get = [&](int i, uint64_t& u, uint32_t& p) {
+        u = key_of_i64(tie_f[i]);
+        p = (uint32_t)tie_c[i];
+      };
+      int64_t lo, hi;
+      wide_bucket_range(beta, lo, hi);
+      thr = tie_threshold<NT>(get, (int)nt, need, ssh, &thr_sc, &sh_thr, key_of_i64(lo),
+                              key_of_i64(hi), pos_bits_below(max_ctx));
     }
 #pragma unroll
     for (int k = 0; k < PER; k++) {

@@ -237,6 +237,7 @@ __global__ __launch_bounds__(kEmitThreads) void k_topc_emit(
   __shared__ uint32_t bm_l[kSelectChunkWords];
   __shared__ typename Cfg::E lds_t[Cfg::kTies];  // (key, position) of the ties
   __shared__ Threshold sh_thr;
+  __shared__ ThresholdScratch thr_sc;  // the tie search's short list
   const int n_runs = gridDim.x;  // workgroups per request
   // (run, request), numbered so that one request's workgroups share an
   // XCD's L2 (they all read the request's tie list)
@@ -299,20 +300,15 @@ __global__ __launch_bounds__(kEmitThreads) void k_topc_emit(
     __syncthreads();
     if (need < n_tie) {
       if (in_lds) {
-        if (wave_id() == 0) {
-          auto get = [&](int i, uint64_t& u, uint32_t& p) {
-            const typename Cfg::E e = lds_t[i];
-            u = Cfg::key(e);
-            p = Cfg::pos(e);
-          };
-          typename S::T lo, hi;
-          S::range(beta, lo, hi);
-          const Threshold t = wave_threshold(get, (int)n_tie, need, ssh.hist, Cfg::key_of(lo),
-                                             Cfg::key_of(hi), pos_bits_below(max_ctx));
-          if (lane_id() == 0) sh_thr = t;
-        }
-        __syncthreads();
-        thr = sh_thr;
+        auto get = [&](int i, uint64_t& u, uint32_t& p) {
+          const typename Cfg::E e = lds_t[i];
+          u = Cfg::key(e);
+          p = Cfg::pos(e);
+        };
+        typename S::T lo, hi;
+        S::range(beta, lo, hi);
+        thr = tie_threshold<NT>(get, (int)n_tie, need, ssh, &thr_sc, &sh_thr, Cfg::key_of(lo),
+                                Cfg::key_of(hi), pos_bits_below(max_ctx));
       } else {
         auto get = [&](int i, uint64_t& u, uint32_t& p) {
           u = Cfg::key_of(ts[i]);

@@ -194,11 +194,14 @@ __device__ __forceinline__ void wave_digit(const Entry& entry, int n, uint32_t* 
   for (int i0 = l; i0 < n; i0 += 4 * kWave) {
     uint32_t d[4];
     bool m[4];
+    // entries read unconditionally (index clamped, n >= 1), so the four
+    // reads are in flight together instead of one branch and wait each
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int i = i0 + j * kWave;
       d[j] = 0;
-      m[j] = i < n && entry(i, d[j]);
+      const bool ok = entry(min(i, n - 1), d[j]);
+      m[j] = i < n && ok;
     }
 #pragma unroll
     for (int j = 0; j < 4; j++)
@@ -234,6 +237,15 @@ __device__ __forceinline__ void wave_digit(const Entry& entry, int n, uint32_t* 
   *cnt = wave_read(bc, src);
   wave_lds_sync();
 }
+
+// LDS scratch of a tie search: the entries that survive the first key digit,
+// when few enough, so that the remaining digits run over a short list.
+constexpr int kThrScratch = 256;
+struct ThresholdScratch {
+  uint64_t key[kThrScratch];
+  uint32_t pos[kThrScratch];
+  uint32_t fill;
+};
 
 template <class Get>
 __device__ Threshold wave_threshold(const Get& get, int n, uint32_t need, uint32_t* hist,
@@ -281,6 +293,79 @@ __device__ Threshold wave_threshold(const Get& get, int n, uint32_t need, uint32
     if (cnt == need) return Threshold{cut, (uint32_t)(pprefix + ((1ull << shft) - 1ull)), 1};
   }
   return Threshold{cut, (uint32_t)pprefix, 1};
+}
+
+// ----------------------------------------------------------------------------
+// The tie search of the selections: the exact threshold over a list whose
+// keys lie in [key_lo, key_hi] (a histogram bucket's range).  The first key
+// digit -- the only step that touches every entry -- is counted by the whole
+// workgroup (NT threads), and the entries that fall in the chosen digit are
+// copied to sc by the whole workgroup; one wave then finishes over that short
+// list (wave_threshold).  With more than kThrScratch entries in the chosen
+// digit, or nothing to split on, the wave continues over the whole list.
+// Every thread returns the threshold.  Contains workgroup barriers; sh_thr
+// is LDS.
+template <int NT, class Get>
+__device__ Threshold tie_threshold(const Get& get, int n, uint32_t need, SelectShared& sh,
+                                   ThresholdScratch* sc, Threshold* sh_thr, uint64_t key_lo,
+                                   uint64_t key_hi, int pos_bits) {
+  const int tid = threadIdx.x;
+  const int nb = (key_lo == key_hi) ? 0 : 64 - __clzll(key_lo ^ key_hi);
+  if (nb > 0 && n > kThrScratch) {  // workgroup-uniform
+    const int d = nb < 8 ? nb : 8;
+    const int shft = nb - d;
+    const uint64_t dmask = (1ull << d) - 1ull;
+    const uint64_t top = (nb >= 64) ? 0ull : ((key_hi >> nb) << nb);  // bits every key shares
+    for (int i = tid; i < 256; i += NT) sh.hist[i] = 0;
+    if (tid == 0) sc->fill = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += NT) {
+      uint64_t u;
+      uint32_t p;
+      get(i, u, p);
+      atomicAdd(&sh.hist[(uint32_t)((u >> shft) & dmask)], 1u);
+    }
+    __syncthreads();
+    find_crossing(sh, need, true);
+    __syncthreads();
+    const uint32_t beta = sh.beta, before = sh.before, cnt = sh.cnt;
+    need -= before;
+    const uint64_t prefix = top | ((uint64_t)beta << shft);
+    const uint64_t low = (1ull << shft) - 1ull;
+    if (cnt == need) return Threshold{prefix, 0u, 0};  // the whole digit is kept
+    if (cnt <= (uint32_t)kThrScratch) {
+      for (int i = tid; i < n; i += NT) {
+        uint64_t u;
+        uint32_t p;
+        get(i, u, p);
+        if ((u >> shft) == (prefix >> shft)) {
+          const uint32_t k = atomicAdd(&sc->fill, 1u);  // k < cnt
+          sc->key[k] = u;
+          sc->pos[k] = p;
+        }
+      }
+      __syncthreads();
+      if (wave_id() == 0) {
+        auto get_sc = [&](int i, uint64_t& u, uint32_t& p) {
+          u = sc->key[i];
+          p = sc->pos[i];
+        };
+        const Threshold t = wave_threshold(get_sc, (int)cnt, need, sh.hist, prefix, prefix | low,
+                                           pos_bits);
+        if (lane_id() == 0) *sh_thr = t;
+      }
+      __syncthreads();
+      return *sh_thr;
+    }
+    key_lo = prefix;
+    key_hi = prefix | low;
+  }
+  if (wave_id() == 0) {
+    const Threshold t = wave_threshold(get, n, need, sh.hist, key_lo, key_hi, pos_bits);
+    if (lane_id() == 0) *sh_thr = t;
+  }
+  __syncthreads();
+  return *sh_thr;
 }
 
 }  // namespace ls
