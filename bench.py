@@ -35,6 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "sparse-decode layer-steps/s at 128K (B=32) + % of HBM roofline"
+REPEATS = 5  # timed runs of K steps (the first one gives the value)
 HBM_PEAK_GBS = 8000.0
 STAGES = ["coarse_score", "candidate_select", "refine_topk_resolve", "miss_gather",
           "attention", "combine"]
@@ -313,9 +314,10 @@ def main():
                  ctx_len=r["ctx_len"], q_attn=r["q_attn"], pos2slot=r["pos2slot"],
                  hot_kv=r["hot_kv"], pool_kv=r["pool_kv"], events=events)
 
-    print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
-    for i in range(args.warmup):
-        run(i)
+    # host-side set-up first (the miss-count check after one step, the
+    # events), so that the warm-up runs right up to the timed region and the
+    # GPU enters it busy rather than after a host-side pause
+    run(0)
     torch.cuda.synchronize()
     miss_now = step.n_miss.cpu().tolist()
     assert miss_now == n_miss, "hot buffer miss counts drifted: %s" % miss_now
@@ -333,8 +335,12 @@ def main():
         for e in pair:
             e.record()
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start.record()
+    t_end.record()
+    print("[bench] warmup %d, then timing %d steps" % (args.warmup, K), file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        run(i)
     torch.cuda.synchronize()
-    print("[bench] timing %d steps" % K, file=sys.stderr, flush=True)
     t_start.record()
     for i in range(K):
         pair = coarse_ev.get(i)
@@ -344,6 +350,20 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / K
     coarse_ms = sum(p[0].elapsed_time(p[1]) for p in coarse_ev.values()) / len(coarse_ev)
+
+    # the same K steps timed again, without any event inside: the spread of
+    # the rate over repeated runs (the value above is the first run's)
+    rep_ms = [ms_per_step]
+    for _ in range(REPEATS - 1):
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        r0.record()
+        for i in range(K):
+            run(i)
+        r1.record()
+        torch.cuda.synchronize()
+        rep_ms.append(r0.elapsed_time(r1) / K)
+    rates = sorted(1000.0 / m for m in rep_ms)
 
     # stage breakdown from a separate instrumented run (every stage bracketed)
     n_inst = min(K, 20)
@@ -412,6 +432,14 @@ def main():
         "coarse_events_sampled": len(coarse_ev),
         "stages_us_instrumented": {n: round(v * 1000, 2) for n, v in zip(STAGES, stage_ms)},
         "request_layer_steps_per_s": round(steps_per_s * wl.batch, 1),
+        "repeats": {
+            "runs": len(rates), "steps_each": K,
+            "median": round(rates[len(rates) // 2], 2),
+            "p10": round(rates[max(0, int(0.1 * (len(rates) - 1)))], 2),
+            "p90": round(rates[int(round(0.9 * (len(rates) - 1)))], 2),
+            "note": "layer-steps/s of the first run (the value) and of the same K steps repeated "
+                    "without events",
+        },
         "graph": graph,
     }
     coarse_ops = 2 * wl.batch * wl.ctx * wl.idx_heads * wl.idx_dim

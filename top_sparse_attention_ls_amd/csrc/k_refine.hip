@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
   __shared__ Threshold sh_thr;
   __shared__ ThresholdScratch thr_sc;  // the tie search's short list
   __shared__ int sh_beta;
-  __shared__ uint32_t sh_above, n_tie, sh_tot;
+  __shared__ uint32_t sh_above, n_tie;
   // (slice, request), numbered so that a request's workgroups share an XCD's
   // L2 (they all read the request's candidates)
   const int lin = xcd_major(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
@@ -249,18 +249,27 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
     for (int k = 0; k < PER; k++) sel[k] = c[k] >= 0;
   } else {
     const uint32_t need = need_all - sh_above;  // 1 <= need <= ties
+    // the wave's ties of all PER batches, with one reservation in the list
+    uint64_t mt[PER];
+    uint32_t wave_ties = 0;
 #pragma unroll
     for (int k = 0; k < PER; k++) {
-      const bool tie = c[k] >= 0 && (int)bk[k] == beta;
-      const uint64_t mt = __ballot(tie);
-      if (mt) {
-        uint32_t base = 0;
-        if (l == 0) base = atomicAdd(&n_tie, (uint32_t)__popcll(mt));
-        const uint32_t i = wave_read(base, 0) + lane_rank(mt);
-        if (tie && i < (uint32_t)kTopkTieLds) {
-          tie_f[i] = f[k];
-          tie_c[i] = c[k];
+      mt[k] = __ballot(c[k] >= 0 && (int)bk[k] == beta);
+      wave_ties += (uint32_t)__popcll(mt[k]);
+    }
+    if (wave_ties) {  // wave-uniform
+      uint32_t base = 0;
+      if (l == 0) base = atomicAdd(&n_tie, wave_ties);
+      uint32_t i = wave_read(base, 0);
+#pragma unroll
+      for (int k = 0; k < PER; k++) {
+        const bool tie = (mt[k] >> l) & 1ull;
+        const uint32_t j = i + lane_rank(mt[k]);
+        if (tie && j < (uint32_t)kTopkTieLds) {
+          tie_f[j] = f[k];
+          tie_c[j] = c[k];
         }
+        i += (uint32_t)__popcll(mt[k]);
       }
     }
     __syncthreads();
@@ -304,7 +313,10 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
     if (l == 0) tab[k * NW + wv] = (uint32_t)__popcll(ms[k]) | ((uint32_t)__popcll(mm[k]) << 16);
   }
   __syncthreads();
-  if (wv == 0) {  // exclusive scan of the table in (k, wave) order
+  // every wave scans the table itself (exclusive, in (k, wave) order) and
+  // keeps the offset of its own entry of slice m: no second barrier
+  uint32_t my_base, tot;
+  {
     constexpr int Q = NTAB >= kWave ? NTAB / kWave : 1;
     uint32_t v[Q];
     uint32_t sum = 0;
@@ -315,25 +327,23 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
       sum += v[q];
     }
     const uint32_t incl = wave_incl_scan(sum);
+    tot = wave_read(incl, kWave - 1);
+    // entry (m, wv) sits at e = m * NW + wv: lane e / Q, position e % Q
+    const int e_me = m * NW + wv;
     uint32_t run = incl - sum;
 #pragma unroll
-    for (int q = 0; q < Q; q++) {
-      const int e = l * Q + q;
-      if (e < NTAB) tab[e] = run;
-      run += v[q];
-    }
-    if (l == kWave - 1) sh_tot = incl;
+    for (int q = 0; q < Q; q++)
+      if (q < e_me % Q) run += v[q];
+    my_base = wave_read(run, e_me / Q);
   }
-  __syncthreads();
   int32_t* tb = topk + (size_t)b * K;
   int64_t* sb = topk_score ? topk_score + (size_t)b * K : nullptr;
   int32_t* rb = rows ? rows + (size_t)b * K : nullptr;
   int32_t* mb = miss_pos ? miss_pos + (size_t)b * K : nullptr;
-  const uint32_t tot = sh_tot;
 #pragma unroll
   for (int k = 0; k < PER; k++) {
     if (k != m) continue;  // this workgroup's slice (workgroup-uniform)
-    const uint32_t base = tab[k * NW + wv];
+    const uint32_t base = my_base;
     const uint32_t o = (base & 0xFFFFu) + lane_rank(ms[k]);
     if (!sel[k] || o >= (uint32_t)K) continue;  // exactly min(K, valid) are kept
     tb[o] = c[k];
