@@ -59,6 +59,28 @@ def test_prefill_head_shapes(ls, H, D):
     run_case(ls, n_query=40, ctx=4500, H=H, D=D, topk=100, q_pos0=4500 - 40)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_full_range_weights(ls, D):
+    # weights over the whole int8 range (negative ones too) and extreme keys:
+    # head sums beyond 32 bits and of either sign, next to rows (every third)
+    # that keep the workload's small positive weights
+    wl = dataclasses.replace(PF, idx_heads=64, idx_dim=D, topk=128)
+    n_query, ctx = 60, 5000
+    inp = synth.prefill_inputs(wl, 0, "cpu", n_query=n_query, ctx=ctx)
+    q, w, keys = inp["q"], inp["w"].clone(), inp["keys"].clone()
+    g = torch.Generator().manual_seed(21 + D)
+    big = torch.randint(-128, 128, w.shape, generator=g, dtype=torch.int32).to(torch.int8)
+    keep_small = (torch.arange(n_query) % 3 == 0)[:, None]
+    w = torch.where(keep_small, w, big)
+    # keys at the int8 extremes, so that full-range rows really exceed 32 bits
+    keys[:64] = 127
+    keys[64:128] = -128
+    q_pos0 = ctx - n_query
+    got = np_(ls.prefill_index_topk(q.to(DEV), w.to(DEV), keys.to(DEV), q_pos0, wl.topk))
+    valid_rows(got, q_pos0, wl.topk, ctx)
+    check_rows(got, q.numpy(), w.numpy(), keys.numpy(), q_pos0, wl.topk, range(n_query))
+
+
 def test_prefill_all_keys_equal_takes_lowest_positions(ls):
     q = torch.randint(-127, 128, (16, 8, 64), dtype=torch.int32).to(torch.int8)
     w = torch.randint(1, 17, (16, 8), dtype=torch.int32).to(torch.int8)
