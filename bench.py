@@ -41,13 +41,20 @@ STAGES = ["coarse_score", "candidate_select", "refine_topk_resolve", "miss_gathe
           "attention", "combine"]
 
 
-def algorithmic_bytes(wl, n_miss_total: int) -> dict:
-    """Bytes the step must move at minimum, by part (see the design notes)."""
+def algorithmic_bytes(wl, n_miss_total: int, n_key_miss_total: int = 0) -> dict:
+    """HBM bytes the step must move at minimum, by part (see the design
+    notes).  With the original keys on the host, only the key-cache hits are
+    HBM reads (plus their slot lookups); the misses cross PCIe instead."""
     B, L, H, D = wl.batch, wl.ctx, wl.idx_heads, wl.idx_dim
     row = wl.qk_dim * 2
+    if wl.keys_on_host:
+        refine = (B * wl.n_cand - n_key_miss_total) * D + (B * wl.n_cand * 4
+                                                            if wl.key_slots else 0)
+    else:
+        refine = B * wl.n_cand * D
     parts = {
         "coarse_keys": B * L * D // 2,
-        "refine_keys": B * wl.n_cand * D,
+        "refine_keys": refine,
         "slot_table": B * wl.topk * 4 if wl.hot_slots else 0,
         "miss_read": n_miss_total * row,
         "miss_write": n_miss_total * row,
@@ -148,16 +155,29 @@ def build_inputs(ls, synth, wl, dev, replicas):
     cand = ls.index_coarse(inp["q"], inp["w"], kc, ctx_len, wl.n_cand)
     sel, _ = ls.refine_topk(inp["q"], inp["w"], keys, cand, ctx_len, wl.topk)
     pos2slot, hot, n_miss = synth.hot_fill(wl, sel, pool, dev)
+    key_cache, n_key_miss = None, None
+    if wl.key_slots:
+        # the indexer-key cache is laid out from the same candidate set
+        kp, kcache, n_key_miss = synth.key_cache_fill(wl, cand, keys, dev)
+        key_cache = dict(kpos2slot=kp, kcache=kcache)
+    if wl.keys_on_host:
+        # the original keys leave HBM: one pinned host copy, shared by the
+        # replicas (as a host pool is)
+        keys = keys.to("cpu").pin_memory()
     reps = []
     for r in range(replicas):
-        reps.append(dict(
+        rep_ = dict(
             q_idx=inp["q"], w_idx=inp["w"], ctx_len=ctx_len,
-            k8=keys if r == 0 else keys.clone(), kc=kc if r == 0 else kc.clone(),
+            k8=keys if (r == 0 or wl.keys_on_host) else keys.clone(),
+            kc=kc if r == 0 else kc.clone(),
             q_attn=q_attn if r == 0 else q_attn.clone(),
             pos2slot=pos2slot if r == 0 else pos2slot.clone(),
-            hot_kv=hot if r == 0 else hot.clone(), pool_kv=pool))
+            hot_kv=hot if r == 0 else hot.clone(), pool_kv=pool)
+        if key_cache is not None:
+            rep_.update({k: v if r == 0 else v.clone() for k, v in key_cache.items()})
+        reps.append(rep_)
     torch.cuda.synchronize()
-    return reps, n_miss, inp, q_attn, pool, pos2slot, hot
+    return reps, n_miss, n_key_miss, inp, q_attn, pool, pos2slot, hot
 
 
 def cpu_baseline(wl, inp, q_attn, pool, pos2slot, hot, n_sample):
@@ -301,18 +321,20 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print("[bench] building inputs for %s" % wl.name, file=sys.stderr, flush=True)
-    reps, n_miss, inp, q_attn, pool, pos2slot, hot = build_inputs(ls, synth, wl, dev,
-                                                                  args.replicas)
+    reps, n_miss, n_key_miss, inp, q_attn, pool, pos2slot, hot = build_inputs(
+        ls, synth, wl, dev, args.replicas)
     step = ls.DecodeStep(batch=wl.batch, max_ctx=wl.ctx, idx_heads=wl.idx_heads,
                          idx_dim=wl.idx_dim, n_cand=wl.n_cand, topk=wl.topk,
                          q_heads=wl.q_heads, qk_dim=wl.qk_dim, v_dim=wl.v_dim, scale=wl.scale,
-                         hot_slots=wl.hot_slots, pool_on_host=wl.pool_on_host, device=dev)
+                         hot_slots=wl.hot_slots, pool_on_host=wl.pool_on_host,
+                         keys_on_host=wl.keys_on_host, key_slots=wl.key_slots, device=dev)
 
     def run(i, events=None):
         r = reps[i % len(reps)]
         step.run(q_idx=r["q_idx"], w_idx=r["w_idx"], kc=r["kc"], k8=r["k8"],
                  ctx_len=r["ctx_len"], q_attn=r["q_attn"], pos2slot=r["pos2slot"],
-                 hot_kv=r["hot_kv"], pool_kv=r["pool_kv"], events=events)
+                 hot_kv=r["hot_kv"], pool_kv=r["pool_kv"], kpos2slot=r.get("kpos2slot"),
+                 kcache=r.get("kcache"), events=events)
 
     # host-side set-up first (the miss-count check after one step, the
     # events), so that the warm-up runs right up to the timed region and the
@@ -321,6 +343,18 @@ def main():
     torch.cuda.synchronize()
     miss_now = step.n_miss.cpu().tolist()
     assert miss_now == n_miss, "hot buffer miss counts drifted: %s" % miss_now
+    if wl.keys_on_host:
+        # candidates whose key is not in the key cache: their rows cross PCIe
+        c = step.cand.long()
+        kp = reps[0].get("kpos2slot")
+        if kp is None:
+            key_miss_now = (c >= 0).sum(1).tolist()
+        else:
+            hit = kp.gather(1, c.clamp(min=0)) >= 0
+            key_miss_now = ((c >= 0) & ~hit).sum(1).tolist()
+        if n_key_miss is not None:
+            assert key_miss_now == n_key_miss, "key cache miss counts drifted"
+        n_key_miss = key_miss_now
 
     K = args.steps
     # timed region: whole steps back to back; on every SAMPLE-th step the
@@ -388,7 +422,7 @@ def main():
         graph = {"error": repr(exc)}
     torch.cuda.synchronize()
 
-    ab = algorithmic_bytes(wl, sum(n_miss))
+    ab = algorithmic_bytes(wl, sum(n_miss), sum(n_key_miss or [0]))
     steps_per_s = 1000.0 / ms_per_step
     coarse_bytes = wl.batch * wl.ctx * wl.idx_dim // 2 + wl.batch * wl.idx_heads * (wl.idx_dim + 1)
     achieved = coarse_bytes / (coarse_ms * 1e-3) / 1e9
@@ -411,6 +445,8 @@ def main():
             "q_heads": wl.q_heads, "latent": wl.qk_dim, "v_dim": wl.v_dim,
             "hot_slots": wl.hot_slots, "miss_rate": wl.miss_rate,
             "pool": "pinned-host" if wl.pool_on_host else "hbm",
+            "keys": "pinned-host" if wl.keys_on_host else "hbm",
+            "key_slots": wl.key_slots, "key_miss_rate": wl.key_miss_rate,
             "replicas": args.replicas, "parallelism": "single-gpu",
         },
         "hbm_roofline_step": {
@@ -442,6 +478,19 @@ def main():
         },
         "graph": graph,
     }
+    if wl.keys_on_host:
+        full_keys = wl.batch * wl.ctx * wl.idx_dim
+        cache = wl.batch * wl.key_slots * (wl.idx_dim) + (wl.batch * wl.ctx * 4
+                                                           if wl.key_slots else 0)
+        pcie = sum(n_key_miss) * wl.idx_dim
+        result["key_store"] = {
+            "pcie_key_bytes_per_step": pcie,
+            "pcie_GBs_at_value": round(pcie * steps_per_s / 1e9, 2),
+            "hbm_bytes_full_keys": full_keys,
+            "hbm_bytes_key_cache_and_table": cache,
+            "hbm_saved_bytes": full_keys - cache,
+            "hbm_saved_per_request": (full_keys - cache) // wl.batch,
+        }
     coarse_ops = 2 * wl.batch * wl.ctx * wl.idx_heads * wl.idx_dim
     attn_flops = 2 * wl.batch * wl.q_heads * wl.topk * (wl.qk_dim + wl.v_dim)
     attn_ms = stage_ms[STAGES.index("attention")]

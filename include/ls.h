@@ -75,7 +75,7 @@ extern "C" {
 typedef struct ihipStream_t *ls_stream_t;
 typedef struct ihipEvent_t *ls_event_t;
 
-#define LS_ABI_VERSION 1
+#define LS_ABI_VERSION 2
 
 enum {
     LS_OK = 0,
@@ -96,9 +96,28 @@ enum {
 };
 
 /* Indexer shapes.  n_heads in [1, 64]; head_dim 64 or 128; n_cand >= 1;
- * topk >= 1 (topk > n_cand is allowed and pads); max_ctx in [1, 2^28).      */
+ * topk >= 1 (topk > n_cand is allowed and pads); max_ctx in [1, 2^28).
+ *
+ * Where the original int8 keys live (the refinement reads only the
+ * candidates' rows of them):
+ *   keys_on_host = 0: k8 [B, max_ctx, D] is device memory;
+ *   keys_on_host = 1: k8 is pinned, device-mapped host memory, read over
+ *     PCIe, so the full key history takes no HBM (only the compact keys
+ *     stay on the GPU).
+ *   key_slots > 0 adds a per-request indexer-key cache in device memory:
+ *     kcache [B, key_slots, D] int8 with kpos2slot [B, max_ctx] int32 (the
+ *     cache row of token t, -1 if absent; values outside [0, key_slots)
+ *     count as absent).  A candidate whose key is cached is read from the
+ *     cache and its k8 row is not touched.  The caller keeps the cache
+ *     coherent with k8 (a cached row must equal the token's key); the
+ *     library only reads it.  key_slots = 0: no cache, both pointers may be
+ *     NULL.  key_slots <= 2^24.
+ * [LeanSparse Abstract: the original indexer keys are kept off the GPU,
+ *  fetched only for candidate refinement, and held in an indexer-key cache
+ *  of their own that is reused across generation steps.]                    */
 typedef struct {
     int32_t batch, max_ctx, n_heads, head_dim, n_cand, topk;
+    int32_t keys_on_host, key_slots;
 } ls_idx_desc;
 
 /* Hot KV buffer of one layer.  Each request owns hot_slots resident rows
@@ -149,6 +168,8 @@ typedef struct {
     const int8_t *w_idx_dev;    /* [B, H] int8 per-head weights              */
     const uint8_t *kc_dev;      /* [B, max_ctx, D/2] packed compact keys     */
     const int8_t *k8_dev;       /* [B, max_ctx, D] original int8 keys        */
+    const int32_t *kpos2slot_dev;/* [B, max_ctx] key-cache row or -1 (nullable)*/
+    const int8_t *kcache_dev;   /* [B, key_slots, D] key cache (nullable)    */
     const int32_t *ctx_len_dev; /* [B] valid tokens per request              */
     int32_t *cand_dev;          /* out [B, n_cand] candidates                */
     int32_t *topk_dev;          /* out [B, topk] selected positions          */
@@ -205,14 +226,15 @@ int ls_index_coarse(const ls_idx_desc *desc, const int8_t *q_dev, const int8_t *
                     void *ws_dev, size_t ws_bytes, ls_stream_t stream);
 
 /* Stage 1b + 2: exact scores of the candidates from their original int8 keys
- * k8 [B,max_ctx,D], then the topk best.  cand as produced by ls_index_coarse
- * (ascending, -1 padded).  topk: out [B,topk] ascending, -1 padded;
- * topk_score: out [B,topk] int64 (nullable; 0 in padded slots).
+ * k8 [B,max_ctx,D] (or the key cache, see ls_idx_desc), then the topk best.
+ * cand as produced by ls_index_coarse (ascending, -1 padded).  topk: out
+ * [B,topk] ascending, -1 padded; topk_score: out [B,topk] int64 (nullable;
+ * 0 in padded slots).  kpos2slot / kcache: required iff desc->key_slots > 0.
  * [LeanSparse Abstract: original keys fetched only for refinement.]         */
 int ls_refine_topk(const ls_idx_desc *desc, const int8_t *q_dev, const int8_t *w_dev,
-                   const int8_t *k8_dev, const int32_t *cand_dev, const int32_t *ctx_len_dev,
-                   int32_t *topk_dev, int64_t *topk_score_dev, void *ws_dev, size_t ws_bytes,
-                   ls_stream_t stream);
+                   const int8_t *k8_dev, const int32_t *kpos2slot_dev, const int8_t *kcache_dev,
+                   const int32_t *cand_dev, const int32_t *ctx_len_dev, int32_t *topk_dev,
+                   int64_t *topk_score_dev, void *ws_dev, size_t ws_bytes, ls_stream_t stream);
 
 /* Stage 3: resolve the selected positions topk [B,topk] against
  * pos2slot [B,max_ctx] (slot of a resident token, -1 if absent).  A hit reads

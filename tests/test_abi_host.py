@@ -52,7 +52,7 @@ def test_struct_layouts_match_header(tmp_path):
 
 
 def test_version_and_error_string(lib):
-    assert lib.ls_abi_version() == 1
+    assert lib.ls_abi_version() == ls.ABI_VERSION == 2
     assert isinstance(lib.ls_last_error(), bytes)
 
 
@@ -104,9 +104,27 @@ def test_null_pointers_rejected(lib):
     d = idx()
     rc = lib.ls_index_coarse(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
     assert rc == ls.LS_E_ARG and b"null" in lib.ls_last_error()
-    rc = lib.ls_refine_topk(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, FAKE, None, FAKE,
-                            1 << 30, None)
+    rc = lib.ls_refine_topk(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE,
+                            None, FAKE, 1 << 30, None)
     assert rc == ls.LS_E_ARG
+
+
+@pytest.mark.parametrize("kw,kp,kc,needle", [
+    (dict(keys_on_host=2), None, None, b"keys_on_host"),
+    (dict(key_slots=-1), None, None, b"key_slots"),
+    (dict(key_slots=(1 << 24) + 1), FAKE, FAKE, b"key_slots"),
+    (dict(key_slots=1024), None, FAKE, b"kpos2slot"),
+    (dict(key_slots=1024), FAKE, None, b"kcache"),
+    (dict(key_slots=1024), FAKE, ctypes.c_void_p(0x100008), b"aligned"),
+])
+def test_refine_key_source_validated(lib, kw, kp, kc, needle):
+    # the key source is checked on the host before any launch (and before
+    # any pointer query), whatever the key cache and host-key flags say
+    d = idx(**kw)
+    rc = lib.ls_refine_topk(ctypes.byref(d), FAKE, FAKE, FAKE, kp, kc, FAKE, FAKE, FAKE, None,
+                            FAKE, 1 << 30, None)
+    assert rc == ls.LS_E_ARG
+    assert needle in lib.ls_last_error()
 
 
 def test_misaligned_rejected(lib):

@@ -8,7 +8,11 @@ so no oracle input comes from the GPU.  On every request, sampled or not,
 the test also checks what holds at any size: ascending, in-range, unique
 positions; selected scores equal to the oracle's exact score of those
 positions; hot-buffer rows and miss list consistent with the slot table; the
-gathered rows byte-equal to the pool rows."""
+gathered rows byte-equal to the pool rows.
+
+With the original keys on the host, the key cache is laid out the same way
+(the planted positions cached, the remaining rows random tokens), so the
+candidates' keys come from both the cache and the host store."""
 import numpy as np
 import pytest
 import torch
@@ -37,13 +41,20 @@ def run_full(ls, name, sample):
     keys = inp["keys"]
     kc = ls.pack_coarse(keys)
     ctx_len = torch.full((B,), L, dtype=torch.int32, device=DEV)
+    key_cache, k8 = {}, keys
+    if wl.key_slots:
+        kp, kcache, _ = synth.key_cache_fill(wl, planted, keys, DEV, miss_rate=0.0)
+        key_cache = dict(kpos2slot=kp, kcache=kcache)
+    if wl.keys_on_host:
+        k8 = keys.to("cpu").pin_memory()
     step = ls.DecodeStep(batch=B, max_ctx=L, idx_heads=wl.idx_heads, idx_dim=wl.idx_dim,
                          n_cand=wl.n_cand, topk=wl.topk, q_heads=wl.q_heads, qk_dim=wl.qk_dim,
                          v_dim=wl.v_dim, scale=wl.scale, hot_slots=wl.hot_slots,
-                         pool_on_host=wl.pool_on_host, device=DEV)
+                         pool_on_host=wl.pool_on_host, keys_on_host=wl.keys_on_host,
+                         key_slots=wl.key_slots, device=DEV)
     print("[fullsize] %s: step" % name, flush=True)
-    out, lse = step.run(q_idx=inp["q"], w_idx=inp["w"], kc=kc, k8=keys, ctx_len=ctx_len,
-                        q_attn=qa, pos2slot=pos2slot, hot_kv=hot, pool_kv=pool)
+    out, lse = step.run(q_idx=inp["q"], w_idx=inp["w"], kc=kc, k8=k8, ctx_len=ctx_len,
+                        q_attn=qa, pos2slot=pos2slot, hot_kv=hot, pool_kv=pool, **key_cache)
     torch.cuda.synchronize()
 
     cand, topk, score = np_(step.cand), np_(step.topk), np_(step.topk_score)
@@ -93,6 +104,10 @@ def run_full(ls, name, sample):
 
 def test_fullsize_decode_128k_b32(ls):
     run_full(ls, "decode-128k-b32", sample=[0, 31])
+
+
+def test_fullsize_decode_128k_b32_host_keys_with_key_cache(ls):
+    run_full(ls, "decode-128k-b32-hostkeys", sample=[17])
 
 
 def test_fullsize_decode_16k_b192_pinned_host_pool(ls):

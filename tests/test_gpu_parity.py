@@ -123,14 +123,17 @@ def test_index_coarse_every_token_a_candidate(ls):
 
 # ------------------------------------------------------ refine + top-k --
 
-def run_refine_case(ls, inp, ctx_len, C, K):
+def run_refine_case(ls, inp, ctx_len, C, K, k8=None, kpos2slot=None, kcache=None):
+    """k8: the key store the library reads (default: the keys, on the
+    device); the oracle always scores with the true keys inp["keys"]."""
     q, w, keys = inp["q"], inp["w"], inp["keys"]
     B = q.shape[0]
     cands = np.stack([oracle_cand(q[b].numpy(), w[b].numpy(), keys[b].numpy(), ctx_len[b], C)
                       for b in range(B)])
     cl = torch.tensor(ctx_len, dtype=torch.int32, device=DEV)
-    tk, sc = ls.refine_topk(q.to(DEV), w.to(DEV), keys.to(DEV), torch.from_numpy(cands).to(DEV),
-                            cl, K)
+    tk, sc = ls.refine_topk(q.to(DEV), w.to(DEV), keys.to(DEV) if k8 is None else k8,
+                            torch.from_numpy(cands).to(DEV), cl, K, kpos2slot=kpos2slot,
+                            kcache=kcache)
     tk, sc = np_(tk), np_(sc)
     for b in range(B):
         ep, es = oracle_topk(q[b].numpy(), w[b].numpy(), keys[b].numpy(), cands[b], K)
@@ -165,6 +168,58 @@ def test_refine_topk_ties(ls):
     for b in range(2):
         inp["keys"][b] = inp["keys"][b, :4][pick[b]]
     run_refine_case(ls, inp, [6000, 6000], 2000, 333)
+
+
+def test_refine_topk_pinned_host_keys(ls):
+    # the original keys stay in pinned host memory; the refinement reads the
+    # candidates' rows over PCIe
+    ctx = [SHRUNK.ctx, 3000, 200]
+    inp = idx_inputs(SHRUNK, ctx_len=ctx)
+    run_refine_case(ls, inp, ctx, SHRUNK.n_cand, SHRUNK.topk, k8=inp["keys"].pin_memory())
+
+
+def cached_key_store(wl, inp, ctx, C, rate, S, host):
+    """Key cache holding (1 - rate) of the oracle's candidates; the k8 rows of
+    cached tokens are overwritten with unrelated keys (so a read of k8 for a
+    cached token changes the result), and a few uncached tokens get slot
+    values outside [0, S), which must count as absent."""
+    q, w, keys = inp["q"], inp["w"], inp["keys"]
+    B = q.shape[0]
+    cands = torch.stack([torch.from_numpy(oracle_cand(q[b].numpy(), w[b].numpy(),
+                                                      keys[b].numpy(), ctx[b], C))
+                         for b in range(B)])
+    kp, kcache, n_miss = synth.key_cache_fill(wl, cands, keys, "cpu", miss_rate=rate,
+                                              key_slots=S)
+    store = keys.clone()
+    g = torch.Generator().manual_seed(23)
+    cached = kp >= 0
+    junk = torch.randint(-127, 128, (int(cached.sum()), keys.shape[2]), generator=g,
+                         dtype=torch.int32).to(torch.int8)
+    store[cached] = junk
+    for b in range(B):
+        miss = [int(t) for t in cands[b] if t >= 0 and kp[b, int(t)] < 0][:8]
+        for i, t in enumerate(miss):
+            kp[b, t] = S + i if i % 2 == 0 else -2 - i
+    assert (sum(n_miss) > 0) == (rate > 0)
+    return (store.pin_memory() if host else store.to(DEV)), kp.to(DEV), kcache.to(DEV)
+
+
+@pytest.mark.parametrize("host", [True, False], ids=["host-keys", "device-keys"])
+def test_refine_topk_key_cache(ls, host):
+    ctx = [SHRUNK.ctx, 3000, 200]
+    inp = idx_inputs(SHRUNK, ctx_len=ctx)
+    k8, kp, kcache = cached_key_store(SHRUNK, inp, ctx, SHRUNK.n_cand, 0.3, 1500, host)
+    run_refine_case(ls, inp, ctx, SHRUNK.n_cand, SHRUNK.topk, k8=k8, kpos2slot=kp,
+                    kcache=kcache)
+
+
+def test_refine_topk_key_cache_d64_all_cached(ls):
+    # head_dim 64, every candidate cached: k8 is never read for a candidate
+    wl = dataclasses.replace(TINY, batch=2, ctx=3000)
+    ctx = [3000, 1700]
+    inp = idx_inputs(wl, ctx_len=ctx)
+    k8, kp, kcache = cached_key_store(wl, inp, ctx, 1024, 0.0, 1024, True)
+    run_refine_case(ls, inp, ctx, 1024, 256, k8=k8, kpos2slot=kp, kcache=kcache)
 
 
 def three_level_patterns(q, w, keys, coarse):
@@ -417,7 +472,10 @@ def test_decode_step_tiny_mha(ls):
     assert_attention_close(out, lse, r["out"][None], r["lse"][None], "tiny step")
 
 
-def mla_step_case(ls, wl, ctx_len, device_pool=True):
+def mla_step_case(ls, wl, ctx_len, key_rate=None):
+    """With key_rate set, the original keys are in pinned host memory behind
+    a key cache that misses key_rate of the candidates (k8 rows of cached
+    tokens hold unrelated keys)."""
     B = wl.batch
     inp = idx_inputs(wl, ctx_len=ctx_len)
     qa = synth.attention_query(wl, "cpu")
@@ -430,17 +488,25 @@ def mla_step_case(ls, wl, ctx_len, device_pool=True):
                             cand, wl.topk)
         sel.append(torch.from_numpy(tk))
     pos2slot, hot, n_miss = synth.hot_fill(wl, torch.stack(sel), pool, "cpu")
+    keys = inp["keys"].to(DEV)
+    key_cache = {}
+    if key_rate is None:
+        k8, S = keys, 0
+    else:
+        S = wl.n_cand
+        k8, kp, kcache = cached_key_store(wl, inp, ctx_len, wl.n_cand, key_rate, S, True)
+        key_cache = dict(kpos2slot=kp, kcache=kcache)
     step = ls.DecodeStep(batch=B, max_ctx=wl.ctx, idx_heads=wl.idx_heads, idx_dim=wl.idx_dim,
                          n_cand=wl.n_cand, topk=wl.topk, q_heads=wl.q_heads, qk_dim=wl.qk_dim,
-                         v_dim=wl.v_dim, scale=wl.scale, hot_slots=wl.hot_slots)
+                         v_dim=wl.v_dim, scale=wl.scale, hot_slots=wl.hot_slots,
+                         keys_on_host=key_rate is not None, key_slots=S)
     for t in (step.cand, step.topk, step.topk_score, step.rows, step.n_miss, step.out, step.lse):
         poison_(t)
-    keys = inp["keys"].to(DEV)
     hot_dev = hot.to(DEV)
     cl = torch.tensor(ctx_len, dtype=torch.int32, device=DEV)
     out, lse = step.run(q_idx=inp["q"].to(DEV), w_idx=inp["w"].to(DEV), kc=ls.pack_coarse(keys),
-                        k8=keys, ctx_len=cl, q_attn=qa.to(DEV), pos2slot=pos2slot.to(DEV),
-                        hot_kv=hot_dev, pool_kv=pool.to(DEV))
+                        k8=k8, ctx_len=cl, q_attn=qa.to(DEV), pos2slot=pos2slot.to(DEV),
+                        hot_kv=hot_dev, pool_kv=pool.to(DEV), **key_cache)
     torch.cuda.synchronize()
     for b in range(B):
         hot_b = bits(hot[b]).copy()
@@ -462,6 +528,12 @@ def test_decode_step_shrunk_mla(ls):
     wl = dataclasses.replace(SHRUNK, batch=3, ctx=16384 + 5, n_cand=2048, topk=512,
                              hot_slots=1024, planted=163)
     mla_step_case(ls, wl, [wl.ctx, 9000, 300])
+
+
+def test_decode_step_host_keys_with_key_cache(ls):
+    wl = dataclasses.replace(SHRUNK, batch=3, ctx=8192 + 37, n_cand=1024, topk=256,
+                             hot_slots=512)
+    mla_step_case(ls, wl, [wl.ctx, 5000, 300], key_rate=0.25)
 
 
 def test_decode_step_deterministic(ls):

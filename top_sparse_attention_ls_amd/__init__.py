@@ -29,12 +29,14 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "ls.h")
 LS_OK, LS_E_ARG, LS_E_UNSUPPORTED, LS_E_WORKSPACE, LS_E_HIP = 0, -1, -2, -3, -4
 OP_COARSE, OP_REFINE, OP_HOT, OP_ATTN, OP_STEP, OP_PREFILL = 1, 2, 3, 4, 5, 6
 STEP_EVENTS = 7
+ABI_VERSION = 2
 
 _I32, _I64, _F32, _P = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
 
 
 class IdxDesc(ctypes.Structure):
-    _fields_ = [(n, _I32) for n in ("batch", "max_ctx", "n_heads", "head_dim", "n_cand", "topk")]
+    _fields_ = [(n, _I32) for n in ("batch", "max_ctx", "n_heads", "head_dim", "n_cand", "topk",
+                                    "keys_on_host", "key_slots")]
 
 
 class HotDesc(ctypes.Structure):
@@ -55,7 +57,8 @@ class StepDesc(ctypes.Structure):
 
 class StepIO(ctypes.Structure):
     _fields_ = [(n, _P) for n in (
-        "q_idx_dev", "w_idx_dev", "kc_dev", "k8_dev", "ctx_len_dev", "cand_dev", "topk_dev",
+        "q_idx_dev", "w_idx_dev", "kc_dev", "k8_dev", "kpos2slot_dev", "kcache_dev",
+        "ctx_len_dev", "cand_dev", "topk_dev",
         "topk_score_dev", "pos2slot_dev", "hot_kv_dev", "pool_kv_dev", "rows_dev", "n_miss_dev",
         "q_attn_dev", "k_cache_dev", "v_cache_dev", "out_dev", "lse_dev", "stage_events")]
 
@@ -78,6 +81,9 @@ def load():
                            "top_sparse_attention_ls_amd.build" % LIB_PATH)
     L = ctypes.CDLL(LIB_PATH)
     L.ls_abi_version.restype = _I32
+    if L.ls_abi_version() != ABI_VERSION:
+        raise RuntimeError("%s has ABI version %d, this binding expects %d; rebuild it"
+                           % (LIB_PATH, L.ls_abi_version(), ABI_VERSION))
     L.ls_last_error.restype = ctypes.c_char_p
     L.ls_last_hip_error.restype = _I32
     L.ls_workspace_size.argtypes = [_I32, _P]
@@ -85,7 +91,8 @@ def load():
     L.ls_workspace_init.argtypes = [_P, ctypes.c_size_t, _P]
     L.ls_pack_coarse.argtypes = [_P, _P, _I64, _I32, _P]
     L.ls_index_coarse.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
-    L.ls_refine_topk.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    L.ls_refine_topk.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                 _P]
     L.ls_hot_gather.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     L.ls_sparse_attn_decode.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     L.ls_decode_step.argtypes = [_P, _P, _P, ctypes.c_size_t, _P]
@@ -189,9 +196,10 @@ def pack_coarse(k8: torch.Tensor) -> torch.Tensor:
     return kc
 
 
-def idx_desc(q, keys_like_rows: int, n_cand: int, topk: int) -> IdxDesc:
+def idx_desc(q, keys_like_rows: int, n_cand: int, topk: int, keys_on_host: bool = False,
+             key_slots: int = 0) -> IdxDesc:
     B, H, D = q.shape
-    return IdxDesc(B, keys_like_rows, H, D, n_cand, topk)
+    return IdxDesc(B, keys_like_rows, H, D, n_cand, topk, 1 if keys_on_host else 0, key_slots)
 
 
 def index_coarse(q, w, kc, ctx_len, n_cand: int, topk: int = 1, ws=None) -> torch.Tensor:
@@ -208,19 +216,37 @@ def index_coarse(q, w, kc, ctx_len, n_cand: int, topk: int = 1, ws=None) -> torc
     return cand
 
 
-def refine_topk(q, w, k8, cand, ctx_len, topk: int, ws=None):
-    """Returns (topk [B,topk] int32, scores [B,topk] int64)."""
+def _key_cache(kpos2slot, kcache, B, L, D):
+    """Checks an optional key cache; returns its row count (0 without one)."""
+    if (kpos2slot is None) != (kcache is None):
+        raise ValueError("kpos2slot and kcache go together")
+    if kcache is None:
+        return 0
+    _need(kpos2slot, torch.int32, "kpos2slot", (B, L))
+    _need(kcache, torch.int8, "kcache", (B, kcache.shape[1], D))
+    if not (kpos2slot.is_cuda and kcache.is_cuda):
+        raise ValueError("the key cache and its slot table must be device memory")
+    return kcache.shape[1]
+
+
+def refine_topk(q, w, k8, cand, ctx_len, topk: int, ws=None, kpos2slot=None, kcache=None):
+    """k8 [B,L,D] int8 on the device or in pinned host memory (read over PCIe,
+    candidates' rows only); optional key cache kcache [B,S,D] int8 with its
+    slot table kpos2slot [B,L] int32 (-1: not cached), both on the device.
+    Returns (topk [B,topk] int32, scores [B,topk] int64)."""
     _need(q, torch.int8, "q")
     B, H, D = q.shape
     _need(w, torch.int8, "w", (B, H)), _need(k8, torch.int8, "k8", (B, k8.shape[1], D))
     _need(cand, torch.int32, "cand", (B, cand.shape[1]))
     _need(ctx_len, torch.int32, "ctx_len", (B,))
-    d = idx_desc(q, k8.shape[1], cand.shape[1], topk)
+    S = _key_cache(kpos2slot, kcache, B, k8.shape[1], D)
+    d = idx_desc(q, k8.shape[1], cand.shape[1], topk, keys_on_host=not k8.is_cuda, key_slots=S)
     ws = workspace(OP_REFINE, d, q.device) if ws is None else ws
     out = torch.empty((q.shape[0], topk), dtype=torch.int32, device=q.device)
     sc = torch.empty((q.shape[0], topk), dtype=torch.int64, device=q.device)
-    _check(load().ls_refine_topk(ctypes.byref(d), _p(q), _p(w), _p(k8), _p(cand), _p(ctx_len),
-                                 _p(out), _p(sc), _p(ws), ws.numel(), _stream()))
+    _check(load().ls_refine_topk(ctypes.byref(d), _p(q), _p(w), _p(k8), _p(kpos2slot),
+                                 _p(kcache), _p(cand), _p(ctx_len), _p(out), _p(sc), _p(ws),
+                                 ws.numel(), _stream()))
     return out, sc
 
 
@@ -278,9 +304,11 @@ class DecodeStep:
 
     def __init__(self, *, batch, max_ctx, idx_heads, idx_dim, n_cand, topk, q_heads, qk_dim,
                  v_dim, scale, hot_slots=0, kv_heads=1, kv_row_stride=None, kv_head_stride=0,
-                 pool_on_host=False, n_splits=0, device="cuda"):
+                 pool_on_host=False, keys_on_host=False, key_slots=0, n_splits=0,
+                 device="cuda"):
         self.use_hot = hot_slots > 0
-        idx = IdxDesc(batch, max_ctx, idx_heads, idx_dim, n_cand, topk)
+        idx = IdxDesc(batch, max_ctx, idx_heads, idx_dim, n_cand, topk, 1 if keys_on_host else 0,
+                      key_slots)
         row = qk_dim
         if self.use_hot:
             hot = HotDesc(batch, max_ctx, topk, hot_slots, row, 1 if pool_on_host else 0)
@@ -304,12 +332,18 @@ class DecodeStep:
         self.lse = torch.empty((batch, q_heads), dtype=torch.float32, device=dev)
 
     def run(self, *, q_idx, w_idx, kc, k8, ctx_len, q_attn, pos2slot=None, hot_kv=None,
-            pool_kv=None, k_cache=None, v_cache=None, events=None):
+            pool_kv=None, k_cache=None, v_cache=None, kpos2slot=None, kcache=None,
+            events=None):
         i, a, h = self.desc.idx, self.desc.attn, self.desc.hot
         B, L, H, D = i.batch, i.max_ctx, i.n_heads, i.head_dim
         _need(q_idx, torch.int8, "q_idx", (B, H, D)), _need(w_idx, torch.int8, "w_idx", (B, H))
         _need(kc, torch.uint8, "kc", (B, L, D // 2)), _need(k8, torch.int8, "k8", (B, L, D))
         _need(ctx_len, torch.int32, "ctx_len", (B,))
+        if k8.is_cuda == bool(i.keys_on_host):
+            raise ValueError("k8 must be %s memory for this step" %
+                             ("pinned host" if i.keys_on_host else "device"))
+        if _key_cache(kpos2slot, kcache, B, L, D) != i.key_slots:
+            raise ValueError("this step was built for a key cache of %d rows" % i.key_slots)
         _need(q_attn, torch.bfloat16, "q_attn", (B, a.n_q_heads, a.qk_dim))
         if self.use_hot:
             row = h.row_elems
@@ -328,6 +362,8 @@ class DecodeStep:
         io = StepIO()
         io.q_idx_dev, io.w_idx_dev = q_idx.data_ptr(), w_idx.data_ptr()
         io.kc_dev, io.k8_dev, io.ctx_len_dev = kc.data_ptr(), k8.data_ptr(), ctx_len.data_ptr()
+        if i.key_slots:
+            io.kpos2slot_dev, io.kcache_dev = kpos2slot.data_ptr(), kcache.data_ptr()
         io.cand_dev, io.topk_dev = self.cand.data_ptr(), self.topk.data_ptr()
         io.topk_score_dev = self.topk_score.data_ptr()
         if self.use_hot:

@@ -23,10 +23,16 @@ namespace ls {
 // hot slot.  Per-head dots are exact in int32 (|dot| < 2^21);
 // w * relu(dot) < 2^28 and groups of four stay below 2^30 before widening
 // to int64.  Invalid candidates (-1) score 0 and are never selected.
-template <int D, int HT>
+// With a key cache (KC), a candidate whose key row is resident in the
+// request's cache (kslot[t] in [0, key_slots)) is read from there, in HBM;
+// the others from k8, which may then be pinned host memory read over PCIe.
+// The slot lookup adds one dependent load before the key load.
+template <int D, int HT, bool KC>
 __global__ __launch_bounds__(256) void k_refine(const int8_t* __restrict__ q,
                                                 const int8_t* __restrict__ w,
                                                 const int8_t* __restrict__ k8,
+                                                const int32_t* __restrict__ kslot,
+                                                const int8_t* __restrict__ kcache, int key_slots,
                                                 const int32_t* __restrict__ cand,
                                                 int64_t* __restrict__ fs,
                                                 const int32_t* __restrict__ pos2slot,
@@ -40,6 +46,8 @@ __global__ __launch_bounds__(256) void k_refine(const int8_t* __restrict__ q,
 
   const int c_base = blockIdx.x * kRefinePerWG + wave_id() * 64;
   const int8_t* kb = k8 + (size_t)b * max_ctx * D;
+  const int32_t* ksb = KC ? kslot + (size_t)b * max_ctx : nullptr;
+  const int8_t* kcb = KC ? kcache + (size_t)b * key_slots * D : nullptr;
   // Every load below is unconditional (indices clamped, results selected
   // afterwards): a load under a divergent condition becomes a branch that
   // waits for it, which would serialise the whole prologue.
@@ -56,10 +64,15 @@ __global__ __launch_bounds__(256) void k_refine(const int8_t* __restrict__ q,
     const int32_t pr = cb[min(c, C - 1)];
     pos[tt] = (c < C) ? pr : -1;
     const int p = max(pos[tt], 0);
+    const int8_t* row = kb + (size_t)p * D;
+    if (KC) {
+      const int32_t ks = ksb[p];
+      row = ((uint32_t)ks < (uint32_t)key_slots) ? kcb + (size_t)ks * D : row;
+    }
 #pragma unroll
     for (int mf = 0; mf < NMF; mf++) {
       const int off = (D == 128) ? 32 * g + 16 * mf : 16 * g;
-      raw[tt][mf] = *(const v4i*)(kb + (size_t)p * D + off);
+      raw[tt][mf] = *(const v4i*)(row + off);
     }
   }
 
@@ -454,16 +467,20 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(
   if (tid == 0 && n_miss) n_miss[b] = p2s ? (int32_t)tot_miss : 0;
 }
 
-hipError_t launch_refine_topk(const int8_t* q, const int8_t* w, const int8_t* k8,
+hipError_t launch_refine_topk(const int8_t* q, const int8_t* w, const KeySource& keys,
                               const int32_t* cand, const RefineWS& ws, int32_t* topk,
                               int64_t* topk_score, const int32_t* pos2slot, int32_t* rows,
                               int32_t* n_miss, int hot_slots, int B, int H, int D, int max_ctx,
                               int C, int K, hipStream_t st) {
   dim3 grid((C + kRefinePerWG - 1) / kRefinePerWG, B);
   const int HT = (H + 15) / 16;
+#define LS_REFINE_KC(DD, TT, KC)                                                             \
+  hipLaunchKernelGGL((k_refine<DD, TT, KC>), grid, dim3(256), 0, st, q, w, keys.k8, keys.kslot, \
+                     keys.kcache, keys.key_slots, cand, ws.fs, pos2slot, ws.slot, H, max_ctx, C)
 #define LS_REFINE(DD, TT)                                                                     \
-  hipLaunchKernelGGL((k_refine<DD, TT>), grid, dim3(256), 0, st, q, w, k8, cand, ws.fs,     \
-                     pos2slot, ws.slot, H, max_ctx, C)
+  do {                                                                                        \
+    if (keys.key_slots > 0) LS_REFINE_KC(DD, TT, true); else LS_REFINE_KC(DD, TT, false);     \
+  } while (0)
   if (D == 128) {
     if (HT == 1) LS_REFINE(128, 1); else if (HT == 2) LS_REFINE(128, 2);
     else if (HT == 3) LS_REFINE(128, 3); else LS_REFINE(128, 4);
@@ -472,6 +489,7 @@ hipError_t launch_refine_topk(const int8_t* q, const int8_t* w, const int8_t* k8
     else if (HT == 3) LS_REFINE(64, 3); else LS_REFINE(64, 4);
   }
 #undef LS_REFINE
+#undef LS_REFINE_KC
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 #define LS_TOPK(P)                                                                           \

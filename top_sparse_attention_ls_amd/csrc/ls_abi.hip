@@ -56,6 +56,10 @@ int check_idx(const ls_idx_desc* d) {
     return fail(LS_E_UNSUPPORTED, "n_heads > 64 is not supported (got %d)", d->n_heads);
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(LS_E_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", d->head_dim);
+  if (d->keys_on_host != 0 && d->keys_on_host != 1)
+    return fail(LS_E_ARG, "keys_on_host must be 0 or 1");
+  if (d->key_slots < 0 || d->key_slots > (1 << 24))
+    return fail(LS_E_ARG, "key_slots must be in [0, 2^24] (got %d)", d->key_slots);
   return LS_OK;
 }
 
@@ -303,24 +307,53 @@ int check_idx_ptrs(const int8_t* q, const int8_t* w, const int32_t* ctx_len) {
   return LS_OK;
 }
 
-// A pool declared host-resident must be pinned, device-mapped host memory;
-// the kernels read it through its device alias.  Anything else is rejected
-// here, before a kernel could touch an unmapped address.
-int resolve_pool(const void* pool, int on_host, const void** dev_ptr) {
+// A buffer declared host-resident (the pool, the original int8 keys) must
+// be pinned, device-mapped host memory; the kernels read it through its
+// device alias.  Anything else is rejected here, before a kernel could touch
+// an unmapped address.
+int resolve_host(const void* p, int on_host, const void** dev_ptr, const char* what) {
   if (!on_host) {
-    *dev_ptr = pool;
+    *dev_ptr = p;
     return LS_OK;
   }
   hipPointerAttribute_t attr;
-  hipError_t e = hipPointerGetAttributes(&attr, pool);
+  hipError_t e = hipPointerGetAttributes(&attr, p);
   if (e != hipSuccess) {
     (void)hipGetLastError();
-    return fail(LS_E_ARG, "pool_on_host = 1 but the pool is not pinned host memory (%s)",
+    return fail(LS_E_ARG, "%s is declared host-resident but is not pinned host memory (%s)", what,
                 hipGetErrorString(e));
   }
   if (attr.type != hipMemoryTypeHost || attr.devicePointer == nullptr)
-    return fail(LS_E_ARG, "pool_on_host = 1 but the pool is not device-mapped pinned host memory");
+    return fail(LS_E_ARG, "%s is declared host-resident but is not device-mapped pinned host memory",
+                what);
   *dev_ptr = attr.devicePointer;
+  return LS_OK;
+}
+
+int resolve_pool(const void* pool, int on_host, const void** dev_ptr) {
+  return resolve_host(pool, on_host, dev_ptr, "the pool (pool_on_host = 1)");
+}
+
+// The refinement's key source: k8 (through its device alias when it is host
+// memory) and, with key_slots > 0, the device-resident key cache.
+int resolve_keys(const ls_idx_desc* d, const int8_t* k8, const int32_t* kpos2slot,
+                 const int8_t* kcache, ls::KeySource* ks) {
+  LS_NONNULL(k8);
+  LS_ALIGNED(k8);
+  const void* p = nullptr;
+  LS_TRY(resolve_host(k8, d->keys_on_host, &p, "k8 (keys_on_host = 1)"));
+  ks->k8 = (const int8_t*)p;
+  ks->key_slots = d->key_slots;
+  ks->kslot = nullptr;
+  ks->kcache = nullptr;
+  if (d->key_slots > 0) {
+    LS_NONNULL(kpos2slot);
+    LS_NONNULL(kcache);
+    LS_ALIGNED(kpos2slot);
+    LS_ALIGNED(kcache);
+    ks->kslot = kpos2slot;
+    ks->kcache = kcache;
+  }
   return LS_OK;
 }
 
@@ -380,21 +413,21 @@ int ls_index_coarse(const ls_idx_desc* desc, const int8_t* q_dev, const int8_t* 
 }
 
 int ls_refine_topk(const ls_idx_desc* desc, const int8_t* q_dev, const int8_t* w_dev,
-                   const int8_t* k8_dev, const int32_t* cand_dev, const int32_t* ctx_len_dev,
-                   int32_t* topk_dev, int64_t* topk_score_dev, void* ws_dev, size_t ws_bytes,
-                   ls_stream_t stream) {
+                   const int8_t* k8_dev, const int32_t* kpos2slot_dev, const int8_t* kcache_dev,
+                   const int32_t* cand_dev, const int32_t* ctx_len_dev, int32_t* topk_dev,
+                   int64_t* topk_score_dev, void* ws_dev, size_t ws_bytes, ls_stream_t stream) {
   LS_TRY(check_idx(desc));
   LS_TRY(check_idx_ptrs(q_dev, w_dev, ctx_len_dev));
-  LS_NONNULL(k8_dev);
   LS_NONNULL(cand_dev);
   LS_NONNULL(topk_dev);
-  LS_ALIGNED(k8_dev);
   LS_TRY(check_ws(LS_OP_REFINE, desc, ws_dev, ws_bytes));
+  ls::KeySource k8;
+  LS_TRY(resolve_keys(desc, k8_dev, kpos2slot_dev, kcache_dev, &k8));
   Carve c;
   c.base = (char*)ws_dev;
   ls::RefineWS ws;
   carve_refine(c, desc, &ws);
-  LS_HIP(ls::launch_refine_topk(q_dev, w_dev, k8_dev, cand_dev, ws, topk_dev, topk_score_dev,
+  LS_HIP(ls::launch_refine_topk(q_dev, w_dev, k8, cand_dev, ws, topk_dev, topk_score_dev,
                                 nullptr, nullptr, nullptr, 0, desc->batch, desc->n_heads,
                                 desc->head_dim, desc->max_ctx, desc->n_cand, desc->topk,
                                 (hipStream_t)stream),
@@ -501,14 +534,12 @@ int ls_decode_step(const ls_step_desc* desc, const ls_step_io* io, void* ws_dev,
     return fail(LS_E_ARG, "attention batch/topk must match the indexer's");
   LS_TRY(check_idx_ptrs(io->q_idx_dev, io->w_idx_dev, io->ctx_len_dev));
   LS_NONNULL(io->kc_dev);
-  LS_NONNULL(io->k8_dev);
   LS_NONNULL(io->cand_dev);
   LS_NONNULL(io->topk_dev);
   LS_NONNULL(io->q_attn_dev);
   LS_NONNULL(io->out_dev);
   LS_NONNULL(io->lse_dev);
   LS_ALIGNED(io->kc_dev);
-  LS_ALIGNED(io->k8_dev);
   LS_ALIGNED(io->q_attn_dev);
   LS_ALIGNED(io->out_dev);
   const void *kb, *vb;
@@ -542,6 +573,8 @@ int ls_decode_step(const ls_step_desc* desc, const ls_step_io* io, void* ws_dev,
   LS_TRY(check_ws(LS_OP_STEP, desc, ws_dev, ws_bytes));
   const void* pool = nullptr;
   if (desc->use_hot) LS_TRY(resolve_pool(io->pool_kv_dev, desc->hot.pool_on_host, &pool));
+  ls::KeySource k8;
+  LS_TRY(resolve_keys(id, io->k8_dev, io->kpos2slot_dev, io->kcache_dev, &k8));
 
   Carve c;
   c.base = (char*)ws_dev;
@@ -562,7 +595,7 @@ int ls_decode_step(const ls_step_desc* desc, const ls_step_io* io, void* ws_dev,
   LS_TRY(run_coarse(id, io->q_idx_dev, io->w_idx_dev, io->kc_dev, io->ctx_len_dev, io->cand_dev,
                     cws, st, ev));
   if (ev && ev[2]) LS_HIP(hipEventRecord((hipEvent_t)ev[2], st), "event record");
-  LS_HIP(ls::launch_refine_topk(io->q_idx_dev, io->w_idx_dev, io->k8_dev, io->cand_dev, rws,
+  LS_HIP(ls::launch_refine_topk(io->q_idx_dev, io->w_idx_dev, k8, io->cand_dev, rws,
                                 io->topk_dev, io->topk_score_dev,
                                 desc->use_hot ? io->pos2slot_dev : nullptr,
                                 desc->use_hot ? io->rows_dev : nullptr,

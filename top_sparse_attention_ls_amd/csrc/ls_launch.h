@@ -55,6 +55,17 @@ __host__ __device__ inline int emit_chunks_per_run(int rows, int n_chunks) {
 using CoarseWS = SelectWS<int32_t>;  // coarse scores, kCoarseBins buckets
 using WideWS = SelectWS<int64_t>;    // int64 scores, 7552 buckets
 
+// Where the refinement reads a candidate's original int8 key row: k8
+// [B, max_ctx, D] (device memory, or the device alias of pinned host
+// memory), unless key_slots > 0 and kslot[b, t] names a row of the request's
+// key cache kcache [B, key_slots, D] in device memory.
+struct KeySource {
+  const int8_t* k8;
+  const int32_t* kslot;
+  const int8_t* kcache;
+  int key_slots;
+};
+
 struct RefineWS {
   int64_t* fs;         // [B, n_cand]
   int32_t* slot;       // [B, n_cand] hot slot of each candidate (with a slot table)
@@ -91,7 +102,7 @@ hipError_t launch_wide_emit(const int32_t* ctx_len, const WideWS& ws, int32_t* o
 
 // Refine + top-k; with pos2slot != nullptr also the hot-buffer resolve
 // (rows, n_miss, miss list in ws.miss_pos).
-hipError_t launch_refine_topk(const int8_t* q, const int8_t* w, const int8_t* k8,
+hipError_t launch_refine_topk(const int8_t* q, const int8_t* w, const KeySource& keys,
                               const int32_t* cand, const RefineWS& ws, int32_t* topk,
                               int64_t* topk_score, const int32_t* pos2slot, int32_t* rows,
                               int32_t* n_miss, int hot_slots, int B, int H, int D, int max_ctx,

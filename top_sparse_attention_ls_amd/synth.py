@@ -29,7 +29,8 @@ import numpy as np
 import torch
 
 # tensor ids for seeding
-T_QIDX, T_WIDX, T_KEYS, T_PLANT, T_QATT, T_POOL, T_HOT, T_KCACHE, T_VCACHE, T_RAGGED = range(10)
+(T_QIDX, T_WIDX, T_KEYS, T_PLANT, T_QATT, T_POOL, T_HOT, T_KCACHE, T_VCACHE, T_RAGGED,
+ T_KEYCACHE) = range(11)
 
 
 @dataclass(frozen=True)
@@ -55,6 +56,9 @@ class Workload:
     hot_slots: int = 0               # 0: no hot buffer
     miss_rate: float = 0.0
     pool_on_host: bool = False
+    keys_on_host: bool = False       # original int8 keys in pinned host memory
+    key_slots: int = 0               # rows of the per-request indexer-key cache (0: none)
+    key_miss_rate: float = 0.0       # share of the candidates whose key is not cached
     # prefill only
     n_query: int = 0
     layers: int = 0
@@ -75,6 +79,14 @@ WORKLOADS = {
                                 idx_heads=64, idx_dim=128, n_cand=4096, topk=2048,
                                 planted=163, hot_slots=4096, miss_rate=0.4,
                                 pool_on_host=True),
+    # the same step with the original int8 keys off the GPU (pinned host) and
+    # a 16384-row indexer-key cache per request that holds 80% of the step's
+    # candidates
+    "decode-128k-b32-hostkeys": Workload("decode-128k-b32-hostkeys", 1001, batch=32,
+                                         ctx=131072, idx_heads=64, idx_dim=128, n_cand=8192,
+                                         topk=2048, planted=1310, hot_slots=4096,
+                                         miss_rate=0.2, keys_on_host=True, key_slots=16384,
+                                         key_miss_rate=0.2),
     # decode near 1M context, 4 requests, planted tokens in 8 bursts of 512
     "decode-950k-b4": Workload("decode-950k-b4", 1003, batch=4, ctx=950000, idx_heads=64,
                                idx_dim=128, n_cand=16384, topk=2048, bursts=(8, 512),
@@ -246,6 +258,48 @@ def hot_fill(wl: Workload, selected: torch.Tensor, pool: torch.Tensor, device,
         hot[b, res_slot.to(torch.int64).to(device)] = src.to(device)
         n_miss.append(nm)
     return pos2slot, hot, n_miss
+
+
+def key_cache_fill(wl: Workload, cand: torch.Tensor, keys: torch.Tensor, device,
+                   miss_rate=None, key_slots=None):
+    """Lay out the indexer-key cache so that a fixed share of a known
+    candidate set misses it.
+
+    cand: [B, n] int32 candidate positions per request (-1 padding), as
+    computed by the caller; keys: [B, L, D] int8 (any device).  For each
+    request, round(rate * n_valid) candidates are left out; the others are
+    made resident at random distinct rows, and the remaining rows hold
+    random non-candidate tokens.  Cached rows are byte copies of the keys.
+    Returns kpos2slot [B, L] int32, kcache [B, S, D] int8, n_key_miss list."""
+    rate = wl.key_miss_rate if miss_rate is None else miss_rate
+    S = wl.key_slots if key_slots is None else key_slots
+    B, n = cand.shape
+    L, D = keys.shape[1], keys.shape[2]
+    cand_cpu = cand.to("cpu")
+    kpos2slot = torch.full((B, L), -1, dtype=torch.int32, device=device)
+    kcache = torch.zeros((B, S, D), dtype=torch.int8, device=device)
+    n_miss = []
+    for b in range(B):
+        g = generator(wl.seed, T_KEYCACHE, b, "cpu")
+        valid = cand_cpu[b][cand_cpu[b] >= 0].to(torch.int64)
+        n_val = int(valid.numel())
+        nm = int(math.floor(rate * n_val + 0.5))
+        n_hit = n_val - nm
+        if n_hit > S:
+            raise ValueError("a key cache of %d rows cannot hold %d candidates" % (S, n_hit))
+        hits = valid[torch.randperm(n_val, generator=g)[:n_hit]]
+        rows = torch.randperm(S, generator=g)
+        mask = torch.ones(L, dtype=torch.bool)
+        mask[valid] = False
+        others = torch.randperm(L, generator=g)
+        others = others[mask[others]][: max(S - n_hit, 0)]
+        res_pos = torch.cat([hits, others])
+        res_row = rows[: res_pos.numel()].to(torch.int32)
+        kpos2slot[b, res_pos.to(device)] = res_row.to(device)
+        src = keys[b].index_select(0, res_pos.to(keys.device))
+        kcache[b, res_row.to(torch.int64).to(device)] = src.to(device)
+        n_miss.append(nm)
+    return kpos2slot, kcache, n_miss
 
 
 def ragged_lengths(wl: Workload, batch: int, max_ctx: int, min_ctx: int = 0) -> list:
