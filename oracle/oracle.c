@@ -206,6 +206,114 @@ int32_t orc_hot_resolve(const int32_t *sel, int32_t n_sel, const int32_t *pos2sl
     return n_miss;
 }
 
+/* ---------------------------------------------------------- cache commit --
+ *
+ * [LS] Abstract: the indexer-key cache and the KV cache are kept apart and
+ * reused across generation steps; [XM] digest, hot buffer section: a step
+ * fetches only the selected rows missing from the buffer.  Neither page
+ * gives an insertion or eviction policy.  Reading (least recently used):
+ *
+ *   A cache of n_slots rows serves one request.  stamp[s] is the step that
+ *   last used slot s (0: never), slot2pos[s] the position it holds (-1: free),
+ *   pos2slot[t] the slot of position t (-1: absent).  One step uses the
+ *   entries pos[0..n) (ascending positions, -1 = padding, skipped):
+ *     1. an entry t with 0 <= pos2slot[t] < n_slots is a hit: its slot's
+ *        stamp becomes now;
+ *     2. an entry with pos2slot[t] < 0 is a miss; misses are numbered
+ *        j = 0, 1, ... in entry order;
+ *     3. victims: among the slots not hit in this step, the
+ *        min(#misses, #slots not hit) smallest by (stamp ascending, slot
+ *        ascending); they are then taken in ascending slot order;
+ *     4. miss j (while victims remain) moves into victim v_j: the position
+ *        the victim held (if any) loses its slot, pos2slot[t_j] = v_j,
+ *        slot2pos[v_j] = t_j, stamp[v_j] = now.
+ *   dst[i] is entry i's slot after the commit (hits: their slot; inserted
+ *   misses: their victim; misses left out and padding: -1).  Entries whose
+ *   pos2slot value lies at or beyond n_slots are neither hits nor misses.
+ *   Returns the number of misses inserted.                                  */
+typedef struct {
+    uint32_t stamp;
+    int32_t slot;
+} stamped_slot;
+
+static int by_stamp_then_slot(const void *a, const void *b)
+{
+    const stamped_slot *x = (const stamped_slot *)a, *y = (const stamped_slot *)b;
+    if (x->stamp != y->stamp)
+        return x->stamp < y->stamp ? -1 : 1;
+    return (x->slot > y->slot) - (x->slot < y->slot);
+}
+
+static int by_int32(const void *a, const void *b)
+{
+    int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+    return (x > y) - (x < y);
+}
+
+int32_t orc_cache_commit(const int32_t *pos, int32_t n, int32_t n_slots, uint32_t now,
+                         int32_t *pos2slot, int64_t n_pos, int32_t *slot2pos, uint32_t *stamp,
+                         int32_t *dst)
+{
+    char *hit = (char *)calloc((size_t)n_slots + 1, 1);
+    stamped_slot *order = (stamped_slot *)malloc(((size_t)n_slots + 1) * sizeof(stamped_slot));
+    int32_t *victim = (int32_t *)malloc(((size_t)n_slots + 1) * sizeof(int32_t));
+    char *miss = (char *)calloc((size_t)n + 1, 1);
+    int32_t n_miss = 0, n_hit = 0, n_free = 0;
+
+    /* 1. hits (and 2. the misses, marked from the same table state) */
+    for (int32_t i = 0; i < n; i++) {
+        dst[i] = -1;
+        if (pos[i] < 0)
+            continue;
+        int32_t s = pos2slot[pos[i]];
+        if (s >= 0 && s < n_slots) {
+            dst[i] = s;
+            if (!hit[s]) {
+                hit[s] = 1;
+                n_hit++;
+            }
+        } else if (s < 0) {
+            miss[i] = 1;
+            n_miss++;
+        }
+    }
+    /* 3. victims: the oldest slots not hit, then in slot order */
+    for (int32_t s = 0; s < n_slots; s++) {
+        if (!hit[s]) {
+            order[n_free].stamp = stamp[s];
+            order[n_free].slot = s;
+            n_free++;
+        }
+    }
+    qsort(order, (size_t)n_free, sizeof(stamped_slot), by_stamp_then_slot);
+    int32_t n_vic = n_miss < n_free ? n_miss : n_free;
+    for (int32_t j = 0; j < n_vic; j++)
+        victim[j] = order[j].slot;
+    qsort(victim, (size_t)n_vic, sizeof(int32_t), by_int32);
+    for (int32_t s = 0; s < n_slots; s++)
+        if (hit[s])
+            stamp[s] = now;
+    /* 2 + 4. misses in entry order move into the victims */
+    int32_t j = 0;
+    for (int32_t i = 0; i < n && j < n_vic; i++) {
+        if (!miss[i])
+            continue;
+        int32_t v = victim[j++];
+        int32_t old = slot2pos[v];
+        if (old >= 0 && old < n_pos)
+            pos2slot[old] = -1;
+        pos2slot[pos[i]] = v;
+        slot2pos[v] = pos[i];
+        stamp[v] = now;
+        dst[i] = v;
+    }
+    free(hit);
+    free(order);
+    free(victim);
+    free(miss);
+    return n_vic;
+}
+
 /* Fetch the missed rows from the full-history pool into the hot buffer's
  * scratch rows: hot[hot_slots + j] := pool[miss_pos[j]] (a byte copy of
  * row_bytes bytes).                                                         */

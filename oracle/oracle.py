@@ -65,6 +65,8 @@ def _declare(L):
     L.orc_hot_resolve.argtypes = [_P, _I32, _P, _I32, _P, _P]
     L.orc_hot_resolve.restype = _I32
     L.orc_hot_gather.argtypes = [_P, _I64, _P, _I32, _P, _I32]
+    L.orc_cache_commit.argtypes = [_P, _I32, _I32, ctypes.c_uint32, _P, _I64, _P, _P, _P]
+    L.orc_cache_commit.restype = _I32
     L.orc_attention.argtypes = [_P, _I32, _I32, _I32, _I32, _P, _P, _I64, _I64, _P, _I32,
                                 _D, _P, _P]
     L.orc_decode_request.argtypes = [_P, _P, _I32, _I32, _P, _I32, _I32, _I32, _P, _I32,
@@ -168,6 +170,22 @@ def hot_gather(pool: np.ndarray, miss_pos: np.ndarray, hot: np.ndarray, hot_slot
     assert hot.strides[0] == row_bytes
     mp = _c(miss_pos, np.int32)
     lib().orc_hot_gather(_ptr(pool), row_bytes, _ptr(mp), mp.shape[0], _ptr(hot), int(hot_slots))
+
+
+def cache_commit(pos: np.ndarray, n_slots: int, now: int, pos2slot: np.ndarray,
+                 slot2pos: np.ndarray, stamp: np.ndarray):
+    """Least-recently-used commit of one step's entries into one request's
+    cache (see orc_cache_commit).  pos2slot [L] int32, slot2pos [n_slots]
+    int32 and stamp [n_slots] uint32 are updated in place (they must be
+    contiguous arrays of those types).  Returns (dst [n] int32, n_inserted)."""
+    for a, t in ((pos2slot, np.int32), (slot2pos, np.int32), (stamp, np.uint32)):
+        assert a.dtype == t and a.flags.c_contiguous
+    assert slot2pos.shape[0] == stamp.shape[0] == n_slots
+    p = _c(pos, np.int32)
+    dst = np.empty(max(p.shape[0], 1), np.int32)
+    n_ins = lib().orc_cache_commit(_ptr(p), p.shape[0], int(n_slots), int(now), _ptr(pos2slot),
+                                   pos2slot.shape[0], _ptr(slot2pos), _ptr(stamp), _ptr(dst))
+    return dst[: p.shape[0]], int(n_ins)
 
 
 # ------------------------------------------------------------- attention --

@@ -412,3 +412,120 @@ def test_decode_request_with_hot_buffer_end_to_end():
                                    bits_to_f64(pool[top])[:, :dv], 0.07)
     np.testing.assert_allclose(r["out"], e_out, atol=1e-12)
     np.testing.assert_allclose(r["lse"], e_lse, atol=1e-12)
+
+
+# ------------------------------------------------------------ cache commit --
+# Pins of orc_cache_commit (least-recently-used insertion of a step's misses,
+# a reading: the pages name caches reused across steps but no policy).
+
+def fresh_cache(n_slots, n_pos):
+    return (np.full(n_pos, -1, np.int32), np.full(n_slots, -1, np.int32),
+            np.zeros(n_slots, np.uint32))
+
+
+def test_cache_commit_hand_example():
+    # four slots holding positions 10..13, last used at steps 5, 2, 2, 7
+    p2s, s2p, st = fresh_cache(4, 64)
+    for s_, t in enumerate([10, 11, 12, 13]):
+        p2s[t], s2p[s_] = s_, t
+    st[:] = [5, 2, 2, 7]
+    dst, n_ins = orc.cache_commit(np.array([11, 20, 13, 30, 40], np.int32), 4, 9, p2s, s2p, st)
+    # hits 11 (slot 1) and 13 (slot 3); misses 20, 30, 40; the two slots not
+    # hit (0 at step 5, 2 at step 2) are both victims, taken in slot order
+    assert dst.tolist() == [1, 0, 3, 2, -1] and n_ins == 2
+    assert s2p.tolist() == [20, 11, 30, 13]
+    assert st.tolist() == [9, 9, 9, 9]
+    assert p2s[10] == -1 and p2s[12] == -1 and p2s[20] == 0 and p2s[30] == 2 and p2s[40] == -1
+    assert p2s[11] == 1 and p2s[13] == 3
+
+
+def test_cache_commit_oldest_first_then_lowest_slot():
+    # six slots, one miss at a time: the victim is always the slot with the
+    # oldest stamp, the lowest index among equal stamps
+    p2s, s2p, st = fresh_cache(6, 100)
+    for s_ in range(6):
+        p2s[50 + s_], s2p[s_] = s_, 50 + s_
+    st[:] = [4, 1, 3, 1, 2, 9]
+    expect = [1, 3, 4, 2, 0, 5]
+    for k, e in enumerate(expect):
+        dst, n_ins = orc.cache_commit(np.array([k], np.int32), 6, 10 + k, p2s, s2p, st)
+        assert dst.tolist() == [e] and n_ins == 1
+
+
+def test_cache_commit_fills_free_slots_in_order_and_padding_is_skipped():
+    p2s, s2p, st = fresh_cache(8, 40)
+    dst, n_ins = orc.cache_commit(np.array([3, -1, 7, 9, -1], np.int32), 8, 1, p2s, s2p, st)
+    assert dst.tolist() == [0, -1, 1, 2, -1] and n_ins == 3
+    assert s2p.tolist()[:3] == [3, 7, 9] and st.tolist() == [1, 1, 1, 0, 0, 0, 0, 0]
+
+
+def test_cache_commit_more_misses_than_slots():
+    p2s, s2p, st = fresh_cache(3, 40)
+    dst, n_ins = orc.cache_commit(np.arange(5, 10, dtype=np.int32), 3, 1, p2s, s2p, st)
+    assert dst.tolist() == [0, 1, 2, -1, -1] and n_ins == 3
+    # next step: hits on 5 and 7 keep their slots; only slot 1 may be evicted
+    dst, n_ins = orc.cache_commit(np.array([5, 7, 20, 21], np.int32), 3, 2, p2s, s2p, st)
+    assert dst.tolist() == [0, 2, 1, -1] and n_ins == 1
+    assert p2s[6] == -1 and s2p.tolist() == [5, 20, 7]
+
+
+class ListLRU:
+    """An independent model of the same policy: the resident positions kept
+    in one recency list (least recent first).  After each step the slots the
+    step used move to the most-recent end in ascending slot order (equal
+    recency is broken by slot index); victims are the first entries of the
+    list that the step did not hit."""
+
+    def __init__(self, n_slots):
+        self.order = list(range(n_slots))   # slots, least recent first
+        self.slot_pos = [-1] * n_slots
+        self.where = {}
+
+    def step(self, entries):
+        hit = sorted({self.where[t] for t in entries if t >= 0 and t in self.where})
+        misses = [t for t in entries if t >= 0 and t not in self.where]
+        free = [s for s in self.order if s not in set(hit)]
+        vic = sorted(free[: len(misses)])
+        dst = []
+        j = 0
+        for t in entries:
+            if t < 0:
+                dst.append(-1)
+            elif t in self.where:
+                dst.append(self.where[t])
+            elif j < len(vic):
+                v = vic[j]
+                j += 1
+                if self.slot_pos[v] >= 0:
+                    del self.where[self.slot_pos[v]]
+                self.slot_pos[v], self.where[t] = t, v
+                dst.append(v)
+            else:
+                dst.append(-1)
+        used = sorted(set(hit) | set(vic))
+        self.order = [s for s in self.order if s not in set(used)] + used
+        return dst
+
+
+@pytest.mark.parametrize("n_slots,n_pos,n_entries,seed", [(16, 64, 12, 0), (64, 512, 40, 1),
+                                                           (33, 200, 50, 2)])
+def test_cache_commit_matches_recency_list_model(n_slots, n_pos, n_entries, seed):
+    rng = np.random.default_rng(seed)
+    p2s, s2p, st = fresh_cache(n_slots, n_pos)
+    model = ListLRU(n_slots)
+    hot = rng.choice(n_pos, size=n_pos // 4, replace=False)
+    for now in range(1, 40):
+        # a drifting working set: most entries from a hot set, some anywhere
+        pick = np.where(rng.random(n_entries) < 0.7, rng.choice(hot, n_entries),
+                        rng.integers(0, n_pos, n_entries))
+        ent = np.unique(pick).astype(np.int32)
+        pad = rng.integers(0, 3)
+        ent = np.concatenate([ent, np.full(pad, -1, np.int32)])
+        dst, n_ins = orc.cache_commit(ent, n_slots, now, p2s, s2p, st)
+        assert dst.tolist() == model.step(ent.tolist()), now
+        # the tables stay coherent
+        occ = np.where(s2p >= 0)[0]
+        assert (p2s[s2p[occ]] == occ).all()
+        assert int((p2s >= 0).sum()) == len(occ)
+        if now % 7 == 0:
+            hot = rng.choice(n_pos, size=n_pos // 4, replace=False)
