@@ -75,7 +75,7 @@ extern "C" {
 typedef struct ihipStream_t *ls_stream_t;
 typedef struct ihipEvent_t *ls_event_t;
 
-#define LS_ABI_VERSION 2
+#define LS_ABI_VERSION 3
 
 enum {
     LS_OK = 0,
@@ -144,6 +144,30 @@ typedef struct {
     int32_t n_splits;
 } ls_attn_desc;
 
+/* Cache commit of a step: the caches keep what the step used, so that the
+ * next steps reuse it.  [LeanSparse Abstract: the indexer-key cache and the
+ * KV cache are separate and reused across generation steps; XM-Sparse
+ * digest, hot buffer section: only the selected rows missing from the
+ * buffer are fetched.]  The pages give no policy; this one is least
+ * recently used (see ls_cache_commit):
+ *   hot = 1: the step's KV misses move into victim slots of the hot buffer
+ *     (the gather writes each row straight into its slot, rows[] names the
+ *     slot, pos2slot / slot2pos / stamp are updated); misses beyond the
+ *     free slots stay in the scratch rows, uncached.  Needs use_hot = 1,
+ *     hot_slots in [1, 16384], topk <= 16384.
+ *   keys = 1: the step's candidates missing from the key cache move into
+ *     victim rows of it (the refinement copies each key row it reads from
+ *     k8 into its row; kpos2slot / kslot2pos / kstamp are updated).  Needs
+ *     key_slots in [1, 16384], n_cand <= 16384.
+ *   now: this step's stamp, below 2^32 - 1 and above every stamp already
+ *     in the tables (a step counter starting at 1 over zeroed stamps).
+ * Without commit (both 0) the step only reads the caches and is
+ * idempotent.                                                               */
+typedef struct {
+    int32_t hot, keys;
+    uint32_t now;
+} ls_commit_desc;
+
 /* Whole step.  With use_hot = 1 attention reads the hot buffer (MLA latent
  * rows, k_base = v_base = hot_kv); with use_hot = 0 it reads k_cache /
  * v_cache at the selected positions.                                        */
@@ -152,6 +176,7 @@ typedef struct {
     ls_hot_desc hot;
     ls_attn_desc attn;
     int32_t use_hot;
+    ls_commit_desc commit;
 } ls_step_desc;
 
 /* Number of stage events ls_decode_step records when given an event array:
@@ -168,13 +193,16 @@ typedef struct {
     const int8_t *w_idx_dev;    /* [B, H] int8 per-head weights              */
     const uint8_t *kc_dev;      /* [B, max_ctx, D/2] packed compact keys     */
     const int8_t *k8_dev;       /* [B, max_ctx, D] original int8 keys        */
-    const int32_t *kpos2slot_dev;/* [B, max_ctx] key-cache row or -1 (nullable)*/
-    const int8_t *kcache_dev;   /* [B, key_slots, D] key cache (nullable)    */
+    int32_t *kpos2slot_dev;     /* [B, max_ctx] key-cache row or -1 (nullable;
+                                   written by commit.keys)                   */
+    int8_t *kcache_dev;         /* [B, key_slots, D] key cache (nullable;
+                                   written by commit.keys)                   */
     const int32_t *ctx_len_dev; /* [B] valid tokens per request              */
     int32_t *cand_dev;          /* out [B, n_cand] candidates                */
     int32_t *topk_dev;          /* out [B, topk] selected positions          */
     int64_t *topk_score_dev;    /* out [B, topk] their fine scores (nullable)*/
-    const int32_t *pos2slot_dev;/* [B, max_ctx] hot slot of a token or -1    */
+    int32_t *pos2slot_dev;      /* [B, max_ctx] hot slot of a token or -1
+                                   (written by commit.hot)                   */
     void *hot_kv_dev;           /* [B, hot_slots + topk, row] bf16 (in/out)  */
     const void *pool_kv_dev;    /* [B, max_ctx, row] bf16 full history       */
     int32_t *rows_dev;          /* out [B, topk] row read for each selected  */
@@ -185,6 +213,12 @@ typedef struct {
     void *out_dev;              /* out [B, Hq, v_dim] bf16                   */
     float *lse_dev;             /* out [B, Hq] fp32                          */
     ls_event_t *stage_events;   /* nullable: LS_STEP_EVENTS events to record */
+    int32_t *slot2pos_dev;      /* [B, hot_slots] token of each slot or -1,
+                                   in/out (commit.hot; else nullable)        */
+    uint32_t *stamp_dev;        /* [B, hot_slots] step that last used each
+                                   slot, in/out (commit.hot; else nullable)  */
+    int32_t *kslot2pos_dev;     /* [B, key_slots] (commit.keys; else nullable)*/
+    uint32_t *kstamp_dev;       /* [B, key_slots] (commit.keys; else nullable)*/
 } ls_step_io;
 
 /* Prefill chunk: n_query query tokens at absolute positions
@@ -260,6 +294,47 @@ int ls_sparse_attn_decode(const ls_attn_desc *desc, const void *q_dev, const voi
 /* The whole decode step, stages 1-4 in order on one stream.                 */
 int ls_decode_step(const ls_step_desc *desc, const ls_step_io *io, void *ws_dev,
                    size_t ws_bytes, ls_stream_t stream);
+
+/* One least-recently-used commit per request into a cache of n_slots rows
+ * (the hot KV buffer or the indexer-key cache; the step runs the same
+ * commit when ls_commit_desc asks for it).  entries [B, n]: the positions
+ * the step used, ascending, -1 padded.  Tables, updated in place:
+ * pos2slot [B, max_ctx] (slot of a token or -1), slot2pos [B, n_slots]
+ * (token of a slot or -1), stamp [B, n_slots] (step that last used the
+ * slot, 0 = never).
+ *   1. an entry with pos2slot in [0, n_slots) is a hit: stamp := now;
+ *   2. an entry with pos2slot < 0 is a miss; misses are numbered in entry
+ *      order;
+ *   3. victims: of the slots not hit, the min(#misses, #not hit) with the
+ *      smallest (stamp, slot index), taken in ascending slot order;
+ *   4. miss j moves into victim j: the token the victim held loses its slot,
+ *      pos2slot / slot2pos updated, stamp := now.
+ * dst: out [B, n], each entry's slot after the commit (-1: padding or a
+ * miss left out).  n_inserted: out [B] (nullable).  n_slots and n in
+ * [1, 16384]; now < 2^32 - 1.  Moving the rows' data is the caller's (the
+ * decode step does it for both caches).  Tables must be coherent
+ * (pos2slot[slot2pos[s]] == s); positions must be below max_ctx.
+ * [Reading of LeanSparse Abstract, caches reused across steps.]            */
+int ls_cache_commit(int32_t batch, int32_t max_ctx, int32_t n_slots, int32_t n, uint32_t now,
+                    const int32_t *entries_dev, int32_t *pos2slot_dev, int32_t *slot2pos_dev,
+                    uint32_t *stamp_dev, int32_t *dst_dev, int32_t *n_inserted_dev,
+                    ls_stream_t stream);
+
+/* New-token append (once per generated token and layer): the token of
+ * request b goes to position ctx_len[b] when that is below max_ctx (a full
+ * request is left unchanged): new_k8 [B, head_dim] int8 into k8 (device, or
+ * pinned host with keys_on_host = 1), its compact form into kc, and, with
+ * row_elems > 0, new_kv [B, row_elems] bf16 into pool (device, or pinned
+ * host with pool_on_host = 1); then ctx_len[b] += 1.
+ * [XM-Sparse digest: each step's new KV is written back to the full
+ *  history; LeanSparse Abstract: compact keys for the search.]             */
+typedef struct {
+    int32_t batch, max_ctx, head_dim, row_elems, keys_on_host, pool_on_host;
+} ls_append_desc;
+
+int ls_append_token(const ls_append_desc *desc, const int8_t *new_k8_dev, const void *new_kv_dev,
+                    int8_t *k8, uint8_t *kc_dev, void *pool, int32_t *ctx_len_dev,
+                    ls_stream_t stream);
 
 /* Prefill indexer on device-resident keys [max_ctx, D]: for each query row
  * i (q [n_query,H,D], w [n_query,H]), the topk best keys among 0..q_pos0+i.

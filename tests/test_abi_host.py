@@ -40,19 +40,22 @@ def test_struct_layouts_match_header(tmp_path):
                    'int main(void){ printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n",'
                    ' sizeof(ls_idx_desc), sizeof(ls_hot_desc), sizeof(ls_attn_desc),'
                    ' sizeof(ls_step_desc), sizeof(ls_step_io), sizeof(ls_prefill_desc),'
-                   ' offsetof(ls_attn_desc, scale), offsetof(ls_step_desc, attn)); return 0; }\n')
+                   ' offsetof(ls_attn_desc, scale), offsetof(ls_step_desc, attn));'
+                   ' printf("%zu %zu %zu\\n", sizeof(ls_commit_desc), sizeof(ls_append_desc),'
+                   ' offsetof(ls_step_desc, commit)); return 0; }\n')
     exe = tmp_path / "s"
     subprocess.check_call(["gcc", "-std=c99", "-I", ls.HEADER_PATH.rsplit("/", 1)[0], str(src),
                            "-o", str(exe)])
     got = [int(x) for x in subprocess.check_output([str(exe)]).split()]
     want = [ctypes.sizeof(ls.IdxDesc), ctypes.sizeof(ls.HotDesc), ctypes.sizeof(ls.AttnDesc),
             ctypes.sizeof(ls.StepDesc), ctypes.sizeof(ls.StepIO), ctypes.sizeof(ls.PrefillDesc),
-            ls.AttnDesc.scale.offset, ls.StepDesc.attn.offset]
+            ls.AttnDesc.scale.offset, ls.StepDesc.attn.offset, ctypes.sizeof(ls.CommitDesc),
+            ctypes.sizeof(ls.AppendDesc), ls.StepDesc.commit.offset]
     assert got == want
 
 
 def test_version_and_error_string(lib):
-    assert lib.ls_abi_version() == ls.ABI_VERSION == 2
+    assert lib.ls_abi_version() == ls.ABI_VERSION == 3
     assert isinstance(lib.ls_last_error(), bytes)
 
 
@@ -202,3 +205,72 @@ def test_binding_rejects_mis_sized_tensors():
         ls._need(t.transpose(1, 2), torch.bfloat16, "hot")
     with pytest.raises(ValueError):
         ls._need_rows(t, 81, "k_base")
+
+
+@pytest.mark.parametrize("args,needle", [
+    (dict(n_slots=0), b"slots"),
+    (dict(n_slots=16385), b"slots"),
+    (dict(n=0), b"entries"),
+    (dict(n=16385), b"entries"),
+    (dict(now=0xFFFFFFFF), b"now"),
+    (dict(batch=0), b"batch"),
+])
+def test_cache_commit_rejects_bad_shapes(lib, args, needle):
+    a = dict(batch=2, max_ctx=4096, n_slots=1024, n=256, now=5)
+    a.update(args)
+    rc = lib.ls_cache_commit(a["batch"], a["max_ctx"], a["n_slots"], a["n"], a["now"], FAKE,
+                             FAKE, FAKE, FAKE, FAKE, None, None)
+    assert rc == ls.LS_E_ARG
+    assert needle in lib.ls_last_error()
+
+
+def test_cache_commit_null_table_rejected(lib):
+    rc = lib.ls_cache_commit(2, 4096, 1024, 256, 5, FAKE, FAKE, None, FAKE, FAKE, None, None)
+    assert rc == ls.LS_E_ARG and b"slot2pos" in lib.ls_last_error()
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(head_dim=96), b"head_dim"),
+    (dict(row_elems=12), b"row_elems"),
+    (dict(keys_on_host=3), b"keys_on_host"),
+    (dict(row_elems=576), b"new_kv"),
+])
+def test_append_rejects_bad_arguments(lib, kw, needle):
+    base = dict(batch=2, max_ctx=4096, head_dim=128, row_elems=0, keys_on_host=0, pool_on_host=0)
+    base.update(kw)
+    d = ls.AppendDesc(**base)
+    rc = lib.ls_append_token(ctypes.byref(d), FAKE, None, FAKE, FAKE, None, FAKE, None)
+    assert rc in (ls.LS_E_ARG, ls.LS_E_UNSUPPORTED)
+    assert needle in lib.ls_last_error()
+
+
+def step_desc(commit_hot=0, commit_keys=0, key_slots=0, now=1, hot_slots=4096):
+    i = idx(batch=2, max_ctx=131072, n_cand=8192, topk=2048, key_slots=key_slots)
+    h = ls.HotDesc(2, 131072, 2048, hot_slots, 576, 0)
+    a = ls.AttnDesc(2, 128, 1, 576, 512, 2048, hot_slots + 2048, 576, 0, 0.07, 0)
+    return ls.StepDesc(i, h, a, 1, ls.CommitDesc(commit_hot, commit_keys, now))
+
+
+def fake_io(**kw):
+    io = ls.StepIO()
+    for name, _ in ls.StepIO._fields_:
+        setattr(io, name, 0x100000)
+    io.stage_events = None
+    for k, v in kw.items():
+        setattr(io, k, v)
+    return io
+
+
+@pytest.mark.parametrize("desc,io_kw,needle", [
+    (dict(commit_keys=1), {}, b"key_slots"),
+    (dict(commit_hot=1, hot_slots=20000), {}, b"slots"),
+    (dict(commit_hot=1, now=0xFFFFFFFF), {}, b"now"),
+    (dict(commit_hot=1), dict(stamp_dev=None), b"stamp"),
+    (dict(commit_keys=1, key_slots=16384), dict(kslot2pos_dev=None), b"kslot2pos"),
+    (dict(commit_hot=2), {}, b"commit"),
+])
+def test_step_commit_validated(lib, desc, io_kw, needle):
+    d = step_desc(**desc)
+    rc = lib.ls_decode_step(ctypes.byref(d), ctypes.byref(fake_io(**io_kw)), FAKE, 1 << 40, None)
+    assert rc == ls.LS_E_ARG
+    assert needle in lib.ls_last_error()

@@ -29,7 +29,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "ls.h")
 LS_OK, LS_E_ARG, LS_E_UNSUPPORTED, LS_E_WORKSPACE, LS_E_HIP = 0, -1, -2, -3, -4
 OP_COARSE, OP_REFINE, OP_HOT, OP_ATTN, OP_STEP, OP_PREFILL = 1, 2, 3, 4, 5, 6
 STEP_EVENTS = 7
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _I32, _I64, _F32, _P = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
 
@@ -51,8 +51,18 @@ class AttnDesc(ctypes.Structure):
                 + [("scale", _F32), ("n_splits", _I32)])
 
 
+class CommitDesc(ctypes.Structure):
+    _fields_ = [("hot", _I32), ("keys", _I32), ("now", ctypes.c_uint32)]
+
+
 class StepDesc(ctypes.Structure):
-    _fields_ = [("idx", IdxDesc), ("hot", HotDesc), ("attn", AttnDesc), ("use_hot", _I32)]
+    _fields_ = [("idx", IdxDesc), ("hot", HotDesc), ("attn", AttnDesc), ("use_hot", _I32),
+                ("commit", CommitDesc)]
+
+
+class AppendDesc(ctypes.Structure):
+    _fields_ = [(n, _I32) for n in ("batch", "max_ctx", "head_dim", "row_elems", "keys_on_host",
+                                    "pool_on_host")]
 
 
 class StepIO(ctypes.Structure):
@@ -60,7 +70,8 @@ class StepIO(ctypes.Structure):
         "q_idx_dev", "w_idx_dev", "kc_dev", "k8_dev", "kpos2slot_dev", "kcache_dev",
         "ctx_len_dev", "cand_dev", "topk_dev",
         "topk_score_dev", "pos2slot_dev", "hot_kv_dev", "pool_kv_dev", "rows_dev", "n_miss_dev",
-        "q_attn_dev", "k_cache_dev", "v_cache_dev", "out_dev", "lse_dev", "stage_events")]
+        "q_attn_dev", "k_cache_dev", "v_cache_dev", "out_dev", "lse_dev", "stage_events",
+        "slot2pos_dev", "stamp_dev", "kslot2pos_dev", "kstamp_dev")]
 
 
 class PrefillDesc(ctypes.Structure):
@@ -99,7 +110,10 @@ def load():
     L.ls_prefill_index_topk.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     L.ls_prefill_stream_layers.argtypes = [_P, _I32, _P, _P, _P, _P, _P, _P, _P,
                                            ctypes.c_size_t, _P, _P]
-    for name in ("ls_pack_coarse", "ls_index_coarse", "ls_refine_topk", "ls_hot_gather",
+    L.ls_cache_commit.argtypes = [_I32, _I32, _I32, _I32, ctypes.c_uint32, _P, _P, _P, _P, _P,
+                                  _P, _P]
+    L.ls_append_token.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P]
+    for name in ("ls_cache_commit", "ls_append_token", "ls_pack_coarse", "ls_index_coarse", "ls_refine_topk", "ls_hot_gather",
                  "ls_sparse_attn_decode", "ls_decode_step", "ls_prefill_index_topk",
                  "ls_prefill_stream_layers", "ls_workspace_init"):
         getattr(L, name).restype = ctypes.c_int
@@ -304,8 +318,8 @@ class DecodeStep:
 
     def __init__(self, *, batch, max_ctx, idx_heads, idx_dim, n_cand, topk, q_heads, qk_dim,
                  v_dim, scale, hot_slots=0, kv_heads=1, kv_row_stride=None, kv_head_stride=0,
-                 pool_on_host=False, keys_on_host=False, key_slots=0, n_splits=0,
-                 device="cuda"):
+                 pool_on_host=False, keys_on_host=False, key_slots=0, commit_hot=False,
+                 commit_keys=False, n_splits=0, device="cuda"):
         self.use_hot = hot_slots > 0
         idx = IdxDesc(batch, max_ctx, idx_heads, idx_dim, n_cand, topk, 1 if keys_on_host else 0,
                       key_slots)
@@ -319,7 +333,8 @@ class DecodeStep:
             stride = kv_row_stride if kv_row_stride is not None else kv_heads * qk_dim
             attn = AttnDesc(batch, q_heads, kv_heads, qk_dim, v_dim, topk, max_ctx, stride,
                             kv_head_stride, float(scale), n_splits)
-        self.desc = StepDesc(idx, hot, attn, 1 if self.use_hot else 0)
+        self.desc = StepDesc(idx, hot, attn, 1 if self.use_hot else 0,
+                             CommitDesc(1 if commit_hot else 0, 1 if commit_keys else 0, 0))
         self.device = torch.device(device)
         self.ws = new_workspace(OP_STEP, self.desc, self.device)
         dev = self.device
@@ -333,7 +348,11 @@ class DecodeStep:
 
     def run(self, *, q_idx, w_idx, kc, k8, ctx_len, q_attn, pos2slot=None, hot_kv=None,
             pool_kv=None, k_cache=None, v_cache=None, kpos2slot=None, kcache=None,
-            events=None):
+            slot2pos=None, stamp=None, kslot2pos=None, kstamp=None, now=0, events=None):
+        """With commits, slot2pos / stamp (hot buffer) and kslot2pos / kstamp
+        (key cache) are the caches' LRU state [B, slots] int32 (stamps held
+        as uint32 bits), updated in place with pos2slot / kpos2slot; now is
+        this step's stamp (see cache_commit)."""
         i, a, h = self.desc.idx, self.desc.attn, self.desc.hot
         B, L, H, D = i.batch, i.max_ctx, i.n_heads, i.head_dim
         _need(q_idx, torch.int8, "q_idx", (B, H, D)), _need(w_idx, torch.int8, "w_idx", (B, H))
@@ -374,6 +393,18 @@ class DecodeStep:
             io.k_cache_dev, io.v_cache_dev = k_cache.data_ptr(), v_cache.data_ptr()
         io.q_attn_dev = q_attn.data_ptr()
         io.out_dev, io.lse_dev = self.out.data_ptr(), self.lse.data_ptr()
+        c = self.desc.commit
+        c.now = int(now) & 0xFFFFFFFF
+        if c.hot:
+            S = h.hot_slots
+            _need(slot2pos, torch.int32, "slot2pos", (B, S)), _need(stamp, torch.int32, "stamp",
+                                                                    (B, S))
+            io.slot2pos_dev, io.stamp_dev = slot2pos.data_ptr(), stamp.data_ptr()
+        if c.keys:
+            S = i.key_slots
+            _need(kslot2pos, torch.int32, "kslot2pos", (B, S))
+            _need(kstamp, torch.int32, "kstamp", (B, S))
+            io.kslot2pos_dev, io.kstamp_dev = kslot2pos.data_ptr(), kstamp.data_ptr()
         if events is not None:  # STEP_EVENTS torch events; None entries are skipped
             arr = (ctypes.c_void_p * STEP_EVENTS)(*[e.cuda_event if e is not None else None
                                                     for e in events])
@@ -381,6 +412,49 @@ class DecodeStep:
         _check(load().ls_decode_step(ctypes.byref(self.desc), ctypes.byref(io), _p(self.ws),
                                      self.ws.numel(), _stream()))
         return self.out, self.lse
+
+
+# ------------------------------------------------------------- cache state --
+
+def cache_commit(entries, pos2slot, slot2pos, stamp, now: int):
+    """Least-recently-used commit of the entries [B, n] (ascending positions,
+    -1 padded) into per-request caches of S slots: pos2slot [B, L] int32,
+    slot2pos [B, S] int32, stamp [B, S] int32 holding uint32 stamps, updated
+    in place.  Returns (dst [B, n] int32, n_inserted [B] int32)."""
+    _need(entries, torch.int32, "entries")
+    B, n = entries.shape
+    _need(pos2slot, torch.int32, "pos2slot", (B, pos2slot.shape[1]))
+    S = slot2pos.shape[1]
+    _need(slot2pos, torch.int32, "slot2pos", (B, S)), _need(stamp, torch.int32, "stamp", (B, S))
+    dst = torch.empty((B, n), dtype=torch.int32, device=entries.device)
+    n_ins = torch.empty((B,), dtype=torch.int32, device=entries.device)
+    _check(load().ls_cache_commit(B, pos2slot.shape[1], S, n, int(now) & 0xFFFFFFFF, _p(entries),
+                                  _p(pos2slot), _p(slot2pos), _p(stamp), _p(dst), _p(n_ins),
+                                  _stream()))
+    return dst, n_ins
+
+
+def append_token(new_k8, k8, kc, ctx_len, new_kv=None, pool=None):
+    """Writes each request's new token at position ctx_len[b] (if below
+    max_ctx) and advances ctx_len: new_k8 [B, D] int8 into k8 [B, L, D] and
+    its compact form into kc [B, L, D/2]; new_kv [B, row] bf16 into pool
+    [B, L, row].  k8 and pool may be pinned host memory."""
+    _need(new_k8, torch.int8, "new_k8")
+    B, D = new_k8.shape
+    _need(k8, torch.int8, "k8", (B, k8.shape[1], D))
+    L = k8.shape[1]
+    _need(kc, torch.uint8, "kc", (B, L, D // 2)), _need(ctx_len, torch.int32, "ctx_len", (B,))
+    row = 0
+    if (new_kv is None) != (pool is None):
+        raise ValueError("new_kv and pool go together")
+    if pool is not None:
+        row = pool.shape[2]
+        _need(new_kv, torch.bfloat16, "new_kv", (B, row))
+        _need(pool, torch.bfloat16, "pool", (B, L, row))
+    d = AppendDesc(B, L, D, row, 0 if k8.is_cuda else 1,
+                   0 if (pool is None or pool.is_cuda) else 1)
+    _check(load().ls_append_token(ctypes.byref(d), _p(new_k8), _p(new_kv), _p(k8), _p(kc),
+                                  _p(pool), _p(ctx_len), _stream()))
 
 
 # ------------------------------------------------------------------ prefill --

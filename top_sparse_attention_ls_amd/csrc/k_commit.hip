@@ -1,0 +1,269 @@
+// Cache commit (least recently used) and new-token append.
+//
+// [LeanSparse (arXiv 2611.04671), Abstract]: the indexer-key cache and the
+// KV cache are kept apart and reused across generation steps.  [XM-Sparse
+// digest, hot buffer section]: a step fetches only the selected rows that
+// missed the HBM buffer, and each step's new KV is written back to the full
+// history.  The pages give no insertion or eviction policy; the one here is
+// least recently used:
+//   * an entry of the step (a selected token, or a candidate for the key
+//     cache) whose slot-table value lies in [0, n_slots) is a hit, and its
+//     slot's stamp becomes `now`;
+//   * an entry whose value is negative is a miss; misses are numbered in
+//     entry order (ascending position);
+//   * the victims are the min(#misses, #slots not hit) slots not hit in this
+//     step with the smallest (stamp, slot index), taken in ascending slot
+//     order; miss j moves into victim j: the token the victim held loses its
+//     slot, and the tables and the stamp are updated.
+#include "ls_device.h"
+#include "ls_launch.h"
+
+namespace ls {
+
+// One 1024-thread workgroup per request.  The request's stamps sit in LDS
+// (one word per slot) with a bitmap of the slots hit in this step; the
+// victims are found by an exact radix select of the stamps (three digit
+// passes of 11, 11 and 10 bits over a 2048-bin LDS histogram) and the slots
+// of equal stamp are taken in slot order.  Thread t owns the contiguous slot
+// range [t*SE, t*SE + SE) and the entry range [t*E, t*E + E), so that
+// prefix sums over threads give slot order and entry order.
+//
+// Outputs by mode:
+//   kCommitDst: dst[b, e] = the entry's slot after the commit, or -1;
+//   kCommitHot: for an inserted miss, rows[b, e] := its victim and
+//               miss_dst[b, j] := the victim (j = its miss rank; -1 when not
+//               inserted) -- the gather then writes the row into the slot;
+//   kCommitKey: code[b, e] = the slot of a hit, -(2 + victim) for an
+//               inserted miss (the refinement copies the row it reads into
+//               that slot), -1 otherwise.
+constexpr int kCommitThreads = 1024;
+constexpr int kDigitBins = 2048;
+
+template <int MODE>
+__global__ __launch_bounds__(kCommitThreads) void k_cache_commit(
+    const int32_t* __restrict__ entries, int n, int32_t* __restrict__ pos2slot,
+    int32_t* __restrict__ slot2pos, uint32_t* __restrict__ stamp, int S, int max_ctx,
+    uint32_t now, int32_t* __restrict__ out, int32_t* __restrict__ rows,
+    int32_t* __restrict__ n_ins) {
+  __shared__ uint32_t key[kCommitMaxSlots];        // stamps, then the victim list
+  __shared__ uint32_t hitbits[kCommitMaxSlots / 32];
+  __shared__ uint32_t hist[kDigitBins];
+  __shared__ uint32_t sh_scan[kCommitThreads / kWave];
+  __shared__ uint32_t sh_pick[2];
+
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int32_t* eb = entries + (size_t)b * n;
+  int32_t* p2s = pos2slot + (size_t)b * max_ctx;
+  int32_t* s2p = slot2pos + (size_t)b * S;
+  uint32_t* stb = stamp + (size_t)b * S;
+  int32_t* ob = out + (size_t)b * n;
+
+  for (int s = tid; s < S; s += kCommitThreads) key[s] = stb[s];
+  for (int w = tid; w < kCommitMaxSlots / 32; w += kCommitThreads) hitbits[w] = 0u;
+  __syncthreads();
+
+  // entries: hits set their slot's bit; misses are flagged (mask over the
+  // thread's E entries, taken from the table state before any update)
+  const int E = (n + kCommitThreads - 1) / kCommitThreads;  // <= kCommitMaxEntries / 1024
+  const int e0 = tid * E;
+  uint32_t mmask = 0u, n_m_t = 0u;
+  for (int i = 0; i < E; i++) {
+    const int e = e0 + i;
+    if (e >= n) break;
+    const int32_t t = eb[e];
+    int32_t s = -1;
+    bool miss = false;
+    if (t >= 0 && t < max_ctx) {
+      s = p2s[t];
+      if (s >= 0 && s < S) atomicOr(&hitbits[s >> 5], 1u << (s & 31));
+      miss = s < 0;
+    }
+    if (miss) {
+      mmask |= 1u << i;
+      n_m_t++;
+    }
+    if (MODE == kCommitDst) ob[e] = (s >= 0 && s < S) ? s : -1;
+    if (MODE == kCommitKey) ob[e] = (s >= 0 && s < S) ? s : -1;
+  }
+  __syncthreads();
+
+  // the thread's slots: stamp and whether the step hit it
+  const int SE = (S + kCommitThreads - 1) / kCommitThreads;  // <= 16
+  const int s0 = tid * SE;
+  uint32_t kv[kCommitMaxSlots / kCommitThreads];
+  uint32_t elig = 0u, n_hit_t = 0u;
+#pragma unroll
+  for (int i = 0; i < kCommitMaxSlots / kCommitThreads; i++) {
+    const int s = s0 + i;
+    kv[i] = 0u;
+    if (i < SE && s < S) {
+      kv[i] = key[s];
+      if ((hitbits[s >> 5] >> (s & 31)) & 1u) n_hit_t++;
+      else elig |= 1u << i;
+    }
+  }
+  uint32_t n_m, n_h;
+  const uint32_t m_base = block_excl_scan<kCommitThreads>(n_m_t, sh_scan, &n_m);
+  block_excl_scan<kCommitThreads>(n_hit_t, sh_scan, &n_h);
+  const uint32_t n_v = min(n_m, (uint32_t)S - n_h);
+
+  // radix select: T = the n_v-th smallest stamp among the slots not hit;
+  // need = how many slots of stamp T are victims
+  uint32_t prefix = 0u, pmask = 0u, need = n_v;
+  if (n_v > 0) {
+#pragma unroll 1
+    for (int pass = 0; pass < 3; pass++) {
+      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+      const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
+      for (int i = tid; i < kDigitBins; i += kCommitThreads) hist[i] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kCommitMaxSlots / kCommitThreads; i++)
+        if (((elig >> i) & 1u) && (kv[i] & pmask) == prefix)
+          atomicAdd(&hist[(kv[i] >> shift) & dmask], 1u);
+      __syncthreads();
+      const uint32_t c0 = hist[2 * tid], c1 = hist[2 * tid + 1];
+      uint32_t tot;
+      const uint32_t base = block_excl_scan<kCommitThreads>(c0 + c1, sh_scan, &tot);
+      if (base < need && need <= base + c0) {
+        sh_pick[0] = 2u * tid;
+        sh_pick[1] = base;
+      } else if (base + c0 < need && need <= base + c0 + c1) {
+        sh_pick[0] = 2u * tid + 1u;
+        sh_pick[1] = base + c0;
+      }
+      __syncthreads();
+      prefix |= sh_pick[0] << shift;
+      pmask |= dmask << shift;
+      need -= sh_pick[1];
+      __syncthreads();  // sh_pick and hist are rewritten by the next pass
+    }
+  }
+
+  // victims in slot order: stamps below T, then the first `need` slots of
+  // stamp T
+  uint32_t eq_t = 0u;
+#pragma unroll
+  for (int i = 0; i < kCommitMaxSlots / kCommitThreads; i++)
+    eq_t += (n_v > 0 && ((elig >> i) & 1u) && kv[i] == prefix) ? 1u : 0u;
+  uint32_t tot_eq;
+  uint32_t eq_rank = block_excl_scan<kCommitThreads>(eq_t, sh_scan, &tot_eq);
+  uint32_t vic = 0u, v_t = 0u;
+#pragma unroll
+  for (int i = 0; i < kCommitMaxSlots / kCommitThreads; i++) {
+    if (n_v == 0 || !((elig >> i) & 1u)) continue;
+    bool v = kv[i] < prefix;
+    if (kv[i] == prefix) {
+      v = eq_rank < need;
+      eq_rank++;
+    }
+    if (v) {
+      vic |= 1u << i;
+      v_t++;
+    }
+  }
+  uint32_t tot_v;
+  uint32_t v_rank = block_excl_scan<kCommitThreads>(v_t, sh_scan, &tot_v);
+  // new stamps (hit or victim: now), written by slot owner; then the LDS
+  // words are free to hold the victim list
+#pragma unroll
+  for (int i = 0; i < kCommitMaxSlots / kCommitThreads; i++) {
+    const int s = s0 + i;
+    if (i < SE && s < S && (!((elig >> i) & 1u) || ((vic >> i) & 1u))) stb[s] = now;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kCommitMaxSlots / kCommitThreads; i++)
+    if ((vic >> i) & 1u) key[v_rank++] = (uint32_t)(s0 + i);
+  __syncthreads();
+
+  // misses in entry order move into the victims (tot_v equals n_v; the
+  // minimum only keeps every victim read inside the list)
+  const uint32_t n_use = min(n_v, tot_v);
+  uint32_t j = m_base;
+  for (int i = 0; i < E; i++) {
+    if (!((mmask >> i) & 1u)) continue;
+    const int e = e0 + i;
+    const int32_t t = eb[e];
+    int32_t v = -1;
+    if (j < n_use) {
+      v = (int32_t)min(key[j], (uint32_t)(S - 1));
+      const int32_t old = s2p[v];
+      if (old >= 0 && old < max_ctx) p2s[old] = -1;
+      p2s[t] = v;
+      s2p[v] = t;
+    }
+    if (MODE == kCommitDst) ob[e] = v;
+    if (MODE == kCommitKey) ob[e] = v >= 0 ? -2 - v : -1;
+    if (MODE == kCommitHot) {
+      ob[j] = v;
+      if (v >= 0) rows[(size_t)b * n + e] = v;
+    }
+    j++;
+  }
+  if (tid == 0 && n_ins) n_ins[b] = (int32_t)n_use;
+}
+
+hipError_t launch_cache_commit(int mode, const int32_t* entries, int n, int32_t* pos2slot,
+                               int32_t* slot2pos, uint32_t* stamp, int S, int B, int max_ctx,
+                               uint32_t now, int32_t* out, int32_t* rows, int32_t* n_ins,
+                               hipStream_t st) {
+#define LS_COMMIT(M)                                                                          \
+  hipLaunchKernelGGL(k_cache_commit<M>, dim3(B), dim3(kCommitThreads), 0, st, entries, n,     \
+                     pos2slot, slot2pos, stamp, S, max_ctx, now, out, rows, n_ins)
+  if (mode == kCommitHot) LS_COMMIT(kCommitHot);
+  else if (mode == kCommitKey) LS_COMMIT(kCommitKey);
+  else LS_COMMIT(kCommitDst);
+#undef LS_COMMIT
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- append ----
+// The step's new token of request b goes to position ctx_len[b] (when it is
+// below max_ctx): its int8 key into k8, its compact key into kc, its KV row
+// into the pool; then ctx_len[b] grows by one.  One wave per request; every
+// lane reads ctx_len before lane 0 writes it (one load instruction for the
+// wave, and lane 0's store depends on its own loaded value).
+__global__ __launch_bounds__(64) void k_append_token(const int8_t* __restrict__ new_k8,
+                                                     const uint4* __restrict__ new_kv,
+                                                     int8_t* k8, uint8_t* __restrict__ kc,
+                                                     uint4* pool, int32_t* ctx_len, int D,
+                                                     int max_ctx, int row_chunks) {
+  const int b = blockIdx.x, l = threadIdx.x;
+  const int32_t p = ctx_len[b];
+  if (p < 0 || p >= max_ctx) return;
+  const size_t tok = (size_t)b * max_ctx + p;
+  // key: lane l < D/16 copies 16 bytes and packs them into 8 compact bytes
+  if (l < D / 16) {
+    const uint4 x = *(const uint4*)(new_k8 + (size_t)b * D + 16 * l);
+    *(uint4*)(k8 + tok * D + 16 * l) = x;
+    const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      uint32_t two = 0u;
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        const int32_t e = (int32_t)(int8_t)((w4[i] >> (8 * k)) & 0xFFu) >> 4;
+        two |= ((uint32_t)e & 15u) << (4 * k);
+      }
+      packed[i >> 1] |= two << (16 * (i & 1));
+    }
+    *(uint2*)(kc + tok * (D / 2) + 8 * l) = make_uint2(packed[0], packed[1]);
+  }
+  if (pool) {
+    for (int c = l; c < row_chunks; c += 64)
+      pool[tok * row_chunks + c] = new_kv[(size_t)b * row_chunks + c];
+  }
+  if (l == 0) ctx_len[b] = p + 1;
+}
+
+hipError_t launch_append_token(const int8_t* new_k8, const void* new_kv, int8_t* k8,
+                               uint8_t* kc, void* pool, int32_t* ctx_len, int B, int D,
+                               int max_ctx, int row_elems, hipStream_t st) {
+  hipLaunchKernelGGL(k_append_token, dim3(B), dim3(64), 0, st, new_k8, (const uint4*)new_kv, k8,
+                     kc, (uint4*)pool, ctx_len, D, max_ctx, row_elems * 2 / 16);
+  return hipGetLastError();
+}
+
+}  // namespace ls

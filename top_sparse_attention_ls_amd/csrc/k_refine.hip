@@ -23,16 +23,19 @@ namespace ls {
 // hot slot.  Per-head dots are exact in int32 (|dot| < 2^21);
 // w * relu(dot) < 2^28 and groups of four stay below 2^30 before widening
 // to int64.  Invalid candidates (-1) score 0 and are never selected.
-// With a key cache (KC), a candidate whose key row is resident in the
-// request's cache (kslot[t] in [0, key_slots)) is read from there, in HBM;
-// the others from k8, which may then be pinned host memory read over PCIe.
-// The slot lookup adds one dependent load before the key load.
-template <int D, int HT, bool KC>
+// With a key cache, a candidate whose key row is resident in the request's
+// cache is read from there, in HBM; the others from k8, which may then be
+// pinned host memory read over PCIe.  KC = 1: residency from the slot table
+// (kslot[t] in [0, key_slots)), one dependent load before the key load.
+// KC = 2: from the commit's per-candidate code, loaded beside the candidate;
+// a miss the commit gave a row (code -(2 + v)) is also copied into row v.
+template <int D, int HT, int KC>
 __global__ __launch_bounds__(256) void k_refine(const int8_t* __restrict__ q,
                                                 const int8_t* __restrict__ w,
                                                 const int8_t* __restrict__ k8,
                                                 const int32_t* __restrict__ kslot,
-                                                const int8_t* __restrict__ kcache, int key_slots,
+                                                int8_t* __restrict__ kcache, int key_slots,
+                                                const int32_t* __restrict__ kcode,
                                                 const int32_t* __restrict__ cand,
                                                 int64_t* __restrict__ fs,
                                                 const int32_t* __restrict__ pos2slot,
@@ -46,8 +49,10 @@ __global__ __launch_bounds__(256) void k_refine(const int8_t* __restrict__ q,
 
   const int c_base = blockIdx.x * kRefinePerWG + wave_id() * 64;
   const int8_t* kb = k8 + (size_t)b * max_ctx * D;
-  const int32_t* ksb = KC ? kslot + (size_t)b * max_ctx : nullptr;
-  const int8_t* kcb = KC ? kcache + (size_t)b * key_slots * D : nullptr;
+  const int32_t* ksb = KC == 1 ? kslot + (size_t)b * max_ctx : nullptr;
+  const int32_t* kcd = KC == 2 ? kcode + (size_t)b * C : nullptr;
+  int8_t* kcb = KC ? kcache + (size_t)b * key_slots * D : nullptr;
+  int32_t code[4];
   // Every load below is unconditional (indices clamped, results selected
   // afterwards): a load under a divergent condition becomes a branch that
   // waits for it, which would serialise the whole prologue.
@@ -65,9 +70,14 @@ __global__ __launch_bounds__(256) void k_refine(const int8_t* __restrict__ q,
     pos[tt] = (c < C) ? pr : -1;
     const int p = max(pos[tt], 0);
     const int8_t* row = kb + (size_t)p * D;
-    if (KC) {
+    if (KC == 1) {
       const int32_t ks = ksb[p];
       row = ((uint32_t)ks < (uint32_t)key_slots) ? kcb + (size_t)ks * D : row;
+    }
+    if (KC == 2) {
+      const int32_t cr = kcd[min(c, C - 1)];
+      code[tt] = (c < C && pos[tt] >= 0) ? cr : -1;
+      row = ((uint32_t)code[tt] < (uint32_t)key_slots) ? kcb + (size_t)code[tt] * D : row;
     }
 #pragma unroll
     for (int mf = 0; mf < NMF; mf++) {
@@ -125,6 +135,23 @@ __global__ __launch_bounds__(256) void k_refine(const int8_t* __restrict__ q,
     }
     part[tt] = sum;
   }
+  if (KC == 2) {
+    // misses given a cache row: this lane's slices of the row it read
+    // (stored after the MFMAs, so that no wait for the key loads comes
+    // before the query loads)
+#pragma unroll
+    for (int tt = 0; tt < 4; tt++) {
+      const int32_t v = -2 - code[tt];
+      if (code[tt] <= -2 && v < key_slots) {
+#pragma unroll
+        for (int mf = 0; mf < NMF; mf++) {
+          const int off = (D == 128) ? 32 * g + 16 * mf : 16 * g;
+          *(v4i*)(kcb + (size_t)v * D + off) = raw[tt][mf];
+        }
+      }
+    }
+  }
+
   // reduce-scatter over the four lane groups: lane (n, g) ends with tile g
   const int64_t score = (int64_t)reduce_scatter4((uint64_t)part[0], (uint64_t)part[1],
                                                  (uint64_t)part[2], (uint64_t)part[3]);
@@ -476,10 +503,13 @@ hipError_t launch_refine_topk(const int8_t* q, const int8_t* w, const KeySource&
   const int HT = (H + 15) / 16;
 #define LS_REFINE_KC(DD, TT, KC)                                                             \
   hipLaunchKernelGGL((k_refine<DD, TT, KC>), grid, dim3(256), 0, st, q, w, keys.k8, keys.kslot, \
-                     keys.kcache, keys.key_slots, cand, ws.fs, pos2slot, ws.slot, H, max_ctx, C)
+                     keys.kcache, keys.key_slots, keys.code, cand, ws.fs, pos2slot, ws.slot, H, \
+                     max_ctx, C)
 #define LS_REFINE(DD, TT)                                                                     \
   do {                                                                                        \
-    if (keys.key_slots > 0) LS_REFINE_KC(DD, TT, true); else LS_REFINE_KC(DD, TT, false);     \
+    if (keys.key_slots > 0 && keys.code) LS_REFINE_KC(DD, TT, 2);                             \
+    else if (keys.key_slots > 0) LS_REFINE_KC(DD, TT, 1);                                     \
+    else LS_REFINE_KC(DD, TT, 0);                                                             \
   } while (0)
   if (D == 128) {
     if (HT == 1) LS_REFINE(128, 1); else if (HT == 2) LS_REFINE(128, 2);
@@ -565,8 +595,15 @@ hipError_t launch_hot_resolve(const int32_t* topk, const int32_t* pos2slot, int3
 constexpr int kGatherWGPerReq = 32;
 constexpr int kGatherUnroll = 4;
 
+//
+// With DST (a hot-buffer commit ran), miss j goes to the slot miss_dst[j]
+// when it has one, else to scratch row hot_slots + j; the stores then go
+// through a resource over the request's whole buffer, and pieces past the
+// miss count get an offset beyond it.
+template <bool DST>
 __global__ __launch_bounds__(256) void k_hot_gather(const int32_t* __restrict__ miss_pos,
                                                     const int32_t* __restrict__ n_miss,
+                                                    const int32_t* __restrict__ miss_dst,
                                                     const uint4* pool, uint4* __restrict__ hot,
                                                     int hot_slots, int max_ctx, int K,
                                                     int chunks) {
@@ -582,29 +619,41 @@ __global__ __launch_bounds__(256) void k_hot_gather(const int32_t* __restrict__ 
   const int G = gridDim.x;
   const int32_t* mp = miss_pos + (size_t)b * K;
   const uint4* pb = pool + (size_t)b * max_ctx * chunks;
-  uint4* hb = hot + ((size_t)b * (hot_slots + K) + hot_slots) * chunks;
+  uint4* hb = hot + ((size_t)b * (hot_slots + K) + (DST ? 0 : hot_slots)) * chunks;
+  const int32_t* md = DST ? miss_dst + (size_t)b * K : nullptr;
+  const uint32_t whole = (uint32_t)(hot_slots + K) * (uint32_t)chunks * 16u;
   const int nm_raw = n_miss[b];
   // one round of kGatherUnroll pieces per thread from piece f0 on: every
   // position, then every row, then (after the fence) the stores
   auto round = [&](uint32_t f0, int nm) {
     uint4 v[kGatherUnroll];
     uint32_t off[kGatherUnroll], c[kGatherUnroll];
-    int32_t p[kGatherUnroll];
+    int32_t p[kGatherUnroll], d[kGatherUnroll], j[kGatherUnroll];
 #pragma unroll
     for (int u = 0; u < kGatherUnroll; u++) {
       const uint32_t f = f0 + threadIdx.x + 256u * u;
       const uint32_t m = f / (uint32_t)chunks;
       c[u] = f - m * (uint32_t)chunks;
       const int jj = blockIdx.x + G * (int)m;
+      j[u] = jj;
       off[u] = ((uint32_t)jj * (uint32_t)chunks + c[u]) * 16u;
       p[u] = mp[min(jj, K - 1)];
+      if (DST) d[u] = md[min(jj, K - 1)];
     }
 #pragma unroll
     for (int u = 0; u < kGatherUnroll; u++)
       v[u] = pb[(size_t)min(max(p[u], 0), max_ctx - 1) * chunks + c[u]];
     __builtin_amdgcn_sched_barrier(0);
     if (nm < 0) nm = min(max(nm_raw, 0), K);  // a list never holds more than K misses
-    const __amdgpu_buffer_rsrc_t hres = buffer_rsrc(hb, (uint32_t)nm * (uint32_t)chunks * 16u);
+    if (DST) {
+#pragma unroll
+      for (int u = 0; u < kGatherUnroll; u++) {
+        const int32_t row = (d[u] >= 0 && d[u] < hot_slots) ? d[u] : hot_slots + j[u];
+        off[u] = j[u] < nm ? ((uint32_t)row * (uint32_t)chunks + c[u]) * 16u : whole;
+      }
+    }
+    const __amdgpu_buffer_rsrc_t hres =
+        buffer_rsrc(hb, DST ? whole : (uint32_t)nm * (uint32_t)chunks * 16u);
 #pragma unroll
     for (int u = 0; u < kGatherUnroll; u++)
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v[u]), hres, off[u], 0, 0);
@@ -618,12 +667,18 @@ __global__ __launch_bounds__(256) void k_hot_gather(const int32_t* __restrict__ 
   for (uint32_t f0 = kRound; f0 < my * (uint32_t)chunks; f0 += kRound) round(f0, nm);
 }
 
-hipError_t launch_hot_gather(const int32_t* miss_pos, const int32_t* n_miss, const void* pool,
-                             void* hot, int hot_slots, int B, int max_ctx, int K, int row_elems,
-                             hipStream_t st) {
+hipError_t launch_hot_gather(const int32_t* miss_pos, const int32_t* n_miss,
+                             const int32_t* miss_dst, const void* pool, void* hot, int hot_slots,
+                             int B, int max_ctx, int K, int row_elems, hipStream_t st) {
   const int chunks = row_elems * 2 / 16;
-  hipLaunchKernelGGL(k_hot_gather, dim3(kGatherWGPerReq, B), dim3(256), 0, st, miss_pos, n_miss,
-                     (const uint4*)pool, (uint4*)hot, hot_slots, max_ctx, K, chunks);
+  if (miss_dst)
+    hipLaunchKernelGGL(k_hot_gather<true>, dim3(kGatherWGPerReq, B), dim3(256), 0, st, miss_pos,
+                       n_miss, miss_dst, (const uint4*)pool, (uint4*)hot, hot_slots, max_ctx, K,
+                       chunks);
+  else
+    hipLaunchKernelGGL(k_hot_gather<false>, dim3(kGatherWGPerReq, B), dim3(256), 0, st, miss_pos,
+                       n_miss, nullptr, (const uint4*)pool, (uint4*)hot, hot_slots, max_ctx, K,
+                       chunks);
   return hipGetLastError();
 }
 

@@ -168,6 +168,8 @@ void carve_refine(Carve& c, const ls_idx_desc* d, ls::RefineWS* ws) {
   w.fs = c.take<int64_t>(B * d->n_cand);
   w.slot = c.take<int32_t>(B * d->n_cand);
   w.miss_pos = c.take<int32_t>(B * d->topk);
+  w.kcode = c.take<int32_t>(B * d->n_cand);
+  w.miss_dst = c.take<int32_t>(B * d->topk);
   if (ws) *ws = w;
 }
 
@@ -338,6 +340,7 @@ int resolve_pool(const void* pool, int on_host, const void** dev_ptr) {
 // memory) and, with key_slots > 0, the device-resident key cache.
 int resolve_keys(const ls_idx_desc* d, const int8_t* k8, const int32_t* kpos2slot,
                  const int8_t* kcache, ls::KeySource* ks) {
+  ks->code = nullptr;
   LS_NONNULL(k8);
   LS_ALIGNED(k8);
   const void* p = nullptr;
@@ -352,7 +355,7 @@ int resolve_keys(const ls_idx_desc* d, const int8_t* k8, const int32_t* kpos2slo
     LS_ALIGNED(kpos2slot);
     LS_ALIGNED(kcache);
     ks->kslot = kpos2slot;
-    ks->kcache = kcache;
+    ks->kcache = (int8_t*)kcache;
   }
   return LS_OK;
 }
@@ -457,9 +460,77 @@ int ls_hot_gather(const ls_hot_desc* desc, const int32_t* topk_dev, const int32_
   LS_HIP(ls::launch_hot_resolve(topk_dev, pos2slot_dev, rows_dev, n_miss_dev, miss_pos,
                                 desc->hot_slots, desc->batch, desc->max_ctx, desc->topk, st),
          "hot resolve launch");
-  LS_HIP(ls::launch_hot_gather(miss_pos, n_miss_dev, pool, hot_kv_dev, desc->hot_slots,
+  LS_HIP(ls::launch_hot_gather(miss_pos, n_miss_dev, nullptr, pool, hot_kv_dev, desc->hot_slots,
                                desc->batch, desc->max_ctx, desc->topk, desc->row_elems, st),
          "miss gather launch");
+  return LS_OK;
+}
+
+static int check_commit_shape(int32_t n_slots, int32_t n, uint32_t now, const char* what) {
+  if (n_slots < 1 || n_slots > ls::kCommitMaxSlots)
+    return fail(LS_E_ARG, "%s: a committed cache needs 1..%d slots (got %d)", what,
+                ls::kCommitMaxSlots, n_slots);
+  if (n < 1 || n > ls::kCommitMaxEntries)
+    return fail(LS_E_ARG, "%s: a commit takes 1..%d entries per request (got %d)", what,
+                ls::kCommitMaxEntries, n);
+  if (now == 0xFFFFFFFFu) return fail(LS_E_ARG, "%s: now must be below 2^32 - 1", what);
+  return LS_OK;
+}
+
+int ls_cache_commit(int32_t batch, int32_t max_ctx, int32_t n_slots, int32_t n, uint32_t now,
+                    const int32_t* entries_dev, int32_t* pos2slot_dev, int32_t* slot2pos_dev,
+                    uint32_t* stamp_dev, int32_t* dst_dev, int32_t* n_inserted_dev,
+                    ls_stream_t stream) {
+  if (batch < 1 || max_ctx < 1)
+    return fail(LS_E_ARG, "bad commit shape (batch %d, max_ctx %d)", batch, max_ctx);
+  LS_TRY(check_commit_shape(n_slots, n, now, "cache commit"));
+  LS_NONNULL(entries_dev);
+  LS_NONNULL(pos2slot_dev);
+  LS_NONNULL(slot2pos_dev);
+  LS_NONNULL(stamp_dev);
+  LS_NONNULL(dst_dev);
+  LS_HIP(ls::launch_cache_commit(ls::kCommitDst, entries_dev, n, pos2slot_dev, slot2pos_dev,
+                                 stamp_dev, n_slots, batch, max_ctx, now, dst_dev, nullptr,
+                                 n_inserted_dev, (hipStream_t)stream),
+         "cache commit launch");
+  return LS_OK;
+}
+
+int ls_append_token(const ls_append_desc* desc, const int8_t* new_k8_dev, const void* new_kv_dev,
+                    int8_t* k8, uint8_t* kc_dev, void* pool, int32_t* ctx_len_dev,
+                    ls_stream_t stream) {
+  if (!desc) return fail(LS_E_ARG, "null append descriptor");
+  if (desc->batch < 1 || desc->max_ctx < 1)
+    return fail(LS_E_ARG, "bad append shape (batch %d, max_ctx %d)", desc->batch, desc->max_ctx);
+  if (desc->head_dim != 64 && desc->head_dim != 128)
+    return fail(LS_E_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", desc->head_dim);
+  if (desc->row_elems < 0 || desc->row_elems % 8 != 0)
+    return fail(LS_E_ARG, "row_elems must be 0 or a positive multiple of 8 (got %d)",
+                desc->row_elems);
+  if ((desc->keys_on_host != 0 && desc->keys_on_host != 1) ||
+      (desc->pool_on_host != 0 && desc->pool_on_host != 1))
+    return fail(LS_E_ARG, "keys_on_host and pool_on_host must be 0 or 1");
+  LS_NONNULL(new_k8_dev);
+  LS_NONNULL(k8);
+  LS_NONNULL(kc_dev);
+  LS_NONNULL(ctx_len_dev);
+  LS_ALIGNED(new_k8_dev);
+  LS_ALIGNED(k8);
+  LS_ALIGNED(kc_dev);
+  const void* k8d = nullptr;
+  LS_TRY(resolve_host(k8, desc->keys_on_host, &k8d, "k8 (keys_on_host = 1)"));
+  const void* pd = nullptr;
+  if (desc->row_elems > 0) {
+    LS_NONNULL(new_kv_dev);
+    LS_NONNULL(pool);
+    LS_ALIGNED(new_kv_dev);
+    LS_ALIGNED(pool);
+    LS_TRY(resolve_pool(pool, desc->pool_on_host, &pd));
+  }
+  LS_HIP(ls::launch_append_token(new_k8_dev, new_kv_dev, (int8_t*)k8d, kc_dev, (void*)pd,
+                                 ctx_len_dev, desc->batch, desc->head_dim, desc->max_ctx,
+                                 desc->row_elems, (hipStream_t)stream),
+         "append launch");
   return LS_OK;
 }
 
@@ -570,6 +641,23 @@ int ls_decode_step(const ls_step_desc* desc, const ls_step_io* io, void* ws_dev,
     kb = io->k_cache_dev;
     vb = io->v_cache_dev;
   }
+  const ls_commit_desc* cm = &desc->commit;
+  if ((cm->hot != 0 && cm->hot != 1) || (cm->keys != 0 && cm->keys != 1))
+    return fail(LS_E_ARG, "commit.hot and commit.keys must be 0 or 1");
+  if (cm->hot) {
+    if (!desc->use_hot) return fail(LS_E_ARG, "commit.hot needs the hot buffer (use_hot = 1)");
+    LS_TRY(check_commit_shape(desc->hot.hot_slots, id->topk, cm->now, "commit.hot"));
+    if ((int64_t)(desc->hot.hot_slots + id->topk) * desc->hot.row_elems * 2 >= ((int64_t)1 << 32))
+      return fail(LS_E_ARG, "commit.hot: the hot buffer of a request must stay below 4 GiB");
+    LS_NONNULL(io->slot2pos_dev);
+    LS_NONNULL(io->stamp_dev);
+  }
+  if (cm->keys) {
+    if (id->key_slots < 1) return fail(LS_E_ARG, "commit.keys needs a key cache (key_slots > 0)");
+    LS_TRY(check_commit_shape(id->key_slots, id->n_cand, cm->now, "commit.keys"));
+    LS_NONNULL(io->kslot2pos_dev);
+    LS_NONNULL(io->kstamp_dev);
+  }
   LS_TRY(check_ws(LS_OP_STEP, desc, ws_dev, ws_bytes));
   const void* pool = nullptr;
   if (desc->use_hot) LS_TRY(resolve_pool(io->pool_kv_dev, desc->hot.pool_on_host, &pool));
@@ -595,6 +683,15 @@ int ls_decode_step(const ls_step_desc* desc, const ls_step_io* io, void* ws_dev,
   LS_TRY(run_coarse(id, io->q_idx_dev, io->w_idx_dev, io->kc_dev, io->ctx_len_dev, io->cand_dev,
                     cws, st, ev));
   if (ev && ev[2]) LS_HIP(hipEventRecord((hipEvent_t)ev[2], st), "event record");
+  if (cm->keys) {
+    // the candidates' key-cache hits and the rows their misses move into;
+    // the refinement reads by these codes and fills the rows
+    LS_HIP(ls::launch_cache_commit(ls::kCommitKey, io->cand_dev, id->n_cand, io->kpos2slot_dev,
+                                   io->kslot2pos_dev, io->kstamp_dev, id->key_slots, id->batch,
+                                   id->max_ctx, cm->now, rws.kcode, nullptr, nullptr, st),
+           "key-cache commit launch");
+    k8.code = rws.kcode;
+  }
   LS_HIP(ls::launch_refine_topk(io->q_idx_dev, io->w_idx_dev, k8, io->cand_dev, rws,
                                 io->topk_dev, io->topk_score_dev,
                                 desc->use_hot ? io->pos2slot_dev : nullptr,
@@ -604,10 +701,18 @@ int ls_decode_step(const ls_step_desc* desc, const ls_step_io* io, void* ws_dev,
                                 id->topk, st),
          "refine launch");
   if (ev && ev[3]) LS_HIP(hipEventRecord((hipEvent_t)ev[3], st), "event record");
+  if (cm->hot)
+    // the misses' victim slots (rows[] rewritten to them), before the gather
+    // writes the rows there
+    LS_HIP(ls::launch_cache_commit(ls::kCommitHot, io->topk_dev, id->topk, io->pos2slot_dev,
+                                   io->slot2pos_dev, io->stamp_dev, desc->hot.hot_slots,
+                                   id->batch, id->max_ctx, cm->now, rws.miss_dst, io->rows_dev,
+                                   nullptr, st),
+           "hot-buffer commit launch");
   if (desc->use_hot)
-    LS_HIP(ls::launch_hot_gather(rws.miss_pos, io->n_miss_dev, pool, io->hot_kv_dev,
-                                 desc->hot.hot_slots, id->batch, id->max_ctx, id->topk,
-                                 desc->hot.row_elems, st),
+    LS_HIP(ls::launch_hot_gather(rws.miss_pos, io->n_miss_dev, cm->hot ? rws.miss_dst : nullptr,
+                                 pool, io->hot_kv_dev, desc->hot.hot_slots, id->batch,
+                                 id->max_ctx, id->topk, desc->hot.row_elems, st),
            "miss gather launch");
   if (ev && ev[4]) LS_HIP(hipEventRecord((hipEvent_t)ev[4], st), "event record");
   LS_TRY(run_attention(a, st, ev));

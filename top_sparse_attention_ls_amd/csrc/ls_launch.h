@@ -57,20 +57,38 @@ using WideWS = SelectWS<int64_t>;    // int64 scores, 7552 buckets
 
 // Where the refinement reads a candidate's original int8 key row: k8
 // [B, max_ctx, D] (device memory, or the device alias of pinned host
-// memory), unless key_slots > 0 and kslot[b, t] names a row of the request's
-// key cache kcache [B, key_slots, D] in device memory.
+// memory), unless key_slots > 0 and the candidate's key is in the request's
+// key cache kcache [B, key_slots, D] in device memory.  The cache row comes
+// either from the slot table kslot [B, max_ctx] (code == nullptr) or from a
+// per-candidate code [B, n_cand] written by the key-cache commit: the slot
+// of a hit, -(2 + v) for a miss the refinement copies into row v, -1.
 struct KeySource {
   const int8_t* k8;
   const int32_t* kslot;
-  const int8_t* kcache;
+  int8_t* kcache;
   int key_slots;
+  const int32_t* code;
 };
 
 struct RefineWS {
   int64_t* fs;         // [B, n_cand]
   int32_t* slot;       // [B, n_cand] hot slot of each candidate (with a slot table)
   int32_t* miss_pos;   // [B, topk]
+  int32_t* kcode;      // [B, n_cand] key-cache commit codes
+  int32_t* miss_dst;   // [B, topk] hot-buffer slot of each inserted miss, or -1
 };
+
+// Cache commit (least recently used), one workgroup per request.
+constexpr int kCommitDst = 0, kCommitHot = 1, kCommitKey = 2;
+constexpr int kCommitMaxSlots = 16384;
+constexpr int kCommitMaxEntries = 16384;
+hipError_t launch_cache_commit(int mode, const int32_t* entries, int n, int32_t* pos2slot,
+                               int32_t* slot2pos, uint32_t* stamp, int S, int B, int max_ctx,
+                               uint32_t now, int32_t* out, int32_t* rows, int32_t* n_ins,
+                               hipStream_t st);
+hipError_t launch_append_token(const int8_t* new_k8, const void* new_kv, int8_t* k8,
+                               uint8_t* kc, void* pool, int32_t* ctx_len, int B, int D,
+                               int max_ctx, int row_elems, hipStream_t st);
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 
@@ -112,9 +130,9 @@ hipError_t launch_hot_resolve(const int32_t* topk, const int32_t* pos2slot, int3
                               int32_t* n_miss, int32_t* miss_pos, int hot_slots, int B,
                               int max_ctx, int K, hipStream_t st);
 
-hipError_t launch_hot_gather(const int32_t* miss_pos, const int32_t* n_miss, const void* pool,
-                             void* hot, int hot_slots, int B, int max_ctx, int K, int row_elems,
-                             hipStream_t st);
+hipError_t launch_hot_gather(const int32_t* miss_pos, const int32_t* n_miss,
+                             const int32_t* miss_dst, const void* pool, void* hot, int hot_slots,
+                             int B, int max_ctx, int K, int row_elems, hipStream_t st);
 
 struct AttnArgs {
   const uint16_t* q;
