@@ -292,6 +292,107 @@ def run_prefill(ls, synth, wl, args):
     print(json.dumps(result), flush=True)
 
 
+def run_serve(ls, synth, wl, args):
+    """Decode steps in a row as in serving: the original keys in pinned host
+    memory behind the indexer-key cache, both caches starting empty and
+    committing every step (least recently used), one new token appended per
+    step and request, the indexer query drifting from step to step.  The
+    caches' hit rates emerge from the steps.  value = layer-steps/s of the
+    whole loop (step, commits and append); the PCIe bytes are the key rows
+    of the candidates missing the key cache."""
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, L, H, D, C, K = wl.batch, wl.ctx, wl.idx_heads, wl.idx_dim, wl.n_cand, wl.topk
+    S, SK, row = wl.hot_slots, wl.key_slots, wl.qk_dim
+    n_stat = 8
+    total = args.warmup + args.steps + n_stat
+    print("[bench] building serving state for %s" % wl.name, file=sys.stderr, flush=True)
+    inp = synth.indexer_inputs(wl, dev)
+    keys = inp["keys"]
+    kc = ls.pack_coarse(keys)
+    k8 = keys.to("cpu").pin_memory()
+    del keys, inp["keys"]
+    pool = synth.kv_pool(wl, dev, gen_device=dev)
+    q_attn = synth.attention_query(wl, dev)
+    # room for every appended token
+    ctx_len = torch.full((B,), L - total - 1, dtype=torch.int32, device=dev)
+    g = synth.generator(wl.seed, 100, 0, dev)
+    qs = [inp["q"]]
+    for _ in range(total - 1):
+        qs.append(synth.drift_query(qs[-1], wl.serve_drift, g, dev))
+    new_k = [synth.int8_normal((B, D), 24.0, g, dev) for _ in range(16)]
+    new_kv = [synth.bf16_normal((B, row), g, dev) for _ in range(16)]
+    hot = torch.zeros((B, S + K, row), dtype=torch.bfloat16, device=dev)
+    p2s = torch.full((B, L), -1, dtype=torch.int32, device=dev)
+    s2p = torch.full((B, S), -1, dtype=torch.int32, device=dev)
+    st = torch.zeros((B, S), dtype=torch.int32, device=dev)
+    kp2s = torch.full((B, L), -1, dtype=torch.int32, device=dev)
+    ks2p = torch.full((B, SK), -1, dtype=torch.int32, device=dev)
+    kst = torch.zeros((B, SK), dtype=torch.int32, device=dev)
+    kcache = torch.zeros((B, SK, D), dtype=torch.int8, device=dev)
+    step = ls.DecodeStep(batch=B, max_ctx=L, idx_heads=H, idx_dim=D, n_cand=C, topk=K,
+                         q_heads=wl.q_heads, qk_dim=wl.qk_dim, v_dim=wl.v_dim, scale=wl.scale,
+                         hot_slots=S, keys_on_host=True, key_slots=SK, commit_hot=True,
+                         commit_keys=True, device=dev)
+    counter = [0]
+
+    def one():
+        i = counter[0]
+        counter[0] += 1
+        step.run(q_idx=qs[i], w_idx=inp["w"], kc=kc, k8=k8, ctx_len=ctx_len, q_attn=q_attn,
+                 pos2slot=p2s, hot_kv=hot, pool_kv=pool, kpos2slot=kp2s, kcache=kcache,
+                 slot2pos=s2p, stamp=st, kslot2pos=ks2p, kstamp=kst, now=i + 1)
+        ls.append_token(new_k[i % 16], k8, kc, ctx_len, new_kv=new_kv[i % 16], pool=pool)
+
+    torch.cuda.synchronize()
+    print("[bench] warmup %d, then timing %d steps" % (args.warmup, args.steps),
+          file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        one()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    hot_miss, key_miss = [], []
+    for _ in range(n_stat):
+        one()
+        torch.cuda.synchronize()
+        hot_miss.append(int(step.n_miss.sum()))
+        key_miss.append(int(step.n_key_miss.sum()))
+    km = sum(key_miss) / n_stat
+    result = {
+        "metric": "sparse-decode layer-steps/s, serving loop (commits + append)",
+        "value": round(1000.0 / ms, 2),
+        "unit": "layer-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "ctx": L, "idx_heads": H, "idx_dim": D,
+                   "n_cand": C, "topk": K, "hot_slots": S, "key_slots": SK,
+                   "query_drift": wl.serve_drift, "keys": "pinned-host", "pool": "hbm",
+                   "parallelism": "single-gpu"},
+        "emergent": {
+            "hot_miss_rate": round(sum(hot_miss) / n_stat / (B * K), 4),
+            "key_miss_rate": round(km / (B * C), 4),
+            "pcie_key_bytes_per_step": int(km * D),
+            "pcie_GBs_at_value": round(km * D * 1000.0 / ms / 1e9, 2),
+            "steps_sampled": n_stat,
+        },
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -317,6 +418,9 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     if wl.n_query:
         run_prefill(ls, synth, wl, args)
+        return
+    if wl.serve_drift > 0:
+        run_serve(ls, synth, wl, args)
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -219,6 +219,8 @@ typedef struct {
                                    slot, in/out (commit.hot; else nullable)  */
     int32_t *kslot2pos_dev;     /* [B, key_slots] (commit.keys; else nullable)*/
     uint32_t *kstamp_dev;       /* [B, key_slots] (commit.keys; else nullable)*/
+    int32_t *n_key_miss_dev;    /* out [B] (nullable; written with commit.keys):
+                                   candidates whose key was read from k8     */
 } ls_step_io;
 
 /* Prefill chunk: n_query query tokens at absolute positions

@@ -111,14 +111,6 @@ def test_append_token(ls, host):
     assert np_(cl).tolist() == [1, 18, L]
 
 
-def drift_query(q, rate, seed):
-    """The next step's indexer query: a share of the elements redrawn."""
-    g = torch.Generator().manual_seed(seed)
-    fresh = synth.int8_normal(q.shape, 24.0, g, "cpu")
-    keep = torch.rand(q.shape, generator=g) >= rate
-    return torch.where(keep, q, fresh)
-
-
 def test_decode_steps_with_commits_and_append(ls):
     wl = dataclasses.replace(synth.WORKLOADS["decode-128k-b32"], name="commit-steps", batch=2,
                              ctx=6000, n_cand=1024, topk=256, planted=60, hot_slots=400,
@@ -154,7 +146,7 @@ def test_decode_steps_with_commits_and_append(ls):
     for k in range(5):
         now = k + 1
         if k:
-            q = drift_query(q, 0.15, 100 + k)
+            q = synth.drift_query(q, 0.15, torch.Generator().manual_seed(100 + k), "cpu")
         print("[commit-steps] step %d" % k, flush=True)
         out, lse = step.run(q_idx=q.to(DEV), w_idx=w.to(DEV), kc=kc_d, k8=k8_host, ctx_len=cl_d,
                             q_attn=q_attn.to(DEV), pos2slot=d_tab[0], hot_kv=d_hot,
@@ -167,6 +159,8 @@ def test_decode_steps_with_commits_and_append(ls):
             cand = oracle_cand(qb, wb, kb, ctx[b], C)
             assert np_(step.cand)[b].tolist() == cand.tolist(), (k, b, "cand")
             # key cache: the candidates' hits, then the misses moved in
+            n_kmiss = int(((cand >= 0) & (kp2s[b][np.maximum(cand, 0)] < 0)).sum())
+            assert int(np_(step.n_key_miss)[b]) == n_kmiss, (k, b, "key misses")
             kdst, _ = orc.cache_commit(cand, SK, now, kp2s[b], ks2p[b], kst[b])
             for i, t in enumerate(cand):
                 if t >= 0 and kdst[i] >= 0:

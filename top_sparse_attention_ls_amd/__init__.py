@@ -71,7 +71,7 @@ class StepIO(ctypes.Structure):
         "ctx_len_dev", "cand_dev", "topk_dev",
         "topk_score_dev", "pos2slot_dev", "hot_kv_dev", "pool_kv_dev", "rows_dev", "n_miss_dev",
         "q_attn_dev", "k_cache_dev", "v_cache_dev", "out_dev", "lse_dev", "stage_events",
-        "slot2pos_dev", "stamp_dev", "kslot2pos_dev", "kstamp_dev")]
+        "slot2pos_dev", "stamp_dev", "kslot2pos_dev", "kstamp_dev", "n_key_miss_dev")]
 
 
 class PrefillDesc(ctypes.Structure):
@@ -345,6 +345,8 @@ class DecodeStep:
         self.n_miss = torch.empty((batch,), dtype=torch.int32, device=dev)
         self.out = torch.empty((batch, q_heads, v_dim), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((batch, q_heads), dtype=torch.float32, device=dev)
+        # candidates whose key came from k8 (written when the key cache commits)
+        self.n_key_miss = torch.zeros((batch,), dtype=torch.int32, device=dev)
 
     def run(self, *, q_idx, w_idx, kc, k8, ctx_len, q_attn, pos2slot=None, hot_kv=None,
             pool_kv=None, k_cache=None, v_cache=None, kpos2slot=None, kcache=None,
@@ -405,6 +407,7 @@ class DecodeStep:
             _need(kslot2pos, torch.int32, "kslot2pos", (B, S))
             _need(kstamp, torch.int32, "kstamp", (B, S))
             io.kslot2pos_dev, io.kstamp_dev = kslot2pos.data_ptr(), kstamp.data_ptr()
+            io.n_key_miss_dev = self.n_key_miss.data_ptr()
         if events is not None:  # STEP_EVENTS torch events; None entries are skipped
             arr = (ctypes.c_void_p * STEP_EVENTS)(*[e.cuda_event if e is not None else None
                                                     for e in events])

@@ -25,8 +25,11 @@ namespace ls {
 // victims are found by an exact radix select of the stamps (three digit
 // passes of 11, 11 and 10 bits over a 2048-bin LDS histogram) and the slots
 // of equal stamp are taken in slot order.  Thread t owns the contiguous slot
-// range [t*SE, t*SE + SE) and the entry range [t*E, t*E + E), so that
-// prefix sums over threads give slot order and entry order.
+// range [t*SE, t*SE + SE) and the entry range [t*EPT, t*EPT + EPT), so
+// that prefix sums over threads give slot order and entry order.  Global
+// loads are issued all at once per phase (indices clamped, results selected
+// afterwards): the table lookups are random reads, and a chain of them per
+// thread would serialise their latencies.
 //
 // Outputs by mode:
 //   kCommitDst: dst[b, e] = the entry's slot after the commit, or -1;
@@ -35,11 +38,31 @@ namespace ls {
 //               inserted) -- the gather then writes the row into the slot;
 //   kCommitKey: code[b, e] = the slot of a hit, -(2 + victim) for an
 //               inserted miss (the refinement copies the row it reads into
-//               that slot), -1 otherwise.
+//               that slot), -1 otherwise; n_ins[b] = the number of misses.
 constexpr int kCommitThreads = 1024;
 constexpr int kDigitBins = 2048;
 
-template <int MODE>
+// hist[bin] += 1 for every active lane, with the lanes of the wave that share
+// a bin merged into one LDS atomic for up to two distinct bins (stamps are
+// step numbers, so a wave's slots usually hold a few values, and one LDS
+// address hit by a whole wave's atomics serialises them); lanes left after
+// that add their own.
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool active) {
+  const int l = lane_id();
+#pragma unroll
+  for (int r = 0; r < 2; r++) {
+    const uint64_t act = __ballot(active);
+    if (act == 0) break;
+    const int leader = __ffsll((unsigned long long)act) - 1;
+    const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, leader);
+    const uint64_t m = __ballot(active && bin == lb);
+    if (l == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(m));
+    active = active && bin != lb;
+  }
+  if (active) atomicAdd(&hist[bin], 1u);
+}
+
+template <int MODE, int EPT>
 __global__ __launch_bounds__(kCommitThreads) void k_cache_commit(
     const int32_t* __restrict__ entries, int n, int32_t* __restrict__ pos2slot,
     int32_t* __restrict__ slot2pos, uint32_t* __restrict__ stamp, int S, int max_ctx,
@@ -50,6 +73,7 @@ __global__ __launch_bounds__(kCommitThreads) void k_cache_commit(
   __shared__ uint32_t hist[kDigitBins];
   __shared__ uint32_t sh_scan[kCommitThreads / kWave];
   __shared__ uint32_t sh_pick[2];
+  __shared__ uint32_t sh_lo[kCommitThreads / kWave], sh_hi[kCommitThreads / kWave];
 
   const int b = blockIdx.x, tid = threadIdx.x;
   const int32_t* eb = entries + (size_t)b * n;
@@ -58,32 +82,43 @@ __global__ __launch_bounds__(kCommitThreads) void k_cache_commit(
   uint32_t* stb = stamp + (size_t)b * S;
   int32_t* ob = out + (size_t)b * n;
 
-  for (int s = tid; s < S; s += kCommitThreads) key[s] = stb[s];
+  constexpr int kSlotIters = kCommitMaxSlots / kCommitThreads;
+  const int e0 = tid * EPT;
+  // the entries and their table values, all loads in flight together
+  int32_t t[EPT], sl[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; i++) t[i] = eb[min(e0 + i, n - 1)];
+  {
+    uint32_t sv[kSlotIters];
+#pragma unroll
+    for (int i = 0; i < kSlotIters; i++) sv[i] = stb[min(tid + kCommitThreads * i, S - 1)];
+#pragma unroll
+    for (int i = 0; i < EPT; i++) {
+      const bool ok = e0 + i < n && t[i] >= 0 && t[i] < max_ctx;
+      t[i] = ok ? t[i] : -1;
+      sl[i] = p2s[ok ? t[i] : 0];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kSlotIters; i++)
+      if (tid + kCommitThreads * i < S) key[tid + kCommitThreads * i] = sv[i];
+  }
   for (int w = tid; w < kCommitMaxSlots / 32; w += kCommitThreads) hitbits[w] = 0u;
   __syncthreads();
 
   // entries: hits set their slot's bit; misses are flagged (mask over the
-  // thread's E entries, taken from the table state before any update)
-  const int E = (n + kCommitThreads - 1) / kCommitThreads;  // <= kCommitMaxEntries / 1024
-  const int e0 = tid * E;
+  // thread's entries, from the table state before any update)
   uint32_t mmask = 0u, n_m_t = 0u;
-  for (int i = 0; i < E; i++) {
-    const int e = e0 + i;
-    if (e >= n) break;
-    const int32_t t = eb[e];
-    int32_t s = -1;
-    bool miss = false;
-    if (t >= 0 && t < max_ctx) {
-      s = p2s[t];
-      if (s >= 0 && s < S) atomicOr(&hitbits[s >> 5], 1u << (s & 31));
-      miss = s < 0;
-    }
-    if (miss) {
+#pragma unroll
+  for (int i = 0; i < EPT; i++) {
+    const int32_t s = t[i] >= 0 ? sl[i] : -1;
+    if (s >= 0 && s < S) atomicOr(&hitbits[s >> 5], 1u << (s & 31));
+    if (t[i] >= 0 && s < 0) {
       mmask |= 1u << i;
       n_m_t++;
     }
-    if (MODE == kCommitDst) ob[e] = (s >= 0 && s < S) ? s : -1;
-    if (MODE == kCommitKey) ob[e] = (s >= 0 && s < S) ? s : -1;
+    if ((MODE == kCommitDst || MODE == kCommitKey) && e0 + i < n)
+      ob[e0 + i] = (s >= 0 && s < S) ? s : -1;
   }
   __syncthreads();
 
@@ -107,10 +142,54 @@ __global__ __launch_bounds__(kCommitThreads) void k_cache_commit(
   block_excl_scan<kCommitThreads>(n_hit_t, sh_scan, &n_h);
   const uint32_t n_v = min(n_m, (uint32_t)S - n_h);
 
-  // radix select: T = the n_v-th smallest stamp among the slots not hit;
-  // need = how many slots of stamp T are victims
+  // the range of the eligible stamps
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int i = 0; i < kCommitMaxSlots / kCommitThreads; i++) {
+    if ((elig >> i) & 1u) {
+      lo = min(lo, kv[i]);
+      hi = max(hi, kv[i]);
+    }
+  }
+  lo = (uint32_t)wave_min_u64(lo);
+  hi = (uint32_t)wave_max_u64(hi);
+  if (lane_id() == 0) {
+    sh_lo[wave_id()] = lo;
+    sh_hi[wave_id()] = hi;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kCommitThreads / kWave; w++) {
+    lo = min(lo, sh_lo[w]);
+    hi = max(hi, sh_hi[w]);
+  }
+
+  // select T = the n_v-th smallest stamp among the slots not hit, and
+  // need = how many slots of stamp T are victims: one histogram pass over
+  // stamp - lo when the stamps span fewer than 2048 values (stamps are step
+  // numbers, so they usually do), else a radix select over the 32 bits
   uint32_t prefix = 0u, pmask = 0u, need = n_v;
-  if (n_v > 0) {
+  if (n_v > 0 && hi - lo < (uint32_t)kDigitBins) {
+    for (int i = tid; i < kDigitBins; i += kCommitThreads) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kCommitMaxSlots / kCommitThreads; i++)
+      hist_add(hist, kv[i] - lo, (elig >> i) & 1u);
+    __syncthreads();
+    const uint32_t c0 = hist[2 * tid], c1 = hist[2 * tid + 1];
+    uint32_t tot;
+    const uint32_t base = block_excl_scan<kCommitThreads>(c0 + c1, sh_scan, &tot);
+    if (base < need && need <= base + c0) {
+      sh_pick[0] = 2u * tid;
+      sh_pick[1] = base;
+    } else if (base + c0 < need && need <= base + c0 + c1) {
+      sh_pick[0] = 2u * tid + 1u;
+      sh_pick[1] = base + c0;
+    }
+    __syncthreads();
+    prefix = lo + sh_pick[0];
+    need -= sh_pick[1];
+  } else if (n_v > 0) {
 #pragma unroll 1
     for (int pass = 0; pass < 3; pass++) {
       const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
@@ -119,8 +198,7 @@ __global__ __launch_bounds__(kCommitThreads) void k_cache_commit(
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < kCommitMaxSlots / kCommitThreads; i++)
-        if (((elig >> i) & 1u) && (kv[i] & pmask) == prefix)
-          atomicAdd(&hist[(kv[i] >> shift) & dmask], 1u);
+        hist_add(hist, (kv[i] >> shift) & dmask, ((elig >> i) & 1u) && (kv[i] & pmask) == prefix);
       __syncthreads();
       const uint32_t c0 = hist[2 * tid], c1 = hist[2 * tid + 1];
       uint32_t tot;
@@ -180,41 +258,60 @@ __global__ __launch_bounds__(kCommitThreads) void k_cache_commit(
   // misses in entry order move into the victims (tot_v equals n_v; the
   // minimum only keeps every victim read inside the list)
   const uint32_t n_use = min(n_v, tot_v);
+  uint32_t jr[EPT];
+  int32_t v[EPT], old[EPT];
   uint32_t j = m_base;
-  for (int i = 0; i < E; i++) {
+#pragma unroll
+  for (int i = 0; i < EPT; i++) {
+    const bool m = (mmask >> i) & 1u;
+    jr[i] = j;
+    v[i] = (m && j < n_use) ? (int32_t)min(key[j], (uint32_t)(S - 1)) : -1;
+    j += m ? 1u : 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < EPT; i++) old[i] = s2p[max(v[i], 0)];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < EPT; i++) {
     if (!((mmask >> i) & 1u)) continue;
     const int e = e0 + i;
-    const int32_t t = eb[e];
-    int32_t v = -1;
-    if (j < n_use) {
-      v = (int32_t)min(key[j], (uint32_t)(S - 1));
-      const int32_t old = s2p[v];
-      if (old >= 0 && old < max_ctx) p2s[old] = -1;
-      p2s[t] = v;
-      s2p[v] = t;
+    if (v[i] >= 0) {
+      if (old[i] >= 0 && old[i] < max_ctx) p2s[old[i]] = -1;
+      p2s[t[i]] = v[i];
+      s2p[v[i]] = t[i];
     }
-    if (MODE == kCommitDst) ob[e] = v;
-    if (MODE == kCommitKey) ob[e] = v >= 0 ? -2 - v : -1;
+    if (MODE == kCommitDst) ob[e] = v[i];
+    if (MODE == kCommitKey) ob[e] = v[i] >= 0 ? -2 - v[i] : -1;
     if (MODE == kCommitHot) {
-      ob[j] = v;
-      if (v >= 0) rows[(size_t)b * n + e] = v;
+      ob[jr[i]] = v[i];
+      if (v[i] >= 0) rows[(size_t)b * n + e] = v[i];
     }
-    j++;
   }
-  if (tid == 0 && n_ins) n_ins[b] = (int32_t)n_use;
+  // n_ins: misses inserted; for the key cache, the misses (every one of
+  // them is read from the key store, inserted or not)
+  if (tid == 0 && n_ins) n_ins[b] = (int32_t)(MODE == kCommitKey ? n_m : n_use);
 }
 
 hipError_t launch_cache_commit(int mode, const int32_t* entries, int n, int32_t* pos2slot,
                                int32_t* slot2pos, uint32_t* stamp, int S, int B, int max_ctx,
                                uint32_t now, int32_t* out, int32_t* rows, int32_t* n_ins,
                                hipStream_t st) {
-#define LS_COMMIT(M)                                                                          \
-  hipLaunchKernelGGL(k_cache_commit<M>, dim3(B), dim3(kCommitThreads), 0, st, entries, n,     \
+#define LS_COMMIT_E(M, E)                                                                      \
+  hipLaunchKernelGGL((k_cache_commit<M, E>), dim3(B), dim3(kCommitThreads), 0, st, entries, n, \
                      pos2slot, slot2pos, stamp, S, max_ctx, now, out, rows, n_ins)
+#define LS_COMMIT(M)                                                                          \
+  do {                                                                                        \
+    if (n <= kCommitThreads) LS_COMMIT_E(M, 1);                                               \
+    else if (n <= 2 * kCommitThreads) LS_COMMIT_E(M, 2);                                      \
+    else if (n <= 4 * kCommitThreads) LS_COMMIT_E(M, 4);                                      \
+    else if (n <= 8 * kCommitThreads) LS_COMMIT_E(M, 8);                                      \
+    else LS_COMMIT_E(M, 16);                                                                  \
+  } while (0)
   if (mode == kCommitHot) LS_COMMIT(kCommitHot);
   else if (mode == kCommitKey) LS_COMMIT(kCommitKey);
   else LS_COMMIT(kCommitDst);
 #undef LS_COMMIT
+#undef LS_COMMIT_E
   return hipGetLastError();
 }
 

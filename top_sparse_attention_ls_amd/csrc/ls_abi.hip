@@ -688,7 +688,8 @@ int ls_decode_step(const ls_step_desc* desc, const ls_step_io* io, void* ws_dev,
     // the refinement reads by these codes and fills the rows
     LS_HIP(ls::launch_cache_commit(ls::kCommitKey, io->cand_dev, id->n_cand, io->kpos2slot_dev,
                                    io->kslot2pos_dev, io->kstamp_dev, id->key_slots, id->batch,
-                                   id->max_ctx, cm->now, rws.kcode, nullptr, nullptr, st),
+                                   id->max_ctx, cm->now, rws.kcode, nullptr, io->n_key_miss_dev,
+                                   st),
            "key-cache commit launch");
     k8.code = rws.kcode;
   }

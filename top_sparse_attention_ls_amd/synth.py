@@ -59,6 +59,9 @@ class Workload:
     keys_on_host: bool = False       # original int8 keys in pinned host memory
     key_slots: int = 0               # rows of the per-request indexer-key cache (0: none)
     key_miss_rate: float = 0.0       # share of the candidates whose key is not cached
+    # multi-step serving: both caches commit each step, a token is appended,
+    # and the indexer query drifts (each element redrawn with this rate)
+    serve_drift: float = 0.0
     # prefill only
     n_query: int = 0
     layers: int = 0
@@ -87,6 +90,13 @@ WORKLOADS = {
                                          topk=2048, planted=1310, hot_slots=4096,
                                          miss_rate=0.2, keys_on_host=True, key_slots=16384,
                                          key_miss_rate=0.2),
+    # serving: steps in a row over the host-keys layout, both caches starting
+    # empty and committing every step, one token appended per step and
+    # request, the indexer query drifting by 10% of its elements per step
+    "decode-128k-b32-serve": Workload("decode-128k-b32-serve", 1001, batch=32, ctx=131072,
+                                      idx_heads=64, idx_dim=128, n_cand=8192, topk=2048,
+                                      planted=1310, hot_slots=4096, keys_on_host=True,
+                                      key_slots=16384, serve_drift=0.1),
     # decode near 1M context, 4 requests, planted tokens in 8 bursts of 512
     "decode-950k-b4": Workload("decode-950k-b4", 1003, batch=4, ctx=950000, idx_heads=64,
                                idx_dim=128, n_cand=16384, topk=2048, bursts=(8, 512),
@@ -300,6 +310,15 @@ def key_cache_fill(wl: Workload, cand: torch.Tensor, keys: torch.Tensor, device,
         kcache[b, res_row.to(torch.int64).to(device)] = src.to(device)
         n_miss.append(nm)
     return kpos2slot, kcache, n_miss
+
+
+def drift_query(q: torch.Tensor, rate: float, g: torch.Generator, device) -> torch.Tensor:
+    """The next decode step's indexer query: each element redrawn from the
+    query distribution with probability rate (a synthetic model of how a
+    request's selection carries over from step to step)."""
+    fresh = int8_normal(q.shape, 24.0, g, device)
+    keep = torch.rand(q.shape, generator=g, device=device) >= rate
+    return torch.where(keep, q, fresh)
 
 
 def ragged_lengths(wl: Workload, batch: int, max_ctx: int, min_ctx: int = 0) -> list:
