@@ -25,6 +25,7 @@ Prints one JSON line with:
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -293,60 +294,97 @@ def run_prefill(ls, synth, wl, args):
 
 
 def run_serve(ls, synth, wl, args):
-    """Decode steps in a row as in serving: the original keys in pinned host
-    memory behind the indexer-key cache, both caches starting empty and
-    committing every step (least recently used), one new token appended per
-    step and request, the indexer query drifting from step to step.  The
-    caches' hit rates emerge from the steps.  value = layer-steps/s of the
-    whole loop (step, commits and append); the PCIe bytes are the key rows
-    of the candidates missing the key cache."""
+    """Decode steps in a row as in serving, over wl.layers layers (default
+    one): per layer, the original keys in pinned host memory behind the
+    indexer-key cache, both caches starting empty and committing every step
+    (least recently used), one new token appended per step and request; the
+    indexer queries drift from step to step (a ring of 32 drifted queries per
+    layer).  One token step runs every layer in turn, then advances the
+    stamp counter on the device.  value = layer-steps/s of that loop; with
+    --graph the whole token step (every layer, its commits and appends, the
+    counter) is captured once in a HIP graph and replayed, one graph per
+    query of the ring.  The PCIe bytes are the key rows of the candidates
+    missing the key cache."""
     import torch
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     B, L, H, D, C, K = wl.batch, wl.ctx, wl.idx_heads, wl.idx_dim, wl.n_cand, wl.topk
     S, SK, row = wl.hot_slots, wl.key_slots, wl.qk_dim
-    n_stat = 8
-    total = args.warmup + args.steps + n_stat
-    print("[bench] building serving state for %s" % wl.name, file=sys.stderr, flush=True)
-    inp = synth.indexer_inputs(wl, dev)
-    keys = inp["keys"]
-    kc = ls.pack_coarse(keys)
-    k8 = keys.to("cpu").pin_memory()
-    del keys, inp["keys"]
-    pool = synth.kv_pool(wl, dev, gen_device=dev)
-    q_attn = synth.attention_query(wl, dev)
-    # room for every appended token
-    ctx_len = torch.full((B,), L - total - 1, dtype=torch.int32, device=dev)
-    g = synth.generator(wl.seed, 100, 0, dev)
-    qs = [inp["q"]]
-    for _ in range(total - 1):
-        qs.append(synth.drift_query(qs[-1], wl.serve_drift, g, dev))
-    new_k = [synth.int8_normal((B, D), 24.0, g, dev) for _ in range(16)]
-    new_kv = [synth.bf16_normal((B, row), g, dev) for _ in range(16)]
-    hot = torch.zeros((B, S + K, row), dtype=torch.bfloat16, device=dev)
-    p2s = torch.full((B, L), -1, dtype=torch.int32, device=dev)
-    s2p = torch.full((B, S), -1, dtype=torch.int32, device=dev)
-    st = torch.zeros((B, S), dtype=torch.int32, device=dev)
-    kp2s = torch.full((B, L), -1, dtype=torch.int32, device=dev)
-    ks2p = torch.full((B, SK), -1, dtype=torch.int32, device=dev)
-    kst = torch.zeros((B, SK), dtype=torch.int32, device=dev)
-    kcache = torch.zeros((B, SK, D), dtype=torch.int8, device=dev)
-    step = ls.DecodeStep(batch=B, max_ctx=L, idx_heads=H, idx_dim=D, n_cand=C, topk=K,
-                         q_heads=wl.q_heads, qk_dim=wl.qk_dim, v_dim=wl.v_dim, scale=wl.scale,
-                         hot_slots=S, keys_on_host=True, key_slots=SK, commit_hot=True,
-                         commit_keys=True, device=dev)
-    counter = [0]
+    n_layers = max(wl.layers, 1)
+    ring, n_stat = 32, 8
+    total = args.warmup + args.steps + n_stat + 2 * ring
+    print("[bench] building serving state for %s (%d layers)" % (wl.name, n_layers),
+          file=sys.stderr, flush=True)
+    layers = []
+    for layer in range(n_layers):
+        lw = dataclasses.replace(wl, seed=wl.seed + 7919 * layer)
+        inp = synth.indexer_inputs(lw, dev)
+        kc = ls.pack_coarse(inp["keys"])
+        k8 = inp["keys"].to("cpu").pin_memory()
+        del inp["keys"]
+        g = synth.generator(lw.seed, 100, 0, dev)
+        qs = [inp["q"]]
+        for _ in range(ring - 1):
+            qs.append(synth.drift_query(qs[-1], wl.serve_drift, g, dev))
+        st = dict(
+            w=inp["w"], qs=qs, kc=kc, k8=k8, pool=synth.kv_pool(lw, dev, gen_device=dev),
+            q_attn=synth.attention_query(lw, dev),
+            ctx_len=torch.full((B,), L - total - 1, dtype=torch.int32, device=dev),
+            new_k=[synth.int8_normal((B, D), 24.0, g, dev) for _ in range(4)],
+            new_kv=[synth.bf16_normal((B, row), g, dev) for _ in range(4)],
+            hot=torch.zeros((B, S + K, row), dtype=torch.bfloat16, device=dev),
+            p2s=torch.full((B, L), -1, dtype=torch.int32, device=dev),
+            s2p=torch.full((B, S), -1, dtype=torch.int32, device=dev),
+            st=torch.zeros((B, S), dtype=torch.int32, device=dev),
+            kp2s=torch.full((B, L), -1, dtype=torch.int32, device=dev),
+            ks2p=torch.full((B, SK), -1, dtype=torch.int32, device=dev),
+            kst=torch.zeros((B, SK), dtype=torch.int32, device=dev),
+            kcache=torch.zeros((B, SK, D), dtype=torch.int8, device=dev),
+            step=ls.DecodeStep(batch=B, max_ctx=L, idx_heads=H, idx_dim=D, n_cand=C, topk=K,
+                               q_heads=wl.q_heads, qk_dim=wl.qk_dim, v_dim=wl.v_dim,
+                               scale=wl.scale, hot_slots=S, keys_on_host=True, key_slots=SK,
+                               commit_hot=True, commit_keys=True, device=dev))
+        layers.append(st)
+    now = torch.ones((1,), dtype=torch.int32, device=dev)
 
-    def one():
-        i = counter[0]
-        counter[0] += 1
-        step.run(q_idx=qs[i], w_idx=inp["w"], kc=kc, k8=k8, ctx_len=ctx_len, q_attn=q_attn,
-                 pos2slot=p2s, hot_kv=hot, pool_kv=pool, kpos2slot=kp2s, kcache=kcache,
-                 slot2pos=s2p, stamp=st, kslot2pos=ks2p, kstamp=kst, now=i + 1)
-        ls.append_token(new_k[i % 16], k8, kc, ctx_len, new_kv=new_kv[i % 16], pool=pool)
+    def token_step(i):
+        for x in layers:
+            x["step"].run(q_idx=x["qs"][i % ring], w_idx=x["w"], kc=x["kc"], k8=x["k8"],
+                          ctx_len=x["ctx_len"], q_attn=x["q_attn"], pos2slot=x["p2s"],
+                          hot_kv=x["hot"], pool_kv=x["pool"], kpos2slot=x["kp2s"],
+                          kcache=x["kcache"], slot2pos=x["s2p"], stamp=x["st"],
+                          kslot2pos=x["ks2p"], kstamp=x["kst"], now=now)
+            ls.append_token(x["new_k"][i % 4], x["k8"], x["kc"], x["ctx_len"],
+                            new_kv=x["new_kv"][i % 4], pool=x["pool"])
+        now.add_(1)
+
+    counter = [0]
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(ring):       # warm the caches (and the allocator) eagerly
+                token_step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for i in range(ring):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                token_step(i)
+            graphs.append(gr)
+        torch.cuda.synchronize()
+
+        def one():
+            graphs[counter[0] % ring].replay()
+            counter[0] += 1
+    else:
+        def one():
+            token_step(counter[0])
+            counter[0] += 1
 
     torch.cuda.synchronize()
-    print("[bench] warmup %d, then timing %d steps" % (args.warmup, args.steps),
+    print("[bench] warmup %d, then timing %d token steps" % (args.warmup, args.steps),
           file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         one()
@@ -357,13 +395,13 @@ def run_serve(ls, synth, wl, args):
         one()
     t1.record()
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    ms = t0.elapsed_time(t1) / args.steps / n_layers       # per layer-step
     hot_miss, key_miss = [], []
     for _ in range(n_stat):
         one()
         torch.cuda.synchronize()
-        hot_miss.append(int(step.n_miss.sum()))
-        key_miss.append(int(step.n_key_miss.sum()))
+        hot_miss.append(sum(int(x["step"].n_miss.sum()) for x in layers) / n_layers)
+        key_miss.append(sum(int(x["step"].n_key_miss.sum()) for x in layers) / n_layers)
     km = sum(key_miss) / n_stat
     result = {
         "metric": "sparse-decode layer-steps/s, serving loop (commits + append)",
@@ -379,13 +417,15 @@ def run_serve(ls, synth, wl, args):
         "dtype": "int8+bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "ctx": L, "idx_heads": H, "idx_dim": D,
-                   "n_cand": C, "topk": K, "hot_slots": S, "key_slots": SK,
+                   "n_cand": C, "topk": K, "hot_slots": S, "key_slots": SK, "layers": n_layers,
                    "query_drift": wl.serve_drift, "keys": "pinned-host", "pool": "hbm",
+                   "launch": "hip-graph per token step" if args.graph else "eager",
                    "parallelism": "single-gpu"},
+        "token_steps_per_s": round(1000.0 / (ms * n_layers), 2),
         "emergent": {
             "hot_miss_rate": round(sum(hot_miss) / n_stat / (B * K), 4),
             "key_miss_rate": round(km / (B * C), 4),
-            "pcie_key_bytes_per_step": int(km * D),
+            "pcie_key_bytes_per_layer_step": int(km * D),
             "pcie_GBs_at_value": round(km * D * 1000.0 / ms / 1e9, 2),
             "steps_sampled": n_stat,
         },
@@ -402,6 +442,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=2)
     ap.add_argument("--cpu-sample", type=int, default=4,
                     help="requests the CPU oracle baseline runs (0 = skip)")
+    ap.add_argument("--graph", action="store_true",
+                    help="serving workloads: replay each token step from a HIP graph")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="MiB of a plain device copy run after timing (counter scaling)")
     args = ap.parse_args()

@@ -75,7 +75,7 @@ extern "C" {
 typedef struct ihipStream_t *ls_stream_t;
 typedef struct ihipEvent_t *ls_event_t;
 
-#define LS_ABI_VERSION 3
+#define LS_ABI_VERSION 4
 
 enum {
     LS_OK = 0,
@@ -160,7 +160,11 @@ typedef struct {
  *     k8 into its row; kpos2slot / kslot2pos / kstamp are updated).  Needs
  *     key_slots in [1, 16384], n_cand <= 16384.
  *   now: this step's stamp, below 2^32 - 1 and above every stamp already
- *     in the tables (a step counter starting at 1 over zeroed stamps).
+ *     in the tables (a step counter starting at 1 over zeroed stamps).  With
+ *     ls_step_io.now_dev set, the stamp is read from that device word
+ *     instead, when the kernels run: a step captured once in a graph then
+ *     stamps each replay with the counter's current value (the caller
+ *     advances it between replays, for example inside the same graph).
  * Without commit (both 0) the step only reads the caches and is
  * idempotent.                                                               */
 typedef struct {
@@ -221,6 +225,8 @@ typedef struct {
     uint32_t *kstamp_dev;       /* [B, key_slots] (commit.keys; else nullable)*/
     int32_t *n_key_miss_dev;    /* out [B] (nullable; written with commit.keys):
                                    candidates whose key was read from k8     */
+    const uint32_t *now_dev;    /* nullable: the commit's stamp, read on the
+                                   device (see ls_commit_desc)               */
 } ls_step_io;
 
 /* Prefill chunk: n_query query tokens at absolute positions

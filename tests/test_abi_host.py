@@ -55,7 +55,7 @@ def test_struct_layouts_match_header(tmp_path):
 
 
 def test_version_and_error_string(lib):
-    assert lib.ls_abi_version() == ls.ABI_VERSION == 3
+    assert lib.ls_abi_version() == ls.ABI_VERSION == 4
     assert isinstance(lib.ls_last_error(), bytes)
 
 

@@ -64,3 +64,90 @@ def test_decode_step_graph_replays_match_eager(ls):
         torch.cuda.synchronize()
         for a, b in zip(ref, state(out, lse)):
             assert torch.equal(a, b), "eager step after replay %d differs" % i
+
+
+def serving_layer(ls, wl, seed, dev):
+    lw = dataclasses.replace(wl, seed=seed)
+    B, L, D, S, SK, K, row = (lw.batch, lw.ctx, lw.idx_dim, lw.hot_slots, lw.key_slots, lw.topk,
+                              lw.qk_dim)
+    inp = synth.indexer_inputs(lw, dev)
+    g = torch.Generator(device=dev).manual_seed(seed)
+    return dict(
+        q=inp["q"], w=inp["w"], kc=ls.pack_coarse(inp["keys"]), k8=inp["keys"].cpu().pin_memory(),
+        pool=synth.kv_pool(lw, dev), q_attn=synth.attention_query(lw, dev),
+        ctx_len=torch.tensor([L - 8, L // 2], dtype=torch.int32, device=dev),
+        new_k=synth.int8_normal((B, D), 24.0, g, dev), new_kv=synth.bf16_normal((B, row), g, dev),
+        hot=torch.zeros((B, S + K, row), dtype=torch.bfloat16, device=dev),
+        p2s=torch.full((B, L), -1, dtype=torch.int32, device=dev),
+        s2p=torch.full((B, S), -1, dtype=torch.int32, device=dev),
+        st=torch.zeros((B, S), dtype=torch.int32, device=dev),
+        kp2s=torch.full((B, L), -1, dtype=torch.int32, device=dev),
+        ks2p=torch.full((B, SK), -1, dtype=torch.int32, device=dev),
+        kst=torch.zeros((B, SK), dtype=torch.int32, device=dev),
+        kcache=torch.zeros((B, SK, D), dtype=torch.int8, device=dev),
+        step=ls.DecodeStep(batch=B, max_ctx=L, idx_heads=lw.idx_heads, idx_dim=D,
+                           n_cand=lw.n_cand, topk=K, q_heads=lw.q_heads, qk_dim=lw.qk_dim,
+                           v_dim=lw.v_dim, scale=lw.scale, hot_slots=S, keys_on_host=True,
+                           key_slots=SK, commit_hot=True, commit_keys=True, device=dev))
+
+
+def test_layer_stack_serving_graph_matches_eager(ls):
+    # two layers, each with its own caches committing every step and a token
+    # appended per step; the stamp comes from a device counter that the token
+    # step advances, so one captured token step replays correctly step after
+    # step.  The graph runs on one copy of the state, the eager steps on an
+    # identical copy; after every replay (with eager work and synchronisation
+    # in between) both copies must agree bit for bit.
+    wl = dataclasses.replace(synth.WORKLOADS["decode-128k-b32"], name="stack", batch=2,
+                             ctx=8192, n_cand=1024, topk=256, planted=82, hot_slots=600,
+                             key_slots=1500)
+    copies = [[serving_layer(ls, wl, 500 + l, DEV) for l in range(2)] for _ in range(2)]
+    nows = [torch.ones((1,), dtype=torch.int32, device=DEV) for _ in range(2)]
+
+    def token_step(layers, now):
+        for x in layers:
+            x["step"].run(q_idx=x["q"], w_idx=x["w"], kc=x["kc"], k8=x["k8"],
+                          ctx_len=x["ctx_len"], q_attn=x["q_attn"], pos2slot=x["p2s"],
+                          hot_kv=x["hot"], pool_kv=x["pool"], kpos2slot=x["kp2s"],
+                          kcache=x["kcache"], slot2pos=x["s2p"], stamp=x["st"],
+                          kslot2pos=x["ks2p"], kstamp=x["kst"], now=now)
+            ls.append_token(x["new_k"], x["k8"], x["kc"], x["ctx_len"], new_kv=x["new_kv"],
+                            pool=x["pool"])
+        now.add_(1)
+
+    def snapshot(layers, now):
+        out = [now.clone()]
+        for x in layers:
+            s = x["step"]
+            out += [t.clone() for t in (s.cand, s.topk, s.topk_score, s.rows, s.n_miss,
+                                        s.n_key_miss, s.out.view(torch.int16), s.lse,
+                                        x["hot"].view(torch.int16), x["p2s"], x["s2p"], x["st"],
+                                        x["kp2s"], x["ks2p"], x["kst"], x["kcache"], x["kc"],
+                                        x["ctx_len"], x["pool"].view(torch.int16))]
+            out.append(x["k8"].clone())
+        return out
+
+    # capture on copy 1 (the capture itself runs nothing); a first eager step
+    # on a side stream warms the allocator the way the capture will see it --
+    # run on both copies so that they stay identical
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        token_step(copies[0], nows[0])
+        token_step(copies[1], nows[1])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        token_step(copies[1], nows[1])
+    torch.cuda.synchronize()
+    for k in range(4):
+        token_step(copies[0], nows[0])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        a, b = snapshot(copies[0], nows[0]), snapshot(copies[1], nows[1])
+        for i, (x, y) in enumerate(zip(a, b)):
+            assert torch.equal(x, y), (k, i)
+    # the caches did get used across the steps
+    assert int(copies[1][0]["step"].n_miss.sum()) < 2 * wl.topk

@@ -29,7 +29,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "ls.h")
 LS_OK, LS_E_ARG, LS_E_UNSUPPORTED, LS_E_WORKSPACE, LS_E_HIP = 0, -1, -2, -3, -4
 OP_COARSE, OP_REFINE, OP_HOT, OP_ATTN, OP_STEP, OP_PREFILL = 1, 2, 3, 4, 5, 6
 STEP_EVENTS = 7
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _I32, _I64, _F32, _P = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
 
@@ -71,7 +71,8 @@ class StepIO(ctypes.Structure):
         "ctx_len_dev", "cand_dev", "topk_dev",
         "topk_score_dev", "pos2slot_dev", "hot_kv_dev", "pool_kv_dev", "rows_dev", "n_miss_dev",
         "q_attn_dev", "k_cache_dev", "v_cache_dev", "out_dev", "lse_dev", "stage_events",
-        "slot2pos_dev", "stamp_dev", "kslot2pos_dev", "kstamp_dev", "n_key_miss_dev")]
+        "slot2pos_dev", "stamp_dev", "kslot2pos_dev", "kstamp_dev", "n_key_miss_dev",
+        "now_dev")]
 
 
 class PrefillDesc(ctypes.Structure):
@@ -354,7 +355,8 @@ class DecodeStep:
         """With commits, slot2pos / stamp (hot buffer) and kslot2pos / kstamp
         (key cache) are the caches' LRU state [B, slots] int32 (stamps held
         as uint32 bits), updated in place with pos2slot / kpos2slot; now is
-        this step's stamp (see cache_commit)."""
+        this step's stamp (see cache_commit), an int or a one-element int32
+        device tensor read when the kernels run (for graph capture)."""
         i, a, h = self.desc.idx, self.desc.attn, self.desc.hot
         B, L, H, D = i.batch, i.max_ctx, i.n_heads, i.head_dim
         _need(q_idx, torch.int8, "q_idx", (B, H, D)), _need(w_idx, torch.int8, "w_idx", (B, H))
@@ -396,7 +398,13 @@ class DecodeStep:
         io.q_attn_dev = q_attn.data_ptr()
         io.out_dev, io.lse_dev = self.out.data_ptr(), self.lse.data_ptr()
         c = self.desc.commit
-        c.now = int(now) & 0xFFFFFFFF
+        if isinstance(now, torch.Tensor):
+            _need(now, torch.int32, "now", (1,))
+            if not now.is_cuda:
+                raise ValueError("a tensor now must be device memory")
+            c.now, io.now_dev = 0, now.data_ptr()
+        else:
+            c.now = int(now) & 0xFFFFFFFF
         if c.hot:
             S = h.hot_slots
             _need(slot2pos, torch.int32, "slot2pos", (B, S)), _need(stamp, torch.int32, "stamp",

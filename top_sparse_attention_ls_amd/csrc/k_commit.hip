@@ -66,8 +66,8 @@ template <int MODE, int EPT>
 __global__ __launch_bounds__(kCommitThreads) void k_cache_commit(
     const int32_t* __restrict__ entries, int n, int32_t* __restrict__ pos2slot,
     int32_t* __restrict__ slot2pos, uint32_t* __restrict__ stamp, int S, int max_ctx,
-    uint32_t now, int32_t* __restrict__ out, int32_t* __restrict__ rows,
-    int32_t* __restrict__ n_ins) {
+    uint32_t now_arg, const uint32_t* __restrict__ now_dev, int32_t* __restrict__ out,
+    int32_t* __restrict__ rows, int32_t* __restrict__ n_ins) {
   __shared__ uint32_t key[kCommitMaxSlots];        // stamps, then the victim list
   __shared__ uint32_t hitbits[kCommitMaxSlots / 32];
   __shared__ uint32_t hist[kDigitBins];
@@ -76,6 +76,8 @@ __global__ __launch_bounds__(kCommitThreads) void k_cache_commit(
   __shared__ uint32_t sh_lo[kCommitThreads / kWave], sh_hi[kCommitThreads / kWave];
 
   const int b = blockIdx.x, tid = threadIdx.x;
+  // the step's stamp: the argument, or a device counter (graph replays)
+  const uint32_t now = now_dev ? *now_dev : now_arg;
   const int32_t* eb = entries + (size_t)b * n;
   int32_t* p2s = pos2slot + (size_t)b * max_ctx;
   int32_t* s2p = slot2pos + (size_t)b * S;
@@ -294,11 +296,11 @@ __global__ __launch_bounds__(kCommitThreads) void k_cache_commit(
 
 hipError_t launch_cache_commit(int mode, const int32_t* entries, int n, int32_t* pos2slot,
                                int32_t* slot2pos, uint32_t* stamp, int S, int B, int max_ctx,
-                               uint32_t now, int32_t* out, int32_t* rows, int32_t* n_ins,
-                               hipStream_t st) {
+                               uint32_t now, const uint32_t* now_dev, int32_t* out,
+                               int32_t* rows, int32_t* n_ins, hipStream_t st) {
 #define LS_COMMIT_E(M, E)                                                                      \
   hipLaunchKernelGGL((k_cache_commit<M, E>), dim3(B), dim3(kCommitThreads), 0, st, entries, n, \
-                     pos2slot, slot2pos, stamp, S, max_ctx, now, out, rows, n_ins)
+                     pos2slot, slot2pos, stamp, S, max_ctx, now, now_dev, out, rows, n_ins)
 #define LS_COMMIT(M)                                                                          \
   do {                                                                                        \
     if (n <= kCommitThreads) LS_COMMIT_E(M, 1);                                               \

@@ -490,7 +490,8 @@ int ls_cache_commit(int32_t batch, int32_t max_ctx, int32_t n_slots, int32_t n, 
   LS_NONNULL(stamp_dev);
   LS_NONNULL(dst_dev);
   LS_HIP(ls::launch_cache_commit(ls::kCommitDst, entries_dev, n, pos2slot_dev, slot2pos_dev,
-                                 stamp_dev, n_slots, batch, max_ctx, now, dst_dev, nullptr,
+                                 stamp_dev, n_slots, batch, max_ctx, now, nullptr, dst_dev,
+                                 nullptr,
                                  n_inserted_dev, (hipStream_t)stream),
          "cache commit launch");
   return LS_OK;
@@ -688,7 +689,8 @@ int ls_decode_step(const ls_step_desc* desc, const ls_step_io* io, void* ws_dev,
     // the refinement reads by these codes and fills the rows
     LS_HIP(ls::launch_cache_commit(ls::kCommitKey, io->cand_dev, id->n_cand, io->kpos2slot_dev,
                                    io->kslot2pos_dev, io->kstamp_dev, id->key_slots, id->batch,
-                                   id->max_ctx, cm->now, rws.kcode, nullptr, io->n_key_miss_dev,
+                                   id->max_ctx, cm->now, io->now_dev, rws.kcode, nullptr,
+                                   io->n_key_miss_dev,
                                    st),
            "key-cache commit launch");
     k8.code = rws.kcode;
@@ -707,7 +709,8 @@ int ls_decode_step(const ls_step_desc* desc, const ls_step_io* io, void* ws_dev,
     // writes the rows there
     LS_HIP(ls::launch_cache_commit(ls::kCommitHot, io->topk_dev, id->topk, io->pos2slot_dev,
                                    io->slot2pos_dev, io->stamp_dev, desc->hot.hot_slots,
-                                   id->batch, id->max_ctx, cm->now, rws.miss_dst, io->rows_dev,
+                                   id->batch, id->max_ctx, cm->now, io->now_dev, rws.miss_dst,
+                                   io->rows_dev,
                                    nullptr, st),
            "hot-buffer commit launch");
   if (desc->use_hot)

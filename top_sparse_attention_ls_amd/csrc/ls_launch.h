@@ -84,8 +84,8 @@ constexpr int kCommitMaxSlots = 16384;
 constexpr int kCommitMaxEntries = 16384;
 hipError_t launch_cache_commit(int mode, const int32_t* entries, int n, int32_t* pos2slot,
                                int32_t* slot2pos, uint32_t* stamp, int S, int B, int max_ctx,
-                               uint32_t now, int32_t* out, int32_t* rows, int32_t* n_ins,
-                               hipStream_t st);
+                               uint32_t now, const uint32_t* now_dev, int32_t* out,
+                               int32_t* rows, int32_t* n_ins, hipStream_t st);
 hipError_t launch_append_token(const int8_t* new_k8, const void* new_kv, int8_t* k8,
                                uint8_t* kc, void* pool, int32_t* ctx_len, int B, int D,
                                int max_ctx, int row_elems, hipStream_t st);

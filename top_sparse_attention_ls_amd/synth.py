@@ -97,6 +97,12 @@ WORKLOADS = {
                                       idx_heads=64, idx_dim=128, n_cand=8192, topk=2048,
                                       planted=1310, hot_slots=4096, keys_on_host=True,
                                       key_slots=16384, serve_drift=0.1),
+    # the serving loop over a stack of four layers (each its own state)
+    "decode-128k-b32-serve-4l": Workload("decode-128k-b32-serve-4l", 1001, batch=32,
+                                         ctx=131072, idx_heads=64, idx_dim=128, n_cand=8192,
+                                         topk=2048, planted=1310, hot_slots=4096,
+                                         keys_on_host=True, key_slots=16384, serve_drift=0.1,
+                                         layers=4),
     # decode near 1M context, 4 requests, planted tokens in 8 bursts of 512
     "decode-950k-b4": Workload("decode-950k-b4", 1003, batch=4, ctx=950000, idx_heads=64,
                                idx_dim=128, n_cand=16384, topk=2048, bursts=(8, 512),
