@@ -637,6 +637,24 @@ def main():
             "hbm_saved_bytes": full_keys - cache,
             "hbm_saved_per_request": (full_keys - cache) // wl.batch,
         }
+    if wl.hot_slots:
+        # the compute-plus-I/O model of the hot-buffer analysis: the measured
+        # step without its KV miss I/O, plus the missed rows' bytes over a
+        # link of each modelled bandwidth, the two not overlapping
+        stage = dict(zip(STAGES, stage_ms))
+        compute_us = (sum(stage_ms) - stage["miss_gather"]) * 1000
+        miss_bytes = sum(n_miss) * wl.qk_dim * 2
+        result["io_model"] = {
+            "compute_us_without_kv_io": round(compute_us, 1),
+            "kv_miss_bytes": miss_bytes,
+            "modeled_us": {str(bw): round(compute_us + miss_bytes / (bw * 1e3), 1)
+                           for bw in (64, 225, 900)},
+            "measured_us": round(ms_per_step * 1000, 1),
+            "measured_gather_us": round(stage["miss_gather"] * 1000, 1),
+            "gather_GBs": round(miss_bytes / (stage["miss_gather"] * 1e-3) / 1e9, 1),
+            "link": "pinned host (PCIe)" if wl.pool_on_host else "HBM",
+            "note": "stage times from the instrumented run (an event between stages)",
+        }
     coarse_ops = 2 * wl.batch * wl.ctx * wl.idx_heads * wl.idx_dim
     attn_flops = 2 * wl.batch * wl.q_heads * wl.topk * (wl.qk_dim + wl.v_dim)
     attn_ms = stage_ms[STAGES.index("attention")]
