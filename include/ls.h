@@ -306,7 +306,7 @@ int ls_decode_step(const ls_step_desc *desc, const ls_step_io *io, void *ws_dev,
 /* One least-recently-used commit per request into a cache of n_slots rows
  * (the hot KV buffer or the indexer-key cache; the step runs the same
  * commit when ls_commit_desc asks for it).  entries [B, n]: the positions
- * the step used, ascending, -1 padded.  Tables, updated in place:
+ * the step used, ascending and distinct, -1 padded.  Tables, updated in place:
  * pos2slot [B, max_ctx] (slot of a token or -1), slot2pos [B, n_slots]
  * (token of a slot or -1), stamp [B, n_slots] (step that last used the
  * slot, 0 = never).

@@ -404,6 +404,9 @@ class DecodeStep:
                 raise ValueError("a tensor now must be device memory")
             c.now, io.now_dev = 0, now.data_ptr()
         else:
+            if (c.hot or c.keys) and not 0 < int(now) < 0xFFFFFFFF:
+                raise ValueError("a committing step needs a stamp now in [1, 2^32 - 2] "
+                                 "(0 marks a slot never used)")
             c.now = int(now) & 0xFFFFFFFF
         if c.hot:
             S = h.hot_slots
