@@ -5,6 +5,7 @@ import ctypes
 import subprocess
 
 import pytest
+import torch
 
 import top_sparse_attention_ls_amd as ls
 
@@ -274,3 +275,26 @@ def test_step_commit_validated(lib, desc, io_kw, needle):
     rc = lib.ls_decode_step(ctypes.byref(d), ctypes.byref(fake_io(**io_kw)), FAKE, 1 << 40, None)
     assert rc == ls.LS_E_ARG
     assert needle in lib.ls_last_error()
+
+
+def test_binding_checks_key_cache_and_append_arguments():
+    # argument checks of the binding run before anything touches a device
+    q = torch.zeros((2, 4, 64), dtype=torch.int8)
+    w = torch.zeros((2, 4), dtype=torch.int8)
+    k8 = torch.zeros((2, 100, 64), dtype=torch.int8)
+    cand = torch.zeros((2, 16), dtype=torch.int32)
+    cl = torch.zeros((2,), dtype=torch.int32)
+    with pytest.raises(ValueError, match="go together"):
+        ls.refine_topk(q, w, k8, cand, cl, 8, kpos2slot=torch.zeros((2, 100), dtype=torch.int32))
+    with pytest.raises(ValueError, match="kpos2slot"):
+        ls.refine_topk(q, w, k8, cand, cl, 8, kpos2slot=torch.zeros((2, 99), dtype=torch.int32),
+                       kcache=torch.zeros((2, 10, 64), dtype=torch.int8))
+    with pytest.raises(ValueError, match="device memory"):
+        ls.refine_topk(q, w, k8, cand, cl, 8, kpos2slot=torch.zeros((2, 100), dtype=torch.int32),
+                       kcache=torch.zeros((2, 10, 64), dtype=torch.int8))
+    kc = torch.zeros((2, 100, 32), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="go together"):
+        ls.append_token(torch.zeros((2, 64), dtype=torch.int8), k8, kc, cl,
+                        new_kv=torch.zeros((2, 576), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="kc"):
+        ls.append_token(torch.zeros((2, 64), dtype=torch.int8), k8, kc[:, :, :16].contiguous(), cl)

@@ -11,7 +11,11 @@ Stages (see include/ls.h for the exact contracts):
   refine_topk          exact int8 scores of the candidates -> top-k
   hot_gather           resolve against the hot buffer, copy misses from the pool
   sparse_attn_decode   attention over the selected rows
-  DecodeStep           the whole step, one call
+  DecodeStep           the whole step, one call (optionally with the original
+                       keys on the host behind a key cache, and with both
+                       caches committing)
+  cache_commit         least-recently-used commit of one step's entries
+  append_token         the new token's keys and KV row at ctx_len, ctx_len += 1
   prefill_index_topk / prefill_stream_layers   prefill-chunk indexer
 """
 from __future__ import annotations
