@@ -39,6 +39,11 @@ namespace ls {
 //   kCommitKey: code[b, e] = the slot of a hit, -(2 + victim) for an
 //               inserted miss (the refinement copies the row it reads into
 //               that slot), -1 otherwise; n_ins[b] = the number of misses.
+//               On entry code[] holds each entry's slot-table value
+//               (k_slot_lookup), so the random table reads spread over the
+//               grid instead of one workgroup per request.
+// For kCommitHot the entries' table values come from rows[] as the top-k
+// resolved them (slot tables hold values in [-1, n_slots)).
 constexpr int kCommitThreads = 1024;
 constexpr int kDigitBins = 2048;
 
@@ -98,7 +103,18 @@ __global__ __launch_bounds__(kCommitThreads) void k_cache_commit(
     for (int i = 0; i < EPT; i++) {
       const bool ok = e0 + i < n && t[i] >= 0 && t[i] < max_ctx;
       t[i] = ok ? t[i] : -1;
-      sl[i] = p2s[ok ? t[i] : 0];
+      // the entry's table value: looked up here (one workgroup's random
+      // reads), or already gathered across the grid and read coalesced: for
+      // the hot buffer the top-k's rows (a slot, or hot_slots + rank for a
+      // miss), for the key cache the lookup pass's output in code[]
+      if (MODE == kCommitHot) {
+        const int32_t r = rows[(size_t)b * n + min(e0 + i, n - 1)];
+        sl[i] = r < S ? r : -1;
+      } else if (MODE == kCommitKey) {
+        sl[i] = out[(size_t)b * n + min(e0 + i, n - 1)];
+      } else {
+        sl[i] = p2s[ok ? t[i] : 0];
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -294,6 +310,20 @@ __global__ __launch_bounds__(kCommitThreads) void k_cache_commit(
   if (tid == 0 && n_ins) n_ins[b] = (int32_t)(MODE == kCommitKey ? n_m : n_use);
 }
 
+// out[b, e] = pos2slot[b, entries[b, e]] (-1 for padding): the table reads
+// of the key-cache commit, spread over the grid.
+__global__ __launch_bounds__(256) void k_slot_lookup(const int32_t* __restrict__ entries, int n,
+                                                     const int32_t* __restrict__ pos2slot,
+                                                     int max_ctx, int32_t* __restrict__ out) {
+  const int b = blockIdx.y;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  const int32_t t = entries[(size_t)b * n + e];
+  const bool ok = t >= 0 && t < max_ctx;
+  const int32_t s = pos2slot[(size_t)b * max_ctx + (ok ? t : 0)];
+  out[(size_t)b * n + e] = ok ? s : -1;
+}
+
 hipError_t launch_cache_commit(int mode, const int32_t* entries, int n, int32_t* pos2slot,
                                int32_t* slot2pos, uint32_t* stamp, int S, int B, int max_ctx,
                                uint32_t now, const uint32_t* now_dev, int32_t* out,
@@ -309,6 +339,12 @@ hipError_t launch_cache_commit(int mode, const int32_t* entries, int n, int32_t*
     else if (n <= 8 * kCommitThreads) LS_COMMIT_E(M, 8);                                      \
     else LS_COMMIT_E(M, 16);                                                                  \
   } while (0)
+  if (mode == kCommitKey) {
+    hipLaunchKernelGGL(k_slot_lookup, dim3((n + 255) / 256, B), dim3(256), 0, st, entries, n,
+                       pos2slot, max_ctx, out);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (mode == kCommitHot) LS_COMMIT(kCommitHot);
   else if (mode == kCommitKey) LS_COMMIT(kCommitKey);
   else LS_COMMIT(kCommitDst);
