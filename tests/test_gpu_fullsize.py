@@ -19,7 +19,7 @@ import torch
 
 from oracle import oracle as orc
 from top_sparse_attention_ls_amd import synth
-from tests.gpu_common import np_, bits, assert_attention_close
+from tests.gpu_common import np_, bits, assert_attention_close, oracle_cand, oracle_topk
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -117,3 +117,84 @@ def test_fullsize_decode_16k_b192_pinned_host_pool(ls):
 @pytest.mark.timeout(300)
 def test_fullsize_decode_950k_b4(ls):
     run_full(ls, "decode-950k-b4", sample=[3])
+
+
+@pytest.mark.timeout(300)
+def test_fullsize_serving_steps_keep_the_caches_coherent(ls):
+    # the serving workload at full size, as the benchmark runs it (both caches
+    # committing from empty, one token appended per step): after each step
+    # the tables are coherent, every cached row holds its token's bytes, the
+    # stamps are this step's or older, and request 5's candidates, selection
+    # and commits equal the oracle's, stepped alongside from the generator's
+    # inputs
+    wl = synth.WORKLOADS["decode-128k-b32-serve"]
+    B, L, D, C, K, S, SK, row = (wl.batch, wl.ctx, wl.idx_dim, wl.n_cand, wl.topk, wl.hot_slots,
+                                 wl.key_slots, wl.qk_dim)
+    print("[fullsize] serve: building inputs", flush=True)
+    inp = synth.indexer_inputs(wl, DEV)
+    keys = inp["keys"]
+    kc = ls.pack_coarse(keys)
+    k8 = keys.to("cpu").pin_memory()
+    pool = synth.kv_pool(wl, DEV, gen_device=DEV)
+    qa = synth.attention_query(wl, DEV)
+    ctx_len = torch.full((B,), L - 16, dtype=torch.int32, device=DEV)
+    hot = torch.zeros((B, S + K, row), dtype=torch.bfloat16, device=DEV)
+    p2s = torch.full((B, L), -1, dtype=torch.int32, device=DEV)
+    s2p = torch.full((B, S), -1, dtype=torch.int32, device=DEV)
+    st = torch.zeros((B, S), dtype=torch.int32, device=DEV)
+    kp2s = torch.full((B, L), -1, dtype=torch.int32, device=DEV)
+    ks2p = torch.full((B, SK), -1, dtype=torch.int32, device=DEV)
+    kst = torch.zeros((B, SK), dtype=torch.int32, device=DEV)
+    kcache = torch.zeros((B, SK, D), dtype=torch.int8, device=DEV)
+    step = ls.DecodeStep(batch=B, max_ctx=L, idx_heads=wl.idx_heads, idx_dim=D, n_cand=C,
+                         topk=K, q_heads=wl.q_heads, qk_dim=wl.qk_dim, v_dim=wl.v_dim,
+                         scale=wl.scale, hot_slots=S, keys_on_host=True, key_slots=SK,
+                         commit_hot=True, commit_keys=True, device=DEV)
+    g = synth.generator(wl.seed, 100, 0, DEV)
+    q = inp["q"]
+    r, ctx_r = 5, L - 16
+    o_hot = [np_(p2s[r]).copy(), np_(s2p[r]).copy(), np_(st[r]).view(np.uint32).copy()]
+    o_key = [np_(kp2s[r]).copy(), np_(ks2p[r]).copy(), np_(kst[r]).view(np.uint32).copy()]
+    for k in range(3):
+        now = k + 1
+        print("[fullsize] serve: step %d" % k, flush=True)
+        step.run(q_idx=q, w_idx=inp["w"], kc=kc, k8=k8, ctx_len=ctx_len, q_attn=qa,
+                 pos2slot=p2s, hot_kv=hot, pool_kv=pool, kpos2slot=kp2s, kcache=kcache,
+                 slot2pos=s2p, stamp=st, kslot2pos=ks2p, kstamp=kst, now=now)
+        torch.cuda.synchronize()
+        # the oracle's step of request r: candidates, selection, both commits
+        qr, wr, kr = np_(q[r]), np_(inp["w"][r]), np_(keys[r])
+        e_cand = oracle_cand(qr, wr, kr, ctx_r, C)
+        e_tk, _ = oracle_topk(qr, wr, kr, e_cand, K)
+        assert np_(step.cand)[r].tolist() == e_cand.tolist(), (k, "cand")
+        assert np_(step.topk)[r].tolist() == e_tk.tolist(), (k, "topk")
+        e_dst, _ = orc.cache_commit(e_tk, S, now, *o_hot)
+        orc.cache_commit(e_cand, SK, now, *o_key)
+        assert np.array_equal(np_(p2s[r]), o_hot[0]) and np.array_equal(np_(s2p[r]), o_hot[1])
+        assert np.array_equal(np_(st[r]).view(np.uint32), o_hot[2])
+        assert np.array_equal(np_(kp2s[r]), o_key[0]) and np.array_equal(np_(ks2p[r]), o_key[1])
+        assert np.array_equal(np_(kst[r]).view(np.uint32), o_key[2])
+        sel = e_tk
+        got_rows = np_(step.rows)[r]
+        for i in range(len(sel)):
+            if sel[i] >= 0 and e_dst[i] >= 0:
+                assert got_rows[i] == e_dst[i], (k, i)
+        # every request: coherent tables, cached rows equal to their tokens'
+        for b in range(B):
+            for tab, s2p_, cache, src in ((p2s, s2p, hot, pool), (kp2s, ks2p, kcache, keys)):
+                sp = s2p_[b]
+                occ = torch.nonzero(sp >= 0).flatten()
+                pos = sp[occ].long()
+                assert torch.equal(tab[b, pos], occ.to(torch.int32)), (k, b, "table")
+                assert int((tab[b] >= 0).sum()) == occ.numel(), (k, b, "extra entries")
+                assert torch.equal(cache[b, occ], src[b, pos]), (k, b, "cached rows")
+        assert int(st.max()) == now and int(kst.max()) == now
+        new_k = synth.int8_normal((B, D), 24.0, g, DEV)
+        new_kv = synth.bf16_normal((B, row), g, DEV)
+        pos_new = ctx_len.long().clone()
+        ls.append_token(new_k, k8, kc, ctx_len, new_kv=new_kv, pool=pool)
+        keys[torch.arange(B, device=DEV), pos_new] = new_k
+        ctx_r += 1
+        q = synth.drift_query(q, wl.serve_drift, g, DEV)
+    torch.cuda.synchronize()
+    assert torch.equal(k8, keys.cpu())
