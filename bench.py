@@ -293,6 +293,24 @@ def run_prefill(ls, synth, wl, args):
     print(json.dumps(result), flush=True)
 
 
+def micro_batch(ls, st, b0, Bm, wl, dev):
+    """Requests [b0, b0 + Bm) of a layer's serving state: views of every
+    per-request tensor (the batch is the leading dimension, so each view is
+    contiguous) and a step of their own."""
+    sl = slice(b0, b0 + Bm)
+    y = {k: v[sl] for k, v in st.items() if k not in ("qs", "new_k", "new_kv")}
+    y["qs"] = [q[sl] for q in st["qs"]]
+    y["new_k"] = [t[sl] for t in st["new_k"]]
+    y["new_kv"] = [t[sl] for t in st["new_kv"]]
+    y["step"] = ls.DecodeStep(batch=Bm, max_ctx=wl.ctx, idx_heads=wl.idx_heads,
+                              idx_dim=wl.idx_dim, n_cand=wl.n_cand, topk=wl.topk,
+                              q_heads=wl.q_heads, qk_dim=wl.qk_dim, v_dim=wl.v_dim,
+                              scale=wl.scale, hot_slots=wl.hot_slots, keys_on_host=True,
+                              key_slots=wl.key_slots, commit_hot=True, commit_keys=True,
+                              device=dev)
+    return y
+
+
 def run_serve(ls, synth, wl, args):
     """Decode steps in a row as in serving, over wl.layers layers (default
     one): per layer, the original keys in pinned host memory behind the
@@ -311,6 +329,12 @@ def run_serve(ls, synth, wl, args):
     B, L, H, D, C, K = wl.batch, wl.ctx, wl.idx_heads, wl.idx_dim, wl.n_cand, wl.topk
     S, SK, row = wl.hot_slots, wl.key_slots, wl.qk_dim
     n_layers = max(wl.layers, 1)
+    mb = args.microbatches or wl.serve_microbatches
+    if B % mb:
+        raise SystemExit("the batch of %d does not split into %d micro-batches" % (B, mb))
+    if mb > 1 and args.graph:
+        raise SystemExit("--graph replays one stream: use it with one micro-batch")
+    Bm = B // mb
     ring, n_stat = 32, 8
     total = args.warmup + args.steps + n_stat + 2 * ring
     print("[bench] building serving state for %s (%d layers)" % (wl.name, n_layers),
@@ -339,23 +363,40 @@ def run_serve(ls, synth, wl, args):
             kp2s=torch.full((B, L), -1, dtype=torch.int32, device=dev),
             ks2p=torch.full((B, SK), -1, dtype=torch.int32, device=dev),
             kst=torch.zeros((B, SK), dtype=torch.int32, device=dev),
-            kcache=torch.zeros((B, SK, D), dtype=torch.int8, device=dev),
-            step=ls.DecodeStep(batch=B, max_ctx=L, idx_heads=H, idx_dim=D, n_cand=C, topk=K,
-                               q_heads=wl.q_heads, qk_dim=wl.qk_dim, v_dim=wl.v_dim,
-                               scale=wl.scale, hot_slots=S, keys_on_host=True, key_slots=SK,
-                               commit_hot=True, commit_keys=True, device=dev))
+            kcache=torch.zeros((B, SK, D), dtype=torch.int8, device=dev))
+        # micro-batches: contiguous request ranges (views), each its own step
+        st["mb"] = [micro_batch(ls, st, m * Bm, Bm, wl, dev) for m in range(mb)]
         layers.append(st)
     now = torch.ones((1,), dtype=torch.int32, device=dev)
+    side_streams = [torch.cuda.Stream() for _ in range(mb - 1)]
+    sel_ev = [[torch.cuda.Event() for _ in range(mb)] for _ in layers]
 
     def token_step(i):
-        for x in layers:
-            x["step"].run(q_idx=x["qs"][i % ring], w_idx=x["w"], kc=x["kc"], k8=x["k8"],
-                          ctx_len=x["ctx_len"], q_attn=x["q_attn"], pos2slot=x["p2s"],
-                          hot_kv=x["hot"], pool_kv=x["pool"], kpos2slot=x["kp2s"],
-                          kcache=x["kcache"], slot2pos=x["s2p"], stamp=x["st"],
-                          kslot2pos=x["ks2p"], kstamp=x["kst"], now=now)
-            ls.append_token(x["new_k"][i % 4], x["k8"], x["kc"], x["ctx_len"],
-                            new_kv=x["new_kv"][i % 4], pool=x["pool"])
+        # micro-batch m runs on stream m and starts each layer once micro-batch
+        # m-1 has selected its candidates, so that one's key reads over PCIe
+        # overlap the next one's coarse pass in HBM
+        main = torch.cuda.current_stream()
+        streams = [main] + side_streams
+        for strm in side_streams:
+            strm.wait_stream(main)
+        for li, x in enumerate(layers):
+            for m, y in enumerate(x["mb"]):
+                with torch.cuda.stream(streams[m]):
+                    if m > 0:
+                        streams[m].wait_event(sel_ev[li][m - 1])
+                    ev = None
+                    if m < mb - 1:
+                        ev = [None] * ls.STEP_EVENTS
+                        ev[2] = sel_ev[li][m]
+                    y["step"].run(q_idx=y["qs"][i % ring], w_idx=y["w"], kc=y["kc"], k8=y["k8"],
+                                  ctx_len=y["ctx_len"], q_attn=y["q_attn"], pos2slot=y["p2s"],
+                                  hot_kv=y["hot"], pool_kv=y["pool"], kpos2slot=y["kp2s"],
+                                  kcache=y["kcache"], slot2pos=y["s2p"], stamp=y["st"],
+                                  kslot2pos=y["ks2p"], kstamp=y["kst"], now=now, events=ev)
+                    ls.append_token(y["new_k"][i % 4], y["k8"], y["kc"], y["ctx_len"],
+                                    new_kv=y["new_kv"][i % 4], pool=y["pool"])
+        for strm in side_streams:
+            main.wait_stream(strm)
         now.add_(1)
 
     counter = [0]
@@ -400,8 +441,10 @@ def run_serve(ls, synth, wl, args):
     for _ in range(n_stat):
         one()
         torch.cuda.synchronize()
-        hot_miss.append(sum(int(x["step"].n_miss.sum()) for x in layers) / n_layers)
-        key_miss.append(sum(int(x["step"].n_key_miss.sum()) for x in layers) / n_layers)
+        hot_miss.append(sum(int(y["step"].n_miss.sum()) for x in layers for y in x["mb"])
+                        / n_layers)
+        key_miss.append(sum(int(y["step"].n_key_miss.sum()) for x in layers for y in x["mb"])
+                        / n_layers)
     km = sum(key_miss) / n_stat
     result = {
         "metric": "sparse-decode layer-steps/s, serving loop (commits + append)",
@@ -420,6 +463,7 @@ def run_serve(ls, synth, wl, args):
                    "n_cand": C, "topk": K, "hot_slots": S, "key_slots": SK, "layers": n_layers,
                    "query_drift": wl.serve_drift, "keys": "pinned-host", "pool": "hbm",
                    "launch": "hip-graph per token step" if args.graph else "eager",
+                   "micro_batches": mb,
                    "parallelism": "single-gpu"},
         "token_steps_per_s": round(1000.0 / (ms * n_layers), 2),
         "emergent": {
@@ -442,6 +486,9 @@ def main():
     ap.add_argument("--replicas", type=int, default=2)
     ap.add_argument("--cpu-sample", type=int, default=4,
                     help="requests the CPU oracle baseline runs (0 = skip)")
+    ap.add_argument("--microbatches", type=int, default=0,
+                    help="serving workloads: split the batch into this many micro-batches on "
+                         "their own streams (0: the workload's default)")
     ap.add_argument("--graph", action="store_true",
                     help="serving workloads: replay each token step from a HIP graph")
     ap.add_argument("--copy-calib", type=int, default=0,

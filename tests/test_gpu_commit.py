@@ -209,3 +209,79 @@ def test_decode_steps_with_commits_and_append(ls):
         assert torch.equal(k8_host, keys)
     # the drifting query keeps part of its selection from step to step
     assert hits_seen > 0
+
+
+def serve_state(ls, wl, B, dev):
+    L, D, S, SK, K, row = wl.ctx, wl.idx_dim, wl.hot_slots, wl.key_slots, wl.topk, wl.qk_dim
+    inp = synth.indexer_inputs(wl, dev)
+    g = torch.Generator(device=dev).manual_seed(3)
+    return dict(
+        q=inp["q"], w=inp["w"], kc=ls.pack_coarse(inp["keys"]), k8=inp["keys"].cpu().pin_memory(),
+        pool=synth.kv_pool(wl, dev), q_attn=synth.attention_query(wl, dev),
+        ctx_len=torch.tensor([L - 9, L // 2, 1000, L - 1][:B], dtype=torch.int32, device=dev),
+        new_k=synth.int8_normal((B, D), 24.0, g, dev), new_kv=synth.bf16_normal((B, row), g, dev),
+        hot=torch.zeros((B, S + K, row), dtype=torch.bfloat16, device=dev),
+        p2s=torch.full((B, L), -1, dtype=torch.int32, device=dev),
+        s2p=torch.full((B, S), -1, dtype=torch.int32, device=dev),
+        st=torch.zeros((B, S), dtype=torch.int32, device=dev),
+        kp2s=torch.full((B, L), -1, dtype=torch.int32, device=dev),
+        ks2p=torch.full((B, SK), -1, dtype=torch.int32, device=dev),
+        kst=torch.zeros((B, SK), dtype=torch.int32, device=dev),
+        kcache=torch.zeros((B, SK, D), dtype=torch.int8, device=dev))
+
+
+def test_micro_batches_on_two_streams_match_one_batch(ls):
+    # the serving loop's overlap pattern: the batch split into two request
+    # ranges (views into the same state, the pinned keys included), each with
+    # its own step on its own stream, the second starting each step once the
+    # first has selected its candidates; every table, cache row, output and
+    # appended token must equal one step over the whole batch
+    wl = dataclasses.replace(synth.WORKLOADS["decode-128k-b32"], name="mb", batch=4, ctx=6000,
+                             n_cand=1024, topk=256, planted=60, hot_slots=400, key_slots=1500)
+    B, Bm = 4, 2
+    one, two = serve_state(ls, wl, B, DEV), serve_state(ls, wl, B, DEV)
+
+    def make_step(batch):
+        return ls.DecodeStep(batch=batch, max_ctx=wl.ctx, idx_heads=wl.idx_heads,
+                             idx_dim=wl.idx_dim, n_cand=wl.n_cand, topk=wl.topk,
+                             q_heads=wl.q_heads, qk_dim=wl.qk_dim, v_dim=wl.v_dim, scale=wl.scale,
+                             hot_slots=wl.hot_slots, keys_on_host=True, key_slots=wl.key_slots,
+                             commit_hot=True, commit_keys=True, n_splits=4)
+
+    def run(step, x, now, events=None):
+        step.run(q_idx=x["q"], w_idx=x["w"], kc=x["kc"], k8=x["k8"], ctx_len=x["ctx_len"],
+                 q_attn=x["q_attn"], pos2slot=x["p2s"], hot_kv=x["hot"], pool_kv=x["pool"],
+                 kpos2slot=x["kp2s"], kcache=x["kcache"], slot2pos=x["s2p"], stamp=x["st"],
+                 kslot2pos=x["ks2p"], kstamp=x["kst"], now=now, events=events)
+        ls.append_token(x["new_k"], x["k8"], x["kc"], x["ctx_len"], new_kv=x["new_kv"],
+                        pool=x["pool"])
+
+    whole = make_step(B)
+    parts = [make_step(Bm), make_step(Bm)]
+    views = [{k: v[m * Bm:(m + 1) * Bm] for k, v in two.items()} for m in range(2)]
+    side = torch.cuda.Stream()
+    sel = torch.cuda.Event()
+    for k in range(4):
+        now = k + 1
+        run(whole, one, now)
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        ev = [None] * ls.STEP_EVENTS
+        ev[2] = sel
+        run(parts[0], views[0], now, ev)
+        with torch.cuda.stream(side):
+            side.wait_event(sel)
+            run(parts[1], views[1], now)
+        main.wait_stream(side)
+        torch.cuda.synchronize()
+        for name in ("cand", "topk", "topk_score", "rows", "n_miss", "n_key_miss", "lse"):
+            got = torch.cat([getattr(p_, name) for p_ in parts])
+            assert torch.equal(got, getattr(whole, name)), (k, name)
+        got_out = torch.cat([p_.out for p_ in parts])
+        assert torch.equal(got_out.view(torch.int16), whole.out.view(torch.int16)), k
+        for key in ("hot", "p2s", "s2p", "st", "kp2s", "ks2p", "kst", "kcache", "kc", "ctx_len",
+                    "pool", "k8"):
+            a, b_ = one[key], two[key]
+            if a.dtype == torch.bfloat16:
+                a, b_ = a.view(torch.int16), b_.view(torch.int16)
+            assert torch.equal(a, b_), (k, key)

@@ -328,7 +328,11 @@ int resolve_host(const void* p, int on_host, const void** dev_ptr, const char* w
   if (attr.type != hipMemoryTypeHost || attr.devicePointer == nullptr)
     return fail(LS_E_ARG, "%s is declared host-resident but is not device-mapped pinned host memory",
                 what);
-  *dev_ptr = attr.devicePointer;
+  // a pointer inside a pinned allocation (a slice of a larger tensor): the
+  // alias keeps its offset from the host address the attributes report
+  const char* dev = (const char*)attr.devicePointer;
+  if (attr.hostPointer) dev += (const char*)p - (const char*)attr.hostPointer;
+  *dev_ptr = dev;
   return LS_OK;
 }
 

@@ -62,6 +62,7 @@ class Workload:
     # multi-step serving: both caches commit each step, a token is appended,
     # and the indexer query drifts (each element redrawn with this rate)
     serve_drift: float = 0.0
+    serve_microbatches: int = 1      # micro-batches on their own streams in the serving loop
     # prefill only
     n_query: int = 0
     layers: int = 0
