@@ -111,7 +111,9 @@ def test_append_token(ls, host):
     assert np_(cl).tolist() == [1, 18, L]
 
 
-def test_decode_steps_with_commits_and_append(ls):
+@pytest.mark.parametrize("keys_host,pool_host", [(True, False), (False, True)],
+                         ids=["host-keys", "host-pool"])
+def test_decode_steps_with_commits_and_append(ls, keys_host, pool_host):
     wl = dataclasses.replace(synth.WORKLOADS["decode-128k-b32"], name="commit-steps", batch=2,
                              ctx=6000, n_cand=1024, topk=256, planted=60, hot_slots=400,
                              keys_on_host=True, key_slots=1500)
@@ -133,14 +135,16 @@ def test_decode_steps_with_commits_and_append(ls):
     d_tab = to_dev(p2s, s2p, st)
     d_ktab = to_dev(kp2s, ks2p, kst)
     d_kcache = torch.zeros((B, SK, D), dtype=torch.int8, device=DEV)
-    k8_host = keys.pin_memory()
-    pool_d = pool.to(DEV)
+    # the key store and the pool where the case puts them (the names keep
+    # the host-keys case's)
+    k8_host = keys.pin_memory() if keys_host else keys.to(DEV)
+    pool_d = pool.pin_memory() if pool_host else pool.to(DEV)
     kc_d = ls.pack_coarse(keys.to(DEV))
     cl_d = torch.tensor(ctx, dtype=torch.int32, device=DEV)
     step = ls.DecodeStep(batch=B, max_ctx=L, idx_heads=H, idx_dim=D, n_cand=C, topk=K,
                          q_heads=wl.q_heads, qk_dim=wl.qk_dim, v_dim=wl.v_dim, scale=wl.scale,
-                         hot_slots=S, keys_on_host=True, key_slots=SK, commit_hot=True,
-                         commit_keys=True)
+                         hot_slots=S, keys_on_host=keys_host, key_slots=SK, commit_hot=True,
+                         commit_keys=True, pool_on_host=pool_host)
     g = torch.Generator().manual_seed(77)
     hits_seen = 0
     for k in range(5):
@@ -206,7 +210,8 @@ def test_decode_steps_with_commits_and_append(ls):
             pool[b, ctx[b]] = new_kv[b]
             ctx[b] += 1
         assert np_(cl_d).tolist() == ctx
-        assert torch.equal(k8_host, keys)
+        assert torch.equal(k8_host.cpu(), keys)
+        assert torch.equal(pool_d.cpu().view(torch.int16), pool.view(torch.int16))
     # the drifting query keeps part of its selection from step to step
     assert hits_seen > 0
 
