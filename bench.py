@@ -466,6 +466,13 @@ def run_serve(ls, synth, wl, args):
                    "micro_batches": mb,
                    "parallelism": "single-gpu"},
         "token_steps_per_s": round(1000.0 / (ms * n_layers), 2),
+        # per layer: the original keys leave HBM; the key cache, its slot
+        # table and its LRU state (slot -> token, stamp) stay
+        "memory_per_layer": {
+            "hbm_bytes_full_keys": B * L * D,
+            "hbm_bytes_key_cache_and_tables": B * SK * D + B * L * 4 + B * SK * 8,
+            "hbm_saved_bytes": B * L * D - (B * SK * D + B * L * 4 + B * SK * 8),
+        },
         "emergent": {
             "hot_miss_rate": round(sum(hot_miss) / n_stat / (B * K), 4),
             "key_miss_rate": round(km / (B * C), 4),
