@@ -22,9 +22,11 @@ namespace ls {
 
 // One 1024-thread workgroup per request.  The request's stamps sit in LDS
 // (one word per slot) with a bitmap of the slots hit in this step; the
-// victims are found by an exact radix select of the stamps (three digit
-// passes of 11, 11 and 10 bits over a 2048-bin LDS histogram) and the slots
-// of equal stamp are taken in slot order.  Thread t owns the contiguous slot
+// victims' stamp threshold comes from one histogram pass over stamp - min
+// when the eligible stamps span fewer than 2048 values (step numbers usually
+// do), else from an exact radix select (three digit passes of 11, 11 and 10
+// bits over the same 2048-bin LDS histogram); slots of the threshold stamp
+// are taken in slot order.  Thread t owns the contiguous slot
 // range [t*SE, t*SE + SE) and the entry range [t*EPT, t*EPT + EPT), so
 // that prefix sums over threads give slot order and entry order.  Global
 // loads are issued all at once per phase (indices clamped, results selected
