@@ -21,6 +21,16 @@ Prints one JSON line with:
   copy_GBs    a plain 1 GiB device-to-device copy, read + write bytes per
               second (context for the HBM figures)
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
+  io_model    (hot-buffer workloads) the measured step without its KV miss
+              I/O plus the missed rows over 64 / 225 / 900 GB/s, no overlap
+  key_store   (original keys on the host) PCIe bytes per step, HBM saved
+
+Other workloads (--workload): decode-16k-b192 (pinned-host pool),
+decode-950k-b4, decode-128k-b32-hostkeys (keys on the host behind a key
+cache), decode-128k-b32-serve and -serve-4l (the serving loop: both caches
+committing, a token appended per step; --graph replays each token step from
+a HIP graph, --microbatches splits the batch over streams), prefill-4k-128k
+(the layer-streamed prefill indexer, int8 TOPS).
 """
 from __future__ import annotations
 
