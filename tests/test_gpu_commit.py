@@ -114,12 +114,12 @@ def test_append_token(ls, host):
 @pytest.mark.parametrize("keys_host,pool_host", [(True, False), (False, True)],
                          ids=["host-keys", "host-pool"])
 def test_decode_steps_with_commits_and_append(ls, keys_host, pool_host):
-    wl = dataclasses.replace(synth.WORKLOADS["decode-128k-b32"], name="commit-steps", batch=2,
+    wl = dataclasses.replace(synth.WORKLOADS["decode-128k-b32"], name="commit-steps", batch=3,
                              ctx=6000, n_cand=1024, topk=256, planted=60, hot_slots=400,
                              keys_on_host=True, key_slots=1500)
     B, L, H, D, C, K, S, SK = (wl.batch, wl.ctx, wl.idx_heads, wl.idx_dim, wl.n_cand, wl.topk,
                                wl.hot_slots, wl.key_slots)
-    ctx = [L - 10, 4000]
+    ctx = [L - 10, 4000, 0]           # full-ish, partial, empty (grows by the appends)
     inp = synth.indexer_inputs(wl, "cpu", ctx_len=ctx)
     q, w, keys = inp["q"], inp["w"], inp["keys"].clone()
     pool = synth.kv_pool(wl, "cpu")
