@@ -122,9 +122,9 @@ typedef struct {
 
 /* Hot KV buffer of one layer.  Each request owns hot_slots resident rows
  * followed by topk scratch rows that receive the step's misses; a row is
- * row_elems bf16 values (a multiple of 8, with topk * row_elems / 8 below
- * 2^31).  pool_on_host = 1 means the pool is pinned host memory that the
- * device reads over PCIe.                                                   */
+ * row_elems bf16 values (a multiple of 8, with topk * row_elems * 2 bytes
+ * below 2^32, else LS_E_UNSUPPORTED).  pool_on_host = 1 means the pool is
+ * pinned host memory that the device reads over PCIe.                       */
 typedef struct {
     int32_t batch, max_ctx, topk, hot_slots, row_elems, pool_on_host;
 } ls_hot_desc;
@@ -231,7 +231,8 @@ typedef struct {
 
 /* Prefill chunk: n_query query tokens at absolute positions
  * q_pos0 .. q_pos0 + n_query - 1 over a history of max_ctx keys (causal:
- * query i sees keys 0 .. q_pos0 + i).                                      */
+ * query i sees keys 0 .. q_pos0 + i).  max_ctx * head_dim below 2^31 (else
+ * LS_E_UNSUPPORTED).                                                       */
 typedef struct {
     int32_t n_query, max_ctx, q_pos0, n_heads, head_dim, topk;
 } ls_prefill_desc;

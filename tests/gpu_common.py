@@ -1,5 +1,8 @@
 """Shared helpers of the GPU parity tests: oracle-side reference results for
 one request, tensor <-> numpy conversion, tolerances."""
+import concurrent.futures
+import os
+
 import numpy as np
 import torch
 
@@ -50,13 +53,19 @@ def assert_attention_close(out, lse, e_out, e_lse, what=""):
     fin = np.isfinite(e_lse)
     assert np.array_equal(np.isfinite(l_), fin), what + ": -inf pattern of lse differs"
     if fin.any():
-        # 1e-4 absolute, widened only where fp32 itself cannot resolve 1e-4
-        # (|lse| above ~100: 8 ulps of the value)
-        ulp = np.spacing(np.abs(e_lse[fin]).astype(np.float32)).astype(np.float64)
-        tol = np.maximum(LSE_TOL, 8 * ulp)
         err = np.abs(l_[fin] - e_lse[fin])
-        assert (err <= tol).all(), "%s: lse max abs err %.3g (tol %.3g)" % (
-            what, err.max(), tol[np.argmax(err - tol)])
+        assert (err <= LSE_TOL).all(), "%s: lse max abs err %.3g (tol %.3g)" % (
+            what, err.max(), LSE_TOL)
     err_o = np.abs(o - e_out).max() if o.size else 0.0
     assert err_o <= OUT_TOL, "%s: out max abs err %.3g" % (what, err_o)
     return err_o
+
+
+def parallel_map(fn, items, max_workers=16):
+    """fn over items on a pool of host threads (the oracle's C calls release
+    the interpreter lock), in item order; at most 16 threads, the host share
+    of one GPU."""
+    items = list(items)
+    n = max(1, min(max_workers, os.cpu_count() or 1, len(items)))
+    with concurrent.futures.ThreadPoolExecutor(n) as ex:
+        return list(ex.map(fn, items))

@@ -298,3 +298,18 @@ def test_binding_checks_key_cache_and_append_arguments():
                         new_kv=torch.zeros((2, 576), dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="kc"):
         ls.append_token(torch.zeros((2, 64), dtype=torch.int8), k8, kc[:, :, :16].contiguous(), cl)
+
+
+def test_shapes_whose_32_bit_offsets_would_wrap_are_rejected(lib):
+    # the miss gather addresses a request's miss rows, and the prefill
+    # scoring the key history, with 32-bit byte offsets: shapes beyond them
+    # are refused before any launch instead of wrapping
+    h = ls.HotDesc(2, 4096, 1 << 20, 64, 2048, 0)          # 2^20 * 2048 * 2 = 2^32 bytes
+    rc = lib.ls_hot_gather(ctypes.byref(h), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                           None)
+    assert rc == ls.LS_E_UNSUPPORTED and b"2^32" in lib.ls_last_error()
+    p = ls.PrefillDesc(16, (1 << 24) + 8, 0, 64, 128, 64)   # max_ctx * 128 > 2^31
+    rc = lib.ls_prefill_index_topk(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert rc == ls.LS_E_UNSUPPORTED and b"2^31" in lib.ls_last_error()
+    p = ls.PrefillDesc(16, 1 << 23, 0, 64, 128, 64)         # 2^30: accepted by the shape check
+    assert lib.ls_workspace_size(ls.OP_PREFILL, ctypes.byref(p)) > 0

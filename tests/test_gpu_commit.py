@@ -12,15 +12,11 @@ import torch
 
 from oracle import oracle as orc
 from top_sparse_attention_ls_amd import synth
-from tests.gpu_common import np_, bits, oracle_cand, oracle_topk, assert_attention_close
+from tests.gpu_common import np_, bits
+from tests.serve_oracle import ServeShadow, empty_tables
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-
-
-def empty_tables(B, L, S):
-    return (np.full((B, L), -1, np.int32), np.full((B, S), -1, np.int32),
-            np.zeros((B, S), np.uint32))
 
 
 def to_dev(p2s, s2p, st):
@@ -126,11 +122,10 @@ def test_decode_steps_with_commits_and_append(ls, keys_host, pool_host):
     q_attn = synth.attention_query(wl, "cpu")
     row = wl.qk_dim
 
-    # both caches start empty; the oracle's state is kept in numpy
-    hot = np.zeros((B, S + K, row), np.uint16)
+    # both caches start empty; the oracle's state is kept by the shadow
+    shadow = ServeShadow(wl, keys, pool, q_attn, ctx)
     p2s, s2p, st = empty_tables(B, L, S)
     kp2s, ks2p, kst = empty_tables(B, L, SK)
-    kcache = np.zeros((B, SK, D), np.int8)
     d_hot = torch.zeros((B, S + K, row), dtype=torch.bfloat16, device=DEV)
     d_tab = to_dev(p2s, s2p, st)
     d_ktab = to_dev(kp2s, ks2p, kst)
@@ -146,7 +141,6 @@ def test_decode_steps_with_commits_and_append(ls, keys_host, pool_host):
                          hot_slots=S, keys_on_host=keys_host, key_slots=SK, commit_hot=True,
                          commit_keys=True, pool_on_host=pool_host)
     g = torch.Generator().manual_seed(77)
-    hits_seen = 0
     for k in range(5):
         now = k + 1
         if k:
@@ -158,62 +152,18 @@ def test_decode_steps_with_commits_and_append(ls, keys_host, pool_host):
                             slot2pos=d_tab[1], stamp=d_tab[2], kslot2pos=d_ktab[1],
                             kstamp=d_ktab[2], now=now)
         torch.cuda.synchronize()
-        for b in range(B):
-            qb, wb, kb = q[b].numpy(), w[b].numpy(), keys[b].numpy()
-            cand = oracle_cand(qb, wb, kb, ctx[b], C)
-            assert np_(step.cand)[b].tolist() == cand.tolist(), (k, b, "cand")
-            # key cache: the candidates' hits, then the misses moved in
-            n_kmiss = int(((cand >= 0) & (kp2s[b][np.maximum(cand, 0)] < 0)).sum())
-            assert int(np_(step.n_key_miss)[b]) == n_kmiss, (k, b, "key misses")
-            kdst, _ = orc.cache_commit(cand, SK, now, kp2s[b], ks2p[b], kst[b])
-            for i, t in enumerate(cand):
-                if t >= 0 and kdst[i] >= 0:
-                    kcache[b, kdst[i]] = kb[t]
-            tk, ts = oracle_topk(qb, wb, kb, cand, K)
-            assert np_(step.topk)[b].tolist() == tk.tolist(), (k, b, "topk")
-            assert np_(step.topk_score)[b].tolist() == ts.tolist(), (k, b, "scores")
-            # hot buffer: resolve against the state before the commit
-            hot_b = hot[b].copy()
-            r = orc.decode_request(qb, wb, kb, ctx[b], C, K, bits(q_attn[b]), wl.scale,
-                                   pos2slot=p2s[b].copy(), hot_bits=hot_b,
-                                   pool_bits=bits(pool[b]))
-            n_hit = int(((tk >= 0) & (p2s[b][np.maximum(tk, 0)] >= 0)).sum())
-            hits_seen += n_hit
-            dst, _ = orc.cache_commit(tk, S, now, p2s[b], s2p[b], st[b])
-            rows = r["rows"].copy()
-            j = 0
-            for i, t in enumerate(tk):
-                if t < 0:
-                    continue
-                if rows[i] >= S:               # a miss: into its slot, or scratch row S + j
-                    if dst[i] >= 0:
-                        rows[i] = dst[i]
-                        hot[b, dst[i]] = bits(pool[b, t])
-                    else:
-                        hot[b, S + j] = bits(pool[b, t])
-                    j += 1
-            assert np_(step.rows)[b].tolist() == rows.tolist(), (k, b, "rows")
-            assert int(np_(step.n_miss)[b]) == r["n_miss"], (k, b, "n_miss")
-            assert_attention_close(out[b:b + 1], lse[b:b + 1], r["out"][None], r["lse"][None],
-                                   "step %d request %d" % (k, b))
-        check_tables(d_tab, (p2s, s2p, st), "hot step %d" % k)
-        check_tables(d_ktab, (kp2s, ks2p, kst), "keys step %d" % k)
-        assert np.array_equal(bits(d_hot)[:, :S], hot[:, :S]), k
-        assert np.array_equal(np_(d_kcache), kcache), k
+        shadow.step(step, out, lse, q, w, now, "step %d" % k)
+        shadow.check_state(d_hot, d_tab, d_ktab, d_kcache, "step %d" % k)
         # the step's new token, appended on both sides
         new_k = synth.int8_normal((B, D), 24.0, g, "cpu")
         new_kv = torch.randn(B, row, generator=g).to(torch.bfloat16)
         ls.append_token(new_k.to(DEV), k8_host, kc_d, cl_d, new_kv=new_kv.to(DEV), pool=pool_d)
         torch.cuda.synchronize()
-        for b in range(B):
-            keys[b, ctx[b]] = new_k[b]
-            pool[b, ctx[b]] = new_kv[b]
-            ctx[b] += 1
-        assert np_(cl_d).tolist() == ctx
-        assert torch.equal(k8_host.cpu(), keys)
-        assert torch.equal(pool_d.cpu().view(torch.int16), pool.view(torch.int16))
+        shadow.append(new_k, new_kv)
+        shadow.check_stores(k8_host, pool_d, cl_d, "append %d" % k)
+        assert np.array_equal(np_(kc_d), orc.pack_coarse(shadow.keys.numpy())), k
     # the drifting query keeps part of its selection from step to step
-    assert hits_seen > 0
+    assert shadow.hits > 0
 
 
 def serve_state(ls, wl, B, dev):
@@ -235,12 +185,21 @@ def serve_state(ls, wl, B, dev):
         kcache=torch.zeros((B, SK, D), dtype=torch.int8, device=dev))
 
 
+class Joined:
+    """The step outputs of consecutive request ranges, as one batch."""
+
+    def __init__(self, parts):
+        for name in ("cand", "topk", "topk_score", "rows", "n_miss", "n_key_miss"):
+            setattr(self, name, torch.cat([getattr(p_, name) for p_ in parts]))
+
+
 def test_micro_batches_on_two_streams_match_one_batch(ls):
     # the serving loop's overlap pattern: the batch split into two request
     # ranges (views into the same state, the pinned keys included), each with
     # its own step on its own stream, the second starting each step once the
     # first has selected its candidates; every table, cache row, output and
-    # appended token must equal one step over the whole batch
+    # appended token must equal the oracle's serving loop stepped alongside,
+    # and one step over the whole batch
     wl = dataclasses.replace(synth.WORKLOADS["decode-128k-b32"], name="mb", batch=4, ctx=6000,
                              n_cand=1024, topk=256, planted=60, hot_slots=400, key_slots=1500)
     B, Bm = 4, 2
@@ -264,6 +223,8 @@ def test_micro_batches_on_two_streams_match_one_batch(ls):
     whole = make_step(B)
     parts = [make_step(Bm), make_step(Bm)]
     views = [{k: v[m * Bm:(m + 1) * Bm] for k, v in two.items()} for m in range(2)]
+    shadow = ServeShadow(wl, two["k8"], two["pool"], two["q_attn"], np_(two["ctx_len"]).tolist())
+    q_cpu, w_cpu = two["q"].cpu(), two["w"].cpu()
     side = torch.cuda.Stream()
     sel = torch.cuda.Event()
     for k in range(4):
@@ -279,6 +240,15 @@ def test_micro_batches_on_two_streams_match_one_batch(ls):
             run(parts[1], views[1], now)
         main.wait_stream(side)
         torch.cuda.synchronize()
+        # the two ranges against the oracle
+        got_out = torch.cat([p_.out for p_ in parts])
+        got_lse = torch.cat([p_.lse for p_ in parts])
+        shadow.step(Joined(parts), got_out, got_lse, q_cpu, w_cpu, now, "step %d" % k)
+        shadow.check_state(two["hot"], (two["p2s"], two["s2p"], two["st"]),
+                           (two["kp2s"], two["ks2p"], two["kst"]), two["kcache"], "step %d" % k)
+        shadow.append(two["new_k"].cpu(), two["new_kv"].cpu())
+        shadow.check_stores(two["k8"], two["pool"], two["ctx_len"], "append %d" % k)
+        # and against one step over the whole batch
         for name in ("cand", "topk", "topk_score", "rows", "n_miss", "n_key_miss", "lse"):
             got = torch.cat([getattr(p_, name) for p_ in parts])
             assert torch.equal(got, getattr(whole, name)), (k, name)

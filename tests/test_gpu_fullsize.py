@@ -1,6 +1,7 @@
 """GPU parity at the served workloads' full sizes, in the launch configuration
 the benchmark times (one DecodeStep call over the whole batch, automatic
-split count), against the CPU oracle on sampled requests.
+split count), against the CPU oracle on every request (the oracle runs on a
+pool of host threads).
 
 The hot buffer is laid out from the generator's planted positions (all of
 them resident, the remaining slots random), which the HIP path never sees,
@@ -19,7 +20,8 @@ import torch
 
 from oracle import oracle as orc
 from top_sparse_attention_ls_amd import synth
-from tests.gpu_common import np_, bits, assert_attention_close, oracle_cand, oracle_topk
+from tests.gpu_common import (np_, bits, assert_attention_close, oracle_cand, oracle_topk,
+                              parallel_map)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -84,12 +86,16 @@ def run_full(ls, name, sample):
         assert np.array_equal(got, bits(pool[b].index_select(
             0, torch.from_numpy(t[miss]).to(pool.device, torch.int64)))), b
 
-    for b in sample:
-        print("[fullsize] %s: oracle on request %d" % (name, b), flush=True)
+    def oracle_of(b):
         hot_b = bits(hot0[b]).copy()
         r = orc.decode_request(np_(inp["q"][b]), np_(inp["w"][b]), np_(keys[b]), L, wl.n_cand,
                                wl.topk, bits(qa[b]), wl.scale, pos2slot=p2s[b],
                                hot_bits=hot_b, pool_bits=bits(pool[b]))
+        return b, r, hot_b
+
+    print("[fullsize] %s: oracle on %d requests (host threads)" % (name, len(sample)),
+          flush=True)
+    for b, r, hot_b in parallel_map(oracle_of, sample):
         bad = np.where(cand[b] != r["cand"])[0]
         assert len(bad) == 0, (b, "candidates differ at", bad[:8], cand[b][bad[:4]], r["cand"][bad[:4]])
         bad = np.where(topk[b] != r["topk"])[0]
@@ -102,21 +108,24 @@ def run_full(ls, name, sample):
                                "%s request %d" % (name, b))
 
 
+@pytest.mark.timeout(300)
 def test_fullsize_decode_128k_b32(ls):
-    run_full(ls, "decode-128k-b32", sample=[0, 31])
+    run_full(ls, "decode-128k-b32", sample=range(32))
 
 
+@pytest.mark.timeout(300)
 def test_fullsize_decode_128k_b32_host_keys_with_key_cache(ls):
-    run_full(ls, "decode-128k-b32-hostkeys", sample=[17])
+    run_full(ls, "decode-128k-b32-hostkeys", sample=range(32))
 
 
+@pytest.mark.timeout(300)
 def test_fullsize_decode_16k_b192_pinned_host_pool(ls):
-    run_full(ls, "decode-16k-b192", sample=[0, 95, 191])
+    run_full(ls, "decode-16k-b192", sample=range(192))
 
 
 @pytest.mark.timeout(300)
 def test_fullsize_decode_950k_b4(ls):
-    run_full(ls, "decode-950k-b4", sample=[3])
+    run_full(ls, "decode-950k-b4", sample=range(4))
 
 
 @pytest.mark.timeout(300)

@@ -2,13 +2,17 @@
 (no allocation, no memset, no host synchronisation), so it can be captured;
 every replay -- with eager steps and synchronisations in between -- must give
 the eager step's results bit for bit, including the hot-buffer scratch rows
-it writes and the workspace it leaves cleared for the next call."""
+it writes and the workspace it leaves cleared for the next call.  The
+captured layer stack of the serving loop is also stepped against the
+oracle's serving loop after every replay."""
 import dataclasses
 
 import pytest
 import torch
 
 from top_sparse_attention_ls_amd import synth
+from tests.gpu_common import np_
+from tests.serve_oracle import ServeShadow
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -127,6 +131,21 @@ def test_layer_stack_serving_graph_matches_eager(ls):
             out.append(x["k8"].clone())
         return out
 
+    # the oracle's serving loop of each layer, stepped alongside copy 1 (the
+    # graph's copy) from the same inputs
+    shadows = [ServeShadow(wl, x["k8"], x["pool"], x["q_attn"], np_(x["ctx_len"]).tolist())
+               for x in copies[1]]
+
+    def check_with_oracle(now, what):
+        for l_, (x, sh) in enumerate(zip(copies[1], shadows)):
+            s = x["step"]
+            tag = "%s layer %d" % (what, l_)
+            sh.step(s, s.out, s.lse, x["q"].cpu(), x["w"].cpu(), now, tag)
+            sh.check_state(x["hot"], (x["p2s"], x["s2p"], x["st"]),
+                           (x["kp2s"], x["ks2p"], x["kst"]), x["kcache"], tag)
+            sh.append(x["new_k"].cpu(), x["new_kv"].cpu())
+            sh.check_stores(x["k8"], x["pool"], x["ctx_len"], tag)
+
     # capture on copy 1 (the capture itself runs nothing); a first eager step
     # on a side stream warms the allocator the way the capture will see it --
     # run on both copies so that they stay identical
@@ -137,6 +156,7 @@ def test_layer_stack_serving_graph_matches_eager(ls):
         token_step(copies[1], nows[1])
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
+    check_with_oracle(1, "eager step")
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         token_step(copies[1], nows[1])
@@ -146,6 +166,9 @@ def test_layer_stack_serving_graph_matches_eager(ls):
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
+        # every replay equals the oracle's next serving step (stamp k + 2)...
+        check_with_oracle(k + 2, "replay %d" % k)
+        # ...and the same step run eagerly on the identical copy
         a, b = snapshot(copies[0], nows[0]), snapshot(copies[1], nows[1])
         for i, (x, y) in enumerate(zip(a, b)):
             assert torch.equal(x, y), (k, i)

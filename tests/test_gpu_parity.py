@@ -170,6 +170,38 @@ def test_refine_topk_ties(ls):
     run_refine_case(ls, inp, [6000, 6000], 2000, 333)
 
 
+def test_refine_topk_more_than_16384_candidates(ls):
+    # C > 16384: the per-request block selection (k_topk) instead of the
+    # histogram slices; a ragged second request with fewer valid tokens
+    # than C
+    wl = dataclasses.replace(SHRUNK, batch=2, ctx=40000)
+    ctx = [40000, 17000]
+    inp = idx_inputs(wl, ctx_len=ctx)
+    run_refine_case(ls, inp, ctx, 20000, 2048)
+
+
+def test_refine_topk_tie_list_overflow(ls):
+    # more than 8192 candidates in the threshold bucket: the histogram
+    # kernel's tie list cannot hold them and the exact cut runs over every
+    # candidate in global memory.  Request 0: every key equal (all 10000
+    # candidates tie, the lowest 333 positions win).  Request 1: 100 strong
+    # tokens, 9500 of one equal weaker score with the cut inside that group,
+    # weak tokens after
+    wl = dataclasses.replace(SHRUNK, batch=2, ctx=12000)
+    inp = idx_inputs(wl)
+    q, w, keys = inp["q"], inp["w"], inp["keys"]
+    keys[0] = keys[0, :1]
+    pats = ordered_patterns(q[1].numpy(), w[1].numpy(), keys[1])
+    g = torch.Generator().manual_seed(12)
+    perm = torch.randperm(12000, generator=g)
+    lvl = torch.full((12000,), 2, dtype=torch.long)
+    lvl[perm[:100]] = 0
+    lvl[perm[100:9600]] = 1
+    keys[1] = pats[lvl]
+    tk = run_refine_case(ls, inp, [12000, 12000], 10000, 333)
+    assert tk[0].tolist() == list(range(333))
+
+
 def test_refine_topk_pinned_host_keys(ls):
     # the original keys stay in pinned host memory; the refinement reads the
     # candidates' rows over PCIe
@@ -220,6 +252,21 @@ def test_refine_topk_key_cache_d64_all_cached(ls):
     inp = idx_inputs(wl, ctx_len=ctx)
     k8, kp, kcache = cached_key_store(wl, inp, ctx, 1024, 0.0, 1024, True)
     run_refine_case(ls, inp, ctx, 1024, 256, k8=k8, kpos2slot=kp, kcache=kcache)
+
+
+def ordered_patterns(q, w, keys):
+    """Three key rows whose coarse and fine scores both strictly decrease."""
+    cs = orc.index_scores(q, w, keys[:256].numpy(), True)
+    fs = orc.index_scores(q, w, keys[:256].numpy(), False)
+    order = np.lexsort((-cs, -fs))
+    for i in range(1, len(order) - 1):
+        hi, mid = order[0], order[i]
+        if not (fs[hi] > fs[mid] and cs[hi] > cs[mid]):
+            continue
+        for lo in order[::-1]:
+            if fs[mid] > fs[lo] and cs[mid] > cs[lo]:
+                return keys[[int(hi), int(mid), int(lo)]].clone()
+    raise AssertionError("no ordered patterns")
 
 
 def three_level_patterns(q, w, keys, coarse):
@@ -399,24 +446,46 @@ def test_attention_mla_edge_rows(ls):
     assert_attention_close(out[1:], lse[1:], e_out[1:], e_lse[1:], "edge")
 
 
+def exact_grid_bf16(shape, g, lo=-4, hi=4):
+    """bf16 values k/4 for integers k in [lo, hi]: every product of two of
+    them, and every partial sum of up to 576 such products, is a multiple of
+    1/16 far below 2^20, so an fp32 dot product of them is exact whatever the
+    accumulation order (the fp32 rounding of the scores then plays no part)."""
+    return (torch.randint(lo, hi + 1, shape, generator=g).float() / 4).to(torch.bfloat16)
+
+
 def test_attention_mla_score_jump_recomputes(ls):
-    # rows after the first 32-row tile score thousands of log2 units above the
-    # first tile's maximum: the kernel must fall back to its exact-max pass
+    # rows after the first 32-row tile score about 90 log2 units above the
+    # first tile's maximum (more than the 64 units of headroom of the first
+    # pass's base): the kernel must fall back to its exact-max pass.  The
+    # values sit on a 1/4 grid so that every score is exact in fp32 and the
+    # 1e-4 LSE bound applies at |lse| ~ 60 as it does at ~ 10
     B, Hq, K, S = 2, 128, 256, 64
-    q, kv, rows = mla_case(B, Hq, [256, 200], K, S, seed=77)
-    g = torch.Generator().manual_seed(78)
-    kvf = kv.float()
+    g = torch.Generator().manual_seed(77)
+    q = exact_grid_bf16((B, Hq, 576), g)
+    kv = exact_grid_bf16((B, S + K, 576), g)
+    rows = torch.full((B, K), -1, dtype=torch.int32)
+    for b, n in enumerate([256, 200]):
+        rows[b, :n] = torch.randperm(S + K, generator=g)[:n].to(torch.int32)
     for b in range(B):
         late = rows[b, 40:60].long()
-        # only the 64 rope dims grow (scores jump ~250 log2 units); V, the
-        # first 512 dims, stays N(0, 1) so the output keeps its usual scale
-        kvf[b, late, 512:] = 40.0 * q[b, (torch.arange(20) * 5) % Hq, 512:].float() + \
-            0.1 * torch.randn(20, 64, generator=g)
-    kv = kvf.to(torch.bfloat16)
+        # only the 64 rope dims grow (32 x a head's own rope query: the head's
+        # score jumps by ~850 x scale); V, the first 512 dims, stays on the grid
+        kv[b, late, 512:] = (32.0 * q[b, (torch.arange(20) * 5) % Hq, 512:].float()).to(
+            torch.bfloat16)
     kvd = kv.to(DEV)
-    out, lse = ls.sparse_attn_decode(q.to(DEV), kvd, kvd, rows.to(DEV), 1 / math.sqrt(192), 1,
+    scale = 1 / math.sqrt(192)
+    out, lse = ls.sparse_attn_decode(q.to(DEV), kvd, kvd, rows.to(DEV), scale, 1,
                                      512, S + K, 576, n_splits=1)
-    e_out, e_lse = oracle_mla(q, kv, rows, 1 / math.sqrt(192))
+    e_out, e_lse = oracle_mla(q, kv, rows, scale)
+    # the case does reach the second pass: some head's score exceeds the
+    # first tile's maximum by more than 64 log2 units
+    qf, kf = q.double(), kv.double()
+    for b in range(B):
+        n_first = min(32, int((rows[b] >= 0).sum()))
+        s = scale / math.log(2) * torch.einsum("hd,nd->hn", qf[b], kf[b, rows[b, :200].long()])
+        jump = (s.max(1).values - s[:, :n_first].max(1).values).max()
+        assert float(jump) > 64.0, float(jump)
     assert np.isfinite(np_(lse)).all()
     assert_attention_close(out, lse, e_out, e_lse, "score jump")
 
@@ -534,6 +603,14 @@ def test_decode_step_host_keys_with_key_cache(ls):
     wl = dataclasses.replace(SHRUNK, batch=3, ctx=8192 + 37, n_cand=1024, topk=256,
                              hot_slots=512)
     mla_step_case(ls, wl, [wl.ctx, 5000, 300], key_rate=0.25)
+
+
+def test_decode_step_more_than_16384_candidates(ls):
+    # the whole step with C > 16384: the block top-k also resolves the hot
+    # buffer (rows, miss list, miss count) before the gather and attention
+    wl = dataclasses.replace(SHRUNK, batch=2, ctx=40000, n_cand=20000, topk=2048,
+                             hot_slots=4096, planted=400)
+    mla_step_case(ls, wl, [40000, 23000])
 
 
 def test_decode_step_deterministic(ls):

@@ -11,7 +11,7 @@ import torch
 
 from oracle import oracle as orc
 from top_sparse_attention_ls_amd import synth
-from tests.gpu_common import np_
+from tests.gpu_common import np_, parallel_map
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -19,8 +19,9 @@ PF = synth.WORKLOADS["prefill-4k-128k"]
 
 
 def check_rows(got, q, w, keys, q_pos0, topk, rows):
-    for i in rows:
-        exp, _ = orc.prefill_row(q[i], w[i], keys, q_pos0 + i, topk)
+    rows = list(rows)
+    exps = parallel_map(lambda i: orc.prefill_row(q[i], w[i], keys, q_pos0 + i, topk)[0], rows)
+    for i, exp in zip(rows, exps):
         bad = np.where(got[i] != exp)[0]
         assert len(bad) == 0, ("row", i, bad[:8], got[i][bad[:4]], exp[bad[:4]])
 
@@ -120,7 +121,9 @@ def test_prefill_fullsize_streamed_sampled_rows(ls):
     print("[prefill] streamed run", flush=True)
     outs = ls.prefill_stream_layers(qs, ws_, kh, q_pos0, wl.topk)
     torch.cuda.synchronize()
-    rows = [0, 1365, 2730, Tq - 1]
+    # 64 rows per layer: the first, the last and 62 evenly spaced between
+    rows = sorted(set(np.linspace(0, Tq - 1, 64).round().astype(int).tolist()))
+    assert len(rows) == 64
     for l in range(wl.layers):
         got = np_(outs[l])
         valid_rows(got, q_pos0, wl.topk, L)

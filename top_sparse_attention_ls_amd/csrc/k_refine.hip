@@ -600,7 +600,11 @@ constexpr int kGatherUnroll = 4;
 // when it has one, else to scratch row hot_slots + j; the stores then go
 // through a resource over the request's whole buffer, and pieces past the
 // miss count get an offset beyond it.
-template <bool DST>
+//
+// HOST (the pool is pinned host memory): the miss count is waited for before
+// any row load, and pieces past it are not loaded at all -- a speculative
+// load would be a wasted PCIe read there.
+template <bool DST, bool HOST>
 __global__ __launch_bounds__(256) void k_hot_gather(const int32_t* __restrict__ miss_pos,
                                                     const int32_t* __restrict__ n_miss,
                                                     const int32_t* __restrict__ miss_dst,
@@ -640,9 +644,15 @@ __global__ __launch_bounds__(256) void k_hot_gather(const int32_t* __restrict__ 
       p[u] = mp[min(jj, K - 1)];
       if (DST) d[u] = md[min(jj, K - 1)];
     }
+    if (HOST && nm < 0) nm = min(max(nm_raw, 0), K);
 #pragma unroll
-    for (int u = 0; u < kGatherUnroll; u++)
-      v[u] = pb[(size_t)min(max(p[u], 0), max_ctx - 1) * chunks + c[u]];
+    for (int u = 0; u < kGatherUnroll; u++) {
+      const size_t src = (size_t)min(max(p[u], 0), max_ctx - 1) * chunks + c[u];
+      if (HOST)
+        v[u] = j[u] < nm ? pb[src] : uint4{0, 0, 0, 0};
+      else
+        v[u] = pb[src];
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (nm < 0) nm = min(max(nm_raw, 0), K);  // a list never holds more than K misses
     if (DST) {
@@ -669,16 +679,19 @@ __global__ __launch_bounds__(256) void k_hot_gather(const int32_t* __restrict__ 
 
 hipError_t launch_hot_gather(const int32_t* miss_pos, const int32_t* n_miss,
                              const int32_t* miss_dst, const void* pool, void* hot, int hot_slots,
-                             int B, int max_ctx, int K, int row_elems, hipStream_t st) {
+                             int B, int max_ctx, int K, int row_elems, bool pool_on_host,
+                             hipStream_t st) {
   const int chunks = row_elems * 2 / 16;
-  if (miss_dst)
-    hipLaunchKernelGGL(k_hot_gather<true>, dim3(kGatherWGPerReq, B), dim3(256), 0, st, miss_pos,
-                       n_miss, miss_dst, (const uint4*)pool, (uint4*)hot, hot_slots, max_ctx, K,
-                       chunks);
-  else
-    hipLaunchKernelGGL(k_hot_gather<false>, dim3(kGatherWGPerReq, B), dim3(256), 0, st, miss_pos,
-                       n_miss, nullptr, (const uint4*)pool, (uint4*)hot, hot_slots, max_ctx, K,
-                       chunks);
+#define LS_GATHER(DST, HOST)                                                                  \
+  hipLaunchKernelGGL((k_hot_gather<DST, HOST>), dim3(kGatherWGPerReq, B), dim3(256), 0, st,     \
+                     miss_pos, n_miss, miss_dst, (const uint4*)pool, (uint4*)hot, hot_slots,    \
+                     max_ctx, K, chunks)
+  if (miss_dst) {
+    if (pool_on_host) LS_GATHER(true, true); else LS_GATHER(true, false);
+  } else {
+    if (pool_on_host) LS_GATHER(false, true); else LS_GATHER(false, false);
+  }
+#undef LS_GATHER
   return hipGetLastError();
 }
 

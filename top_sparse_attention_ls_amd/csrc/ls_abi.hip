@@ -70,8 +70,9 @@ int check_hot(const ls_hot_desc* d) {
                 d->batch, d->max_ctx, d->topk, d->hot_slots);
   if (d->row_elems < 8 || d->row_elems % 8 != 0)
     return fail(LS_E_ARG, "row_elems must be a positive multiple of 8 (got %d)", d->row_elems);
-  if ((int64_t)d->topk * (d->row_elems / 8) >= (int64_t)1 << 31)
-    return fail(LS_E_ARG, "topk * row_elems / 8 must stay below 2^31");
+  // the gather addresses a request's miss rows with 32-bit byte offsets
+  if ((int64_t)d->topk * d->row_elems * 2 >= (int64_t)1 << 32)
+    return fail(LS_E_UNSUPPORTED, "topk * row_elems * 2 bytes must stay below 2^32");
   if (d->pool_on_host != 0 && d->pool_on_host != 1)
     return fail(LS_E_ARG, "pool_on_host must be 0 or 1");
   return LS_OK;
@@ -89,6 +90,10 @@ int check_prefill(const ls_prefill_desc* d) {
     return fail(LS_E_UNSUPPORTED, "n_heads > 64 is not supported (got %d)", d->n_heads);
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(LS_E_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", d->head_dim);
+  // the scoring kernel addresses the key history with 32-bit byte offsets
+  if ((int64_t)d->max_ctx * d->head_dim >= (int64_t)1 << 31)
+    return fail(LS_E_UNSUPPORTED, "max_ctx * head_dim must stay below 2^31 (got %lld)",
+                (long long)d->max_ctx * d->head_dim);
   return LS_OK;
 }
 
@@ -465,7 +470,8 @@ int ls_hot_gather(const ls_hot_desc* desc, const int32_t* topk_dev, const int32_
                                 desc->hot_slots, desc->batch, desc->max_ctx, desc->topk, st),
          "hot resolve launch");
   LS_HIP(ls::launch_hot_gather(miss_pos, n_miss_dev, nullptr, pool, hot_kv_dev, desc->hot_slots,
-                               desc->batch, desc->max_ctx, desc->topk, desc->row_elems, st),
+                               desc->batch, desc->max_ctx, desc->topk, desc->row_elems,
+                               desc->pool_on_host != 0, st),
          "miss gather launch");
   return LS_OK;
 }
@@ -720,7 +726,8 @@ int ls_decode_step(const ls_step_desc* desc, const ls_step_io* io, void* ws_dev,
   if (desc->use_hot)
     LS_HIP(ls::launch_hot_gather(rws.miss_pos, io->n_miss_dev, cm->hot ? rws.miss_dst : nullptr,
                                  pool, io->hot_kv_dev, desc->hot.hot_slots, id->batch,
-                                 id->max_ctx, id->topk, desc->hot.row_elems, st),
+                                 id->max_ctx, id->topk, desc->hot.row_elems,
+                                 desc->hot.pool_on_host != 0, st),
            "miss gather launch");
   if (ev && ev[4]) LS_HIP(hipEventRecord((hipEvent_t)ev[4], st), "event record");
   LS_TRY(run_attention(a, st, ev));

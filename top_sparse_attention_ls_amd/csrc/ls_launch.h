@@ -132,7 +132,8 @@ hipError_t launch_hot_resolve(const int32_t* topk, const int32_t* pos2slot, int3
 
 hipError_t launch_hot_gather(const int32_t* miss_pos, const int32_t* n_miss,
                              const int32_t* miss_dst, const void* pool, void* hot, int hot_slots,
-                             int B, int max_ctx, int K, int row_elems, hipStream_t st);
+                             int B, int max_ctx, int K, int row_elems, bool pool_on_host,
+                             hipStream_t st);
 
 struct AttnArgs {
   const uint16_t* q;
