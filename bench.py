@@ -6,31 +6,42 @@ request of the batch (coarse scoring, candidate selection, refinement and
 top-k, hot-buffer resolve and miss gather, split attention and combine).
 Inputs are synthetic and already resident in HBM when timing starts.
 
-Prints one JSON line with:
+Prints one JSON line (the default workload, decode-128k-b32) with:
   value       layer-steps/s (whole-step throughput, steps timed back to back)
-  roofline    the dominant kernel (coarse scoring) against the 8 TB/s HBM peak:
+  hbm_roofline_step  the whole step's algorithmic bytes x steps/s against the
+              8 TB/s HBM peak
+  roofline    the dominant kernel (coarse scoring) against the HBM peak:
               algorithmic bytes per launch / its average duration, measured
               with two HIP events the library records on the launch stream
               around that kernel, on every 8th step of the timed region
-  stages_us_instrumented  per-stage times from a separate run in which every
-              stage is bracketed by events (each adds a few microseconds)
+  stages_us_instrumented / stages_roofline  per-stage times from a separate
+              run in which every stage is bracketed by events (each adds a
+              few microseconds), and each stage's fraction of the HBM peak
+  indexer_key_bytes  indexer-key bytes per step, coarse-to-fine against
+              scoring every token with its full int8 key
   graph       the same steps replayed from HIP graphs (one per input replica)
   mfma_util   int8 TOPS of the coarse scoring (live events) and bf16 TFLOP/s
               of the attention kernel (instrumented run) against the dense
               MFMA peaks
   copy_GBs    a plain 1 GiB device-to-device copy, read + write bytes per
-              second (context for the HBM figures)
-  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
+              second; read_probe: the library's read probe on the step's
+              patterns (streaming read, random 1152-byte and 128-byte rows)
+  cpu_baseline  the CPU oracle timed on sampled requests of the same step,
+              on one thread and on up to 16 host threads at once
   io_model    (hot-buffer workloads) the measured step without its KV miss
               I/O plus the missed rows over 64 / 225 / 900 GB/s, no overlap
   key_store   (original keys on the host) PCIe bytes per step, HBM saved
+  workloads   the other workloads of the same run, each with its own metric:
+              tiny-4k (latency), decode-16k-b192 (pool in pinned host
+              memory: PCIe-inclusive rate and achieved PCIe GB/s),
+              decode-950k-b4, prefill-4k-128k (int8 TOPS, overlap, CPU
+              baseline extrapolated from sampled rows)
 
-Other workloads (--workload): decode-16k-b192 (pinned-host pool),
-decode-950k-b4, decode-128k-b32-hostkeys (keys on the host behind a key
-cache), decode-128k-b32-serve and -serve-4l (the serving loop: both caches
-committing, a token appended per step; --graph replays each token step from
-a HIP graph, --microbatches splits the batch over streams), prefill-4k-128k
-(the layer-streamed prefill indexer, int8 TOPS).
+Other workloads alone (--workload): the ones above, decode-128k-b32-hostkeys
+(keys on the host behind a key cache), decode-128k-b32-serve and -serve-4l
+(the serving loop: both caches committing, a token appended per step;
+--graph replays each token step from a HIP graph, --microbatches splits the
+batch over streams).
 """
 from __future__ import annotations
 
@@ -69,7 +80,8 @@ def algorithmic_bytes(wl, n_miss_total: int, n_key_miss_total: int = 0) -> dict:
         "slot_table": B * wl.topk * 4 if wl.hot_slots else 0,
         "miss_read": n_miss_total * row,
         "miss_write": n_miss_total * row,
-        "kv_rows": B * wl.topk * row,
+        "kv_rows": (B * wl.topk * wl.kv_heads * (wl.qk_dim + wl.v_dim) * 2 if wl.attn == "mha"
+                    else B * wl.topk * row),
         "attn_q": B * wl.q_heads * wl.qk_dim * 2,
         "out_lse": B * wl.q_heads * (wl.v_dim * 2 + 4),
         "idx_q_w": B * H * (D + 1),
@@ -153,19 +165,105 @@ def copy_calibration(nbytes):
     torch.cuda.synchronize()
 
 
+def read_probes(ls, wl, hot=None, keys=None, reps=5):
+    """Bandwidth the hardware delivers to the step's read patterns (the
+    library's ls_read_probe, timed with events): a streaming read of 1 GiB,
+    and gathers of random whole rows drawn request by request as the step
+    draws them -- the step's number of 1152-byte latent rows from each
+    request's hot-buffer block (the attention's pattern), and its number of
+    128-byte key rows from each request's key block (the refinement's).
+    Context for the roofline figures."""
+    import torch
+    dev = torch.device("cuda:0")
+    out = {}
+
+    def timed(fn):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(3)
+    t = timed(lambda: ls.read_probe(buf))
+    out["seq_read_GBs"] = round((1 << 30) / t / 1e9, 1)
+    del buf
+    g = torch.Generator(device=dev).manual_seed(5)
+
+    def per_request(n_req, block, n_each):
+        r = torch.randint(0, block, (n_req, n_each), generator=g, device=dev, dtype=torch.int64)
+        r += torch.arange(n_req, device=dev, dtype=torch.int64)[:, None] * block
+        return r.to(torch.int32).flatten()
+
+    if hot is not None:
+        B, block = hot.shape[0], hot.shape[1]
+        rows = per_request(B, block, wl.topk)
+        t = timed(lambda: ls.read_probe(hot, rows, 1152))
+        out["rows_1152B_GBs"] = round(rows.numel() * 1152 / t / 1e9, 1)
+        out["rows_1152B"] = "%d random rows of each request's %d-row hot-buffer block" % (
+            wl.topk, block)
+    if keys is not None:
+        B, block = keys.shape[0], keys.shape[1]
+        rows = per_request(B, block, wl.n_cand)
+        t = timed(lambda: ls.read_probe(keys, rows, 128))
+        out["rows_128B_GBs"] = round(rows.numel() * 128 / t / 1e9, 1)
+        out["rows_128B"] = "%d random rows of each request's %d-row key block" % (wl.n_cand,
+                                                                                   block)
+    torch.cuda.empty_cache()
+    return out
+
+
+def metric_for(wl) -> str:
+    """The metric string of a decode workload's line (the headline workload
+    keeps the benchmark's own metric)."""
+    if wl.name == "decode-128k-b32":
+        return METRIC
+    ctx = "%dK" % (wl.ctx // 1024) if wl.ctx % 1024 == 0 else "%dK" % round(wl.ctx / 1000)
+    extra = ""
+    if wl.attn == "mha":
+        extra = ", MHA %dx%d, latency" % (wl.q_heads, wl.qk_dim)
+    if wl.pool_on_host:
+        extra += ", pool in pinned host memory (PCIe-inclusive)"
+    if wl.keys_on_host:
+        extra += ", original keys in pinned host memory"
+    return "sparse-decode layer-steps/s at %s (B=%d)%s + %% of HBM roofline" % (ctx, wl.batch,
+                                                                                extra)
+
+
+def indexer_key_bytes(wl, ab) -> dict:
+    """Indexer-key bytes read per step: the coarse-to-fine pass (every compact
+    key, plus the candidates' original keys) against scoring every token
+    with its full int8 key."""
+    full = wl.batch * wl.ctx * wl.idx_dim
+    c2f = ab["coarse_keys"] + ab["refine_keys"]
+    return {"coarse_pass": ab["coarse_keys"], "refine": ab["refine_keys"],
+            "coarse_to_fine_total": c2f, "full_key_scoring": full,
+            "ratio": round(c2f / full, 4)}
+
+
 def build_inputs(ls, synth, wl, dev, replicas):
     import torch
     inp = synth.indexer_inputs(wl, dev)
     keys = inp["keys"]
     kc = ls.pack_coarse(keys)
     q_attn = synth.attention_query(wl, dev)
-    pool = synth.kv_pool(wl, dev, pin=wl.pool_on_host, gen_device=dev)
     ctx_len = torch.full((wl.batch,), wl.ctx, dtype=torch.int32, device=dev)
-    # the hot buffer is laid out from this workload's own selection, computed
-    # once here (setup, untimed) so that exactly the stated share misses
-    cand = ls.index_coarse(inp["q"], inp["w"], kc, ctx_len, wl.n_cand)
-    sel, _ = ls.refine_topk(inp["q"], inp["w"], keys, cand, ctx_len, wl.topk)
-    pos2slot, hot, n_miss = synth.hot_fill(wl, sel, pool, dev)
+    pool = pos2slot = hot = kv = None
+    n_miss = [0] * wl.batch
+    if wl.hot_slots:
+        pool = synth.kv_pool(wl, dev, pin=wl.pool_on_host, gen_device=dev)
+        # the hot buffer is laid out from this workload's own selection,
+        # computed once here (setup, untimed) so that exactly the stated share
+        # misses
+        cand = ls.index_coarse(inp["q"], inp["w"], kc, ctx_len, wl.n_cand)
+        sel, _ = ls.refine_topk(inp["q"], inp["w"], keys, cand, ctx_len, wl.topk)
+        pos2slot, hot, n_miss = synth.hot_fill(wl, sel, pool, dev)
+    else:
+        kv = synth.kv_cache_mha(wl, dev)
     key_cache, n_key_miss = None, None
     if wl.key_slots:
         # the indexer-key cache is laid out from the same candidate set
@@ -177,22 +275,59 @@ def build_inputs(ls, synth, wl, dev, replicas):
         keys = keys.to("cpu").pin_memory()
     reps = []
     for r in range(replicas):
-        rep_ = dict(
-            q_idx=inp["q"], w_idx=inp["w"], ctx_len=ctx_len,
-            k8=keys if (r == 0 or wl.keys_on_host) else keys.clone(),
-            kc=kc if r == 0 else kc.clone(),
-            q_attn=q_attn if r == 0 else q_attn.clone(),
-            pos2slot=pos2slot if r == 0 else pos2slot.clone(),
-            hot_kv=hot if r == 0 else hot.clone(), pool_kv=pool)
+        def rep(t):
+            return t if (r == 0 or t is None) else t.clone()
+        rep_ = dict(q_idx=inp["q"], w_idx=inp["w"], ctx_len=ctx_len,
+                    k8=keys if wl.keys_on_host else rep(keys), kc=rep(kc),
+                    q_attn=rep(q_attn), pos2slot=rep(pos2slot), hot_kv=rep(hot), pool_kv=pool)
+        if kv is not None:
+            rep_.update(k_cache=rep(kv[0]), v_cache=rep(kv[1]))
         if key_cache is not None:
-            rep_.update({k: v if r == 0 else v.clone() for k, v in key_cache.items()})
+            rep_.update({k: rep(v) for k, v in key_cache.items()})
         reps.append(rep_)
     torch.cuda.synchronize()
-    return reps, n_miss, n_key_miss, inp, q_attn, pool, pos2slot, hot
+    return dict(reps=reps, n_miss=n_miss, n_key_miss=n_key_miss, inp=inp, q_attn=q_attn,
+                pool=pool, pos2slot=pos2slot, hot=hot, kv=kv)
 
 
-def cpu_baseline(wl, inp, q_attn, pool, pos2slot, hot, n_sample):
-    """The oracle, as it stands, on n_sample requests of the same step."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def host_threads() -> int:
+    """Host threads of the parallel CPU baseline: the CPU share of one GPU
+    (16), or fewer if the machine has fewer."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def timed_pool(fn, items, n_threads):
+    """fn over items on n_threads host threads; (wall seconds, per-item
+    seconds).  The oracle's C calls release the interpreter lock."""
+    import concurrent.futures
+
+    def one(x):
+        t0 = time.perf_counter()
+        fn(x)
+        return time.perf_counter() - t0
+
+    t0 = time.perf_counter()
+    with concurrent.futures.ThreadPoolExecutor(n_threads) as ex:
+        per = list(ex.map(one, items))
+    return time.perf_counter() - t0, per
+
+
+def cpu_baseline(wl, st, n_single, n_parallel):
+    """The oracle, as it stands, on sampled requests of the same step: one
+    thread on n_single requests, then n_parallel requests at once on that
+    many host threads (independent requests, as independent processes would
+    split the batch).  value = the parallel rate scaled to the batch."""
     import numpy as np
     import torch
     from oracle import oracle as orc
@@ -200,38 +335,343 @@ def cpu_baseline(wl, inp, q_attn, pool, pos2slot, hot, n_sample):
     def bits(t):
         return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
-    t_total = 0.0
-    for b in range(n_sample):
-        q, w = inp["q"][b].cpu().numpy(), inp["w"][b].cpu().numpy()
-        keys = inp["keys"][b].cpu().numpy()
-        qa = bits(q_attn[b])
-        p2s = pos2slot[b].cpu().numpy()
-        hb = bits(hot[b]).copy()
-        pb = bits(pool[b])
-        t0 = time.perf_counter()
-        orc.decode_request(q, w, keys, wl.ctx, wl.n_cand, wl.topk, qa, wl.scale,
-                           pos2slot=p2s, hot_bits=hb, pool_bits=pb, v_dim=wl.v_dim,
-                           row_stride=wl.qk_dim)
-        t_total += time.perf_counter() - t0
-    per_request = t_total / n_sample
+    inp = st["inp"]
+
+    def prepared(b):
+        x = dict(q=inp["q"][b].cpu().numpy(), w=inp["w"][b].cpu().numpy(),
+                 keys=inp["keys"][b].cpu().numpy(), qa=bits(st["q_attn"][b]))
+        if wl.hot_slots:
+            x.update(p2s=st["pos2slot"][b].cpu().numpy(), hot=bits(st["hot"][b]).copy(),
+                     pool=bits(st["pool"][b]))
+        else:
+            x.update(kc=bits(st["kv"][0][b]).reshape(-1), vc=bits(st["kv"][1][b]).reshape(-1))
+        return x
+
+    def run(x):
+        if wl.hot_slots:
+            orc.decode_request(x["q"], x["w"], x["keys"], wl.ctx, wl.n_cand, wl.topk, x["qa"],
+                               wl.scale, pos2slot=x["p2s"], hot_bits=x["hot"],
+                               pool_bits=x["pool"], v_dim=wl.v_dim, row_stride=wl.qk_dim)
+        else:
+            orc.decode_request(x["q"], x["w"], x["keys"], wl.ctx, wl.n_cand, wl.topk, x["qa"],
+                               wl.scale, k_cache_bits=x["kc"], v_cache_bits=x["vc"],
+                               n_kv_heads=wl.kv_heads, v_dim=wl.v_dim,
+                               row_stride=wl.kv_heads * wl.qk_dim, head_stride=wl.qk_dim)
+
+    res = {"unit": "layer-steps/s", "kind": "oracle", "cpu_model": cpu_model(),
+           "host_cpus_visible": os.cpu_count()}
+    per_single = None
+    if n_single > 0:
+        xs = [prepared(b % wl.batch) for b in range(n_single)]
+        _, per = timed_pool(run, xs, 1)
+        per_single = sum(per) / len(per)
+        del xs
+        res["single_thread"] = {"value": 1.0 / (per_single * wl.batch), "cores": 1,
+                                "s_per_request": round(per_single, 3),
+                                "requests_sampled": n_single}
+    P = min(n_parallel, host_threads())
+    if P > 0:
+        xs = [prepared(b % wl.batch) for b in range(P)]
+        wall, per = timed_pool(run, xs, P)
+        del xs
+        rate = P / wall / wl.batch
+        res.update(value=rate, cores=P,
+                   sample="%d requests of %s at once on %d host threads (whole step per "
+                          "request: coarse scores, candidates, refine, top-k, hot resolve + "
+                          "gather, attention; single-threaded C each), %.2f s wall, scaled to "
+                          "the %d-request batch" % (P, wl.name, P, wall, wl.batch))
+        if per_single is None:
+            res["single_thread"] = {"value": 1.0 / (sum(per) / P * wl.batch), "cores": 1,
+                                    "s_per_request": round(sum(per) / P, 3),
+                                    "note": "per-request times inside the parallel run"}
+    else:
+        res.update(value=res["single_thread"]["value"], cores=1,
+                   sample="%d requests of %s, single-threaded C" % (n_single, wl.name))
+    return res
+
+
+STAGE_KERNELS = {
+    "coarse_score": "k_coarse",
+    "candidate_select": "k_topc_filter + k_topc_emit",
+    "refine_topk_resolve": "k_refine + k_topk_hist",
+    "miss_gather": "k_hot_gather",
+    "attention": "k_attn_mfma",
+    "combine": "k_combine",
+}
+
+
+def stage_bytes(wl, ab) -> dict:
+    """Algorithmic bytes of each stage (the parts of algorithmic_bytes)."""
     return {
-        "value": 1.0 / (per_request * wl.batch),
-        "unit": "layer-steps/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": "%d of %d requests of %s, whole step per request (coarse scores, "
-                  "candidates, refine, top-k, hot resolve + gather, attention), "
-                  "single-threaded C; %.2f s per request, scaled to the %d-request batch"
-                  % (n_sample, wl.batch, wl.name, per_request, wl.batch),
+        "coarse_score": ab["coarse_keys"] + ab["idx_q_w"],
+        "candidate_select": 0,
+        "refine_topk_resolve": ab["refine_keys"] + ab["slot_table"],
+        "miss_gather": ab["miss_read"] + ab["miss_write"],
+        "attention": ab["kv_rows"] + ab["attn_q"],
+        "combine": ab["out_lse"],
     }
 
 
-def run_prefill(ls, synth, wl, args):
+def run_decode(ls, synth, wl, steps, warmup, replicas, full=True, n_single=0, n_parallel=0):
+    """Time K = steps whole decode steps of workload wl back to back (after
+    warmup untimed ones) and return the result object.  full: also the
+    repeats, the HIP-graph replay and the stage breakdown of an instrumented
+    run; otherwise only the timed run and a short instrumented run."""
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("[bench] building inputs for %s" % wl.name, file=sys.stderr, flush=True)
+    st = build_inputs(ls, synth, wl, dev, replicas)
+    reps, n_miss, n_key_miss = st["reps"], st["n_miss"], st["n_key_miss"]
+    mha = not wl.hot_slots
+    step = ls.DecodeStep(batch=wl.batch, max_ctx=wl.ctx, idx_heads=wl.idx_heads,
+                         idx_dim=wl.idx_dim, n_cand=wl.n_cand, topk=wl.topk,
+                         q_heads=wl.q_heads, qk_dim=wl.qk_dim, v_dim=wl.v_dim, scale=wl.scale,
+                         hot_slots=wl.hot_slots, pool_on_host=wl.pool_on_host,
+                         keys_on_host=wl.keys_on_host, key_slots=wl.key_slots,
+                         kv_heads=wl.kv_heads,
+                         kv_row_stride=wl.kv_heads * wl.qk_dim if mha else None,
+                         kv_head_stride=wl.qk_dim if mha else 0, device=dev)
+
+    def run(i, events=None):
+        r = reps[i % len(reps)]
+        step.run(q_idx=r["q_idx"], w_idx=r["w_idx"], kc=r["kc"], k8=r["k8"],
+                 ctx_len=r["ctx_len"], q_attn=r["q_attn"], pos2slot=r["pos2slot"],
+                 hot_kv=r["hot_kv"], pool_kv=r["pool_kv"], kpos2slot=r.get("kpos2slot"),
+                 kcache=r.get("kcache"), k_cache=r.get("k_cache"), v_cache=r.get("v_cache"),
+                 events=events)
+
+    # host-side set-up first (the miss-count check after one step, the
+    # events), so that the warm-up runs right up to the timed region and the
+    # GPU enters it busy rather than after a host-side pause
+    run(0)
+    torch.cuda.synchronize()
+    if wl.hot_slots:
+        miss_now = step.n_miss.cpu().tolist()
+        assert miss_now == n_miss, "hot buffer miss counts drifted: %s" % miss_now
+    if wl.keys_on_host:
+        # candidates whose key is not in the key cache: their rows cross PCIe
+        c = step.cand.long()
+        kp = reps[0].get("kpos2slot")
+        if kp is None:
+            key_miss_now = (c >= 0).sum(1).tolist()
+        else:
+            hit = kp.gather(1, c.clamp(min=0)) >= 0
+            key_miss_now = ((c >= 0) & ~hit).sum(1).tolist()
+        if n_key_miss is not None:
+            assert key_miss_now == n_key_miss, "key cache miss counts drifted"
+        n_key_miss = key_miss_now
+
+    K = steps
+    # timed region: whole steps back to back; on every SAMPLE-th step the
+    # library also records two events around the coarse kernel (an event
+    # costs the stream a few microseconds, so only the measured kernel is
+    # bracketed, and only on a sample of the steps)
+    SAMPLE = 8
+    coarse_ev = {}
+    for i in range(0, K, SAMPLE):
+        coarse_ev[i] = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for pair in coarse_ev.values():  # create the underlying events before use
+        for e in pair:
+            e.record()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start.record()
+    t_end.record()
+    print("[bench] %s: warmup %d, then timing %d steps" % (wl.name, warmup, K), file=sys.stderr,
+          flush=True)
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(K):
+        pair = coarse_ev.get(i)
+        run(i, None if pair is None else [pair[0], pair[1]] + [None] * (ls.STEP_EVENTS - 2))
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / K
+    coarse_ms = sum(p[0].elapsed_time(p[1]) for p in coarse_ev.values()) / len(coarse_ev)
+
+    # the same K steps timed again, without any event inside: the spread of
+    # the rate over repeated runs (the value above is the first run's)
+    rep_ms = [ms_per_step]
+    for _ in range(REPEATS - 1 if full else 0):
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        r0.record()
+        for i in range(K):
+            run(i)
+        r1.record()
+        torch.cuda.synchronize()
+        rep_ms.append(r0.elapsed_time(r1) / K)
+    rates = sorted(1000.0 / m for m in rep_ms)
+
+    # stage breakdown from a separate instrumented run (every stage bracketed)
+    n_inst = min(K, 20 if full else 8)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ls.STEP_EVENTS)]
+           for _ in range(n_inst)]
+    for row in evs:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    for i in range(n_inst):
+        run(i, evs[i])
+    torch.cuda.synchronize()
+    stage_ms = [0.0] * (ls.STEP_EVENTS - 1)
+    for row in evs:
+        for s_ in range(ls.STEP_EVENTS - 1):
+            stage_ms[s_] += row[s_].elapsed_time(row[s_ + 1]) / n_inst
+
+    graph = None
+    if full:
+        # the same steps replayed from HIP graphs (reported beside the eager value)
+        try:
+            graph = graph_timing(run, len(reps), K)
+        except Exception as exc:  # reported, never hidden: the eager value stands
+            graph = {"error": repr(exc)}
+        torch.cuda.synchronize()
+
+    ab = algorithmic_bytes(wl, sum(n_miss), sum(n_key_miss or [0]))
+    steps_per_s = 1000.0 / ms_per_step
+    coarse_bytes = ab["coarse_keys"] + ab["idx_q_w"]
+    achieved = coarse_bytes / (coarse_ms * 1e-3) / 1e9
+    step_frac = ab["total"] * steps_per_s / 1e9 / HBM_PEAK_GBS
+    result = {
+        "metric": metric_for(wl),
+        "value": round(steps_per_s, 2),
+        "unit": "layer-steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "batch": wl.batch, "ctx": wl.ctx, "idx_heads": wl.idx_heads,
+            "idx_dim": wl.idx_dim, "n_cand": wl.n_cand, "topk": wl.topk,
+            "attention": "%s %d heads x %d" % (wl.attn.upper(), wl.q_heads, wl.qk_dim),
+            "v_dim": wl.v_dim, "hot_slots": wl.hot_slots, "miss_rate": wl.miss_rate,
+            "pool": ("pinned-host" if wl.pool_on_host else "hbm") if wl.hot_slots else "none",
+            "keys": "pinned-host" if wl.keys_on_host else "hbm",
+            "key_slots": wl.key_slots, "key_miss_rate": wl.key_miss_rate,
+            "replicas": replicas, "parallelism": "single-gpu",
+        },
+        "hbm_roofline_step": {
+            "algorithmic_bytes": ab["total"],
+            "achieved_GBs": round(ab["total"] * steps_per_s / 1e9, 1),
+            "frac": round(step_frac, 4),
+        },
+        # the dominant kernel of the step against the HBM peak (live events);
+        # the whole step's fraction is hbm_roofline_step.frac
+        "roofline": {
+            "kernel": "coarse_score (k_coarse)",
+            "scope": "dominant kernel; whole step in hbm_roofline_step",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic(wl.name),
+            "algorithmic_bytes_per_launch": coarse_bytes,
+            "avg_launch_us": round(coarse_ms * 1000, 2),
+            "step_frac": round(step_frac, 4),
+        },
+        "coarse_events_sampled": len(coarse_ev),
+        "stages_us_instrumented": {n: round(v * 1000, 2) for n, v in zip(STAGES, stage_ms)},
+        "request_layer_steps_per_s": round(steps_per_s * wl.batch, 1),
+        "indexer_key_bytes": indexer_key_bytes(wl, ab),
+    }
+    # every stage against its own roofline (stage times from the instrumented
+    # run: each includes the event it ends on, a few microseconds)
+    sb = stage_bytes(wl, ab)
+    result["stages_roofline"] = {
+        n: {"kernels": STAGE_KERNELS[n], "us": round(v * 1000, 2), "algorithmic_bytes": sb[n],
+            "frac_of_hbm": round(sb[n] / (v * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if v > 0 else None}
+        for n, v in zip(STAGES, stage_ms)}
+    if mha:
+        result["latency_us"] = round(ms_per_step * 1000, 2)
+        result["hbm_roofline_step"]["note"] = ("%.2f MB per step stays in the caches: the step "
+                                               "is latency-bound" % (ab["total"] / 1e6))
+    if full:
+        result["repeats"] = {
+            "runs": len(rates), "steps_each": K,
+            "median": round(rates[len(rates) // 2], 2),
+            "p10": round(rates[max(0, int(0.1 * (len(rates) - 1)))], 2),
+            "p90": round(rates[int(round(0.9 * (len(rates) - 1)))], 2),
+            "note": "layer-steps/s of the first run (the value) and of the same K steps "
+                    "repeated without events",
+        }
+        result["graph"] = graph
+    if wl.keys_on_host:
+        full_keys = wl.batch * wl.ctx * wl.idx_dim
+        cache = wl.batch * wl.key_slots * (wl.idx_dim) + (wl.batch * wl.ctx * 4
+                                                           if wl.key_slots else 0)
+        pcie = sum(n_key_miss) * wl.idx_dim
+        result["key_store"] = {
+            "pcie_key_bytes_per_step": pcie,
+            "pcie_GBs_at_value": round(pcie * steps_per_s / 1e9, 2),
+            "hbm_bytes_full_keys": full_keys,
+            "hbm_bytes_key_cache_and_table": cache,
+            "hbm_saved_bytes": full_keys - cache,
+            "hbm_saved_per_request": (full_keys - cache) // wl.batch,
+        }
+    if wl.hot_slots:
+        # the compute-plus-I/O model of the hot-buffer analysis: the measured
+        # step without its KV miss I/O, plus the missed rows' bytes over a
+        # link of each modelled bandwidth, the two not overlapping
+        stage = dict(zip(STAGES, stage_ms))
+        compute_us = (sum(stage_ms) - stage["miss_gather"]) * 1000
+        miss_bytes = sum(n_miss) * wl.qk_dim * 2
+        result["io_model"] = {
+            "compute_us_without_kv_io": round(compute_us, 1),
+            "kv_miss_bytes": miss_bytes,
+            "modeled_us": {str(bw): round(compute_us + miss_bytes / (bw * 1e3), 1)
+                           for bw in (64, 225, 900)},
+            "measured_us": round(ms_per_step * 1000, 1),
+            "measured_gather_us": round(stage["miss_gather"] * 1000, 1),
+            "gather_GBs": round(miss_bytes / (stage["miss_gather"] * 1e-3) / 1e9, 1),
+            "link": "pinned host (PCIe)" if wl.pool_on_host else "HBM",
+            "note": "stage times from the instrumented run (an event between stages)",
+        }
+        if wl.pool_on_host:
+            result["pcie"] = {
+                "miss_bytes_per_step": miss_bytes,
+                "gather_us": round(stage["miss_gather"] * 1000, 1),
+                "achieved_GBs": round(miss_bytes / (stage["miss_gather"] * 1e-3) / 1e9, 1),
+                "rate_without_pcie_gather": round(1e6 / compute_us, 1),
+                "note": "value is PCIe-inclusive (the gather reads the missed rows over PCIe "
+                        "inside the step); the HBM fraction counts only device bytes",
+            }
+    coarse_ops = 2 * wl.batch * wl.ctx * wl.idx_heads * wl.idx_dim
+    attn_flops = 2 * wl.batch * wl.q_heads * wl.topk * (wl.qk_dim + wl.v_dim)
+    attn_ms = stage_ms[STAGES.index("attention")]
+    result["mfma_util"] = {
+        "coarse_int8_TOPS": round(coarse_ops / (coarse_ms * 1e-3) / 1e12, 1),
+        "coarse_frac_of_5000": round(coarse_ops / (coarse_ms * 1e-3) / 1e12 / 5000.0, 4),
+        "attention_bf16_TFLOPs": round(attn_flops / (attn_ms * 1e-3) / 1e12, 1),
+        "attention_frac_of_2500": round(attn_flops / (attn_ms * 1e-3) / 1e12 / 2500.0, 4),
+        "note": "from event timings; the counter-measured busy fractions are in profiles/",
+    }
+    if n_single > 0 or n_parallel > 0:
+        print("[bench] %s: cpu baseline" % wl.name, file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, st, n_single, n_parallel)
+    probe_src = (st["hot"] if wl.hot_slots else None,
+                 st["inp"]["keys"] if not wl.keys_on_host else None)
+    del reps, st, step
+    return result, probe_src
+
+
+def run_prefill(ls, synth, wl, steps, warmup, n_rows_cpu=0):
     """The prefill-chunk indexer: every layer's history streamed from pinned
     host memory through two device buffers, the copy of layer l+1 overlapping
     the indexer of layer l.  value = int8 TOPS of the causal score GEMM over
     the whole streamed run; also the compute-only time (keys already on the
-    device) and the overlap efficiency (compute-only / streamed)."""
+    device) and the overlap efficiency (compute-only / streamed).  With
+    n_rows_cpu > 0 the oracle is timed on that many sampled query rows of
+    layer 0 on as many host threads, and its rate extrapolated to the chunk."""
     import torch
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -255,11 +695,11 @@ def run_prefill(ls, synth, wl, args):
     def compute_only():
         return [ls.prefill_index_topk(qs[l], ws_[l], kd[l], q_pos0, K) for l in range(wl.layers)]
 
-    for _ in range(max(args.warmup, 1)):
+    for _ in range(max(warmup, 1)):
         streamed()
         compute_only()
     torch.cuda.synchronize()
-    steps = max(1, min(args.steps, 10))
+    steps = max(1, min(steps, 10))
 
     def timed(fn):
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -282,7 +722,7 @@ def run_prefill(ls, synth, wl, args):
         "unit": "TOPS",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": max(args.warmup, 1),
+        "warmup": max(warmup, 1),
         "ms_per_step": round(ms_stream, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -298,9 +738,32 @@ def run_prefill(ls, synth, wl, args):
         "compute_only_ms": round(ms_compute, 4),
         "compute_only_tops": round(tops_c, 1),
         "overlap_efficiency": round(ms_compute / ms_stream, 4),
+        "h2d_bytes_per_layer": L * D,
         "int8_ops": ops,
     }
-    print(json.dumps(result), flush=True)
+    if n_rows_cpu > 0:
+        import numpy as np
+        from oracle import oracle as orc
+        P = min(n_rows_cpu, host_threads())
+        rows = np.linspace(0, Tq - 1, P).round().astype(int).tolist()
+        q0, w0, k0 = qs[0].cpu().numpy(), ws_[0].cpu().numpy(), kh[0].numpy()
+        print("[bench] prefill cpu baseline on %d rows" % P, file=sys.stderr, flush=True)
+        wall, per = timed_pool(lambda i: orc.prefill_row(q0[i], w0[i], k0, q_pos0 + i, K), rows,
+                               P)
+        row_ops = sum(2 * (q_pos0 + i + 1) * H * D for i in rows)
+        # each row's time scales with the keys it sees; extrapolate by ops
+        rate = row_ops / wall
+        result["cpu_baseline"] = {
+            "value": round(rate / 1e12, 6), "unit": "TOPS", "cores": P, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus_visible": os.cpu_count(),
+            "extrapolated_ms_per_chunk": round(ops / rate * 1e3, 1),
+            "single_thread_s_per_row": round(sum(per) / len(per), 3),
+            "sample": "%d query rows of layer 0 (first, last, evenly spaced) at once on %d host "
+                      "threads, single-threaded C each (%.2f s wall); extrapolated to the "
+                      "%d x %d-layer chunk by int8 operations" % (P, P, wall, Tq, wl.layers),
+        }
+    del layers, qs, ws_, kh, kd, buf0, buf1
+    return result
 
 
 def micro_batch(ls, st, b0, Bm, wl, dev):
@@ -501,8 +964,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode-128k-b32")
     ap.add_argument("--replicas", type=int, default=2)
-    ap.add_argument("--cpu-sample", type=int, default=4,
-                    help="requests the CPU oracle baseline runs (0 = skip)")
+    ap.add_argument("--cpu-sample", type=int, default=16,
+                    help="requests the CPU oracle baseline runs at once on as many host threads "
+                         "(0 = skip the baseline)")
+    ap.add_argument("--extras", type=int, default=1,
+                    help="default workload: also measure the other workloads (4K latency, "
+                         "16K x 192 with the pool on the host, 950K x 4, the prefill chunk) "
+                         "and report them under 'workloads' (0 = skip)")
     ap.add_argument("--microbatches", type=int, default=0,
                     help="serving workloads: split the batch into this many micro-batches on "
                          "their own streams (0: the workload's default)")
@@ -516,6 +984,7 @@ def main():
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
+    import gc
     import torch
     import top_sparse_attention_ls_amd as ls
     from top_sparse_attention_ls_amd import synth
@@ -523,219 +992,42 @@ def main():
     ls.load()
     wl = synth.WORKLOADS[args.workload]
     if wl.n_query:
-        run_prefill(ls, synth, wl, args)
+        print(json.dumps(run_prefill(ls, synth, wl, args.steps, args.warmup,
+                                     n_rows_cpu=args.cpu_sample)), flush=True)
         return
     if wl.serve_drift > 0:
         run_serve(ls, synth, wl, args)
         return
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    print("[bench] building inputs for %s" % wl.name, file=sys.stderr, flush=True)
-    reps, n_miss, n_key_miss, inp, q_attn, pool, pos2slot, hot = build_inputs(
-        ls, synth, wl, dev, args.replicas)
-    step = ls.DecodeStep(batch=wl.batch, max_ctx=wl.ctx, idx_heads=wl.idx_heads,
-                         idx_dim=wl.idx_dim, n_cand=wl.n_cand, topk=wl.topk,
-                         q_heads=wl.q_heads, qk_dim=wl.qk_dim, v_dim=wl.v_dim, scale=wl.scale,
-                         hot_slots=wl.hot_slots, pool_on_host=wl.pool_on_host,
-                         keys_on_host=wl.keys_on_host, key_slots=wl.key_slots, device=dev)
-
-    def run(i, events=None):
-        r = reps[i % len(reps)]
-        step.run(q_idx=r["q_idx"], w_idx=r["w_idx"], kc=r["kc"], k8=r["k8"],
-                 ctx_len=r["ctx_len"], q_attn=r["q_attn"], pos2slot=r["pos2slot"],
-                 hot_kv=r["hot_kv"], pool_kv=r["pool_kv"], kpos2slot=r.get("kpos2slot"),
-                 kcache=r.get("kcache"), events=events)
-
-    # host-side set-up first (the miss-count check after one step, the
-    # events), so that the warm-up runs right up to the timed region and the
-    # GPU enters it busy rather than after a host-side pause
-    run(0)
-    torch.cuda.synchronize()
-    miss_now = step.n_miss.cpu().tolist()
-    assert miss_now == n_miss, "hot buffer miss counts drifted: %s" % miss_now
-    if wl.keys_on_host:
-        # candidates whose key is not in the key cache: their rows cross PCIe
-        c = step.cand.long()
-        kp = reps[0].get("kpos2slot")
-        if kp is None:
-            key_miss_now = (c >= 0).sum(1).tolist()
-        else:
-            hit = kp.gather(1, c.clamp(min=0)) >= 0
-            key_miss_now = ((c >= 0) & ~hit).sum(1).tolist()
-        if n_key_miss is not None:
-            assert key_miss_now == n_key_miss, "key cache miss counts drifted"
-        n_key_miss = key_miss_now
-
-    K = args.steps
-    # timed region: whole steps back to back; on every SAMPLE-th step the
-    # library also records two events around the coarse kernel (an event
-    # costs the stream a few microseconds, so only the measured kernel is
-    # bracketed, and only on a sample of the steps)
-    SAMPLE = 8
-    coarse_ev = {}
-    for i in range(0, K, SAMPLE):
-        coarse_ev[i] = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    for pair in coarse_ev.values():  # create the underlying events before use
-        for e in pair:
-            e.record()
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_start.record()
-    t_end.record()
-    print("[bench] warmup %d, then timing %d steps" % (args.warmup, K), file=sys.stderr, flush=True)
-    for i in range(args.warmup):
-        run(i)
-    torch.cuda.synchronize()
-    t_start.record()
-    for i in range(K):
-        pair = coarse_ev.get(i)
-        run(i, None if pair is None else [pair[0], pair[1]] + [None] * (ls.STEP_EVENTS - 2))
-    t_end.record()
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / K
-    coarse_ms = sum(p[0].elapsed_time(p[1]) for p in coarse_ev.values()) / len(coarse_ev)
-
-    # the same K steps timed again, without any event inside: the spread of
-    # the rate over repeated runs (the value above is the first run's)
-    rep_ms = [ms_per_step]
-    for _ in range(REPEATS - 1):
-        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        r0.record()
-        for i in range(K):
-            run(i)
-        r1.record()
-        torch.cuda.synchronize()
-        rep_ms.append(r0.elapsed_time(r1) / K)
-    rates = sorted(1000.0 / m for m in rep_ms)
-
-    # stage breakdown from a separate instrumented run (every stage bracketed)
-    n_inst = min(K, 20)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ls.STEP_EVENTS)]
-           for _ in range(n_inst)]
-    for row in evs:
-        for e in row:
-            e.record()
-    torch.cuda.synchronize()
-    for i in range(n_inst):
-        run(i, evs[i])
-    torch.cuda.synchronize()
-    stage_ms = [0.0] * (ls.STEP_EVENTS - 1)
-    for row in evs:
-        for s_ in range(ls.STEP_EVENTS - 1):
-            stage_ms[s_] += row[s_].elapsed_time(row[s_ + 1]) / n_inst
-
-    # the same steps replayed from HIP graphs (reported beside the eager value)
-    try:
-        graph = graph_timing(run, len(reps), K)
-    except Exception as exc:  # reported, never hidden: the eager value stands
-        graph = {"error": repr(exc)}
-    torch.cuda.synchronize()
-
-    ab = algorithmic_bytes(wl, sum(n_miss), sum(n_key_miss or [0]))
-    steps_per_s = 1000.0 / ms_per_step
-    coarse_bytes = wl.batch * wl.ctx * wl.idx_dim // 2 + wl.batch * wl.idx_heads * (wl.idx_dim + 1)
-    achieved = coarse_bytes / (coarse_ms * 1e-3) / 1e9
-    result = {
-        "metric": METRIC,
-        "value": round(steps_per_s, 2),
-        "unit": "layer-steps/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "int8+bf16",
-        "data": "synthetic",
-        "config": {
-            "workload": wl.name, "batch": wl.batch, "ctx": wl.ctx, "idx_heads": wl.idx_heads,
-            "idx_dim": wl.idx_dim, "n_cand": wl.n_cand, "topk": wl.topk,
-            "q_heads": wl.q_heads, "latent": wl.qk_dim, "v_dim": wl.v_dim,
-            "hot_slots": wl.hot_slots, "miss_rate": wl.miss_rate,
-            "pool": "pinned-host" if wl.pool_on_host else "hbm",
-            "keys": "pinned-host" if wl.keys_on_host else "hbm",
-            "key_slots": wl.key_slots, "key_miss_rate": wl.key_miss_rate,
-            "replicas": args.replicas, "parallelism": "single-gpu",
-        },
-        "hbm_roofline_step": {
-            "algorithmic_bytes": ab["total"],
-            "achieved_GBs": round(ab["total"] * steps_per_s / 1e9, 1),
-            "frac": round(ab["total"] * steps_per_s / 1e9 / HBM_PEAK_GBS, 4),
-        },
-        "roofline": {
-            "kernel": "coarse_score (k_coarse)",
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": load_traffic(wl.name),
-            "algorithmic_bytes_per_launch": coarse_bytes,
-            "avg_launch_us": round(coarse_ms * 1000, 2),
-        },
-        "coarse_events_sampled": len(coarse_ev),
-        "stages_us_instrumented": {n: round(v * 1000, 2) for n, v in zip(STAGES, stage_ms)},
-        "request_layer_steps_per_s": round(steps_per_s * wl.batch, 1),
-        "repeats": {
-            "runs": len(rates), "steps_each": K,
-            "median": round(rates[len(rates) // 2], 2),
-            "p10": round(rates[max(0, int(0.1 * (len(rates) - 1)))], 2),
-            "p90": round(rates[int(round(0.9 * (len(rates) - 1)))], 2),
-            "note": "layer-steps/s of the first run (the value) and of the same K steps repeated "
-                    "without events",
-        },
-        "graph": graph,
-    }
-    if wl.keys_on_host:
-        full_keys = wl.batch * wl.ctx * wl.idx_dim
-        cache = wl.batch * wl.key_slots * (wl.idx_dim) + (wl.batch * wl.ctx * 4
-                                                           if wl.key_slots else 0)
-        pcie = sum(n_key_miss) * wl.idx_dim
-        result["key_store"] = {
-            "pcie_key_bytes_per_step": pcie,
-            "pcie_GBs_at_value": round(pcie * steps_per_s / 1e9, 2),
-            "hbm_bytes_full_keys": full_keys,
-            "hbm_bytes_key_cache_and_table": cache,
-            "hbm_saved_bytes": full_keys - cache,
-            "hbm_saved_per_request": (full_keys - cache) // wl.batch,
-        }
-    if wl.hot_slots:
-        # the compute-plus-I/O model of the hot-buffer analysis: the measured
-        # step without its KV miss I/O, plus the missed rows' bytes over a
-        # link of each modelled bandwidth, the two not overlapping
-        stage = dict(zip(STAGES, stage_ms))
-        compute_us = (sum(stage_ms) - stage["miss_gather"]) * 1000
-        miss_bytes = sum(n_miss) * wl.qk_dim * 2
-        result["io_model"] = {
-            "compute_us_without_kv_io": round(compute_us, 1),
-            "kv_miss_bytes": miss_bytes,
-            "modeled_us": {str(bw): round(compute_us + miss_bytes / (bw * 1e3), 1)
-                           for bw in (64, 225, 900)},
-            "measured_us": round(ms_per_step * 1000, 1),
-            "measured_gather_us": round(stage["miss_gather"] * 1000, 1),
-            "gather_GBs": round(miss_bytes / (stage["miss_gather"] * 1e-3) / 1e9, 1),
-            "link": "pinned host (PCIe)" if wl.pool_on_host else "HBM",
-            "note": "stage times from the instrumented run (an event between stages)",
-        }
-    coarse_ops = 2 * wl.batch * wl.ctx * wl.idx_heads * wl.idx_dim
-    attn_flops = 2 * wl.batch * wl.q_heads * wl.topk * (wl.qk_dim + wl.v_dim)
-    attn_ms = stage_ms[STAGES.index("attention")]
-    result["mfma_util"] = {
-        "coarse_int8_TOPS": round(coarse_ops / (coarse_ms * 1e-3) / 1e12, 1),
-        "coarse_frac_of_5000": round(coarse_ops / (coarse_ms * 1e-3) / 1e12 / 5000.0, 4),
-        "attention_bf16_TFLOPs": round(attn_flops / (attn_ms * 1e-3) / 1e12, 1),
-        "attention_frac_of_2500": round(attn_flops / (attn_ms * 1e-3) / 1e12 / 2500.0, 4),
-    }
+    headline = wl.name == "decode-128k-b32"
+    result, probe_src = run_decode(ls, synth, wl, args.steps, args.warmup, args.replicas,
+                                   full=True, n_single=2 if args.cpu_sample else 0,
+                                   n_parallel=args.cpu_sample)
     result["copy_GBs"] = copy_bandwidth()
+    result["read_probe"] = read_probes(ls, wl, *probe_src)
+    del probe_src
+    gc.collect()
+    torch.cuda.empty_cache()
     if args.copy_calib > 0:
         copy_calibration(args.copy_calib << 20)
-    if args.cpu_sample > 0:
-        print("[bench] cpu baseline on %d requests" % args.cpu_sample, file=sys.stderr,
-              flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl, inp, q_attn, pool, pos2slot, hot,
-                                              min(args.cpu_sample, wl.batch))
+    if headline and args.extras:
+        # the other workloads, each a sub-object with its own metric; their
+        # inputs are built and freed in turn
+        extra = {}
+        for name, steps, warm, reps_, n1, npar in (
+                ("tiny-4k", 50, 5, 1, 1, 4),
+                ("decode-16k-b192", 10, 2, 1, 1, 16),
+                ("decode-950k-b4", 20, 3, 2, 0, 4)):
+            sub, _ = run_decode(ls, synth, synth.WORKLOADS[name], steps, warm, reps_,
+                                full=False, n_single=n1 if args.cpu_sample else 0,
+                                n_parallel=npar if args.cpu_sample else 0)
+            extra[name] = sub
+            gc.collect()
+            torch.cuda.empty_cache()
+        extra["prefill-4k-128k"] = run_prefill(ls, synth, synth.WORKLOADS["prefill-4k-128k"], 3,
+                                               1, n_rows_cpu=16 if args.cpu_sample else 0)
+        gc.collect()
+        torch.cuda.empty_cache()
+        result["workloads"] = extra
     print(json.dumps(result), flush=True)
 
 

@@ -75,7 +75,7 @@ extern "C" {
 typedef struct ihipStream_t *ls_stream_t;
 typedef struct ihipEvent_t *ls_event_t;
 
-#define LS_ABI_VERSION 4
+#define LS_ABI_VERSION 5
 
 enum {
     LS_OK = 0,
@@ -365,6 +365,20 @@ int ls_prefill_stream_layers(const ls_prefill_desc *desc, int32_t n_layers,
                              const int8_t *const *keys_host, int8_t *buf0_dev, int8_t *buf1_dev,
                              int32_t *const *topk_dev, void *ws_dev, size_t ws_bytes,
                              ls_stream_t stream, ls_stream_t copy_stream);
+
+/* ---------------------------------------------------------- measurement -- */
+
+/* Memory-read probe: reads device memory the way the decode step does and
+ * folds it into a value that decides a rare write of *sink_dev (one uint32),
+ * computing nothing of the method.  rows_dev == NULL: a streaming read of
+ * [base_dev, base_dev + bytes) (bytes a multiple of 16) -- the coarse pass's
+ * pattern.  rows_dev != NULL: a gather of the n_rows rows rows_dev[i] of
+ * row_bytes each (128 or 1152, else LS_E_UNSUPPORTED) at base_dev +
+ * rows_dev[i] * row_bytes, ids clamped into the range's whole rows -- the
+ * refinement's key rows and the attention's latent rows.  Timing it gives the bandwidth the hardware
+ * delivers to each pattern, the context of the roofline figures.           */
+int ls_read_probe(const void *base_dev, uint64_t bytes, const int32_t *rows_dev, int64_t n_rows,
+                  int32_t row_bytes, uint32_t *sink_dev, ls_stream_t stream);
 
 #ifdef __cplusplus
 }

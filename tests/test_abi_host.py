@@ -56,7 +56,7 @@ def test_struct_layouts_match_header(tmp_path):
 
 
 def test_version_and_error_string(lib):
-    assert lib.ls_abi_version() == ls.ABI_VERSION == 4
+    assert lib.ls_abi_version() == ls.ABI_VERSION == 5
     assert isinstance(lib.ls_last_error(), bytes)
 
 
@@ -313,3 +313,15 @@ def test_shapes_whose_32_bit_offsets_would_wrap_are_rejected(lib):
     assert rc == ls.LS_E_UNSUPPORTED and b"2^31" in lib.ls_last_error()
     p = ls.PrefillDesc(16, 1 << 23, 0, 64, 128, 64)         # 2^30: accepted by the shape check
     assert lib.ls_workspace_size(ls.OP_PREFILL, ctypes.byref(p)) > 0
+
+
+def test_read_probe_validation(lib):
+    # measurement helper: checked on the host like every entry point
+    assert lib.ls_read_probe(None, 1024, None, 0, 0, FAKE, None) == ls.LS_E_ARG
+    assert lib.ls_read_probe(FAKE, 1000, None, 0, 0, FAKE, None) == ls.LS_E_ARG
+    assert b"multiple of 16" in lib.ls_last_error()
+    assert lib.ls_read_probe(FAKE, 1024, FAKE, 4, 100, FAKE, None) == ls.LS_E_ARG
+    assert lib.ls_read_probe(FAKE, 1024, FAKE, 4, 2048, FAKE, None) == ls.LS_E_ARG
+    assert b"whole row" in lib.ls_last_error()
+    assert lib.ls_read_probe(FAKE, 1024, FAKE, 4, 256, FAKE, None) == ls.LS_E_UNSUPPORTED
+    assert lib.ls_read_probe(FAKE, 1024, None, 0, 0, None, None) == ls.LS_E_ARG

@@ -17,6 +17,7 @@ Stages (see include/ls.h for the exact contracts):
   cache_commit         least-recently-used commit of one step's entries
   append_token         the new token's keys and KV row at ctx_len, ctx_len += 1
   prefill_index_topk / prefill_stream_layers   prefill-chunk indexer
+  read_probe           memory-read bandwidth probe (measurement context only)
 """
 from __future__ import annotations
 
@@ -33,7 +34,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "ls.h")
 LS_OK, LS_E_ARG, LS_E_UNSUPPORTED, LS_E_WORKSPACE, LS_E_HIP = 0, -1, -2, -3, -4
 OP_COARSE, OP_REFINE, OP_HOT, OP_ATTN, OP_STEP, OP_PREFILL = 1, 2, 3, 4, 5, 6
 STEP_EVENTS = 7
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _I32, _I64, _F32, _P = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
 
@@ -118,9 +119,11 @@ def load():
     L.ls_cache_commit.argtypes = [_I32, _I32, _I32, _I32, ctypes.c_uint32, _P, _P, _P, _P, _P,
                                   _P, _P]
     L.ls_append_token.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P]
-    for name in ("ls_cache_commit", "ls_append_token", "ls_pack_coarse", "ls_index_coarse", "ls_refine_topk", "ls_hot_gather",
-                 "ls_sparse_attn_decode", "ls_decode_step", "ls_prefill_index_topk",
-                 "ls_prefill_stream_layers", "ls_workspace_init"):
+    L.ls_read_probe.argtypes = [_P, ctypes.c_uint64, _P, _I64, _I32, _P, _P]
+    for name in ("ls_cache_commit", "ls_append_token", "ls_pack_coarse", "ls_index_coarse",
+                 "ls_refine_topk", "ls_hot_gather", "ls_sparse_attn_decode", "ls_decode_step",
+                 "ls_prefill_index_topk", "ls_prefill_stream_layers", "ls_workspace_init",
+                 "ls_read_probe"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -427,8 +430,8 @@ class DecodeStep:
             arr = (ctypes.c_void_p * STEP_EVENTS)(*[e.cuda_event if e is not None else None
                                                     for e in events])
             io.stage_events = ctypes.cast(arr, ctypes.c_void_p)
-        _check(load().ls_decode_step(ctypes.byref(self.desc), ctypes.byref(io), _p(self.ws),
-                                     self.ws.numel(), _stream()))
+        _check(load().ls_decode_step(ctypes.byref(self.desc), ctypes.byref(io),
+                                     _p(self.ws), self.ws.numel(), _stream()))
         return self.out, self.lse
 
 
@@ -532,3 +535,21 @@ def prefill_stream_layers(qs, ws_, keys_host, q_pos0: int, topk: int, buf0=None,
                                            _p(buf0), _p(buf1), arr(outs), _p(ws), ws.numel(),
                                            _stream(), ctypes.c_void_p(copy_stream.cuda_stream)))
     return outs
+
+
+def read_probe(base, rows=None, row_bytes=0, sink=None):
+    """ls_read_probe: a streaming read of the whole tensor base (rows None) or
+    a gather of the rows rows (int32, device) of row_bytes each; returns the
+    sink word (a device tensor, for the caller to synchronise on)."""
+    if not base.is_cuda or not base.is_contiguous():
+        raise ValueError("base must be a contiguous device tensor")
+    if sink is None:
+        sink = torch.zeros((1,), dtype=torch.int32, device=base.device)
+    nbytes = base.numel() * base.element_size()
+    if rows is not None:
+        _need(rows, torch.int32, "rows")
+        n, rp = rows.numel(), _p(rows)
+    else:
+        n, rp = 0, None
+    _check(load().ls_read_probe(_p(base), nbytes, rp, n, int(row_bytes), _p(sink), _stream()))
+    return sink

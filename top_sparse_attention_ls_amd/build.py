@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libls.so")
 SOURCES = ["ls_abi.hip", "k_index.hip", "k_select.hip", "k_refine.hip", "k_attn.hip",
-           "k_commit.hip", "k_prefill.hip"]
+           "k_commit.hip", "k_prefill.hip", "k_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -107,13 +107,21 @@ __device__ __forceinline__ void wait_tiles_ahead(int ahead) {
   }
 }
 
-template <int DQK, int DV, int NBUF>
+// The miss gather folded into the attention (GATHER, pool in device memory).
+// A selected row that missed the hot buffer is read by the tile DMA straight
+// from the pool (src[i] holds its pool position), so no workgroup waits for a
+// copy.  The copy itself -- hot[row of miss j] := pool[miss_pos[j]], the row
+// being the scratch row hot_slots + j or the victim slot a commit gave it --
+// is shared out over the launch: workgroup (split s) copies misses s,
+// s + n_splits, ... in its prologue, its pool reads in flight with the first
+// tiles' DMA.  No workgroup of the launch reads the rows being written.
+template <int DQK, int DV, int NBUF, bool GATHER>
 __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ rows, uint16_t* __restrict__ out, float* __restrict__ lse,
     uint16_t* __restrict__ part_o, float* __restrict__ part_lse, int Hq, int K,
     int64_t rows_per_req, int64_t row_stride, float scale_log2, int n_splits,
-    int rows_per_split) {
+    int rows_per_split, AttnGather ga) {
   constexpr int NW = kAttnWaves;
   constexpr int QK_STEPS = DQK / 16;
   constexpr int DT = DV / 32;
@@ -141,44 +149,121 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
   const int n_rows = max(i_end - i_begin, 0);
   const int n_tiles = (n_rows + kTileR - 1) / kTileR;
   const int32_t* rq = rows + (size_t)b * K;
+  const int32_t* sq = GATHER ? ga.src + (size_t)b * K : nullptr;
   const uint16_t* kvb = kv + (size_t)b * rows_per_req * row_stride;
+  const uint16_t* poolb = GATHER ? ga.pool + (size_t)b * ga.pool_rows * row_stride : nullptr;
   // the tile row this lane loads in every DMA instruction, and its chunk parity
   const int dma_row = (l & 31) ^ (half << 3);
-  // row id at position i of the split, clamped into the request's list
-  // (loads are unconditional; positions past the split are padding)
-  auto rid_at = [&](int i) { return rq[min(i_begin + min(i, max(n_rows - 1, 0)), K - 1)]; };
-  // what a tile position holds: its row, or -1 for padding and ids out of range
-  auto rid_valid = [&](int i, int32_t r) { return (i < n_rows && r >= 0 && r < rows_per_req) ? r : -1; };
+  // row id (and, gathering, pool position) at position i of the split,
+  // clamped into the request's list (loads are unconditional; positions
+  // past the split are padding)
+  auto at = [&](int i) { return min(i_begin + min(i, max(n_rows - 1, 0)), K - 1); };
+  auto rid_at = [&](int i) { return rq[at(i)]; };
+  auto src_at = [&](int i) { return GATHER ? sq[at(i)] : -1; };
+  // What a tile position holds, as one code: >= 0 a hot-buffer row, <= -2 the
+  // pool row -(code + 2) of a missed entry, -1 padding (and ids out of range)
+  auto code_of = [&](int i, int32_t r, int32_t sp) {
+    if (GATHER && i < n_rows && sp >= 0 && sp < ga.pool_rows) return -2 - sp;
+    return (i < n_rows && r >= 0 && r < rows_per_req) ? r : -1;
+  };
 
-  // Tile DMA of tile t, this lane's row being rid (padding loads row 0):
-  // wave w issues instructions k = w, w + NW, ...  (lds_dma16: the waits on it
-  // are the explicit vmcnt waits below)
-  auto issue_dma_row = [&](int t, int32_t rid) {
-    const uint8_t* src = (const uint8_t*)(kvb + (size_t)(rid >= 0 ? rid : 0) * row_stride) +
-                         16 * (2 * w + half);
+  // Tile DMA of tile t, this lane's row given by its code (padding loads
+  // hot row 0): wave w issues instructions k = w, w + NW, ...  (lds_dma16:
+  // the waits on it are the explicit vmcnt waits below)
+  auto issue_dma_row = [&](int t, int32_t code) {
+    const uint16_t* rowp = kvb + (size_t)(code >= 0 ? code : 0) * row_stride;
+    if (GATHER && code <= -2) rowp = poolb + (size_t)(-2 - code) * row_stride;
+    const uint8_t* src = (const uint8_t*)rowp + 16 * (2 * w + half);
     const uint32_t dst = lds_addr(&tiles[t % NBUF][0]) + 1024u * w;
 #pragma unroll
     for (int j = 0; j < DMA_PER_WAVE; j++) lds_dma16(src + 32 * NW * j, dst + 1024u * NW * j);
   };
   auto issue_dma = [&](int t) { issue_dma_row(t, rid_lds[t * kTileR + dma_row]); };
 
-  // Prologue in two round trips.  First each lane's own DMA rows of the
-  // first tiles, whose DMA then starts at once; then the split's row ids (to
-  // be staged in LDS) and the query, which load while that DMA is in flight.
-  {
-    int32_t r0[NBUF - 1];
+  // The copy share of this workgroup (GATHER): its k-th miss is miss
+  // j = split + n_splits k; 16-byte piece f of the share is piece f % CH of
+  // that miss's row.  Pieces go to threads f = tid + 256 u, kCopyU per round.
+  // Reads and writes go through buffer resources over the request's pool and
+  // hot-buffer blocks: a piece past the share gets an offset beyond the
+  // block, so its load returns zero and its store is dropped, with no branch.
+  constexpr int kCopyU = 16;
+  constexpr int kCopyRound = NW * 64 * kCopyU;
+  int my_pieces = 0;
+  int32_t cp_pos[kCopyU], cp_dst[kCopyU];
+  uint4 cp_v[kCopyU];
+  const uint32_t pool_block = GATHER ? (uint32_t)(ga.pool_rows * row_stride * 2) : 0u;
+  const uint32_t hot_block = GATHER ? (uint32_t)(rows_per_req * row_stride * 2) : 0u;
+  auto copy_list = [&](int f0) {
 #pragma unroll
-    for (int t = 0; t < NBUF - 1; t++) r0[t] = rid_at(t * kTileR + dma_row);
+    for (int u = 0; u < kCopyU; u++) {
+      const int f = f0 + (int)threadIdx.x + NW * 64 * u;
+      const int jj = min(split + n_splits * (f / CH), K - 1);
+      cp_pos[u] = ga.miss_pos[(size_t)b * K + jj];
+      cp_dst[u] = ga.miss_dst ? ga.miss_dst[(size_t)b * K + jj] : -1;
+    }
+  };
+  auto copy_load = [&](int f0) {
+    const __amdgpu_buffer_rsrc_t pres = buffer_rsrc(poolb, pool_block);
+#pragma unroll
+    for (int u = 0; u < kCopyU; u++) {
+      const int f = f0 + (int)threadIdx.x + NW * 64 * u;
+      const int c = f % CH;
+      const uint32_t p = (uint32_t)min(max(cp_pos[u], 0), (int)ga.pool_rows - 1);
+      const uint32_t off = f < my_pieces ? p * (uint32_t)(row_stride * 2) + 16u * c : pool_block;
+      cp_v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(pres, off, 0, 0));
+    }
+  };
+  auto copy_store = [&](int f0) {
+    const __amdgpu_buffer_rsrc_t hres = buffer_rsrc(kvb, hot_block);
+#pragma unroll
+    for (int u = 0; u < kCopyU; u++) {
+      const int f = f0 + (int)threadIdx.x + NW * 64 * u;
+      const int c = f % CH;
+      const int j = split + n_splits * (f / CH);
+      const int row = (cp_dst[u] >= 0 && cp_dst[u] < ga.hot_slots) ? cp_dst[u] : ga.hot_slots + j;
+      const uint32_t off =
+          f < my_pieces ? (uint32_t)row * (uint32_t)(row_stride * 2) + 16u * c : hot_block;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, cp_v[u]), hres, off, 0, 0);
+    }
+  };
+
+  // Prologue in two round trips.  First each lane's own DMA rows of the
+  // first tiles (and, gathering, the miss count and this workgroup's first
+  // round of the miss list), whose DMA then starts at once; then the copy's
+  // pool reads, the split's row ids (to be staged in LDS) and the query,
+  // which load while that DMA is in flight.
+  {
+    int32_t r0[NBUF - 1], s0[NBUF - 1];
+    int nm_raw = 0;
+#pragma unroll
+    for (int t = 0; t < NBUF - 1; t++) {
+      r0[t] = rid_at(t * kTileR + dma_row);
+      s0[t] = src_at(t * kTileR + dma_row);
+    }
+    if (GATHER) {
+      nm_raw = ga.n_miss[b];
+      copy_list(0);
+    }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 #pragma unroll
     for (int t = 0; t < NBUF - 1; t++)
-      if (t < n_tiles) issue_dma_row(t, rid_valid(t * kTileR + dma_row, r0[t]));
+      if (t < n_tiles) issue_dma_row(t, code_of(t * kTileR + dma_row, r0[t], s0[t]));
+    if (GATHER) {
+      // misses of this split (a list never holds more than K misses)
+      const int nm = min(max(nm_raw, 0), K);
+      const int my = nm > split ? (nm - 1 - split) / n_splits + 1 : 0;
+      my_pieces = my * CH;
+      copy_load(0);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   constexpr int kRidIters = (kMaxSplitRows + kTileR + NW * 64 - 1) / (NW * 64);
-  int32_t rv[kRidIters];
+  int32_t rv[kRidIters], sv[kRidIters];
 #pragma unroll
-  for (int k = 0; k < kRidIters; k++) rv[k] = rid_at(threadIdx.x + k * NW * 64);
+  for (int k = 0; k < kRidIters; k++) {
+    rv[k] = rid_at(threadIdx.x + k * NW * 64);
+    sv[k] = src_at(threadIdx.x + k * NW * 64);
+  }
   // B operand of S^T = K Q^T: head n, dims 16 ks + 8 half .. +7 (loaded
   // unconditionally from a clamped head, then selected)
   v8bf qB[QK_STEPS];
@@ -195,10 +280,20 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
   // wait on every iteration, which would also drain the tile DMA in flight);
   // the loop then waits for each tile's DMA alone.
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  if (GATHER) {
+    // the copy's first round has landed: store it; further rounds (only at
+    // high miss rates) load their list and rows here, one round trip each
+    copy_store(0);
+    for (int f0 = kCopyRound; f0 < my_pieces; f0 += kCopyRound) {
+      copy_list(f0);
+      copy_load(f0);
+      copy_store(f0);
+    }
+  }
 #pragma unroll
   for (int k = 0; k < kRidIters; k++) {
     const int i = threadIdx.x + k * NW * 64;
-    if (i < n_tiles * kTileR) rid_lds[i] = rid_valid(i, rv[k]);
+    if (i < n_tiles * kTileR) rid_lds[i] = code_of(i, rv[k], sv[k]);
   }
   __shared__ int redo;
   if (threadIdx.x == 0) redo = 0;
@@ -242,7 +337,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
     wg_barrier();  // tile t is in LDS for every wave
     const uint8_t* cur = &tiles[t % NBUF][0];
     const uint32_t vmask =
-        (uint32_t)__ballot(l < kTileR && rid_lds[t * kTileR + (l & 31)] >= 0);
+        (uint32_t)__ballot(l < kTileR && rid_lds[t * kTileR + (l & 31)] != -1);
 
     // S^T = K Q^T (32 rows x 32 heads): operand reads run 4 steps ahead of
     // their MFMAs, and even/odd steps feed two accumulators so consecutive
@@ -622,10 +717,20 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
     if (rps > kMaxSplitRows) return hipErrorInvalidValue;
     const int hpw = kHeadsPerWave * kAttnWaves;
     dim3 grid(a.n_splits, (a.Hq + hpw - 1) / hpw, a.B);
-    hipLaunchKernelGGL((k_attn_mfma<576, 512, kAttnBufs>), grid, dim3(64 * kAttnWaves), 0, st,
-                       a.q, a.k, a.rows,
-                       a.out, a.lse, a.part_o, a.part_lse, a.Hq, a.K, a.rows_per_req,
-                       a.row_stride, a.scale * kLog2e, a.n_splits, rps);
+    if (a.gather.src) {
+      // the gathering form writes the hot buffer: its grid must cover each
+      // split once (one head group)
+      if (grid.y != 1) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((k_attn_mfma<576, 512, kAttnBufs, true>), grid, dim3(64 * kAttnWaves),
+                         0, st, a.q, a.k, a.rows, a.out, a.lse, a.part_o, a.part_lse, a.Hq, a.K,
+                         a.rows_per_req, a.row_stride, a.scale * kLog2e, a.n_splits, rps,
+                         a.gather);
+    } else {
+      hipLaunchKernelGGL((k_attn_mfma<576, 512, kAttnBufs, false>), grid, dim3(64 * kAttnWaves),
+                         0, st, a.q, a.k, a.rows, a.out, a.lse, a.part_o, a.part_lse, a.Hq, a.K,
+                         a.rows_per_req, a.row_stride, a.scale * kLog2e, a.n_splits, rps,
+                         a.gather);
+    }
   } else {
     hipLaunchKernelGGL(k_attn_valu, dim3(a.Hq, a.B), dim3(256), 0, st, a.q, a.k, a.v, a.rows,
                        a.out, a.lse, a.Hq, a.n_kv, a.qk_dim, a.v_dim, a.K, a.rows_per_req,

@@ -200,7 +200,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
     const int32_t* __restrict__ cslot, int32_t* __restrict__ topk,
     int64_t* __restrict__ topk_score, const int32_t* __restrict__ pos2slot,
     int32_t* __restrict__ rows, int32_t* __restrict__ n_miss, int32_t* __restrict__ miss_pos,
-    int hot_slots, int max_ctx, int C, int K) {
+    int32_t* __restrict__ srcw, int hot_slots, int max_ctx, int C, int K) {
   constexpr int NT = kTopkThreads;
   constexpr int NW = NT / kWave;
   constexpr int BPT = kFineBinsPad / NT;  // bins per thread
@@ -380,6 +380,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
   int64_t* sb = topk_score ? topk_score + (size_t)b * K : nullptr;
   int32_t* rb = rows ? rows + (size_t)b * K : nullptr;
   int32_t* mb = miss_pos ? miss_pos + (size_t)b * K : nullptr;
+  int32_t* xb = srcw ? srcw + (size_t)b * K : nullptr;
 #pragma unroll
   for (int k = 0; k < PER; k++) {
     if (k != m) continue;  // this workgroup's slice (workgroup-uniform)
@@ -396,6 +397,8 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
         rb[o] = hot_slots + (int32_t)om;
         mb[om] = c[k];
       }
+      // the pool position of a miss (for a gathering attention), -1 for a hit
+      if (xb) xb[o] = slot[k] >= 0 ? -1 : c[k];
     }
   }
   if (m == 0) {
@@ -403,6 +406,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
       tb[j] = -1;
       if (sb) sb[j] = 0;
       if (rb) rb[j] = -1;
+      if (xb) xb[j] = -1;
     }
     if (tid == 0 && n_miss) n_miss[b] = resolve ? (int32_t)(tot >> 16) : 0;
   }
@@ -412,7 +416,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(
     const int32_t* __restrict__ cand, const int64_t* __restrict__ fs, int32_t* __restrict__ topk,
     int64_t* __restrict__ topk_score, const int32_t* __restrict__ pos2slot,
     int32_t* __restrict__ rows, int32_t* __restrict__ n_miss, int32_t* __restrict__ miss_pos,
-    int hot_slots, int max_ctx, int C, int K) {
+    int32_t* __restrict__ srcw, int hot_slots, int max_ctx, int C, int K) {
   constexpr int NT = kTopkThreads;
   __shared__ uint32_t scan_sh[NT / kWave];
   __shared__ SelectShared ssh;
@@ -467,6 +471,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(
   int64_t* sb = topk_score ? topk_score + (size_t)b * K : nullptr;
   int32_t* rb = rows ? rows + (size_t)b * K : nullptr;
   int32_t* mb = miss_pos ? miss_pos + (size_t)b * K : nullptr;
+  int32_t* xb = srcw ? srcw + (size_t)b * K : nullptr;
   for (int i = i0; i < i1; i++) {
     const int32_t p = cc[i];
     if (!(all || keep(thr, key_of_i64(ff[i]), (uint32_t)p))) continue;
@@ -482,6 +487,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(
           mb[o_miss] = p;
           o_miss++;
         }
+        if (xb) xb[o_sel] = slot >= 0 ? -1 : p;
       }
     }
     o_sel++;
@@ -490,6 +496,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(
     tb[j] = -1;
     if (sb) sb[j] = 0;
     if (rb) rb[j] = -1;
+    if (xb) xb[j] = -1;
   }
   if (tid == 0 && n_miss) n_miss[b] = p2s ? (int32_t)tot_miss : 0;
 }
@@ -522,9 +529,10 @@ hipError_t launch_refine_topk(const int8_t* q, const int8_t* w, const KeySource&
 #undef LS_REFINE_KC
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  int32_t* srcw = pos2slot ? ws.src : nullptr;
 #define LS_TOPK(P)                                                                           \
   hipLaunchKernelGGL(k_topk_hist<P>, dim3(P, B), dim3(kTopkThreads), 0, st, cand, ws.fs,       \
-                     ws.slot, topk, topk_score, pos2slot, rows, n_miss, ws.miss_pos,           \
+                     ws.slot, topk, topk_score, pos2slot, rows, n_miss, ws.miss_pos, srcw,     \
                      hot_slots, max_ctx, C, K)
   if (C <= kTopkThreads) LS_TOPK(1);
   else if (C <= 2 * kTopkThreads) LS_TOPK(2);
@@ -533,7 +541,7 @@ hipError_t launch_refine_topk(const int8_t* q, const int8_t* w, const KeySource&
   else if (C <= 16 * kTopkThreads) LS_TOPK(16);
   else
     hipLaunchKernelGGL(k_topk, dim3(B), dim3(kTopkThreads), 0, st, cand, ws.fs, topk, topk_score,
-                       pos2slot, rows, n_miss, ws.miss_pos, hot_slots, max_ctx, C, K);
+                       pos2slot, rows, n_miss, ws.miss_pos, srcw, hot_slots, max_ctx, C, K);
 #undef LS_TOPK
   return hipGetLastError();
 }

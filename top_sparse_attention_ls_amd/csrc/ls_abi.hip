@@ -175,6 +175,7 @@ void carve_refine(Carve& c, const ls_idx_desc* d, ls::RefineWS* ws) {
   w.miss_pos = c.take<int32_t>(B * d->topk);
   w.kcode = c.take<int32_t>(B * d->n_cand);
   w.miss_dst = c.take<int32_t>(B * d->topk);
+  w.src = c.take<int32_t>(B * d->topk);
   if (ws) *ws = w;
 }
 
@@ -567,6 +568,7 @@ static int attn_args(const ls_attn_desc* d, const void* q, const void* k, const 
   if (!mfma && d->topk > 8192)
     return fail(LS_E_UNSUPPORTED, "topk > 8192 needs the latent (576/512, one kv head) layout");
   a->n_splits = attn_splits(d, k, v);
+  a->gather = ls::AttnGather{};  // no gather unless the step folds it in
   (void)ws;
   return LS_OK;
 }
@@ -603,8 +605,15 @@ int ls_sparse_attn_decode(const ls_attn_desc* desc, const void* q_dev, const voi
   return run_attention(a, (hipStream_t)stream, nullptr);
 }
 
-int ls_decode_step(const ls_step_desc* desc, const ls_step_io* io, void* ws_dev,
-                   size_t ws_bytes, ls_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The whole step on workspace ws_dev.  clear_bytes > 0: a fill kernel first
+// zeroes ws_dev[0, clear_bytes) -- after every check, so that a rejected call
+// enqueues nothing.
+int decode_step_impl(const ls_step_desc* desc, const ls_step_io* io, void* ws_dev,
+                     size_t ws_bytes, ls_stream_t stream, size_t clear_bytes) {
   if (!desc) return fail(LS_E_ARG, "null step descriptor");
   if (!io) return fail(LS_E_ARG, "null step io");
   const ls_idx_desc* id = &desc->idx;
@@ -690,6 +699,7 @@ int ls_decode_step(const ls_step_desc* desc, const ls_step_io* io, void* ws_dev,
 
   hipStream_t st = (hipStream_t)stream;
   ls_event_t* ev = io->stage_events;
+  if (clear_bytes) LS_HIP(ls::launch_fill_zero(ws_dev, clear_bytes, st), "scratch clear");
   if (ev && ev[0]) LS_HIP(hipEventRecord((hipEvent_t)ev[0], st), "event record");
   LS_TRY(run_coarse(id, io->q_idx_dev, io->w_idx_dev, io->kc_dev, io->ctx_len_dev, io->cand_dev,
                     cws, st, ev));
@@ -723,15 +733,71 @@ int ls_decode_step(const ls_step_desc* desc, const ls_step_io* io, void* ws_dev,
                                    io->rows_dev,
                                    nullptr, st),
            "hot-buffer commit launch");
-  if (desc->use_hot)
+  // With the pool in device memory the attention itself reads the misses
+  // from the pool and copies them into their hot-buffer rows (one launch
+  // fewer); a pool in host memory keeps the separate gather, so that the
+  // attention never waits on PCIe.
+  const bool fuse_gather = desc->use_hot && !desc->hot.pool_on_host &&
+                           ls::attn_uses_mfma(ad->n_q_heads, ad->n_kv_heads, ad->qk_dim,
+                                              ad->v_dim, io->hot_kv_dev, io->hot_kv_dev) &&
+                           ad->n_q_heads <= 128 &&
+                           (int64_t)id->max_ctx * desc->hot.row_elems * 2 < ((int64_t)1 << 32) &&
+                           (int64_t)(desc->hot.hot_slots + id->topk) * desc->hot.row_elems * 2 <
+                               ((int64_t)1 << 32);
+  if (fuse_gather) {
+    a.gather.src = rws.src;
+    a.gather.pool = (const uint16_t*)pool;
+    a.gather.pool_rows = id->max_ctx;
+    a.gather.miss_pos = rws.miss_pos;
+    a.gather.n_miss = io->n_miss_dev;
+    a.gather.miss_dst = cm->hot ? rws.miss_dst : nullptr;
+    a.gather.hot_slots = desc->hot.hot_slots;
+  } else if (desc->use_hot) {
     LS_HIP(ls::launch_hot_gather(rws.miss_pos, io->n_miss_dev, cm->hot ? rws.miss_dst : nullptr,
                                  pool, io->hot_kv_dev, desc->hot.hot_slots, id->batch,
                                  id->max_ctx, id->topk, desc->hot.row_elems,
                                  desc->hot.pool_on_host != 0, st),
            "miss gather launch");
+  }
   if (ev && ev[4]) LS_HIP(hipEventRecord((hipEvent_t)ev[4], st), "event record");
   LS_TRY(run_attention(a, st, ev));
   if (ev && ev[6]) LS_HIP(hipEventRecord((hipEvent_t)ev[6], st), "event record");
+  return LS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ls_decode_step(const ls_step_desc* desc, const ls_step_io* io, void* ws_dev,
+                   size_t ws_bytes, ls_stream_t stream) {
+  try {
+    return decode_step_impl(desc, io, ws_dev, ws_bytes, stream, 0);
+  } catch (...) {
+    return fail(LS_E_ARG, "internal error");
+  }
+}
+
+int ls_read_probe(const void* base_dev, uint64_t bytes, const int32_t* rows_dev, int64_t n_rows,
+                  int32_t row_bytes, uint32_t* sink_dev, ls_stream_t stream) {
+  LS_NONNULL(base_dev);
+  LS_NONNULL(sink_dev);
+  LS_ALIGNED(base_dev);
+  if (bytes % 16 != 0) return fail(LS_E_ARG, "bytes must be a multiple of 16");
+  if (rows_dev) {
+    if (row_bytes < 16 || row_bytes % 16 != 0)
+      return fail(LS_E_ARG, "row_bytes must be a positive multiple of 16 (got %d)", row_bytes);
+    if (n_rows < 0) return fail(LS_E_ARG, "n_rows must be >= 0");
+    if ((uint64_t)row_bytes > bytes) return fail(LS_E_ARG, "the range holds no whole row");
+    if (row_bytes != 128 && row_bytes != 1152)
+      return fail(LS_E_UNSUPPORTED, "row_bytes must be 128 or 1152 (the step's row sizes)");
+    if ((uint64_t)n_rows * (row_bytes / 16) >= ((uint64_t)1 << 31) ||
+        bytes / (uint64_t)row_bytes >= ((uint64_t)1 << 31))
+      return fail(LS_E_UNSUPPORTED, "too many rows for the probe");
+  }
+  LS_HIP(ls::launch_read_probe(base_dev, bytes, rows_dev, n_rows, row_bytes, sink_dev,
+                               (hipStream_t)stream),
+         "read probe launch");
   return LS_OK;
 }
 

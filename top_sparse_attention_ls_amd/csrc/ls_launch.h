@@ -76,6 +76,7 @@ struct RefineWS {
   int32_t* miss_pos;   // [B, topk]
   int32_t* kcode;      // [B, n_cand] key-cache commit codes
   int32_t* miss_dst;   // [B, topk] hot-buffer slot of each inserted miss, or -1
+  int32_t* src;        // [B, topk] pool position of each selected miss, -1 otherwise
 };
 
 // Cache commit (least recently used), one workgroup per request.
@@ -135,6 +136,21 @@ hipError_t launch_hot_gather(const int32_t* miss_pos, const int32_t* n_miss,
                              int B, int max_ctx, int K, int row_elems, bool pool_on_host,
                              hipStream_t st);
 
+// The miss gather folded into the latent attention (pool in device memory):
+// src [B, K] is the pool position of each selected entry that missed the hot
+// buffer (-1 for hits and padding); miss_pos / n_miss / miss_dst are the
+// resolve's miss list, count and (after a hot-buffer commit) destination
+// slots.  src == nullptr: no gather, the attention reads the hot buffer only.
+struct AttnGather {
+  const int32_t* src;
+  const uint16_t* pool;
+  int64_t pool_rows;        // rows per request in the pool (max_ctx)
+  const int32_t* miss_pos;
+  const int32_t* n_miss;
+  const int32_t* miss_dst;  // nullable
+  int hot_slots;
+};
+
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -148,6 +164,7 @@ struct AttnArgs {
   int64_t rows_per_req, row_stride, head_stride;
   float scale;
   int n_splits;
+  AttnGather gather;  // zero-initialised: no gather
 };
 
 // Rows one workgroup of the latent attention kernel handles at most; the
@@ -159,5 +176,11 @@ bool attn_uses_mfma(int Hq, int n_kv, int qk_dim, int v_dim, const void* k, cons
 int attn_auto_splits(int B, int Hq, int K, bool mfma);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
 hipError_t launch_combine(const AttnArgs& a, hipStream_t st);
+
+// Memory-read probe (measurement only): a streaming read of [base, base +
+// bytes) when rows == nullptr, else a gather of rows rows[0 .. n_rows) of
+// row_bytes each; the data is folded into *sink.
+hipError_t launch_read_probe(const void* base, uint64_t bytes, const int32_t* rows,
+                             int64_t n_rows, int row_bytes, uint32_t* sink, hipStream_t st);
 
 }  // namespace ls

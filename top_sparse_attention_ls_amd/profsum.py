@@ -12,6 +12,13 @@
       reads for the plain N MiB device copy that bench.py --copy-calib runs
       last.  Writes profiles/k_coarse.NAME.traffic.json (read by bench.py,
       keyed to the kernel's source hash) and a .md beside it.
+
+  python -m top_sparse_attention_ls_amd.profsum counters PASS_CSV ... \
+      --copy-mib N --workload NAME --out profiles/NAME.md --cmd "..." ...
+      every counter of every pass (one rocprofv3 --pmc run each), averaged
+      per launch for each of the library's kernels; FETCH_SIZE / WRITE_SIZE
+      scaled by the calibration copy as above and set against each kernel's
+      algorithmic bytes per launch at that workload.
 """
 from __future__ import annotations
 
@@ -118,6 +125,103 @@ def cmd_traffic(args):
     print("\n".join(lines))
 
 
+# Algorithmic bytes per launch of each decode-step kernel, from the parts of
+# the step's byte count (bench.algorithmic_bytes): the workload's own reads
+# and writes, never the workspace.
+KERNEL_PARTS = {
+    "k_coarse": ("coarse_keys", "idx_q_w"),
+    "k_refine": ("refine_keys", "slot_table"),
+    "k_hot_gather": ("miss_read", "miss_write"),
+    "k_attn_mfma": ("kv_rows", "attn_q"),
+    "k_attn_fused": ("kv_rows", "attn_q", "miss_read", "miss_write"),
+    "k_combine": ("out_lse",),
+}
+
+
+def kernel_algorithmic_bytes(workload):
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+    from top_sparse_attention_ls_amd import synth
+    wl = synth.WORKLOADS[workload]
+    n_miss = round(wl.miss_rate * wl.topk) * wl.batch if wl.hot_slots else 0
+    ab = bench.algorithmic_bytes(wl, n_miss)
+    return {k: sum(ab[p] for p in parts) for k, parts in KERNEL_PARTS.items()}
+
+
+def _all_counters(path):
+    """{(kernel short name, counter): [values in dispatch order]}"""
+    out = {}
+    rows = []
+    for r in csv.DictReader(open(path)):
+        rows.append((int(r["Dispatch_Id"]), short_name(r["Kernel_Name"]), r["Counter_Name"],
+                     float(r["Counter_Value"])))
+    rows.sort()
+    for _, k, c, v in rows:
+        out.setdefault((k, c), []).append(v)
+    return out
+
+
+def cmd_counters(args):
+    copy_kib = args.copy_mib * 1024.0
+    per = {}     # kernel -> counter -> average per launch (later half of the launches)
+    launches = {}
+    factors = {}
+    for path in args.passes:
+        vals = _all_counters(path)
+        for (k, c), v in vals.items():
+            if k == COPY_KERNEL or k.endswith(COPY_KERNEL):
+                if c in ("FETCH_SIZE", "WRITE_SIZE") and len(v) >= 2:
+                    factors[c] = copy_kib / (sum(v[-2:]) / 2)
+                continue
+            if not k.startswith("ls::"):
+                continue
+            steady = v[len(v) // 2:] if len(v) > 2 else v
+            per.setdefault(k, {})[c] = sum(steady) / len(steady)
+            launches[k] = max(launches.get(k, 0), len(v))
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        f = factors.get(c)
+        if f is not None and not (0.4 < f < 2.6):
+            raise SystemExit("%s calibration factor %.3f is implausible" % (c, f))
+    alg = kernel_algorithmic_bytes(args.workload) if args.workload else {}
+    res = {"workload": args.workload, "commands": args.cmd, "calibration_factors": factors,
+           "kernels": {}}
+    counters = sorted({c for d in per.values() for c in d})
+    lines = ["# Per-kernel counters, %s" % args.workload, "",
+             "Commands (one rocprofv3 --pmc pass each):", "", "```"] + args.cmd + ["```", ""]
+    if factors:
+        lines += ["FETCH_SIZE / WRITE_SIZE are KiB per dispatch, scaled by what each reads for a "
+                  "plain %d MiB device copy in the same run (factors: %s)." % (
+                      args.copy_mib, ", ".join("%s %.3f" % kv for kv in sorted(factors.items()))),
+                  ""]
+    hdr = ["kernel", "launches"]
+    if "FETCH_SIZE" in counters and "WRITE_SIZE" in counters:
+        hdr += ["HBM bytes / launch (fetch + write)", "algorithmic bytes", "ratio"]
+    other = [c for c in counters if c not in ("FETCH_SIZE", "WRITE_SIZE")]
+    hdr += other
+    lines += ["| " + " | ".join(hdr) + " |", "|" + "---|" * len(hdr)]
+    for k in sorted(per, key=lambda k: -per[k].get("FETCH_SIZE", 0)):
+        d = per[k]
+        base = k.split("<")[0].replace("ls::", "")
+        row = ["`%s`" % k, str(launches[k])]
+        entry = {"launches": launches[k], "counters": d}
+        if "FETCH_SIZE" in counters and "WRITE_SIZE" in counters:
+            fb = d.get("FETCH_SIZE", 0) * factors.get("FETCH_SIZE", 1.0) * 1024
+            wb = d.get("WRITE_SIZE", 0) * factors.get("WRITE_SIZE", 1.0) * 1024
+            a = alg.get(base)
+            entry.update(fetch_bytes=round(fb), write_bytes=round(wb), algorithmic_bytes=a)
+            row += ["%.3g + %.3g = %.4g" % (fb, wb, fb + wb), "%d" % a if a else "-",
+                    "%.3f" % ((fb + wb) / a) if a else "-"]
+        row += ["%.4g" % d[c] if c in d else "-" for c in other]
+        res["kernels"][k] = entry
+        lines.append("| " + " | ".join(row) + " |")
+    if args.note:
+        lines += ["", args.note]
+    open(args.out, "w").write("\n".join(lines) + "\n")
+    json.dump(res, open(os.path.splitext(args.out)[0] + ".json", "w"), indent=1)
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="action", required=True)
@@ -135,8 +239,15 @@ def main():
     t.add_argument("--algorithmic", type=int, default=0)
     t.add_argument("--cmd-fetch", required=True)
     t.add_argument("--cmd-write", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("passes", nargs="+")
+    c.add_argument("--copy-mib", type=int, default=0)
+    c.add_argument("--workload", default="")
+    c.add_argument("--out", required=True)
+    c.add_argument("--cmd", action="append", default=[])
+    c.add_argument("--note", default="")
     args = ap.parse_args()
-    (cmd_stats if args.action == "stats" else cmd_traffic)(args)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[args.action](args)
 
 
 if __name__ == "__main__":
