@@ -304,6 +304,19 @@ int ls_sparse_attn_decode(const ls_attn_desc *desc, const void *q_dev, const voi
 int ls_decode_step(const ls_step_desc *desc, const ls_step_io *io, void *ws_dev,
                    size_t ws_bytes, ls_stream_t stream);
 
+/* The same step without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Its scratch is a static 128 MiB array
+ * that the library holds on each device it runs on until the process ends;
+ * a step whose workspace (ls_workspace_size(LS_OP_STEP, desc)) exceeds it is
+ * rejected with LS_E_UNSUPPORTED before anything is enqueued.  Each call
+ * first clears the part of the scratch that must start at zero (one small
+ * fill kernel), then runs exactly the kernels of ls_decode_step.  Every call
+ * on a device shares that device's scratch: calls that overlap on one device
+ * (two streams, or two threads) race and must not be issued.  Nothing here
+ * allocates or frees memory.                                                */
+int ls_decode_step_noalloc(const ls_step_desc *desc, const ls_step_io *io, ls_stream_t stream);
+
 /* One least-recently-used commit per request into a cache of n_slots rows
  * (the hot KV buffer or the indexer-key cache; the step runs the same
  * commit when ls_commit_desc asks for it).  entries [B, n]: the positions

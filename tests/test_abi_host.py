@@ -325,3 +325,16 @@ def test_read_probe_validation(lib):
     assert b"whole row" in lib.ls_last_error()
     assert lib.ls_read_probe(FAKE, 1024, FAKE, 4, 256, FAKE, None) == ls.LS_E_UNSUPPORTED
     assert lib.ls_read_probe(FAKE, 1024, None, 0, 0, None, None) == ls.LS_E_ARG
+
+
+def test_noalloc_step_checks_its_scratch_limit_before_the_device(lib):
+    # ls_decode_step_noalloc refuses a step whose workspace exceeds its static
+    # scratch, and a null descriptor, before any device call
+    assert lib.ls_decode_step_noalloc(None, FAKE, None) == ls.LS_E_ARG
+    i = idx(batch=64, max_ctx=131072, n_cand=8192, topk=2048)
+    h = ls.HotDesc(64, 131072, 2048, 4096, 576, 0)
+    a = ls.AttnDesc(64, 128, 1, 576, 512, 2048, 4096 + 2048, 576, 0, 0.07, 0)
+    d = ls.StepDesc(i, h, a, 1)
+    assert lib.ls_workspace_size(ls.OP_STEP, ctypes.byref(d)) > 128 << 20
+    rc = lib.ls_decode_step_noalloc(ctypes.byref(d), ctypes.byref(ls.StepIO()), None)
+    assert rc == ls.LS_E_UNSUPPORTED and b"static scratch" in lib.ls_last_error()

@@ -120,10 +120,11 @@ def load():
                                   _P, _P]
     L.ls_append_token.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P]
     L.ls_read_probe.argtypes = [_P, ctypes.c_uint64, _P, _I64, _I32, _P, _P]
+    L.ls_decode_step_noalloc.argtypes = [_P, _P, _P]
     for name in ("ls_cache_commit", "ls_append_token", "ls_pack_coarse", "ls_index_coarse",
                  "ls_refine_topk", "ls_hot_gather", "ls_sparse_attn_decode", "ls_decode_step",
                  "ls_prefill_index_topk", "ls_prefill_stream_layers", "ls_workspace_init",
-                 "ls_read_probe"):
+                 "ls_read_probe", "ls_decode_step_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -358,12 +359,15 @@ class DecodeStep:
 
     def run(self, *, q_idx, w_idx, kc, k8, ctx_len, q_attn, pos2slot=None, hot_kv=None,
             pool_kv=None, k_cache=None, v_cache=None, kpos2slot=None, kcache=None,
-            slot2pos=None, stamp=None, kslot2pos=None, kstamp=None, now=0, events=None):
+            slot2pos=None, stamp=None, kslot2pos=None, kstamp=None, now=0, events=None,
+            noalloc=False):
         """With commits, slot2pos / stamp (hot buffer) and kslot2pos / kstamp
         (key cache) are the caches' LRU state [B, slots] int32 (stamps held
         as uint32 bits), updated in place with pos2slot / kpos2slot; now is
         this step's stamp (see cache_commit), an int or a one-element int32
-        device tensor read when the kernels run (for graph capture)."""
+        device tensor read when the kernels run (for graph capture).
+        noalloc: run ls_decode_step_noalloc, on the library's static scratch
+        instead of this step's workspace."""
         i, a, h = self.desc.idx, self.desc.attn, self.desc.hot
         B, L, H, D = i.batch, i.max_ctx, i.n_heads, i.head_dim
         _need(q_idx, torch.int8, "q_idx", (B, H, D)), _need(w_idx, torch.int8, "w_idx", (B, H))
@@ -430,8 +434,12 @@ class DecodeStep:
             arr = (ctypes.c_void_p * STEP_EVENTS)(*[e.cuda_event if e is not None else None
                                                     for e in events])
             io.stage_events = ctypes.cast(arr, ctypes.c_void_p)
-        _check(load().ls_decode_step(ctypes.byref(self.desc), ctypes.byref(io),
-                                     _p(self.ws), self.ws.numel(), _stream()))
+        if noalloc:
+            _check(load().ls_decode_step_noalloc(ctypes.byref(self.desc), ctypes.byref(io),
+                                                 _stream()))
+        else:
+            _check(load().ls_decode_step(ctypes.byref(self.desc), ctypes.byref(io),
+                                         _p(self.ws), self.ws.numel(), _stream()))
         return self.out, self.lse
 
 

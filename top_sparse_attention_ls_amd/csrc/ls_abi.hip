@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -765,6 +766,40 @@ int decode_step_impl(const ls_step_desc* desc, const ls_step_io* io, void* ws_de
   return LS_OK;
 }
 
+// Bytes at the start of a step workspace that must read zero when a call
+// begins (the score histograms and the counters, carved first).
+size_t step_zero_prefix(const ls_step_desc* d) {
+  Carve c;
+  c.take<uint32_t>((size_t)d->idx.batch * ls::kCoarseBins);
+  c.take<uint32_t>((size_t)d->idx.batch * ls::kCtrStride);
+  return round_up(c.off, 256);
+}
+
+// Static scratch of the allocation-free step (see ls_decode_step_noalloc):
+// one copy per device, held until the process ends.  The array's name is a
+// host-side stand-in; kernels get the device address from
+// hipGetSymbolAddress, looked up once per device.
+constexpr size_t kStaticScratchBytes = (size_t)128 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+int static_scratch(void** out) {
+  int dev = -1;
+  LS_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(LS_E_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    LS_HIP(hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch)), "scratch symbol address");
+    if (!ptr) return fail(LS_E_HIP, "scratch symbol address is null");
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return LS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -773,6 +808,23 @@ int ls_decode_step(const ls_step_desc* desc, const ls_step_io* io, void* ws_dev,
                    size_t ws_bytes, ls_stream_t stream) {
   try {
     return decode_step_impl(desc, io, ws_dev, ws_bytes, stream, 0);
+  } catch (...) {
+    return fail(LS_E_ARG, "internal error");
+  }
+}
+
+int ls_decode_step_noalloc(const ls_step_desc* desc, const ls_step_io* io, ls_stream_t stream) {
+  try {
+    if (!desc) return fail(LS_E_ARG, "null step descriptor");
+    const size_t need = ws_size(LS_OP_STEP, desc);
+    if (need == 0) return LS_E_ARG;
+    if (need > kStaticScratchBytes)
+      return fail(LS_E_UNSUPPORTED,
+                  "the step needs %zu bytes of scratch, more than the %zu bytes of the static "
+                  "scratch of ls_decode_step_noalloc", need, kStaticScratchBytes);
+    void* ws = nullptr;
+    LS_TRY(static_scratch(&ws));
+    return decode_step_impl(desc, io, ws, kStaticScratchBytes, stream, step_zero_prefix(desc));
   } catch (...) {
     return fail(LS_E_ARG, "internal error");
   }
