@@ -108,13 +108,14 @@ __device__ __forceinline__ void wait_tiles_ahead(int ahead) {
 }
 
 // The miss gather folded into the attention (GATHER, pool in device memory).
-// A selected row that missed the hot buffer is read by the tile DMA straight
-// from the pool (src[i] holds its pool position), so no workgroup waits for a
-// copy.  The copy itself -- hot[row of miss j] := pool[miss_pos[j]], the row
-// being the scratch row hot_slots + j or the victim slot a commit gave it --
-// is shared out over the launch: workgroup (split s) copies misses s,
-// s + n_splits, ... in its prologue, its pool reads in flight with the first
-// tiles' DMA.  No workgroup of the launch reads the rows being written.
+// Each workgroup copies the selected rows of its own split that missed the
+// hot buffer, pool[src[i]] -> hot[rows[i]] (rows[i] being the miss's scratch
+// row, or the victim slot a commit gave it), in its prologue.  The first
+// NBUF-1 tiles, whose DMA starts before that copy, read their missed rows
+// straight from the pool; every later tile reads all its rows from the hot
+// buffer, after the copy (a pool spread over the whole history costs the
+// tile DMA address-translation misses that the request's compact hot block
+// does not).  No workgroup reads rows another one writes.
 template <int DQK, int DV, int NBUF, bool GATHER>
 __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
@@ -161,10 +162,15 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
   auto rid_at = [&](int i) { return rq[at(i)]; };
   auto src_at = [&](int i) { return GATHER ? sq[at(i)] : -1; };
   // What a tile position holds, as one code: >= 0 a hot-buffer row, <= -2 the
-  // pool row -(code + 2) of a missed entry, -1 padding (and ids out of range)
+  // pool row -(code + 2) of a missed entry, -1 padding (and ids out of range).
+  // Gathering, a miss reads the pool in the first NBUF-1 tiles and its hot
+  // row (written by the prologue's copy) in the others.
   auto code_of = [&](int i, int32_t r, int32_t sp) {
-    if (GATHER && i < n_rows && sp >= 0 && sp < ga.pool_rows) return -2 - sp;
-    return (i < n_rows && r >= 0 && r < rows_per_req) ? r : -1;
+    const bool r_ok = i < n_rows && r >= 0 && r < rows_per_req;
+    if (GATHER && i < n_rows && sp >= 0 && sp < ga.pool_rows &&
+        (i < (NBUF - 1) * kTileR || !r_ok))
+      return -2 - sp;
+    return r_ok ? r : -1;
   };
 
   // Tile DMA of tile t, this lane's row given by its code (padding loads
@@ -180,89 +186,87 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
   };
   auto issue_dma = [&](int t) { issue_dma_row(t, rid_lds[t * kTileR + dma_row]); };
 
-  // The copy share of this workgroup (GATHER): its k-th miss is miss
-  // j = split + n_splits k; 16-byte piece f of the share is piece f % CH of
-  // that miss's row.  Pieces go to threads f = tid + 256 u, kCopyU per round.
-  // Reads and writes go through buffer resources over the request's pool and
-  // hot-buffer blocks: a piece past the share gets an offset beyond the
-  // block, so its load returns zero and its store is dropped, with no branch.
+  // The copy (GATHER).  Wave w owns the split's entries w*64 + lane + 256 k;
+  // those that missed go to the wave's compact list (pool row, hot row) in
+  // LDS -- in tile buffer NBUF-1, which no DMA fills before the loop -- and
+  // the wave copies its list, 16-byte piece p (row p / CH, chunk p % CH) by
+  // lane p % 64, kCopyU pieces per lane and round, through buffer resources
+  // over the request's pool and hot blocks (a piece past the list gets an
+  // offset beyond the block: its load returns zero, its store is dropped).
+  constexpr int kRidIters = (kMaxSplitRows + kTileR + NW * 64 - 1) / (NW * 64);
   constexpr int kCopyU = 16;
-  constexpr int kCopyRound = NW * 64 * kCopyU;
-  int my_pieces = 0;
-  int32_t cp_pos[kCopyU], cp_dst[kCopyU];
+  constexpr int kListMax = kRidIters * 64;
+  static_assert(NW * kListMax * 8 <= TILE_BYTES, "copy lists fit a tile buffer");
+  int32_t* cl_src = (int32_t*)&tiles[NBUF - 1][0] + w * 2 * kListMax;
+  int32_t* cl_dst = cl_src + kListMax;
+  int m_list = 0;  // wave-uniform
   uint4 cp_v[kCopyU];
   const uint32_t pool_block = GATHER ? (uint32_t)(ga.pool_rows * row_stride * 2) : 0u;
   const uint32_t hot_block = GATHER ? (uint32_t)(rows_per_req * row_stride * 2) : 0u;
-  auto copy_list = [&](int f0) {
-#pragma unroll
-    for (int u = 0; u < kCopyU; u++) {
-      const int f = f0 + (int)threadIdx.x + NW * 64 * u;
-      const int jj = min(split + n_splits * (f / CH), K - 1);
-      cp_pos[u] = ga.miss_pos[(size_t)b * K + jj];
-      cp_dst[u] = ga.miss_dst ? ga.miss_dst[(size_t)b * K + jj] : -1;
-    }
-  };
-  auto copy_load = [&](int f0) {
+  const uint32_t row_bytes = (uint32_t)(row_stride * 2);
+  auto copy_load = [&](int p0) {
     const __amdgpu_buffer_rsrc_t pres = buffer_rsrc(poolb, pool_block);
 #pragma unroll
     for (int u = 0; u < kCopyU; u++) {
-      const int f = f0 + (int)threadIdx.x + NW * 64 * u;
-      const int c = f % CH;
-      const uint32_t p = (uint32_t)min(max(cp_pos[u], 0), (int)ga.pool_rows - 1);
-      const uint32_t off = f < my_pieces ? p * (uint32_t)(row_stride * 2) + 16u * c : pool_block;
+      const int p = p0 + l + 64 * u;
+      const int e = min(p / CH, max(m_list - 1, 0));
+      const uint32_t off =
+          p < m_list * CH ? (uint32_t)cl_src[e] * row_bytes + 16u * (p - (p / CH) * CH)
+                          : pool_block;
       cp_v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(pres, off, 0, 0));
     }
   };
-  auto copy_store = [&](int f0) {
+  auto copy_store = [&](int p0) {
     const __amdgpu_buffer_rsrc_t hres = buffer_rsrc(kvb, hot_block);
 #pragma unroll
     for (int u = 0; u < kCopyU; u++) {
-      const int f = f0 + (int)threadIdx.x + NW * 64 * u;
-      const int c = f % CH;
-      const int j = split + n_splits * (f / CH);
-      const int row = (cp_dst[u] >= 0 && cp_dst[u] < ga.hot_slots) ? cp_dst[u] : ga.hot_slots + j;
+      const int p = p0 + l + 64 * u;
+      const int e = min(p / CH, max(m_list - 1, 0));
       const uint32_t off =
-          f < my_pieces ? (uint32_t)row * (uint32_t)(row_stride * 2) + 16u * c : hot_block;
+          p < m_list * CH ? (uint32_t)cl_dst[e] * row_bytes + 16u * (p - (p / CH) * CH)
+                          : hot_block;
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, cp_v[u]), hres, off, 0, 0);
     }
   };
 
   // Prologue in two round trips.  First each lane's own DMA rows of the
-  // first tiles (and, gathering, the miss count and this workgroup's first
-  // round of the miss list), whose DMA then starts at once; then the copy's
-  // pool reads, the split's row ids (to be staged in LDS) and the query,
-  // which load while that DMA is in flight.
+  // first tiles and the split's row ids (to be staged in LDS) -- with their
+  // pool positions, gathering; the first tiles' DMA then starts at once, and
+  // the copy's pool reads and the query load while it is in flight.
+  int32_t rv[kRidIters], sv[kRidIters];
   {
     int32_t r0[NBUF - 1], s0[NBUF - 1];
-    int nm_raw = 0;
 #pragma unroll
     for (int t = 0; t < NBUF - 1; t++) {
       r0[t] = rid_at(t * kTileR + dma_row);
       s0[t] = src_at(t * kTileR + dma_row);
     }
-    if (GATHER) {
-      nm_raw = ga.n_miss[b];
-      copy_list(0);
+#pragma unroll
+    for (int k = 0; k < kRidIters; k++) {
+      rv[k] = rid_at(threadIdx.x + k * NW * 64);
+      sv[k] = src_at(threadIdx.x + k * NW * 64);
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 #pragma unroll
     for (int t = 0; t < NBUF - 1; t++)
       if (t < n_tiles) issue_dma_row(t, code_of(t * kTileR + dma_row, r0[t], s0[t]));
-    if (GATHER) {
-      // misses of this split (a list never holds more than K misses)
-      const int nm = min(max(nm_raw, 0), K);
-      const int my = nm > split ? (nm - 1 - split) / n_splits + 1 : 0;
-      my_pieces = my * CH;
-      copy_load(0);
-    }
   }
   __builtin_amdgcn_sched_barrier(0);
-  constexpr int kRidIters = (kMaxSplitRows + kTileR + NW * 64 - 1) / (NW * 64);
-  int32_t rv[kRidIters], sv[kRidIters];
+  if (GATHER) {
 #pragma unroll
-  for (int k = 0; k < kRidIters; k++) {
-    rv[k] = rid_at(threadIdx.x + k * NW * 64);
-    sv[k] = src_at(threadIdx.x + k * NW * 64);
+    for (int k = 0; k < kRidIters; k++) {
+      const int i = threadIdx.x + k * NW * 64;
+      const bool miss = i < n_rows && sv[k] >= 0 && sv[k] < ga.pool_rows && rv[k] >= 0 &&
+                        rv[k] < rows_per_req;
+      const uint64_t mask = __ballot(miss);
+      if (miss) {
+        const int e = m_list + (int)lane_rank(mask);
+        cl_src[e] = sv[k];
+        cl_dst[e] = rv[k];
+      }
+      m_list += __popcll(mask);
+    }
+    if (m_list > 0) copy_load(0);
   }
   // B operand of S^T = K Q^T: head n, dims 16 ks + 8 half .. +7 (loaded
   // unconditionally from a clamped head, then selected)
@@ -280,14 +284,13 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
   // wait on every iteration, which would also drain the tile DMA in flight);
   // the loop then waits for each tile's DMA alone.
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  if (GATHER) {
-    // the copy's first round has landed: store it; further rounds (only at
-    // high miss rates) load their list and rows here, one round trip each
+  if (GATHER && m_list > 0) {
+    // the copy's first round has landed: store it; further rounds (more than
+    // kCopyU * 64 / CH misses in a wave's 64 entries) one round trip each
     copy_store(0);
-    for (int f0 = kCopyRound; f0 < my_pieces; f0 += kCopyRound) {
-      copy_list(f0);
-      copy_load(f0);
-      copy_store(f0);
+    for (int p0 = 64 * kCopyU; p0 < m_list * CH; p0 += 64 * kCopyU) {
+      copy_load(p0);
+      copy_store(p0);
     }
   }
 #pragma unroll

@@ -749,10 +749,6 @@ int decode_step_impl(const ls_step_desc* desc, const ls_step_io* io, void* ws_de
     a.gather.src = rws.src;
     a.gather.pool = (const uint16_t*)pool;
     a.gather.pool_rows = id->max_ctx;
-    a.gather.miss_pos = rws.miss_pos;
-    a.gather.n_miss = io->n_miss_dev;
-    a.gather.miss_dst = cm->hot ? rws.miss_dst : nullptr;
-    a.gather.hot_slots = desc->hot.hot_slots;
   } else if (desc->use_hot) {
     LS_HIP(ls::launch_hot_gather(rws.miss_pos, io->n_miss_dev, cm->hot ? rws.miss_dst : nullptr,
                                  pool, io->hot_kv_dev, desc->hot.hot_slots, id->batch,

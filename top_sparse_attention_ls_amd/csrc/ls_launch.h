@@ -138,17 +138,13 @@ hipError_t launch_hot_gather(const int32_t* miss_pos, const int32_t* n_miss,
 
 // The miss gather folded into the latent attention (pool in device memory):
 // src [B, K] is the pool position of each selected entry that missed the hot
-// buffer (-1 for hits and padding); miss_pos / n_miss / miss_dst are the
-// resolve's miss list, count and (after a hot-buffer commit) destination
-// slots.  src == nullptr: no gather, the attention reads the hot buffer only.
+// buffer (-1 for hits and padding); the entry's row in rows[] is the hot row
+// the miss is copied into.  src == nullptr: no gather, the attention reads
+// the hot buffer only.
 struct AttnGather {
   const int32_t* src;
   const uint16_t* pool;
-  int64_t pool_rows;        // rows per request in the pool (max_ctx)
-  const int32_t* miss_pos;
-  const int32_t* n_miss;
-  const int32_t* miss_dst;  // nullable
-  int hot_slots;
+  int64_t pool_rows;  // rows per request in the pool (max_ctx)
 };
 
 struct AttnArgs {
