@@ -136,7 +136,10 @@ typedef struct {
  * + g * kv_head_stride + d].  For a latent (MLA-style) cache pass the same
  * base for K and V: V is then the first v_dim elements of the K row.
  * n_splits: number of row splits per request (0 = chosen by the library;
- * the latent-layout kernel raises it so that no split exceeds 1024 rows).  */
+ * the latent-layout kernel raises it so that no split exceeds 1024 rows).
+ * qk_dim is a multiple of 8; outside the latent layout (576 / 512, one kv
+ * head) v_dim and both strides must be multiples of 8 too and topk at most
+ * 8192, else LS_E_UNSUPPORTED.                                              */
 typedef struct {
     int32_t batch, n_q_heads, n_kv_heads, qk_dim, v_dim, topk;
     int64_t kv_rows_per_req, kv_row_stride, kv_head_stride;

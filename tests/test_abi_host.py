@@ -159,6 +159,11 @@ def test_attention_validation(lib):
     rc = lib.ls_sparse_attn_decode(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                    1 << 30, None)
     assert rc == ls.LS_E_UNSUPPORTED
+    # the generic kernel reads 16-byte pieces: a row stride off the 8-element grid is refused
+    a = ls.AttnDesc(2, 8, 8, 64, 64, 16, 100, 516, 64, 0.1, 0)
+    rc = lib.ls_sparse_attn_decode(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   1 << 30, None)
+    assert rc == ls.LS_E_UNSUPPORTED and b"multiples of 8" in lib.ls_last_error()
 
 
 def test_step_validation(lib):

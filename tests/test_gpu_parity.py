@@ -511,6 +511,28 @@ def test_attention_mha_parity(ls, Hq, n_kv, D):
     assert_attention_close(out, lse, np.stack(e_out), np.stack(e_lse), "mha")
 
 
+def test_attention_mha_many_rows_per_thread(ls):
+    # 2000 selected rows: every thread of the generic kernel scores 8 of them;
+    # the second request's list ends early (-1 padding)
+    B, L, K, Hq, n_kv, D = 2, 3000, 2000, 8, 4, 128
+    g = torch.Generator().manual_seed(31)
+    q = torch.randn(B, Hq, D, generator=g).to(torch.bfloat16)
+    Kc = torch.randn(B, L, n_kv, D, generator=g).to(torch.bfloat16)
+    Vc = torch.randn(B, L, n_kv, D, generator=g).to(torch.bfloat16)
+    rows = torch.full((B, K), -1, dtype=torch.int32)
+    rows[0] = torch.sort(torch.randperm(L, generator=g)[:K]).values.to(torch.int32)
+    rows[1, :1500] = torch.sort(torch.randperm(L, generator=g)[:1500]).values.to(torch.int32)
+    out, lse = ls.sparse_attn_decode(q.to(DEV), Kc.to(DEV), Vc.to(DEV), rows.to(DEV), 0.09, n_kv,
+                                     D, L, n_kv * D, D)
+    e_out, e_lse = [], []
+    for b in range(B):
+        o, l_ = orc.attention(bits(q[b]), bits(Kc[b]).reshape(-1), bits(Vc[b]).reshape(-1),
+                              np_(rows[b]), 0.09, n_kv, D, n_kv * D, D)
+        e_out.append(o)
+        e_lse.append(l_)
+    assert_attention_close(out, lse, np.stack(e_out), np.stack(e_lse), "mha 2000 rows")
+
+
 # --------------------------------------------------------- whole step --
 
 def test_decode_step_tiny_mha(ls):

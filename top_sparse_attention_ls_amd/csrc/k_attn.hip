@@ -500,10 +500,18 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
 }
 
 // ---------------------------------------------------------------- VALU path --
-// One workgroup per (query head, request): scores in LDS, block softmax, then
-// the weighted sum of V rows with threads over (row group, dim).
+// One workgroup per (query head, request), for any head layout (MHA / GQA,
+// head dims up to kValuMaxDim).  Scores: every thread takes whole rows (row
+// i = tid + 256 k) and loads each row's head slice with 16-byte loads, all of
+// them issued before any is used, so the whole score phase costs one round
+// trip (the query, staged in LDS as fp32, is read by every thread); block
+// max and sum, then P.V with the threads over (row group, 8-dim chunk), the V
+// chunk loads of a thread again issued together (the row ids staged in LDS
+// by the score phase).  dqk, dv and both strides are multiples of 8 (the
+// 16-byte pieces).
 constexpr int kValuMaxRows = 8192;
 constexpr int kValuMaxDim = 1024;
+constexpr int kValuRowsPerThread = kValuMaxRows / 256;
 
 __device__ __forceinline__ float block_reduce_max(float v, float* sh) {
 #pragma unroll
@@ -525,6 +533,19 @@ __device__ __forceinline__ float block_reduce_sum(float v, float* sh) {
   return r;
 }
 
+// dot of the fp32 query in LDS with a row's head slice, 8 dims per piece
+__device__ __forceinline__ float dot8(const float* qs, int d0, uint4 v) {
+  const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    acc = fmaf(qs[d0 + 2 * e], __uint_as_float(x[e] << 16), acc);
+    acc = fmaf(qs[d0 + 2 * e + 1], __uint_as_float(x[e] & 0xFFFF0000u), acc);
+  }
+  return acc;
+}
+
+template <int DP>  // 16-byte pieces of the score head slice handled per row at once
 __global__ __launch_bounds__(256) void k_attn_valu(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kbase,
     const uint16_t* __restrict__ vbase, const int32_t* __restrict__ rows,
@@ -532,66 +553,101 @@ __global__ __launch_bounds__(256) void k_attn_valu(
     int K, int64_t rows_per_req, int64_t row_stride, int64_t head_stride, float scale) {
   __shared__ float qs[kValuMaxDim];
   __shared__ float sc[kValuMaxRows];
+  __shared__ int32_t rid_sh[kValuMaxRows];
   __shared__ float red[4];
-  __shared__ float acc_sh[256];
+  __shared__ float acc_sh[256 * 8];
   const int h = blockIdx.x, b = blockIdx.y;
   const int kvh = h / (Hq / n_kv);
-  const int tid = threadIdx.x, l = lane_id(), wv = wave_id();
+  const int tid = threadIdx.x;
   const uint16_t* qh = q + ((size_t)b * Hq + h) * dqk;
   for (int d = tid; d < dqk; d += 256) qs[d] = bf16_to_f32(qh[d]);
-  __syncthreads();
   const int32_t* rb = rows + (size_t)b * K;
   const size_t req_off = (size_t)b * rows_per_req * row_stride + (size_t)kvh * head_stride;
-  for (int i = wv; i < K; i += 4) {
-    const int32_t r0 = rb[i];
-    const int32_t r = (r0 >= 0 && r0 < rows_per_req) ? r0 : -1;  // out of range = padding
-    float dot = 0.f;
-    if (r >= 0) {
-      const uint16_t* kr = kbase + req_off + (size_t)r * row_stride;
-      for (int d = l; d < dqk; d += 64) dot += qs[d] * bf16_to_f32(kr[d]);
-    }
+  // this thread's rows (ids loaded together; out-of-range ids are padding)
+  int32_t r_of[kValuRowsPerThread];
+  const int my_rows = K > tid ? (K - 1 - tid) / 256 + 1 : 0;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o, kWave);
-    if (l == 0) sc[i] = (r >= 0) ? dot * scale : -INFINITY;
+  for (int k = 0; k < kValuRowsPerThread; k++) {
+    const int i = tid + 256 * k;
+    const int32_t r0 = k < my_rows ? rb[i] : -1;
+    r_of[k] = (r0 >= 0 && r0 < rows_per_req) ? r0 : -1;
   }
-  __syncthreads();
-  float m = -INFINITY;
-  for (int i = tid; i < K; i += 256) m = fmaxf(m, sc[i]);
-  m = block_reduce_max(m, red);
+  __syncthreads();  // query staged
+  const int n_pc = dqk / 8;
+  float m_loc = -INFINITY;
+#pragma unroll 1
+  for (int k = 0; k < my_rows; k++) {
+    const int32_t r = r_of[k];
+    const uint4* kr = (const uint4*)(kbase + req_off + (size_t)(r >= 0 ? r : 0) * row_stride);
+    float dot = 0.f;
+    for (int c0 = 0; c0 < n_pc; c0 += DP) {
+      uint4 v[DP];
+#pragma unroll
+      for (int u = 0; u < DP; u++) v[u] = kr[min(c0 + u, n_pc - 1)];
+#pragma unroll
+      for (int u = 0; u < DP; u++)
+        if (c0 + u < n_pc) dot += dot8(qs, 8 * (c0 + u), v[u]);
+    }
+    const float s_ = (r >= 0) ? dot * scale : -INFINITY;
+    sc[tid + 256 * k] = s_;
+    rid_sh[tid + 256 * k] = r;
+    m_loc = fmaxf(m_loc, s_);
+  }
+  const float m = block_reduce_max(m_loc, red);
   float lsum = 0.f;
   if (m != -INFINITY) {
-    for (int i = tid; i < K; i += 256) {
+    for (int k = 0; k < my_rows; k++) {
+      const int i = tid + 256 * k;
       const float p = (sc[i] == -INFINITY) ? 0.f : expf(sc[i] - m);
       sc[i] = p;
       lsum += p;
     }
   }
-  lsum = block_reduce_sum(lsum, red);
-  __syncthreads();
+  lsum = block_reduce_sum(lsum, red);  // (its barriers also publish sc)
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   uint16_t* ob = out + ((size_t)b * Hq + h) * dv;
-  // threads = (row group rg, dim d); dims in chunks of at most 256
-  for (int d0 = 0; d0 < dv; d0 += 256) {
-    const int nd = min(256, dv - d0);
-    const int groups = 256 / nd;
-    const int d = d0 + tid % nd, rg = tid / nd;
-    float acc = 0.f;
-    if (rg < groups && m != -INFINITY) {
-      for (int i = rg; i < K; i += groups) {
-        const int32_t r = rb[i];
-        if (r >= 0 && r < rows_per_req)
-          acc += sc[i] * bf16_to_f32(vbase[req_off + (size_t)r * row_stride + d]);
+  // P.V: thread (row group rg, 8-dim chunk c); chunks of at most 256 / groups
+  const int n_vc = dv / 8;
+  const int groups = max(256 / n_vc, 1);
+  for (int c0 = 0; c0 < n_vc; c0 += 256) {
+    const int nc = min(256, n_vc - c0);
+    const int grp = max(256 / nc, 1);
+    const int c = c0 + tid % nc, rg = tid / nc;
+    float a8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (rg < grp && m != -INFINITY) {
+      for (int i0 = rg; i0 < K; i0 += 4 * grp) {
+        uint4 v[4];
+        float pw[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          const int i = i0 + grp * u;
+          const int32_t r0 = i < K ? rid_sh[i] : -1;   // -1: padding or out of range
+          pw[u] = r0 >= 0 ? sc[i] : 0.f;
+          v[u] = *((const uint4*)(vbase + req_off + (size_t)(r0 >= 0 ? r0 : 0) * row_stride) + c);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          const uint32_t x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            a8[2 * e] = fmaf(pw[u], __uint_as_float(x[e] << 16), a8[2 * e]);
+            a8[2 * e + 1] = fmaf(pw[u], __uint_as_float(x[e] & 0xFFFF0000u), a8[2 * e + 1]);
+          }
+        }
       }
     }
-    acc_sh[tid] = (rg < groups) ? acc : 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; e++) acc_sh[tid * 8 + e] = (rg < grp) ? a8[e] : 0.f;
     __syncthreads();
-    if (tid < nd) {
+    if (tid < nc * 8) {
+      const int cc = tid / 8, e = tid % 8;
       float tot = 0.f;
-      for (int k = 0; k < groups; k++) tot += acc_sh[k * nd + tid];
-      ob[d0 + tid] = f32_to_bf16_rne(tot * inv);
+      for (int g = 0; g < grp; g++) tot += acc_sh[(g * nc + cc) * 8 + e];
+      ob[8 * (c0 + cc) + e] = f32_to_bf16_rne(tot * inv);
     }
     __syncthreads();
   }
+  (void)groups;
   if (tid == 0) lse[(size_t)b * Hq + h] = (lsum > 0.f) ? m + logf(lsum) : -INFINITY;
 }
 
@@ -735,7 +791,10 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
                          a.gather);
     }
   } else {
-    hipLaunchKernelGGL(k_attn_valu, dim3(a.Hq, a.B), dim3(256), 0, st, a.q, a.k, a.v, a.rows,
+    if (a.qk_dim % 8 != 0 || a.v_dim % 8 != 0 || a.qk_dim > kValuMaxDim ||
+        a.v_dim > kValuMaxDim || a.K > kValuMaxRows)
+      return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_attn_valu<8>, dim3(a.Hq, a.B), dim3(256), 0, st, a.q, a.k, a.v, a.rows,
                        a.out, a.lse, a.Hq, a.n_kv, a.qk_dim, a.v_dim, a.K, a.rows_per_req,
                        a.row_stride, a.head_stride, a.scale);
   }

@@ -568,6 +568,9 @@ static int attn_args(const ls_attn_desc* d, const void* q, const void* k, const 
   const bool mfma = ls::attn_uses_mfma(d->n_q_heads, d->n_kv_heads, d->qk_dim, d->v_dim, k, v);
   if (!mfma && d->topk > 8192)
     return fail(LS_E_UNSUPPORTED, "topk > 8192 needs the latent (576/512, one kv head) layout");
+  if (!mfma && (d->v_dim % 8 != 0 || d->kv_row_stride % 8 != 0 || d->kv_head_stride % 8 != 0))
+    return fail(LS_E_UNSUPPORTED, "the generic attention reads 16-byte pieces: v_dim and the "
+                                  "row and head strides must be multiples of 8");
   a->n_splits = attn_splits(d, k, v);
   a->gather = ls::AttnGather{};  // no gather unless the step folds it in
   (void)ws;
