@@ -415,6 +415,19 @@ def test_attention_mla_parity_many_splits(ls, n_splits):
     assert_attention_close(out, lse, e_out, e_lse, "mla splits=%d" % n_splits)
 
 
+def test_attention_mla_parity_32_splits(ls):
+    # the largest automatic split count (a small batch spread over the
+    # CUs): 32 splits of 32 rows, four combine load rounds
+    B, K, S = 2, 1024, 200
+    q, kv, rows = mla_case(B, 128, [1024, 700], K, S, seed=132)
+    scale = 1 / math.sqrt(192)
+    kvd = kv.to(DEV)
+    out, lse = ls.sparse_attn_decode(q.to(DEV), kvd, kvd, rows.to(DEV), scale, 1, 512, S + K,
+                                     576, n_splits=32)
+    e_out, e_lse = oracle_mla(q, kv, rows, scale)
+    assert_attention_close(out, lse, e_out, e_lse, "mla splits=32")
+
+
 def test_attention_mla_all_rows_equal_dense(ls):
     # k >= context: sparse attention over every row equals dense attention
     B, Hq, L = 2, 32, 200

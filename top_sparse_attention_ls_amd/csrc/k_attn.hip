@@ -762,7 +762,7 @@ int attn_auto_splits(int B, int Hq, int K, bool mfma) {
   const int groups = (Hq + kHeadsPerWave * kAttnWaves - 1) / (kHeadsPerWave * kAttnWaves);
   int s = (256 + B * groups - 1) / (B * groups);
   const int max_s = (K + kTileR - 1) / kTileR;
-  if (s > 16) s = 16;
+  if (s > 32) s = 32;
   if (s > max_s) s = max_s;
   const int min_s = (K + kMaxSplitRows - 1) / kMaxSplitRows;
   if (s < min_s) s = min_s;

@@ -301,16 +301,37 @@ __device__ Threshold wave_threshold(const Get& get, int n, uint32_t need, uint32
 // digit -- the only step that touches every entry -- is counted by the whole
 // workgroup (NT threads), and the entries that fall in the chosen digit are
 // copied to sc by the whole workgroup; one wave then finishes over that short
-// list (wave_threshold).  With more than kThrScratch entries in the chosen
-// digit, or nothing to split on, the wave continues over the whole list.
-// Every thread returns the threshold.  Contains workgroup barriers; sh_thr
-// is LDS.
+// list (wave_threshold).  A list longer than kThrScratch whose chosen digit
+// still holds more than kThrScratch entries, or whose keys are all equal
+// (nothing to split on but positions), is searched by the whole workgroup
+// (block_threshold): one wave walking every digit of a long list is the
+// slow case.  Every thread
+// returns the threshold.  Contains workgroup barriers; sh_thr is LDS.
+constexpr int kEqualCheck = 2048;
+
 template <int NT, class Get>
 __device__ Threshold tie_threshold(const Get& get, int n, uint32_t need, SelectShared& sh,
                                    ThresholdScratch* sc, Threshold* sh_thr, uint64_t key_lo,
                                    uint64_t key_hi, int pos_bits) {
   const int tid = threadIdx.x;
   const int nb = (key_lo == key_hi) ? 0 : 64 - __clzll(key_lo ^ key_hi);
+  const uint32_t need_all = need;
+  if (n > kEqualCheck) {  // workgroup-uniform
+    // the keys' own range first: a long list of equal keys (a large group of
+    // equal scores at the cut) would put every entry of the first digit's
+    // histogram into one bin, one LDS atomic after another (shorter lists
+    // skip this pass: their worst case costs less than the pass itself)
+    uint64_t mn = ~0ull, mx = 0;
+    for (int i = tid; i < n; i += NT) {
+      uint64_t u;
+      uint32_t p;
+      get(i, u, p);
+      mn = u < mn ? u : mn;
+      mx = u > mx ? u : mx;
+    }
+    block_minmax<NT>(mn, mx, sh);
+    if (mn == mx) return block_threshold<NT>(get, n, need_all, sh);
+  }
   if (nb > 0 && n > kThrScratch) {  // workgroup-uniform
     const int d = nb < 8 ? nb : 8;
     const int shft = nb - d;
@@ -357,8 +378,7 @@ __device__ Threshold tie_threshold(const Get& get, int n, uint32_t need, SelectS
       __syncthreads();
       return *sh_thr;
     }
-    key_lo = prefix;
-    key_hi = prefix | low;
+    return block_threshold<NT>(get, n, need_all, sh);
   }
   if (wave_id() == 0) {
     const Threshold t = wave_threshold(get, n, need, sh.hist, key_lo, key_hi, pos_bits);
