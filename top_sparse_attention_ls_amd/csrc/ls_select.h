@@ -74,6 +74,24 @@ __device__ __forceinline__ void find_crossing(SelectShared& sh, uint32_t need, b
   }
 }
 
+// hist[bin] += 1 for every active lane with `on`.  The lanes that share the
+// bin of the wave's first such lane add with one atomic between them, so a
+// run of equal keys costs one LDS atomic per wave rather than one per lane
+// (same-address atomics serialise); the other lanes add their own.
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool on) {
+  const uint64_t act = __ballot(on);
+  if (act == 0) return;
+  const int first = __ffsll((unsigned long long)act) - 1;
+  const uint32_t b0 = wave_read(bin, first);
+  const uint64_t same = __ballot(on && bin == b0);
+  if (on) {
+    if (bin != b0)
+      atomicAdd(&hist[bin], 1u);
+    else if ((int)lane_id() == first)
+      atomicAdd(&hist[b0], (uint32_t)__popcll(same));
+  }
+}
+
 // Block-cooperative threshold search over n entries (key, position), keys
 // unsigned, positions unique.  Finds the threshold that keeps exactly `need`
 // entries (1 <= need < n) under the order key descending, position
@@ -103,12 +121,13 @@ __device__ Threshold block_threshold(const Get& get, int n, uint32_t need, Selec
     const uint64_t dmask = (1ull << d) - 1ull;
     for (int i = tid; i < 256; i += NT) sh.hist[i] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += NT) {
+    for (int i0 = 0; i0 < n; i0 += NT) {  // whole waves: hist_add is per wave
+      const int i = i0 + tid;
       uint64_t u;
       uint32_t p;
-      get(i, u, p);
-      bool in = (nb >= 64) || ((u >> nb) == (prefix >> nb));
-      if (in) atomicAdd(&sh.hist[(uint32_t)((u >> shft) & dmask)], 1u);
+      get(min(i, n - 1), u, p);
+      const bool in = i < n && ((nb >= 64) || ((u >> nb) == (prefix >> nb)));
+      hist_add(sh.hist, (uint32_t)((u >> shft) & dmask), in);
     }
     __syncthreads();
     find_crossing(sh, need, true);
@@ -301,13 +320,13 @@ __device__ Threshold wave_threshold(const Get& get, int n, uint32_t need, uint32
 // digit -- the only step that touches every entry -- is counted by the whole
 // workgroup (NT threads), and the entries that fall in the chosen digit are
 // copied to sc by the whole workgroup; one wave then finishes over that short
-// list (wave_threshold).  A list longer than kThrScratch whose chosen digit
-// still holds more than kThrScratch entries, or whose keys are all equal
-// (nothing to split on but positions), is searched by the whole workgroup
-// (block_threshold): one wave walking every digit of a long list is the
-// slow case.  Every thread
+// list (wave_threshold).  With more than kThrScratch entries in the chosen
+// digit (or nothing to split on) the wave continues over the whole list,
+// up to kWaveTies entries; beyond that the whole workgroup searches it
+// (block_threshold), as one wave walking every digit of a long list -- a
+// large group of equal scores at the cut -- is the slow case.  Every thread
 // returns the threshold.  Contains workgroup barriers; sh_thr is LDS.
-constexpr int kEqualCheck = 2048;
+constexpr int kWaveTies = 2048;
 
 template <int NT, class Get>
 __device__ Threshold tie_threshold(const Get& get, int n, uint32_t need, SelectShared& sh,
@@ -316,22 +335,6 @@ __device__ Threshold tie_threshold(const Get& get, int n, uint32_t need, SelectS
   const int tid = threadIdx.x;
   const int nb = (key_lo == key_hi) ? 0 : 64 - __clzll(key_lo ^ key_hi);
   const uint32_t need_all = need;
-  if (n > kEqualCheck) {  // workgroup-uniform
-    // the keys' own range first: a long list of equal keys (a large group of
-    // equal scores at the cut) would put every entry of the first digit's
-    // histogram into one bin, one LDS atomic after another (shorter lists
-    // skip this pass: their worst case costs less than the pass itself)
-    uint64_t mn = ~0ull, mx = 0;
-    for (int i = tid; i < n; i += NT) {
-      uint64_t u;
-      uint32_t p;
-      get(i, u, p);
-      mn = u < mn ? u : mn;
-      mx = u > mx ? u : mx;
-    }
-    block_minmax<NT>(mn, mx, sh);
-    if (mn == mx) return block_threshold<NT>(get, n, need_all, sh);
-  }
   if (nb > 0 && n > kThrScratch) {  // workgroup-uniform
     const int d = nb < 8 ? nb : 8;
     const int shft = nb - d;
@@ -340,11 +343,21 @@ __device__ Threshold tie_threshold(const Get& get, int n, uint32_t need, SelectS
     for (int i = tid; i < 256; i += NT) sh.hist[i] = 0;
     if (tid == 0) sc->fill = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += NT) {
-      uint64_t u;
-      uint32_t p;
-      get(i, u, p);
-      atomicAdd(&sh.hist[(uint32_t)((u >> shft) & dmask)], 1u);
+    if (n > kWaveTies) {  // a long list may be one run of equal keys
+      for (int i0 = 0; i0 < n; i0 += NT) {  // whole waves: hist_add is per wave
+        const int i = i0 + tid;
+        uint64_t u;
+        uint32_t p;
+        get(min(i, n - 1), u, p);
+        hist_add(sh.hist, (uint32_t)((u >> shft) & dmask), i < n);
+      }
+    } else {
+      for (int i = tid; i < n; i += NT) {
+        uint64_t u;
+        uint32_t p;
+        get(i, u, p);
+        atomicAdd(&sh.hist[(uint32_t)((u >> shft) & dmask)], 1u);
+      }
     }
     __syncthreads();
     find_crossing(sh, need, true);
@@ -378,8 +391,11 @@ __device__ Threshold tie_threshold(const Get& get, int n, uint32_t need, SelectS
       __syncthreads();
       return *sh_thr;
     }
-    return block_threshold<NT>(get, n, need_all, sh);
+    if (cnt > (uint32_t)kWaveTies) return block_threshold<NT>(get, n, need_all, sh);
+    key_lo = prefix;
+    key_hi = prefix | low;
   }
+  if (nb == 0 && n > kWaveTies) return block_threshold<NT>(get, n, need_all, sh);
   if (wave_id() == 0) {
     const Threshold t = wave_threshold(get, n, need, sh.hist, key_lo, key_hi, pos_bits);
     if (lane_id() == 0) *sh_thr = t;

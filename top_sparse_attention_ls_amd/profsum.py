@@ -203,6 +203,8 @@ def cmd_counters(args):
     for k in sorted(per, key=lambda k: -per[k].get("FETCH_SIZE", 0)):
         d = per[k]
         base = k.split("<")[0].replace("ls::", "")
+        if base == "k_attn_mfma" and k.replace(" ", "").endswith(",true>"):
+            base = "k_attn_fused"  # the miss gather folded into the tile DMA
         row = ["`%s`" % k, str(launches[k])]
         entry = {"launches": launches[k], "counters": d}
         if "FETCH_SIZE" in counters and "WRITE_SIZE" in counters:
