@@ -1000,6 +1000,8 @@ def main():
     if wl.n_query:
         print(json.dumps(run_prefill(ls, synth, wl, args.steps, args.warmup,
                                      n_rows_cpu=args.cpu_sample)), flush=True)
+        if args.copy_calib > 0:
+            copy_calibration(args.copy_calib << 20)
         return
     if wl.serve_drift > 0:
         run_serve(ls, synth, wl, args)
