@@ -58,3 +58,16 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=60)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_gather_folded_only_for_device_pools_on_the_latent_path():
+    # the library folds the miss gather into the attention's tile DMA when
+    # the pool is in device memory and the rows are latent (MLA) rows; the
+    # bench then books the gather's bytes to the attention stage
+    import bench
+    from top_sparse_attention_ls_amd import synth
+    W = synth.WORKLOADS
+    assert bench.gather_folded(W["decode-128k-b32"])
+    assert bench.gather_folded(W["decode-950k-b4"])
+    assert not bench.gather_folded(W["decode-16k-b192"])    # pool in pinned host memory
+    assert not bench.gather_folded(W["tiny-4k"])            # no hot buffer, MHA rows
