@@ -777,9 +777,9 @@ def run_prefill(ls, synth, wl, steps, warmup, n_rows_cpu=0):
         import numpy as np
         from oracle import oracle as orc
         P = min(n_rows_cpu, host_threads())
-        rows = np.linspace(0, Tq - 1, P).round().astype(int).tolist()
+        rows = np.linspace(0, Tq - 1, n_rows_cpu).round().astype(int).tolist()
         q0, w0, k0 = qs[0].cpu().numpy(), ws_[0].cpu().numpy(), kh[0].numpy()
-        print("[bench] prefill cpu baseline on %d rows" % P, file=sys.stderr, flush=True)
+        print("[bench] prefill cpu baseline on %d rows" % len(rows), file=sys.stderr, flush=True)
         wall, per = timed_pool(lambda i: orc.prefill_row(q0[i], w0[i], k0, q_pos0 + i, K), rows,
                                P)
         row_ops = sum(2 * (q_pos0 + i + 1) * H * D for i in rows)
@@ -790,9 +790,10 @@ def run_prefill(ls, synth, wl, steps, warmup, n_rows_cpu=0):
             "cpu_model": cpu_model(), "host_cpus_visible": os.cpu_count(),
             "extrapolated_ms_per_chunk": round(ops / rate * 1e3, 1),
             "single_thread_s_per_row": round(sum(per) / len(per), 3),
-            "sample": "%d query rows of layer 0 (first, last, evenly spaced) at once on %d host "
+            "sample": "%d query rows of layer 0 (first, last, evenly spaced) on %d host "
                       "threads, single-threaded C each (%.2f s wall); extrapolated to the "
-                      "%d x %d-layer chunk by int8 operations" % (P, P, wall, Tq, wl.layers),
+                      "%d x %d-layer chunk by int8 operations" % (len(rows), P, wall, Tq,
+                                                                 wl.layers),
         }
     del layers, qs, ws_, kh, kd, buf0, buf1
     return result
@@ -998,7 +999,7 @@ def main():
     ap.add_argument("--replicas", type=int, default=2)
     ap.add_argument("--cpu-sample", type=int, default=16,
                     help="requests the CPU oracle baseline runs at once on as many host threads "
-                         "(0 = skip the baseline)")
+                         "(prefill: four times as many query rows; 0 = skip the baseline)")
     ap.add_argument("--extras", type=int, default=1,
                     help="default workload: also measure the other workloads (4K latency, "
                          "16K x 192 with the pool on the host, 950K x 4, the prefill chunk) "
@@ -1025,7 +1026,7 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     if wl.n_query:
         print(json.dumps(run_prefill(ls, synth, wl, args.steps, args.warmup,
-                                     n_rows_cpu=args.cpu_sample)), flush=True)
+                                     n_rows_cpu=4 * args.cpu_sample)), flush=True)
         if args.copy_calib > 0:
             copy_calibration(args.copy_calib << 20)
         return
@@ -1058,7 +1059,7 @@ def main():
             gc.collect()
             torch.cuda.empty_cache()
         extra["prefill-4k-128k"] = run_prefill(ls, synth, synth.WORKLOADS["prefill-4k-128k"], 3,
-                                               1, n_rows_cpu=16 if args.cpu_sample else 0)
+                                               1, n_rows_cpu=64 if args.cpu_sample else 0)
         gc.collect()
         torch.cuda.empty_cache()
         result["workloads"] = extra
