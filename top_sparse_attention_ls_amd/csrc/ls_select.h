@@ -161,12 +161,14 @@ __device__ Threshold block_threshold(const Get& get, int n, uint32_t need, Selec
     const uint64_t dmask = (1ull << d) - 1ull;
     for (int i = tid; i < 256; i += NT) sh.hist[i] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += NT) {
+    for (int i0 = 0; i0 < n; i0 += NT) {  // whole waves: hist_add is per wave
+      const int i = i0 + tid;
       uint64_t u;
       uint32_t p;
-      get(i, u, p);
-      if (u == cut && ((uint64_t)p >> pb) == (pprefix >> pb))
-        atomicAdd(&sh.hist[(uint32_t)(((uint64_t)p >> shft) & dmask)], 1u);
+      get(min(i, n - 1), u, p);
+      // (runs of consecutive positions -- bursts of equal scores -- share a bin)
+      hist_add(sh.hist, (uint32_t)(((uint64_t)p >> shft) & dmask),
+               i < n && u == cut && ((uint64_t)p >> pb) == (pprefix >> pb));
     }
     __syncthreads();
     find_crossing(sh, need, false);
