@@ -994,7 +994,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=60,
+                    help="untimed steps first (the GPU reaches its steady clocks)")
     ap.add_argument("--workload", default="decode-128k-b32")
     ap.add_argument("--replicas", type=int, default=2)
     ap.add_argument("--cpu-sample", type=int, default=16,
@@ -1049,9 +1050,9 @@ def main():
         # inputs are built and freed in turn
         extra = {}
         for name, steps, warm, reps_, n1, npar in (
-                ("tiny-4k", 50, 5, 1, 1, 4),
-                ("decode-16k-b192", 10, 2, 1, 1, 16),
-                ("decode-950k-b4", 20, 3, 2, 0, 4)):
+                ("tiny-4k", 50, 20, 1, 1, 4),
+                ("decode-16k-b192", 10, 4, 1, 1, 16),
+                ("decode-950k-b4", 20, 20, 2, 0, 4)):
             sub, _ = run_decode(ls, synth, synth.WORKLOADS[name], steps, warm, reps_,
                                 full=False, n_single=n1 if args.cpu_sample else 0,
                                 n_parallel=npar if args.cpu_sample else 0)
