@@ -202,6 +202,61 @@ def test_refine_topk_tie_list_overflow(ls):
     assert tk[0].tolist() == list(range(333))
 
 
+def wide_bucket_of(x):
+    """The float-like bucket of an int64 score (exact below 128, then 64 per
+    power of two): used only to build two different scores that share a
+    bucket."""
+    x = int(x)
+
+    def mag(y):
+        if y < 128:
+            return y
+        e = y.bit_length() - 1
+        return 128 + (e - 7) * 64 + ((y >> (e - 6)) & 63)
+    return mag(x) if x >= 0 else -1 - mag(-(x + 1))
+
+
+def near_pattern(q, w, row):
+    """A copy of key row `row` with one element moved by one whose fine score
+    differs from the row's but lies in the same bucket."""
+    base = int(orc.index_scores(q, w, row[None].numpy(), False)[0])
+    for d in range(row.shape[0]):
+        for delta in (1, -1):
+            v = int(row[d]) + delta
+            if not -128 <= v <= 127:
+                continue
+            r = row.clone()
+            r[d] = v
+            sc = int(orc.index_scores(q, w, r[None].numpy(), False)[0])
+            if sc != base and wide_bucket_of(sc) == wide_bucket_of(base):
+                return r
+    raise AssertionError("no near pattern")
+
+
+def test_refine_topk_long_tie_lists(ls):
+    # more than 2048 ties in the threshold bucket, all within the LDS list.
+    # Request 0: 3000 tokens of one equal score with the cut inside the group
+    # (the one-key shortcut, ties ranked by position).  Request 1: the same
+    # 3000 tokens split between two different scores of one bucket, the cut
+    # inside the lower one (the shortcut must not apply; the workgroup search
+    # runs).  Every token is a candidate, 200 strong ones above the group.
+    wl = dataclasses.replace(SHRUNK, batch=2, ctx=6000)
+    inp = idx_inputs(wl)
+    q, w, keys = inp["q"], inp["w"], inp["keys"]
+    g = torch.Generator().manual_seed(21)
+    for b in range(2):
+        pats = ordered_patterns(q[b].numpy(), w[b].numpy(), keys[b])
+        perm = torch.randperm(6000, generator=g)
+        lvl = torch.full((6000,), 2, dtype=torch.long)
+        lvl[perm[:200]] = 0
+        lvl[perm[200:3200]] = 1
+        rows = pats[lvl]
+        if b == 1:
+            rows[perm[1700:3200]] = near_pattern(q[b].numpy(), w[b].numpy(), pats[1])
+        keys[b] = rows
+    run_refine_case(ls, inp, [6000, 6000], 6000, 2400)
+
+
 def test_refine_topk_pinned_host_keys(ls):
     # the original keys stay in pinned host memory; the refinement reads the
     # candidates' rows over PCIe

@@ -211,6 +211,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
   __shared__ int64_t tie_f[kTopkTieLds];
   __shared__ int32_t tie_c[kTopkTieLds];
   __shared__ uint32_t tab[NTAB];
+  __shared__ uint32_t ttab[NTAB];  // ties per (batch, wave), for ranks by position
   __shared__ Threshold sh_thr;
   __shared__ ThresholdScratch thr_sc;  // the tie search's short list
   __shared__ int sh_beta;
@@ -316,7 +317,52 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
     const uint32_t nt = n_tie;
     const bool overflow = nt > (uint32_t)kTopkTieLds;
     Threshold thr{0ull, 0u, 0};
-    if (overflow) {  // every valid candidate takes part: the cut is exact on its own
+    // A long tie list may be one run of equal scores (repeated content, or the
+    // identical planted tokens of the synthetic workloads): then the cut is the
+    // need-th tie in position order, found without searching the list.  Only
+    // long lists are checked, so the common path pays one uniform branch.
+    bool one_key = false;
+    if (need < nt && nt > (uint32_t)kWaveTies) {  // workgroup-uniform
+      const int64_t ref = tie_f[0];  // the first reserved entry (nt >= 1)
+      bool same = true;
+#pragma unroll
+      for (int k = 0; k < PER; k++) same = same && !(((mt[k] >> l) & 1ull) && f[k] != ref);
+      if (l == 0) {
+#pragma unroll
+        for (int k = 0; k < PER; k++) ttab[k * NW + wv] = (uint32_t)__popcll(mt[k]);
+      }
+      one_key = __syncthreads_and(same) != 0;
+    }
+    if (one_key) {  // workgroup-uniform
+      // Every tie has the same key (a group of equal scores at the cut): the
+      // cut is the need-th tie in position order, and the candidates are in
+      // position order (index k * NT + tid), so a tie's rank is the ties
+      // before its (batch, wave) entry plus its rank in the wave's ballot --
+      // no search over the list.  Each wave scans the count table itself.
+      constexpr int Q = NTAB >= kWave ? NTAB / kWave : 1;
+      uint32_t v[Q];
+      uint32_t sum = 0;
+#pragma unroll
+      for (int q = 0; q < Q; q++) {
+        const int e = l * Q + q;
+        v[q] = e < NTAB ? ttab[e] : 0u;
+        sum += v[q];
+      }
+      const uint32_t excl = wave_incl_scan(sum) - sum;
+#pragma unroll
+      for (int k = 0; k < PER; k++) {
+        const int e = k * NW + wv;  // entry (k, wave): lane e / Q, position e % Q
+        uint32_t run = excl;
+#pragma unroll
+        for (int q = 0; q < Q; q++)
+          if (q < e % Q) run += v[q];
+        const uint32_t pre = wave_read(run, e / Q);
+        if (((mt[k] >> l) & 1ull) && pre + lane_rank(mt[k]) == need - 1u)
+          sh_thr = Threshold{key_of_i64(f[k]), (uint32_t)c[k], 1};
+      }
+      __syncthreads();
+      thr = sh_thr;
+    } else if (overflow) {  // every valid candidate takes part: the cut is exact on its own
       auto get = [&](int i, uint64_t& u, uint32_t& p) {
         u = key_of_i64(fb[i]);
         p = (uint32_t)cb[i];
