@@ -193,6 +193,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // out so that the compiler neither reorders LDS accesses across it nor
 // counts it: the caller waits for it with an explicit vmcnt.  It has no VGPR
 // destination, so nothing it writes can be reused while it is in flight.
+// m0 is a reserved register that the compiler never holds a value in across
+// other code on gfx950 (it sets m0 right before the few instructions that read
+// it), so the clobber below only documents the write; clang warns that it
+// names a reserved register, which is expected here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
@@ -200,6 +206,7 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
                : "v"(src), "s"(m0)
                : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // 24-bit signed multiply-add, c + a * b modulo 2^32 (one v_mad_i32_i24; the
 // compiler would otherwise split the chain into multiplies and 3-way adds).
