@@ -191,7 +191,9 @@ typedef struct {
  * [3] after refinement + top-k (+ hot resolve), [4] after the miss gather,
  * [5] after the attention kernel, [6] after the combine pass (end).  A NULL
  * entry is skipped (each recorded event costs the stream a few
- * microseconds, so a caller that times one stage records only its two).   */
+ * microseconds, so a caller that times one stage records only its two).
+ * [0] and [1] given together are recorded by the coarse kernel's launch at
+ * the kernel's own start and end, so their interval is that kernel alone.  */
 #define LS_STEP_EVENTS 7
 
 /* Device pointers of one step (see the individual stages for shapes). */

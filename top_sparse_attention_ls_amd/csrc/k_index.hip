@@ -5,6 +5,8 @@
 // Method: LeanSparse (arXiv 2611.04671), Abstract -- coarse-to-fine indexing
 // scores compact key representations and keeps candidates; only those are
 // refined with the original indexer keys (k_refine.hip).
+#include <hip/hip_ext.h>
+
 #include "ls_device.h"
 #include "ls_launch.h"
 #include "ls_bucket.h"
@@ -326,12 +328,20 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
 
 hipError_t launch_coarse_scores(const int8_t* q, const int8_t* w, const uint8_t* kc,
                                 const int32_t* ctx_len, const CoarseWS& ws, int B, int H,
-                                int D, int max_ctx, hipStream_t st) {
+                                int D, int max_ctx, hipStream_t st, hipEvent_t start,
+                                hipEvent_t stop) {
   dim3 grid((max_ctx + kCoarseTokPerWG - 1) / kCoarseTokPerWG, B);
   const int HT = (H + 15) / 16;
-#define LS_COARSE(DD, TT)                                                                  \
-  hipLaunchKernelGGL((k_coarse<DD, TT>), grid, dim3(256), 0, st, q, w, kc, ctx_len, ws.scores, \
-                     ws.hist, H, max_ctx)
+  const bool timed = start != nullptr && stop != nullptr;
+#define LS_COARSE(DD, TT)                                                                    \
+  do {                                                                                       \
+    if (timed)                                                                               \
+      hipExtLaunchKernelGGL((k_coarse<DD, TT>), grid, dim3(256), 0, st, start, stop, 0u, q, w, \
+                            kc, ctx_len, ws.scores, ws.hist, H, max_ctx);                    \
+    else                                                                                     \
+      hipLaunchKernelGGL((k_coarse<DD, TT>), grid, dim3(256), 0, st, q, w, kc, ctx_len,        \
+                         ws.scores, ws.hist, H, max_ctx);                                    \
+  } while (0)
   if (D == 128) {
     if (HT == 1) LS_COARSE(128, 1); else if (HT == 2) LS_COARSE(128, 2);
     else if (HT == 3) LS_COARSE(128, 3); else LS_COARSE(128, 4);

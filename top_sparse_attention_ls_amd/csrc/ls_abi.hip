@@ -299,10 +299,15 @@ int check_ws(int32_t op, const void* desc, void* ws, size_t ws_bytes) {
 int run_coarse(const ls_idx_desc* d, const int8_t* q, const int8_t* w, const uint8_t* kc,
                const int32_t* ctx_len, int32_t* cand, const ls::CoarseWS& ws, hipStream_t st,
                ls_event_t* ev) {
+  // events [0] and [1] together: the launch records them at the coarse
+  // kernel's own start and end; either alone: a record command in the stream
+  const bool both = ev && ev[0] && ev[1];
+  if (ev && ev[0] && !both) LS_HIP(hipEventRecord((hipEvent_t)ev[0], st), "event record");
   LS_HIP(ls::launch_coarse_scores(q, w, kc, ctx_len, ws, d->batch, d->n_heads, d->head_dim,
-                                  d->max_ctx, st),
+                                  d->max_ctx, st, both ? (hipEvent_t)ev[0] : nullptr,
+                                  both ? (hipEvent_t)ev[1] : nullptr),
          "coarse score launch");
-  if (ev && ev[1]) LS_HIP(hipEventRecord((hipEvent_t)ev[1], st), "event record");
+  if (ev && ev[1] && !both) LS_HIP(hipEventRecord((hipEvent_t)ev[1], st), "event record");
   LS_HIP(ls::launch_topc_select(ctx_len, ws, cand, d->batch, d->max_ctx, d->n_cand, st),
          "candidate select launch");
   return LS_OK;
@@ -704,7 +709,6 @@ int decode_step_impl(const ls_step_desc* desc, const ls_step_io* io, void* ws_de
   hipStream_t st = (hipStream_t)stream;
   ls_event_t* ev = io->stage_events;
   if (clear_bytes) LS_HIP(ls::launch_fill_zero(ws_dev, clear_bytes, st), "scratch clear");
-  if (ev && ev[0]) LS_HIP(hipEventRecord((hipEvent_t)ev[0], st), "event record");
   LS_TRY(run_coarse(id, io->q_idx_dev, io->w_idx_dev, io->kc_dev, io->ctx_len_dev, io->cand_dev,
                     cws, st, ev));
   if (ev && ev[2]) LS_HIP(hipEventRecord((hipEvent_t)ev[2], st), "event record");

@@ -96,9 +96,12 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_pack_coarse(const int8_t* k8, uint8_t* kc, int64_t n_rows, int dim,
                               hipStream_t st);
 
+// With start and stop events given, the launch itself records them when the
+// kernel begins and ends (the kernel's own duration, no separate commands).
 hipError_t launch_coarse_scores(const int8_t* q, const int8_t* w, const uint8_t* kc,
                                 const int32_t* ctx_len, const CoarseWS& ws, int B, int H,
-                                int D, int max_ctx, hipStream_t st);
+                                int D, int max_ctx, hipStream_t st,
+                                hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 hipError_t launch_topc_select(const int32_t* ctx_len, const CoarseWS& ws, int32_t* cand, int B,
                               int max_ctx, int C, hipStream_t st);
