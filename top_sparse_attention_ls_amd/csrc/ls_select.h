@@ -320,14 +320,17 @@ __device__ Threshold wave_threshold(const Get& get, int n, uint32_t need, uint32
 // The tie search of the selections: the exact threshold over a list whose
 // keys lie in [key_lo, key_hi] (a histogram bucket's range).  The first key
 // digit -- the only step that touches every entry -- is counted by the whole
-// workgroup (NT threads), and the entries that fall in the chosen digit are
-// copied to sc by the whole workgroup; one wave then finishes over that short
-// list (wave_threshold).  With more than kThrScratch entries in the chosen
-// digit (or nothing to split on) the wave continues over the whole list,
-// up to kWaveTies entries; beyond that the whole workgroup searches it
-// (block_threshold), as one wave walking every digit of a long list -- a
-// large group of equal scores at the cut -- is the slow case.  Every thread
-// returns the threshold.  Contains workgroup barriers; sh_thr is LDS.
+// workgroup (NT threads; over more than kWaveTies entries with one LDS add per
+// wave and bin, hist_add, since a long list may be one run of equal keys, whose
+// per-lane adds to one bin would serialise), and the entries that fall in
+// the chosen digit are copied to sc by the whole workgroup; one wave then
+// finishes over that short list (wave_threshold).  With more than
+// kThrScratch entries in the chosen digit (or nothing to split on) the wave
+// continues over the whole list, up to kWaveTies entries; beyond that the
+// whole workgroup searches it (block_threshold), as one wave walking every
+// digit of a long list -- a large group of equal scores at the cut -- is the
+// slow case.  Every thread returns the threshold.  Contains workgroup
+// barriers; sh_thr is LDS.
 constexpr int kWaveTies = 2048;
 
 template <int NT, class Get>
