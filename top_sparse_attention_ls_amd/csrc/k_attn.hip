@@ -229,10 +229,23 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
     }
   };
 
-  // Prologue in two round trips.  First each lane's own DMA rows of the
-  // first tiles and the split's row ids (to be staged in LDS) -- with their
-  // pool positions, gathering; the first tiles' DMA then starts at once, and
-  // the copy's pool reads and the query load while it is in flight.
+  // Prologue in two round trips.  First the query (which needs no row id),
+  // each lane's own DMA rows of the first tiles and the split's row ids (to
+  // be staged in LDS) -- with their pool positions, gathering; the first
+  // tiles' DMA then starts at once, with the copy's pool reads beside it.
+  // The query (147 KB per workgroup at 128 heads of 576 dims) thus comes in
+  // while the row ids are awaited rather than competing with the first tiles.
+  // B operand of S^T = K Q^T: head n, dims 16 ks + 8 half .. +7 (loaded
+  // unconditionally from a clamped head, then selected)
+  v8bf qB[QK_STEPS];
+  {
+    const uint16_t* qh = q + ((size_t)b * Hq + min(h, Hq - 1)) * DQK + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < QK_STEPS; ks++) {
+      const v8u16 v = *(const v8u16*)(qh + 16 * ks);
+      qB[ks] = __builtin_bit_cast(v8bf, h_ok ? v : v8u16{0, 0, 0, 0, 0, 0, 0, 0});
+    }
+  }
   int32_t rv[kRidIters], sv[kRidIters];
   {
     int32_t r0[NBUF - 1], s0[NBUF - 1];
@@ -267,17 +280,6 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
       m_list += __popcll(mask);
     }
     if (m_list > 0) copy_load(0);
-  }
-  // B operand of S^T = K Q^T: head n, dims 16 ks + 8 half .. +7 (loaded
-  // unconditionally from a clamped head, then selected)
-  v8bf qB[QK_STEPS];
-  {
-    const uint16_t* qh = q + ((size_t)b * Hq + min(h, Hq - 1)) * DQK + 8 * half;
-#pragma unroll
-    for (int ks = 0; ks < QK_STEPS; ks++) {
-      const v8u16 v = *(const v8u16*)(qh + 16 * ks);
-      qB[ks] = __builtin_bit_cast(v8bf, h_ok ? v : v8u16{0, 0, 0, 0, 0, 0, 0, 0});
-    }
   }
   // Everything has landed (the first tiles too) before the loop, so the
   // compiler has no load of its own outstanding there (it would otherwise
