@@ -107,7 +107,9 @@ def test_index_coarse_negative_weights(ls):
     run_coarse_case(ls, inp, [9000, 8999], 777)
 
 
-@pytest.mark.parametrize("H,D", [(4, 64), (20, 64), (33, 128), (64, 64)])
+# up to 16 heads one 16-head tile, more heads 32-head tiles (one or two)
+@pytest.mark.parametrize("H,D", [(4, 64), (16, 128), (17, 128), (20, 64), (32, 128), (33, 128),
+                                 (64, 64)])
 def test_index_coarse_head_shapes(ls, H, D):
     wl = dataclasses.replace(SHRUNK, batch=2, ctx=6000, idx_heads=H, idx_dim=D)
     inp = idx_inputs(wl)

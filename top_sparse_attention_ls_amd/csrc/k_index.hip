@@ -70,7 +70,9 @@ hipError_t launch_pack_coarse(const int8_t* k8, uint8_t* kc, int64_t n_rows, int
 //
 // As an int8 GEMM [heads x D] x [D x tokens] on v_mfma_i32_16x16x64_i8: the
 // A operand is the int8 query (16 heads per tile, held in VGPRs for the
-// whole kernel), the B operand is 16 tokens' compact keys.  A stored nibble
+// whole kernel), the B operand is 16 tokens' compact keys.  This form runs
+// requests of up to 16 heads; k_coarse32 below, the same scheme on 32-head
+// tiles, runs more.  A stored nibble
 // b (two's complement, value v in [-8, 7]) read as b ^ 8 is the offset-binary
 // value v + 8 in [0, 15], so one xor and one mask widen it to a byte and the
 // MFMA returns dot + c_h with c_h = 8 * sum_d q[h][d]; the query is laid out
@@ -326,28 +328,230 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
   }
 }
 
+// ------------------------------------------- coarse score, 32-head tiles ----
+//
+// The same scores for more than 16 heads, on v_mfma_i32_32x32x32_i8: one
+// instruction does the work of two 16x16x64 ones, and an MFMA instruction
+// holds the SIMD's issue for about the same few cycles whatever its size, so
+// halving their number leaves more issue to the VALU epilogue beside them
+// (at two waves per SIMD, 64 independent VALU operations beside eight
+// 16x16x64 MFMAs took 289 ns per iteration, beside four 32x32x32 ones
+// 266 ns, and alone 239 ns).
+//
+// Lane l, t = l % 32, hf = l / 32.  A row t is head 32 mt + t, B column t is
+// token 32 tt + t of the wave's 64-token step, and both hold the 16 dims of
+// K-slice hf of each K-step: with LB = D / 4 bytes of the packed row per
+// half, K-step s of half hf is packed bytes [LB hf + 8 s, +8), widened to
+// their 8 low nibbles (even dims) then their 8 high nibbles (odd dims), and
+// the query is laid out alike.  D register r of lane l holds head 32 mt +
+// 8 (r/4) + 4 hf + r%4 of token t, so a lane's heads give half of its
+// token's score and lane l ^ 32 the other half: one 32-lane swap finishes
+// both tiles, token l of the step in lane l.  Offsets, exactness and the
+// fused histogram are as in k_coarse.
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// Query operand for head row qh, half hf, K-step s: dims [2 (LB hf + 8 s),
+// +16), the 8 even ones then the 8 odd ones.
+template <int D>
+__device__ __forceinline__ v4i coarse32_q_operand(const int8_t* qh, int hf, int s) {
+  constexpr int LB = D / 4;
+  const v4i a = *(const v4i*)(qh + 2 * (LB * hf + 8 * s));
+  const uint32_t w0 = (uint32_t)a[0], w1 = (uint32_t)a[1], w2 = (uint32_t)a[2],
+                 w3 = (uint32_t)a[3];
+  return v4i{(int)__builtin_amdgcn_perm(w1, w0, 0x06040200u),
+             (int)__builtin_amdgcn_perm(w3, w2, 0x06040200u),
+             (int)__builtin_amdgcn_perm(w1, w0, 0x07050301u),
+             (int)__builtin_amdgcn_perm(w3, w2, 0x07050301u)};
+}
+
+template <int D, int HT2>
+__global__ __launch_bounds__(256) void k_coarse32(const int8_t* __restrict__ q,
+                                                  const int8_t* __restrict__ w,
+                                                  const uint8_t* __restrict__ kc,
+                                                  const int32_t* __restrict__ ctx_len,
+                                                  int32_t* __restrict__ scores,
+                                                  uint32_t* __restrict__ hist, int H,
+                                                  int max_ctx) {
+  constexpr int KB = D / 2;   // packed bytes per token
+  constexpr int LB = D / 4;   // packed bytes per lane (half a row) per token
+  constexpr int NL = LB / 16;  // 16-byte loads per lane per token tile
+  constexpr int KS = D / 32;   // K-steps of 32 dims
+  static_assert(D == 64 || D == 128, "indexer dim");
+  __shared__ uint32_t lhist[kCoarseBins];
+  __shared__ __attribute__((aligned(16))) int32_t lsc[kCoarseTokPerWG];
+
+  const int b = blockIdx.y;
+  const int n_valid = clamp_ctx(ctx_len, b, max_ctx);
+  const int t_begin = blockIdx.x * kCoarseTokPerWG;
+  if (t_begin >= n_valid) return;
+  const int t_end = min(t_begin + kCoarseTokPerWG, n_valid);
+
+  for (int i = threadIdx.x; i < kCoarseBins; i += 256) lhist[i] = 0;
+
+  const int l = lane_id(), t = l & 31, hf = l >> 5;
+  const int8_t* qb = q + (size_t)b * H * D;
+  // c_h = 8 * sum_d q[h][d] of every head, through LDS
+  __shared__ int32_t hsum[64];
+  if (threadIdx.x < H) {
+    const v4i* qh = (const v4i*)(qb + (size_t)threadIdx.x * D);
+    int32_t sacc = 0;
+#pragma unroll
+    for (int j = 0; j < D / 16; j++) {
+      const v4i v = qh[j];
+#pragma unroll
+      for (int k = 0; k < 4; k++) sacc = __builtin_amdgcn_sdot4(v[k], 0x01010101, sacc, false);
+    }
+    hsum[threadIdx.x] = 8 * sacc;
+  }
+  v4i qa[HT2][KS];
+  int32_t wv[HT2][16];
+#pragma unroll
+  for (int mt = 0; mt < HT2; mt++) {
+    // unconditional loads from clamped heads, then selected
+    const int h = 32 * mt + t;
+#pragma unroll
+    for (int s = 0; s < KS; s++) {
+      const v4i v = coarse32_q_operand<D>(qb + (size_t)min(h, H - 1) * D, hf, s);
+      qa[mt][s] = h < H ? v : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int hh = 32 * mt + 8 * (r >> 2) + 4 * hf + (r & 3);
+      const int32_t wr = (int32_t)w[(size_t)b * H + min(hh, H - 1)];
+      wv[mt][r] = hh < H ? wr : 0;
+    }
+  }
+  __syncthreads();
+  int32_t cv[HT2][16];
+  uint32_t k_lane = 0;  // sum of w * c_h over this lane's heads
+#pragma unroll
+  for (int mt = 0; mt < HT2; mt++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int hh = 32 * mt + 8 * (r >> 2) + 4 * hf + (r & 3);
+      cv[mt][r] = hh < H ? hsum[hh] : 0;
+      k_lane += (uint32_t)(wv[mt][r] * cv[mt][r]);
+    }
+
+  // this workgroup's compact keys (tokens past t_end read as zero)
+  const __amdgpu_buffer_rsrc_t kres = buffer_rsrc(kc + ((size_t)b * max_ctx + t_begin) * KB,
+                                                  (uint32_t)(t_end - t_begin) * KB);
+  const uint32_t lane_off = (uint32_t)(t * KB + hf * LB);
+  // the two 32-token tiles of the 64-token step at base (counted from the
+  // workgroup's first token): scalar tile offset, constant lane offset
+  auto load = [&](int base, v4i (&r)[2][NL]) {
+#pragma unroll
+    for (int tt = 0; tt < 2; tt++) {
+      const int so = __builtin_amdgcn_readfirstlane((base + 32 * tt) * KB);
+#pragma unroll
+      for (int i = 0; i < NL; i++)
+        r[tt][i] = __builtin_bit_cast(
+            v4i, __builtin_amdgcn_raw_buffer_load_b128(kres, lane_off + 16u * i, so, 0));
+    }
+  };
+
+  // One 64-token step: both tiles' MFMAs, then both epilogues.
+  auto process = [&](int base, const v4i (&raw)[2][NL]) {
+    const uint32_t m = 0x0F0F0F0Fu, f = 0x08080808u;
+    v16i acc[2][HT2];
+#pragma unroll
+    for (int tt = 0; tt < 2; tt++) {
+      uint32_t x[4 * NL];
+#pragma unroll
+      for (int i = 0; i < NL; i++)
+#pragma unroll
+        for (int k = 0; k < 4; k++) x[4 * i + k] = (uint32_t)raw[tt][i][k];
+#pragma unroll
+      for (int s = 0; s < KS; s++) {
+        const v4i bop = v4i{(int)((x[2 * s] & m) ^ f), (int)((x[2 * s + 1] & m) ^ f),
+                            (int)(((x[2 * s] >> 4) & m) ^ f),
+                            (int)(((x[2 * s + 1] >> 4) & m) ^ f)};
+#pragma unroll
+        for (int mt = 0; mt < HT2; mt++)
+          acc[tt][mt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+              qa[mt][s], bop, s == 0 ? v16i{} : acc[tt][mt], 0, 0, 0);
+      }
+    }
+    uint32_t part[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; tt++) {
+      uint32_t s = 0u - k_lane;
+#pragma unroll
+      for (int mt = 0; mt < HT2; mt++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) s = mad_i24(wv[mt][r], max(acc[tt][mt][r], cv[mt][r]), s);
+      part[tt] = s;
+    }
+    // lanes l and l ^ 32 hold the two halves of each token's head sum
+    swap32(part[0], part[1]);
+    const int32_t score = (int32_t)(part[0] + part[1]);
+    const int tok = base + l;
+    // no branch: lanes past t_end land on slots that are never written out
+    // (or on the last slot, clamped), and they add 0 to the histogram
+    lsc[min(tok - t_begin, kCoarseTokPerWG - 1)] = score;
+    atomicAdd(&lhist[coarse_bucket(score)], tok < t_end ? 1u : 0u);
+  };
+
+  // the register ring of k_coarse (kCoarseDepth buffers, whole groups of
+  // steps in a straight-line loop body, the last steps from loaded buffers)
+  constexpr int S = 256;  // tokens per workgroup step (4 waves x 64)
+  constexpr int R = kCoarseDepth;
+  const int base0 = __builtin_amdgcn_readfirstlane(t_begin + wave_id() * 64);
+  const int n_steps = base0 < t_end ? (t_end - base0 + S - 1) / S : 0;  // wave-uniform
+  if (n_steps > 0) {
+    v4i buf[R][2][NL];
+#pragma unroll
+    for (int k = 0; k < R - 1; k++) load(base0 - t_begin + k * S, buf[k]);
+    int k0 = 0;
+    for (; k0 + R <= n_steps; k0 += R) {
+#pragma unroll
+      for (int j = 0; j < R; j++) {
+        load(base0 - t_begin + (k0 + j + R - 1) * S, buf[(j + R - 1) % R]);
+        __builtin_amdgcn_sched_barrier(0);
+        process(base0 + (k0 + j) * S, buf[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < R - 1; j++)
+      if (k0 + j < n_steps) process(base0 + (k0 + j) * S, buf[j]);
+  }
+  __syncthreads();
+  {
+    const int n_tok = t_end - t_begin;
+    int32_t* sb = scores + (size_t)b * max_ctx + t_begin;
+    const int n4 = ((uintptr_t)sb & 15) == 0 ? n_tok / 4 : 0;
+    for (int i = threadIdx.x; i < n4; i += 256) *(int4*)(sb + 4 * i) = *(const int4*)&lsc[4 * i];
+    for (int j = 4 * n4 + threadIdx.x; j < n_tok; j += 256) sb[j] = lsc[j];
+  }
+  uint32_t* hb = hist + (size_t)b * kCoarseBins;
+  for (int i = threadIdx.x; i < kCoarseBins; i += 256) {
+    uint32_t c = lhist[i];
+    if (c) atomicAdd(&hb[i], c);
+  }
+}
+
 hipError_t launch_coarse_scores(const int8_t* q, const int8_t* w, const uint8_t* kc,
                                 const int32_t* ctx_len, const CoarseWS& ws, int B, int H,
                                 int D, int max_ctx, hipStream_t st, hipEvent_t start,
                                 hipEvent_t stop) {
   dim3 grid((max_ctx + kCoarseTokPerWG - 1) / kCoarseTokPerWG, B);
-  const int HT = (H + 15) / 16;
   const bool timed = start != nullptr && stop != nullptr;
-#define LS_COARSE(DD, TT)                                                                    \
+#define LS_COARSE(KERN)                                                                      \
   do {                                                                                       \
     if (timed)                                                                               \
-      hipExtLaunchKernelGGL((k_coarse<DD, TT>), grid, dim3(256), 0, st, start, stop, 0u, q, w, \
-                            kc, ctx_len, ws.scores, ws.hist, H, max_ctx);                    \
+      hipExtLaunchKernelGGL(KERN, grid, dim3(256), 0, st, start, stop, 0u, q, w, kc, ctx_len, \
+                            ws.scores, ws.hist, H, max_ctx);                                 \
     else                                                                                     \
-      hipLaunchKernelGGL((k_coarse<DD, TT>), grid, dim3(256), 0, st, q, w, kc, ctx_len,        \
-                         ws.scores, ws.hist, H, max_ctx);                                    \
+      hipLaunchKernelGGL(KERN, grid, dim3(256), 0, st, q, w, kc, ctx_len, ws.scores, ws.hist, \
+                         H, max_ctx);                                                        \
   } while (0)
-  if (D == 128) {
-    if (HT == 1) LS_COARSE(128, 1); else if (HT == 2) LS_COARSE(128, 2);
-    else if (HT == 3) LS_COARSE(128, 3); else LS_COARSE(128, 4);
+  // up to 16 heads: one 16-head tile; more: 32-head tiles (up to 64 heads)
+  if (H <= 16) {
+    if (D == 128) LS_COARSE((k_coarse<128, 1>)); else LS_COARSE((k_coarse<64, 1>));
+  } else if (H <= 32) {
+    if (D == 128) LS_COARSE((k_coarse32<128, 1>)); else LS_COARSE((k_coarse32<64, 1>));
   } else {
-    if (HT == 1) LS_COARSE(64, 1); else if (HT == 2) LS_COARSE(64, 2);
-    else if (HT == 3) LS_COARSE(64, 3); else LS_COARSE(64, 4);
+    if (D == 128) LS_COARSE((k_coarse32<128, 2>)); else LS_COARSE((k_coarse32<64, 2>));
   }
 #undef LS_COARSE
   return hipGetLastError();
