@@ -205,6 +205,8 @@ def cmd_counters(args):
         base = k.split("<")[0].replace("ls::", "")
         if base == "k_attn_mfma" and k.replace(" ", "").endswith(",true>"):
             base = "k_attn_fused"  # the miss gather folded into the tile DMA
+        if base == "k_coarse32":
+            base = "k_coarse"  # the same pass on 32-head tiles
         row = ["`%s`" % k, str(launches[k])]
         entry = {"launches": launches[k], "counters": d}
         if "FETCH_SIZE" in counters and "WRITE_SIZE" in counters:
