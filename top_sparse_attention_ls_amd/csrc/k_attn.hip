@@ -345,9 +345,10 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
         (uint32_t)__ballot(l < kTileR && rid_lds[t * kTileR + (l & 31)] != -1);
 
     // S^T = K Q^T (32 rows x 32 heads): operand reads run 4 steps ahead of
-    // their MFMAs, and even/odd steps feed two accumulators so consecutive
-    // MFMAs never wait on each other.
-    v16f sacc0 = {}, sacc1 = {};
+    // their MFMAs, all on one accumulator.  Back-to-back MFMAs on the same
+    // accumulator pass it along inside the matrix core, and a second chain
+    // would cost 16 registers the wave does not have (at 512 they spill).
+    v16f sacc = {};
     {
       v8u16 ab[4];
 #pragma unroll
@@ -356,12 +357,8 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
       for (int ks = 0; ks < QK_STEPS; ks++) {
         const v8u16 a = ab[ks & 3];
         if (ks + 4 < QK_STEPS) ab[ks & 3] = *(const v8u16*)(cur + qk_off + 1024 * (ks + 4));
-        if (ks & 1)
-          sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), qB[ks],
-                                                          sacc1, 0, 0, 0);
-        else
-          sacc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), qB[ks],
-                                                          sacc0, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), qB[ks], sacc,
+                                                       0, 0, 0);
       }
       // scheduling contract for the loop above: 4 reads, then MFMA/read pairs
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -372,7 +369,6 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
-    const v16f sacc = sacc0 + sacc1;
     // phase fences for the scheduler: keep the PV operand reads from being
     // hoisted over QK and the softmax, where they would starve QK of VGPRs
     __builtin_amdgcn_sched_barrier(0);
