@@ -250,12 +250,9 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
     n_tie = 0;
   }
   __syncthreads();
-  uint32_t bk[PER];
 #pragma unroll
-  for (int k = 0; k < PER; k++) {
-    bk[k] = wide_bucket(f[k]);
-    if (c[k] >= 0) atomicAdd(&hist[bk[k]], 1u);
-  }
+  for (int k = 0; k < PER; k++)
+    if (c[k] >= 0) atomicAdd(&hist[wide_bucket(f[k])], 1u);
   __syncthreads();
 
   // bucket where the count from the top crosses K (thread 0: top bins)
@@ -290,12 +287,17 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
     for (int k = 0; k < PER; k++) sel[k] = c[k] >= 0;
   } else {
     const uint32_t need = need_all - sh_above;  // 1 <= need <= ties
+    // bucket beta holds the scores [b_lo, b_hi] (buckets are contiguous
+    // ranges, so comparing a score with them places it as its bucket would,
+    // without keeping the buckets in registers)
+    int64_t b_lo, b_hi;
+    wide_bucket_range(beta, b_lo, b_hi);
     // the wave's ties of all PER batches, with one reservation in the list
     uint64_t mt[PER];
     uint32_t wave_ties = 0;
 #pragma unroll
     for (int k = 0; k < PER; k++) {
-      mt[k] = __ballot(c[k] >= 0 && (int)bk[k] == beta);
+      mt[k] = __ballot(c[k] >= 0 && f[k] >= b_lo && f[k] <= b_hi);
       wave_ties += (uint32_t)__popcll(mt[k]);
     }
     if (wave_ties) {  // wave-uniform
@@ -373,10 +375,8 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
         u = key_of_i64(tie_f[i]);
         p = (uint32_t)tie_c[i];
       };
-      int64_t lo, hi;
-      wide_bucket_range(beta, lo, hi);
-      thr = tie_threshold<NT>(get, (int)nt, need, ssh, &thr_sc, &sh_thr, key_of_i64(lo),
-                              key_of_i64(hi), pos_bits_below(max_ctx));
+      thr = tie_threshold<NT>(get, (int)nt, need, ssh, &thr_sc, &sh_thr, key_of_i64(b_lo),
+                              key_of_i64(b_hi), pos_bits_below(max_ctx));
     }
 #pragma unroll
     for (int k = 0; k < PER; k++) {
@@ -384,8 +384,8 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(
       if (overflow)
         sel[k] = v && keep(thr, key_of_i64(f[k]), (uint32_t)c[k]);
       else
-        sel[k] = v && ((int)bk[k] > beta ||
-                       ((int)bk[k] == beta && keep(thr, key_of_i64(f[k]), (uint32_t)c[k])));
+        sel[k] = v && (f[k] > b_hi ||
+                       (f[k] >= b_lo && keep(thr, key_of_i64(f[k]), (uint32_t)c[k])));
     }
   }
 
