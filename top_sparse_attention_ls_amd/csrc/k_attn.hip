@@ -345,9 +345,10 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void k_attn_mfma(
         (uint32_t)__ballot(l < kTileR && rid_lds[t * kTileR + (l & 31)] != -1);
 
     // S^T = K Q^T (32 rows x 32 heads): operand reads run 4 steps ahead of
-    // their MFMAs, all on one accumulator.  Back-to-back MFMAs on the same
-    // accumulator pass it along inside the matrix core, and a second chain
-    // would cost 16 registers the wave does not have (at 512 they spill).
+    // their MFMAs, all on one accumulator.  Back-to-back MFMAs on one AGPR
+    // accumulator measured faster here than two alternating ones, and a
+    // second chain would cost 16 registers the wave does not have (at 512
+    // the kernel spills).
     v16f sacc = {};
     {
       v8u16 ab[4];
