@@ -397,7 +397,7 @@ def cpu_baseline(wl, st, n_single, n_parallel):
 
 
 STAGE_KERNELS = {
-    "coarse_score": "k_coarse",
+    "coarse_score": "k_coarse32 (k_coarse up to 16 heads)",
     "candidate_select": "k_topc_filter + k_topc_emit",
     "refine_topk_resolve": "k_refine + k_topk_hist",
     "miss_gather": "k_hot_gather",
@@ -581,7 +581,7 @@ def run_decode(ls, synth, wl, steps, warmup, replicas, full=True, n_single=0, n_
         # the dominant kernel of the step against the HBM peak (live events);
         # the whole step's fraction is hbm_roofline_step.frac
         "roofline": {
-            "kernel": "coarse_score (k_coarse)",
+            "kernel": "coarse_score (k_coarse32)",
             "scope": "dominant kernel; whole step in hbm_roofline_step",
             "bound": "hbm",
             "achieved": round(achieved, 1),
