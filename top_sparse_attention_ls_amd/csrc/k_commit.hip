@@ -76,6 +76,12 @@ __global__ __launch_bounds__(kCommitThreads) void k_cache_commit(
     uint32_t now_arg, const uint32_t* __restrict__ now_dev, int32_t* __restrict__ out,
     int32_t* __restrict__ rows, int32_t* __restrict__ n_ins) {
   __shared__ uint32_t key[kCommitMaxSlots];        // stamps, then the victim list
+  // The key cache (16384 slots per request) keeps each slot's token in LDS
+  // and writes its stamps back whole; the hot buffer (a few thousand slots)
+  // measured faster with per-slot stamp stores and a read of each victim's
+  // token at the end.
+  constexpr bool kWholeStamps = MODE == kCommitKey;
+  __shared__ int32_t s2p_l[kWholeStamps ? kCommitMaxSlots : 1];  // slot tokens before the commit
   __shared__ uint32_t hitbits[kCommitMaxSlots / 32];
   __shared__ uint32_t hist[kDigitBins];
   __shared__ uint32_t sh_scan[kCommitThreads / kWave];
@@ -99,8 +105,16 @@ __global__ __launch_bounds__(kCommitThreads) void k_cache_commit(
   for (int i = 0; i < EPT; i++) t[i] = eb[min(e0 + i, n - 1)];
   {
     uint32_t sv[kSlotIters];
+    int32_t pv[kSlotIters];
 #pragma unroll
-    for (int i = 0; i < kSlotIters; i++) sv[i] = stb[min(tid + kCommitThreads * i, S - 1)];
+    for (int i = 0; i < kSlotIters; i++) {
+      sv[i] = 0u;
+      pv[i] = -1;
+      if (kCommitThreads * i < S) {  // uniform: only the rounds that hold slots
+        sv[i] = stb[min(tid + kCommitThreads * i, S - 1)];
+        if (kWholeStamps) pv[i] = s2p[min(tid + kCommitThreads * i, S - 1)];
+      }
+    }
 #pragma unroll
     for (int i = 0; i < EPT; i++) {
       const bool ok = e0 + i < n && t[i] >= 0 && t[i] < max_ctx;
@@ -121,7 +135,10 @@ __global__ __launch_bounds__(kCommitThreads) void k_cache_commit(
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < kSlotIters; i++)
-      if (tid + kCommitThreads * i < S) key[tid + kCommitThreads * i] = sv[i];
+      if (tid + kCommitThreads * i < S) {
+        key[tid + kCommitThreads * i] = sv[i];
+        if (kWholeStamps) s2p_l[tid + kCommitThreads * i] = pv[i];
+      }
   }
   for (int w = tid; w < kCommitMaxSlots / 32; w += kCommitThreads) hitbits[w] = 0u;
   __syncthreads();
@@ -157,9 +174,12 @@ __global__ __launch_bounds__(kCommitThreads) void k_cache_commit(
       else elig |= 1u << i;
     }
   }
-  uint32_t n_m, n_h;
-  const uint32_t m_base = block_excl_scan<kCommitThreads>(n_m_t, sh_scan, &n_m);
-  block_excl_scan<kCommitThreads>(n_hit_t, sh_scan, &n_h);
+  // misses (low half) and hits (high half) in one scan: each total is at
+  // most 16384, so the halves never carry into each other
+  uint32_t tot_mh;
+  const uint32_t m_base =
+      block_excl_scan<kCommitThreads>(n_m_t | (n_hit_t << 16), sh_scan, &tot_mh) & 0xFFFFu;
+  const uint32_t n_m = tot_mh & 0xFFFFu, n_h = tot_mh >> 16;
   const uint32_t n_v = min(n_m, (uint32_t)S - n_h);
 
   // the range of the eligible stamps
@@ -262,22 +282,43 @@ __global__ __launch_bounds__(kCommitThreads) void k_cache_commit(
   }
   uint32_t tot_v;
   uint32_t v_rank = block_excl_scan<kCommitThreads>(v_t, sh_scan, &tot_v);
-  // new stamps (hit or victim: now), written by slot owner; then the LDS
-  // words are free to hold the victim list
+  // misses in entry order move into the victims (tot_v equals n_v; the
+  // minimum only keeps every victim read inside the list)
+  const uint32_t n_use = min(n_v, tot_v);
+  if (kWholeStamps) {
+    // new stamps (hit or victim: now) into the LDS copy by each slot's
+    // owner, and the token a used victim held loses its slot (cleared by the
+    // owner: such a token is cached, so no entry of this step names it)
 #pragma unroll
-  for (int i = 0; i < kCommitMaxSlots / kCommitThreads; i++) {
-    const int s = s0 + i;
-    if (i < SE && s < S && (!((elig >> i) & 1u) || ((vic >> i) & 1u))) stb[s] = now;
+    for (int i = 0; i < kCommitMaxSlots / kCommitThreads; i++) {
+      const int s = s0 + i;
+      if (i < SE && s < S && (!((elig >> i) & 1u) || ((vic >> i) & 1u))) key[s] = now;
+    }
+    uint32_t r = v_rank;
+#pragma unroll
+    for (int i = 0; i < kCommitMaxSlots / kCommitThreads; i++)
+      if ((vic >> i) & 1u) {
+        const int32_t old = s2p_l[s0 + i];
+        if (r < n_use && old >= 0 && old < max_ctx) p2s[old] = -1;
+        r++;
+      }
+    __syncthreads();
+    // every stamp written back whole (coalesced)
+    for (int s = tid; s < S; s += kCommitThreads) stb[s] = key[s];
+  } else {
+    // new stamps (hit or victim: now), written by each slot's owner
+#pragma unroll
+    for (int i = 0; i < kCommitMaxSlots / kCommitThreads; i++) {
+      const int s = s0 + i;
+      if (i < SE && s < S && (!((elig >> i) & 1u) || ((vic >> i) & 1u))) stb[s] = now;
+    }
   }
-  __syncthreads();
+  __syncthreads();  // then the LDS words are free to hold the victim list
 #pragma unroll
   for (int i = 0; i < kCommitMaxSlots / kCommitThreads; i++)
     if ((vic >> i) & 1u) key[v_rank++] = (uint32_t)(s0 + i);
   __syncthreads();
 
-  // misses in entry order move into the victims (tot_v equals n_v; the
-  // minimum only keeps every victim read inside the list)
-  const uint32_t n_use = min(n_v, tot_v);
   uint32_t jr[EPT];
   int32_t v[EPT], old[EPT];
   uint32_t j = m_base;
@@ -288,8 +329,9 @@ __global__ __launch_bounds__(kCommitThreads) void k_cache_commit(
     v[i] = (m && j < n_use) ? (int32_t)min(key[j], (uint32_t)(S - 1)) : -1;
     j += m ? 1u : 0u;
   }
+  // the token each used victim held (key cache: already cleared above)
 #pragma unroll
-  for (int i = 0; i < EPT; i++) old[i] = s2p[max(v[i], 0)];
+  for (int i = 0; i < EPT; i++) old[i] = kWholeStamps ? -1 : s2p[max(v[i], 0)];
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < EPT; i++) {
