@@ -233,6 +233,10 @@ def decode_request(q_idx, w_idx, keys, ctx, n_cand, topk, q_attn_bits, scale, *,
     if pos2slot is not None:
         p2s = _c(pos2slot, np.int32)
         assert hot_bits.flags.c_contiguous and pool_bits.flags.c_contiguous
+        # a row of the hot buffer and the pool is one latent row of row_stride
+        # elements (the C side indexes both with it)
+        assert hot_bits.shape[1] == row_stride and pool_bits.shape[1] == row_stride, \
+            "hot/pool rows must be row_stride elements"
         hot_slots = hot_bits.shape[0] - topk
         kc = vc = None
     else:

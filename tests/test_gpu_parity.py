@@ -673,7 +673,8 @@ def mla_step_case(ls, wl, ctx_len, key_rate=None):
         hot_b = bits(hot[b]).copy()
         r = orc.decode_request(inp["q"][b].numpy(), inp["w"][b].numpy(), inp["keys"][b].numpy(),
                                ctx_len[b], wl.n_cand, wl.topk, bits(qa[b]), wl.scale,
-                               pos2slot=np_(pos2slot[b]), hot_bits=hot_b, pool_bits=bits(pool[b]))
+                               pos2slot=np_(pos2slot[b]), hot_bits=hot_b, pool_bits=bits(pool[b]),
+                               v_dim=wl.v_dim, row_stride=wl.qk_dim)
         assert np_(step.cand)[b].tolist() == r["cand"].tolist(), b
         assert np_(step.topk)[b].tolist() == r["topk"].tolist(), b
         assert np_(step.topk_score)[b].tolist() == r["topk_score"].tolist(), b
@@ -703,6 +704,19 @@ def test_decode_step_more_than_16384_candidates(ls):
     wl = dataclasses.replace(SHRUNK, batch=2, ctx=40000, n_cand=20000, topk=2048,
                              hot_slots=4096, planted=400)
     mla_step_case(ls, wl, [40000, 23000])
+
+
+def test_decode_step_many_requests_multi_chunk_emit(ls):
+    # 256 requests: each emit workgroup takes both 16384-position chunks of
+    # its request in one run; latent rows of 16 elements take the attention
+    # without matrix cores and the separate miss gather; most requests are
+    # short, every 32nd spans both chunks
+    B = 256
+    wl = dataclasses.replace(SHRUNK, batch=B, ctx=16400, n_cand=512, topk=64, hot_slots=128,
+                             planted=20, idx_heads=4, idx_dim=64, q_heads=8, qk_dim=16, v_dim=16)
+    ctx_len = [16400 if b % 32 == 0 else (16384 + 9 if b % 32 == 16 else 200 + (37 * b) % 900)
+               for b in range(B)]
+    mla_step_case(ls, wl, ctx_len)
 
 
 def test_decode_step_deterministic(ls):
