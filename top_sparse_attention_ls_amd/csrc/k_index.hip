@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
                                                 const int32_t* __restrict__ ctx_len,
                                                 int32_t* __restrict__ scores,
                                                 uint32_t* __restrict__ hist, int H,
-                                                int max_ctx) {
+                                                int max_ctx, int tpw) {
   constexpr int KB = D / 2;       // packed bytes per token
   constexpr int NMF = D / 64;     // MFMAs (K = 64) per head tile
   constexpr int LB = KB / 4;      // bytes per lane per token
@@ -169,9 +169,9 @@ __global__ __launch_bounds__(256) void k_coarse(const int8_t* __restrict__ q,
 
   const int b = blockIdx.y;
   const int n_valid = clamp_ctx(ctx_len, b, max_ctx);
-  const int t_begin = blockIdx.x * kCoarseTokPerWG;
+  const int t_begin = blockIdx.x * tpw;
   if (t_begin >= n_valid) return;
-  const int t_end = min(t_begin + kCoarseTokPerWG, n_valid);
+  const int t_end = min(t_begin + tpw, n_valid);
 
   for (int i = threadIdx.x; i < kCoarseBins; i += 256) lhist[i] = 0;
 
@@ -371,7 +371,7 @@ __global__ __launch_bounds__(256) void k_coarse32(const int8_t* __restrict__ q,
                                                   const int32_t* __restrict__ ctx_len,
                                                   int32_t* __restrict__ scores,
                                                   uint32_t* __restrict__ hist, int H,
-                                                  int max_ctx) {
+                                                  int max_ctx, int tpw) {
   constexpr int KB = D / 2;   // packed bytes per token
   constexpr int LB = D / 4;   // packed bytes per lane (half a row) per token
   constexpr int NL = LB / 16;  // 16-byte loads per lane per token tile
@@ -382,9 +382,9 @@ __global__ __launch_bounds__(256) void k_coarse32(const int8_t* __restrict__ q,
 
   const int b = blockIdx.y;
   const int n_valid = clamp_ctx(ctx_len, b, max_ctx);
-  const int t_begin = blockIdx.x * kCoarseTokPerWG;
+  const int t_begin = blockIdx.x * tpw;
   if (t_begin >= n_valid) return;
-  const int t_end = min(t_begin + kCoarseTokPerWG, n_valid);
+  const int t_end = min(t_begin + tpw, n_valid);
 
   for (int i = threadIdx.x; i < kCoarseBins; i += 256) lhist[i] = 0;
 
@@ -534,16 +534,17 @@ hipError_t launch_coarse_scores(const int8_t* q, const int8_t* w, const uint8_t*
                                 const int32_t* ctx_len, const CoarseWS& ws, int B, int H,
                                 int D, int max_ctx, hipStream_t st, hipEvent_t start,
                                 hipEvent_t stop) {
-  dim3 grid((max_ctx + kCoarseTokPerWG - 1) / kCoarseTokPerWG, B);
+  const int tpw = coarse_tokens_per_wg(B, max_ctx);
+  dim3 grid((max_ctx + tpw - 1) / tpw, B);
   const bool timed = start != nullptr && stop != nullptr;
 #define LS_COARSE(KERN)                                                                      \
   do {                                                                                       \
     if (timed)                                                                               \
       hipExtLaunchKernelGGL(KERN, grid, dim3(256), 0, st, start, stop, 0u, q, w, kc, ctx_len, \
-                            ws.scores, ws.hist, H, max_ctx);                                 \
+                            ws.scores, ws.hist, H, max_ctx, tpw);                            \
     else                                                                                     \
       hipLaunchKernelGGL(KERN, grid, dim3(256), 0, st, q, w, kc, ctx_len, ws.scores, ws.hist, \
-                         H, max_ctx);                                                        \
+                         H, max_ctx, tpw);                                                   \
   } while (0)
   // up to 16 heads: one 16-head tile; more: 32-head tiles (up to 64 heads)
   if (H <= 16) {

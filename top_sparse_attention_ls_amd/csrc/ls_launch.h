@@ -16,8 +16,18 @@ constexpr int kCoarseBins = 3328;
 constexpr int kWideBins = 7552;
 // Per-request counters sit on their own 128-byte lines (32 words apart).
 constexpr int kCtrStride = 32;
-// Tokens scored by one workgroup of the coarse kernel.
+// Tokens scored by one workgroup of the coarse kernel, at most (its LDS
+// holds that many scores).
 constexpr int kCoarseTokPerWG = 8192;
+// The tokens per workgroup a launch uses: kCoarseTokPerWG, halved (down to
+// 256, one 64-token step per wave) while the grid would hold fewer than 256
+// workgroups, so that short batches spread over the GPU instead of running
+// on a few CUs.
+inline int coarse_tokens_per_wg(int B, int max_ctx) {
+  int tpw = kCoarseTokPerWG;
+  while (tpw > 256 && (int64_t)B * ((max_ctx + tpw - 1) / tpw) < 256) tpw /= 2;
+  return tpw;
+}
 // Candidates scored by one workgroup of the refine kernel.
 constexpr int kRefinePerWG = 256;
 // Keys scored by one workgroup of the prefill indexer, and query rows per
