@@ -116,6 +116,16 @@ def test_index_coarse_head_shapes(ls, H, D):
     run_coarse_case(ls, inp, [6000, 4321], 500)
 
 
+def test_index_coarse_balanced_grid(ls):
+    # 64 requests of 40000 tokens fill fewer than 512 workgroups at 8192
+    # tokens each, so the launch cuts every row into 8 pieces of 5120 tokens
+    # (workgroup boundaries off the 8192 grid); ragged lengths end mid-piece
+    wl = dataclasses.replace(SHRUNK, batch=64, ctx=40000, idx_heads=4, idx_dim=64)
+    ctx = [40000 - 613 * b for b in range(64)]
+    inp = idx_inputs(wl, ctx_len=ctx)
+    run_coarse_case(ls, inp, ctx, 700)
+
+
 def test_index_coarse_every_token_a_candidate(ls):
     wl = dataclasses.replace(SHRUNK, batch=2, ctx=3000)
     inp = idx_inputs(wl)

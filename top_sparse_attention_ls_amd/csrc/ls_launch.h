@@ -4,6 +4,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -19,11 +21,26 @@ constexpr int kCtrStride = 32;
 // Tokens scored by one workgroup of the coarse kernel, at most (its LDS
 // holds that many scores).
 constexpr int kCoarseTokPerWG = 8192;
-// The tokens per workgroup a launch uses: kCoarseTokPerWG, halved (down to
-// 256, one 64-token step per wave) while the grid would hold fewer than 256
-// workgroups, so that short batches spread over the GPU instead of running
-// on a few CUs.
+// Workgroups of the coarse kernel resident on the GPU at once: two per CU
+// (two waves per SIMD) on 256 CUs.
+constexpr int kCoarseSlots = 512;
+// The tokens per workgroup a launch uses.
+//   - kCoarseTokPerWG while that fills every slot.
+//   - Else, when a row cut into floor(slots / B) pieces (rounded up to whole
+//     256-token workgroup steps) keeps at least 2048 tokens per piece, those
+//     pieces: all workgroups run at once with the work spread evenly, instead
+//     of some CUs holding two full workgroups while others hold one.
+//   - Else (little work per request) kCoarseTokPerWG halved, down to 256,
+//     while the grid would hold fewer than 256 workgroups: smaller pieces
+//     than that pay more in each workgroup's fixed work (its histogram, the
+//     query operands) than they gain.
 inline int coarse_tokens_per_wg(int B, int max_ctx) {
+  const int64_t full = (int64_t)B * ((max_ctx + kCoarseTokPerWG - 1) / kCoarseTokPerWG);
+  if (full >= kCoarseSlots) return kCoarseTokPerWG;
+  const int pieces = (int)std::max<int64_t>(1, kCoarseSlots / std::max(B, 1));
+  const int64_t per = ((int64_t)max_ctx + pieces - 1) / pieces;
+  const int64_t bal = (per + 255) / 256 * 256;
+  if (bal >= 2048) return (int)std::min<int64_t>(bal, kCoarseTokPerWG);
   int tpw = kCoarseTokPerWG;
   while (tpw > 256 && (int64_t)B * ((max_ctx + tpw - 1) / tpw) < 256) tpw /= 2;
   return tpw;
