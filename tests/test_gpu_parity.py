@@ -467,9 +467,10 @@ def test_attention_mla_parity(ls, Hq, n_splits):
     assert_attention_close(out, lse, e_out, e_lse, "mla Hq=%d splits=%d" % (Hq, n_splits))
 
 
-@pytest.mark.parametrize("n_splits", [9, 11, 16])
+@pytest.mark.parametrize("n_splits", [9, 11, 16, 40, 64])
 def test_attention_mla_parity_many_splits(ls, n_splits):
-    # more splits than the combine loads at once (8), a partial last group,
+    # more than eight splits: the combine loads the first 32 at once, then
+    # eight at a time (40, 64); a partial last group,
     # a request with no rows at all and one whose rows fill only the first
     # split (the others end with no rows and lse = -inf)
     B, K, S = 3, 512, 300
@@ -484,7 +485,7 @@ def test_attention_mla_parity_many_splits(ls, n_splits):
 
 def test_attention_mla_parity_32_splits(ls):
     # the largest automatic split count (a small batch spread over the
-    # CUs): 32 splits of 32 rows, four combine load rounds
+    # CUs): 32 splits of 32 rows, all loaded by the combine in one round
     B, K, S = 2, 1024, 200
     q, kv, rows = mla_case(B, 128, [1024, 700], K, S, seed=132)
     scale = 1 / math.sqrt(192)

@@ -656,9 +656,13 @@ __global__ __launch_bounds__(256) void k_attn_valu(
 // attention grid so that a request's partials are read on the XCD that wrote
 // them.  Each lane combines 8 consecutive dims, eight splits at a time.  The
 // split LSEs are read eight at a time (L by a running max and rescaled sum),
-// and the first batch of them and of the partials -- for 512 dims and up to
-// eight splits, all of the data -- load together: one round trip per head.
-// DV is a multiple of 8.
+// and the first CB batches of them and of the partials -- for 512 dims and up
+// to 8 CB splits, all of the data -- load together: one round trip per head.
+// CB = 1 for up to eight splits; with more (few requests, many splits each)
+// CB = 4, so that 32 splits take one round trip instead of a chain of them
+// (a separate instance: its 128 registers of partials would cut the
+// occupancy of the many-request launches).  DV is a multiple of 8.
+template <int CB>
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ part_o,
                                                  const float* __restrict__ part_lse,
                                                  uint16_t* __restrict__ out,
@@ -683,10 +687,14 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ pa
       x[u] = j0 + u < n_splits ? y : -INFINITY;
     }
   };
-  uint4 v0[8];
-  float ls0[8];
-  load8(0, 8 * l, v0);
-  load_lse8(0, ls0);
+  // batches past the last split load clamped data with weight 0
+  uint4 v0[CB][8];
+  float ls0[CB][8];
+#pragma unroll
+  for (int c = 0; c < CB; c++) {
+    load8(8 * c, 8 * l, v0[c]);
+    load_lse8(8 * c, ls0[c]);
+  }
   __builtin_amdgcn_sched_barrier(0);
   float M = -INFINITY, W = 0.f;  // running max and sum of 2^(lse - M)
   auto fold = [&](const float (&x)[8]) {
@@ -701,8 +709,9 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ pa
     W = s;
     M = Mn;
   };
-  fold(ls0);
-  for (int j0 = 8; j0 < n_splits; j0 += 8) {
+#pragma unroll
+  for (int c = 0; c < CB; c++) fold(ls0[c]);
+  for (int j0 = 8 * CB; j0 < n_splits; j0 += 8) {
     float x[8];
     load_lse8(j0, x);
     fold(x);
@@ -728,16 +737,16 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ pa
   };
   for (int d = 8 * l; d < DV; d += 8 * kWave) {
     float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < n_splits; j0 += 8) {
-      if (d == 8 * l && j0 == 0) {
-        accum(v0, ls0, a);
-      } else {
-        uint4 v[8];
-        float x[8];
-        load8(j0, d, v);
-        load_lse8(j0, x);
-        accum(v, x, a);
-      }
+    if (d == 8 * l) {
+#pragma unroll
+      for (int c = 0; c < CB; c++) accum(v0[c], ls0[c], a);
+    }
+    for (int j0 = d == 8 * l ? 8 * CB : 0; j0 < n_splits; j0 += 8) {
+      uint4 v[8];
+      float x[8];
+      load8(j0, d, v);
+      load_lse8(j0, x);
+      accum(v, x, a);
     }
     uint4 pk;
     pk.x = (uint32_t)f32_to_bf16_rne(a[0]) | ((uint32_t)f32_to_bf16_rne(a[1]) << 16);
@@ -803,8 +812,12 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
 hipError_t launch_combine(const AttnArgs& a, hipStream_t st) {
   if (a.v_dim % 8 != 0) return hipErrorInvalidValue;
   const int BH = a.B * a.Hq;
-  hipLaunchKernelGGL(k_combine, dim3((BH + 3) / 4), dim3(256), 0, st, a.part_o, a.part_lse, a.out,
-                     a.lse, BH, a.v_dim, a.n_splits);
+  if (a.n_splits > 8)
+    hipLaunchKernelGGL(k_combine<4>, dim3((BH + 3) / 4), dim3(256), 0, st, a.part_o, a.part_lse,
+                       a.out, a.lse, BH, a.v_dim, a.n_splits);
+  else
+    hipLaunchKernelGGL(k_combine<1>, dim3((BH + 3) / 4), dim3(256), 0, st, a.part_o, a.part_lse,
+                       a.out, a.lse, BH, a.v_dim, a.n_splits);
   return hipGetLastError();
 }
 
