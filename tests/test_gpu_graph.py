@@ -2,7 +2,8 @@
 (no allocation, no memset, no host synchronisation), so it can be captured;
 every replay -- with eager steps and synchronisations in between -- must give
 the eager step's results bit for bit, including the hot-buffer scratch rows
-it writes and the workspace it leaves cleared for the next call.  The
+it writes and the workspace it leaves cleared for the next call; the
+single-request MHA step's replays are also checked against the oracle.  The
 captured layer stack of the serving loop is also stepped against the
 oracle's serving loop after every replay."""
 import dataclasses
@@ -10,8 +11,9 @@ import dataclasses
 import pytest
 import torch
 
+from oracle import oracle as orc
 from top_sparse_attention_ls_amd import synth
-from tests.gpu_common import np_
+from tests.gpu_common import np_, bits, poison_, assert_attention_close
 from tests.serve_oracle import ServeShadow
 
 pytestmark = pytest.mark.gpu
@@ -68,6 +70,65 @@ def test_decode_step_graph_replays_match_eager(ls):
         torch.cuda.synchronize()
         for a, b in zip(ref, state(out, lse)):
             assert torch.equal(a, b), "eager step after replay %d differs" % i
+
+
+def test_tiny_mha_step_graph_replays_match_oracle(ls):
+    # the single-request 4K step (generic MHA attention, no hot buffer) as the
+    # bench replays it: every replay, with eager steps between, against the
+    # oracle's request and bit for bit against the eager step
+    wl = synth.WORKLOADS["tiny-4k"]
+    inp = synth.indexer_inputs(wl, "cpu")
+    qa = synth.attention_query(wl, "cpu")
+    Kc, Vc = synth.kv_cache_mha(wl, "cpu")
+    step = ls.DecodeStep(batch=1, max_ctx=wl.ctx, idx_heads=wl.idx_heads, idx_dim=wl.idx_dim,
+                         n_cand=wl.n_cand, topk=wl.topk, q_heads=wl.q_heads, qk_dim=wl.qk_dim,
+                         v_dim=wl.v_dim, scale=wl.scale, kv_heads=wl.kv_heads,
+                         kv_row_stride=wl.kv_heads * wl.qk_dim, kv_head_stride=wl.qk_dim)
+    keys = inp["keys"].to(DEV)
+    args = dict(q_idx=inp["q"].to(DEV), w_idx=inp["w"].to(DEV), kc=ls.pack_coarse(keys), k8=keys,
+                ctx_len=torch.tensor([wl.ctx], dtype=torch.int32, device=DEV),
+                q_attn=qa.to(DEV), k_cache=Kc.to(DEV), v_cache=Vc.to(DEV))
+    r = orc.decode_request(inp["q"][0].numpy(), inp["w"][0].numpy(), inp["keys"][0].numpy(),
+                           wl.ctx, wl.n_cand, wl.topk, bits(qa[0]), wl.scale,
+                           k_cache_bits=bits(Kc[0]).reshape(-1),
+                           v_cache_bits=bits(Vc[0]).reshape(-1), n_kv_heads=wl.kv_heads,
+                           v_dim=wl.v_dim, row_stride=wl.kv_heads * wl.qk_dim,
+                           head_stride=wl.qk_dim)
+
+    def check(out, lse, what):
+        assert np_(step.cand)[0].tolist() == r["cand"].tolist(), what
+        assert np_(step.topk)[0].tolist() == r["topk"].tolist(), what
+        assert np_(step.topk_score)[0].tolist() == r["topk_score"].tolist(), what
+        assert_attention_close(out, lse, r["out"][None], r["lse"][None], what)
+
+    out, lse = step.run(**args)
+    torch.cuda.synchronize()
+    check(out, lse, "eager step")
+    ref = [t.clone() for t in (step.cand, step.topk, step.topk_score, out.view(torch.int16), lse)]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step.run(**args)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gout, glse = step.run(**args)
+    torch.cuda.synchronize()
+
+    for i in range(3):
+        for t in (step.cand, step.topk, step.topk_score, gout, glse):
+            poison_(t)
+        graph.replay()
+        torch.cuda.synchronize()
+        check(gout, glse, "replay %d" % i)
+        got = (step.cand, step.topk, step.topk_score, gout.view(torch.int16), glse)
+        for a, b in zip(ref, got):
+            assert torch.equal(a, b), "replay %d differs from the eager step" % i
+        out, lse = step.run(**args)  # eager work between the replays
+        torch.cuda.synchronize()
+        check(out, lse, "eager step after replay %d" % i)
 
 
 def serving_layer(ls, wl, seed, dev):
