@@ -402,7 +402,7 @@ STAGE_KERNELS = {
     "refine_topk_resolve": "k_refine + k_topk_hist",
     "miss_gather": "k_hot_gather",
     "attention": "k_attn_mfma",
-    "combine": "k_combine",
+    "combine": "k_combine (k_combine_wide when the rows are few)",
 }
 
 

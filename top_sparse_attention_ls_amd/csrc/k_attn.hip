@@ -9,7 +9,8 @@
 //                 v_mfma_f32_16x16x32_bf16 for Q.K^T and P.V, online softmax
 //                 in fp32 (exp2 domain), split over the row list.
 // k_attn_valu  -- any head layout (MHA / GQA, small head dims), plain VALU.
-// k_combine    -- merges the per-split partials (normalised o, log2-lse).
+// k_combine    -- merges the per-split partials (normalised o, log2-lse);
+//                 k_combine_wide, one workgroup per row, when the rows are few.
 #include "ls_device.h"
 #include "ls_launch.h"
 
@@ -758,6 +759,89 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ pa
   if (l == 0) lse[bh] = L * kLn2;
 }
 
+// The merge for launches with few (request, head) rows, where one wave per
+// row would leave most CUs idle (four requests with 32 splits: 512 rows, 128
+// workgroups on 256 CUs): one workgroup per row, wave w taking splits
+// w, w+4, ...  Each wave keeps its own running max M_w, sum W_w of
+// 2^(lse - M_w) and the partials weighted by 2^(lse - M_w) (lane l: dims
+// 8l .. 8l+7, all of a wave's loads issued together), then the waves meet
+// in LDS: L = M + log2(sum_w W_w 2^(M_w - M)) with M the largest M_w, and
+// o = sum_w 2^(M_w - L) acc_w.  DV <= 8 * 64, a multiple of 8; n_splits <=
+// 4 * kWideSplitsPerWave.
+constexpr int kWideSplitsPerWave = 16;
+
+__global__ __launch_bounds__(256) void k_combine_wide(const uint16_t* __restrict__ part_o,
+                                                      const float* __restrict__ part_lse,
+                                                      uint16_t* __restrict__ out,
+                                                      float* __restrict__ lse, int DV,
+                                                      int n_splits) {
+  __shared__ float sh_m[4], sh_w[4];
+  __shared__ __attribute__((aligned(16))) float sh_acc[4][512];
+  const int bh = xcd_major(blockIdx.x, gridDim.x);
+  const int l = lane_id(), w = wave_id();
+  const float* pl = part_lse + (size_t)bh * n_splits;
+  const uint16_t* po = part_o + (size_t)bh * n_splits * DV;
+  const int dc = min(8 * l, DV - 8);  // lanes past DV load clamped dims, store nothing
+  // this wave's splits: w + 4 u (unconditional loads of a clamped split;
+  // splits past the end get weight 0)
+  uint4 v[kWideSplitsPerWave];
+  float x[kWideSplitsPerWave];
+#pragma unroll
+  for (int u = 0; u < kWideSplitsPerWave; u++) {
+    const int j = w + 4 * u;
+    const int jc = min(j, n_splits - 1);
+    v[u] = *(const uint4*)(po + (size_t)jc * DV + dc);
+    const float y = pl[jc];
+    x[u] = j < n_splits ? y : -INFINITY;
+  }
+  float mw = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kWideSplitsPerWave; u++) mw = fmaxf(mw, x[u]);
+  float ww = 0.f;
+  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (mw != -INFINITY) {
+#pragma unroll
+    for (int u = 0; u < kWideSplitsPerWave; u++) {
+      const float wj = exp2f(x[u] - mw);  // 0 for splits past the end
+      ww += wj;
+      const uint32_t y[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        a[2 * e] += wj * __uint_as_float(y[e] << 16);
+        a[2 * e + 1] += wj * __uint_as_float(y[e] & 0xFFFF0000u);
+      }
+    }
+  }
+  if (l == 0) {
+    sh_m[w] = mw;
+    sh_w[w] = ww;
+  }
+  __syncthreads();
+  const float M = fmaxf(fmaxf(sh_m[0], sh_m[1]), fmaxf(sh_m[2], sh_m[3]));
+  uint16_t* ob = out + (size_t)bh * DV;
+  if (M == -INFINITY) {  // no valid row in any split
+    for (int d = 2 * threadIdx.x; d < DV; d += 512) *(uint32_t*)(ob + d) = 0u;
+    if (threadIdx.x == 0) lse[bh] = -INFINITY;
+    return;
+  }
+  float W = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; k++) W += sh_w[k] * exp2f(sh_m[k] - M);  // 0 for empty waves
+  const float L = M + log2f(W);
+  const float sc = mw == -INFINITY ? 0.f : exp2f(mw - L);
+#pragma unroll
+  for (int e = 0; e < 8; e++) sh_acc[w][8 * l + e] = a[e] * sc;
+  __syncthreads();
+  // thread t: dims 2t, 2t+1
+  for (int d = 2 * threadIdx.x; d < DV; d += 512) {
+    const float o0 = sh_acc[0][d] + sh_acc[1][d] + sh_acc[2][d] + sh_acc[3][d];
+    const float o1 = sh_acc[0][d + 1] + sh_acc[1][d + 1] + sh_acc[2][d + 1] + sh_acc[3][d + 1];
+    *(uint32_t*)(ob + d) =
+        (uint32_t)f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16);
+  }
+  if (threadIdx.x == 0) lse[bh] = L * kLn2;
+}
+
 // ---------------------------------------------------------------- launchers --
 
 bool attn_uses_mfma(int Hq, int n_kv, int qk_dim, int v_dim, const void* k, const void* v) {
@@ -809,9 +893,22 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// The one-workgroup-per-row merge when one wave per row would fill fewer
+// than 256 workgroups (about one per CU) and each wave still gets at least
+// two splits.
+bool combine_uses_wide(int BH, int DV, int n_splits) {
+  return (BH + 3) / 4 < 256 && n_splits >= 8 && n_splits <= 4 * kWideSplitsPerWave &&
+         DV <= 512;
+}
+
 hipError_t launch_combine(const AttnArgs& a, hipStream_t st) {
   if (a.v_dim % 8 != 0) return hipErrorInvalidValue;
   const int BH = a.B * a.Hq;
+  if (combine_uses_wide(BH, a.v_dim, a.n_splits)) {
+    hipLaunchKernelGGL(k_combine_wide, dim3(BH), dim3(256), 0, st, a.part_o, a.part_lse, a.out,
+                       a.lse, a.v_dim, a.n_splits);
+    return hipGetLastError();
+  }
   if (a.n_splits > 8)
     hipLaunchKernelGGL(k_combine<4>, dim3((BH + 3) / 4), dim3(256), 0, st, a.part_o, a.part_lse,
                        a.out, a.lse, BH, a.v_dim, a.n_splits);

@@ -207,6 +207,8 @@ def cmd_counters(args):
             base = "k_attn_fused"  # the miss gather folded into the tile DMA
         if base == "k_coarse32":
             base = "k_coarse"  # the same pass on 32-head tiles
+        if base == "k_combine_wide":
+            base = "k_combine"  # the same merge, one workgroup per row
         row = ["`%s`" % k, str(launches[k])]
         entry = {"launches": launches[k], "counters": d}
         if "FETCH_SIZE" in counters and "WRITE_SIZE" in counters:
